@@ -1,0 +1,423 @@
+"""CPU oracle for the sparsely-gated noisy top-k Mixture-of-Experts layer forward.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import or call this module.  The product path never
+routes through it, and it shares no code with the HIP implementation: it takes
+plain numpy arrays and computes, in float64, what the pages define, one step
+after the other, with no blocking, fusion or reordering.
+
+Pages cited (titles as published):
+  [MoE lesson]  "MoE:稀疏门控混合专家" (nengyongai.cn lesson on Shazeer et al.
+                2017): section 二 (what one MoE layer looks like: the 512 ->
+                1024 -> 512 expert FFN and y = sum_i G(x)_i E_i(x)), section 三
+                (how the gate picks: score table W_g, KeepTopK to -inf, softmax,
+                the worked 8-expert top-2 example, the 16 x 256 "-h"
+                hierarchy), section 四 (noise: H = x W_g + noise * softplus(x
+                W_noise), noise redrawn every call).
+  [Paper card]  "Outrageously Large Neural Networks: The Sparsely-Gated
+                Mixture-of-Experts Layer - 中文验证版" (ai-papers.xuzou.cn):
+                section 瓶颈 (each expert receives about k*b/n rows), section
+                方法适配 (k = 4 in many LM runs; importance and load losses keep
+                rows spread over experts).
+  [Reading note] "Outrageously Large Neural Networks — MoE 怎样让模型“很大但
+                不每次全算”" (wudongming97.github.io): sections 核心想法 and
+                方法怎么做 (top-k gating, learnable noise, importance loss on
+                per-expert gate totals and load loss on per-expert row counts).
+  [Mixtral page] "MoE 混合专家：参数大、计算省" (transformer.xph.ink), section
+                核心概念 (Mixtral: 8 experts, top-2 routing).
+
+Readings of points the pages leave open (each also listed with its reason in
+the design notes):
+  * top-k ties go to the lower expert index; the k kept experts of a token are
+    stored in ascending expert index ("slot" order);
+  * softplus is exact, with no added floor;
+  * the noise draw eps ~ N(0,1) is an input; no eps means noise-free gating;
+  * the importance of expert e is the sum over tokens of its gate; the load of
+    expert e is the sum over tokens of the probability that e would still be
+    in the top-k if only its own noise were redrawn, Phi((clean - theta) /
+    softplus(raw)) with theta the k-th largest noisy logit among the other
+    experts; CV^2 is population variance over squared mean (0 when the mean
+    is 0); without noise the load is the hard row count;
+  * the hierarchy multiplies the primary (group) gate by the secondary
+    (expert-in-group) gate; each group has its own secondary tables, which are
+    the rows g*Eg .. (g+1)*Eg-1 of the flat [E][d] tables;
+  * the SwiGLU expert is (silu(X W_gate) * (X W_up)) W_down, no biases.
+  * parity unpinned: the hierarchical load (reported as hard counts per
+    expert) has no page formula.
+
+Array layouts follow the library's: x [T][d]; w_gate, w_noise [E][d] (the
+pages' d x n table stored transposed); w1 [E][h][d]; w3 [E][h][d]; w2 [E][d][h].
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+from scipy.special import erfc
+
+
+def _f64(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor (bf16 is up-cast exactly)
+        a = a.detach().to("cpu").float().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Scalar functions
+# ---------------------------------------------------------------------------
+
+def softplus(z: np.ndarray) -> np.ndarray:
+    """softplus(z) = ln(1 + e^z), written in the overflow-safe form
+    max(z, 0) + ln(1 + e^-|z|).  [MoE lesson, section 四: the noise scale]"""
+    z = np.asarray(z, dtype=np.float64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def normal_cdf(z: np.ndarray) -> np.ndarray:
+    """Standard normal CDF, Phi(z) = erfc(-z / sqrt 2) / 2."""
+    return 0.5 * erfc(-np.asarray(z, dtype=np.float64) / math.sqrt(2.0))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + e^-z), the gate nonlinearity of the
+    SwiGLU expert; sigmoid is written (1 + tanh(z/2)) / 2 so that no
+    exponential overflows."""
+    z = np.asarray(z, dtype=np.float64)
+    return z * (0.5 * (1.0 + np.tanh(0.5 * z)))
+
+
+# ---------------------------------------------------------------------------
+# Gating  [MoE lesson, sections 三 and 四]
+# ---------------------------------------------------------------------------
+
+def noisy_logits(x, w_gate, w_noise=None, bias=None, eps=None):
+    """Scores of every expert for every token.
+
+    clean = x W_g (+ bias), one score per expert column of the table;
+    with noise: H = clean + eps * softplus(x W_noise); without: H = clean.
+    Returns (clean, sp, H); sp is None without noise.
+    [MoE lesson, section 三 (score table) and section 四 (the noisy score)]
+    """
+    x = _f64(x)
+    clean = x @ _f64(w_gate).T
+    if bias is not None:
+        clean = clean + _f64(bias)[None, :]
+    if eps is None or w_noise is None:
+        return clean, None, clean.copy()
+    sp = softplus(x @ _f64(w_noise).T)
+    H = clean + _f64(eps) * sp
+    return clean, sp, H
+
+
+def keep_top_k(H: np.ndarray, k: int):
+    """KeepTopK: per token, the k largest scores survive, the rest become -inf.
+
+    Ties are broken toward the lower expert index (a stable sort of the
+    negated scores keeps equal scores in index order).  Returns
+      idx    [T][k] int32, the kept experts in ascending index order,
+      kth    [T]  the k-th largest score,
+      k1th   [T]  the (k+1)-th largest score (-inf if k == E),
+      margin [T]  kth - k1th.
+    [MoE lesson, section 三, step 2]
+    """
+    H = np.asarray(H, dtype=np.float64)
+    T, E = H.shape
+    order = np.argsort(-H, axis=1, kind="stable")
+    kept = order[:, :k]
+    idx = np.sort(kept, axis=1).astype(np.int32)
+    rows = np.arange(T)
+    kth = H[rows, order[:, k - 1]] if T else np.zeros(0)
+    if k < E:
+        k1th = H[rows, order[:, k]] if T else np.zeros(0)
+    else:
+        k1th = np.full(T, -np.inf)
+    with np.errstate(invalid="ignore"):
+        margin = kth - k1th
+    return idx, kth, k1th, margin
+
+
+def kept_softmax(H: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Softmax over the kept scores only; the dropped ones are -inf and their
+    exponential is 0.  Returns gates [T][k] in the slot order of idx.
+    [MoE lesson, section 三, step 3]"""
+    H = np.asarray(H, dtype=np.float64)
+    kept = np.take_along_axis(H, idx.astype(np.int64), axis=1)
+    if kept.shape[0] == 0:
+        return kept
+    m = kept.max(axis=1, keepdims=True)
+    w = np.exp(kept - m)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def dense_gates(idx: np.ndarray, gates: np.ndarray, n_experts: int) -> np.ndarray:
+    """The sparse gate vector G(x) as a dense [T][E] array, zero off the kept set."""
+    T = idx.shape[0]
+    G = np.zeros((T, n_experts), dtype=np.float64)
+    for s in range(idx.shape[1]):
+        G[np.arange(T), idx[:, s]] = gates[:, s]
+    return G
+
+
+def flat_gate(x, w_gate, w_noise, bias, eps, k):
+    """Noisy top-k gate of the flat layer.  Returns a dict with clean, sp, H,
+    idx, gates, kth, k1th, margin."""
+    clean, sp, H = noisy_logits(x, w_gate, w_noise, bias, eps)
+    idx, kth, k1th, margin = keep_top_k(H, k)
+    gates = kept_softmax(H, idx)
+    return dict(clean=clean, sp=sp, H=H, idx=idx, gates=gates,
+                kth=kth, k1th=k1th, margin=margin)
+
+
+def hier_gate(x, w_gate_p, w_noise_p, eps_p, w_gate, w_noise, eps,
+              n_groups, k_groups, k_per_group):
+    """Two-level gate of the "-h" layer: the primary gate keeps k_groups of the
+    n_groups groups, then inside each kept group a secondary gate keeps
+    k_per_group of its experts; the final gate is the product of the two
+    levels' gates.  Expert j of group g is global expert g*Eg + j.
+    [MoE lesson, section 三: 16 groups x 256 experts, 2 groups then 2 experts]
+    The product rule is a reading (the page gives only the selection rule).
+    Returns idx [T][k] (ascending expert index), gates [T][k], the primary
+    gate's dict, and margin [T] = the smallest margin over both levels.
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    E = _f64(w_gate).shape[0]
+    Eg = E // n_groups
+    prim = flat_gate(x, w_gate_p, w_noise_p, None, eps_p, k_groups)
+    k = k_groups * k_per_group
+    idx = np.zeros((T, k), dtype=np.int32)
+    gates = np.zeros((T, k), dtype=np.float64)
+    margin = prim["margin"].copy()
+    wg = _f64(w_gate)
+    wn = _f64(w_noise) if w_noise is not None else None
+    ep = _f64(eps) if eps is not None else None
+    for t in range(T):
+        s = 0
+        for a in range(k_groups):          # groups in ascending order
+            g = int(prim["idx"][t, a])
+            rows = slice(g * Eg, (g + 1) * Eg)
+            sub = flat_gate(x[t:t + 1], wg[rows], None if wn is None else wn[rows],
+                            None, None if ep is None else ep[t:t + 1, g, :],
+                            k_per_group)
+            margin[t] = min(margin[t], sub["margin"][0])
+            for b in range(k_per_group):   # experts in ascending order
+                idx[t, s] = g * Eg + sub["idx"][0, b]
+                gates[t, s] = prim["gates"][t, a] * sub["gates"][0, b]
+                s += 1
+    return dict(idx=idx, gates=gates, margin=margin, primary=prim)
+
+
+# ---------------------------------------------------------------------------
+# Routing: group the (token, slot) pairs by expert  [Paper card, section 瓶颈]
+# ---------------------------------------------------------------------------
+
+def route(idx: np.ndarray, n_experts: int):
+    """Stable grouping of the T*k (token, slot) assignments by expert.
+
+    counts[e]  number of assignments to expert e;
+    offsets    exclusive prefix sum of counts, length E+1;
+    perm[p]    the assignment t*k+s placed at position p: expert-contiguous,
+               tokens ascending inside each expert;
+    inv[t*k+s] the position p of that assignment (inverse of perm).
+    """
+    T, k = idx.shape
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in idx.reshape(-1):
+        counts[e] += 1
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    fill = offsets[:-1].copy()
+    perm = np.zeros(T * k, dtype=np.int64)
+    inv = np.zeros(T * k, dtype=np.int64)
+    for t in range(T):
+        for s in range(k):
+            e = idx[t, s]
+            p = fill[e]
+            fill[e] += 1
+            perm[p] = t * k + s
+            inv[t * k + s] = p
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            perm.astype(np.int32), inv.astype(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# Experts  [MoE lesson, section 二: a one-hidden-layer FFN, 512 -> 1024 -> 512]
+# ---------------------------------------------------------------------------
+
+def expert_relu(X, w1_e, w2_e) -> np.ndarray:
+    """E(X) = max(X W1, 0) W2 with W1 stored [h][d] and W2 stored [d][h]."""
+    X = _f64(X)
+    hid = np.maximum(X @ _f64(w1_e).T, 0.0)
+    return hid @ _f64(w2_e).T
+
+
+def expert_swiglu(X, w1_e, w3_e, w2_e) -> np.ndarray:
+    """E(X) = (silu(X W_gate) * (X W_up)) W_down, with W_gate = w1 [h][d],
+    W_up = w3 [h][d], W_down = w2 [d][h].  [Mixtral page, section 核心概念]"""
+    X = _f64(X)
+    hid = silu(X @ _f64(w1_e).T) * (X @ _f64(w3_e).T)
+    return hid @ _f64(w2_e).T
+
+
+def expert_apply(X, e, w1, w2, w3=None) -> np.ndarray:
+    if w3 is None:
+        return expert_relu(X, w1[e], w2[e])
+    return expert_swiglu(X, w1[e], w3[e], w2[e])
+
+
+def run_experts(x, perm, offsets, k, w1, w2, w3=None) -> np.ndarray:
+    """y_sorted[p] = E_e(x[perm[p] // k]) for every position p of expert e.
+    Experts with no rows are not evaluated (their gate is zero for every
+    token).  [MoE lesson, section 二: dropped experts are skipped]"""
+    x = _f64(x)
+    E = len(offsets) - 1
+    A = int(offsets[-1])
+    d = x.shape[1]
+    y_sorted = np.zeros((A, _f64(w2[0]).shape[0] if E else d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        toks = perm[lo:hi] // k
+        y_sorted[lo:hi] = expert_apply(x[toks], e, w1, w2, w3)
+    return y_sorted
+
+
+def combine(y_sorted, inv, gates) -> np.ndarray:
+    """y_t = sum over slots s of gate[t,s] * y_sorted[inv[t*k+s]], slots in
+    ascending order.  [MoE lesson, section 二: y = sum_i G(x)_i E_i(x)]"""
+    gates = np.asarray(gates, dtype=np.float64)
+    T, k = gates.shape
+    d = y_sorted.shape[1] if y_sorted.ndim == 2 else 0
+    y = np.zeros((T, d))
+    for s in range(k):
+        y += gates[:, s:s + 1] * y_sorted[inv.reshape(T, k)[:, s]]
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Balance statistics  [Reading note, sections 核心想法/方法怎么做; Paper card,
+# section 方法适配]
+# ---------------------------------------------------------------------------
+
+def cv_squared(v) -> float:
+    """Squared coefficient of variation: population variance / mean^2
+    (0 for an all-zero vector)."""
+    v = np.asarray(v, dtype=np.float64)
+    if v.size == 0:
+        return 0.0
+    m = v.mean()
+    if m == 0.0:
+        return 0.0
+    return float(((v - m) ** 2).mean() / (m * m))
+
+
+def importance(idx, gates, n_experts) -> np.ndarray:
+    """Importance_e = sum over tokens of G(x)_e."""
+    return dense_gates(idx, gates, n_experts).sum(axis=0)
+
+
+def load_estimate(clean, sp, H, idx, kth, k1th) -> np.ndarray:
+    """Smooth load: Load_e = sum_t P(e in top-k of token t when only expert e's
+    noise is redrawn) = sum_t Phi((clean[t,e] - theta[t,e]) / sp[t,e]),
+    theta[t,e] = k-th largest noisy score among the experts other than e,
+    which is the (k+1)-th largest score if e is kept and the k-th otherwise.
+    """
+    T, E = H.shape
+    kept = np.zeros((T, E), dtype=bool)
+    for s in range(idx.shape[1]):
+        kept[np.arange(T), idx[:, s]] = True
+    theta = np.where(kept, k1th[:, None], kth[:, None])
+    return normal_cdf((clean - theta) / sp).sum(axis=0)
+
+
+def balance_stats(n_experts, idx, gates, counts, gate_info=None,
+                  w_importance=1.0, w_load=1.0):
+    """importance[E], load[E], cv2 of each, and the weighted loss.
+
+    gate_info is the flat gate's dict when the smooth load applies (flat noisy
+    gating); otherwise the load is the hard row count of each expert.
+    """
+    imp = importance(idx, gates, n_experts)
+    if gate_info is not None and gate_info.get("sp") is not None:
+        load = load_estimate(gate_info["clean"], gate_info["sp"], gate_info["H"],
+                             gate_info["idx"], gate_info["kth"], gate_info["k1th"])
+    else:
+        load = np.asarray(counts, dtype=np.float64)
+    ci, cl = cv_squared(imp), cv_squared(load)
+    return dict(importance=imp, load=load, cv2_importance=ci, cv2_load=cl,
+                loss=w_importance * ci + w_load * cl)
+
+
+# ---------------------------------------------------------------------------
+# The layer
+# ---------------------------------------------------------------------------
+
+def gate(inp: Dict, cfg) -> Dict:
+    """Flat or hierarchical gate, chosen by cfg.n_groups."""
+    if cfg.n_groups:
+        return hier_gate(inp["x"], inp["w_gate_p"], inp.get("w_noise_p"),
+                         inp.get("eps_p"), inp["w_gate"], inp.get("w_noise"),
+                         inp.get("eps"), cfg.n_groups, cfg.k_groups,
+                         cfg.k_per_group)
+    return flat_gate(inp["x"], inp["w_gate"], inp.get("w_noise"), inp.get("bias"),
+                     inp.get("eps"), cfg.top_k)
+
+
+def forward(inp: Dict, cfg, w_importance=1.0, w_load=1.0,
+            with_experts: bool = True) -> Dict:
+    """Whole layer: gate -> route -> experts -> combine -> balance stats.
+    Returns every intermediate the HIP path exposes."""
+    g = gate(inp, cfg)
+    idx, gates = g["idx"], g["gates"]
+    counts, offsets, perm, inv = route(idx, cfg.n_experts)
+    out = dict(idx=idx, gates=gates, margin=g["margin"], counts=counts,
+               offsets=offsets, perm=perm, inv=inv, gate_info=g)
+    if with_experts:
+        w1 = _f64(inp["w1"])
+        w2 = _f64(inp["w2"])
+        w3 = _f64(inp.get("w3"))
+        y_sorted = run_experts(inp["x"], perm, offsets, cfg.top_k, w1, w2, w3)
+        out["y_sorted"] = y_sorted
+        out["y"] = combine(y_sorted, inv, gates)
+    out.update(balance_stats(cfg.n_experts, idx, gates, counts,
+                             None if cfg.n_groups else g, w_importance, w_load))
+    return out
+
+
+def token_outputs(inp: Dict, cfg, tokens, idx, gates) -> np.ndarray:
+    """y for a subset of tokens, given that token's selection and gates:
+    y_t = sum_s gates[t,s] * E_{idx[t,s]}(x_t).  Used to check sampled rows of
+    large layers one by one."""
+    x = _f64(inp["x"])
+    out = []
+    for t in tokens:
+        acc = 0.0
+        for s in range(idx.shape[1]):
+            e = int(idx[t, s])
+            w1 = _f64(inp["w1"][e])
+            w2 = _f64(inp["w2"][e])
+            if inp.get("w3") is not None:
+                ye = expert_swiglu(x[t:t + 1], w1, _f64(inp["w3"][e]), w2)
+            else:
+                ye = expert_relu(x[t:t + 1], w1, w2)
+            acc = acc + gates[t, s] * ye[0]
+        out.append(acc)
+    return np.array(out)
+
+
+def dense_forward(inp: Dict, cfg) -> np.ndarray:
+    """Brute force: evaluate every expert on every token and sum with the dense
+    gate vector, y_t = sum over all e of G(x_t)_e E_e(x_t).  Tiny inputs only.
+    [MoE lesson, section 二]"""
+    g = gate(inp, cfg)
+    G = dense_gates(g["idx"], g["gates"], cfg.n_experts)
+    x = _f64(inp["x"])
+    w1, w2, w3 = _f64(inp["w1"]), _f64(inp["w2"]), _f64(inp.get("w3"))
+    y = np.zeros((x.shape[0], w2.shape[1]))
+    for e in range(cfg.n_experts):
+        y += G[:, e:e + 1] * expert_apply(x, e, w1, w2, w3)
+    return y

@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against facts fixed outside it: values the pages
+print, closed forms, textbook special cases, library routines, brute force on
+tiny inputs and invariants.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, MoEConfig, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _small(**kw):
+    base = dict(name="small", tokens=64, d_model=32, n_experts=6, d_hidden=48,
+                top_k=2, noisy=True, dtype="f32", gate_std=0.3)
+    base.update(kw)
+    return MoEConfig(**base)
+
+
+# ---------------------------------------------------------------- gate ----
+
+def test_worked_example_from_the_lesson_page():
+    """8 experts, keep 2: scores 2.5 and 2.1 win and give gates ~0.60/0.40;
+    the other six scores must not matter (their values are not printed)."""
+    g = _load("worked_example.json")
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        H = rng.uniform(-5.0, 2.09, size=(1, g["n_experts"]))
+        H[0, g["kept_experts"]] = g["kept_scores"]
+        idx, _, _, _ = oracle.keep_top_k(H, g["top_k"])
+        assert idx.tolist() == [g["kept_experts"]]
+        gates = oracle.kept_softmax(H, idx)[0]
+        # printed values, to the printed number of decimals
+        assert [round(math.exp(s), g["printed_exp_decimals"]) for s in g["kept_scores"]] == g["printed_exp"]
+        assert np.round(gates, g["printed_gate_decimals"]).tolist() == g["printed_gates"]
+        # exact value: a 2-way softmax is the logistic of the score gap
+        assert gates[0] == pytest.approx(1.0 / (1.0 + math.exp(-0.4)), rel=1e-14)
+        assert gates[1] == pytest.approx(1.0 / (1.0 + math.exp(0.4)), rel=1e-14)
+
+
+def test_zero_tables_give_uniform_gates_and_lowest_index_ties():
+    """W_g = W_noise = 0 and eps = 0 make every score 0: the tie-break keeps
+    experts 0..k-1 and each gate is 1/k."""
+    T, d, E, k = 5, 7, 9, 3
+    x = np.random.default_rng(0).standard_normal((T, d))
+    z = np.zeros((E, d))
+    g = oracle.flat_gate(x, z, z, None, np.zeros((T, E)), k)
+    assert (g["idx"] == np.arange(k)).all()
+    assert np.allclose(g["gates"], 1.0 / k, rtol=0, atol=1e-15)
+    assert (g["margin"] == 0).all()
+
+
+def test_ties_prefer_lower_index():
+    H = np.array([[1.0, 3.0, 3.0, 0.5, 3.0]])
+    idx, kth, k1th, _ = oracle.keep_top_k(H, 2)
+    assert idx.tolist() == [[1, 2]]
+    assert kth[0] == 3.0 and k1th[0] == 3.0
+
+
+def test_noisy_logits_hand_example():
+    """x = [1, 2], W_g = identity, W_noise = 0 (softplus(0) = ln 2), eps = [1, -1]:
+    H = [1 + ln 2, 2 - ln 2]; with a bias of [0.5, -0.5] the clean part shifts."""
+    x = np.array([[1.0, 2.0]])
+    wg = np.eye(2)
+    wn = np.zeros((2, 2))
+    eps = np.array([[1.0, -1.0]])
+    clean, sp, H = oracle.noisy_logits(x, wg, wn, None, eps)
+    assert clean.tolist() == [[1.0, 2.0]]
+    assert np.allclose(sp, math.log(2.0), rtol=1e-15)
+    assert np.allclose(H, [[1 + math.log(2), 2 - math.log(2)]], rtol=1e-15)
+    clean_b, _, H_b = oracle.noisy_logits(x, wg, wn, np.array([0.5, -0.5]), eps)
+    assert np.allclose(clean_b, [[1.5, 1.5]])
+    assert np.allclose(H_b, [[1.5 + math.log(2), 1.5 - math.log(2)]])
+    # a non-identity table: x W_g uses the row of expert e, W_g stored [E][d]
+    wg2 = np.array([[1.0, 0.0], [3.0, -1.0], [0.0, 2.0]])
+    c2, _, _ = oracle.noisy_logits(x, wg2)
+    assert c2.tolist() == [[1.0, 1.0, 4.0]]
+    # raw noise scale uses W_noise rows the same way: softplus(x . [0, 1]) = softplus(2)
+    wn2 = np.array([[0.0, 1.0], [0.0, 0.0]])
+    _, sp2, _ = oracle.noisy_logits(x, wg, wn2, None, eps)
+    assert sp2[0, 0] == pytest.approx(math.log1p(math.exp(2.0)), rel=1e-15)
+    assert sp2[0, 1] == pytest.approx(math.log(2.0), rel=1e-15)
+
+
+def test_softplus_closed_forms():
+    assert oracle.softplus(0.0) == pytest.approx(math.log(2.0), rel=1e-15)
+    assert oracle.softplus(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert oracle.softplus(-40.0) == pytest.approx(math.exp(-40.0), rel=1e-12)
+    z = np.linspace(-20, 20, 401)
+    assert np.allclose(oracle.softplus(z) - oracle.softplus(-z), z, rtol=0, atol=1e-12)
+    assert np.allclose(oracle.softplus(np.array([1.0, -3.0])),
+                       [math.log1p(math.e), math.log1p(math.exp(-3.0))], rtol=1e-14)
+
+
+def test_normal_cdf_closed_forms():
+    assert oracle.normal_cdf(0.0) == 0.5
+    assert oracle.normal_cdf(1.959963984540054) == pytest.approx(0.975, rel=1e-12)
+    assert oracle.normal_cdf(-1.0) == pytest.approx(0.15865525393145707, rel=1e-12)
+    z = np.linspace(-6, 6, 121)
+    assert np.allclose(oracle.normal_cdf(z) + oracle.normal_cdf(-z), 1.0, atol=1e-15)
+
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-14)
+    assert oracle.silu(-2.0) == pytest.approx(-2.0 / (1.0 + math.exp(2.0)), rel=1e-13)
+    assert oracle.silu(50.0) == pytest.approx(50.0, rel=1e-15)
+    z = torch.linspace(-8, 8, 161, dtype=torch.float64)
+    assert np.allclose(oracle.silu(z.numpy()), torch.nn.functional.silu(z).numpy(), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_top_k_equals_brute_force_best_subset(k):
+    """With distinct scores the kept set is the k-subset of largest sum."""
+    rng = np.random.default_rng(k)
+    E = 6
+    H = rng.standard_normal((40, E))
+    idx, kth, k1th, margin = oracle.keep_top_k(H, k)
+    for t in range(H.shape[0]):
+        best = max(itertools.combinations(range(E), k), key=lambda s: H[t, list(s)].sum())
+        assert idx[t].tolist() == list(best)
+        srt = np.sort(H[t])[::-1]
+        assert kth[t] == srt[k - 1] and k1th[t] == srt[k]
+        assert margin[t] == srt[k - 1] - srt[k]
+
+
+def test_k_equal_E_is_the_full_softmax():
+    rng = np.random.default_rng(3)
+    H = rng.standard_normal((10, 5)) * 3
+    idx, _, k1th, _ = oracle.keep_top_k(H, 5)
+    g = oracle.kept_softmax(H, idx)
+    assert np.isneginf(k1th).all()
+    assert np.allclose(g, scipy.special.softmax(H, axis=1), rtol=1e-14)
+
+
+def test_gate_invariants_random():
+    cfg = _small(tokens=200, n_experts=16, top_k=4)
+    inp = make_inputs(cfg, seed=5)
+    g = oracle.gate(inp, cfg)
+    G = oracle.dense_gates(g["idx"], g["gates"], cfg.n_experts)
+    assert ((G > 0).sum(axis=1) == cfg.top_k).all()
+    assert np.allclose(G.sum(axis=1), 1.0, atol=1e-14)
+    assert (np.diff(g["idx"], axis=1) > 0).all()           # ascending, distinct
+    # every kept score beats every dropped score
+    H = g["H"]
+    for t in range(cfg.tokens):
+        kept = H[t, g["idx"][t]]
+        dropped = np.delete(H[t], g["idx"][t])
+        assert kept.min() >= dropped.max()
+
+
+def test_noise_draw_is_mostly_within_two():
+    """The lesson page says the noise draw mostly lands in [-2, 2]; for a
+    standard normal the share is erf(sqrt 2) ~ 95.45 %."""
+    inp = make_inputs(CONFIGS["tiny"].replace(tokens=4096), seed=0, with_experts=False)
+    e = inp["eps"].numpy().ravel()
+    share = np.mean(np.abs(e) <= 2.0)
+    assert abs(share - math.erf(math.sqrt(2.0))) < 0.005
+
+
+# -------------------------------------------------------------- routing ---
+
+def test_route_hand_example():
+    g = _load("route_hand.json")
+    counts, offsets, perm, inv = oracle.route(np.array(g["idx"], dtype=np.int32), g["n_experts"])
+    assert counts.tolist() == g["counts"]
+    assert offsets.tolist() == g["offsets"]
+    assert perm.tolist() == g["perm"]
+    assert inv.tolist() == g["inv"]
+
+
+def test_route_invariants_random():
+    rng = np.random.default_rng(11)
+    T, E, k = 300, 13, 3
+    idx = np.sort(np.array([rng.choice(E, k, replace=False) for _ in range(T)]), axis=1).astype(np.int32)
+    counts, offsets, perm, inv = oracle.route(idx, E)
+    assert counts.sum() == T * k
+    assert offsets[0] == 0 and offsets[-1] == T * k
+    assert sorted(perm.tolist()) == list(range(T * k))      # bijection
+    assert (perm[inv] == np.arange(T * k)).all()            # perm o inv = id
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert (idx.reshape(-1)[seg] == e).all()
+        assert (np.diff(seg // k) > 0).all()                 # tokens ascending
+        assert len(seg) == np.count_nonzero(idx == e)
+
+
+# -------------------------------------------------------- experts/combine --
+
+def test_single_expert_is_a_plain_relu_ffn():
+    """E = k = 1: the layer is one 2-layer ReLU FFN (torch CPU float64)."""
+    cfg = _small(n_experts=1, top_k=1)
+    inp = make_inputs(cfg, seed=2)
+    out = oracle.forward(inp, cfg)
+    x = inp["x"].double()
+    ref = torch.relu(x @ inp["w1"][0].double().T) @ inp["w2"][0].double().T
+    assert np.allclose(out["gates"], 1.0)
+    assert np.allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_swiglu_matches_torch():
+    cfg = _small(n_experts=1, top_k=1, ffn="swiglu", noisy=False)
+    inp = make_inputs(cfg, seed=4)
+    out = oracle.forward(inp, cfg)
+    x = inp["x"].double()
+    ref = (torch.nn.functional.silu(x @ inp["w1"][0].double().T) * (x @ inp["w3"][0].double().T)) \
+        @ inp["w2"][0].double().T
+    assert np.allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("ffn", ["relu", "swiglu"])
+def test_sparse_layer_equals_dense_brute_force(ffn):
+    """Sum over every expert of G_e * E_e(x) (no routing) equals the routed,
+    grouped and combined result."""
+    cfg = _small(tokens=48, n_experts=7, top_k=3, ffn=ffn)
+    inp = make_inputs(cfg, seed=7)
+    out = oracle.forward(inp, cfg)
+    dense = oracle.dense_forward(inp, cfg)
+    assert np.allclose(out["y"], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_dense_mixture_when_k_equals_E():
+    """k = E: the textbook dense softmax mixture of all experts."""
+    cfg = _small(tokens=32, n_experts=4, top_k=4)
+    inp = make_inputs(cfg, seed=9)
+    out = oracle.forward(inp, cfg)
+    _, _, H = oracle.noisy_logits(inp["x"], inp["w_gate"], inp["w_noise"], None, inp["eps"])
+    P = scipy.special.softmax(H, axis=1)
+    x = inp["x"].double()
+    ref = torch.zeros(cfg.tokens, cfg.d_model, dtype=torch.float64)
+    for e in range(4):
+        ref += torch.from_numpy(P[:, e:e + 1]) * (torch.relu(x @ inp["w1"][e].double().T) @ inp["w2"][e].double().T)
+    assert np.allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_combine_hand_example():
+    y_sorted = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 2.0], [4.0, -4.0]])
+    inv = np.array([3, 0, 1, 2])          # token0 slots -> rows 3,0; token1 -> 1,2
+    gates = np.array([[0.25, 0.75], [0.5, 0.5]])
+    y = oracle.combine(y_sorted, inv, gates)
+    assert y.tolist() == [[0.25 * 4 + 0.75 * 1, 0.25 * -4], [1.0, 1.5]]
+
+
+def test_expert_shape_matches_the_lesson_page():
+    """512 x 1024 + 1024 x 512 = 1,048,576 parameters per expert."""
+    cfg = CONFIGS["flat256"]
+    assert cfg.d_model * cfg.d_hidden + cfg.d_hidden * cfg.d_model == 1048576
+    small = cfg.replace(n_experts=2, tokens=4)
+    inp = make_inputs(small, seed=0)
+    assert inp["w1"][0].numel() + inp["w2"][0].numel() == 1048576
+
+
+# ------------------------------------------------------------- hierarchy ---
+
+def test_hierarchy_constructed_case():
+    """Primary scores make groups 1 and 3 win; inside group 1 experts 0 and 2
+    win, inside group 3 experts 1 and 3.  Final experts 1*4+0, 1*4+2, 3*4+1,
+    3*4+3 with gates = product of the two levels' softmaxes."""
+    G, Eg, d = 4, 4, 4
+    x = np.array([[1.0, 0.0, 0.0, 0.0]])
+    wgp = np.zeros((G, d)); wgp[:, 0] = [0.0, 2.0, -1.0, 1.5]
+    wg = np.zeros((G * Eg, d))
+    wg[4:8, 0] = [3.0, 0.0, 2.0, -1.0]
+    wg[12:16, 0] = [0.0, 1.0, -2.0, 0.7]
+    wg[0:4, 0] = [9.0, 9.0, 9.0, 9.0]   # unchosen group: must not leak in
+    h = oracle.hier_gate(x, wgp, None, None, wg, None, None, G, 2, 2)
+    assert h["idx"].tolist() == [[4, 6, 13, 15]]
+    gp = scipy.special.softmax([2.0, 1.5])
+    g1 = scipy.special.softmax([3.0, 2.0])
+    g3 = scipy.special.softmax([1.0, 0.7])
+    exp = [gp[0] * g1[0], gp[0] * g1[1], gp[1] * g3[0], gp[1] * g3[1]]
+    assert np.allclose(h["gates"][0], exp, rtol=1e-14)
+
+
+def test_hierarchy_invariants_random():
+    cfg = _small(tokens=64, n_experts=24, n_groups=4, k_groups=2, k_per_group=2,
+                 top_k=4, gate_std=0.5)
+    inp = make_inputs(cfg, seed=13)
+    h = oracle.gate(inp, cfg)
+    Eg = cfg.experts_per_group
+    for t in range(cfg.tokens):
+        ids = h["idx"][t]
+        assert len(set(ids.tolist())) == 4
+        groups = ids // Eg
+        assert groups[0] == groups[1] and groups[2] == groups[3] and groups[0] < groups[2]
+    assert np.allclose(h["gates"].sum(axis=1), 1.0, atol=1e-14)
+
+
+def test_hierarchy_with_one_group_is_flat():
+    cfg = _small(tokens=50, n_experts=8, top_k=2, gate_std=0.5)
+    inp = make_inputs(cfg, seed=17)
+    flat = oracle.flat_gate(inp["x"], inp["w_gate"], inp["w_noise"], None, inp["eps"], 2)
+    x = inp["x"]
+    T = cfg.tokens
+    h = oracle.hier_gate(x, np.zeros((1, cfg.d_model)), np.zeros((1, cfg.d_model)),
+                         np.zeros((T, 1)), inp["w_gate"], inp["w_noise"],
+                         inp["eps"].reshape(T, 1, 8), 1, 1, 2)
+    assert (h["idx"] == flat["idx"]).all()
+    assert np.allclose(h["gates"], flat["gates"], rtol=1e-15)
+
+
+# ------------------------------------------------------------- balance ----
+
+def test_cv_squared_closed_forms():
+    assert oracle.cv_squared(np.full(10, 3.7)) < 1e-30
+    assert oracle.cv_squared(np.full(8, 2.0)) == 0.0
+    n = 12
+    one_hot = np.zeros(n); one_hot[5] = 2.5
+    assert oracle.cv_squared(one_hot) == pytest.approx(n - 1, rel=1e-14)
+    assert oracle.cv_squared([1.0, 3.0]) == pytest.approx(0.25, rel=1e-15)
+    assert oracle.cv_squared(np.zeros(4)) == 0.0
+
+
+def test_importance_sums_to_token_count():
+    cfg = _small(tokens=120, n_experts=10, top_k=3)
+    inp = make_inputs(cfg, seed=21)
+    out = oracle.forward(inp, cfg, with_experts=False)
+    assert out["importance"].sum() == pytest.approx(cfg.tokens, rel=1e-13)
+    assert out["counts"].sum() == cfg.tokens * cfg.top_k
+
+
+def test_load_two_experts_top1_closed_form():
+    """E = 2, k = 1: expert 0 stays kept after redrawing its noise iff
+    clean0 + eps' sp0 > H1, probability Phi((clean0 - H1) / sp0)."""
+    clean = np.array([[0.3, -0.1]])
+    sp = np.array([[0.8, 0.5]])
+    eps = np.array([[0.2, 1.1]])
+    H = clean + eps * sp
+    idx, kth, k1th, _ = oracle.keep_top_k(H, 1)
+    load = oracle.load_estimate(clean, sp, H, idx, kth, k1th)
+    p0 = 0.5 * math.erfc(-((0.3 - H[0, 1]) / 0.8) / math.sqrt(2))
+    p1 = 0.5 * math.erfc(-((-0.1 - H[0, 0]) / 0.5) / math.sqrt(2))
+    assert load[0] == pytest.approx(p0, rel=1e-14)
+    assert load[1] == pytest.approx(p1, rel=1e-14)
+
+
+def test_load_estimate_monte_carlo():
+    """For fixed x and every other expert's noise, redraw expert e's noise many
+    times: the share of draws that keep e in the top-k matches the oracle's
+    per-token load term within Monte Carlo error."""
+    cfg = _small(tokens=6, n_experts=8, top_k=3, gate_std=0.4)
+    inp = make_inputs(cfg, seed=23)
+    g = oracle.gate(inp, cfg)
+    clean, sp, H = g["clean"], g["sp"], g["H"]
+    rng = np.random.default_rng(0)
+    n = 200000
+    kept = np.zeros(H.shape, dtype=bool)
+    for s in range(cfg.top_k):
+        kept[np.arange(cfg.tokens), g["idx"][:, s]] = True
+    theta = np.where(kept, g["k1th"][:, None], g["kth"][:, None])
+    P = oracle.normal_cdf((clean - theta) / sp)
+    for t in range(cfg.tokens):
+        for e in range(cfg.n_experts):
+            draws = clean[t, e] + rng.standard_normal(n) * sp[t, e]
+            others = np.delete(H[t], e)
+            # e stays in the top-k iff fewer than k others beat it
+            beat = (others[None, :] > draws[:, None]).sum(axis=1)
+            frac = np.mean(beat < cfg.top_k)
+            sd = math.sqrt(max(P[t, e] * (1 - P[t, e]), 1e-12) / n)
+            assert abs(frac - P[t, e]) < 5 * sd + 1e-5
+    load = oracle.load_estimate(clean, sp, H, g["idx"], g["kth"], g["k1th"])
+    assert np.allclose(load, P.sum(axis=0), rtol=1e-14)
+
+
+def test_balance_loss_weights():
+    cfg = _small(tokens=80, n_experts=6, top_k=2)
+    inp = make_inputs(cfg, seed=29)
+    a = oracle.forward(inp, cfg, w_importance=0.1, w_load=0.0, with_experts=False)
+    b = oracle.forward(inp, cfg, w_importance=0.0, w_load=0.2, with_experts=False)
+    assert a["loss"] == pytest.approx(0.1 * a["cv2_importance"], rel=1e-15)
+    assert b["loss"] == pytest.approx(0.2 * b["cv2_load"], rel=1e-15)
+    assert a["cv2_load"] > 0 and a["cv2_importance"] > 0
+
+
+def test_noise_free_load_is_the_row_count():
+    cfg = _small(tokens=80, n_experts=6, top_k=2, noisy=False)
+    inp = make_inputs(cfg, seed=31)
+    out = oracle.forward(inp, cfg, with_experts=False)
+    assert out["load"].tolist() == out["counts"].astype(float).tolist()
+
+
+def test_empty_batch():
+    cfg = _small(tokens=0)
+    inp = make_inputs(cfg, seed=0)
+    out = oracle.forward(inp, cfg)
+    assert out["idx"].shape == (0, cfg.top_k)
+    assert out["counts"].sum() == 0 and out["y"].shape == (0, cfg.d_model)
+    assert out["cv2_importance"] == 0.0
