@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward on one MI355X; prints ONE JSON line.
+
+A step is one call of moe_forward (gate -> route -> experts -> combine ->
+balance statistics) over one batch of synthetic inputs already resident in
+HBM.  Default workload: 8192 tokens, d_model 512, 256 ReLU experts
+512 -> 1024 -> 512, noisy top-4 gating (bf16, fp32 accumulation).
+
+Besides the timed steps, the same stages are replayed through their own entry
+points with HIP events between them (same stream, same kernels) to give the
+per-stage times and the roofline of the dominant stage.  The CPU oracle is
+timed on a bounded token sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + expert TFLOPS (% MFMA peak), d512/h1024, 256 experts, k=4"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def describe(cfg):
+    kind = "SwiGLU" if cfg.ffn == "swiglu" else "ReLU"
+    gate = ("hierarchical %d groups x %d, top-%d groups then top-%d" %
+            (cfg.n_groups, cfg.experts_per_group, cfg.k_groups, cfg.k_per_group)
+            if cfg.hierarchical else "top-%d" % cfg.top_k)
+    return ("%s: %d tokens, d_model %d, %d experts %s %d->%d->%d, %s %s gating, %s" %
+            (cfg.name, cfg.tokens, cfg.d_model, cfg.n_experts, kind, cfg.d_model, cfg.d_hidden,
+             cfg.d_model, "noisy" if cfg.noisy else "noise-free", gate, cfg.dtype))
+
+
+class Stages:
+    """gate / route / experts / combine / balance through their own entry
+    points, with argument blocks built once."""
+
+    def __init__(self, L, cfg, inp):
+        import torch
+        self.L, self.cfg = L, cfg
+        T = cfg.tokens
+        dev = inp["x"].device
+        self.ws = L.workspace(cfg, T, dev)
+        A = T * cfg.top_k
+        E = cfg.n_experts
+        act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+        self.gate = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+        self.thr = None if cfg.hierarchical else torch.empty((T, 2), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.perm = torch.empty(A, dtype=torch.int32, device=dev)
+        self.inv = torch.empty(A, dtype=torch.int32, device=dev)
+        self.ys = torch.empty((A, cfg.d_model), dtype=act, device=dev)
+        self.y = torch.empty((T, cfg.d_model), dtype=act, device=dev)
+        self.imp = torch.empty(E, dtype=torch.float32, device=dev)
+        self.load = torch.empty(E, dtype=torch.float32, device=dev)
+        self.out = torch.empty(3, dtype=torch.float32, device=dev)
+        self.c = L.make_config(cfg, T)
+        self.p = L.make_params(inp)
+        self.n = L.make_noise(inp)
+        self.x = inp["x"]
+        self.lib = L.load()
+        P = L._ptr
+        self.args = dict(
+            gate=(ctypes.byref(self.c), P(self.x), ctypes.byref(self.p), ctypes.byref(self.n),
+                  P(self.idx), P(self.gate), P(self.thr), self.ws.ptr, self.ws.nbytes),
+            route=(ctypes.byref(self.c), P(self.idx), P(self.counts), P(self.offsets),
+                   P(self.perm), P(self.inv), None, None, self.ws.ptr, self.ws.nbytes),
+            experts=(ctypes.byref(self.c), P(self.x), P(self.perm), P(self.offsets),
+                     ctypes.byref(self.p), P(self.ys), self.ws.ptr, self.ws.nbytes),
+            combine=(ctypes.byref(self.c), P(self.ys), P(self.inv), P(self.gate), P(self.y)),
+            balance=(ctypes.byref(self.c), P(self.x), ctypes.byref(self.p), P(self.idx),
+                     P(self.gate), P(self.thr), P(self.perm), P(self.offsets), 1.0, 1.0,
+                     P(self.imp), P(self.load), P(self.out), self.ws.ptr, self.ws.nbytes))
+        self.fns = dict(gate=self.lib.moe_gate, route=self.lib.moe_route,
+                        experts=self.lib.moe_expert_ffn, combine=self.lib.moe_combine,
+                        balance=self.lib.moe_balance_loss)
+        self.names = ["gate", "route", "experts", "combine", "balance"]
+
+    def call(self, name, stream):
+        st = self.fns[name](*self.args[name], stream)
+        if st != 0:
+            raise RuntimeError(f"{name}: {self.lib.moe_last_error().decode()}")
+
+
+def stage_times(st, steps):
+    import torch
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    n = len(st.names)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    for name in st.names:  # warm
+        st.call(name, s)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        for j, name in enumerate(st.names):
+            st.call(name, s)
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
+            for j, name in enumerate(st.names)}
+
+
+def expert_work(cfg, counts):
+    """Algorithmic flops and HBM bytes of the expert stage: the weights of
+    every expert that receives a row (read once), the routed activation rows
+    read, the expert outputs written."""
+    import numpy as np
+    A = cfg.tokens * cfg.top_k
+    el = 2 if cfg.dtype == "bf16" else 4
+    mats = 3 if cfg.ffn == "swiglu" else 2
+    hit = int((np.asarray(counts) > 0).sum())
+    flops = 2.0 * A * mats * cfg.d_model * cfg.d_hidden
+    wbytes = hit * mats * cfg.d_model * cfg.d_hidden * el
+    abytes = 2 * A * cfg.d_model * el
+    return flops, wbytes + abytes, hit
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    """The oracle, as it is, on the first S tokens of the same inputs."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cpu = {k: (v.detach().cpu() if v is not None else None) for k, v in inp.items()}
+    w = {k: (oracle.moe_oracle._f64(cpu[k]) if cpu.get(k) is not None else None)
+         for k in ("w1", "w2", "w3")}
+    S = min(cfg.tokens, 512)
+    while True:
+        sample = dict(cpu)
+        for k in ("x", "eps", "eps_p"):
+            if sample.get(k) is not None:
+                sample[k] = sample[k][:S]
+        sample.update(w)
+        c = cfg.replace(tokens=S)
+        t0 = time.perf_counter()
+        oracle.forward(sample, c)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or S >= cfg.tokens:
+            break
+        S = min(cfg.tokens, S * 2)
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.tokens} tokens, whole layer incl. balance stats, "
+                      f"fp64 numpy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="flat256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-stages", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every expert of this layer sits on one MI355X and "
+              f"there is no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparsely_gated_mixture_noisy_amd import _lib as L
+    from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    print(f"[bench] {describe(cfg)}", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    fwd = L.Forward(cfg, inp["x"], inp, inp, balance=True)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        fwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] moe_forward {ms:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})",
+          file=sys.stderr, flush=True)
+    counts = fwd.out.counts.cpu().numpy()
+
+    res = {
+        "metric": METRIC,
+        "value": cfg.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) activations and noise, N(0,0.02^2) gate tables, "
+                "N(0,1/fan_in) experts)",
+        "config": {"workload": describe(cfg), "tokens": cfg.tokens, "d_model": cfg.d_model,
+                   "n_experts": cfg.n_experts, "d_hidden": cfg.d_hidden, "top_k": cfg.top_k,
+                   "ffn": cfg.ffn, "noisy": cfg.noisy},
+    }
+    flops, ebytes, hit = expert_work(cfg, counts)
+    if not args.no_stages:
+        st = Stages(L, cfg, inp)
+        stages = stage_times(st, args.steps)
+        print(f"[bench] stages ms: {json.dumps({k: round(v, 4) for k, v in stages.items()})}",
+              file=sys.stderr, flush=True)
+        t_exp = stages["experts"] * 1e-3
+        achieved = ebytes / t_exp / 1e9
+        peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+        tflops = flops / t_exp / 1e12
+        res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "kernel": "expert FFN stage (moe_expert_ffn)",
+                           "bytes_per_launch": ebytes}
+        res["stages_ms"] = stages
+        res["expert_tflops"] = tflops
+        res["expert_mfma_frac"] = tflops / peak_tf
+        res["experts_hit"] = hit
+    res["counts_max_over_mean"] = float(counts.max() / max(counts.mean(), 1e-9))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * moe.h -- C ABI of libmoe, the forward pass of the sparsely-gated noisy
+ * top-k Mixture-of-Experts layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages on Shazeer et al. 2017 describe it:
+ *   - "MoE:稀疏门控混合专家" (nengyongai.cn), section 二: one MoE layer is
+ *     y = sum_i G(x)_i E_i(x) over n experts; an expert is a one-hidden-layer
+ *     FFN (512 -> 1024 -> 512); experts with gate 0 are not evaluated.
+ *   - same page, section 三: scores x W_g (one table column per expert),
+ *     KeepTopK sets all but the k best scores to -inf, softmax turns the kept
+ *     scores into weights summing to 1; with thousands of experts the gate
+ *     picks groups first, then experts inside the chosen groups ("-h").
+ *   - same page, section 四: noisy scores
+ *     H(x)_i = (x W_g)_i + eps * softplus((x W_noise)_i), eps redrawn per call.
+ *   - "Outrageously Large Neural Networks ... 中文验证版" (ai-papers.xuzou.cn),
+ *     section 瓶颈: each expert receives about k*b/n rows (the sub-batch that
+ *     routing builds); section 方法适配: importance and load losses.
+ *   - "MoE 混合专家：参数大、计算省" (transformer.xph.ink), section 核心概念:
+ *     the Mixtral-style top-2 layer whose SwiGLU expert variant is provided.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a DEVICE pointer to caller-owned memory (or NULL where
+ *     a parameter says "nullable").  The library never allocates, frees,
+ *     copies to the host or synchronizes; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and results are valid once
+ *     the stream has reached that point.
+ *   - Scratch memory is the caller's workspace `ws` of `ws_bytes` bytes,
+ *     256-byte aligned, at least moe_workspace_size(cfg) bytes.  Its contents
+ *     need no initialization and are clobbered.
+ *   - Arguments are validated before anything is enqueued.  On error the
+ *     call returns a negative moe_status, writes no output and enqueues
+ *     nothing; moe_last_error() describes the problem (thread-local).
+ *   - Results are deterministic: repeated calls with the same inputs give
+ *     bitwise identical outputs (no floating-point atomics).
+ *   - Layouts are row-major.  T = tokens, d = d_model, E = n_experts,
+ *     h = d_hidden, k = top_k, A = T*k assignments (a = t*k + s for slot s of
+ *     token t), G = n_groups, Eg = E/G.
+ *   - Element type of x, gate tables and expert tables is cfg->dtype
+ *     (MOE_F32 or MOE_BF16).  Gates, scores, noise and bias are float32.
+ *
+ * Limits: 1 <= k <= 8, k <= E; bf16 needs d % 64 == 0 and h % 64 == 0;
+ * tokens < 2^31 / 8.  Anything else returns MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, negative size, k > E, ... */
+  MOE_ERR_UNSUPPORTED = -2, /* valid layer the library does not implement */
+  MOE_ERR_WORKSPACE = -3,   /* ws too small or misaligned */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum moe_ffn {
+  MOE_FFN_RELU = 0,  /* E(x) = max(x W1, 0) W2                 */
+  MOE_FFN_SWIGLU = 1 /* E(x) = (silu(x W1) * (x W3)) W2        */
+} moe_ffn;
+
+typedef struct moe_config {
+  int64_t tokens;      /* T >= 0 */
+  int32_t d_model;     /* d */
+  int32_t n_experts;   /* E */
+  int32_t d_hidden;    /* h */
+  int32_t top_k;       /* k; for the hierarchy k = k_groups * k_per_group */
+  int32_t n_groups;    /* 0 = flat gate; else G groups of E/G experts */
+  int32_t k_groups;    /* groups kept per token (hierarchy only) */
+  int32_t k_per_group; /* experts kept inside each kept group */
+  int32_t noisy;       /* 1 = noisy gating (noise tables and eps given) */
+  int32_t ffn;         /* moe_ffn */
+  int32_t dtype;       /* moe_dtype */
+} moe_config;
+
+/* Gate and expert parameters.  Tables hold one ROW per output unit (the
+ * pages' d x n gate table is stored transposed, [E][d]).
+ *   w_gate    [E][d]    clean score table W_g
+ *   w_noise   [E][d]    noise scale table W_noise (NULL unless noisy)
+ *   bias      [E] f32   per-expert score bias added to x W_g (nullable)
+ *   w_gate_p  [G][d]    primary (group) score table (hierarchy only)
+ *   w_noise_p [G][d]    primary noise table (hierarchy and noisy only)
+ *   w1        [E][h][d] first expert layer (ReLU: in; SwiGLU: gate)
+ *   w3        [E][h][d] SwiGLU up projection (NULL for ReLU)
+ *   w2        [E][d][h] second expert layer (out / down)
+ * For the hierarchy, rows g*Eg .. g*Eg+Eg-1 of w_gate / w_noise are the
+ * secondary tables of group g. */
+typedef struct moe_params {
+  const void* w_gate;
+  const void* w_noise;
+  const float* bias;
+  const void* w_gate_p;
+  const void* w_noise_p;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+} moe_params;
+
+/* Noise draws, float32 ~ N(0,1), supplied by the caller (NULL = no noise).
+ *   eps    flat: [T][E];  hierarchy: [T][G][Eg], only the slices of the
+ *          groups a token keeps are read
+ *   eps_p  hierarchy: [T][G] primary noise */
+typedef struct moe_noise {
+  const float* eps;
+  const float* eps_p;
+} moe_noise;
+
+/* Bytes of workspace needed by any entry point for this configuration. */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* Gate: noisy scores, KeepTopK and softmax over the kept scores
+ * (nengyongai.cn lesson, sections 三 and 四).
+ *   x         [T][d]
+ *   topk_idx  [T][k] int32 out: kept experts, ascending expert index
+ *   topk_gate [T][k] f32 out: their gates (softmax over the kept scores)
+ *   thr       [T][2] f32 out, nullable, flat gate only: the k-th and
+ *             (k+1)-th largest noisy score (-inf when k == E)
+ * Ties between equal scores go to the lower expert index.  The hierarchy
+ * keeps k_groups groups by the primary scores, then k_per_group experts in
+ * each kept group; a gate is the product of the primary and secondary
+ * softmax weights. */
+moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
+                    const moe_noise* noise, int32_t* topk_idx, float* topk_gate,
+                    float* thr, void* ws, size_t ws_bytes, void* stream);
+
+/* Route: group the A assignments by expert (the per-expert sub-batch of the
+ * paper card, section 瓶颈).
+ *   topk_idx  [T][k] int32 in
+ *   counts    [E] int32 out: rows per expert
+ *   offsets   [E+1] int32 out: exclusive prefix sum of counts
+ *   perm      [A] int32 out: perm[p] = assignment placed at position p;
+ *             positions are expert-contiguous, tokens ascending inside each
+ *             expert (stable)
+ *   inv       [A] int32 out: inv[a] = position of assignment a
+ *   x, x_sorted  nullable pair: when both are given, x_sorted[p] = x[perm[p]/k]
+ * Out-of-range expert ids in topk_idx are undefined behaviour. */
+moe_status moe_route(const moe_config* cfg, const int32_t* topk_idx,
+                     int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* inv, const void* x, void* x_sorted, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Expert FFNs over the routed rows (lesson page, section 二): for every
+ * position p of expert e, y_sorted[p] = E_e(row p), where row p is
+ * x[perm[p]/k] when perm is given, else x[p] (x is then the x_sorted of
+ * moe_route, [A][d]).  Experts with no rows cost nothing.
+ *   offsets   [E+1] int32 from moe_route
+ *   y_sorted  [A][d] out (cfg dtype)
+ * bf16: products exact in fp32, fp32 accumulation, hidden activations
+ * rounded to bf16 before the second layer, outputs rounded to bf16. */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x,
+                          const int32_t* perm, const int32_t* offsets,
+                          const moe_params* p, void* y_sorted, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Combine: y[t] = sum over slots s (ascending) of
+ * topk_gate[t][s] * y_sorted[inv[t*k+s]], accumulated in fp32
+ * (lesson page, section 二).  y [T][d] out (cfg dtype). */
+moe_status moe_combine(const moe_config* cfg, const void* y_sorted,
+                       const int32_t* inv, const float* topk_gate, void* y,
+                       void* stream);
+
+/* Balance statistics (reading note page, sections 核心想法 / 方法怎么做;
+ * paper card, section 方法适配):
+ *   importance[e] = sum_t G(x_t)_e
+ *   load[e]       = flat noisy gate: sum_t Phi((clean[t,e] - theta[t,e]) /
+ *                   softplus(x_t W_noise)_e), clean = x W_g + bias, theta =
+ *                   thr[t][1] if e is kept by token t else thr[t][0];
+ *                   otherwise (no noise, or hierarchy): counts[e]
+ *   out[0] = CV^2(importance), out[1] = CV^2(load),
+ *   out[2] = w_importance * out[0] + w_load * out[1]
+ * CV^2 = population variance / mean^2 (0 when the mean is 0).
+ * Inputs: x, p (w_gate, w_noise, bias) and thr are used only for the smooth
+ * load; perm/offsets from moe_route; topk_idx/topk_gate/thr from moe_gate.
+ * importance, load [E] f32 out; out [3] f32 out. */
+moe_status moe_balance_loss(const moe_config* cfg, const void* x,
+                            const moe_params* p, const int32_t* topk_idx,
+                            const float* topk_gate, const float* thr,
+                            const int32_t* perm, const int32_t* offsets,
+                            float w_importance, float w_load, float* importance,
+                            float* load, float* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Outputs of moe_forward.  y is required; the rest are nullable (the
+ * library then keeps them in the workspace). */
+typedef struct moe_outputs {
+  void* y;            /* [T][d] */
+  int32_t* topk_idx;  /* [T][k] */
+  float* topk_gate;   /* [T][k] */
+  int32_t* counts;    /* [E] */
+  float* importance;  /* [E]; balance statistics are computed only when */
+  float* load;        /* [E]; `balance` is non-NULL */
+  float* balance;     /* [3]: cv2 importance, cv2 load, weighted loss */
+} moe_outputs;
+
+/* The whole layer: gate -> route -> experts -> combine (-> balance). */
+moe_status moe_forward(const moe_config* cfg, const void* x,
+                       const moe_params* p, const moe_noise* noise,
+                       float w_importance, float w_load, moe_outputs* out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* Detail of the last error returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,460 @@
+// C ABI of libmoe: argument validation, workspace layout and launch order.
+// Nothing here computes; every step of the layer runs in the kernels of
+// gate.hip, route.hip, expert.hip and combine.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+constexpr int MAX_K = 8;
+constexpr int MAX_EXPERTS = 8192;  // route kernels keep 8 bytes per expert in LDS
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+// Every workspace region, at fixed offsets for a given configuration.
+struct Layout {
+  size_t idx, gate, thr, counts, offsets, perm, inv, blk, ticket, tiles, hid, ysorted, part, imp,
+      load;
+  size_t idx_p, gate_p, counts_g, offsets_g, perm_g, inv_g, blk_g, tiles_g;
+  size_t total;
+  int nb, load_blocks, load_tiles;
+};
+
+Layout layout(const moe_config* c) {
+  Layout L;
+  const int64_t T = c->tokens, A = T * c->top_k;
+  const int E = c->n_experts;
+  L.nb = (int)((T + ROUTE_BLOCK_TOKENS - 1) / ROUTE_BLOCK_TOKENS);
+  L.load_blocks = load_partial_blocks(T, &L.load_tiles);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.idx = take(4 * (size_t)A);
+  L.gate = take(4 * (size_t)A);
+  L.thr = take(8 * (size_t)T);
+  L.counts = take(4 * (size_t)E);
+  L.offsets = take(4 * (size_t)(E + 1));
+  L.perm = take(4 * (size_t)A);
+  L.inv = take(4 * (size_t)A);
+  L.blk = take(4 * (size_t)L.nb * E);
+  L.ticket = take(4);
+  L.tiles = take(4 * (size_t)(E + 1));
+  L.hid = take(elem_size(c) * (size_t)A * c->d_hidden);
+  L.ysorted = take(elem_size(c) * (size_t)A * c->d_model);
+  L.part = take(4 * (size_t)L.load_blocks * E);
+  L.imp = take(4 * (size_t)E);
+  L.load = take(4 * (size_t)E);
+  const int G = c->n_groups > 0 ? c->n_groups : 0;
+  const int64_t Ag = T * (G ? c->k_groups : 0);
+  L.idx_p = take(4 * (size_t)Ag);
+  L.gate_p = take(4 * (size_t)Ag);
+  L.counts_g = take(4 * (size_t)G);
+  L.offsets_g = take(4 * (size_t)(G + 1));
+  L.perm_g = take(4 * (size_t)Ag);
+  L.inv_g = take(4 * (size_t)Ag);
+  L.blk_g = take(4 * (size_t)L.nb * G);
+  L.tiles_g = take(4 * (size_t)(G + 1));
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->tokens < 0) return fail(MOE_ERR_INVALID_ARG, "tokens < 0");
+  if (c->d_model < 1 || c->d_hidden < 1 || c->n_experts < 1)
+    return fail(MOE_ERR_INVALID_ARG, "d_model, d_hidden and n_experts must be >= 1");
+  if (c->top_k < 1 || c->top_k > c->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, n_experts]");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (c->ffn != MOE_FFN_RELU && c->ffn != MOE_FFN_SWIGLU)
+    return fail(MOE_ERR_INVALID_ARG, "unknown ffn %d", c->ffn);
+  if (c->noisy != 0 && c->noisy != 1) return fail(MOE_ERR_INVALID_ARG, "noisy must be 0 or 1");
+  if (c->n_groups < 0) return fail(MOE_ERR_INVALID_ARG, "n_groups < 0");
+  if (c->n_groups > 0) {
+    const int G = c->n_groups;
+    if (c->n_experts % G != 0)
+      return fail(MOE_ERR_INVALID_ARG, "n_experts %% n_groups != 0");
+    if (c->k_groups < 1 || c->k_groups > G)
+      return fail(MOE_ERR_INVALID_ARG, "k_groups must be in [1, n_groups]");
+    if (c->k_per_group < 1 || c->k_per_group > c->n_experts / G)
+      return fail(MOE_ERR_INVALID_ARG, "k_per_group must be in [1, n_experts / n_groups]");
+    if (c->top_k != c->k_groups * c->k_per_group)
+      return fail(MOE_ERR_INVALID_ARG, "top_k != k_groups * k_per_group");
+  }
+  if (c->top_k > MAX_K) return fail(MOE_ERR_UNSUPPORTED, "top_k > %d", MAX_K);
+  if (c->n_experts > MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MAX_EXPERTS);
+  if (c->tokens * (int64_t)c->top_k > (int64_t)INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k exceeds int32 positions");
+  if (c->dtype == MOE_BF16 && (c->d_model % 64 != 0 || c->d_hidden % 64 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d_model and d_hidden multiples of 64");
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
+  const size_t need = layout(c).total;
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  return MOE_OK;
+}
+
+moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_params* p,
+                             const moe_noise* n) {
+  if (!x && c->tokens > 0) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "params is NULL");
+  if (!p->w_gate) return fail(MOE_ERR_INVALID_ARG, "w_gate is NULL");
+  // an empty batch reads no activations and no noise
+  const bool rows = c->tokens > 0;
+  if (c->noisy) {
+    if (rows && (!n || !n->eps)) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps");
+    if (!p->w_noise) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs w_noise");
+  }
+  if (c->n_groups > 0) {
+    if (!p->w_gate_p) return fail(MOE_ERR_INVALID_ARG, "hierarchy needs w_gate_p");
+    if (p->bias) return fail(MOE_ERR_UNSUPPORTED, "bias is supported by the flat gate only");
+    if (c->noisy && ((rows && !n->eps_p) || !p->w_noise_p))
+      return fail(MOE_ERR_INVALID_ARG, "noisy hierarchy needs eps_p and w_noise_p");
+  }
+  return MOE_OK;
+}
+
+moe_status check_expert_inputs(const moe_config* c, const moe_params* p) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "params is NULL");
+  if (!p->w1 || !p->w2) return fail(MOE_ERR_INVALID_ARG, "w1 / w2 is NULL");
+  if (c->ffn == MOE_FFN_SWIGLU && !p->w3) return fail(MOE_ERR_INVALID_ARG, "SwiGLU needs w3");
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)              \
+  do {                             \
+    moe_status _st = (expr);       \
+    if (_st != MOE_OK) return _st; \
+  } while (0)
+
+// ---- enqueue helpers (arguments already validated) -------------------------
+
+moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const moe_params* p,
+                   const moe_noise* n, int32_t* idx, float* gate, float* thr, void* ws,
+                   hipStream_t s) {
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool noisy = c->noisy != 0;
+  if (c->n_groups == 0) {
+    GateFlatArgs a;
+    a.x = x;
+    a.w_gate = p->w_gate;
+    a.w_noise = noisy ? p->w_noise : nullptr;
+    a.bias = p->bias;
+    a.eps = noisy ? n->eps : nullptr;
+    a.T = c->tokens;
+    a.d = c->d_model;
+    a.E = c->n_experts;
+    a.k = c->top_k;
+    a.idx = idx;
+    a.gate = gate;
+    a.thr = thr;
+    return hip_status(launch_gate_flat(a, bf16, s), "gate");
+  }
+  const int G = c->n_groups, kg = c->k_groups;
+  int32_t* idx_p = at<int32_t>(ws, L.idx_p);
+  float* gate_p = at<float>(ws, L.gate_p);
+  GateFlatArgs a;
+  a.x = x;
+  a.w_gate = p->w_gate_p;
+  a.w_noise = noisy ? p->w_noise_p : nullptr;
+  a.bias = nullptr;
+  a.eps = noisy ? n->eps_p : nullptr;
+  a.T = c->tokens;
+  a.d = c->d_model;
+  a.E = G;
+  a.k = kg;
+  a.idx = idx_p;
+  a.gate = gate_p;
+  a.thr = nullptr;
+  MOE_TRY(hip_status(launch_gate_flat(a, bf16, s), "primary gate"));
+  if (c->tokens == 0) return MOE_OK;
+  RouteArgs r;
+  r.idx = idx_p;
+  r.T = c->tokens;
+  r.k = kg;
+  r.E = G;
+  r.NB = L.nb;
+  r.blk = at<int32_t>(ws, L.blk_g);
+  r.ticket = at<int32_t>(ws, L.ticket);
+  r.counts = at<int32_t>(ws, L.counts_g);
+  r.offsets = at<int32_t>(ws, L.offsets_g);
+  r.perm = at<int32_t>(ws, L.perm_g);
+  r.inv = at<int32_t>(ws, L.inv_g);
+  MOE_TRY(hip_status(launch_route(r, s), "group routing"));
+  int32_t* tiles_g = at<int32_t>(ws, L.tiles_g);
+  MOE_TRY(hip_status(launch_tile_map(r.offsets, G, 32, tiles_g, s), "group tiles"));
+  GateGroupArgs ga;
+  ga.x = x;
+  ga.w_gate = p->w_gate;
+  ga.w_noise = noisy ? p->w_noise : nullptr;
+  ga.eps = noisy ? n->eps : nullptr;
+  ga.d = c->d_model;
+  ga.G = G;
+  ga.Eg = c->n_experts / G;
+  ga.kg = kg;
+  ga.kpg = c->k_per_group;
+  ga.perm_g = r.perm;
+  ga.offsets_g = r.offsets;
+  ga.tiles_g = tiles_g;
+  ga.gate_p = gate_p;
+  ga.idx = idx;
+  ga.gate = gate;
+  const int64_t grid = (c->tokens * kg + 31) / 32 + G;
+  return hip_status(launch_gate_group(ga, (int)grid, bf16, s), "secondary gate");
+}
+
+moe_status do_route(const moe_config* c, const Layout& L, const int32_t* idx, int32_t* counts,
+                    int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, hipStream_t s) {
+  RouteArgs r;
+  r.idx = idx;
+  r.T = c->tokens;
+  r.k = c->top_k;
+  r.E = c->n_experts;
+  r.NB = L.nb;
+  r.blk = at<int32_t>(ws, L.blk);
+  r.ticket = at<int32_t>(ws, L.ticket);
+  r.counts = counts;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.inv = inv;
+  return hip_status(launch_route(r, s), "route");
+}
+
+moe_status do_ffn(const moe_config* c, const Layout& L, const void* x, const int32_t* perm,
+                  const int32_t* offsets, const moe_params* p, void* y_sorted, void* ws,
+                  hipStream_t s) {
+  const bool bf16 = c->dtype == MOE_BF16;
+  const int sw = c->ffn == MOE_FFN_SWIGLU;
+  FfnArgs f;
+  f.x = x;
+  f.perm = perm;
+  f.k = c->top_k;
+  f.offsets = offsets;
+  int32_t* tiles = at<int32_t>(ws, L.tiles);
+  f.tiles = tiles;
+  f.E = c->n_experts;
+  f.d = c->d_model;
+  f.h = c->d_hidden;
+  f.w1 = p->w1;
+  f.w3 = sw ? p->w3 : nullptr;
+  f.w2 = p->w2;
+  f.hid = at<void>(ws, L.hid);
+  f.y_sorted = y_sorted;
+  f.A = c->tokens * c->top_k;
+  if (f.A == 0) return MOE_OK;
+  if (bf16)
+    MOE_TRY(hip_status(launch_tile_map(offsets, c->n_experts,
+                                       ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw), tiles, s),
+                       "expert tiles"));
+  return hip_status(launch_expert_ffn(f, bf16, sw, s), "experts");
+}
+
+moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const moe_params* p,
+                      const int32_t* idx, const float* gate, const float* thr,
+                      const int32_t* perm, const int32_t* offsets, float wi, float wl,
+                      float* importance, float* load, float* out, void* ws, hipStream_t s) {
+  const int E = c->n_experts;
+  MOE_TRY(hip_status(launch_importance(perm, offsets, gate, E, importance, s), "importance"));
+  const bool smooth = c->n_groups == 0 && c->noisy && c->tokens > 0;
+  float* part = nullptr;
+  if (smooth) {
+    part = at<float>(ws, L.part);
+    LoadArgs la;
+    la.x = x;
+    la.w_gate = p->w_gate;
+    la.w_noise = p->w_noise;
+    la.bias = p->bias;
+    la.idx = idx;
+    la.thr = thr;
+    la.T = c->tokens;
+    la.d = c->d_model;
+    la.E = E;
+    la.k = c->top_k;
+    la.tiles = L.load_tiles;
+    la.part = part;
+    MOE_TRY(hip_status(launch_load_partial(la, L.load_blocks, c->dtype == MOE_BF16, s), "load"));
+  }
+  MOE_TRY(hip_status(launch_load_reduce(part, L.load_blocks, offsets, E, load, s), "load reduce"));
+  return hip_status(launch_cv2(importance, load, E, wi, wl, out, s), "cv2");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return layout(cfg).total;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
+                    const moe_noise* noise, int32_t* topk_idx, float* topk_gate, float* thr,
+                    void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg));
+  MOE_TRY(check_gate_inputs(cfg, x, p, noise));
+  if (cfg->tokens > 0 && (!topk_idx || !topk_gate))
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_gate is NULL");
+  if (thr && cfg->n_groups > 0) return fail(MOE_ERR_INVALID_ARG, "thr is for the flat gate only");
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  MOE_TRY(do_gate(cfg, layout(cfg), x, p, noise, topk_idx, topk_gate, thr, ws,
+                  (hipStream_t)stream));
+  return ok();
+}
+
+moe_status moe_route(const moe_config* cfg, const int32_t* topk_idx, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* inv, const void* x, void* x_sorted,
+                     void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg));
+  if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "counts / offsets is NULL");
+  if (cfg->tokens > 0 && (!topk_idx || !perm || !inv))
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx / perm / inv is NULL");
+  if ((x == nullptr) != (x_sorted == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "x and x_sorted must be given together");
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(do_route(cfg, layout(cfg), topk_idx, counts, offsets, perm, inv, ws, s));
+  if (x)
+    MOE_TRY(hip_status(launch_gather_rows(x, perm, cfg->top_k, cfg->tokens * cfg->top_k,
+                                          cfg->d_model, (int)elem_size(cfg), x_sorted, s),
+                       "gather"));
+  return ok();
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* perm,
+                          const int32_t* offsets, const moe_params* p, void* y_sorted, void* ws,
+                          size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg));
+  MOE_TRY(check_expert_inputs(cfg, p));
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if (cfg->tokens > 0 && (!x || !y_sorted)) return fail(MOE_ERR_INVALID_ARG, "x / y_sorted is NULL");
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  MOE_TRY(do_ffn(cfg, layout(cfg), x, perm, offsets, p, y_sorted, ws, (hipStream_t)stream));
+  return ok();
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const int32_t* inv,
+                       const float* topk_gate, void* y, void* stream) {
+  MOE_TRY(check_config(cfg));
+  if (cfg->tokens > 0 && (!y_sorted || !inv || !topk_gate || !y))
+    return fail(MOE_ERR_INVALID_ARG, "y_sorted / inv / topk_gate / y is NULL");
+  MOE_TRY(hip_status(launch_combine(y_sorted, inv, topk_gate, cfg->tokens, cfg->top_k,
+                                    cfg->d_model, cfg->dtype == MOE_BF16, y, (hipStream_t)stream),
+                     "combine"));
+  return ok();
+}
+
+moe_status moe_balance_loss(const moe_config* cfg, const void* x, const moe_params* p,
+                            const int32_t* topk_idx, const float* topk_gate, const float* thr,
+                            const int32_t* perm, const int32_t* offsets, float w_importance,
+                            float w_load, float* importance, float* load, float* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg));
+  if (!importance || !load || !out || !offsets)
+    return fail(MOE_ERR_INVALID_ARG, "importance / load / out / offsets is NULL");
+  if (cfg->tokens > 0 && (!perm || !topk_gate))
+    return fail(MOE_ERR_INVALID_ARG, "perm / topk_gate is NULL");
+  const bool smooth = cfg->n_groups == 0 && cfg->noisy && cfg->tokens > 0;
+  if (smooth && (!x || !p || !p->w_gate || !p->w_noise || !topk_idx || !thr))
+    return fail(MOE_ERR_INVALID_ARG, "smooth load needs x, w_gate, w_noise, topk_idx and thr");
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  MOE_TRY(do_balance(cfg, layout(cfg), x, p, topk_idx, topk_gate, thr, perm, offsets,
+                     w_importance, w_load, importance, load, out, ws, (hipStream_t)stream));
+  return ok();
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p,
+                       const moe_noise* noise, float w_importance, float w_load, moe_outputs* out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg));
+  MOE_TRY(check_gate_inputs(cfg, x, p, noise));
+  MOE_TRY(check_expert_inputs(cfg, p));
+  if (!out || (!out->y && cfg->tokens > 0)) return fail(MOE_ERR_INVALID_ARG, "out / out->y is NULL");
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  const Layout L = layout(cfg);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* idx = out->topk_idx ? out->topk_idx : at<int32_t>(ws, L.idx);
+  float* gate = out->topk_gate ? out->topk_gate : at<float>(ws, L.gate);
+  int32_t* counts = out->counts ? out->counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  void* y_sorted = at<void>(ws, L.ysorted);
+  const bool balance = out->balance != nullptr;
+  float* thr = (balance && cfg->n_groups == 0 && cfg->noisy) ? at<float>(ws, L.thr) : nullptr;
+  MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, ws, s));
+  MOE_TRY(do_route(cfg, L, idx, counts, offsets, perm, inv, ws, s));
+  MOE_TRY(do_ffn(cfg, L, x, perm, offsets, p, y_sorted, ws, s));
+  MOE_TRY(hip_status(launch_combine(y_sorted, inv, gate, cfg->tokens, cfg->top_k, cfg->d_model,
+                                    cfg->dtype == MOE_BF16, out->y, s),
+                     "combine"));
+  if (balance) {
+    float* imp = out->importance ? out->importance : at<float>(ws, L.imp);
+    float* load = out->load ? out->load : at<float>(ws, L.load);
+    MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, perm, offsets, w_importance, w_load, imp,
+                       load, out->balance, ws, s));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+// Expert FFNs over the routed rows.
+//
+// Expert e is a one-hidden-layer FFN ("MoE:稀疏门控混合专家", nengyongai.cn,
+// section 二: 512 -> 1024 -> 512, ReLU); the SwiGLU variant of the Mixtral
+// page ("MoE 混合专家：参数大、计算省", section 核心概念) uses gate/up/down
+// tables.  Only the rows routed to an expert are evaluated: the grid walks a
+// tile map built from the routing offsets, so experts with no rows cost
+// nothing.
+//
+// bf16 path: two grouped GEMMs on MFMA (v_mfma_f32_32x32x16_bf16), both
+// operands K-contiguous ([rows][K] activations, [N][K] weight tables):
+//   hid[p]      = act(x[row p] W1_e^T (, x[row p] W3_e^T))   bf16, [A][h]
+//   y_sorted[p] = hid[p] W2_e^T                              bf16, [A][d]
+// 128x128 output tiles, K staged through LDS in 32-wide double-buffered
+// slices, fp32 accumulation.
+// fp32 path: one thread per output, fp32 FMA (small layers).
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int GM_BM = 128, GM_BN = 128, GM_BK = 32, GM_LD = GM_BK + 8;
+
+enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+
+struct GemmArgs {
+  const bf16_t* A;
+  int64_t lda;
+  const int32_t* perm;  // null: source row of position p is p; else perm[p] / k
+  int k;
+  const bf16_t* B;      // [E][N][K]
+  const bf16_t* B3;     // [E][N][K] (SwiGLU up) or null
+  int N, K;
+  const int32_t* offsets;  // [E+1]
+  const int32_t* tiles;    // [E+1] tiles of GM_BM rows
+  int E;
+  bf16_t* C;               // [A][ldc]
+  int64_t ldc;
+  int ncol;                // ceil(N / GM_BN)
+};
+
+// Expert owning tile q: the largest e with tiles[e] <= q (tiles non-decreasing).
+__device__ __forceinline__ int expert_of_tile(const int32_t* tiles, int E, int q) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (tiles[mid] <= q) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
+  constexpr bool SW = (EPI == EPI_SWIGLU);
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][GM_BM][GM_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][GM_BN][GM_LD];
+  constexpr int B3B = SW ? 2 : 1, B3R = SW ? GM_BN : 1;
+  __shared__ __attribute__((aligned(16))) bf16_t B3s[B3B][B3R][GM_LD];
+  __shared__ int s_e, s_row0, s_m;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q = blockIdx.x / g.ncol, ct = blockIdx.x % g.ncol;
+  if (tid == 0) {
+    int Q = g.tiles[g.E];
+    if (q < Q) {
+      int e = expert_of_tile(g.tiles, g.E, q);
+      int row0 = g.offsets[e] + (q - g.tiles[e]) * GM_BM;
+      s_e = e;
+      s_row0 = row0;
+      s_m = min(GM_BM, g.offsets[e + 1] - row0);
+    } else {
+      s_e = -1;
+    }
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e < 0) return;
+  const int row0 = s_row0, m = s_m;
+  const int n0 = ct * GM_BN;
+
+  // global -> LDS assignment: 2 chunks of 16 bytes per thread per operand
+  const int lrow = tid >> 2, lk = (tid & 3) * 8;
+  const bf16_t* ap[2];
+  const bf16_t* bp[2];
+  const bf16_t* b3p[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int r = lrow + 64 * i;
+    int p = row0 + min(r, m - 1);
+    int64_t src = g.perm ? (int64_t)(g.perm[p] / g.k) : (int64_t)p;
+    ap[i] = g.A + src * g.lda + lk;
+    int n = min(n0 + r, g.N - 1);
+    bp[i] = g.B + ((int64_t)e * g.N + n) * g.K + lk;
+    b3p[i] = SW ? g.B3 + ((int64_t)e * g.N + n) * g.K + lk : g.B;
+  }
+
+  const int wm = w >> 1, wn = w & 1;
+  const bool active = wm * 64 < m;
+  f32x16 acc[2][2], acc3[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = f32x16{};
+      acc3[i][j] = f32x16{};
+    }
+
+  u32x4 ra[2], rb[2], rb3[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0);
+      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0);
+      if constexpr (SW) rb3[i] = *reinterpret_cast<const u32x4*>(b3p[i] + k0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<u32x4*>(&As[buf][lrow + 64 * i][lk]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][lrow + 64 * i][lk]) = rb[i];
+      if constexpr (SW) *reinterpret_cast<u32x4*>(&B3s[buf][lrow + 64 * i][lk]) = rb3[i];
+    }
+  };
+
+  const int nk = g.K / GM_BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * GM_BK);
+    if (active) {
+#pragma unroll
+      for (int ks = 0; ks < GM_BK; ks += 16) {
+        bf16x8 af[2], bf[2], b3f[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * 64 + i * 32 + fr][ks + fk]);
+          bf[i] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * 64 + i * 32 + fr][ks + fk]);
+          if constexpr (SW)
+            b3f[i] = *reinterpret_cast<const bf16x8*>(&B3s[buf][wn * 64 + i * 32 + fr][ks + fk]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+            if constexpr (SW) acc3[i][j] = mfma32(af[i], b3f[j], acc3[i][j]);
+          }
+      }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (row < m && col < g.N) {
+          float v = acc[i][j][r];
+          if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+          if constexpr (EPI == EPI_SWIGLU) v = silu_f(v) * acc3[i][j][r];
+          g.C[(int64_t)(row0 + row) * g.ldc + col] = f32_to_bf16(v);
+        }
+      }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one thread per output element.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int p) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void ffn1_f32_kernel(FfnArgs a, int swiglu) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.A * a.h) return;
+  const int p = (int)(i / a.h), j = (int)(i % a.h);
+  const int e = expert_of_row(a.offsets, a.E, p);
+  const int64_t src = a.perm ? (int64_t)(a.perm[p] / a.k) : (int64_t)p;
+  const float* xr = (const float*)a.x + src * a.d;
+  const float* w1 = (const float*)a.w1 + ((int64_t)e * a.h + j) * a.d;
+  float s = 0.f;
+  for (int c = 0; c < a.d; ++c) s = fmaf(xr[c], w1[c], s);
+  float v;
+  if (swiglu) {
+    const float* w3 = (const float*)a.w3 + ((int64_t)e * a.h + j) * a.d;
+    float u = 0.f;
+    for (int c = 0; c < a.d; ++c) u = fmaf(xr[c], w3[c], u);
+    v = silu_f(s) * u;
+  } else {
+    v = fmaxf(s, 0.f);
+  }
+  ((float*)a.hid)[i] = v;
+}
+
+__global__ __launch_bounds__(256) void ffn2_f32_kernel(FfnArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.A * a.d) return;
+  const int p = (int)(i / a.d), n = (int)(i % a.d);
+  const int e = expert_of_row(a.offsets, a.E, p);
+  const float* hr = (const float*)a.hid + (int64_t)p * a.h;
+  const float* w2 = (const float*)a.w2 + ((int64_t)e * a.d + n) * a.h;
+  float s = 0.f;
+  for (int c = 0; c < a.h; ++c) s = fmaf(hr[c], w2[c], s);
+  ((float*)a.y_sorted)[i] = s;
+}
+
+int ffn_tile_rows(bool bf16, int, int, int) { return bf16 ? GM_BM : 1; }
+
+hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_t s) {
+  if (a.A == 0) return hipSuccess;
+  if (!bf16) {
+    hipLaunchKernelGGL(ffn1_f32_kernel, dim3((unsigned)((a.A * a.h + 255) / 256)), dim3(256), 0, s,
+                       a, swiglu);
+    hipLaunchKernelGGL(ffn2_f32_kernel, dim3((unsigned)((a.A * a.d + 255) / 256)), dim3(256), 0, s,
+                       a);
+    return hipGetLastError();
+  }
+  // upper bound of tiles: each non-empty expert adds at most one partial tile
+  const int64_t qmax = (a.A + GM_BM - 1) / GM_BM + a.E;
+  GemmArgs g1;
+  g1.A = (const bf16_t*)a.x;
+  g1.lda = a.d;
+  g1.perm = a.perm;
+  g1.k = a.k;
+  g1.B = (const bf16_t*)a.w1;
+  g1.B3 = (const bf16_t*)a.w3;
+  g1.N = a.h;
+  g1.K = a.d;
+  g1.offsets = a.offsets;
+  g1.tiles = a.tiles;
+  g1.E = a.E;
+  g1.C = (bf16_t*)a.hid;
+  g1.ldc = a.h;
+  g1.ncol = (a.h + GM_BN - 1) / GM_BN;
+  if (swiglu)
+    hipLaunchKernelGGL(grouped_gemm_kernel<EPI_SWIGLU>, dim3((unsigned)(qmax * g1.ncol)), dim3(256),
+                       0, s, g1);
+  else
+    hipLaunchKernelGGL(grouped_gemm_kernel<EPI_RELU>, dim3((unsigned)(qmax * g1.ncol)), dim3(256), 0,
+                       s, g1);
+  GemmArgs g2 = g1;
+  g2.A = (const bf16_t*)a.hid;
+  g2.lda = a.h;
+  g2.perm = nullptr;
+  g2.B = (const bf16_t*)a.w2;
+  g2.B3 = nullptr;
+  g2.N = a.d;
+  g2.K = a.h;
+  g2.C = (bf16_t*)a.y_sorted;
+  g2.ldc = a.d;
+  g2.ncol = (a.d + GM_BN - 1) / GM_BN;
+  hipLaunchKernelGGL(grouped_gemm_kernel<EPI_NONE>, dim3((unsigned)(qmax * g2.ncol)), dim3(256), 0,
+                     s, g2);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,91 @@
+// Device-side helpers shared by the HIP kernels of the MoE layer (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // storage type of bfloat16 values in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+
+// float -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// 16-byte vector load of 8 bf16 values as the MFMA operand type.
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
+  u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// D(32x32, fp32) += A(32x16) * B(16x32); operands bf16.
+// Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32];
+// accumulator register r of lane l holds D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16, fp32) += A(16x32) * B(32x16); operands bf16.
+// Lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16];
+// accumulator register r of lane l holds D[4*(l/16) + r][l%16].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float softplus_f(float z) {
+  // ln(1 + e^z) = max(z, 0) + log1p(e^-|z|)
+  return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+}
+
+__device__ __forceinline__ float normal_cdf_f(float z) {
+  return 0.5f * erfcf(-z * 0.70710678118654752440f);
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// Ranking of gate candidates: larger score first, lower expert index on ties.
+__device__ __forceinline__ bool ranks_before(float v1, int e1, float v2, int e2) {
+  return v1 > v2 || (v1 == v2 && e1 < e2);
+}
+
+// Map a linear workgroup id to a tile id so that consecutive tile ids land on
+// the same XCD (workgroups are dispatched round-robin over the 8 XCDs) and are
+// dispatched close in time; tiles of one expert then share that XCD's L2.
+__device__ __forceinline__ int xcd_tile_id(int bid, int grid) {
+  const int nx = 8;
+  int per = (grid + nx - 1) / nx;
+  int x = bid % nx, slot = bid / nx;
+  return x * per + slot;
+}
+
+}  // namespace moe

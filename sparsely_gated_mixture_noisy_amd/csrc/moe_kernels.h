@@ -1,0 +1,106 @@
+// Kernel argument blocks and host-side launchers of libmoe (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ----------------------------------------------------------------- gate ----
+struct GateFlatArgs {
+  const void* x;
+  const void* w_gate;   // [E][d]
+  const void* w_noise;  // [E][d] or null
+  const float* bias;    // [E] or null
+  const float* eps;     // [T][E] or null
+  int64_t T;
+  int d, E, k;
+  int32_t* idx;   // [T][k]
+  float* gate;    // [T][k]
+  float* thr;     // [T][2] or null
+};
+hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s);
+
+struct GateGroupArgs {
+  const void* x;
+  const void* w_gate;   // [E][d], group g = rows g*Eg ..
+  const void* w_noise;  // [E][d] or null
+  const float* eps;     // [T][G][Eg] or null
+  int d, G, Eg, kg, kpg;
+  const int32_t* perm_g;     // group routing of the primary selection
+  const int32_t* offsets_g;  // [G+1]
+  const int32_t* tiles_g;    // [G+1], 32-row tiles per group (exclusive scan)
+  const float* gate_p;       // [T][kg] primary gates
+  int32_t* idx;              // [T][kg*kpg] final experts
+  float* gate;               // [T][kg*kpg] final gates
+};
+hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStream_t s);
+
+struct LoadArgs {
+  const void* x;
+  const void* w_gate;
+  const void* w_noise;
+  const float* bias;
+  const int32_t* idx;  // [T][k]
+  const float* thr;    // [T][2]
+  int64_t T;
+  int d, E, k;
+  int tiles;           // 32-row tiles per workgroup
+  float* part;         // [blocks][E]
+};
+int load_partial_blocks(int64_t T, int* tiles_per_block);
+hipError_t launch_load_partial(const LoadArgs& a, int blocks, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- route ----
+constexpr int ROUTE_BLOCK_TOKENS = 64;
+struct RouteArgs {
+  const int32_t* idx;  // [T][k]
+  int64_t T;
+  int k, E;
+  int NB;              // ceil(T / 64)
+  int32_t* blk;        // [NB][E] workspace
+  int32_t* ticket;     // [1] workspace
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E+1]
+  int32_t* perm;       // [A]
+  int32_t* inv;        // [A]
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// x_sorted[p] = x[perm[p] / k] for p < A (elem_bytes per element, d per row)
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, int k, int64_t A, int d,
+                              int elem_bytes, void* out, hipStream_t s);
+
+// tiles[e] = sum_{e' < e} ceil(count_{e'} / rows), tiles[E] = total
+hipError_t launch_tile_map(const int32_t* offsets, int E, int rows, int32_t* tiles,
+                           hipStream_t s);
+
+// --------------------------------------------------------------- experts ---
+struct FfnArgs {
+  const void* x;          // rows source
+  const int32_t* perm;    // null: row p is x[p]; else x[perm[p] / k]
+  int k;
+  const int32_t* offsets; // [E+1]
+  const int32_t* tiles;   // [E+1] tile map for the kernel's row tile
+  int E, d, h;
+  const void* w1;         // [E][h][d]
+  const void* w3;         // [E][h][d] or null
+  const void* w2;         // [E][d][h]
+  void* hid;              // [A][h] workspace (unfused paths)
+  void* y_sorted;         // [A][d]
+  int64_t A;
+};
+int ffn_tile_rows(bool bf16, int d, int h, int swiglu);
+hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_t s);
+
+// -------------------------------------------------------- combine / stats --
+hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float* gate, int64_t T,
+                          int k, int d, bool bf16, void* y, hipStream_t s);
+hipError_t launch_importance(const int32_t* perm, const int32_t* offsets, const float* gate,
+                             int E, float* importance, hipStream_t s);
+// load[e] = sum_b part[b][e] (part != null) or counts[e] (part == null)
+hipError_t launch_load_reduce(const float* part, int blocks, const int32_t* offsets, int E,
+                              float* load, hipStream_t s);
+hipError_t launch_cv2(const float* importance, const float* load, int E, float w_imp,
+                      float w_load, float* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/moe.h declares, and rejects bad arguments before touching a GPU.
+No call here reaches a kernel launch."""
+import ctypes
+
+import pytest
+
+from sparsely_gated_mixture_noisy_amd import _lib as L
+from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, MoEConfig
+
+FAKE = 1 << 20  # a non-null, 256-byte aligned stand-in pointer (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_exports_every_header_function(lib):
+    names = L.header_functions()
+    assert {"moe_gate", "moe_route", "moe_expert_ffn", "moe_combine", "moe_balance_loss",
+            "moe_forward", "moe_workspace_size", "moe_status_string", "moe_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"ok"
+    assert b"workspace" in lib.moe_status_string(L.MOE_ERR_WORKSPACE)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_sizes(name):
+    cfg = CONFIGS[name]
+    n = L.workspace_size(cfg)
+    assert n > 0 and n % 256 == 0
+    # grows with the batch
+    assert L.workspace_size(cfg, tokens=cfg.tokens * 2) > n
+
+
+def _gate_call(lib, cfg, params=None, noise=None, ws_bytes=1 << 40, ws=FAKE, thr=None):
+    c = L.make_config(cfg)
+    p = params or L.moe_params(w_gate=FAKE, w_noise=FAKE, w1=FAKE, w2=FAKE, w3=FAKE,
+                               w_gate_p=FAKE, w_noise_p=FAKE)
+    n = noise or L.moe_noise(eps=FAKE, eps_p=FAKE)
+    return lib.moe_gate(ctypes.byref(c), FAKE, ctypes.byref(p), ctypes.byref(n), FAKE, FAKE, thr,
+                        ws, ws_bytes, None)
+
+
+def test_invalid_configs_rejected_before_launch(lib):
+    base = CONFIGS["flat256"]
+    assert _gate_call(lib, base.replace(top_k=300)) == L.MOE_ERR_INVALID_ARG
+    assert _gate_call(lib, base.replace(top_k=0)) == L.MOE_ERR_INVALID_ARG
+    assert _gate_call(lib, base.replace(tokens=-1)) == L.MOE_ERR_INVALID_ARG
+    assert _gate_call(lib, base.replace(d_model=100)) == L.MOE_ERR_UNSUPPORTED
+    assert _gate_call(lib, base.replace(top_k=9)) == L.MOE_ERR_UNSUPPORTED
+    assert _gate_call(lib, base.replace(n_experts=9000)) == L.MOE_ERR_UNSUPPORTED
+    assert b"n_experts" in lib.moe_last_error()
+    hier = CONFIGS["hier4096"]
+    assert _gate_call(lib, hier.replace(k_groups=3)) == L.MOE_ERR_INVALID_ARG  # 3*2 != 4
+    assert _gate_call(lib, hier.replace(n_groups=15)) == L.MOE_ERR_INVALID_ARG
+    assert _gate_call(lib, hier, thr=FAKE) == L.MOE_ERR_INVALID_ARG
+
+
+def test_missing_tensors_rejected(lib):
+    cfg = CONFIGS["flat256"]
+    no_noise = L.moe_params(w_gate=FAKE, w_noise=None, w1=FAKE, w2=FAKE)
+    assert _gate_call(lib, cfg, params=no_noise) == L.MOE_ERR_INVALID_ARG
+    assert _gate_call(lib, cfg, noise=L.moe_noise(eps=None, eps_p=None)) == L.MOE_ERR_INVALID_ARG
+    c = L.make_config(CONFIGS["mixtral"])
+    p = L.moe_params(w_gate=FAKE, w1=FAKE, w2=FAKE, w3=None)
+    assert lib.moe_expert_ffn(ctypes.byref(c), FAKE, FAKE, FAKE, ctypes.byref(p), FAKE, FAKE,
+                              1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert b"w3" in lib.moe_last_error()
+
+
+def test_workspace_checks(lib):
+    cfg = CONFIGS["flat256"]
+    need = L.workspace_size(cfg)
+    assert _gate_call(lib, cfg, ws_bytes=need - 1) == L.MOE_ERR_WORKSPACE
+    assert _gate_call(lib, cfg, ws=FAKE + 8) == L.MOE_ERR_WORKSPACE
+    assert _gate_call(lib, cfg, ws=None) == L.MOE_ERR_WORKSPACE
+
+
+def test_binding_raises_with_detail():
+    cfg = CONFIGS["flat256"].replace(top_k=0)
+    with pytest.raises(L.MoEError) as ei:
+        L._check(_gate_call(L.load(), cfg), "moe_gate")
+    assert ei.value.status == L.MOE_ERR_INVALID_ARG

@@ -1,0 +1,221 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases run the whole layer through the oracle; the five full-size
+workloads compare routing and gates over every token, layer outputs on a
+sample of tokens, and the balance statistics."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_check import (check_balance, check_close, check_gate, check_routing, excluded, np_)
+from sparsely_gated_mixture_noisy_amd import _lib as L
+from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def cpu_inputs(inp):
+    return {k: (v.detach().to("cpu") if v is not None else None) for k, v in inp.items()}
+
+
+def top_k1_sets(ref, cfg):
+    g = ref["gate_info"]
+    if cfg.hierarchical:
+        prim = g["primary"]
+        order = np.argsort(-prim["H"], axis=1, kind="stable")[:, :cfg.k_groups + 1]
+        Eg = cfg.experts_per_group
+        return [np.concatenate([np.arange(q * Eg, (q + 1) * Eg) for q in row]) for row in order]
+    order = np.argsort(-g["H"], axis=1, kind="stable")[:, :cfg.top_k + 1]
+    return [row for row in order]
+
+
+def run_staged(cfg, inp):
+    """gate -> route -> experts -> combine -> balance, one entry point each."""
+    x = inp["x"]
+    ws = L.workspace(cfg, x.shape[0])
+    idx, gate, thr = L.gate(cfg, x, inp, inp, ws=ws)
+    counts, offsets, perm, inv, _ = L.route(cfg, idx, ws=ws)
+    ys = L.expert_ffn(cfg, x, perm, offsets, inp, ws=ws)
+    y = L.combine(cfg, ys, inv, gate)
+    imp, load, out = L.balance_loss(cfg, x, inp, idx, gate, thr, perm, offsets, 1.0, 1.0, ws=ws)
+    torch.cuda.synchronize()
+    return dict(idx=idx, gate=gate, thr=thr, counts=counts, offsets=offsets, perm=perm, inv=inv,
+                y_sorted=ys, y=y, importance=imp, load=load, balance=out)
+
+
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    "tiny_ragged": CONFIGS["tiny"].replace(tokens=77),
+    "tiny_k_eq_E": CONFIGS["tiny"].replace(tokens=100, top_k=8),
+    "tiny_swiglu": CONFIGS["tiny"].replace(tokens=90, ffn="swiglu", noisy=False),
+    "tiny_hier": CONFIGS["tiny"].replace(tokens=123, n_experts=12, n_groups=3, k_groups=2,
+                                         k_per_group=2, top_k=4, gate_std=0.3),
+    "flat256_t1000": CONFIGS["flat256"].replace(tokens=1000),
+    "flat256_k1": CONFIGS["flat256"].replace(tokens=333, top_k=1),
+    "zipf2048_t2000": CONFIGS["zipf2048"].replace(tokens=2000),
+    "hier4096_t300": CONFIGS["hier4096"].replace(tokens=300),
+    "hier_g16_e64": CONFIGS["hier4096"].replace(tokens=700, n_experts=1024),
+    "swiglu_bf16_small": CONFIGS["mixtral"].replace(tokens=200, d_model=512, d_hidden=1536),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_layer(name):
+    cfg = SMALL[name]
+    _say(f"[parity] {name}: {cfg}")
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    got = run_staged(cfg, inp)
+    ref = oracle.forward(cpu_inputs(inp), cfg)
+    excl = excluded(ref)
+    rep = {}
+    check_gate(got["idx"], got["gate"], ref, excl, thr=got["thr"], report=rep)
+    check_routing(got["counts"], got["offsets"], got["perm"], got["inv"], got["idx"], ref, excl,
+                  cfg.top_k)
+    rows = np.nonzero(~excl)[0]
+    worst = check_close(got["y"], ref["y"], RTOL[cfg.dtype], rows=rows)
+    check_balance(got["importance"], got["load"], got["balance"], ref, excl, ref["idx"],
+                  k1_sets=top_k1_sets(ref, cfg), smooth=(cfg.noisy and not cfg.hierarchical))
+    # moe_forward gives bitwise the staged results
+    fo = L.forward(cfg, inp["x"], inp, inp)
+    torch.cuda.synchronize()
+    for a, b in [(fo.y, got["y"]), (fo.topk_idx, got["idx"]), (fo.topk_gate, got["gate"]),
+                 (fo.counts, got["counts"]), (fo.importance, got["importance"]),
+                 (fo.load, got["load"]), (fo.balance, got["balance"])]:
+        assert torch.equal(a, b)
+    _say(f"[parity] {name}: ok excluded={rep['excluded']} worst_y={worst:.2e}")
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_full_size(name):
+    cfg = CONFIGS[name]
+    _say(f"[parity-full] {name}: {cfg}")
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    got = run_staged(cfg, inp)
+    cin = cpu_inputs({k: v for k, v in inp.items() if k not in ("w1", "w2", "w3")})
+    ref = oracle.forward(cin, cfg, with_experts=False)
+    excl = excluded(ref)
+    rep = {}
+    check_gate(got["idx"], got["gate"], ref, excl, thr=got["thr"], report=rep)
+    check_routing(got["counts"], got["offsets"], got["perm"], got["inv"], got["idx"], ref, excl,
+                  cfg.top_k)
+    check_balance(got["importance"], got["load"], got["balance"], ref, excl, ref["idx"],
+                  k1_sets=top_k1_sets(ref, cfg), smooth=(cfg.noisy and not cfg.hierarchical))
+    # layer outputs on sampled included tokens, computed expert by expert
+    rng = np.random.default_rng(1)
+    inc = np.nonzero(~excl)[0]
+    sample = np.sort(rng.choice(inc, size=min(96, inc.size), replace=False))
+    x = cin["x"]
+    y_ref = np.zeros((sample.size, cfg.d_model))
+    ridx, rg = ref["idx"][sample], ref["gates"][sample]
+    for e in np.unique(ridx):
+        rows, slots = np.nonzero(ridx == e)
+        w1 = inp["w1"][e].cpu()
+        w2 = inp["w2"][e].cpu()
+        w3 = inp["w3"][e].cpu() if inp["w3"] is not None else None
+        xe = x[sample[rows]]
+        ye = oracle.expert_swiglu(xe, w1, w3, w2) if w3 is not None else oracle.expert_relu(xe, w1, w2)
+        y_ref[rows] += rg[rows, slots][:, None] * ye
+    worst = check_close(got["y"][torch.from_numpy(sample).cuda()], y_ref, RTOL[cfg.dtype])
+    fo = L.forward(cfg, inp["x"], inp, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fo.y, got["y"]) and torch.equal(fo.topk_idx, got["idx"])
+    c = np_(got["counts"])
+    _say(f"[parity-full] {name}: ok excluded={rep['excluded']} worst_y={worst:.2e} "
+         f"counts max/mean={c.max() / max(c.mean(), 1e-9):.1f} zero={int((c == 0).sum())}")
+
+
+def test_determinism_bitwise():
+    cfg = CONFIGS["flat256"]
+    inp = make_inputs(cfg, seed=3, device="cuda")
+    f = L.Forward(cfg, inp["x"], inp, inp)
+    a = f()
+    y1 = a.y.clone(); b1 = a.balance.clone(); g1 = a.topk_gate.clone()
+    for _ in range(3):
+        b = f()
+        torch.cuda.synchronize()
+        assert torch.equal(b.y, y1) and torch.equal(b.balance, b1) and torch.equal(b.topk_gate, g1)
+
+
+def test_empty_batch():
+    cfg = CONFIGS["flat256"].replace(tokens=0)
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    fo = L.forward(cfg, inp["x"], inp, inp)
+    torch.cuda.synchronize()
+    assert fo.y.shape == (0, cfg.d_model)
+    assert int(fo.counts.sum()) == 0
+    assert fo.balance.tolist() == [0.0, 0.0, 0.0]
+
+
+def test_single_token_and_single_expert():
+    for cfg in (CONFIGS["flat256"].replace(tokens=1),
+                CONFIGS["flat256"].replace(tokens=50, n_experts=1, top_k=1),
+                CONFIGS["tiny"].replace(tokens=5, n_experts=1, top_k=1)):
+        inp = make_inputs(cfg, seed=0, device="cuda")
+        got = run_staged(cfg, inp)
+        ref = oracle.forward(cpu_inputs(inp), cfg)
+        excl = excluded(ref)
+        check_gate(got["idx"], got["gate"], ref, excl)
+        check_close(got["y"], ref["y"], RTOL[cfg.dtype], rows=np.nonzero(~excl)[0])
+
+
+def test_identical_tokens_max_skew():
+    """Every token the same and no noise: all T rows go to the same k experts
+    (ties in the bf16 scores fall to the lower index, as in the oracle)."""
+    cfg = CONFIGS["flat256"].replace(tokens=2048, noisy=False)
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    inp["x"] = inp["x"][:1].expand(cfg.tokens, -1).contiguous()
+    got = run_staged(cfg, inp)
+    ref = oracle.forward(cpu_inputs(inp), cfg)
+    excl = excluded(ref)
+    assert not excl.any()
+    c = np_(got["counts"])
+    assert (np.sort(c)[-cfg.top_k:] == cfg.tokens).all() and c.sum() == cfg.tokens * cfg.top_k
+    check_gate(got["idx"], got["gate"], ref, excl)
+    check_routing(got["counts"], got["offsets"], got["perm"], got["inv"], got["idx"], ref, excl,
+                  cfg.top_k)
+    check_close(got["y"], ref["y"], RTOL[cfg.dtype])
+
+
+def test_half_experts_starved_by_bias():
+    """A bias of -1e4 on the odd experts: they receive no rows at all."""
+    cfg = CONFIGS["flat256"].replace(tokens=1500)
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    b = torch.zeros(cfg.n_experts, dtype=torch.float32, device="cuda")
+    b[1::2] = -1e4
+    inp["bias"] = b
+    got = run_staged(cfg, inp)
+    ref = oracle.forward(cpu_inputs(inp), cfg)
+    excl = excluded(ref)
+    c = np_(got["counts"])
+    assert (c[1::2] == 0).all()
+    check_gate(got["idx"], got["gate"], ref, excl, thr=got["thr"])
+    check_routing(got["counts"], got["offsets"], got["perm"], got["inv"], got["idx"], ref, excl,
+                  cfg.top_k)
+    check_close(got["y"], ref["y"], RTOL[cfg.dtype], rows=np.nonzero(~excl)[0])
+    check_balance(got["importance"], got["load"], got["balance"], ref, excl, ref["idx"],
+                  k1_sets=top_k1_sets(ref, cfg))
+
+
+def test_route_x_sorted_gather():
+    cfg = CONFIGS["flat256"].replace(tokens=700)
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    idx, gate, _ = L.gate(cfg, inp["x"], inp, inp)
+    counts, offsets, perm, inv, xs = L.route(cfg, idx, x=inp["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(xs, inp["x"][(perm // cfg.top_k).long()])
+    # experts on the gathered rows give bitwise the gathered-in-kernel result
+    y1 = L.expert_ffn(cfg, inp["x"], perm, offsets, inp)
+    y2 = L.expert_ffn(cfg, xs, None, offsets, inp, tokens=cfg.tokens)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
