@@ -90,6 +90,10 @@ typedef struct moe_config {
  *   w1        [E][h][d] first expert layer (ReLU: in; SwiGLU: gate)
  *   w3        [E][h][d] SwiGLU up projection (NULL for ReLU)
  *   w2        [E][d][h] second expert layer (out / down)
+ *   w_packed  nullable: w1 and w2 repacked by moe_pack_experts; when given,
+ *             the expert stage reads it instead of w1 / w2 (which may then
+ *             be NULL).  Same values, laid out in the order the expert
+ *             kernel streams them.
  * For the hierarchy, rows g*Eg .. g*Eg+Eg-1 of w_gate / w_noise are the
  * secondary tables of group g. */
 typedef struct moe_params {
@@ -101,6 +105,7 @@ typedef struct moe_params {
   const void* w1;
   const void* w3;
   const void* w2;
+  const void* w_packed;
 } moe_params;
 
 /* Noise draws, float32 ~ N(0,1), supplied by the caller (NULL = no noise).
@@ -158,6 +163,19 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x,
                           const int32_t* perm, const int32_t* offsets,
                           const moe_params* p, void* y_sorted, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* Bytes of the packed expert tables for cfg, or 0 when the configuration
+ * has no packed form (packing applies to bf16 ReLU experts with
+ * d_model == 512 and d_hidden % 256 == 0). */
+size_t moe_packed_experts_size(const moe_config* cfg);
+
+/* Repack p->w1 and p->w2 into `packed` (moe_packed_experts_size bytes,
+ * 16-byte aligned) in the fragment order the expert kernel consumes, so
+ * that each of its wave-wide weight loads reads 1 KB of contiguous memory.
+ * A one-time transform of the parameters; the values are unchanged.
+ * Returns MOE_ERR_UNSUPPORTED when the configuration has no packed form. */
+moe_status moe_pack_experts(const moe_config* cfg, const moe_params* p, void* packed,
+                            void* stream);
 
 /* Combine: y[t] = sum over slots s (ascending) of
  * topk_gate[t][s] * y_sorted[inv[t*k+s]], accumulated in fp32

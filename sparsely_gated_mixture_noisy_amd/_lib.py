@@ -46,7 +46,8 @@ class moe_config(ctypes.Structure):
 
 class moe_params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_gate", "w_noise", "bias", "w_gate_p", "w_noise_p", "w1", "w3", "w2")]
+                ("w_gate", "w_noise", "bias", "w_gate_p", "w_noise_p", "w1", "w3", "w2",
+                 "w_packed")]
 
 
 class moe_noise(ctypes.Structure):
@@ -74,6 +75,9 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(moe_config), _P, ctypes.POINTER(moe_params),
                                    ctypes.POINTER(moe_noise), ctypes.c_float, ctypes.c_float,
                                    ctypes.POINTER(moe_outputs), _P, ctypes.c_size_t, _P]),
+    "moe_packed_experts_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config)]),
+    "moe_pack_experts": (ctypes.c_int, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_params),
+                                        _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -139,6 +143,25 @@ def make_params(p: Dict[str, Optional[torch.Tensor]]) -> moe_params:
 
 def make_noise(p: Dict[str, Optional[torch.Tensor]]) -> moe_noise:
     return moe_noise(eps=_ptr(p.get("eps")), eps_p=_ptr(p.get("eps_p")))
+
+
+def packed_experts_size(cfg: MoEConfig) -> int:
+    c = make_config(cfg)
+    return int(load().moe_packed_experts_size(ctypes.byref(c)))
+
+
+def pack_experts(cfg: MoEConfig, params) -> Optional[torch.Tensor]:
+    """The expert tables w1/w2 repacked for the expert kernel's weight
+    stream (a bf16 tensor on the tables' device), or None when the layer has
+    no packed form."""
+    n = packed_experts_size(cfg)
+    if n == 0:
+        return None
+    out = torch.empty(n // 2, dtype=torch.bfloat16, device=params["w1"].device)
+    c, p = make_config(cfg), make_params(params)
+    _check(load().moe_pack_experts(ctypes.byref(c), ctypes.byref(p), _ptr(out), _stream()),
+           "moe_pack_experts")
+    return out
 
 
 def workspace_size(cfg: MoEConfig, tokens: Optional[int] = None) -> int:

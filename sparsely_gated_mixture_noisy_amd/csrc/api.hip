@@ -40,11 +40,11 @@ size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
 // Every workspace region, at fixed offsets for a given configuration.
 struct Layout {
-  size_t idx, gate, thr, counts, offsets, perm, inv, blk, ticket, tiles, hid, ysorted, part, imp,
-      load;
+  size_t idx, gate, thr, counts, offsets, perm, inv, blk, ticket, tiles, desc, hid, ysorted, part,
+      imp, load;
   size_t idx_p, gate_p, counts_g, offsets_g, perm_g, inv_g, blk_g, tiles_g;
   size_t total;
-  int nb, load_blocks, load_tiles;
+  int nb, load_blocks;
 };
 
 Layout layout(const moe_config* c) {
@@ -52,7 +52,7 @@ Layout layout(const moe_config* c) {
   const int64_t T = c->tokens, A = T * c->top_k;
   const int E = c->n_experts;
   L.nb = (int)((T + ROUTE_BLOCK_TOKENS - 1) / ROUTE_BLOCK_TOKENS);
-  L.load_blocks = load_partial_blocks(T, &L.load_tiles);
+  L.load_blocks = load_partial_blocks(T);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -69,6 +69,8 @@ Layout layout(const moe_config* c) {
   L.blk = take(4 * (size_t)L.nb * E);
   L.ticket = take(4);
   L.tiles = take(4 * (size_t)(E + 1));
+  // tile descriptors of the fused expert kernel (64-row tiles)
+  L.desc = take(12 * (size_t)((A + 63) / 64 + E));
   L.hid = take(elem_size(c) * (size_t)A * c->d_hidden);
   L.ysorted = take(elem_size(c) * (size_t)A * c->d_model);
   L.part = take(4 * (size_t)L.load_blocks * E);
@@ -157,8 +159,18 @@ moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_param
   return MOE_OK;
 }
 
+bool packable(const moe_config* c) {
+  return c->dtype == MOE_BF16 && fused_ffn_supported(c->d_model, c->d_hidden, c->ffn);
+}
+
 moe_status check_expert_inputs(const moe_config* c, const moe_params* p) {
   if (!p) return fail(MOE_ERR_INVALID_ARG, "params is NULL");
+  if (p->w_packed) {
+    if (!packable(c)) return fail(MOE_ERR_UNSUPPORTED, "packed expert tables need bf16 ReLU, d_model 512");
+    if (reinterpret_cast<uintptr_t>(p->w_packed) & 15)
+      return fail(MOE_ERR_INVALID_ARG, "w_packed must be 16-byte aligned");
+    return MOE_OK;
+  }
   if (!p->w1 || !p->w2) return fail(MOE_ERR_INVALID_ARG, "w1 / w2 is NULL");
   if (c->ffn == MOE_FFN_SWIGLU && !p->w3) return fail(MOE_ERR_INVALID_ARG, "SwiGLU needs w3");
   return MOE_OK;
@@ -177,9 +189,11 @@ moe_status hip_status(hipError_t e, const char* what) {
 
 // ---- enqueue helpers (arguments already validated) -------------------------
 
+// part != null (flat noisy gate with E <= GATE_FUSED_LOAD_MAX_E): the gate
+// kernel also writes the smooth-load partial sums.
 moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const moe_params* p,
-                   const moe_noise* n, int32_t* idx, float* gate, float* thr, void* ws,
-                   hipStream_t s) {
+                   const moe_noise* n, int32_t* idx, float* gate, float* thr, float* part,
+                   void* ws, hipStream_t s) {
   const bool bf16 = c->dtype == MOE_BF16;
   const bool noisy = c->noisy != 0;
   if (c->n_groups == 0) {
@@ -196,6 +210,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
     a.idx = idx;
     a.gate = gate;
     a.thr = thr;
+    a.part = part;
     return hip_status(launch_gate_flat(a, bf16, s), "gate");
   }
   const int G = c->n_groups, kg = c->k_groups;
@@ -214,6 +229,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   a.idx = idx_p;
   a.gate = gate_p;
   a.thr = nullptr;
+  a.part = nullptr;
   MOE_TRY(hip_status(launch_gate_flat(a, bf16, s), "primary gate"));
   if (c->tokens == 0) return MOE_OK;
   RouteArgs r;
@@ -230,7 +246,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   r.inv = at<int32_t>(ws, L.inv_g);
   MOE_TRY(hip_status(launch_route(r, s), "group routing"));
   int32_t* tiles_g = at<int32_t>(ws, L.tiles_g);
-  MOE_TRY(hip_status(launch_tile_map(r.offsets, G, 32, tiles_g, s), "group tiles"));
+  MOE_TRY(hip_status(launch_tile_map(r.offsets, G, 32, tiles_g, nullptr, s), "group tiles"));
   GateGroupArgs ga;
   ga.x = x;
   ga.w_gate = p->w_gate;
@@ -289,24 +305,31 @@ moe_status do_ffn(const moe_config* c, const Layout& L, const void* x, const int
   f.hid = at<void>(ws, L.hid);
   f.y_sorted = y_sorted;
   f.A = c->tokens * c->top_k;
+  f.wpacked = p->w_packed;
+  const bool fused = bf16 && fused_ffn_supported(c->d_model, c->d_hidden, sw);
+  int32_t* desc = fused ? at<int32_t>(ws, L.desc) : nullptr;
+  f.desc = desc;
   if (f.A == 0) return MOE_OK;
   if (bf16)
     MOE_TRY(hip_status(launch_tile_map(offsets, c->n_experts,
-                                       ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw), tiles, s),
+                                       ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw), tiles,
+                                       desc, s),
                        "expert tiles"));
   return hip_status(launch_expert_ffn(f, bf16, sw, s), "experts");
 }
 
+// have_part: the gate kernel already wrote the smooth-load partial sums.
 moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const moe_params* p,
                       const int32_t* idx, const float* gate, const float* thr,
                       const int32_t* perm, const int32_t* offsets, float wi, float wl,
-                      float* importance, float* load, float* out, void* ws, hipStream_t s) {
+                      float* importance, float* load, float* out, bool have_part, void* ws,
+                      hipStream_t s) {
   const int E = c->n_experts;
   MOE_TRY(hip_status(launch_importance(perm, offsets, gate, E, importance, s), "importance"));
   const bool smooth = c->n_groups == 0 && c->noisy && c->tokens > 0;
   float* part = nullptr;
-  if (smooth) {
-    part = at<float>(ws, L.part);
+  if (smooth) part = at<float>(ws, L.part);
+  if (smooth && !have_part) {
     LoadArgs la;
     la.x = x;
     la.w_gate = p->w_gate;
@@ -318,9 +341,8 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
     la.d = c->d_model;
     la.E = E;
     la.k = c->top_k;
-    la.tiles = L.load_tiles;
     la.part = part;
-    MOE_TRY(hip_status(launch_load_partial(la, L.load_blocks, c->dtype == MOE_BF16, s), "load"));
+    MOE_TRY(hip_status(launch_load_partial(la, c->dtype == MOE_BF16, s), "load"));
   }
   MOE_TRY(hip_status(launch_load_reduce(part, L.load_blocks, offsets, E, load, s), "load reduce"));
   return hip_status(launch_cv2(importance, load, E, wi, wl, out, s), "cv2");
@@ -348,6 +370,25 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
+size_t moe_packed_experts_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK || !packable(cfg)) return 0;
+  return fused_packed_bytes(cfg->n_experts, cfg->d_model, cfg->d_hidden);
+}
+
+moe_status moe_pack_experts(const moe_config* cfg, const moe_params* p, void* packed,
+                            void* stream) {
+  MOE_TRY(check_config(cfg));
+  if (!packable(cfg))
+    return fail(MOE_ERR_UNSUPPORTED, "packed expert tables need bf16 ReLU, d_model 512");
+  if (!p || !p->w1 || !p->w2 || !packed) return fail(MOE_ERR_INVALID_ARG, "w1 / w2 / packed is NULL");
+  if (reinterpret_cast<uintptr_t>(packed) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  MOE_TRY(hip_status(launch_pack_experts(p->w1, p->w2, cfg->n_experts, cfg->d_model,
+                                         cfg->d_hidden, packed, (hipStream_t)stream),
+                     "pack"));
+  return ok();
+}
+
 moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
                     const moe_noise* noise, int32_t* topk_idx, float* topk_gate, float* thr,
                     void* ws, size_t ws_bytes, void* stream) {
@@ -357,7 +398,7 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
     return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_gate is NULL");
   if (thr && cfg->n_groups > 0) return fail(MOE_ERR_INVALID_ARG, "thr is for the flat gate only");
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
-  MOE_TRY(do_gate(cfg, layout(cfg), x, p, noise, topk_idx, topk_gate, thr, ws,
+  MOE_TRY(do_gate(cfg, layout(cfg), x, p, noise, topk_idx, topk_gate, thr, nullptr, ws,
                   (hipStream_t)stream));
   return ok();
 }
@@ -419,7 +460,8 @@ moe_status moe_balance_loss(const moe_config* cfg, const void* x, const moe_para
     return fail(MOE_ERR_INVALID_ARG, "smooth load needs x, w_gate, w_noise, topk_idx and thr");
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   MOE_TRY(do_balance(cfg, layout(cfg), x, p, topk_idx, topk_gate, thr, perm, offsets,
-                     w_importance, w_load, importance, load, out, ws, (hipStream_t)stream));
+                     w_importance, w_load, importance, load, out, false, ws,
+                     (hipStream_t)stream));
   return ok();
 }
 
@@ -441,8 +483,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   int32_t* inv = at<int32_t>(ws, L.inv);
   void* y_sorted = at<void>(ws, L.ysorted);
   const bool balance = out->balance != nullptr;
-  float* thr = (balance && cfg->n_groups == 0 && cfg->noisy) ? at<float>(ws, L.thr) : nullptr;
-  MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, ws, s));
+  const bool smooth = balance && cfg->n_groups == 0 && cfg->noisy && cfg->tokens > 0;
+  float* thr = smooth ? at<float>(ws, L.thr) : nullptr;
+  // small expert counts: the gate kernel produces the load partials itself
+  const bool fused_load = smooth && gate_fuses_load(cfg->n_experts);
+  float* part = fused_load ? at<float>(ws, L.part) : nullptr;
+  MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, part, ws, s));
   MOE_TRY(do_route(cfg, L, idx, counts, offsets, perm, inv, ws, s));
   MOE_TRY(do_ffn(cfg, L, x, perm, offsets, p, y_sorted, ws, s));
   MOE_TRY(hip_status(launch_combine(y_sorted, inv, gate, cfg->tokens, cfg->top_k, cfg->d_model,
@@ -452,7 +498,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
     float* imp = out->importance ? out->importance : at<float>(ws, L.imp);
     float* load = out->load ? out->load : at<float>(ws, L.load);
     MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, perm, offsets, w_importance, w_load, imp,
-                       load, out->balance, ws, s));
+                       load, out->balance, fused_load, ws, s));
   }
   return ok();
 }

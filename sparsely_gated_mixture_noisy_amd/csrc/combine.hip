@@ -101,24 +101,36 @@ hipError_t launch_importance(const int32_t* perm, const int32_t* offsets, const 
   return hipGetLastError();
 }
 
-// load[e] = sum_b part[b][e] in ascending b, or the row count of e.
-__global__ __launch_bounds__(256) void load_reduce_kernel(const float* part, int blocks,
-                                                         const int32_t* offsets, int E,
-                                                         float* load) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
+// load[e] = sum_b part[b][e] in a fixed order, or the row count of e.
+// Workgroup: 64 experts x 16 waves; wave w sums a contiguous range of b in
+// ascending order, then the 16 wave sums are added in wave order.
+__global__ __launch_bounds__(1024) void load_reduce_kernel(const float* part, int blocks,
+                                                          const int32_t* offsets, int E,
+                                                          float* load) {
+  __shared__ float red[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
   if (!part) {
-    load[e] = (float)(offsets[e + 1] - offsets[e]);
+    if (w == 0 && e < E) load[e] = (float)(offsets[e + 1] - offsets[e]);
     return;
   }
+  const int per = (blocks + 15) / 16;
+  const int b0 = w * per, b1 = min(blocks, b0 + per);
   float s = 0.f;
-  for (int b = 0; b < blocks; ++b) s += part[(int64_t)b * E + e];
-  load[e] = s;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) s += part[(int64_t)b * E + e];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && e < E) {
+    float t = 0.f;
+    for (int i = 0; i < 16; ++i) t += red[i][lane];
+    load[e] = t;
+  }
 }
 
 hipError_t launch_load_reduce(const float* part, int blocks, const int32_t* offsets, int E,
                               float* load, hipStream_t s) {
-  hipLaunchKernelGGL(load_reduce_kernel, dim3((E + 255) / 256), dim3(256), 0, s, part, blocks,
+  hipLaunchKernelGGL(load_reduce_kernel, dim3((E + 63) / 64), dim3(1024), 0, s, part, blocks,
                      offsets, E, load);
   return hipGetLastError();
 }

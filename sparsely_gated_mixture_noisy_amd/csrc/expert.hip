@@ -219,7 +219,10 @@ __global__ __launch_bounds__(256) void ffn2_f32_kernel(FfnArgs a) {
   ((float*)a.y_sorted)[i] = s;
 }
 
-int ffn_tile_rows(bool bf16, int, int, int) { return bf16 ? GM_BM : 1; }
+int ffn_tile_rows(bool bf16, int d, int h, int swiglu) {
+  if (!bf16) return 1;
+  return fused_ffn_supported(d, h, swiglu) ? fused_ffn_tile_rows() : GM_BM;
+}
 
 hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_t s) {
   if (a.A == 0) return hipSuccess;
@@ -230,6 +233,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
                        a);
     return hipGetLastError();
   }
+  if (fused_ffn_supported(a.d, a.h, swiglu)) return launch_fused_ffn(a, s);
   // upper bound of tiles: each non-empty expert adds at most one partial tile
   const int64_t qmax = (a.A + GM_BM - 1) / GM_BM + a.E;
   GemmArgs g1;

@@ -1,0 +1,333 @@
+// Fused ReLU expert FFN for d_model = 512: y = max(x W1^T, 0) W2^T per routed
+// row, the hidden activation never leaving the chip.
+//
+// The expert is the one-hidden-layer ReLU FFN of the MoE lesson page
+// ("MoE:稀疏门控混合专家", section 二: 512 -> 1024 -> 512).  With k*b/n rows
+// per expert (paper card, section 瓶颈: about 128 at 8192 tokens, 256 experts,
+// k = 4) the expert stage is bound by streaming the expert tables from HBM,
+// not by MFMA, so the kernel is organised to read each table byte once:
+//
+//   * one workgroup = one tile of at most 64 rows of one expert (an expert
+//     with m rows gets ceil(m/64) tiles of near-equal size); the tiles of an
+//     expert have consecutive ids that land on one XCD and are dispatched
+//     together, so they share the weight stream through that XCD's L2;
+//   * the tile's gathered input rows sit in LDS (64 x 512 bf16);
+//   * the hidden layer is produced 256 units at a time: each wave computes
+//     S = relu(X W1[64 units]^T) for all 64 rows (v_mfma_f32_32x32x16_bf16,
+//     W1 fragments streamed from global memory into a register ring), writes
+//     it as bf16 to LDS, then every wave accumulates Y[:, its 128 columns] +=
+//     S W2[cols, 256 units]^T with W2 fragments streamed the same way;
+//   * Y (64 x 512 fp32) stays in registers across the hidden chunks and is
+//     written once, as bf16, through LDS for coalesced 16-byte stores;
+//   * the expert tables can be repacked once (moe_pack_experts) into the
+//     exact order the waves consume their 16-byte fragments, so that every
+//     wave-wide load reads 1 KB of contiguous memory instead of 32-byte pieces
+//     of 32 rows.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int FZ_M = 64;    // rows per tile
+constexpr int FZ_H = 256;   // hidden units per chunk
+constexpr int FZ_THREADS = 256;
+constexpr int FZ_D = 512;   // d_model handled by this kernel
+
+struct FusedArgs {
+  const bf16_t* x;
+  const int32_t* perm;  // null: row p is x[p]
+  int k;
+  const int32_t* tiles;  // [E+1], tiles of FZ_M rows
+  const int32_t* desc;   // [tiles][3]: expert, first position, rows
+  int E, h;
+  const bf16_t* w1;      // [E][h][D]   (unpacked)
+  const bf16_t* w2;      // [E][D][h]   (unpacked)
+  const bf16_t* wp;      // packed tables, or null
+  bf16_t* y;             // [A][D]
+};
+
+// The weight stream of one wave.  For hidden chunk hc (FZ_H units), wave w
+// consumes NE 16-byte fragments per lane: entries n < 2*(D/16) are W1
+// fragments (k-step n/2, 32-unit block n%2 of the wave's 64 units), the rest
+// W2 fragments (k-step (n-N1)/(D/128), 32-column block (n-N1)%(D/128) of the
+// wave's D/4 output columns).  frag_src gives the element offset of a
+// fragment inside expert e's unpacked tables (table 0: W1 [h][D], table 1:
+// W2 [D][h]); the packed layout stores the fragments contiguously in
+// consumption order: [e][hc][w][n][lane][8 elements].
+template <int D>
+struct Stream {
+  static constexpr int KS1 = D / 16, NT2 = D / 128, KS2 = FZ_H / 16;
+  static constexpr int N1 = 2 * KS1, NE = N1 + NT2 * KS2;
+  static __host__ __device__ inline int64_t src(int h, int hc, int w, int n, int lane,
+                                                int* table) {
+    const int fr = lane & 31, fk = (lane >> 5) * 8;
+    if (n < N1) {
+      const int ks = n >> 1, nt = n & 1;
+      *table = 0;
+      return (int64_t)(hc * FZ_H + w * 64 + nt * 32 + fr) * D + ks * 16 + fk;
+    }
+    const int mm = n - N1, ks = mm / NT2, j = mm % NT2;
+    *table = 1;
+    return (int64_t)(w * (D / 4) + j * 32 + fr) * h + hc * FZ_H + ks * 16 + fk;
+  }
+  static __host__ __device__ inline int64_t packed(int h, int e, int hc, int w, int n, int lane) {
+    const int nch = h / FZ_H;
+    return ((((int64_t)e * nch + hc) * 4 + w) * NE + n) * 512 + lane * 8;
+  }
+};
+
+template <int D, bool PACKED>
+__global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs a) {
+  constexpr int XLD = D + 8;     // LDS row stride of the input tile (elements)
+  constexpr int SLD = FZ_H + 8;  // LDS row stride of the hidden tile
+  constexpr int NW = D / 4;      // output columns per wave
+  constexpr int NT2 = NW / 32;   // 32-wide output tiles per wave
+  constexpr int KS1 = D / 16;    // k-steps of the first layer
+  constexpr int KS2 = FZ_H / 16; // k-steps of the second layer per chunk
+  static_assert(NT2 == Stream<D>::NT2 && KS1 == Stream<D>::KS1, "stream shape");
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+  bf16_t* Xs = lds;
+  bf16_t* Ss = lds + FZ_M * XLD;
+  __shared__ int s_info[3];
+  __shared__ int s_src[FZ_M];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) {
+    const int Q = a.tiles[a.E];
+    const int per = (Q + 7) / 8;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int q = xcd * per + slot;
+    int e = -1, p0 = 0, m = 0;
+    if (slot < per && q < Q) {
+      e = a.desc[3 * q];
+      p0 = a.desc[3 * q + 1];
+      m = a.desc[3 * q + 2];
+    }
+    s_info[0] = e;
+    s_info[1] = p0;
+    s_info[2] = m;
+  }
+  __syncthreads();
+  const int e = s_info[0];
+  if (e < 0) return;
+  const int p0 = s_info[1], m = s_info[2];
+  if (tid < FZ_M) {
+    const int p = p0 + min(tid, m - 1);
+    s_src[tid] = a.perm ? a.perm[p] / a.k : p;
+  }
+  __syncthreads();
+
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  const int nchunks = a.h / FZ_H;
+  using S = Stream<D>;
+  constexpr int N1 = S::N1, NE = S::NE, RING = 32;
+  static_assert(NE % RING == 0, "stream length must be a multiple of the ring");
+  // A ring of RING registers keeps RING weight loads in flight without
+  // draining between the two layers or between chunks: consuming entry n
+  // issues entry n + RING (of this chunk or the next one).
+  const bf16_t* W1e = a.w1 + (int64_t)e * a.h * D;
+  const bf16_t* W2e = a.w2 + (int64_t)e * D * a.h;
+  auto frag_ptr = [&](int hc, int n) -> const bf16_t* {
+    if constexpr (PACKED) {
+      return a.wp + S::packed(a.h, e, hc, w, n, lane);
+    } else {
+      int t;
+      const int64_t o = S::src(a.h, hc, w, n, lane, &t);
+      return (t == 0 ? W1e : W2e) + o;
+    }
+  };
+
+  // gathered input rows (rows past m are zero) and the first RING weight
+  // fragments are requested together
+  u32x4 xv[FZ_M * CPR / FZ_THREADS];
+#pragma unroll
+  for (int i = 0; i < FZ_M * CPR / FZ_THREADS; ++i) {
+    const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
+    xv[i] = r < m ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)s_src[r] * D + cc)
+                  : u32x4{0u, 0u, 0u, 0u};
+  }
+  u32x4 ring[RING];
+#pragma unroll
+  for (int i = 0; i < RING; ++i) ring[i] = *reinterpret_cast<const u32x4*>(frag_ptr(0, i));
+#pragma unroll
+  for (int i = 0; i < FZ_M * CPR / FZ_THREADS; ++i) {
+    const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
+    *reinterpret_cast<u32x4*>(Xs + r * XLD + cc) = xv[i];
+  }
+
+  f32x16 acc[2][NT2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NT2; ++j) acc[i][j] = f32x16{};
+
+  __syncthreads();
+  for (int hc = 0; hc < nchunks; ++hc) {
+    const bool more = hc + 1 < nchunks;
+    // ---- first layer: S[:, w*64 .. +64) = relu(X W1[units]^T) ----
+    f32x16 sa[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sa[i][j] = f32x16{};
+    // input fragments are read from LDS one k-step ahead of their MFMAs
+    bf16x8 xa0 = *reinterpret_cast<const bf16x8*>(Xs + fr * XLD + fk);
+    bf16x8 xa1 = *reinterpret_cast<const bf16x8*>(Xs + (32 + fr) * XLD + fk);
+#pragma unroll
+    for (int ks = 0; ks < KS1; ++ks) {
+      const int n0 = 2 * ks;
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, ring[n0 % RING]);
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, ring[(n0 + 1) % RING]);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int nn = n0 + q + RING;
+        if (nn < NE) ring[(n0 + q) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc, nn));
+        else if (more) ring[(n0 + q) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc + 1, nn - NE));
+      }
+      const bf16x8 a0 = xa0, a1 = xa1;
+      if (ks + 1 < KS1) {
+        xa0 = *reinterpret_cast<const bf16x8*>(Xs + fr * XLD + (ks + 1) * 16 + fk);
+        xa1 = *reinterpret_cast<const bf16x8*>(Xs + (32 + fr) * XLD + (ks + 1) * 16 + fk);
+      }
+      sa[0][0] = mfma32(a0, b0, sa[0][0]);
+      sa[0][1] = mfma32(a0, b1, sa[0][1]);
+      sa[1][0] = mfma32(a1, b0, sa[1][0]);
+      sa[1][1] = mfma32(a1, b1, sa[1][1]);
+    }
+    // relu, bf16, into the hidden tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = w * 64 + j * 32 + fr;
+          Ss[row * SLD + col] = f32_to_bf16(fmaxf(sa[i][j][r], 0.f));
+        }
+    __syncthreads();
+    // ---- second layer: Y[:, w*NW .. +NW) += S W2[cols, units]^T ----
+    bf16x8 sa0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + fk);
+    bf16x8 sa1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + fk);
+#pragma unroll
+    for (int ks = 0; ks < KS2; ++ks) {
+      const int n0 = N1 + ks * NT2;
+      bf16x8 b[NT2];
+#pragma unroll
+      for (int j = 0; j < NT2; ++j) {
+        b[j] = __builtin_bit_cast(bf16x8, ring[(n0 + j) % RING]);
+        const int nn = n0 + j + RING;
+        if (nn < NE) ring[(n0 + j) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc, nn));
+        else if (more) ring[(n0 + j) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc + 1, nn - NE));
+      }
+      const bf16x8 a0 = sa0, a1 = sa1;
+      if (ks + 1 < KS2) {
+        sa0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + (ks + 1) * 16 + fk);
+        sa1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + (ks + 1) * 16 + fk);
+      }
+#pragma unroll
+      for (int j = 0; j < NT2; ++j) acc[0][j] = mfma32(a0, b[j], acc[0][j]);
+#pragma unroll
+      for (int j = 0; j < NT2; ++j) acc[1][j] = mfma32(a1, b[j], acc[1][j]);
+    }
+    __syncthreads();
+  }
+
+  // Y -> bf16 -> LDS (reusing the input tile) -> coalesced stores
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NT2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = w * NW + j * 32 + fr;
+        Xs[row * XLD + col] = f32_to_bf16(acc[i][j][r]);
+      }
+  __syncthreads();
+  for (int c = tid; c < m * CPR; c += FZ_THREADS) {
+    const int r = c / CPR, cc = (c % CPR) * 8;
+    *reinterpret_cast<u32x4*>(a.y + (int64_t)(p0 + r) * D + cc) =
+        *reinterpret_cast<const u32x4*>(Xs + r * XLD + cc);
+  }
+}
+
+bool fused_ffn_supported(int d, int h, int swiglu) {
+  return !swiglu && d == FZ_D && h % FZ_H == 0;
+}
+
+int fused_ffn_tile_rows() { return FZ_M; }
+
+size_t fused_packed_bytes(int E, int d, int h) {
+  return sizeof(bf16_t) * 2 * (size_t)E * d * h;
+}
+
+// packed[e][hc][w][n][lane] <- the fragment frag_src names, 16 bytes a thread
+template <int D>
+__global__ __launch_bounds__(256) void pack_experts_kernel(const bf16_t* w1, const bf16_t* w2,
+                                                           int E, int h, bf16_t* out) {
+  using S = Stream<D>;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // fragment-lane index
+  const int nch = h / FZ_H;
+  const int64_t total = (int64_t)E * nch * 4 * S::NE * 64;
+  if (i >= total) return;
+  const int lane = (int)(i % 64);
+  int64_t r = i / 64;
+  const int n = (int)(r % S::NE);
+  r /= S::NE;
+  const int w = (int)(r % 4);
+  r /= 4;
+  const int hc = (int)(r % nch);
+  const int e = (int)(r / nch);
+  int t;
+  const int64_t o = S::src(h, hc, w, n, lane, &t);
+  const bf16_t* src = (t == 0 ? w1 : w2) + (int64_t)e * h * D + o;
+  *reinterpret_cast<u32x4*>(out + S::packed(h, e, hc, w, n, lane)) =
+      *reinterpret_cast<const u32x4*>(src);
+}
+
+hipError_t launch_pack_experts(const void* w1, const void* w2, int E, int d, int h, void* out,
+                               hipStream_t s) {
+  const int64_t total = (int64_t)E * (h / FZ_H) * 4 * Stream<FZ_D>::NE * 64;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_experts_kernel<FZ_D>, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, s, (const bf16_t*)w1, (const bf16_t*)w2, E, h, (bf16_t*)out);
+  return hipGetLastError();
+}
+
+template <bool PACKED>
+static hipError_t launch_fused_t(const FusedArgs& a, int64_t A, hipStream_t s) {
+  constexpr size_t lds = sizeof(bf16_t) * (size_t)FZ_M * ((FZ_D + 8) + (FZ_H + 8));
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t err = hipFuncSetAttribute((const void*)ffn_relu_fused_kernel<FZ_D, PACKED>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    attr_done = true;
+  }
+  // upper bound of tiles, rounded to whole XCD rows
+  int64_t qmax = (A + FZ_M - 1) / FZ_M + a.E;
+  qmax = (qmax + 7) / 8 * 8;
+  hipLaunchKernelGGL((ffn_relu_fused_kernel<FZ_D, PACKED>), dim3((unsigned)qmax),
+                     dim3(FZ_THREADS), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_ffn(const FfnArgs& f, hipStream_t s) {
+  FusedArgs a;
+  a.x = (const bf16_t*)f.x;
+  a.perm = f.perm;
+  a.k = f.k;
+  a.tiles = f.tiles;
+  a.desc = f.desc;
+  a.E = f.E;
+  a.h = f.h;
+  a.w1 = (const bf16_t*)f.w1;
+  a.w2 = (const bf16_t*)f.w2;
+  a.wp = (const bf16_t*)f.wpacked;
+  a.y = (bf16_t*)f.y_sorted;
+  return a.wp ? launch_fused_t<true>(a, f.A, s) : launch_fused_t<false>(a, f.A, s);
+}
+
+}  // namespace moe

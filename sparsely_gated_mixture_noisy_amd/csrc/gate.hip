@@ -103,6 +103,78 @@ struct Proj<float> {
   }
 };
 
+// bf16 projection with the 32-row input tile in LDS (row stride xld): the
+// A operand comes from LDS, the table rows stream from global memory through
+// a 16-deep register ring so that many loads are in flight per wave.
+__device__ __forceinline__ void proj_lds(const bf16_t* Xs, int xld, int d, const ChunkSpec& cs,
+                                         ProjTile* P) {
+  constexpr int RING = 16;
+  const int lane = threadIdx.x & 63, b = threadIdx.x >> 6;
+  const int c = lane & 31, kh = (lane >> 5) * 8;
+  const BlockCols bc = block_cols(b, cs.wg, cs.wn, cs.noisy, cs.tab_row0, cs.cb, cs.nvalid);
+  const int trow = c < bc.valid ? bc.row0 + c : bc.safe;
+  const bf16_t* wp = (const bf16_t*)bc.tab + (int64_t)trow * d + kh;
+  const bf16_t* xp = Xs + c * xld + kh;
+  const int KS = d / 16;
+  u32x4 rb[RING];
+#pragma unroll
+  for (int i = 0; i < RING; ++i)
+    rb[i] = i < KS ? *reinterpret_cast<const u32x4*>(wp + i * 16) : u32x4{0u, 0u, 0u, 0u};
+  f32x16 acc = {};
+  for (int g = 0; g < KS; g += RING) {
+#pragma unroll
+    for (int i = 0; i < RING; ++i) {
+      const int ks = g + i;
+      if (ks < KS) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, rb[i]);
+        if (ks + RING < KS) rb[i] = *reinterpret_cast<const u32x4*>(wp + (ks + RING) * 16);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(xp + ks * 16);
+        acc = mfma32(av, bv, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    P[b][r][c] = acc[i];
+  }
+}
+
+// Where a tile's input rows come from: global memory (rows[] tokens) or, for
+// bf16 with d <= 1024, an LDS copy Xs of the 32 rows.
+template <typename T>
+struct TileX {
+  const T* x;
+  const int* rows;
+  const bf16_t* Xs;  // null: read x directly
+  int xld;
+};
+
+template <typename T>
+__device__ __forceinline__ void project(const TileX<T>& tx, int d, const ChunkSpec& cs,
+                                        ProjTile* P) {
+  if constexpr (sizeof(T) == 2) {
+    if (tx.Xs) {
+      proj_lds(tx.Xs, tx.xld, d, cs, P);
+      return;
+    }
+  }
+  Proj<T>::run(tx.x, d, tx.rows, cs, P);
+}
+
+// Copy the 32 input rows of a tile to LDS (bf16 only, d % 8 == 0).
+__device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* rows, bf16_t* Xs,
+                                            int xld) {
+  const int cpr = d / 8;
+  for (int c = threadIdx.x; c < GATE_ROWS * cpr; c += GATE_THREADS) {
+    const int r = c / cpr, cc = (c % cpr) * 8;
+    *reinterpret_cast<u32x4*>(Xs + r * xld + cc) =
+        *reinterpret_cast<const u32x4*>(x + (int64_t)rows[r] * d + cc);
+  }
+}
+
+constexpr int GATE_XLDS_MAX_D = 1024;  // input tile in LDS up to this d_model
+
 // Running top-K1 list of one lane (best first).
 template <int K1>
 struct TopList {
@@ -152,11 +224,13 @@ struct TopList {
 // Scores of one 32-row tile against experts [0, E) of a table block, merged
 // into per-lane top-K1 lists.  Table row of expert e is tab_row0 + e; the
 // noise draw of (tile row r, expert e) is erow[e] with erow the row's eps
-// pointer (unused when !noisy).
+// pointer (unused when !noisy).  With keep != null the clean score and the
+// noise scale of every (row, expert) are also kept: keep[r*E+e] and
+// keep[32*E + r*E+e].
 template <typename T, int K1>
-__device__ void score_tile(const T* __restrict__ x, int d, const int* rows, const void* wg,
-                           const void* wn, const float* __restrict__ bias, int tab_row0, int E,
-                           const float* erow, bool noisy, ProjTile* P, TopList<K1>& L) {
+__device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void* wn,
+                           const float* __restrict__ bias, int tab_row0, int E, const float* erow,
+                           bool noisy, ProjTile* P, TopList<K1>& L, float* keep) {
   const int tid = threadIdx.x;
   const int row = tid >> 3, sub = tid & 7;
   const int ce = noisy ? 64 : 128;  // experts per chunk
@@ -164,7 +238,7 @@ __device__ void score_tile(const T* __restrict__ x, int d, const int* rows, cons
     const int nvalid = min(ce, E - cb);
     const ChunkSpec cs{wg, wn, noisy, tab_row0, cb, nvalid};
     __syncthreads();  // P is free
-    Proj<T>::run(x, d, rows, cs, P);
+    project<T>(tx, d, cs, P);
     __syncthreads();
     for (int j = sub; j < nvalid; j += 8) {
       const int e = cb + j;
@@ -172,12 +246,24 @@ __device__ void score_tile(const T* __restrict__ x, int d, const int* rows, cons
       if (bias) c += bias[tab_row0 + e];
       float h = c;
       if (noisy) {
-        float raw = P[2 + (j >> 5)][row][j & 31];
-        h = c + erow[e] * softplus_f(raw);
+        const float sp = softplus_f(P[2 + (j >> 5)][row][j & 31]);
+        h = c + erow[e] * sp;
+        if (keep) {
+          keep[row * E + e] = c;
+          keep[GATE_ROWS * E + row * E + e] = sp;
+        }
       }
       L.insert(h, e);
     }
   }
+}
+
+// One row's load term of expert e: Phi((clean - theta) / sp), theta the k-th
+// largest noisy score among the other experts.
+__device__ __forceinline__ float load_term(float clean, float sp, bool kept, float kth,
+                                           float k1th) {
+  const float th = kept ? k1th : kth;
+  return normal_cdf_f((clean - th) / sp);
 }
 
 // Turn the merged top-(k+1) of a row (rank order) into the kept experts in
@@ -225,30 +311,40 @@ __device__ __forceinline__ void kept_gates(const float* ov, const int* oe, int k
 }
 
 // ---------------------------------------------------------------------------
-// Flat gate: tile = 32 consecutive tokens.
+// Flat gate: tile = 32 consecutive tokens.  With a.part set (noisy gate,
+// E <= 256) the kernel also produces the tile's row of smooth-load partial
+// sums, from the clean scores and noise scales it kept in LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int K1>
 __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a) {
   __shared__ ProjTile P[4];
   __shared__ int rows[GATE_ROWS];
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
   if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
   __syncthreads();
+  const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
+  const int xld = a.d + 8;
+  bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
+  float* keep = a.part ? reinterpret_cast<float*>(dyn + (xl ? sizeof(bf16_t) * GATE_ROWS * xld : 0))
+                       : nullptr;
+  if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
   const int row = tid >> 3;
   const int64_t t = t0 + row;
-  const float* erow = a.eps ? a.eps + (int64_t)rows[row] * a.E : nullptr;
+  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
+  const float* erow = noisy ? a.eps + (int64_t)rows[row] * a.E : nullptr;
   TopList<K1> L;
   L.init();
-  score_tile<T, K1>((const T*)a.x, a.d, rows, a.w_gate, a.w_noise, a.bias, 0, a.E, erow,
-                    a.eps != nullptr && a.w_noise != nullptr, P, L);
+  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, a.bias, 0, a.E, erow, noisy, P, L, keep);
   float ov[K1];
   int oe[K1];
   L.merge8(ov, oe);
+  int ke[K1];
+  float kg[K1], kth, k1th;
+  kept_gates<K1>(ov, oe, a.k, a.E, ke, kg, &kth, &k1th);
   if ((tid & 7) == 0 && t < a.T) {
-    int ke[K1];
-    float kg[K1], kth, k1th;
-    kept_gates<K1>(ov, oe, a.k, a.E, ke, kg, &kth, &k1th);
 #pragma unroll
     for (int j = 0; j < K1; ++j) {
       if (j < a.k) {
@@ -259,6 +355,23 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
     if (a.thr) {
       a.thr[2 * t] = kth;
       a.thr[2 * t + 1] = k1th;
+    }
+  }
+  if (keep) {
+    // this row's load terms, in place of the clean scores (0 past the batch)
+    for (int e = tid & 7; e < a.E; e += 8) {
+      bool in = false;
+#pragma unroll
+      for (int j = 0; j < K1; ++j) in |= (j < a.k && ke[j] == e);
+      const float v = load_term(keep[row * a.E + e], keep[GATE_ROWS * a.E + row * a.E + e], in,
+                                kth, k1th);
+      keep[row * a.E + e] = t < a.T ? v : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < a.E; e += GATE_THREADS) {
+      float sum = 0.f;
+      for (int r = 0; r < GATE_ROWS; ++r) sum += keep[r * a.E + e];
+      a.part[(int64_t)blockIdx.x * a.E + e] = sum;
     }
   }
 }
@@ -275,6 +388,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
   __shared__ int rows[GATE_ROWS];
   __shared__ int asg[GATE_ROWS];
   __shared__ int s_g, s_p0, s_n;
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x;
   if (tid == 0) {
     int q = blockIdx.x, g = -1;
@@ -297,13 +411,19 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
     rows[tid] = as / a.kg;
   }
   __syncthreads();
+  const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
+  const int xld = a.d + 8;
+  bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
+  if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
   const int row = tid >> 3;
   const int Eg = a.Eg;
-  const float* erow = a.eps ? a.eps + ((int64_t)rows[row] * a.G + g) * Eg : nullptr;
+  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
+  const float* erow = noisy ? a.eps + ((int64_t)rows[row] * a.G + g) * Eg : nullptr;
   TopList<K1> L;
   L.init();
-  score_tile<T, K1>((const T*)a.x, a.d, rows, a.w_gate, a.w_noise, nullptr, g * Eg, Eg, erow,
-                    a.eps != nullptr && a.w_noise != nullptr, P, L);
+  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, nullptr, g * Eg, Eg, erow, noisy, P, L,
+                    nullptr);
   float ov[K1];
   int oe[K1];
   L.merge8(ov, oe);
@@ -327,96 +447,123 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Smooth load estimate (flat noisy gate).  Each workgroup covers `tiles`
-// consecutive 32-token tiles and accumulates, per expert e,
-//   sum_t Phi((clean[t,e] - theta[t,e]) / softplus(raw[t,e]))
-// with theta = thr[t][1] if e is kept by t, else thr[t][0].  The per-expert
-// partial sums of the workgroup go to part[blockIdx.x][E] (summed over rows
-// in ascending order), reduced across workgroups in a fixed order later.
+// Smooth load estimate (flat noisy gate), recomputing the projections from
+// the gate's thresholds.  Workgroup b covers tokens [32b, 32b+32) and writes
+//   part[b][e] = sum over its rows (ascending) of
+//                Phi((clean[t,e] - theta[t,e]) / softplus(raw[t,e]))
+// with theta = thr[t][1] if e is kept by t, else thr[t][0]: the same terms,
+// in the same order, as the gate kernel's fused variant.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) {
   __shared__ ProjTile P[4];
   __shared__ int rows[GATE_ROWS];
   __shared__ float Q[GATE_ROWS][65];
-  extern __shared__ float acc[];  // [E]
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x;
   const int row = tid >> 3, sub = tid & 7;
-  for (int e = tid; e < a.E; e += GATE_THREADS) acc[e] = 0.f;
-  for (int tt = 0; tt < a.tiles; ++tt) {
-    const int64_t t0 = ((int64_t)blockIdx.x * a.tiles + tt) * GATE_ROWS;
-    if (t0 >= a.T) break;
-    __syncthreads();
-    if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
-    __syncthreads();
-    const int64_t t = t0 + row;
-    const bool tv = t < a.T;
-    int kept[8];
+  const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
+  __syncthreads();
+  const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
+  const int xld = a.d + 8;
+  bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
+  if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
+  const int64_t t = t0 + row;
+  const bool tv = t < a.T;
+  int kept[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kept[j] = (j < a.k) ? a.idx[(int64_t)rows[row] * a.k + j] : -1;
-    const float th0 = a.thr[2 * (int64_t)rows[row]], th1 = a.thr[2 * (int64_t)rows[row] + 1];
-    for (int cb = 0; cb < a.E; cb += 64) {
-      const int nvalid = min(64, a.E - cb);
-      const ChunkSpec cs{a.w_gate, a.w_noise, true, 0, cb, nvalid};
-      __syncthreads();
-      Proj<T>::run((const T*)a.x, a.d, rows, cs, P);
-      __syncthreads();
-      for (int j = sub; j < 64; j += 8) {
-        float p = 0.f;
-        if (j < nvalid && tv) {
-          const int e = cb + j;
-          float c = P[j >> 5][row][j & 31];
-          if (a.bias) c += a.bias[e];
-          float sp = softplus_f(P[2 + (j >> 5)][row][j & 31]);
-          bool in = false;
+  for (int j = 0; j < 8; ++j) kept[j] = (j < a.k) ? a.idx[(int64_t)rows[row] * a.k + j] : -1;
+  const float th0 = a.thr[2 * (int64_t)rows[row]], th1 = a.thr[2 * (int64_t)rows[row] + 1];
+  for (int cb = 0; cb < a.E; cb += 64) {
+    const int nvalid = min(64, a.E - cb);
+    const ChunkSpec cs{a.w_gate, a.w_noise, true, 0, cb, nvalid};
+    __syncthreads();
+    project<T>(tx, a.d, cs, P);
+    __syncthreads();
+    for (int j = sub; j < 64; j += 8) {
+      float p = 0.f;
+      if (j < nvalid && tv) {
+        const int e = cb + j;
+        float c = P[j >> 5][row][j & 31];
+        if (a.bias) c += a.bias[e];
+        const float sp = softplus_f(P[2 + (j >> 5)][row][j & 31]);
+        bool in = false;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) in |= (kept[q] == e);
-          float th = in ? th1 : th0;
-          p = normal_cdf_f((c - th) / sp);
-        }
-        Q[row][j] = p;
+        for (int q = 0; q < 8; ++q) in |= (kept[q] == e);
+        p = load_term(c, sp, in, th0, th1);
       }
-      __syncthreads();
-      if (tid < 64 && tid < nvalid) {
-        float s = acc[cb + tid];
-        for (int r = 0; r < GATE_ROWS; ++r) s += Q[r][tid];
-        acc[cb + tid] = s;
-      }
+      Q[row][j] = p;
+    }
+    __syncthreads();
+    if (tid < nvalid) {
+      float sum = 0.f;
+      for (int r = 0; r < GATE_ROWS; ++r) sum += Q[r][tid];
+      a.part[(int64_t)blockIdx.x * a.E + cb + tid] = sum;
     }
   }
-  __syncthreads();
-  for (int e = tid; e < a.E; e += GATE_THREADS) a.part[(int64_t)blockIdx.x * a.E + e] = acc[e];
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <typename T>
-static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
+static size_t xtile_bytes(bool bf16, int d) {
+  return (bf16 && d <= GATE_XLDS_MAX_D) ? sizeof(bf16_t) * GATE_ROWS * (size_t)(d + 8) : 0;
+}
+
+// Raise a kernel's dynamic LDS limit when needed; `done` caches the largest
+// size already granted to that kernel.
+template <typename K>
+static hipError_t set_lds(K kernel, size_t bytes, size_t* done) {
+  if (bytes <= 65536 || bytes <= *done) return hipSuccess;
+  hipError_t err = hipFuncSetAttribute((const void*)kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (err == hipSuccess) *done = bytes;
+  return err;
+}
+
+template <typename T, int K1>
+static hipError_t launch_flat_k(const GateFlatArgs& a, size_t sh, hipStream_t s) {
+  static size_t granted = 0;
+  hipError_t err = set_lds(gate_flat_kernel<T, K1>, sh, &granted);
+  if (err != hipSuccess) return err;
   dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
-  if (a.k + 1 <= 3)
-    hipLaunchKernelGGL((gate_flat_kernel<T, 3>), grid, dim3(GATE_THREADS), 0, s, a);
-  else if (a.k + 1 <= 5)
-    hipLaunchKernelGGL((gate_flat_kernel<T, 5>), grid, dim3(GATE_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((gate_flat_kernel<T, 9>), grid, dim3(GATE_THREADS), 0, s, a);
+  hipLaunchKernelGGL((gate_flat_kernel<T, K1>), grid, dim3(GATE_THREADS), sh, s, a);
   return hipGetLastError();
 }
+
+template <typename T>
+static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
+  size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
+  if (a.part) sh += sizeof(float) * 2 * GATE_ROWS * (size_t)a.E;
+  if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, sh, s);
+  if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, sh, s);
+  return launch_flat_k<T, 9>(a, sh, s);
+}
+
+bool gate_fuses_load(int E) { return E <= GATE_FUSED_LOAD_MAX_E; }
 
 hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   return bf16 ? launch_flat_t<bf16_t>(a, s) : launch_flat_t<float>(a, s);
 }
 
+template <typename T, int K1>
+static hipError_t launch_group_k(const GateGroupArgs& a, int grid, size_t sh, hipStream_t s) {
+  static size_t granted = 0;
+  hipError_t err = set_lds(gate_group_kernel<T, K1>, sh, &granted);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((gate_group_kernel<T, K1>), dim3(grid), dim3(GATE_THREADS), sh, s, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_group_t(const GateGroupArgs& a, int grid, hipStream_t s) {
-  if (a.kpg + 1 <= 3)
-    hipLaunchKernelGGL((gate_group_kernel<T, 3>), dim3(grid), dim3(GATE_THREADS), 0, s, a);
-  else if (a.kpg + 1 <= 5)
-    hipLaunchKernelGGL((gate_group_kernel<T, 5>), dim3(grid), dim3(GATE_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((gate_group_kernel<T, 9>), dim3(grid), dim3(GATE_THREADS), 0, s, a);
-  return hipGetLastError();
+  const size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
+  if (a.kpg + 1 <= 3) return launch_group_k<T, 3>(a, grid, sh, s);
+  if (a.kpg + 1 <= 5) return launch_group_k<T, 5>(a, grid, sh, s);
+  return launch_group_k<T, 9>(a, grid, sh, s);
 }
 
 hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStream_t s) {
@@ -424,20 +571,20 @@ hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStr
   return bf16 ? launch_group_t<bf16_t>(a, grid, s) : launch_group_t<float>(a, grid, s);
 }
 
-int load_partial_blocks(int64_t T, int* tiles_per_block) {
-  int64_t tiles = (T + GATE_ROWS - 1) / GATE_ROWS;
-  int per = (int)std::max<int64_t>(1, (tiles + 511) / 512);  // at most ~512 partial rows
-  *tiles_per_block = per;
-  return (int)((tiles + per - 1) / per);
-}
+int load_partial_blocks(int64_t T) { return (int)((T + GATE_ROWS - 1) / GATE_ROWS); }
 
-hipError_t launch_load_partial(const LoadArgs& a, int blocks, bool bf16, hipStream_t s) {
+hipError_t launch_load_partial(const LoadArgs& a, bool bf16, hipStream_t s) {
+  const int blocks = load_partial_blocks(a.T);
   if (blocks == 0) return hipSuccess;
-  size_t sh = sizeof(float) * (size_t)a.E;
-  if (bf16)
+  const size_t sh = xtile_bytes(bf16, a.d);
+  if (bf16) {
+    static size_t granted = 0;
+    hipError_t err = set_lds(load_partial_kernel<bf16_t>, sh, &granted);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL((load_partial_kernel<bf16_t>), dim3(blocks), dim3(GATE_THREADS), sh, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((load_partial_kernel<float>), dim3(blocks), dim3(GATE_THREADS), sh, s, a);
+  }
   return hipGetLastError();
 }
 

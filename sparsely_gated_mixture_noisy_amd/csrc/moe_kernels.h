@@ -17,8 +17,11 @@ struct GateFlatArgs {
   int32_t* idx;   // [T][k]
   float* gate;    // [T][k]
   float* thr;     // [T][2] or null
+  float* part;    // [ceil(T/32)][E] smooth-load partials (noisy, E <= 256) or null
 };
 hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s);
+constexpr int GATE_FUSED_LOAD_MAX_E = 256;
+bool gate_fuses_load(int E);
 
 struct GateGroupArgs {
   const void* x;
@@ -44,11 +47,10 @@ struct LoadArgs {
   const float* thr;    // [T][2]
   int64_t T;
   int d, E, k;
-  int tiles;           // 32-row tiles per workgroup
-  float* part;         // [blocks][E]
+  float* part;         // [ceil(T/32)][E]
 };
-int load_partial_blocks(int64_t T, int* tiles_per_block);
-hipError_t launch_load_partial(const LoadArgs& a, int blocks, bool bf16, hipStream_t s);
+int load_partial_blocks(int64_t T);
+hipError_t launch_load_partial(const LoadArgs& a, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- route ----
 constexpr int ROUTE_BLOCK_TOKENS = 64;
@@ -70,9 +72,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, int k, int64_t A, int d,
                               int elem_bytes, void* out, hipStream_t s);
 
-// tiles[e] = sum_{e' < e} ceil(count_{e'} / rows), tiles[E] = total
+// tiles[e] = sum_{e' < e} ceil(count_{e'} / rows), tiles[E] = total; with
+// desc != null also desc[q] = {expert, first position, rows} for every tile,
+// an expert's rows split into near-equal tiles
 hipError_t launch_tile_map(const int32_t* offsets, int E, int rows, int32_t* tiles,
-                           hipStream_t s);
+                           int32_t* desc, hipStream_t s);
 
 // --------------------------------------------------------------- experts ---
 struct FfnArgs {
@@ -81,6 +85,7 @@ struct FfnArgs {
   int k;
   const int32_t* offsets; // [E+1]
   const int32_t* tiles;   // [E+1] tile map for the kernel's row tile
+  const int32_t* desc;    // [tiles][3] tile descriptors (fused path)
   int E, d, h;
   const void* w1;         // [E][h][d]
   const void* w3;         // [E][h][d] or null
@@ -88,8 +93,16 @@ struct FfnArgs {
   void* hid;              // [A][h] workspace (unfused paths)
   void* y_sorted;         // [A][d]
   int64_t A;
+  const void* wpacked;    // packed expert tables (fused path) or null
 };
 int ffn_tile_rows(bool bf16, int d, int h, int swiglu);
+// fused ReLU path (hidden layer kept on chip), d_model 512
+bool fused_ffn_supported(int d, int h, int swiglu);
+int fused_ffn_tile_rows();
+hipError_t launch_fused_ffn(const FfnArgs& a, hipStream_t s);
+size_t fused_packed_bytes(int E, int d, int h);
+hipError_t launch_pack_experts(const void* w1, const void* w2, int E, int d, int h, void* out,
+                               hipStream_t s);
 hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_t s);
 
 // -------------------------------------------------------- combine / stats --

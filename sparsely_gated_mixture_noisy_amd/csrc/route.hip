@@ -172,10 +172,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// tiles[e] = exclusive prefix of ceil(count_e / rows); one workgroup.
+// tiles[e] = exclusive prefix of ceil(count_e / rows); one workgroup.  With
+// desc, tile tiles[e] + i of expert e (count m_e, n_e tiles) covers
+// floor(m_e / n_e) rows, plus one for the first m_e % n_e tiles.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(SCAN_THREADS) void tile_map_kernel(const int32_t* offsets, int E,
-                                                                int rows, int32_t* tiles) {
+                                                                int rows, int32_t* tiles,
+                                                                int32_t* desc) {
   const int tid = threadIdx.x;
   int carry = 0;
   for (int c0 = 0; c0 < E; c0 += 4 * SCAN_THREADS) {
@@ -191,7 +194,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void tile_map_kernel(const int32_t* o
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int e = c0 + 4 * tid + j;
-      if (e < E) tiles[e] = run;
+      if (e < E) {
+        tiles[e] = run;
+        if (desc && v[j] > 0) {
+          const int m = offsets[e + 1] - offsets[e], base = m / v[j], rem = m % v[j];
+          for (int i = 0; i < v[j]; ++i) {
+            int32_t* d = desc + 3 * (int64_t)(run + i);
+            d[0] = e;
+            d[1] = offsets[e] + i * base + min(i, rem);
+            d[2] = base + (i < rem ? 1 : 0);
+          }
+        }
+      }
       run += v[j];
     }
     carry += total;
@@ -200,8 +214,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void tile_map_kernel(const int32_t* o
 }
 
 hipError_t launch_tile_map(const int32_t* offsets, int E, int rows, int32_t* tiles,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, offsets, E, rows, tiles);
+                           int32_t* desc, hipStream_t s) {
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, offsets, E, rows, tiles,
+                     desc);
   return hipGetLastError();
 }
 

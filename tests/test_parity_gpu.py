@@ -219,3 +219,31 @@ def test_route_x_sorted_gather():
     y2 = L.expert_ffn(cfg, xs, None, offsets, inp, tokens=cfg.tokens)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("tokens", [1000, 8192])
+def test_packed_experts_match_unpacked_bitwise(tokens):
+    """The repacked expert tables hold the same values in stream order: the
+    expert stage gives bitwise the result of the unpacked tables, and the
+    whole layer stays within the oracle's tolerance."""
+    cfg = CONFIGS["flat256"].replace(tokens=tokens)
+    inp = make_inputs(cfg, seed=5, device="cuda")
+    packed = L.pack_experts(cfg, inp)
+    assert packed is not None and packed.numel() * 2 == L.packed_experts_size(cfg)
+    idx, gate, _ = L.gate(cfg, inp["x"], inp, inp)
+    counts, offsets, perm, inv, _ = L.route(cfg, idx)
+    y_plain = L.expert_ffn(cfg, inp["x"], perm, offsets, inp)
+    only_packed = {"w_packed": packed}
+    y_packed = L.expert_ffn(cfg, inp["x"], perm, offsets, only_packed)
+    torch.cuda.synchronize()
+    assert torch.equal(y_plain, y_packed)
+    fo = L.forward(cfg, inp["x"], dict(inp, w_packed=packed), inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fo.y, L.combine(cfg, y_plain, inv, gate))
+
+
+def test_pack_rejects_unsupported_layers():
+    for cfg in (CONFIGS["tiny"], CONFIGS["mixtral"].replace(tokens=4, n_experts=2, d_hidden=256)):
+        assert L.packed_experts_size(cfg) == 0
+        inp = make_inputs(cfg.replace(tokens=4), seed=0, device="cuda")
+        assert L.pack_experts(cfg, inp) is None
