@@ -12,10 +12,12 @@
 //     expert have consecutive ids that land on one XCD and are dispatched
 //     together, so they share the weight stream through that XCD's L2;
 //   * the tile's gathered input rows sit in LDS (64 x 512 bf16);
+//   * eight waves, two per SIMD, so that one wave's MFMAs cover the other's
+//     waits on memory, LDS and barriers;
 //   * the hidden layer is produced 256 units at a time: each wave computes
-//     S = relu(X W1[64 units]^T) for all 64 rows (v_mfma_f32_32x32x16_bf16,
+//     S = relu(X W1[32 units]^T) for all 64 rows (v_mfma_f32_32x32x16_bf16,
 //     W1 fragments streamed from global memory into a register ring), writes
-//     it as bf16 to LDS, then every wave accumulates Y[:, its 128 columns] +=
+//     it as bf16 to LDS, then every wave accumulates Y[:, its 64 columns] +=
 //     S W2[cols, 256 units]^T with W2 fragments streamed the same way;
 //   * Y (64 x 512 fp32) stays in registers across the hidden chunks and is
 //     written once, as bf16, through LDS for coalesced 16-byte stores;
@@ -28,10 +30,12 @@
 
 namespace moe {
 
-constexpr int FZ_M = 64;    // rows per tile
-constexpr int FZ_H = 256;   // hidden units per chunk
-constexpr int FZ_THREADS = 256;
-constexpr int FZ_D = 512;   // d_model handled by this kernel
+constexpr int FZ_M = 64;      // rows per tile
+constexpr int FZ_H = 256;     // hidden units per chunk
+constexpr int FZ_WAVES = 8;
+constexpr int FZ_THREADS = 64 * FZ_WAVES;
+constexpr int FZ_D = 512;     // d_model handled by this kernel
+constexpr int FZ_RING = 16;   // weight fragments in flight per wave
 
 struct FusedArgs {
   const bf16_t* x;
@@ -47,45 +51,50 @@ struct FusedArgs {
 };
 
 // The weight stream of one wave.  For hidden chunk hc (FZ_H units), wave w
-// consumes NE 16-byte fragments per lane: entries n < 2*(D/16) are W1
-// fragments (k-step n/2, 32-unit block n%2 of the wave's 64 units), the rest
-// W2 fragments (k-step (n-N1)/(D/128), 32-column block (n-N1)%(D/128) of the
-// wave's D/4 output columns).  frag_src gives the element offset of a
-// fragment inside expert e's unpacked tables (table 0: W1 [h][D], table 1:
-// W2 [D][h]); the packed layout stores the fragments contiguously in
-// consumption order: [e][hc][w][n][lane][8 elements].
+// consumes NE 16-byte fragments per lane:
+//   n <  N1: W1 fragments, k-step n, of the wave's U1 = 32 hidden units
+//            [hc*FZ_H + 32w, +32);
+//   n >= N1: W2 fragments, k-step (n-N1)/NT2, 32-column block (n-N1)%NT2 of
+//            the wave's C2 = D/8 output columns [w*C2, +C2).
+// src() gives the element offset of a fragment inside expert e's unpacked
+// tables (table 0: W1 [h][D], table 1: W2 [D][h]); the packed layout stores
+// the fragments contiguously in consumption order:
+// [e][hc][w][n][lane][8 elements].
 template <int D>
 struct Stream {
-  static constexpr int KS1 = D / 16, NT2 = D / 128, KS2 = FZ_H / 16;
-  static constexpr int N1 = 2 * KS1, NE = N1 + NT2 * KS2;
+  static constexpr int U1 = FZ_H / FZ_WAVES;   // hidden units per wave per chunk
+  static constexpr int KS1 = D / 16;           // first-layer k-steps
+  static constexpr int C2 = D / FZ_WAVES;      // output columns per wave
+  static constexpr int NT2 = C2 / 32;          // 32-wide output blocks per wave
+  static constexpr int KS2 = FZ_H / 16;        // second-layer k-steps per chunk
+  static constexpr int N1 = KS1, NE = N1 + NT2 * KS2;
+  static_assert(U1 == 32, "one 32-unit block per wave");
   static __host__ __device__ inline int64_t src(int h, int hc, int w, int n, int lane,
                                                 int* table) {
     const int fr = lane & 31, fk = (lane >> 5) * 8;
     if (n < N1) {
-      const int ks = n >> 1, nt = n & 1;
       *table = 0;
-      return (int64_t)(hc * FZ_H + w * 64 + nt * 32 + fr) * D + ks * 16 + fk;
+      return (int64_t)(hc * FZ_H + w * U1 + fr) * D + n * 16 + fk;
     }
     const int mm = n - N1, ks = mm / NT2, j = mm % NT2;
     *table = 1;
-    return (int64_t)(w * (D / 4) + j * 32 + fr) * h + hc * FZ_H + ks * 16 + fk;
+    return (int64_t)(w * C2 + j * 32 + fr) * h + hc * FZ_H + ks * 16 + fk;
   }
   static __host__ __device__ inline int64_t packed(int h, int e, int hc, int w, int n, int lane) {
     const int nch = h / FZ_H;
-    return ((((int64_t)e * nch + hc) * 4 + w) * NE + n) * 512 + lane * 8;
+    return ((((int64_t)e * nch + hc) * FZ_WAVES + w) * NE + n) * 512 + lane * 8;
   }
 };
 
 template <int D, bool PACKED>
 __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs a) {
+  using S = Stream<D>;
   constexpr int XLD = D + 8;     // LDS row stride of the input tile (elements)
   constexpr int SLD = FZ_H + 8;  // LDS row stride of the hidden tile
-  constexpr int NW = D / 4;      // output columns per wave
-  constexpr int NT2 = NW / 32;   // 32-wide output tiles per wave
-  constexpr int KS1 = D / 16;    // k-steps of the first layer
-  constexpr int KS2 = FZ_H / 16; // k-steps of the second layer per chunk
-  static_assert(NT2 == Stream<D>::NT2 && KS1 == Stream<D>::KS1, "stream shape");
   constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int XPT = FZ_M * CPR / FZ_THREADS;  // input chunks per thread
+  constexpr int N1 = S::N1, NE = S::NE, NT2 = S::NT2, RING = FZ_RING;
+  static_assert(NE % RING == 0 && N1 % RING == 0, "stream must be a multiple of the ring");
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
   bf16_t* Xs = lds;
   bf16_t* Ss = lds + FZ_M * XLD;
@@ -120,38 +129,35 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
 
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   const int nchunks = a.h / FZ_H;
-  using S = Stream<D>;
-  constexpr int N1 = S::N1, NE = S::NE, RING = 32;
-  static_assert(NE % RING == 0, "stream length must be a multiple of the ring");
-  // A ring of RING registers keeps RING weight loads in flight without
-  // draining between the two layers or between chunks: consuming entry n
-  // issues entry n + RING (of this chunk or the next one).
   const bf16_t* W1e = a.w1 + (int64_t)e * a.h * D;
   const bf16_t* W2e = a.w2 + (int64_t)e * D * a.h;
-  auto frag_ptr = [&](int hc, int n) -> const bf16_t* {
+  auto frag = [&](int hc, int n) -> u32x4 {
     if constexpr (PACKED) {
-      return a.wp + S::packed(a.h, e, hc, w, n, lane);
+      return *reinterpret_cast<const u32x4*>(a.wp + S::packed(a.h, e, hc, w, n, lane));
     } else {
       int t;
       const int64_t o = S::src(a.h, hc, w, n, lane, &t);
-      return (t == 0 ? W1e : W2e) + o;
+      return *reinterpret_cast<const u32x4*>((t == 0 ? W1e : W2e) + o);
     }
   };
 
   // gathered input rows (rows past m are zero) and the first RING weight
   // fragments are requested together
-  u32x4 xv[FZ_M * CPR / FZ_THREADS];
+  u32x4 xv[XPT];
 #pragma unroll
-  for (int i = 0; i < FZ_M * CPR / FZ_THREADS; ++i) {
+  for (int i = 0; i < XPT; ++i) {
     const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
     xv[i] = r < m ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)s_src[r] * D + cc)
                   : u32x4{0u, 0u, 0u, 0u};
   }
+  // A ring of RING registers keeps RING weight loads in flight without
+  // draining between the two layers or between chunks: consuming entry n
+  // issues entry n + RING (of this chunk or the next one).
   u32x4 ring[RING];
 #pragma unroll
-  for (int i = 0; i < RING; ++i) ring[i] = *reinterpret_cast<const u32x4*>(frag_ptr(0, i));
+  for (int i = 0; i < RING; ++i) ring[i] = frag(0, i);
 #pragma unroll
-  for (int i = 0; i < FZ_M * CPR / FZ_THREADS; ++i) {
+  for (int i = 0; i < XPT; ++i) {
     const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
     *reinterpret_cast<u32x4*>(Xs + r * XLD + cc) = xv[i];
   }
@@ -165,66 +171,49 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
   __syncthreads();
   for (int hc = 0; hc < nchunks; ++hc) {
     const bool more = hc + 1 < nchunks;
-    // ---- first layer: S[:, w*64 .. +64) = relu(X W1[units]^T) ----
-    f32x16 sa[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sa[i][j] = f32x16{};
-    // input fragments are read from LDS one k-step ahead of their MFMAs
+    // consume entry n of this chunk's stream and refill its ring slot
+    auto take = [&](int n) -> bf16x8 {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, ring[n % RING]);
+      const int nn = n + RING;
+      if (nn < NE) ring[n % RING] = frag(hc, nn);
+      else if (more) ring[n % RING] = frag(hc + 1, nn - NE);
+      return v;
+    };
+    // ---- first layer: S[:, 32w .. +32) = relu(X W1[units]^T) ----
+    f32x16 sa[2] = {f32x16{}, f32x16{}};
     bf16x8 xa0 = *reinterpret_cast<const bf16x8*>(Xs + fr * XLD + fk);
     bf16x8 xa1 = *reinterpret_cast<const bf16x8*>(Xs + (32 + fr) * XLD + fk);
 #pragma unroll
-    for (int ks = 0; ks < KS1; ++ks) {
-      const int n0 = 2 * ks;
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, ring[n0 % RING]);
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, ring[(n0 + 1) % RING]);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int nn = n0 + q + RING;
-        if (nn < NE) ring[(n0 + q) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc, nn));
-        else if (more) ring[(n0 + q) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc + 1, nn - NE));
-      }
+    for (int ks = 0; ks < S::KS1; ++ks) {
+      const bf16x8 b = take(ks);
       const bf16x8 a0 = xa0, a1 = xa1;
-      if (ks + 1 < KS1) {
+      if (ks + 1 < S::KS1) {
         xa0 = *reinterpret_cast<const bf16x8*>(Xs + fr * XLD + (ks + 1) * 16 + fk);
         xa1 = *reinterpret_cast<const bf16x8*>(Xs + (32 + fr) * XLD + (ks + 1) * 16 + fk);
       }
-      sa[0][0] = mfma32(a0, b0, sa[0][0]);
-      sa[0][1] = mfma32(a0, b1, sa[0][1]);
-      sa[1][0] = mfma32(a1, b0, sa[1][0]);
-      sa[1][1] = mfma32(a1, b1, sa[1][1]);
+      sa[0] = mfma32(a0, b, sa[0]);
+      sa[1] = mfma32(a1, b, sa[1]);
     }
-    // relu, bf16, into the hidden tile
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int col = w * 64 + j * 32 + fr;
-          Ss[row * SLD + col] = f32_to_bf16(fmaxf(sa[i][j][r], 0.f));
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        Ss[row * SLD + w * S::U1 + fr] = f32_to_bf16(fmaxf(sa[i][r], 0.f));
+      }
     __syncthreads();
-    // ---- second layer: Y[:, w*NW .. +NW) += S W2[cols, units]^T ----
-    bf16x8 sa0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + fk);
-    bf16x8 sa1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + fk);
+    // ---- second layer: Y[:, w*C2 .. +C2) += S W2[cols, units]^T ----
+    bf16x8 sv0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + fk);
+    bf16x8 sv1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + fk);
 #pragma unroll
-    for (int ks = 0; ks < KS2; ++ks) {
-      const int n0 = N1 + ks * NT2;
+    for (int ks = 0; ks < S::KS2; ++ks) {
       bf16x8 b[NT2];
 #pragma unroll
-      for (int j = 0; j < NT2; ++j) {
-        b[j] = __builtin_bit_cast(bf16x8, ring[(n0 + j) % RING]);
-        const int nn = n0 + j + RING;
-        if (nn < NE) ring[(n0 + j) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc, nn));
-        else if (more) ring[(n0 + j) % RING] = *reinterpret_cast<const u32x4*>(frag_ptr(hc + 1, nn - NE));
-      }
-      const bf16x8 a0 = sa0, a1 = sa1;
-      if (ks + 1 < KS2) {
-        sa0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + (ks + 1) * 16 + fk);
-        sa1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + (ks + 1) * 16 + fk);
+      for (int j = 0; j < NT2; ++j) b[j] = take(N1 + ks * NT2 + j);
+      const bf16x8 a0 = sv0, a1 = sv1;
+      if (ks + 1 < S::KS2) {
+        sv0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + (ks + 1) * 16 + fk);
+        sv1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + (ks + 1) * 16 + fk);
       }
 #pragma unroll
       for (int j = 0; j < NT2; ++j) acc[0][j] = mfma32(a0, b[j], acc[0][j]);
@@ -242,7 +231,7 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = w * NW + j * 32 + fr;
+        const int col = w * S::C2 + j * 32 + fr;
         Xs[row * XLD + col] = f32_to_bf16(acc[i][j][r]);
       }
   __syncthreads();
@@ -263,21 +252,21 @@ size_t fused_packed_bytes(int E, int d, int h) {
   return sizeof(bf16_t) * 2 * (size_t)E * d * h;
 }
 
-// packed[e][hc][w][n][lane] <- the fragment frag_src names, 16 bytes a thread
+// packed[e][hc][w][n][lane] <- the fragment Stream::src names, 16 bytes a thread
 template <int D>
 __global__ __launch_bounds__(256) void pack_experts_kernel(const bf16_t* w1, const bf16_t* w2,
                                                            int E, int h, bf16_t* out) {
   using S = Stream<D>;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // fragment-lane index
   const int nch = h / FZ_H;
-  const int64_t total = (int64_t)E * nch * 4 * S::NE * 64;
+  const int64_t total = (int64_t)E * nch * FZ_WAVES * S::NE * 64;
   if (i >= total) return;
   const int lane = (int)(i % 64);
   int64_t r = i / 64;
   const int n = (int)(r % S::NE);
   r /= S::NE;
-  const int w = (int)(r % 4);
-  r /= 4;
+  const int w = (int)(r % FZ_WAVES);
+  r /= FZ_WAVES;
   const int hc = (int)(r % nch);
   const int e = (int)(r / nch);
   int t;
@@ -289,7 +278,7 @@ __global__ __launch_bounds__(256) void pack_experts_kernel(const bf16_t* w1, con
 
 hipError_t launch_pack_experts(const void* w1, const void* w2, int E, int d, int h, void* out,
                                hipStream_t s) {
-  const int64_t total = (int64_t)E * (h / FZ_H) * 4 * Stream<FZ_D>::NE * 64;
+  const int64_t total = (int64_t)E * (h / FZ_H) * FZ_WAVES * Stream<FZ_D>::NE * 64;
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_experts_kernel<FZ_D>, dim3((unsigned)((total + 255) / 256)), dim3(256),
                      0, s, (const bf16_t*)w1, (const bf16_t*)w2, E, h, (bf16_t*)out);
