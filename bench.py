@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized buffer (device to device) a few times and exit: "
+                         "the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: every expert of this layer sits on one MI355X and "
@@ -176,8 +179,17 @@ def main():
     from sparsely_gated_mixture_noisy_amd import _lib as L
     from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs
 
-    cfg = CONFIGS[args.config]
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
+    cfg = CONFIGS[args.config]
     print(f"[bench] {describe(cfg)}", file=sys.stderr, flush=True)
     inp = make_inputs(cfg, seed=0, device="cuda")
     # expert tables repacked once into the expert kernel's stream order (a
