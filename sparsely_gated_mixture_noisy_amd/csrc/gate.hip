@@ -6,142 +6,39 @@
 //   H_e     = clean_e + eps_e * softplus(x . W_noise[e])   (noisy gate)
 //   keep the k largest H_e (ties: lower e), softmax over the kept ones.
 //
-// One workgroup scores a tile of 32 rows against all experts, 128 projection
-// columns at a time (64 experts x {clean, raw} when noisy, 128 experts
-// otherwise).  bf16 projections run on v_mfma_f32_32x32x16_bf16 straight from
-// global memory (each wave owns one 32-column block); the per-row top-(k+1)
-// lists live in registers, 8 lanes per row, and are merged with lane shuffles.
+// A workgroup (8 waves) scores a tile of 32 rows against the experts in
+// blocks of 256: wave w computes the clean and the raw-noise scores of
+// experts blk + 32w .. +31 for all 32 rows with v_mfma_f32_32x32x16_bf16 (one
+// LDS input fragment feeds both tables' MFMAs; the table rows stream from
+// global memory through a register ring).  The scores stay in the MFMA
+// accumulator layout: lane l holds expert (l mod 32) of its wave for the 16
+// tile rows acc_row(i, l).  The noisy scores go through LDS to the selection
+// step, where 16 lanes per row keep running top-(k+1) lists that are merged
+// with lane shuffles.  For the smooth load the clean scores and noise scales
+// never leave the registers.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_kernels.h"
-
-#include <algorithm>
 
 namespace moe {
 
 constexpr int GATE_ROWS = 32;
-constexpr int GATE_THREADS = 256;
-typedef float ProjTile[GATE_ROWS][GATE_ROWS + 1];
+constexpr int GATE_WAVES = 8;
+constexpr int GATE_THREADS = 64 * GATE_WAVES;
+constexpr int GATE_BLOCK_E = 32 * GATE_WAVES;      // experts per projection block
+constexpr int GATE_TPR = GATE_THREADS / GATE_ROWS;  // selection lanes per row
+constexpr int GATE_XLDS_MAX_D = 1024;               // input tile in LDS up to this d_model
+constexpr int GATE_RING = 8;                        // table k-steps in flight per wave
+constexpr int HLD = GATE_BLOCK_E + 1;               // LDS row stride of the score block
 
-// One projection chunk is 4 column blocks of 32 columns.  Block b computes
-// P[b][r][c] = x[rows[r]] . tab[row0 + c] for c < valid; columns at or past
-// `valid` read table row `safe` and are never used.  Columns of chunk cb:
-// noisy -> blocks 0,1 clean scores of experts cb..cb+63, blocks 2,3 the raw
-// noise scores of the same experts; noise-free -> blocks 0..3 clean scores of
-// experts cb..cb+127.  Expert e is table row tab_row0 + e.
-struct BlockCols {
-  const void* tab;
-  int row0, valid, safe;
-};
-
-__device__ __forceinline__ BlockCols block_cols(int b, const void* wg, const void* wn, bool noisy,
-                                                int tab_row0, int cb, int nvalid) {
-  BlockCols bc;
-  const int e0 = noisy ? (b & 1) * 32 : b * 32;
-  bc.tab = (noisy && b >= 2) ? wn : wg;
-  bc.row0 = tab_row0 + cb + e0;
-  bc.valid = max(0, min(32, nvalid - e0));
-  bc.safe = tab_row0;
-  return bc;
-}
-
-struct ChunkSpec {
-  const void* wg;
-  const void* wn;
-  bool noisy;
-  int tab_row0, cb, nvalid;
-};
-
-template <typename T>
-struct Proj;
-
-template <>
-struct Proj<bf16_t> {
-  static __device__ __forceinline__ void run(const bf16_t* __restrict__ x, int d, const int* rows,
-                                             const ChunkSpec& cs, ProjTile* P) {
-    const int lane = threadIdx.x & 63, b = threadIdx.x >> 6;
-    const int c = lane & 31, kh = (lane >> 5) * 8;
-    const BlockCols bc = block_cols(b, cs.wg, cs.wn, cs.noisy, cs.tab_row0, cs.cb, cs.nvalid);
-    const int trow = c < bc.valid ? bc.row0 + c : bc.safe;
-    const bf16_t* wp = (const bf16_t*)bc.tab + (int64_t)trow * d + kh;
-    const bf16_t* xp = x + (int64_t)rows[c] * d + kh;
-    f32x16 acc = {};
-    int k0 = 0;
-    for (; k0 + 64 <= d; k0 += 64) {
-      bf16x8 a0 = load_bf16x8(xp + k0), b0 = load_bf16x8(wp + k0);
-      bf16x8 a1 = load_bf16x8(xp + k0 + 16), b1 = load_bf16x8(wp + k0 + 16);
-      bf16x8 a2 = load_bf16x8(xp + k0 + 32), b2 = load_bf16x8(wp + k0 + 32);
-      bf16x8 a3 = load_bf16x8(xp + k0 + 48), b3 = load_bf16x8(wp + k0 + 48);
-      acc = mfma32(a0, b0, acc);
-      acc = mfma32(a1, b1, acc);
-      acc = mfma32(a2, b2, acc);
-      acc = mfma32(a3, b3, acc);
-    }
-    for (; k0 < d; k0 += 16) acc = mfma32(load_bf16x8(xp + k0), load_bf16x8(wp + k0), acc);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      P[b][r][c] = acc[i];
-    }
-  }
-};
-
-template <>
-struct Proj<float> {
-  static __device__ __forceinline__ void run(const float* __restrict__ x, int d, const int* rows,
-                                             const ChunkSpec& cs, ProjTile* P) {
-    const int col = threadIdx.x & 127;
-    const int b = col >> 5, c = col & 31;
-    const BlockCols bc = block_cols(b, cs.wg, cs.wn, cs.noisy, cs.tab_row0, cs.cb, cs.nvalid);
-    const int trow = c < bc.valid ? bc.row0 + c : bc.safe;
-    const float* wp = (const float*)bc.tab + (int64_t)trow * d;
-    for (int r = threadIdx.x >> 7; r < GATE_ROWS; r += 2) {
-      const float* xp = x + (int64_t)rows[r] * d;
-      float s = 0.f;
-      for (int k = 0; k < d; ++k) s = fmaf(xp[k], wp[k], s);
-      P[b][r][c] = s;
-    }
-  }
-};
-
-// bf16 projection with the 32-row input tile in LDS (row stride xld): the
-// A operand comes from LDS, the table rows stream from global memory through
-// a 16-deep register ring so that many loads are in flight per wave.
-__device__ __forceinline__ void proj_lds(const bf16_t* Xs, int xld, int d, const ChunkSpec& cs,
-                                         ProjTile* P) {
-  constexpr int RING = 16;
-  const int lane = threadIdx.x & 63, b = threadIdx.x >> 6;
-  const int c = lane & 31, kh = (lane >> 5) * 8;
-  const BlockCols bc = block_cols(b, cs.wg, cs.wn, cs.noisy, cs.tab_row0, cs.cb, cs.nvalid);
-  const int trow = c < bc.valid ? bc.row0 + c : bc.safe;
-  const bf16_t* wp = (const bf16_t*)bc.tab + (int64_t)trow * d + kh;
-  const bf16_t* xp = Xs + c * xld + kh;
-  const int KS = d / 16;
-  u32x4 rb[RING];
-#pragma unroll
-  for (int i = 0; i < RING; ++i)
-    rb[i] = i < KS ? *reinterpret_cast<const u32x4*>(wp + i * 16) : u32x4{0u, 0u, 0u, 0u};
-  f32x16 acc = {};
-  for (int g = 0; g < KS; g += RING) {
-#pragma unroll
-    for (int i = 0; i < RING; ++i) {
-      const int ks = g + i;
-      if (ks < KS) {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, rb[i]);
-        if (ks + RING < KS) rb[i] = *reinterpret_cast<const u32x4*>(wp + (ks + RING) * 16);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(xp + ks * 16);
-        acc = mfma32(av, bv, acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    P[b][r][c] = acc[i];
-  }
+// Tile row held in accumulator register i of lane l (32x32 MFMA layout).
+__device__ __forceinline__ int acc_row(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
 // Where a tile's input rows come from: global memory (rows[] tokens) or, for
-// bf16 with d <= 1024, an LDS copy Xs of the 32 rows.
+// bf16 with d <= GATE_XLDS_MAX_D, an LDS copy Xs of the 32 rows.
 template <typename T>
 struct TileX {
   const T* x;
@@ -150,19 +47,7 @@ struct TileX {
   int xld;
 };
 
-template <typename T>
-__device__ __forceinline__ void project(const TileX<T>& tx, int d, const ChunkSpec& cs,
-                                        ProjTile* P) {
-  if constexpr (sizeof(T) == 2) {
-    if (tx.Xs) {
-      proj_lds(tx.Xs, tx.xld, d, cs, P);
-      return;
-    }
-  }
-  Proj<T>::run(tx.x, d, tx.rows, cs, P);
-}
-
-// Copy the 32 input rows of a tile to LDS (bf16 only, d % 8 == 0).
+// Copy the 32 input rows of a tile to LDS (bf16, d % 8 == 0).
 __device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* rows, bf16_t* Xs,
                                             int xld) {
   const int cpr = d / 8;
@@ -173,7 +58,83 @@ __device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* r
   }
 }
 
-constexpr int GATE_XLDS_MAX_D = 1024;  // input tile in LDS up to this d_model
+// Projection of one expert block: ac[i] = x[row] . wg[tab_row0 + e] and (noisy)
+// ar[i] = x[row] . wn[tab_row0 + e] for row = acc_row(i, lane) and
+// e = blk + 32 * wave + (lane & 31).  Columns past E read a valid table row
+// and are never used; waves with no valid column skip the MFMAs.
+template <typename T>
+struct BlockProj;
+
+template <>
+struct BlockProj<bf16_t> {
+  static __device__ __forceinline__ void run(const TileX<bf16_t>& tx, int d, const void* wg,
+                                             const void* wn, bool noisy, int tab_row0, int blk,
+                                             int E, f32x16& ac, f32x16& ar) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = lane & 31, kh = (lane >> 5) * 8;
+    ac = f32x16{};
+    ar = f32x16{};
+    if (blk + w * 32 >= E) return;
+    const int64_t trow = tab_row0 + min(blk + w * 32 + c, E - 1);
+    const bf16_t* pg = (const bf16_t*)wg + trow * d + kh;
+    const bf16_t* pn = noisy ? (const bf16_t*)wn + trow * d + kh : pg;
+    const int KS = d / 16;
+    auto afrag = [&](int ks) -> bf16x8 {
+      if (tx.Xs) return *reinterpret_cast<const bf16x8*>(tx.Xs + c * tx.xld + ks * 16 + kh);
+      return load_bf16x8(tx.x + (int64_t)tx.rows[c] * d + ks * 16 + kh);
+    };
+    u32x4 rg[GATE_RING], rn[GATE_RING];
+#pragma unroll
+    for (int i = 0; i < GATE_RING; ++i) {
+      rg[i] = i < KS ? *reinterpret_cast<const u32x4*>(pg + i * 16) : u32x4{0u, 0u, 0u, 0u};
+      rn[i] = (noisy && i < KS) ? *reinterpret_cast<const u32x4*>(pn + i * 16)
+                                : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int g = 0; g < KS; g += GATE_RING) {
+#pragma unroll
+      for (int i = 0; i < GATE_RING; ++i) {
+        const int ks = g + i;
+        if (ks < KS) {
+          const bf16x8 bg = __builtin_bit_cast(bf16x8, rg[i]);
+          const bf16x8 bn = __builtin_bit_cast(bf16x8, rn[i]);
+          if (ks + GATE_RING < KS) {
+            rg[i] = *reinterpret_cast<const u32x4*>(pg + (ks + GATE_RING) * 16);
+            if (noisy) rn[i] = *reinterpret_cast<const u32x4*>(pn + (ks + GATE_RING) * 16);
+          }
+          const bf16x8 a = afrag(ks);
+          ac = mfma32(a, bg, ac);
+          if (noisy) ar = mfma32(a, bn, ar);
+        }
+      }
+    }
+  }
+};
+
+template <>
+struct BlockProj<float> {
+  static __device__ __forceinline__ void run(const TileX<float>& tx, int d, const void* wg,
+                                             const void* wn, bool noisy, int tab_row0, int blk,
+                                             int E, f32x16& ac, f32x16& ar) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    ac = f32x16{};
+    ar = f32x16{};
+    if (blk + w * 32 >= E) return;
+    const int64_t trow = tab_row0 + min(blk + w * 32 + (lane & 31), E - 1);
+    const float* pg = (const float*)wg + trow * d;
+    const float* pn = noisy ? (const float*)wn + trow * d : pg;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* xr = tx.x + (int64_t)tx.rows[acc_row(i, lane)] * d;
+      float sc = 0.f, sr = 0.f;
+      for (int k = 0; k < d; ++k) {
+        sc = fmaf(xr[k], pg[k], sc);
+        if (noisy) sr = fmaf(xr[k], pn[k], sr);
+      }
+      ac[i] = sc;
+      ar[i] = sr;
+    }
+  }
+};
 
 // Running top-K1 list of one lane (best first).
 template <int K1>
@@ -196,17 +157,17 @@ struct TopList {
       }
     }
   }
-  // Merge the lists of the 8 lanes of a row group: every lane ends with the
-  // group's best K1 (value, expert) pairs in rank order.
-  __device__ __forceinline__ void merge8(float* ov, int* oe) {
+  // Merge the lists of the GATE_TPR lanes of a row: every lane ends with the
+  // row's best K1 (value, expert) pairs in rank order.
+  __device__ __forceinline__ void merge(float* ov, int* oe) {
 #pragma unroll
     for (int round = 0; round < K1; ++round) {
       float bv = v[0];
       int be = e[0];
 #pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        float v2 = __shfl_xor(bv, off, 8);
-        int e2 = __shfl_xor(be, off, 8);
+      for (int off = 1; off < GATE_TPR; off <<= 1) {
+        float v2 = __shfl_xor(bv, off, GATE_TPR);
+        int e2 = __shfl_xor(be, off, GATE_TPR);
         if (ranks_before(v2, e2, bv, be)) { bv = v2; be = e2; }
       }
       ov[round] = bv;
@@ -221,54 +182,9 @@ struct TopList {
   }
 };
 
-// Scores of one 32-row tile against experts [0, E) of a table block, merged
-// into per-lane top-K1 lists.  Table row of expert e is tab_row0 + e; the
-// noise draw of (tile row r, expert e) is erow[e] with erow the row's eps
-// pointer (unused when !noisy).  With keep != null the clean score and the
-// noise scale of every (row, expert) are also kept: keep[r*E+e] and
-// keep[32*E + r*E+e].
-template <typename T, int K1>
-__device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void* wn,
-                           const float* __restrict__ bias, int tab_row0, int E, const float* erow,
-                           bool noisy, ProjTile* P, TopList<K1>& L, float* keep) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 3, sub = tid & 7;
-  const int ce = noisy ? 64 : 128;  // experts per chunk
-  for (int cb = 0; cb < E; cb += ce) {
-    const int nvalid = min(ce, E - cb);
-    const ChunkSpec cs{wg, wn, noisy, tab_row0, cb, nvalid};
-    __syncthreads();  // P is free
-    project<T>(tx, d, cs, P);
-    __syncthreads();
-    for (int j = sub; j < nvalid; j += 8) {
-      const int e = cb + j;
-      float c = P[j >> 5][row][j & 31];
-      if (bias) c += bias[tab_row0 + e];
-      float h = c;
-      if (noisy) {
-        const float sp = softplus_f(P[2 + (j >> 5)][row][j & 31]);
-        h = c + erow[e] * sp;
-        if (keep) {
-          keep[row * E + e] = c;
-          keep[GATE_ROWS * E + row * E + e] = sp;
-        }
-      }
-      L.insert(h, e);
-    }
-  }
-}
-
-// One row's load term of expert e: Phi((clean - theta) / sp), theta the k-th
-// largest noisy score among the other experts.
-__device__ __forceinline__ float load_term(float clean, float sp, bool kept, float kth,
-                                           float k1th) {
-  const float th = kept ? k1th : kth;
-  return normal_cdf_f((clean - th) / sp);
-}
-
 // Turn the merged top-(k+1) of a row (rank order) into the kept experts in
 // ascending index order and their softmax gates; also the k-th and (k+1)-th
-// scores.  Valid in every lane; entries >= k are padding.
+// scores.  Entries >= k are padding.
 template <int K1>
 __device__ __forceinline__ void kept_gates(const float* ov, const int* oe, int k, int E,
                                            int* ke, float* kg, float* kth, float* k1th) {
@@ -278,7 +194,6 @@ __device__ __forceinline__ void kept_gates(const float* ov, const int* oe, int k
     ke[j] = j < k ? oe[j] : 0x7fffffff;
     kv[j] = ov[j];
   }
-  // ascending expert order over the first k entries (padding sorts last)
 #pragma unroll
   for (int i = 1; i < K1; ++i) {
 #pragma unroll
@@ -310,69 +225,146 @@ __device__ __forceinline__ void kept_gates(const float* ov, const int* oe, int k
   *k1th = (k < E) ? b : -INFINITY;
 }
 
+// Per-row facts the load estimate needs, shared through LDS.
+struct RowSel {
+  float kth, k1th;
+  int kept[8];
+};
+
+// One lane's load terms: sum over its 16 tile rows (register order) of
+// Phi((clean - theta) / sp), then the two half-waves holding the same expert
+// are added; rows at or past `valid` contribute 0.  Identical in the gate
+// and in the recompute kernel.
+__device__ __forceinline__ float load_column_sum(const f32x16& clean, const f32x16& sp, int e,
+                                                 int k, const RowSel* sel, int valid) {
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = acc_row(i, lane);
+    const RowSel& rs = sel[r];
+    bool in = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) in |= (j < k && rs.kept[j] == e);
+    const float th = in ? rs.k1th : rs.kth;
+    const float p = normal_cdf_f((clean[i] - th) / sp[i]);
+    s += r < valid ? p : 0.f;
+  }
+  return s + __shfl_xor(s, 32, 64);
+}
+
+// The scoring and selection of one 32-row tile against experts [0, E) of a
+// table block (expert e is table row tab_row0 + e).  eps_row(r) gives the
+// noise row of tile row r (experts contiguous).  On return every lane of a
+// row's group holds the row's top-K1 in ov/oe, and cs/ss the clean scores
+// (bias included) and noise scales of the last expert block.
+template <typename T, int K1, typename EpsRow>
+__device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void* wn,
+                           const float* __restrict__ bias, int tab_row0, int E, bool noisy,
+                           EpsRow eps_row, float (*Hs)[HLD], float* ov, int* oe, f32x16& cs,
+                           f32x16& ss) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row = tid / GATE_TPR, sub = tid % GATE_TPR;
+  TopList<K1> L;
+  L.init();
+  for (int blk = 0; blk < E; blk += GATE_BLOCK_E) {
+    const int e = blk + w * 32 + (lane & 31);
+    const bool ev = e < E;
+    // noise of this lane's 16 (row, expert) pairs, requested before the MFMAs
+    float ep[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ep[i] = (noisy && ev) ? eps_row(acc_row(i, lane))[e] : 0.f;
+    f32x16 ac, ar;
+    BlockProj<T>::run(tx, d, wg, wn, noisy, tab_row0, blk, E, ac, ar);
+    const float b = (bias && ev) ? bias[tab_row0 + e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float c = ac[i] + b;
+      float h = c;
+      if (noisy) {
+        const float sp = softplus_f(ar[i]);
+        h = c + ep[i] * sp;
+        ss[i] = sp;
+      } else {
+        ss[i] = 0.f;
+      }
+      cs[i] = c;
+      Hs[acc_row(i, lane)][w * 32 + (lane & 31)] = h;
+    }
+    __syncthreads();
+    const int nb = min(GATE_BLOCK_E, E - blk);
+    for (int j = sub; j < nb; j += GATE_TPR) L.insert(Hs[row][j], blk + j);
+    __syncthreads();
+  }
+  L.merge(ov, oe);
+}
+
 // ---------------------------------------------------------------------------
 // Flat gate: tile = 32 consecutive tokens.  With a.part set (noisy gate,
-// E <= 256) the kernel also produces the tile's row of smooth-load partial
-// sums, from the clean scores and noise scales it kept in LDS.
+// E <= GATE_FUSED_LOAD_MAX_E) the kernel also writes the tile's row of
+// smooth-load partial sums.
 // ---------------------------------------------------------------------------
 template <typename T, int K1>
 __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a) {
-  __shared__ ProjTile P[4];
+  __shared__ float Hs[GATE_ROWS][HLD];
   __shared__ int rows[GATE_ROWS];
+  __shared__ RowSel sel[GATE_ROWS];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
   if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
   __syncthreads();
   const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
   const int xld = a.d + 8;
   bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
-  float* keep = a.part ? reinterpret_cast<float*>(dyn + (xl ? sizeof(bf16_t) * GATE_ROWS * xld : 0))
-                       : nullptr;
   if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
-  const int row = tid >> 3;
-  const int64_t t = t0 + row;
   const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
-  const float* erow = noisy ? a.eps + (int64_t)rows[row] * a.E : nullptr;
-  TopList<K1> L;
-  L.init();
-  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, a.bias, 0, a.E, erow, noisy, P, L, keep);
+  const float* eps = a.eps;
+  const int E = a.E;
+  auto eps_row = [&](int r) -> const float* { return eps + (int64_t)rows[r] * E; };
   float ov[K1];
   int oe[K1];
-  L.merge8(ov, oe);
+  f32x16 cs, ss;
+  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, a.bias, 0, E, noisy, eps_row, Hs, ov, oe, cs,
+                    ss);
   int ke[K1];
   float kg[K1], kth, k1th;
-  kept_gates<K1>(ov, oe, a.k, a.E, ke, kg, &kth, &k1th);
-  if ((tid & 7) == 0 && t < a.T) {
+  kept_gates<K1>(ov, oe, a.k, E, ke, kg, &kth, &k1th);
+  const int row = tid / GATE_TPR;
+  const int64_t t = t0 + row;
+  if (tid % GATE_TPR == 0) {
+    if (t < a.T) {
 #pragma unroll
-    for (int j = 0; j < K1; ++j) {
-      if (j < a.k) {
-        a.idx[t * a.k + j] = ke[j];
-        a.gate[t * a.k + j] = kg[j];
+      for (int j = 0; j < K1; ++j) {
+        if (j < a.k) {
+          a.idx[t * a.k + j] = ke[j];
+          a.gate[t * a.k + j] = kg[j];
+        }
+      }
+      if (a.thr) {
+        a.thr[2 * t] = kth;
+        a.thr[2 * t + 1] = k1th;
       }
     }
-    if (a.thr) {
-      a.thr[2 * t] = kth;
-      a.thr[2 * t + 1] = k1th;
+    sel[row].kth = kth;
+    sel[row].k1th = k1th;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int v = -1;
+#pragma unroll
+      for (int q = 0; q < K1; ++q)
+        if (q == j && q < a.k) v = ke[q];
+      sel[row].kept[j] = v;
     }
   }
-  if (keep) {
-    // this row's load terms, in place of the clean scores (0 past the batch)
-    for (int e = tid & 7; e < a.E; e += 8) {
-      bool in = false;
-#pragma unroll
-      for (int j = 0; j < K1; ++j) in |= (j < a.k && ke[j] == e);
-      const float v = load_term(keep[row * a.E + e], keep[GATE_ROWS * a.E + row * a.E + e], in,
-                                kth, k1th);
-      keep[row * a.E + e] = t < a.T ? v : 0.f;
-    }
+  if (a.part) {
     __syncthreads();
-    for (int e = tid; e < a.E; e += GATE_THREADS) {
-      float sum = 0.f;
-      for (int r = 0; r < GATE_ROWS; ++r) sum += keep[r * a.E + e];
-      a.part[(int64_t)blockIdx.x * a.E + e] = sum;
-    }
+    const int e = (tid >> 6) * 32 + (lane & 31);
+    const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
+    const float s = load_column_sum(cs, ss, e, a.k, sel, valid);
+    if (lane < 32 && e < E) a.part[(int64_t)blockIdx.x * E + e] = s;
   }
 }
 
@@ -384,7 +376,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
 // ---------------------------------------------------------------------------
 template <typename T, int K1>
 __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs a) {
-  __shared__ ProjTile P[4];
+  __shared__ float Hs[GATE_ROWS][HLD];
   __shared__ int rows[GATE_ROWS];
   __shared__ int asg[GATE_ROWS];
   __shared__ int s_g, s_p0, s_n;
@@ -415,19 +407,19 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
   const int xld = a.d + 8;
   bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
   if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
-  const int row = tid >> 3;
-  const int Eg = a.Eg;
+  const int Eg = a.Eg, G = a.G;
   const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
-  const float* erow = noisy ? a.eps + ((int64_t)rows[row] * a.G + g) * Eg : nullptr;
-  TopList<K1> L;
-  L.init();
-  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, nullptr, g * Eg, Eg, erow, noisy, P, L,
-                    nullptr);
+  const float* eps = a.eps;
+  auto eps_row = [&](int r) -> const float* { return eps + ((int64_t)rows[r] * G + g) * Eg; };
   float ov[K1];
   int oe[K1];
-  L.merge8(ov, oe);
-  if ((tid & 7) == 0 && row < n) {
+  f32x16 cs, ss;
+  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, nullptr, g * Eg, Eg, noisy, eps_row, Hs, ov, oe,
+                    cs, ss);
+  const int row = tid / GATE_TPR;
+  if (tid % GATE_TPR == 0 && row < n) {
     int ke[K1];
     float kg[K1], kth, k1th;
     kept_gates<K1>(ov, oe, a.kpg, Eg, ke, kg, &kth, &k1th);
@@ -449,59 +441,47 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
 // ---------------------------------------------------------------------------
 // Smooth load estimate (flat noisy gate), recomputing the projections from
 // the gate's thresholds.  Workgroup b covers tokens [32b, 32b+32) and writes
-//   part[b][e] = sum over its rows (ascending) of
+//   part[b][e] = sum over its rows of
 //                Phi((clean[t,e] - theta[t,e]) / softplus(raw[t,e]))
 // with theta = thr[t][1] if e is kept by t, else thr[t][0]: the same terms,
 // in the same order, as the gate kernel's fused variant.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) {
-  __shared__ ProjTile P[4];
   __shared__ int rows[GATE_ROWS];
-  __shared__ float Q[GATE_ROWS][65];
+  __shared__ RowSel sel[GATE_ROWS];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
-  const int tid = threadIdx.x;
-  const int row = tid >> 3, sub = tid & 7;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
-  if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
+  if (tid < GATE_ROWS) {
+    const int r = (int)min<int64_t>(t0 + tid, a.T - 1);
+    rows[tid] = r;
+    sel[tid].kth = a.thr[2 * (int64_t)r];
+    sel[tid].k1th = a.thr[2 * (int64_t)r + 1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sel[tid].kept[j] = j < a.k ? a.idx[(int64_t)r * a.k + j] : -1;
+  }
   __syncthreads();
   const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
   const int xld = a.d + 8;
   bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
   if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
-  const int64_t t = t0 + row;
-  const bool tv = t < a.T;
-  int kept[8];
+  const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
+  for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
+    const int e = blk + w * 32 + (lane & 31);
+    f32x16 ac, ar;
+    BlockProj<T>::run(tx, a.d, a.w_gate, a.w_noise, true, 0, blk, a.E, ac, ar);
+    const float b = (a.bias && e < a.E) ? a.bias[e] : 0.f;
+    f32x16 cs, ss;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) kept[j] = (j < a.k) ? a.idx[(int64_t)rows[row] * a.k + j] : -1;
-  const float th0 = a.thr[2 * (int64_t)rows[row]], th1 = a.thr[2 * (int64_t)rows[row] + 1];
-  for (int cb = 0; cb < a.E; cb += 64) {
-    const int nvalid = min(64, a.E - cb);
-    const ChunkSpec cs{a.w_gate, a.w_noise, true, 0, cb, nvalid};
-    __syncthreads();
-    project<T>(tx, a.d, cs, P);
-    __syncthreads();
-    for (int j = sub; j < 64; j += 8) {
-      float p = 0.f;
-      if (j < nvalid && tv) {
-        const int e = cb + j;
-        float c = P[j >> 5][row][j & 31];
-        if (a.bias) c += a.bias[e];
-        const float sp = softplus_f(P[2 + (j >> 5)][row][j & 31]);
-        bool in = false;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) in |= (kept[q] == e);
-        p = load_term(c, sp, in, th0, th1);
-      }
-      Q[row][j] = p;
+    for (int i = 0; i < 16; ++i) {
+      cs[i] = ac[i] + b;
+      ss[i] = softplus_f(ar[i]);
     }
-    __syncthreads();
-    if (tid < nvalid) {
-      float sum = 0.f;
-      for (int r = 0; r < GATE_ROWS; ++r) sum += Q[r][tid];
-      a.part[(int64_t)blockIdx.x * a.E + cb + tid] = sum;
-    }
+    const float s = load_column_sum(cs, ss, e, a.k, sel, valid);
+    if (lane < 32 && e < a.E) a.part[(int64_t)blockIdx.x * a.E + e] = s;
   }
 }
 
@@ -516,7 +496,7 @@ static size_t xtile_bytes(bool bf16, int d) {
 // size already granted to that kernel.
 template <typename K>
 static hipError_t set_lds(K kernel, size_t bytes, size_t* done) {
-  if (bytes <= 65536 || bytes <= *done) return hipSuccess;
+  if (bytes <= 32768 || bytes <= *done) return hipSuccess;
   hipError_t err = hipFuncSetAttribute((const void*)kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (err == hipSuccess) *done = bytes;
@@ -535,8 +515,7 @@ static hipError_t launch_flat_k(const GateFlatArgs& a, size_t sh, hipStream_t s)
 
 template <typename T>
 static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
-  size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
-  if (a.part) sh += sizeof(float) * 2 * GATE_ROWS * (size_t)a.E;
+  const size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
   if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, sh, s);
   if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, sh, s);
   return launch_flat_k<T, 9>(a, sh, s);
