@@ -7,19 +7,19 @@
 // k = 4) the expert stage is bound by streaming the expert tables from HBM,
 // not by MFMA, so the kernel is organised to read each table byte once:
 //
-//   * one workgroup = one tile of at most 64 rows of one expert (an expert
-//     with m rows gets ceil(m/64) tiles of near-equal size); the tiles of an
+//   * one workgroup = one tile of at most 96 rows of one expert (an expert
+//     with m rows gets ceil(m/96) tiles of near-equal size); the tiles of an
 //     expert have consecutive ids that land on one XCD and are dispatched
 //     together, so they share the weight stream through that XCD's L2;
-//   * the tile's gathered input rows sit in LDS (64 x 512 bf16);
+//   * the tile's gathered input rows sit in LDS (96 x 512 bf16);
 //   * eight waves, two per SIMD, so that one wave's MFMAs cover the other's
 //     waits on memory, LDS and barriers;
 //   * the hidden layer is produced 256 units at a time: each wave computes
-//     S = relu(X W1[32 units]^T) for all 64 rows (v_mfma_f32_32x32x16_bf16,
+//     S = relu(X W1[32 units]^T) for all 96 rows (v_mfma_f32_32x32x16_bf16,
 //     W1 fragments streamed from global memory into a register ring), writes
 //     it as bf16 to LDS, then every wave accumulates Y[:, its 64 columns] +=
 //     S W2[cols, 256 units]^T with W2 fragments streamed the same way;
-//   * Y (64 x 512 fp32) stays in registers across the hidden chunks and is
+//   * Y (96 x 512 fp32) stays in registers across the hidden chunks and is
 //     written once, as bf16, through LDS for coalesced 16-byte stores;
 //   * the expert tables can be repacked once (moe_pack_experts) into the
 //     exact order the waves consume their 16-byte fragments, so that every
@@ -30,7 +30,8 @@
 
 namespace moe {
 
-constexpr int FZ_M = 64;      // rows per tile
+constexpr int FZ_MT = 3;      // 32-row blocks per tile (rows per tile: 32 * FZ_MT)
+constexpr int FZ_M = 32 * FZ_MT;
 constexpr int FZ_H = 256;     // hidden units per chunk
 constexpr int FZ_WAVES = 8;
 constexpr int FZ_THREADS = 64 * FZ_WAVES;
@@ -86,20 +87,21 @@ struct Stream {
   }
 };
 
-template <int D, bool PACKED>
+template <int D, int MT, bool PACKED>
 __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs a) {
   using S = Stream<D>;
+  constexpr int M = 32 * MT;     // rows per tile
   constexpr int XLD = D + 8;     // LDS row stride of the input tile (elements)
   constexpr int SLD = FZ_H + 8;  // LDS row stride of the hidden tile
   constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int XPT = FZ_M * CPR / FZ_THREADS;  // input chunks per thread
+  constexpr int XPT = M * CPR / FZ_THREADS;  // input chunks per thread
   constexpr int N1 = S::N1, NE = S::NE, NT2 = S::NT2, RING = FZ_RING;
   static_assert(NE % RING == 0 && N1 % RING == 0, "stream must be a multiple of the ring");
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
   bf16_t* Xs = lds;
-  bf16_t* Ss = lds + FZ_M * XLD;
+  bf16_t* Ss = lds + M * XLD;
   __shared__ int s_info[3];
-  __shared__ int s_src[FZ_M];
+  __shared__ int s_src[M];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) {
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
   const int e = s_info[0];
   if (e < 0) return;
   const int p0 = s_info[1], m = s_info[2];
-  if (tid < FZ_M) {
+  if (tid < M) {
     const int p = p0 + min(tid, m - 1);
     s_src[tid] = a.perm ? a.perm[p] / a.k : p;
   }
@@ -162,9 +164,9 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
     *reinterpret_cast<u32x4*>(Xs + r * XLD + cc) = xv[i];
   }
 
-  f32x16 acc[2][NT2];
+  f32x16 acc[MT][NT2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NT2; ++j) acc[i][j] = f32x16{};
 
@@ -180,22 +182,29 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
       return v;
     };
     // ---- first layer: S[:, 32w .. +32) = relu(X W1[units]^T) ----
-    f32x16 sa[2] = {f32x16{}, f32x16{}};
-    bf16x8 xa0 = *reinterpret_cast<const bf16x8*>(Xs + fr * XLD + fk);
-    bf16x8 xa1 = *reinterpret_cast<const bf16x8*>(Xs + (32 + fr) * XLD + fk);
+    f32x16 sa[MT];
+    bf16x8 xa[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      sa[i] = f32x16{};
+      xa[i] = *reinterpret_cast<const bf16x8*>(Xs + (32 * i + fr) * XLD + fk);
+    }
 #pragma unroll
     for (int ks = 0; ks < S::KS1; ++ks) {
       const bf16x8 b = take(ks);
-      const bf16x8 a0 = xa0, a1 = xa1;
+      bf16x8 av[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) av[i] = xa[i];
       if (ks + 1 < S::KS1) {
-        xa0 = *reinterpret_cast<const bf16x8*>(Xs + fr * XLD + (ks + 1) * 16 + fk);
-        xa1 = *reinterpret_cast<const bf16x8*>(Xs + (32 + fr) * XLD + (ks + 1) * 16 + fk);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          xa[i] = *reinterpret_cast<const bf16x8*>(Xs + (32 * i + fr) * XLD + (ks + 1) * 16 + fk);
       }
-      sa[0] = mfma32(a0, b, sa[0]);
-      sa[1] = mfma32(a1, b, sa[1]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) sa[i] = mfma32(av[i], b, sa[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -203,29 +212,33 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
       }
     __syncthreads();
     // ---- second layer: Y[:, w*C2 .. +C2) += S W2[cols, units]^T ----
-    bf16x8 sv0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + fk);
-    bf16x8 sv1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + fk);
+    bf16x8 sv[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) sv[i] = *reinterpret_cast<const bf16x8*>(Ss + (32 * i + fr) * SLD + fk);
 #pragma unroll
     for (int ks = 0; ks < S::KS2; ++ks) {
       bf16x8 b[NT2];
 #pragma unroll
       for (int j = 0; j < NT2; ++j) b[j] = take(N1 + ks * NT2 + j);
-      const bf16x8 a0 = sv0, a1 = sv1;
+      bf16x8 av[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) av[i] = sv[i];
       if (ks + 1 < S::KS2) {
-        sv0 = *reinterpret_cast<const bf16x8*>(Ss + fr * SLD + (ks + 1) * 16 + fk);
-        sv1 = *reinterpret_cast<const bf16x8*>(Ss + (32 + fr) * SLD + (ks + 1) * 16 + fk);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          sv[i] = *reinterpret_cast<const bf16x8*>(Ss + (32 * i + fr) * SLD + (ks + 1) * 16 + fk);
       }
 #pragma unroll
-      for (int j = 0; j < NT2; ++j) acc[0][j] = mfma32(a0, b[j], acc[0][j]);
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NT2; ++j) acc[1][j] = mfma32(a1, b[j], acc[1][j]);
+        for (int j = 0; j < NT2; ++j) acc[i][j] = mfma32(av[i], b[j], acc[i][j]);
     }
     __syncthreads();
   }
 
   // Y -> bf16 -> LDS (reusing the input tile) -> coalesced stores
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NT2; ++j)
 #pragma unroll
@@ -290,7 +303,7 @@ static hipError_t launch_fused_t(const FusedArgs& a, int64_t A, hipStream_t s) {
   constexpr size_t lds = sizeof(bf16_t) * (size_t)FZ_M * ((FZ_D + 8) + (FZ_H + 8));
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t err = hipFuncSetAttribute((const void*)ffn_relu_fused_kernel<FZ_D, PACKED>,
+    hipError_t err = hipFuncSetAttribute((const void*)ffn_relu_fused_kernel<FZ_D, FZ_MT, PACKED>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     attr_done = true;
@@ -298,7 +311,7 @@ static hipError_t launch_fused_t(const FusedArgs& a, int64_t A, hipStream_t s) {
   // upper bound of tiles, rounded to whole XCD rows
   int64_t qmax = (A + FZ_M - 1) / FZ_M + a.E;
   qmax = (qmax + 7) / 8 * 8;
-  hipLaunchKernelGGL((ffn_relu_fused_kernel<FZ_D, PACKED>), dim3((unsigned)qmax),
+  hipLaunchKernelGGL((ffn_relu_fused_kernel<FZ_D, FZ_MT, PACKED>), dim3((unsigned)qmax),
                      dim3(FZ_THREADS), lds, s, a);
   return hipGetLastError();
 }
