@@ -40,9 +40,9 @@ size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
 // Every workspace region, at fixed offsets for a given configuration.
 struct Layout {
-  size_t idx, gate, thr, counts, offsets, perm, inv, blk, ticket, tiles, desc, hid, ysorted, part,
+  size_t idx, gate, thr, counts, offsets, perm, inv, bits, base, tiles, desc, hid, ysorted, part,
       imp, load;
-  size_t idx_p, gate_p, counts_g, offsets_g, perm_g, inv_g, blk_g, tiles_g;
+  size_t idx_p, gate_p, counts_g, offsets_g, perm_g, inv_g, bits_g, base_g, tiles_g;
   size_t total;
   int nb, load_blocks;
 };
@@ -66,8 +66,9 @@ Layout layout(const moe_config* c) {
   L.offsets = take(4 * (size_t)(E + 1));
   L.perm = take(4 * (size_t)A);
   L.inv = take(4 * (size_t)A);
-  L.blk = take(4 * (size_t)L.nb * E);
-  L.ticket = take(4);
+  L.bits = take(4 * (size_t)L.nb * E);
+  L.base = take(4 * (size_t)L.nb * E);
+
   L.tiles = take(4 * (size_t)(E + 1));
   // tile descriptors of the fused expert kernel (64-row tiles)
   L.desc = take(12 * (size_t)((A + 63) / 64 + E));
@@ -84,7 +85,8 @@ Layout layout(const moe_config* c) {
   L.offsets_g = take(4 * (size_t)(G + 1));
   L.perm_g = take(4 * (size_t)Ag);
   L.inv_g = take(4 * (size_t)Ag);
-  L.blk_g = take(4 * (size_t)L.nb * G);
+  L.bits_g = take(4 * (size_t)L.nb * G);
+  L.base_g = take(4 * (size_t)L.nb * G);
   L.tiles_g = take(4 * (size_t)(G + 1));
   L.total = o;
   return L;
@@ -190,10 +192,11 @@ moe_status hip_status(hipError_t e, const char* what) {
 // ---- enqueue helpers (arguments already validated) -------------------------
 
 // part != null (flat noisy gate with E <= GATE_FUSED_LOAD_MAX_E): the gate
-// kernel also writes the smooth-load partial sums.
+// kernel also writes the smooth-load partial sums.  bits != null (flat gate):
+// it also writes the routing masks of its 32-token tiles.
 moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const moe_params* p,
                    const moe_noise* n, int32_t* idx, float* gate, float* thr, float* part,
-                   void* ws, hipStream_t s) {
+                   uint32_t* bits, void* ws, hipStream_t s) {
   const bool bf16 = c->dtype == MOE_BF16;
   const bool noisy = c->noisy != 0;
   if (c->n_groups == 0) {
@@ -211,6 +214,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
     a.gate = gate;
     a.thr = thr;
     a.part = part;
+    a.bits = bits;
     return hip_status(launch_gate_flat(a, bf16, s), "gate");
   }
   const int G = c->n_groups, kg = c->k_groups;
@@ -230,6 +234,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   a.gate = gate_p;
   a.thr = nullptr;
   a.part = nullptr;
+  a.bits = nullptr;
   MOE_TRY(hip_status(launch_gate_flat(a, bf16, s), "primary gate"));
   if (c->tokens == 0) return MOE_OK;
   RouteArgs r;
@@ -238,15 +243,18 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   r.k = kg;
   r.E = G;
   r.NB = L.nb;
-  r.blk = at<int32_t>(ws, L.blk_g);
-  r.ticket = at<int32_t>(ws, L.ticket);
+  r.bits = at<uint32_t>(ws, L.bits_g);
+  r.base = at<int32_t>(ws, L.base_g);
+  r.have_bits = 0;
   r.counts = at<int32_t>(ws, L.counts_g);
   r.offsets = at<int32_t>(ws, L.offsets_g);
   r.perm = at<int32_t>(ws, L.perm_g);
   r.inv = at<int32_t>(ws, L.inv_g);
-  MOE_TRY(hip_status(launch_route(r, s), "group routing"));
   int32_t* tiles_g = at<int32_t>(ws, L.tiles_g);
-  MOE_TRY(hip_status(launch_tile_map(r.offsets, G, 32, tiles_g, nullptr, s), "group tiles"));
+  r.tile_rows = 32;  // the secondary gate's row tiles
+  r.tiles = tiles_g;
+  r.desc = nullptr;
+  MOE_TRY(hip_status(launch_route(r, s), "group routing"));
   GateGroupArgs ga;
   ga.x = x;
   ga.w_gate = p->w_gate;
@@ -267,26 +275,42 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   return hip_status(launch_gate_group(ga, (int)grid, bf16, s), "secondary gate");
 }
 
+// Expert-stage tile rows of this configuration (0: no tile map needed).
+int expert_tile_rows(const moe_config* c) {
+  if (c->dtype != MOE_BF16) return 0;
+  return ffn_tile_rows(true, c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
+}
+
+// have_bits: the flat gate already wrote the routing masks.  with_tiles: also
+// build the expert stage's tile map.
 moe_status do_route(const moe_config* c, const Layout& L, const int32_t* idx, int32_t* counts,
-                    int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, hipStream_t s) {
+                    int32_t* offsets, int32_t* perm, int32_t* inv, bool have_bits,
+                    bool with_tiles, void* ws, hipStream_t s) {
   RouteArgs r;
   r.idx = idx;
   r.T = c->tokens;
   r.k = c->top_k;
   r.E = c->n_experts;
   r.NB = L.nb;
-  r.blk = at<int32_t>(ws, L.blk);
-  r.ticket = at<int32_t>(ws, L.ticket);
+  r.bits = at<uint32_t>(ws, L.bits);
+  r.base = at<int32_t>(ws, L.base);
+  r.have_bits = have_bits ? 1 : 0;
   r.counts = counts;
   r.offsets = offsets;
   r.perm = perm;
   r.inv = inv;
+  r.tile_rows = with_tiles ? expert_tile_rows(c) : 0;
+  r.tiles = at<int32_t>(ws, L.tiles);
+  const bool fused = c->dtype == MOE_BF16 &&
+                     fused_ffn_supported(c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
+  r.desc = fused ? at<int32_t>(ws, L.desc) : nullptr;
   return hip_status(launch_route(r, s), "route");
 }
 
+// tiles_ready: the routing step already built the tile map.
 moe_status do_ffn(const moe_config* c, const Layout& L, const void* x, const int32_t* perm,
-                  const int32_t* offsets, const moe_params* p, void* y_sorted, void* ws,
-                  hipStream_t s) {
+                  const int32_t* offsets, const moe_params* p, void* y_sorted, bool tiles_ready,
+                  void* ws, hipStream_t s) {
   const bool bf16 = c->dtype == MOE_BF16;
   const int sw = c->ffn == MOE_FFN_SWIGLU;
   FfnArgs f;
@@ -310,7 +334,7 @@ moe_status do_ffn(const moe_config* c, const Layout& L, const void* x, const int
   int32_t* desc = fused ? at<int32_t>(ws, L.desc) : nullptr;
   f.desc = desc;
   if (f.A == 0) return MOE_OK;
-  if (bf16)
+  if (bf16 && !tiles_ready)
     MOE_TRY(hip_status(launch_tile_map(offsets, c->n_experts,
                                        ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw), tiles,
                                        desc, s),
@@ -325,10 +349,8 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
                       float* importance, float* load, float* out, bool have_part, void* ws,
                       hipStream_t s) {
   const int E = c->n_experts;
-  MOE_TRY(hip_status(launch_importance(perm, offsets, gate, E, importance, s), "importance"));
   const bool smooth = c->n_groups == 0 && c->noisy && c->tokens > 0;
-  float* part = nullptr;
-  if (smooth) part = at<float>(ws, L.part);
+  float* part = smooth ? at<float>(ws, L.part) : nullptr;
   if (smooth && !have_part) {
     LoadArgs la;
     la.x = x;
@@ -344,8 +366,19 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
     la.part = part;
     MOE_TRY(hip_status(launch_load_partial(la, c->dtype == MOE_BF16, s), "load"));
   }
-  MOE_TRY(hip_status(launch_load_reduce(part, L.load_blocks, offsets, E, load, s), "load reduce"));
-  return hip_status(launch_cv2(importance, load, E, wi, wl, out, s), "cv2");
+  BalanceArgs b;
+  b.perm = perm;
+  b.offsets = offsets;
+  b.gate = gate;
+  b.part = part;
+  b.blocks = L.load_blocks;
+  b.E = E;
+  b.w_imp = wi;
+  b.w_load = wl;
+  b.importance = importance;
+  b.load = load;
+  b.out = out;
+  return hip_status(launch_balance(b, s), "balance");
 }
 
 }  // namespace
@@ -398,7 +431,7 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
     return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_gate is NULL");
   if (thr && cfg->n_groups > 0) return fail(MOE_ERR_INVALID_ARG, "thr is for the flat gate only");
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
-  MOE_TRY(do_gate(cfg, layout(cfg), x, p, noise, topk_idx, topk_gate, thr, nullptr, ws,
+  MOE_TRY(do_gate(cfg, layout(cfg), x, p, noise, topk_idx, topk_gate, thr, nullptr, nullptr, ws,
                   (hipStream_t)stream));
   return ok();
 }
@@ -414,7 +447,7 @@ moe_status moe_route(const moe_config* cfg, const int32_t* topk_idx, int32_t* co
     return fail(MOE_ERR_INVALID_ARG, "x and x_sorted must be given together");
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
-  MOE_TRY(do_route(cfg, layout(cfg), topk_idx, counts, offsets, perm, inv, ws, s));
+  MOE_TRY(do_route(cfg, layout(cfg), topk_idx, counts, offsets, perm, inv, false, false, ws, s));
   if (x)
     MOE_TRY(hip_status(launch_gather_rows(x, perm, cfg->top_k, cfg->tokens * cfg->top_k,
                                           cfg->d_model, (int)elem_size(cfg), x_sorted, s),
@@ -430,7 +463,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* p
   if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
   if (cfg->tokens > 0 && (!x || !y_sorted)) return fail(MOE_ERR_INVALID_ARG, "x / y_sorted is NULL");
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
-  MOE_TRY(do_ffn(cfg, layout(cfg), x, perm, offsets, p, y_sorted, ws, (hipStream_t)stream));
+  MOE_TRY(do_ffn(cfg, layout(cfg), x, perm, offsets, p, y_sorted, false, ws,
+                 (hipStream_t)stream));
   return ok();
 }
 
@@ -488,9 +522,14 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   // small expert counts: the gate kernel produces the load partials itself
   const bool fused_load = smooth && gate_fuses_load(cfg->n_experts);
   float* part = fused_load ? at<float>(ws, L.part) : nullptr;
-  MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, part, ws, s));
-  MOE_TRY(do_route(cfg, L, idx, counts, offsets, perm, inv, ws, s));
-  MOE_TRY(do_ffn(cfg, L, x, perm, offsets, p, y_sorted, ws, s));
+  // the flat gate writes the routing masks; the routing step builds the
+  // expert tile map
+  const bool flat = cfg->n_groups == 0 && cfg->tokens > 0;
+  uint32_t* bits = flat ? at<uint32_t>(ws, L.bits) : nullptr;
+  const bool tiles = expert_tile_rows(cfg) > 0;
+  MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, part, bits, ws, s));
+  MOE_TRY(do_route(cfg, L, idx, counts, offsets, perm, inv, flat, tiles, ws, s));
+  MOE_TRY(do_ffn(cfg, L, x, perm, offsets, p, y_sorted, tiles, ws, s));
   MOE_TRY(hip_status(launch_combine(y_sorted, inv, gate, cfg->tokens, cfg->top_k, cfg->d_model,
                                     cfg->dtype == MOE_BF16, out->y, s),
                      "combine"));

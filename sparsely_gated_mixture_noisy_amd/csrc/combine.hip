@@ -7,11 +7,9 @@
 //
 // Balance statistics ("Outrageously Large Neural Networks — MoE ..." reading
 // note, sections 核心想法 and 方法怎么做; paper card, section 方法适配):
-//   importance[e] = sum of the gates routed to e, summed over e's routed
-//                   positions by one wave (lane-strided partial sums, then a
-//                   fixed shuffle tree);
-//   load[e]       = fixed-order sum of per-workgroup partials of the smooth
-//                   load, or the row count when there is no noise;
+//   importance[e] = sum of the gates routed to e;
+//   load[e]       = sum of the smooth-load terms of e, or its row count when
+//                   there is no noise;
 //   CV^2          = population variance / mean^2, reduced in fp64.
 // No floating-point atomics anywhere: results are bitwise reproducible.
 #include "moe_device.h"
@@ -78,69 +76,27 @@ hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float*
   return hipGetLastError();
 }
 
-// One wave per expert: importance[e] = sum_{p in segment e} gate[perm[p]].
-__global__ __launch_bounds__(256) void importance_kernel(const int32_t* perm,
-                                                        const int32_t* offsets,
-                                                        const float* gate, int E,
-                                                        float* importance) {
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (e >= E) return;
-  const int p0 = offsets[e], p1 = offsets[e + 1];
-  float s = 0.f;
-  for (int p = p0 + lane; p < p1; p += 64) s += gate[perm[p]];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (lane == 0) importance[e] = s;
-}
+// ---------------------------------------------------------------------------
+// Balance statistics in one launch.  Workgroup (16 waves) b covers the 16
+// experts [16b, 16b+16):
+//   importance[e]: wave w takes expert 16b + w: lane-strided partial sums
+//                  over e's routed positions, then a fixed xor-shuffle tree;
+//   load[e]:       lane l of wave w takes expert 16b + l%16 and the
+//                  (4w + l/16)-th of 64 contiguous ranges of load-partial
+//                  rows, summed in ascending order; the 64 range sums are
+//                  then added in range order (or the row count without
+//                  partials).
+// A one-workgroup kernel then reduces both vectors to CV^2 in fp64 with a
+// fixed tree.
+// ---------------------------------------------------------------------------
+constexpr int BAL_THREADS = 1024;
+constexpr int BAL_EXPERTS = 16;
 
-hipError_t launch_importance(const int32_t* perm, const int32_t* offsets, const float* gate,
-                             int E, float* importance, hipStream_t s) {
-  hipLaunchKernelGGL(importance_kernel, dim3((E + 3) / 4), dim3(256), 0, s, perm, offsets, gate, E,
-                     importance);
-  return hipGetLastError();
-}
-
-// load[e] = sum_b part[b][e] in a fixed order, or the row count of e.
-// Workgroup: 64 experts x 16 waves; wave w sums a contiguous range of b in
-// ascending order, then the 16 wave sums are added in wave order.
-__global__ __launch_bounds__(1024) void load_reduce_kernel(const float* part, int blocks,
-                                                          const int32_t* offsets, int E,
-                                                          float* load) {
-  __shared__ float red[16][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + lane;
-  if (!part) {
-    if (w == 0 && e < E) load[e] = (float)(offsets[e + 1] - offsets[e]);
-    return;
-  }
-  const int per = (blocks + 15) / 16;
-  const int b0 = w * per, b1 = min(blocks, b0 + per);
-  float s = 0.f;
-  if (e < E)
-    for (int b = b0; b < b1; ++b) s += part[(int64_t)b * E + e];
-  red[w][lane] = s;
-  __syncthreads();
-  if (w == 0 && e < E) {
-    float t = 0.f;
-    for (int i = 0; i < 16; ++i) t += red[i][lane];
-    load[e] = t;
-  }
-}
-
-hipError_t launch_load_reduce(const float* part, int blocks, const int32_t* offsets, int E,
-                              float* load, hipStream_t s) {
-  hipLaunchKernelGGL(load_reduce_kernel, dim3((E + 63) / 64), dim3(1024), 0, s, part, blocks,
-                     offsets, E, load);
-  return hipGetLastError();
-}
-
-// Fixed-order fp64 block reduction (256 threads).
 __device__ double block_sum_f64(double v) {
-  __shared__ double red[256];
+  __shared__ double red[BAL_THREADS];
   red[threadIdx.x] = v;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
+  for (int off = BAL_THREADS / 2; off > 0; off >>= 1) {
     if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
     __syncthreads();
   }
@@ -150,32 +106,71 @@ __device__ double block_sum_f64(double v) {
 }
 
 __device__ double cv2_of(const float* v, int E) {
+  auto ld = [&](int i) { return (double)v[i]; };
   double s = 0.0;
-  for (int i = threadIdx.x; i < E; i += 256) s += (double)v[i];
+  for (int i = threadIdx.x; i < E; i += BAL_THREADS) s += ld(i);
   const double mean = block_sum_f64(s) / E;
   double q = 0.0;
-  for (int i = threadIdx.x; i < E; i += 256) {
-    double dv = (double)v[i] - mean;
+  for (int i = threadIdx.x; i < E; i += BAL_THREADS) {
+    const double dv = ld(i) - mean;
     q += dv * dv;
   }
   const double var = block_sum_f64(q) / E;
   return mean == 0.0 ? 0.0 : var / (mean * mean);
 }
 
-__global__ __launch_bounds__(256) void cv2_kernel(const float* importance, const float* load,
-                                                 int E, float w_imp, float w_load, float* out) {
-  const double ci = cv2_of(importance, E);
-  const double cl = cv2_of(load, E);
-  if (threadIdx.x == 0) {
-    out[0] = (float)ci;
-    out[1] = (float)cl;
-    out[2] = (float)((double)w_imp * ci + (double)w_load * cl);
+__global__ __launch_bounds__(BAL_THREADS) void balance_kernel(BalanceArgs a) {
+  __shared__ float red[64][BAL_EXPERTS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e0 = blockIdx.x * BAL_EXPERTS;
+  {
+    const int e = e0 + w;
+    if (e < a.E) {
+      const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
+      float s = 0.f;
+      for (int p = p0 + lane; p < p1; p += 64) s += a.gate[a.perm[p]];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (lane == 0) a.importance[e] = s;
+    }
+  }
+  {
+    const int le = lane % BAL_EXPERTS, range = 4 * w + lane / BAL_EXPERTS;
+    const int e = e0 + le;
+    if (a.part) {
+      const int per = (a.blocks + 63) / 64;
+      const int b0 = range * per, b1 = min(a.blocks, b0 + per);
+      float s = 0.f;
+      if (e < a.E)
+        for (int b = b0; b < b1; ++b) s += a.part[(int64_t)b * a.E + e];
+      red[range][le] = s;
+      __syncthreads();
+      if (threadIdx.x < BAL_EXPERTS && e0 + threadIdx.x < a.E) {
+        float t = 0.f;
+        for (int i = 0; i < 64; ++i) t += red[i][threadIdx.x];
+        a.load[e0 + threadIdx.x] = t;
+      }
+    } else if (threadIdx.x < BAL_EXPERTS && e0 + threadIdx.x < a.E) {
+      const int ee = e0 + threadIdx.x;
+      a.load[ee] = (float)(a.offsets[ee + 1] - a.offsets[ee]);
+    }
   }
 }
 
-hipError_t launch_cv2(const float* importance, const float* load, int E, float w_imp,
-                      float w_load, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(cv2_kernel, dim3(1), dim3(256), 0, s, importance, load, E, w_imp, w_load, out);
+__global__ __launch_bounds__(BAL_THREADS) void cv2_kernel(BalanceArgs a) {
+  const double ci = cv2_of(a.importance, a.E);
+  const double cl = cv2_of(a.load, a.E);
+  if (threadIdx.x == 0) {
+    a.out[0] = (float)ci;
+    a.out[1] = (float)cl;
+    a.out[2] = (float)((double)a.w_imp * ci + (double)a.w_load * cl);
+  }
+}
+
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(balance_kernel, dim3((a.E + BAL_EXPERTS - 1) / BAL_EXPERTS),
+                     dim3(BAL_THREADS), 0, s, a);
+  hipLaunchKernelGGL(cv2_kernel, dim3(1), dim3(BAL_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

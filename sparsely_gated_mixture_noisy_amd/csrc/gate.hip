@@ -312,17 +312,21 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  const int E = a.E;
   if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
-  __syncthreads();
   const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
   const int xld = a.d + 8;
   bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
+  // routing masks of the tile: after the input tile in dynamic LDS
+  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (xl ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
+  if (a.bits)
+    for (int i = tid; i < E; i += GATE_THREADS) sb[i] = 0u;
+  __syncthreads();
   if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
   const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
   const float* eps = a.eps;
-  const int E = a.E;
   auto eps_row = [&](int r) -> const float* { return eps + (int64_t)rows[r] * E; };
   float ov[K1];
   int oe[K1];
@@ -347,6 +351,11 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
         a.thr[2 * t] = kth;
         a.thr[2 * t + 1] = k1th;
       }
+      if (a.bits) {
+#pragma unroll
+        for (int j = 0; j < K1; ++j)
+          if (j < a.k) atomicOr(&sb[ke[j]], 1u << row);
+      }
     }
     sel[row].kth = kth;
     sel[row].k1th = k1th;
@@ -359,8 +368,10 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
       sel[row].kept[j] = v;
     }
   }
+  if (a.part || a.bits) __syncthreads();
+  if (a.bits)
+    for (int i = tid; i < E; i += GATE_THREADS) a.bits[(int64_t)blockIdx.x * E + i] = sb[i];
   if (a.part) {
-    __syncthreads();
     const int e = (tid >> 6) * 32 + (lane & 31);
     const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
     const float s = load_column_sum(cs, ss, e, a.k, sel, valid);
@@ -515,7 +526,8 @@ static hipError_t launch_flat_k(const GateFlatArgs& a, size_t sh, hipStream_t s)
 
 template <typename T>
 static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
-  const size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
+  size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
+  if (a.bits) sh += sizeof(uint32_t) * (size_t)a.E;
   if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, sh, s);
   if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, sh, s);
   return launch_flat_k<T, 9>(a, sh, s);

@@ -18,6 +18,7 @@ struct GateFlatArgs {
   float* gate;    // [T][k]
   float* thr;     // [T][2] or null
   float* part;    // [ceil(T/32)][E] smooth-load partials (noisy, E <= 256) or null
+  uint32_t* bits; // [ceil(T/32)][E] routing masks of the tile's tokens, or null
 };
 hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s);
 constexpr int GATE_FUSED_LOAD_MAX_E = 256;
@@ -53,20 +54,25 @@ int load_partial_blocks(int64_t T);
 hipError_t launch_load_partial(const LoadArgs& a, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- route ----
-constexpr int ROUTE_BLOCK_TOKENS = 64;
+constexpr int ROUTE_BLOCK_TOKENS = 32;
 struct RouteArgs {
   const int32_t* idx;  // [T][k]
   int64_t T;
   int k, E;
-  int NB;              // ceil(T / 64)
-  int32_t* blk;        // [NB][E] workspace
-  int32_t* ticket;     // [1] workspace
+  int NB;              // ceil(T / 32)
+  uint32_t* bits;      // [NB][E] workspace: bit i = token 32b+i kept e
+  int32_t* base;       // [NB][E] workspace
+  int have_bits;       // bits already written (by the flat gate)
   int32_t* counts;     // [E]
   int32_t* offsets;    // [E+1]
   int32_t* perm;       // [A]
   int32_t* inv;        // [A]
+  int tile_rows;       // > 0: also build the expert tile map (tiles, desc)
+  int32_t* tiles;      // [E+1]
+  int32_t* desc;       // [tiles][3] or null
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
 
 // x_sorted[p] = x[perm[p] / k] for p < A (elem_bytes per element, d per row)
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, int k, int64_t A, int d,
@@ -108,12 +114,19 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
 // -------------------------------------------------------- combine / stats --
 hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float* gate, int64_t T,
                           int k, int d, bool bf16, void* y, hipStream_t s);
-hipError_t launch_importance(const int32_t* perm, const int32_t* offsets, const float* gate,
-                             int E, float* importance, hipStream_t s);
-// load[e] = sum_b part[b][e] (part != null) or counts[e] (part == null)
-hipError_t launch_load_reduce(const float* part, int blocks, const int32_t* offsets, int E,
-                              float* load, hipStream_t s);
-hipError_t launch_cv2(const float* importance, const float* load, int E, float w_imp,
-                      float w_load, float* out, hipStream_t s);
+// importance[e], load[e] (= sum_b part[b][e], or the row count when part is
+// null), then the CV^2 / loss triple.
+struct BalanceArgs {
+  const int32_t* perm;
+  const int32_t* offsets;
+  const float* gate;
+  const float* part;  // [blocks][E] or null
+  int blocks, E;
+  float w_imp, w_load;
+  float* importance;
+  float* load;
+  float* out;         // [3]
+};
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -6,17 +6,21 @@
 // ascending inside each expert, so the result is unique.
 //
 // Rank of assignment (t, e) inside expert e = number of earlier tokens that
-// kept e.  Tokens are cut into 64-token blocks; inside a block a 64-bit mask
-// per expert (bit i = token i of the block kept e) gives the in-block rank by
-// a popcount of the bits below the token, and an exclusive scan of the
-// per-block counts over the blocks gives the rest.  Every step is integer
+// kept e.  Tokens are cut into 32-token blocks; a 32-bit mask per (block,
+// expert) (bit i = token i of the block kept e) gives the in-block rank as a
+// popcount of the bits below the token, and an exclusive scan of the mask
+// popcounts over the blocks gives the rest.  Every step is integer
 // arithmetic, so the result does not depend on scheduling.
 //
-//   route_hist:    per block, per expert counts  -> blk[b][e]
-//   route_colscan: per expert, exclusive scan of blk over b, counts[e]; the
-//                  last workgroup to finish scans counts -> offsets
-//   route_scatter: pos = offsets[e] + blk[b][e] + in-block rank;
+//   route_hist:    bits[b][e] (the flat gate can write them itself)
+//   route_colscan: per expert, exclusive scan of popcount(bits) over b into
+//                  base[b][e], and counts[e]
+//   route_scatter: every workgroup scans counts into offsets in LDS (cheap,
+//                  and no workgroup has to wait for another); workgroup 0
+//                  also writes offsets and, when asked, the expert stage's
+//                  tile map; pos = offsets[e] + base[b][e] + in-block rank,
 //                  perm[pos] = a, inv[a] = pos
+// No kernel here fences across workgroups: results cross kernel boundaries.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -24,9 +28,9 @@ namespace moe {
 
 constexpr int SCAN_THREADS = 1024;
 
-// Exclusive scan of n <= 4 * 1024 values held 4 per thread (thread i owns
-// v[4i .. 4i+3]); returns the thread's exclusive base and writes the total
-// to *total.  Block of 1024 threads.
+// Exclusive scan of values held 4 per thread (thread i owns v[4i .. 4i+3]);
+// returns the thread's exclusive base and writes the total to *total.
+// Block of SCAN_THREADS threads.
 __device__ int block_scan4(const int v[4], int* total) {
   __shared__ int wsum[SCAN_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -51,157 +55,37 @@ __device__ int block_scan4(const int v[4], int* total) {
   return wbase + incl - s;
 }
 
-__global__ void fill_i32_kernel(int32_t* p, int n, int v) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-__global__ __launch_bounds__(256) void route_hist_kernel(RouteArgs a) {
-  extern __shared__ uint32_t bits[];  // [E][2]
-  const int b = blockIdx.x, tid = threadIdx.x;
-  if (b == 0 && tid == 0) *a.ticket = 0;
-  for (int i = tid; i < 2 * a.E; i += 256) bits[i] = 0u;
-  __syncthreads();
-  const int64_t t0 = (int64_t)b * ROUTE_BLOCK_TOKENS;
-  const int nt = (int)min<int64_t>(ROUTE_BLOCK_TOKENS, a.T - t0);
-  for (int i = tid; i < nt * a.k; i += 256) {
-    const int tl = i / a.k;
-    const int e = a.idx[t0 * a.k + i];
-    atomicOr(&bits[2 * e + (tl >> 5)], 1u << (tl & 31));
-  }
-  __syncthreads();
-  for (int e = tid; e < a.E; e += 256)
-    a.blk[(int64_t)b * a.E + e] = __popc(bits[2 * e]) + __popc(bits[2 * e + 1]);
-}
-
-__global__ __launch_bounds__(SCAN_THREADS) void route_colscan_kernel(RouteArgs a) {
-  __shared__ int part[SCAN_THREADS / 64][64];
-  __shared__ int last;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int e = blockIdx.x * 64 + lane;
-  const int per = (a.NB + 15) / 16;
-  const int b0 = w * per, b1 = min(a.NB, b0 + per);
-  int s = 0;
-  if (e < a.E)
-    for (int b = b0; b < b1; ++b) s += a.blk[(int64_t)b * a.E + e];
-  part[w][lane] = s;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < 16; ++i) {
-    if (i < w) base += part[i][lane];
-    tot += part[i][lane];
-  }
-  if (e < a.E) {
-    int run = base;
-    for (int b = b0; b < b1; ++b) {
-      int64_t o = (int64_t)b * a.E + e;
-      int c = a.blk[o];
-      a.blk[o] = run;
-      run += c;
-    }
-    if (w == 0) a.counts[e] = tot;
-  }
-  // the last workgroup to finish turns counts into offsets
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = (atomicAdd(a.ticket, 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+// Tile map of the expert stage from per-expert row counts: tiles[e] = first
+// tile of expert e (exclusive scan of ceil(count / rows)), tiles[E] = total;
+// with desc, desc[q] = {expert, first position, rows}, an expert's rows split
+// into near-equal tiles.  counts_of(e) and offsets_of(e) give the routing.
+// Called by all SCAN_THREADS threads of one workgroup.
+template <typename CountF, typename OffF>
+__device__ void build_tile_map(int E, int rows, CountF counts_of, OffF offsets_of, int32_t* tiles,
+                               int32_t* desc) {
+  const int tid = threadIdx.x;
   int carry = 0;
-  for (int c0 = 0; c0 < a.E; c0 += 4 * SCAN_THREADS) {
-    int v[4];
+  for (int c0 = 0; c0 < E; c0 += 4 * SCAN_THREADS) {
+    int v[4], cnt[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int ee = c0 + 4 * tid + j;
-      v[j] = ee < a.E ? __hip_atomic_load(&a.counts[ee], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : 0;
+      const int e = c0 + 4 * tid + j;
+      cnt[j] = e < E ? counts_of(e) : 0;
+      v[j] = (cnt[j] + rows - 1) / rows;
     }
     int total;
     int run = carry + block_scan4(v, &total);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int ee = c0 + 4 * tid + j;
-      if (ee < a.E) a.offsets[ee] = run;
-      run += v[j];
-    }
-    carry += total;
-  }
-  if (tid == 0) a.offsets[a.E] = carry;
-}
-
-__global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
-  extern __shared__ uint32_t bits[];  // [E][2]
-  const int b = blockIdx.x, tid = threadIdx.x;
-  for (int i = tid; i < 2 * a.E; i += 256) bits[i] = 0u;
-  __syncthreads();
-  const int64_t t0 = (int64_t)b * ROUTE_BLOCK_TOKENS;
-  const int nt = (int)min<int64_t>(ROUTE_BLOCK_TOKENS, a.T - t0);
-  for (int i = tid; i < nt * a.k; i += 256) {
-    const int tl = i / a.k;
-    const int e = a.idx[t0 * a.k + i];
-    atomicOr(&bits[2 * e + (tl >> 5)], 1u << (tl & 31));
-  }
-  __syncthreads();
-  for (int i = tid; i < nt * a.k; i += 256) {
-    const int tl = i / a.k;
-    const int64_t as = t0 * a.k + i;
-    const int e = a.idx[as];
-    const uint32_t lo = bits[2 * e], hi = bits[2 * e + 1];
-    int below = (tl < 32) ? __popc(lo & ((1u << tl) - 1u))
-                          : __popc(lo) + __popc(hi & ((1u << (tl - 32)) - 1u));
-    const int pos = a.offsets[e] + a.blk[(int64_t)b * a.E + e] + below;
-    a.perm[pos] = (int32_t)as;
-    a.inv[as] = pos;
-  }
-}
-
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
-  if (a.T == 0) {
-    // empty batch: counts = 0, offsets = 0
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((a.E + 256) / 256), dim3(256), 0, s, a.counts, a.E, 0);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((a.E + 256) / 256), dim3(256), 0, s, a.offsets,
-                       a.E + 1, 0);
-    return hipGetLastError();
-  }
-  size_t sh = sizeof(uint32_t) * 2 * (size_t)a.E;
-  hipLaunchKernelGGL(route_hist_kernel, dim3(a.NB), dim3(256), sh, s, a);
-  hipLaunchKernelGGL(route_colscan_kernel, dim3((a.E + 63) / 64), dim3(SCAN_THREADS), 0, s, a);
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(a.NB), dim3(256), sh, s, a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// tiles[e] = exclusive prefix of ceil(count_e / rows); one workgroup.  With
-// desc, tile tiles[e] + i of expert e (count m_e, n_e tiles) covers
-// floor(m_e / n_e) rows, plus one for the first m_e % n_e tiles.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(SCAN_THREADS) void tile_map_kernel(const int32_t* offsets, int E,
-                                                                int rows, int32_t* tiles,
-                                                                int32_t* desc) {
-  const int tid = threadIdx.x;
-  int carry = 0;
-  for (int c0 = 0; c0 < E; c0 += 4 * SCAN_THREADS) {
-    int v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = c0 + 4 * tid + j;
-      v[j] = e < E ? (offsets[e + 1] - offsets[e] + rows - 1) / rows : 0;
-    }
-    int total;
-    int ex = block_scan4(v, &total);
-    int run = carry + ex;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = c0 + 4 * tid + j;
+      const int e = c0 + 4 * tid + j;
       if (e < E) {
         tiles[e] = run;
         if (desc && v[j] > 0) {
-          const int m = offsets[e + 1] - offsets[e], base = m / v[j], rem = m % v[j];
+          const int m = cnt[j], base = m / v[j], rem = m % v[j], o = offsets_of(e);
           for (int i = 0; i < v[j]; ++i) {
             int32_t* d = desc + 3 * (int64_t)(run + i);
             d[0] = e;
-            d[1] = offsets[e] + i * base + min(i, rem);
+            d[1] = o + i * base + min(i, rem);
             d[2] = base + (i < rem ? 1 : 0);
           }
         }
@@ -211,6 +95,156 @@ __global__ __launch_bounds__(SCAN_THREADS) void tile_map_kernel(const int32_t* o
     carry += total;
   }
   if (tid == 0) tiles[E] = carry;
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int v) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void route_hist_kernel(RouteArgs a) {
+  extern __shared__ uint32_t sb[];  // [E]
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < a.E; i += 256) sb[i] = 0u;
+  __syncthreads();
+  const int64_t t0 = (int64_t)b * ROUTE_BLOCK_TOKENS;
+  const int nt = (int)min<int64_t>(ROUTE_BLOCK_TOKENS, a.T - t0);
+  for (int i = tid; i < nt * a.k; i += 256) atomicOr(&sb[a.idx[t0 * a.k + i]], 1u << (i / a.k));
+  __syncthreads();
+  for (int e = tid; e < a.E; e += 256) a.bits[(int64_t)b * a.E + e] = sb[e];
+}
+
+// Workgroup (16 waves) b covers the 16 experts [16b, 16b+16); lane l of wave
+// w takes expert 16b + l%16 and the (4w + l/16)-th of 64 contiguous ranges of
+// token blocks.
+constexpr int SCAN_EXPERTS = 16;
+
+__global__ __launch_bounds__(SCAN_THREADS) void route_colscan_kernel(RouteArgs a) {
+  __shared__ int part[64][SCAN_EXPERTS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int le = lane % SCAN_EXPERTS, range = 4 * w + lane / SCAN_EXPERTS;
+  const int e = blockIdx.x * SCAN_EXPERTS + le;
+  const int per = (a.NB + 63) / 64;
+  const int b0 = range * per, b1 = min(a.NB, b0 + per);
+  int s = 0;
+  if (e < a.E)
+    for (int b = b0; b < b1; ++b) s += __popc(a.bits[(int64_t)b * a.E + e]);
+  part[range][le] = s;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < 64; ++i) {
+    if (i < range) base += part[i][le];
+    tot += part[i][le];
+  }
+  if (e < a.E) {
+    int run = base;
+    for (int b = b0; b < b1; ++b) {
+      const int64_t o = (int64_t)b * a.E + e;
+      a.base[o] = run;
+      run += __popc(a.bits[o]);
+    }
+    if (range == 0) a.counts[e] = tot;
+  }
+}
+
+constexpr int SCATTER_THREADS = 256;
+
+// Exclusive scan of counts[0..E) into off[0..E] (LDS) by one workgroup of
+// SCATTER_THREADS threads: thread i owns a contiguous run of experts.
+__device__ void scan_counts(const int32_t* counts, int E, int* off) {
+  __shared__ int tsum[SCATTER_THREADS];
+  const int tid = threadIdx.x;
+  const int per = (E + SCATTER_THREADS - 1) / SCATTER_THREADS;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e) {
+    off[e] = s;
+    s += counts[e];
+  }
+  tsum[tid] = s;
+  __syncthreads();
+  // exclusive scan of the 256 thread sums (Hillis-Steele in LDS)
+  for (int d = 1; d < SCATTER_THREADS; d <<= 1) {
+    const int v = tid >= d ? tsum[tid - d] : 0;
+    __syncthreads();
+    tsum[tid] += v;
+    __syncthreads();
+  }
+  const int base = tid > 0 ? tsum[tid - 1] : 0;
+  for (int e = e0; e < e1; ++e) off[e] += base;
+  if (tid == SCATTER_THREADS - 1) off[E] = tsum[tid];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArgs a) {
+  extern __shared__ int off[];  // [E+1]
+  const int b = blockIdx.x, tid = threadIdx.x;
+  scan_counts(a.counts, a.E, off);
+  if (b == 0) {
+    for (int e = tid; e <= a.E; e += SCATTER_THREADS) a.offsets[e] = off[e];
+  }
+  const int64_t t0 = (int64_t)b * ROUTE_BLOCK_TOKENS;
+  const int nt = (int)min<int64_t>(ROUTE_BLOCK_TOKENS, a.T - t0);
+  for (int i = tid; i < nt * a.k; i += SCATTER_THREADS) {
+    const int tl = i / a.k;
+    const int64_t as = t0 * a.k + i;
+    const int e = a.idx[as];
+    const int64_t o = (int64_t)b * a.E + e;
+    const int pos = off[e] + a.base[o] + __popc(a.bits[o] & ((1u << tl) - 1u));
+    a.perm[pos] = (int32_t)as;
+    a.inv[as] = pos;
+  }
+}
+
+// The expert stage's tile map from counts and offsets (one workgroup).
+__global__ __launch_bounds__(SCAN_THREADS) void tile_map_counts_kernel(const int32_t* counts,
+                                                                       const int32_t* offsets,
+                                                                       int E, int rows,
+                                                                       int32_t* tiles,
+                                                                       int32_t* desc) {
+  build_tile_map(
+      E, rows, [&](int e) { return counts[e]; }, [&](int e) { return offsets[e]; }, tiles, desc);
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T == 0) {
+    // empty batch: counts = 0, offsets = 0, no tiles
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((a.E + 256) / 256), dim3(256), 0, s, a.counts, a.E, 0);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((a.E + 256) / 256), dim3(256), 0, s, a.offsets,
+                       a.E + 1, 0);
+    if (a.tile_rows > 0)
+      hipLaunchKernelGGL(fill_i32_kernel, dim3((a.E + 256) / 256), dim3(256), 0, s, a.tiles,
+                         a.E + 1, 0);
+    return hipGetLastError();
+  }
+  if (!a.have_bits)
+    hipLaunchKernelGGL(route_hist_kernel, dim3(a.NB), dim3(256), sizeof(uint32_t) * (size_t)a.E, s,
+                       a);
+  hipLaunchKernelGGL(route_colscan_kernel, dim3((a.E + SCAN_EXPERTS - 1) / SCAN_EXPERTS),
+                     dim3(SCAN_THREADS), 0, s, a);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(a.NB), dim3(SCATTER_THREADS),
+                     sizeof(int) * (size_t)(a.E + 1), s, a);
+  if (a.tile_rows > 0)
+    hipLaunchKernelGGL(tile_map_counts_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a.counts,
+                       a.offsets, a.E, a.tile_rows, a.tiles, a.desc);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Stand-alone tile map (one workgroup) for the expert stage called on its own.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(SCAN_THREADS) void tile_map_kernel(const int32_t* offsets, int E,
+                                                                int rows, int32_t* tiles,
+                                                                int32_t* desc) {
+  build_tile_map(
+      E, rows, [&](int e) { return offsets[e + 1] - offsets[e]; },
+      [&](int e) { return offsets[e]; }, tiles, desc);
 }
 
 hipError_t launch_tile_map(const int32_t* offsets, int E, int rows, int32_t* tiles,
