@@ -58,18 +58,22 @@ __device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* r
   }
 }
 
-// Projection of one expert block: ac[i] = x[row] . wg[tab_row0 + e] and (noisy)
+// Projection of one expert block: ac[i] = x[row] . wg[tab_row0 + e] and (NOISY)
 // ar[i] = x[row] . wn[tab_row0 + e] for row = acc_row(i, lane) and
 // e = blk + 32 * wave + (lane & 31).  Columns past E read a valid table row
-// and are never used; waves with no valid column skip the MFMAs.
-template <typename T>
+// and are never used; waves with no valid column skip the MFMAs.  XLDS: the
+// input rows are in the LDS tile Xs (bf16 only).
+template <typename T, bool NOISY, bool XLDS>
 struct BlockProj;
 
-template <>
-struct BlockProj<bf16_t> {
+template <bool NOISY, bool XLDS>
+struct BlockProj<bf16_t, NOISY, XLDS> {
+  static __device__ __forceinline__ u32x4 ld(const bf16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+  }
   static __device__ __forceinline__ void run(const TileX<bf16_t>& tx, int d, const void* wg,
-                                             const void* wn, bool noisy, int tab_row0, int blk,
-                                             int E, f32x16& ac, f32x16& ar) {
+                                             const void* wn, int tab_row0, int blk, int E,
+                                             f32x16& ac, f32x16& ar) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c = lane & 31, kh = (lane >> 5) * 8;
     ac = f32x16{};
@@ -77,58 +81,62 @@ struct BlockProj<bf16_t> {
     if (blk + w * 32 >= E) return;
     const int64_t trow = tab_row0 + min(blk + w * 32 + c, E - 1);
     const bf16_t* pg = (const bf16_t*)wg + trow * d + kh;
-    const bf16_t* pn = noisy ? (const bf16_t*)wn + trow * d + kh : pg;
+    const bf16_t* pn = NOISY ? (const bf16_t*)wn + trow * d + kh : pg;
+    const bf16_t* pa = XLDS ? tx.Xs + c * tx.xld + kh : tx.x + (int64_t)tx.rows[c] * d + kh;
     const int KS = d / 16;
-    auto afrag = [&](int ks) -> bf16x8 {
-      if (tx.Xs) return *reinterpret_cast<const bf16x8*>(tx.Xs + c * tx.xld + ks * 16 + kh);
-      return load_bf16x8(tx.x + (int64_t)tx.rows[c] * d + ks * 16 + kh);
-    };
+    // ring slot i holds k-step g + i; refills past the last k-step re-read it
     u32x4 rg[GATE_RING], rn[GATE_RING];
 #pragma unroll
     for (int i = 0; i < GATE_RING; ++i) {
-      rg[i] = i < KS ? *reinterpret_cast<const u32x4*>(pg + i * 16) : u32x4{0u, 0u, 0u, 0u};
-      rn[i] = (noisy && i < KS) ? *reinterpret_cast<const u32x4*>(pn + i * 16)
-                                : u32x4{0u, 0u, 0u, 0u};
+      const int s = min(i, KS - 1);
+      rg[i] = ld(pg + s * 16);
+      if (NOISY) rn[i] = ld(pn + s * 16);
     }
-    for (int g = 0; g < KS; g += GATE_RING) {
+    int g = 0;
+    for (; g + GATE_RING < KS; g += GATE_RING) {
 #pragma unroll
       for (int i = 0; i < GATE_RING; ++i) {
-        const int ks = g + i;
-        if (ks < KS) {
-          const bf16x8 bg = __builtin_bit_cast(bf16x8, rg[i]);
-          const bf16x8 bn = __builtin_bit_cast(bf16x8, rn[i]);
-          if (ks + GATE_RING < KS) {
-            rg[i] = *reinterpret_cast<const u32x4*>(pg + (ks + GATE_RING) * 16);
-            if (noisy) rn[i] = *reinterpret_cast<const u32x4*>(pn + (ks + GATE_RING) * 16);
-          }
-          const bf16x8 a = afrag(ks);
-          ac = mfma32(a, bg, ac);
-          if (noisy) ar = mfma32(a, bn, ar);
-        }
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ld(pa + (g + i) * 16));
+        const bf16x8 bg = __builtin_bit_cast(bf16x8, rg[i]);
+        const bf16x8 bn = __builtin_bit_cast(bf16x8, rn[i]);
+        const int nx = min(g + GATE_RING + i, KS - 1);
+        rg[i] = ld(pg + nx * 16);
+        if (NOISY) rn[i] = ld(pn + nx * 16);
+        ac = mfma32(a, bg, ac);
+        if (NOISY) ar = mfma32(a, bn, ar);
       }
+    }
+    // last group: slots past KS carry duplicates and meet a zero input fragment
+#pragma unroll
+    for (int i = 0; i < GATE_RING; ++i) {
+      u32x4 av = ld(pa + min(g + i, KS - 1) * 16);
+      if (g + i >= KS) av = u32x4{0u, 0u, 0u, 0u};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+      ac = mfma32(a, __builtin_bit_cast(bf16x8, rg[i]), ac);
+      if (NOISY) ar = mfma32(a, __builtin_bit_cast(bf16x8, rn[i]), ar);
     }
   }
 };
 
-template <>
-struct BlockProj<float> {
+template <bool NOISY, bool XLDS>
+struct BlockProj<float, NOISY, XLDS> {
   static __device__ __forceinline__ void run(const TileX<float>& tx, int d, const void* wg,
-                                             const void* wn, bool noisy, int tab_row0, int blk,
-                                             int E, f32x16& ac, f32x16& ar) {
+                                             const void* wn, int tab_row0, int blk, int E,
+                                             f32x16& ac, f32x16& ar) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     ac = f32x16{};
     ar = f32x16{};
     if (blk + w * 32 >= E) return;
     const int64_t trow = tab_row0 + min(blk + w * 32 + (lane & 31), E - 1);
     const float* pg = (const float*)wg + trow * d;
-    const float* pn = noisy ? (const float*)wn + trow * d : pg;
+    const float* pn = NOISY ? (const float*)wn + trow * d : pg;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float* xr = tx.x + (int64_t)tx.rows[acc_row(i, lane)] * d;
       float sc = 0.f, sr = 0.f;
       for (int k = 0; k < d; ++k) {
         sc = fmaf(xr[k], pg[k], sc);
-        if (noisy) sr = fmaf(xr[k], pn[k], sr);
+        if (NOISY) sr = fmaf(xr[k], pn[k], sr);
       }
       ac[i] = sc;
       ar[i] = sr;
@@ -225,29 +233,26 @@ __device__ __forceinline__ void kept_gates(const float* ov, const int* oe, int k
   *k1th = (k < E) ? b : -INFINITY;
 }
 
-// Per-row facts the load estimate needs, shared through LDS.
-struct RowSel {
+// Per-row thresholds the load estimate needs, shared through LDS.
+struct RowThr {
   float kth, k1th;
-  int kept[8];
 };
 
 // One lane's load terms: sum over its 16 tile rows (register order) of
 // Phi((clean - theta) / sp), then the two half-waves holding the same expert
-// are added; rows at or past `valid` contribute 0.  Identical in the gate
-// and in the recompute kernel.
-__device__ __forceinline__ float load_column_sum(const f32x16& clean, const f32x16& sp, int e,
-                                                 int k, const RowSel* sel, int valid) {
+// are added; rows at or past `valid` contribute 0.  Bit r of `kept` says
+// whether tile row r keeps this lane's expert.  Identical in the gate and in
+// the recompute kernel.
+__device__ __forceinline__ float load_column_sum(const f32x16& clean, const f32x16& sp,
+                                                 uint32_t kept, const RowThr* thr, int valid) {
   const int lane = threadIdx.x & 63;
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = acc_row(i, lane);
-    const RowSel& rs = sel[r];
-    bool in = false;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) in |= (j < k && rs.kept[j] == e);
-    const float th = in ? rs.k1th : rs.kth;
-    const float p = normal_cdf_f((clean[i] - th) / sp[i]);
+    const RowThr rt = thr[r];
+    const float th = ((kept >> r) & 1u) ? rt.k1th : rt.kth;
+    const float p = normal_cdf_f((clean[i] - th) * rcp_hw(sp[i]));
     s += r < valid ? p : 0.f;
   }
   return s + __shfl_xor(s, 32, 64);
@@ -258,11 +263,10 @@ __device__ __forceinline__ float load_column_sum(const f32x16& clean, const f32x
 // noise row of tile row r (experts contiguous).  On return every lane of a
 // row's group holds the row's top-K1 in ov/oe, and cs/ss the clean scores
 // (bias included) and noise scales of the last expert block.
-template <typename T, int K1, typename EpsRow>
+template <typename T, int K1, bool NOISY, bool XLDS, typename EpsRow>
 __device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void* wn,
-                           const float* __restrict__ bias, int tab_row0, int E, bool noisy,
-                           EpsRow eps_row, float (*Hs)[HLD], float* ov, int* oe, f32x16& cs,
-                           f32x16& ss) {
+                           const float* __restrict__ bias, int tab_row0, int E, EpsRow eps_row,
+                           float (*Hs)[HLD], float* ov, int* oe, f32x16& cs, f32x16& ss) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = tid / GATE_TPR, sub = tid % GATE_TPR;
   TopList<K1> L;
@@ -273,15 +277,15 @@ __device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void
     // noise of this lane's 16 (row, expert) pairs, requested before the MFMAs
     float ep[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ep[i] = (noisy && ev) ? eps_row(acc_row(i, lane))[e] : 0.f;
+    for (int i = 0; i < 16; ++i) ep[i] = (NOISY && ev) ? eps_row(acc_row(i, lane))[e] : 0.f;
     f32x16 ac, ar;
-    BlockProj<T>::run(tx, d, wg, wn, noisy, tab_row0, blk, E, ac, ar);
+    BlockProj<T, NOISY, XLDS>::run(tx, d, wg, wn, tab_row0, blk, E, ac, ar);
     const float b = (bias && ev) ? bias[tab_row0 + e] : 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float c = ac[i] + b;
       float h = c;
-      if (noisy) {
+      if (NOISY) {
         const float sp = softplus_f(ar[i]);
         h = c + ep[i] * sp;
         ss[i] = sp;
@@ -302,37 +306,36 @@ __device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void
 // ---------------------------------------------------------------------------
 // Flat gate: tile = 32 consecutive tokens.  With a.part set (noisy gate,
 // E <= GATE_FUSED_LOAD_MAX_E) the kernel also writes the tile's row of
-// smooth-load partial sums.
+// smooth-load partial sums; with a.bits the tile's routing masks.  Both use
+// the masks sb[E] in LDS (bit r of sb[e]: tile row r keeps expert e).
 // ---------------------------------------------------------------------------
-template <typename T, int K1>
+template <typename T, int K1, bool NOISY, bool XLDS>
 __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a) {
   __shared__ float Hs[GATE_ROWS][HLD];
   __shared__ int rows[GATE_ROWS];
-  __shared__ RowSel sel[GATE_ROWS];
+  __shared__ RowThr thr[GATE_ROWS];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
   const int E = a.E;
   if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
-  const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
   const int xld = a.d + 8;
-  bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
-  // routing masks of the tile: after the input tile in dynamic LDS
-  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (xl ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
-  if (a.bits)
+  bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
+  const bool masks = a.bits || (NOISY && a.part);
+  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
+  if (masks)
     for (int i = tid; i < E; i += GATE_THREADS) sb[i] = 0u;
   __syncthreads();
-  if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
   __syncthreads();
-  const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
-  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
+  const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const float* eps = a.eps;
   auto eps_row = [&](int r) -> const float* { return eps + (int64_t)rows[r] * E; };
   float ov[K1];
   int oe[K1];
   f32x16 cs, ss;
-  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, a.bias, 0, E, noisy, eps_row, Hs, ov, oe, cs,
-                    ss);
+  score_tile<T, K1, NOISY, XLDS>(tx, a.d, a.w_gate, a.w_noise, a.bias, 0, E, eps_row, Hs, ov, oe,
+                                 cs, ss);
   int ke[K1];
   float kg[K1], kth, k1th;
   kept_gates<K1>(ov, oe, a.k, E, ke, kg, &kth, &k1th);
@@ -351,30 +354,23 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
         a.thr[2 * t] = kth;
         a.thr[2 * t + 1] = k1th;
       }
-      if (a.bits) {
+      if (masks) {
 #pragma unroll
         for (int j = 0; j < K1; ++j)
-          if (j < a.k) atomicOr(&sb[ke[j]], 1u << row);
+          if (j < a.k && (unsigned)ke[j] < (unsigned)E) atomicOr(&sb[ke[j]], 1u << row);
       }
     }
-    sel[row].kth = kth;
-    sel[row].k1th = k1th;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int v = -1;
-#pragma unroll
-      for (int q = 0; q < K1; ++q)
-        if (q == j && q < a.k) v = ke[q];
-      sel[row].kept[j] = v;
-    }
+    thr[row].kth = kth;
+    thr[row].k1th = k1th;
   }
-  if (a.part || a.bits) __syncthreads();
+  if (masks) __syncthreads();
   if (a.bits)
     for (int i = tid; i < E; i += GATE_THREADS) a.bits[(int64_t)blockIdx.x * E + i] = sb[i];
-  if (a.part) {
+  if (NOISY && a.part) {
     const int e = (tid >> 6) * 32 + (lane & 31);
     const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
-    const float s = load_column_sum(cs, ss, e, a.k, sel, valid);
+    const uint32_t kept = e < E ? sb[e] : 0u;
+    const float s = load_column_sum(cs, ss, kept, thr, valid);
     if (lane < 32 && e < E) a.part[(int64_t)blockIdx.x * E + e] = s;
   }
 }
@@ -385,7 +381,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
 // group g covers positions offsets_g[g] + 32*(i - tiles_g[g]) onward.
 // Writes the final experts g*Eg + j and gates gate_p * gate_s directly.
 // ---------------------------------------------------------------------------
-template <typename T, int K1>
+template <typename T, int K1, bool NOISY, bool XLDS>
 __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs a) {
   __shared__ float Hs[GATE_ROWS][HLD];
   __shared__ int rows[GATE_ROWS];
@@ -414,21 +410,19 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
     rows[tid] = as / a.kg;
   }
   __syncthreads();
-  const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
   const int xld = a.d + 8;
-  bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
-  if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
   __syncthreads();
-  const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
+  const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const int Eg = a.Eg, G = a.G;
-  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
   const float* eps = a.eps;
   auto eps_row = [&](int r) -> const float* { return eps + ((int64_t)rows[r] * G + g) * Eg; };
   float ov[K1];
   int oe[K1];
   f32x16 cs, ss;
-  score_tile<T, K1>(tx, a.d, a.w_gate, a.w_noise, nullptr, g * Eg, Eg, noisy, eps_row, Hs, ov, oe,
-                    cs, ss);
+  score_tile<T, K1, NOISY, XLDS>(tx, a.d, a.w_gate, a.w_noise, nullptr, g * Eg, Eg, eps_row, Hs,
+                                 ov, oe, cs, ss);
   const int row = tid / GATE_TPR;
   if (tid % GATE_TPR == 0 && row < n) {
     int ke[K1];
@@ -457,33 +451,38 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
 // with theta = thr[t][1] if e is kept by t, else thr[t][0]: the same terms,
 // in the same order, as the gate kernel's fused variant.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool XLDS>
 __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) {
   __shared__ int rows[GATE_ROWS];
-  __shared__ RowSel sel[GATE_ROWS];
+  __shared__ RowThr thr[GATE_ROWS];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  const int xld = a.d + 8;
+  bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
+  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
+  for (int i = tid; i < a.E; i += GATE_THREADS) sb[i] = 0u;
   if (tid < GATE_ROWS) {
     const int r = (int)min<int64_t>(t0 + tid, a.T - 1);
     rows[tid] = r;
-    sel[tid].kth = a.thr[2 * (int64_t)r];
-    sel[tid].k1th = a.thr[2 * (int64_t)r + 1];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sel[tid].kept[j] = j < a.k ? a.idx[(int64_t)r * a.k + j] : -1;
+    thr[tid].kth = a.thr[2 * (int64_t)r];
+    thr[tid].k1th = a.thr[2 * (int64_t)r + 1];
   }
   __syncthreads();
-  const bool xl = sizeof(T) == 2 && a.d <= GATE_XLDS_MAX_D;
-  const int xld = a.d + 8;
-  bf16_t* Xs = xl ? reinterpret_cast<bf16_t*>(dyn) : nullptr;
-  if (xl) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  // kept-expert masks of the tile's valid rows
+  for (int i = tid; i < GATE_ROWS * a.k; i += GATE_THREADS) {
+    const int r = i / a.k;
+    const int e = t0 + r < a.T ? a.idx[(t0 + r) * a.k + i % a.k] : -1;
+    if ((unsigned)e < (unsigned)a.E) atomicOr(&sb[e], 1u << r);
+  }
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
   __syncthreads();
-  const TileX<T> tx{(const T*)a.x, rows, Xs, xld};
+  const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
   for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
     const int e = blk + w * 32 + (lane & 31);
     f32x16 ac, ar;
-    BlockProj<T>::run(tx, a.d, a.w_gate, a.w_noise, true, 0, blk, a.E, ac, ar);
+    BlockProj<T, true, XLDS>::run(tx, a.d, a.w_gate, a.w_noise, 0, blk, a.E, ac, ar);
     const float b = (a.bias && e < a.E) ? a.bias[e] : 0.f;
     f32x16 cs, ss;
 #pragma unroll
@@ -491,7 +490,8 @@ __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) 
       cs[i] = ac[i] + b;
       ss[i] = softplus_f(ar[i]);
     }
-    const float s = load_column_sum(cs, ss, e, a.k, sel, valid);
+    const uint32_t kept = e < a.E ? sb[e] : 0u;
+    const float s = load_column_sum(cs, ss, kept, thr, valid);
     if (lane < 32 && e < a.E) a.part[(int64_t)blockIdx.x * a.E + e] = s;
   }
 }
@@ -502,6 +502,7 @@ __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) 
 static size_t xtile_bytes(bool bf16, int d) {
   return (bf16 && d <= GATE_XLDS_MAX_D) ? sizeof(bf16_t) * GATE_ROWS * (size_t)(d + 8) : 0;
 }
+
 
 // Raise a kernel's dynamic LDS limit when needed; `done` caches the largest
 // size already granted to that kernel.
@@ -514,23 +515,37 @@ static hipError_t set_lds(K kernel, size_t bytes, size_t* done) {
   return err;
 }
 
-template <typename T, int K1>
-static hipError_t launch_flat_k(const GateFlatArgs& a, size_t sh, hipStream_t s) {
+static bool xtile_in_lds(bool bf16, int d) { return bf16 && d <= GATE_XLDS_MAX_D; }
+
+template <typename T, int K1, bool NOISY, bool XLDS>
+static hipError_t launch_flat_v(const GateFlatArgs& a, size_t sh, hipStream_t s) {
   static size_t granted = 0;
-  hipError_t err = set_lds(gate_flat_kernel<T, K1>, sh, &granted);
+  hipError_t err = set_lds(gate_flat_kernel<T, K1, NOISY, XLDS>, sh, &granted);
   if (err != hipSuccess) return err;
   dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
-  hipLaunchKernelGGL((gate_flat_kernel<T, K1>), grid, dim3(GATE_THREADS), sh, s, a);
+  hipLaunchKernelGGL((gate_flat_kernel<T, K1, NOISY, XLDS>), grid, dim3(GATE_THREADS), sh, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int K1>
+static hipError_t launch_flat_k(const GateFlatArgs& a, size_t sh, bool noisy, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (xtile_in_lds(true, a.d))
+      return noisy ? launch_flat_v<T, K1, true, true>(a, sh, s)
+                   : launch_flat_v<T, K1, false, true>(a, sh, s);
+  }
+  return noisy ? launch_flat_v<T, K1, true, false>(a, sh, s)
+               : launch_flat_v<T, K1, false, false>(a, sh, s);
 }
 
 template <typename T>
 static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
+  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
   size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
-  if (a.bits) sh += sizeof(uint32_t) * (size_t)a.E;
-  if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, sh, s);
-  if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, sh, s);
-  return launch_flat_k<T, 9>(a, sh, s);
+  if (a.bits || (noisy && a.part)) sh += sizeof(uint32_t) * (size_t)a.E;
+  if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, sh, noisy, s);
+  if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, sh, noisy, s);
+  return launch_flat_k<T, 9>(a, sh, noisy, s);
 }
 
 bool gate_fuses_load(int E) { return E <= GATE_FUSED_LOAD_MAX_E; }
@@ -540,13 +555,26 @@ hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s) {
   return bf16 ? launch_flat_t<bf16_t>(a, s) : launch_flat_t<float>(a, s);
 }
 
+template <typename T, int K1, bool NOISY, bool XLDS>
+static hipError_t launch_group_v(const GateGroupArgs& a, int grid, size_t sh, hipStream_t s) {
+  static size_t granted = 0;
+  hipError_t err = set_lds(gate_group_kernel<T, K1, NOISY, XLDS>, sh, &granted);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((gate_group_kernel<T, K1, NOISY, XLDS>), dim3(grid), dim3(GATE_THREADS), sh,
+                     s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int K1>
 static hipError_t launch_group_k(const GateGroupArgs& a, int grid, size_t sh, hipStream_t s) {
-  static size_t granted = 0;
-  hipError_t err = set_lds(gate_group_kernel<T, K1>, sh, &granted);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gate_group_kernel<T, K1>), dim3(grid), dim3(GATE_THREADS), sh, s, a);
-  return hipGetLastError();
+  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
+  if constexpr (sizeof(T) == 2) {
+    if (xtile_in_lds(true, a.d))
+      return noisy ? launch_group_v<T, K1, true, true>(a, grid, sh, s)
+                   : launch_group_v<T, K1, false, true>(a, grid, sh, s);
+  }
+  return noisy ? launch_group_v<T, K1, true, false>(a, grid, sh, s)
+               : launch_group_v<T, K1, false, false>(a, grid, sh, s);
 }
 
 template <typename T>
@@ -564,19 +592,22 @@ hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStr
 
 int load_partial_blocks(int64_t T) { return (int)((T + GATE_ROWS - 1) / GATE_ROWS); }
 
+template <typename T, bool XLDS>
+static hipError_t launch_load_v(const LoadArgs& a, int blocks, size_t sh, hipStream_t s) {
+  static size_t granted = 0;
+  hipError_t err = set_lds(load_partial_kernel<T, XLDS>, sh, &granted);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((load_partial_kernel<T, XLDS>), dim3(blocks), dim3(GATE_THREADS), sh, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_load_partial(const LoadArgs& a, bool bf16, hipStream_t s) {
   const int blocks = load_partial_blocks(a.T);
   if (blocks == 0) return hipSuccess;
-  const size_t sh = xtile_bytes(bf16, a.d);
-  if (bf16) {
-    static size_t granted = 0;
-    hipError_t err = set_lds(load_partial_kernel<bf16_t>, sh, &granted);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((load_partial_kernel<bf16_t>), dim3(blocks), dim3(GATE_THREADS), sh, s, a);
-  } else {
-    hipLaunchKernelGGL((load_partial_kernel<float>), dim3(blocks), dim3(GATE_THREADS), sh, s, a);
-  }
-  return hipGetLastError();
+  const size_t sh = xtile_bytes(bf16, a.d) + sizeof(uint32_t) * (size_t)a.E;
+  if (!bf16) return launch_load_v<float, false>(a, blocks, sh, s);
+  return xtile_in_lds(true, a.d) ? launch_load_v<bf16_t, true>(a, blocks, sh, s)
+                                 : launch_load_v<bf16_t, false>(a, blocks, sh, s);
 }
 
 }  // namespace moe

@@ -398,3 +398,24 @@ def test_empty_batch():
     assert out["idx"].shape == (0, cfg.top_k)
     assert out["counts"].sum() == 0 and out["y"].shape == (0, cfg.d_model)
     assert out["cv2_importance"] == 0.0
+
+
+def test_published_erfc_fit_meets_its_error_bound():
+    """The kernels evaluate Phi through the Chebyshev fit of erfc from
+    Numerical Recipes (2nd ed., section 6.2, erfcc), whose stated fractional
+    error is below 1.2e-7.  Check that bound against scipy's erfc in float64
+    over the range the load estimate uses, so the kernel's approximation is
+    pinned to a library routine rather than to itself."""
+    x = np.linspace(-9.0, 9.0, 200001)
+    ax = np.abs(x)
+    t = 1.0 / (1.0 + 0.5 * ax)
+    coeffs = [0.17087277, -0.82215223, 1.48851587, -1.13520398, 0.27886807,
+              -0.18628806, 0.09678418, 0.37409196, 1.00002368, -1.26551223]
+    p = np.zeros_like(t)
+    for c in coeffs:
+        p = p * t + c
+    r = t * np.exp(p - ax * ax)
+    approx = np.where(x >= 0, r, 2.0 - r)
+    exact = scipy.special.erfc(x)
+    rel = np.abs(approx - exact) / exact
+    assert rel.max() < 1.2e-7
