@@ -26,6 +26,39 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_FP32_PEAK_TFLOPS = 157.3
 
+# HBM traffic of one launch of the fused expert kernel on the default workload,
+# from two rocprofv3 --pmc passes over this script (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch, averaged over the dispatches).  Each counter is
+# scaled by what it reads for a plain 512 MiB device-to-device copy
+# (--copy-calibration 512): FETCH_SIZE 262156 KiB for 524288 KiB read,
+# WRITE_SIZE 524288 KiB for 524288 KiB written.  Valid only while the kernel's
+# sources hash to `sources_sha256`; otherwise the traffic is reported as null.
+EXPERT_TRAFFIC = {
+    "config": "flat256",
+    "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
+                "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
+                "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
+    "sources_sha256": "75ff4538defeaba9a44a30bfcec84f7a7679b069f12faec26e8113c0cae9ee4e",
+    "fetch_kib": 288660.0, "fetch_scale": 524288.0 / 262156.0,
+    "write_kib": 32768.0, "write_scale": 524288.0 / 524288.0,
+}
+
+
+def expert_traffic_bytes(config_name, packed):
+    """Counter-derived HBM bytes per fused-kernel launch, or None when the
+    kernel or the workload differs from the one the counters were taken on."""
+    import hashlib
+    t = EXPERT_TRAFFIC
+    if config_name != t["config"] or not packed:
+        return None
+    h = hashlib.sha256()
+    for f in t["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != t["sources_sha256"]:
+        return None
+    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
+
 
 def describe(cfg):
     kind = "SwiGLU" if cfg.ffn == "swiglu" else "ReLU"
@@ -247,7 +280,8 @@ def main():
         peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
         tflops = flops / t_exp / 1e12
         res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                           "traffic": expert_traffic_bytes(args.config, packed is not None),
                            "kernel": "expert FFN stage (moe_expert_ffn)",
                            "bytes_per_launch": ebytes}
         res["stages_ms"] = stages
