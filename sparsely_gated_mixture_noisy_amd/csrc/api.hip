@@ -41,7 +41,7 @@ size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 // Every workspace region, at fixed offsets for a given configuration.
 struct Layout {
   size_t idx, gate, thr, counts, offsets, perm, inv, bits, base, tiles, desc, hid, ysorted, part,
-      imp, load;
+      imp_part, imp, load;
   size_t idx_p, gate_p, counts_g, offsets_g, perm_g, inv_g, bits_g, base_g, tiles_g;
   size_t total;
   int nb, load_blocks;
@@ -75,6 +75,7 @@ Layout layout(const moe_config* c) {
   L.hid = take(elem_size(c) * (size_t)A * c->d_hidden);
   L.ysorted = take(elem_size(c) * (size_t)A * c->d_model);
   L.part = take(4 * (size_t)L.load_blocks * E);
+  L.imp_part = take(gate_fuses_load(E) ? 4 * (size_t)L.nb * E : 0);
   L.imp = take(4 * (size_t)E);
   L.load = take(4 * (size_t)E);
   const int G = c->n_groups > 0 ? c->n_groups : 0;
@@ -196,7 +197,7 @@ moe_status hip_status(hipError_t e, const char* what) {
 // it also writes the routing masks of its 32-token tiles.
 moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const moe_params* p,
                    const moe_noise* n, int32_t* idx, float* gate, float* thr, float* part,
-                   uint32_t* bits, void* ws, hipStream_t s) {
+                   uint32_t* bits, float* imp_part, void* ws, hipStream_t s) {
   const bool bf16 = c->dtype == MOE_BF16;
   const bool noisy = c->noisy != 0;
   if (c->n_groups == 0) {
@@ -215,6 +216,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
     a.thr = thr;
     a.part = part;
     a.bits = bits;
+    a.imp_part = imp_part;
     return hip_status(launch_gate_flat(a, bf16, s), "gate");
   }
   const int G = c->n_groups, kg = c->k_groups;
@@ -283,9 +285,18 @@ int expert_tile_rows(const moe_config* c) {
 
 // have_bits: the flat gate already wrote the routing masks.  with_tiles: also
 // build the expert stage's tile map.
+// Balance statistics reduced by the routing step (flat gate with per-tile
+// partials); imp_part null: none.
+struct RouteStats {
+  const float* imp_part = nullptr;
+  const float* load_part = nullptr;
+  float *importance = nullptr, *load = nullptr, *out = nullptr;
+  float w_imp = 0.f, w_load = 0.f;
+};
+
 moe_status do_route(const moe_config* c, const Layout& L, const int32_t* idx, int32_t* counts,
                     int32_t* offsets, int32_t* perm, int32_t* inv, bool have_bits,
-                    bool with_tiles, void* ws, hipStream_t s) {
+                    bool with_tiles, void* ws, hipStream_t s, const RouteStats& st = RouteStats()) {
   RouteArgs r;
   r.idx = idx;
   r.T = c->tokens;
@@ -304,6 +315,15 @@ moe_status do_route(const moe_config* c, const Layout& L, const int32_t* idx, in
   const bool fused = c->dtype == MOE_BF16 &&
                      fused_ffn_supported(c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
   r.desc = fused ? at<int32_t>(ws, L.desc) : nullptr;
+  if (st.imp_part) {
+    r.imp_part = st.imp_part;
+    r.load_part = st.load_part;
+    r.importance = st.importance;
+    r.load = st.load;
+    r.bal_out = st.out;
+    r.w_imp = st.w_imp;
+    r.w_load = st.w_load;
+  }
   return hip_status(launch_route(r, s), "route");
 }
 
@@ -373,6 +393,7 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
   b.part = part;
   b.blocks = L.load_blocks;
   b.E = E;
+  b.k = c->top_k;
   b.w_imp = wi;
   b.w_load = wl;
   b.importance = importance;
@@ -431,8 +452,8 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
     return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_gate is NULL");
   if (thr && cfg->n_groups > 0) return fail(MOE_ERR_INVALID_ARG, "thr is for the flat gate only");
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
-  MOE_TRY(do_gate(cfg, layout(cfg), x, p, noise, topk_idx, topk_gate, thr, nullptr, nullptr, ws,
-                  (hipStream_t)stream));
+  MOE_TRY(do_gate(cfg, layout(cfg), x, p, noise, topk_idx, topk_gate, thr, nullptr, nullptr,
+                  nullptr, ws, (hipStream_t)stream));
   return ok();
 }
 
@@ -518,27 +539,40 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   void* y_sorted = at<void>(ws, L.ysorted);
   const bool balance = out->balance != nullptr;
   const bool smooth = balance && cfg->n_groups == 0 && cfg->noisy && cfg->tokens > 0;
-  float* thr = smooth ? at<float>(ws, L.thr) : nullptr;
-  // small expert counts: the gate kernel produces the load partials itself
-  const bool fused_load = smooth && gate_fuses_load(cfg->n_experts);
-  float* part = fused_load ? at<float>(ws, L.part) : nullptr;
   // the flat gate writes the routing masks; the routing step builds the
   // expert tile map
   const bool flat = cfg->n_groups == 0 && cfg->tokens > 0;
   uint32_t* bits = flat ? at<uint32_t>(ws, L.bits) : nullptr;
   const bool tiles = expert_tile_rows(cfg) > 0;
-  MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, part, bits, ws, s));
-  MOE_TRY(do_route(cfg, L, idx, counts, offsets, perm, inv, flat, tiles, ws, s));
+  float* imp = balance ? (out->importance ? out->importance : at<float>(ws, L.imp)) : nullptr;
+  float* load = balance ? (out->load ? out->load : at<float>(ws, L.load)) : nullptr;
+  // small expert counts: the gate kernel writes per-tile importance (and
+  // smooth-load) partials and the routing step reduces them
+  const bool fused_stats = balance && flat && gate_fuses_load(cfg->n_experts);
+  // thresholds for the smooth-load recompute kernel
+  float* thr = smooth && !fused_stats ? at<float>(ws, L.thr) : nullptr;
+  RouteStats st;
+  float* part = nullptr;
+  if (fused_stats) {
+    part = smooth ? at<float>(ws, L.part) : nullptr;
+    st.imp_part = at<float>(ws, L.imp_part);
+    st.load_part = part;
+    st.importance = imp;
+    st.load = load;
+    st.out = out->balance;
+    st.w_imp = w_importance;
+    st.w_load = w_load;
+  }
+  MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, part, bits,
+                  const_cast<float*>(st.imp_part), ws, s));
+  MOE_TRY(do_route(cfg, L, idx, counts, offsets, perm, inv, flat, tiles, ws, s, st));
   MOE_TRY(do_ffn(cfg, L, x, perm, offsets, p, y_sorted, tiles, ws, s));
   MOE_TRY(hip_status(launch_combine(y_sorted, inv, gate, cfg->tokens, cfg->top_k, cfg->d_model,
                                     cfg->dtype == MOE_BF16, out->y, s),
                      "combine"));
-  if (balance) {
-    float* imp = out->importance ? out->importance : at<float>(ws, L.imp);
-    float* load = out->load ? out->load : at<float>(ws, L.load);
+  if (balance && !fused_stats)
     MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, perm, offsets, w_importance, w_load, imp,
-                       load, out->balance, fused_load, ws, s));
-  }
+                       load, out->balance, false, ws, s));
   return ok();
 }
 

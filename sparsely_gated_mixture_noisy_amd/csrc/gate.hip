@@ -306,14 +306,18 @@ __device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void
 // ---------------------------------------------------------------------------
 // Flat gate: tile = 32 consecutive tokens.  With a.part set (noisy gate,
 // E <= GATE_FUSED_LOAD_MAX_E) the kernel also writes the tile's row of
-// smooth-load partial sums; with a.bits the tile's routing masks.  Both use
-// the masks sb[E] in LDS (bit r of sb[e]: tile row r keeps expert e).
+// smooth-load partial sums; with a.imp_part (E <= GATE_FUSED_LOAD_MAX_E) its
+// row of gate sums per expert (rows in ascending order); with a.bits the
+// tile's routing masks.  All use the masks sb[E] in LDS (bit r of sb[e]:
+// tile row r keeps expert e).
 // ---------------------------------------------------------------------------
 template <typename T, int K1, bool NOISY, bool XLDS>
 __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a) {
   __shared__ float Hs[GATE_ROWS][HLD];
   __shared__ int rows[GATE_ROWS];
   __shared__ RowThr thr[GATE_ROWS];
+  __shared__ int kle[GATE_ROWS][8];    // kept experts of each row
+  __shared__ float klg[GATE_ROWS][8];  // and their gates
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
   if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
   const int xld = a.d + 8;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
-  const bool masks = a.bits || (NOISY && a.part);
+  const bool masks = a.bits || (NOISY && a.part) || a.imp_part;
   uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
   if (masks)
     for (int i = tid; i < E; i += GATE_THREADS) sb[i] = 0u;
@@ -362,8 +366,28 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
     }
     thr[row].kth = kth;
     thr[row].k1th = k1th;
+#pragma unroll
+    for (int j = 0; j < K1; ++j) {
+      if (j < a.k && j < 8) {
+        kle[row][j] = ke[j];
+        klg[row][j] = kg[j];
+      }
+    }
   }
   if (masks) __syncthreads();
+  if (a.imp_part) {
+    for (int e = tid; e < E; e += GATE_THREADS) {
+      uint32_t m = sb[e];
+      float s = 0.f;
+      while (m) {
+        const int r = __ffs(m) - 1;
+        m &= m - 1u;
+        for (int j = 0; j < a.k; ++j)
+          if (kle[r][j] == e) s += klg[r][j];
+      }
+      a.imp_part[(int64_t)blockIdx.x * E + e] = s;
+    }
+  }
   if (a.bits)
     for (int i = tid; i < E; i += GATE_THREADS) a.bits[(int64_t)blockIdx.x * E + i] = sb[i];
   if (NOISY && a.part) {
@@ -542,7 +566,7 @@ template <typename T>
 static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
   const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
   size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
-  if (a.bits || (noisy && a.part)) sh += sizeof(uint32_t) * (size_t)a.E;
+  if (a.bits || (noisy && a.part) || a.imp_part) sh += sizeof(uint32_t) * (size_t)a.E;
   if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, sh, noisy, s);
   if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, sh, noisy, s);
   return launch_flat_k<T, 9>(a, sh, noisy, s);

@@ -110,6 +110,38 @@ __device__ __forceinline__ bool ranks_before(float v1, int e1, float v2, int e2)
   return v1 > v2 || (v1 == v2 && e1 < e2);
 }
 
+// Sum of one double per thread over a workgroup of NT threads (NT a power of
+// two), by a fixed tree in LDS: the result does not depend on scheduling.
+template <int NT>
+__device__ double block_sum_f64(double v) {
+  __shared__ double red[NT];
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = NT / 2; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// Squared coefficient of variation of v[0..E): population variance / mean^2
+// in fp64 (0 when the mean is 0).  Called by all NT threads of a workgroup.
+template <int NT>
+__device__ double cv2_of(const float* v, int E) {
+  double s = 0.0;
+  for (int i = threadIdx.x; i < E; i += NT) s += (double)v[i];
+  const double mean = block_sum_f64<NT>(s) / E;
+  double q = 0.0;
+  for (int i = threadIdx.x; i < E; i += NT) {
+    const double dv = (double)v[i] - mean;
+    q += dv * dv;
+  }
+  const double var = block_sum_f64<NT>(q) / E;
+  return mean == 0.0 ? 0.0 : var / (mean * mean);
+}
+
 // Map a linear workgroup id to a tile id so that consecutive tile ids land on
 // the same XCD (workgroups are dispatched round-robin over the 8 XCDs) and are
 // dispatched close in time; tiles of one expert then share that XCD's L2.

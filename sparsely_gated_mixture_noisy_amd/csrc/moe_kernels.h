@@ -19,6 +19,7 @@ struct GateFlatArgs {
   float* thr;     // [T][2] or null
   float* part;    // [ceil(T/32)][E] smooth-load partials (noisy, E <= 256) or null
   uint32_t* bits; // [ceil(T/32)][E] routing masks of the tile's tokens, or null
+  float* imp_part = nullptr;  // [ceil(T/32)][E] gate sums of the tile's tokens (E <= 256) or null
 };
 hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s);
 constexpr int GATE_FUSED_LOAD_MAX_E = 256;
@@ -70,6 +71,14 @@ struct RouteArgs {
   int tile_rows;       // > 0: also build the expert tile map (tiles, desc)
   int32_t* tiles;      // [E+1]
   int32_t* desc;       // [tiles][3] or null
+  // Balance statistics from per-block partials, reduced alongside the counts
+  // (importance null: skipped).  load_part null: load = counts.
+  const float* imp_part = nullptr;   // [NB][E]
+  const float* load_part = nullptr;  // [NB][E] or null
+  float* importance = nullptr;       // [E]
+  float* load = nullptr;             // [E]
+  float* bal_out = nullptr;          // [3]: CV^2(importance), CV^2(load), weighted sum
+  float w_imp = 0.f, w_load = 0.f;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
@@ -117,11 +126,11 @@ hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float*
 // importance[e], load[e] (= sum_b part[b][e], or the row count when part is
 // null), then the CV^2 / loss triple.
 struct BalanceArgs {
-  const int32_t* perm;
-  const int32_t* offsets;
-  const float* gate;
-  const float* part;  // [blocks][E] or null
-  int blocks, E;
+  const int32_t* perm;     // expert-sorted assignments (token t, slot s) -> t*k + s
+  const int32_t* offsets;  // [E+1]
+  const float* gate;       // [T][k]
+  const float* part;       // [blocks][E] or null
+  int blocks, E, k;        // blocks = ceil(T / 32)
   float w_imp, w_load;
   float* importance;
   float* load;

@@ -20,6 +20,9 @@
 //                  also writes offsets and, when asked, the expert stage's
 //                  tile map; pos = offsets[e] + base[b][e] + in-block rank,
 //                  perm[pos] = a, inv[a] = pos
+// With balance partials (per-block gate sums and smooth-load terms from the
+// flat gate), route_colscan also reduces them to importance[e] and load[e],
+// and workgroup 0 of route_scatter turns those into the CV^2 values.
 // No kernel here fences across workgroups: results cross kernel boundaries.
 #include "moe_device.h"
 #include "moe_kernels.h"
@@ -145,9 +148,48 @@ __global__ __launch_bounds__(SCAN_THREADS) void route_colscan_kernel(RouteArgs a
     }
     if (range == 0) a.counts[e] = tot;
   }
+  if (a.importance) {
+    // importance and load of the same 16 experts: each range summed in
+    // ascending block order, then the 64 range sums in range order
+    __shared__ float pimp[64][SCAN_EXPERTS], pload[64][SCAN_EXPERTS];
+    float si = 0.f, sl = 0.f;
+    if (e < a.E) {
+      for (int b = b0; b < b1; ++b) {
+        si += a.imp_part[(int64_t)b * a.E + e];
+        if (a.load_part) sl += a.load_part[(int64_t)b * a.E + e];
+      }
+    }
+    pimp[range][le] = si;
+    pload[range][le] = sl;
+    __syncthreads();
+    if (range == 0 && e < a.E) {
+      float ti = 0.f, tl = 0.f;
+      for (int i = 0; i < 64; ++i) {
+        ti += pimp[i][le];
+        tl += pload[i][le];
+      }
+      a.importance[e] = ti;
+      a.load[e] = a.load_part ? tl : (float)tot;
+    }
+  }
 }
 
 constexpr int SCATTER_THREADS = 256;
+
+// Exclusive scan over the 256 thread sums in tsum (Hillis-Steele in LDS);
+// returns the thread's exclusive base; tsum[SCATTER_THREADS - 1] ends as the
+// total.  Called by all SCATTER_THREADS threads.
+__device__ int scan_thread_sums(int* tsum) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  for (int d = 1; d < SCATTER_THREADS; d <<= 1) {
+    const int v = tid >= d ? tsum[tid - d] : 0;
+    __syncthreads();
+    tsum[tid] += v;
+    __syncthreads();
+  }
+  return tid > 0 ? tsum[tid - 1] : 0;
+}
 
 // Exclusive scan of counts[0..E) into off[0..E] (LDS) by one workgroup of
 // SCATTER_THREADS threads: thread i owns a contiguous run of experts.
@@ -162,18 +204,41 @@ __device__ void scan_counts(const int32_t* counts, int E, int* off) {
     s += counts[e];
   }
   tsum[tid] = s;
-  __syncthreads();
-  // exclusive scan of the 256 thread sums (Hillis-Steele in LDS)
-  for (int d = 1; d < SCATTER_THREADS; d <<= 1) {
-    const int v = tid >= d ? tsum[tid - d] : 0;
-    __syncthreads();
-    tsum[tid] += v;
-    __syncthreads();
-  }
-  const int base = tid > 0 ? tsum[tid - 1] : 0;
+  const int base = scan_thread_sums(tsum);
   for (int e = e0; e < e1; ++e) off[e] += base;
   if (tid == SCATTER_THREADS - 1) off[E] = tsum[tid];
   __syncthreads();
+}
+
+// The expert stage's tile map from the offsets in LDS, by one workgroup of
+// SCATTER_THREADS threads: tiles[e] = first tile of expert e (exclusive scan
+// of ceil(count / rows)), tiles[E] = total; with desc (may be null),
+// desc[q] = {expert, first position, rows}, an expert's rows split into
+// near-equal tiles.
+__device__ void scatter_tile_map(const int* off, int E, int rows, int32_t* tiles, int32_t* desc) {
+  __shared__ int tsum[SCATTER_THREADS];
+  const int tid = threadIdx.x;
+  const int per = (E + SCATTER_THREADS - 1) / SCATTER_THREADS;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e) s += (off[e + 1] - off[e] + rows - 1) / rows;
+  tsum[tid] = s;
+  int run = scan_thread_sums(tsum);
+  for (int e = e0; e < e1; ++e) {
+    const int m = off[e + 1] - off[e], nt = (m + rows - 1) / rows;
+    tiles[e] = run;
+    if (desc && nt > 0) {
+      const int base = m / nt, rem = m % nt;
+      for (int i = 0; i < nt; ++i) {
+        int32_t* d = desc + 3 * (int64_t)(run + i);
+        d[0] = e;
+        d[1] = off[e] + i * base + min(i, rem);
+        d[2] = base + (i < rem ? 1 : 0);
+      }
+    }
+    run += nt;
+  }
+  if (tid == SCATTER_THREADS - 1) tiles[E] = tsum[tid];
 }
 
 __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArgs a) {
@@ -182,6 +247,17 @@ __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArg
   scan_counts(a.counts, a.E, off);
   if (b == 0) {
     for (int e = tid; e <= a.E; e += SCATTER_THREADS) a.offsets[e] = off[e];
+    if (a.tile_rows > 0) scatter_tile_map(off, a.E, a.tile_rows, a.tiles, a.desc);
+    if (a.bal_out) {
+      // CV^2 of the vectors the column scan reduced
+      const double ci = cv2_of<SCATTER_THREADS>(a.importance, a.E);
+      const double cl = cv2_of<SCATTER_THREADS>(a.load, a.E);
+      if (tid == 0) {
+        a.bal_out[0] = (float)ci;
+        a.bal_out[1] = (float)cl;
+        a.bal_out[2] = (float)((double)a.w_imp * ci + (double)a.w_load * cl);
+      }
+    }
   }
   const int64_t t0 = (int64_t)b * ROUTE_BLOCK_TOKENS;
   const int nt = (int)min<int64_t>(ROUTE_BLOCK_TOKENS, a.T - t0);
@@ -194,16 +270,6 @@ __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArg
     a.perm[pos] = (int32_t)as;
     a.inv[as] = pos;
   }
-}
-
-// The expert stage's tile map from counts and offsets (one workgroup).
-__global__ __launch_bounds__(SCAN_THREADS) void tile_map_counts_kernel(const int32_t* counts,
-                                                                       const int32_t* offsets,
-                                                                       int E, int rows,
-                                                                       int32_t* tiles,
-                                                                       int32_t* desc) {
-  build_tile_map(
-      E, rows, [&](int e) { return counts[e]; }, [&](int e) { return offsets[e]; }, tiles, desc);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
@@ -224,9 +290,6 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
                      dim3(SCAN_THREADS), 0, s, a);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(a.NB), dim3(SCATTER_THREADS),
                      sizeof(int) * (size_t)(a.E + 1), s, a);
-  if (a.tile_rows > 0)
-    hipLaunchKernelGGL(tile_map_counts_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a.counts,
-                       a.offsets, a.E, a.tile_rows, a.tiles, a.desc);
   return hipGetLastError();
 }
 
