@@ -230,6 +230,10 @@ def main():
     packed = L.pack_experts(cfg, inp)
     if packed is not None:
         inp = dict(inp, w_packed=packed)
+    # likewise the gate tables into the gate kernels' stream order
+    gpacked = L.pack_gate(cfg, inp)
+    if gpacked is not None:
+        inp = dict(inp, w_gate_packed=gpacked)
     torch.cuda.synchronize()
     fwd = L.Forward(cfg, inp["x"], inp, inp, balance=True)
     for _ in range(args.warmup):
@@ -267,7 +271,8 @@ def main():
         "config": {"workload": describe(cfg), "tokens": cfg.tokens, "d_model": cfg.d_model,
                    "n_experts": cfg.n_experts, "d_hidden": cfg.d_hidden, "top_k": cfg.top_k,
                    "ffn": cfg.ffn, "noisy": cfg.noisy,
-                   "expert_tables": "packed" if packed is not None else "plain"},
+                   "expert_tables": "packed" if packed is not None else "plain",
+                   "gate_tables": "packed" if gpacked is not None else "plain"},
     }
     flops, ebytes, hit = expert_work(cfg, counts)
     if not args.no_stages:

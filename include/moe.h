@@ -94,6 +94,10 @@ typedef struct moe_config {
  *             the expert stage reads it instead of w1 / w2 (which may then
  *             be NULL).  Same values, laid out in the order the expert
  *             kernel streams them.
+ *   w_gate_packed  nullable: w_gate and w_noise repacked by moe_pack_gate;
+ *             when given, the gate and smooth-load kernels read it instead
+ *             of w_gate / w_noise (which must still be given: the
+ *             validation and the fp32 paths use them).  Same values.
  * For the hierarchy, rows g*Eg .. g*Eg+Eg-1 of w_gate / w_noise are the
  * secondary tables of group g. */
 typedef struct moe_params {
@@ -106,6 +110,7 @@ typedef struct moe_params {
   const void* w3;
   const void* w2;
   const void* w_packed;
+  const void* w_gate_packed;
 } moe_params;
 
 /* Noise draws, float32 ~ N(0,1), supplied by the caller (NULL = no noise).
@@ -176,6 +181,22 @@ size_t moe_packed_experts_size(const moe_config* cfg);
  * Returns MOE_ERR_UNSUPPORTED when the configuration has no packed form. */
 moe_status moe_pack_experts(const moe_config* cfg, const moe_params* p, void* packed,
                             void* stream);
+
+/* Bytes of the packed gate tables for cfg, or 0 when the configuration has
+ * no packed form (packing applies to bf16 gates with d_model <= 1024). */
+size_t moe_packed_gate_size(const moe_config* cfg);
+
+/* Repack p->w_gate (and p->w_noise when cfg->noisy) into `packed`
+ * (moe_packed_gate_size bytes, 16-byte aligned) in the fragment order the
+ * gate kernels consume, so that each of their wave-wide table loads reads
+ * 1 KB of contiguous memory instead of 32 B from each of 32 rows.  A
+ * one-time transform of the parameters; the values are unchanged and the
+ * gate's results are bitwise those of the unpacked tables.  Layout: per
+ * table group g (the hierarchy's groups, else one), per block of 32 experts
+ * (the last one padded by repeating its last expert), per 64 columns, per
+ * table (gate, then noise), four 1 KB pieces.  Returns MOE_ERR_UNSUPPORTED
+ * when the configuration has no packed form. */
+moe_status moe_pack_gate(const moe_config* cfg, const moe_params* p, void* packed, void* stream);
 
 /* Combine: y[t] = sum over slots s (ascending) of
  * topk_gate[t][s] * y_sorted[inv[t*k+s]], accumulated in fp32

@@ -7,5 +7,5 @@ its absence is an error.
 """
 from .inputs import CONFIGS, MoEConfig, make_inputs  # noqa: F401
 from ._lib import (Forward, ForwardOut, MoEError, Workspace, balance_loss,  # noqa: F401
-                   combine, expert_ffn, forward, gate, load, pack_experts,
-                   packed_experts_size, route, workspace, workspace_size)
+                   combine, expert_ffn, forward, gate, load, pack_experts, pack_gate,
+                   packed_experts_size, packed_gate_size, route, workspace, workspace_size)

@@ -47,7 +47,7 @@ class moe_config(ctypes.Structure):
 class moe_params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_gate", "w_noise", "bias", "w_gate_p", "w_noise_p", "w1", "w3", "w2",
-                 "w_packed")]
+                 "w_packed", "w_gate_packed")]
 
 
 class moe_noise(ctypes.Structure):
@@ -78,6 +78,9 @@ _SIGS = {
     "moe_packed_experts_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config)]),
     "moe_pack_experts": (ctypes.c_int, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_params),
                                         _P, _P]),
+    "moe_packed_gate_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config)]),
+    "moe_pack_gate": (ctypes.c_int, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_params),
+                                     _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -161,6 +164,25 @@ def pack_experts(cfg: MoEConfig, params) -> Optional[torch.Tensor]:
     c, p = make_config(cfg), make_params(params)
     _check(load().moe_pack_experts(ctypes.byref(c), ctypes.byref(p), _ptr(out), _stream()),
            "moe_pack_experts")
+    return out
+
+
+def packed_gate_size(cfg: MoEConfig) -> int:
+    c = make_config(cfg)
+    return int(load().moe_packed_gate_size(ctypes.byref(c)))
+
+
+def pack_gate(cfg: MoEConfig, params) -> Optional[torch.Tensor]:
+    """The gate tables w_gate/w_noise repacked for the gate kernels' table
+    stream (a bf16 tensor on the tables' device), or None when the layer has
+    no packed form."""
+    n = packed_gate_size(cfg)
+    if n == 0:
+        return None
+    out = torch.empty(n // 2, dtype=torch.bfloat16, device=params["w_gate"].device)
+    c, p = make_config(cfg), make_params(params)
+    _check(load().moe_pack_gate(ctypes.byref(c), ctypes.byref(p), _ptr(out), _stream()),
+           "moe_pack_gate")
     return out
 
 

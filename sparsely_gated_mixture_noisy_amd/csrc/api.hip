@@ -142,6 +142,13 @@ moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// Packed gate geometry of cfg: table groups, experts per group, tables.
+bool gate_packable(const moe_config* c) {
+  return gate_pack_supported(c->dtype == MOE_BF16, c->d_model);
+}
+int gate_pack_groups(const moe_config* c) { return c->n_groups > 0 ? c->n_groups : 1; }
+int gate_pack_tables(const moe_config* c) { return c->noisy ? 2 : 1; }
+
 moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_params* p,
                              const moe_noise* n) {
   if (!x && c->tokens > 0) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
@@ -152,6 +159,12 @@ moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_param
   if (c->noisy) {
     if (rows && (!n || !n->eps)) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps");
     if (!p->w_noise) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs w_noise");
+  }
+  if (p->w_gate_packed) {
+    if (!gate_packable(c))
+      return fail(MOE_ERR_UNSUPPORTED, "packed gate tables need bf16 and d_model %% 64 == 0");
+    if (reinterpret_cast<uintptr_t>(p->w_gate_packed) & 15)
+      return fail(MOE_ERR_INVALID_ARG, "w_gate_packed must be 16-byte aligned");
   }
   if (c->n_groups > 0) {
     if (!p->w_gate_p) return fail(MOE_ERR_INVALID_ARG, "hierarchy needs w_gate_p");
@@ -217,6 +230,8 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
     a.part = part;
     a.bits = bits;
     a.imp_part = imp_part;
+    a.w_pack = p->w_gate_packed;
+    a.pack_nt = gate_pack_tables(c);
     return hip_status(launch_gate_flat(a, bf16, s), "gate");
   }
   const int G = c->n_groups, kg = c->k_groups;
@@ -273,6 +288,8 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   ga.gate_p = gate_p;
   ga.idx = idx;
   ga.gate = gate;
+  ga.w_pack = p->w_gate_packed;
+  ga.pack_nt = gate_pack_tables(c);
   const int64_t grid = (c->tokens * kg + 31) / 32 + G;
   return hip_status(launch_gate_group(ga, (int)grid, bf16, s), "secondary gate");
 }
@@ -384,6 +401,7 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
     la.E = E;
     la.k = c->top_k;
     la.part = part;
+    la.w_pack = p->w_gate_packed;
     MOE_TRY(hip_status(launch_load_partial(la, c->dtype == MOE_BF16, s), "load"));
   }
   BalanceArgs b;
@@ -440,6 +458,28 @@ moe_status moe_pack_experts(const moe_config* cfg, const moe_params* p, void* pa
   MOE_TRY(hip_status(launch_pack_experts(p->w1, p->w2, cfg->n_experts, cfg->d_model,
                                          cfg->d_hidden, packed, (hipStream_t)stream),
                      "pack"));
+  return ok();
+}
+
+size_t moe_packed_gate_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK || !gate_packable(cfg)) return 0;
+  const int ng = gate_pack_groups(cfg);
+  return gate_packed_bytes(ng, cfg->n_experts / ng, cfg->d_model, gate_pack_tables(cfg));
+}
+
+moe_status moe_pack_gate(const moe_config* cfg, const moe_params* p, void* packed, void* stream) {
+  MOE_TRY(check_config(cfg));
+  if (!gate_packable(cfg))
+    return fail(MOE_ERR_UNSUPPORTED, "packed gate tables need bf16 and d_model %% 64 == 0");
+  if (!p || !p->w_gate || (cfg->noisy && !p->w_noise) || !packed)
+    return fail(MOE_ERR_INVALID_ARG, "w_gate / w_noise / packed is NULL");
+  if (reinterpret_cast<uintptr_t>(packed) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  const int ng = gate_pack_groups(cfg);
+  MOE_TRY(hip_status(launch_pack_gate(p->w_gate, p->w_noise, ng, cfg->n_experts / ng,
+                                      cfg->d_model, gate_pack_tables(cfg), packed,
+                                      (hipStream_t)stream),
+                     "pack gate"));
   return ok();
 }
 

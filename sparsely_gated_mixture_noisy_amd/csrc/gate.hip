@@ -29,7 +29,7 @@ constexpr int GATE_THREADS = 64 * GATE_WAVES;
 constexpr int GATE_BLOCK_E = 32 * GATE_WAVES;      // experts per projection block
 constexpr int GATE_TPR = GATE_THREADS / GATE_ROWS;  // selection lanes per row
 constexpr int GATE_XLDS_MAX_D = 1024;               // input tile in LDS up to this d_model
-constexpr int GATE_RING = 8;                        // table k-steps in flight per wave
+constexpr int GATE_RING = 16;                       // table k-steps in flight per wave
 constexpr int HLD = GATE_BLOCK_E + 1;               // LDS row stride of the score block
 
 // Tile row held in accumulator register i of lane l (32x32 MFMA layout).
@@ -45,6 +45,20 @@ struct TileX {
   const int* rows;
   const bf16_t* Xs;  // null: read x directly
   int xld;
+};
+
+// Where a block's table rows come from.  Unpacked: expert e is row row0 + e
+// of wg / wn ([*][d]).  Packed (bf16, see launch_pack_gate): 32-expert block
+// b of the group starts at block pk_blk0 + b of pk; per 64 columns it holds
+// pk_nt tables x four 1 KB pieces, piece j of a table giving lane l the 16
+// bytes the unpacked read of step j would give it.
+struct GateTabs {
+  const void* wg;
+  const void* wn;
+  int row0;
+  const bf16_t* pk;
+  int pk_blk0;
+  int pk_nt;
 };
 
 // Copy the 32 input rows of a tile to LDS (bf16, d % 8 == 0).
@@ -66,70 +80,105 @@ __device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* r
 template <typename T, bool NOISY, bool XLDS>
 struct BlockProj;
 
+// bf16: the contraction runs over groups of 64 columns.  Lane (c, h) of a
+// wave (c = lane % 32, h = lane / 32) loads 64 contiguous bytes of its table
+// row, columns 64G + 32h .. +31, as four 16-byte pieces j = 0..3; MFMA step j
+// of the group pairs piece j (columns 64G + 32h + 8j .. +7) with the input
+// columns at the same places.  The k order inside an MFMA is a permutation
+// of the columns, the same for both operands, so every product term appears
+// exactly once; the four loads of a piece run over whole cache lines back to
+// back.  A ring of GATE_RING / 4 groups per table stays in flight.
 template <bool NOISY, bool XLDS>
 struct BlockProj<bf16_t, NOISY, XLDS> {
+  static constexpr int RG = GATE_RING / 4;  // groups in flight per table
   static __device__ __forceinline__ u32x4 ld(const bf16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
   }
-  static __device__ __forceinline__ void run(const TileX<bf16_t>& tx, int d, const void* wg,
-                                             const void* wn, int tab_row0, int blk, int E,
-                                             f32x16& ac, f32x16& ar) {
+  static __device__ __forceinline__ void run(const TileX<bf16_t>& tx, int d, const GateTabs& tb,
+                                             int blk, int E, f32x16& ac, f32x16& ar) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int c = lane & 31, kh = (lane >> 5) * 8;
+    const int c = lane & 31, kh = (lane >> 5) * 32;
     ac = f32x16{};
     ar = f32x16{};
     if (blk + w * 32 >= E) return;
-    const int64_t trow = tab_row0 + min(blk + w * 32 + c, E - 1);
-    const bf16_t* pg = (const bf16_t*)wg + trow * d + kh;
-    const bf16_t* pn = NOISY ? (const bf16_t*)wn + trow * d + kh : pg;
-    const bf16_t* pa = XLDS ? tx.Xs + c * tx.xld + kh : tx.x + (int64_t)tx.rows[c] * d + kh;
-    const int KS = d / 16;
-    // ring slot i holds k-step g + i; refills past the last k-step re-read it
-    u32x4 rg[GATE_RING], rn[GATE_RING];
-#pragma unroll
-    for (int i = 0; i < GATE_RING; ++i) {
-      const int s = min(i, KS - 1);
-      rg[i] = ld(pg + s * 16);
-      if (NOISY) rn[i] = ld(pn + s * 16);
+    const int NG = d / 64;
+    // table piece j of column group G sits at pg + G * gs + j * js
+    const bf16_t *pg, *pn;
+    int gs, js;
+    if (tb.pk) {
+      const int64_t b = tb.pk_blk0 + (blk >> 5) + w;
+      pg = tb.pk + b * NG * tb.pk_nt * 2048 + lane * 8;
+      pn = pg + 2048;
+      gs = tb.pk_nt * 2048;
+      js = 512;
+    } else {
+      const int64_t trow = tb.row0 + min(blk + w * 32 + c, E - 1);
+      pg = (const bf16_t*)tb.wg + trow * d + kh;
+      pn = NOISY ? (const bf16_t*)tb.wn + trow * d + kh : pg;
+      gs = 64;
+      js = 8;
     }
-    int g = 0;
-    for (; g + GATE_RING < KS; g += GATE_RING) {
+    const bf16_t* pa = XLDS ? tx.Xs + c * tx.xld + kh : tx.x + (int64_t)tx.rows[c] * d + kh;
+    u32x4 rg[RG][4], rn[RG][4];
 #pragma unroll
-      for (int i = 0; i < GATE_RING; ++i) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, ld(pa + (g + i) * 16));
-        const bf16x8 bg = __builtin_bit_cast(bf16x8, rg[i]);
-        const bf16x8 bn = __builtin_bit_cast(bf16x8, rn[i]);
-        const int nx = min(g + GATE_RING + i, KS - 1);
-        rg[i] = ld(pg + nx * 16);
-        if (NOISY) rn[i] = ld(pn + nx * 16);
-        ac = mfma32(a, bg, ac);
-        if (NOISY) ar = mfma32(a, bn, ar);
+    for (int sl = 0; sl < RG; ++sl) {
+      const int G = min(sl, NG - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rg[sl][j] = ld(pg + G * gs + j * js);
+        if (NOISY) rn[sl][j] = ld(pn + G * gs + j * js);
       }
     }
-    // last group: slots past KS carry duplicates and meet a zero input fragment
+    int g = 0;
+    for (; g + RG < NG; g += RG) {
 #pragma unroll
-    for (int i = 0; i < GATE_RING; ++i) {
-      u32x4 av = ld(pa + min(g + i, KS - 1) * 16);
-      if (g + i >= KS) av = u32x4{0u, 0u, 0u, 0u};
-      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-      ac = mfma32(a, __builtin_bit_cast(bf16x8, rg[i]), ac);
-      if (NOISY) ar = mfma32(a, __builtin_bit_cast(bf16x8, rn[i]), ar);
+      for (int sl = 0; sl < RG; ++sl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, ld(pa + (g + sl) * 64 + j * 8));
+          ac = mfma32(a, __builtin_bit_cast(bf16x8, rg[sl][j]), ac);
+          if (NOISY) ar = mfma32(a, __builtin_bit_cast(bf16x8, rn[sl][j]), ar);
+        }
+        // refill the slot with the group RG further on (the last one again
+        // past the end)
+        const int nx = min(g + RG + sl, NG - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rg[sl][j] = ld(pg + nx * gs + j * js);
+          if (NOISY) rn[sl][j] = ld(pn + nx * gs + j * js);
+        }
+        // keep the refill ahead of the next slot's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // last groups: slots past NG carry duplicates and meet a zero input
+#pragma unroll
+    for (int sl = 0; sl < RG; ++sl) {
+      const int G = min(g + sl, NG - 1);
+      const bool live = g + sl < NG;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 av = ld(pa + G * 64 + j * 8);
+        if (!live) av = u32x4{0u, 0u, 0u, 0u};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+        ac = mfma32(a, __builtin_bit_cast(bf16x8, rg[sl][j]), ac);
+        if (NOISY) ar = mfma32(a, __builtin_bit_cast(bf16x8, rn[sl][j]), ar);
+      }
     }
   }
 };
 
 template <bool NOISY, bool XLDS>
 struct BlockProj<float, NOISY, XLDS> {
-  static __device__ __forceinline__ void run(const TileX<float>& tx, int d, const void* wg,
-                                             const void* wn, int tab_row0, int blk, int E,
-                                             f32x16& ac, f32x16& ar) {
+  static __device__ __forceinline__ void run(const TileX<float>& tx, int d, const GateTabs& tb,
+                                             int blk, int E, f32x16& ac, f32x16& ar) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     ac = f32x16{};
     ar = f32x16{};
     if (blk + w * 32 >= E) return;
-    const int64_t trow = tab_row0 + min(blk + w * 32 + (lane & 31), E - 1);
-    const float* pg = (const float*)wg + trow * d;
-    const float* pn = NOISY ? (const float*)wn + trow * d : pg;
+    const int64_t trow = tb.row0 + min(blk + w * 32 + (lane & 31), E - 1);
+    const float* pg = (const float*)tb.wg + trow * d;
+    const float* pn = NOISY ? (const float*)tb.wn + trow * d : pg;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float* xr = tx.x + (int64_t)tx.rows[acc_row(i, lane)] * d;
@@ -259,13 +308,13 @@ __device__ __forceinline__ float load_column_sum(const f32x16& clean, const f32x
 }
 
 // The scoring and selection of one 32-row tile against experts [0, E) of a
-// table block (expert e is table row tab_row0 + e).  eps_row(r) gives the
+// table block (tb).  eps_row(r) gives the
 // noise row of tile row r (experts contiguous).  On return every lane of a
 // row's group holds the row's top-K1 in ov/oe, and cs/ss the clean scores
 // (bias included) and noise scales of the last expert block.
 template <typename T, int K1, bool NOISY, bool XLDS, typename EpsRow>
-__device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void* wn,
-                           const float* __restrict__ bias, int tab_row0, int E, EpsRow eps_row,
+__device__ void score_tile(const TileX<T>& tx, int d, const GateTabs& tb,
+                           const float* __restrict__ bias, int E, EpsRow eps_row,
                            float (*Hs)[HLD], float* ov, int* oe, f32x16& cs, f32x16& ss) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = tid / GATE_TPR, sub = tid % GATE_TPR;
@@ -279,8 +328,8 @@ __device__ void score_tile(const TileX<T>& tx, int d, const void* wg, const void
 #pragma unroll
     for (int i = 0; i < 16; ++i) ep[i] = (NOISY && ev) ? eps_row(acc_row(i, lane))[e] : 0.f;
     f32x16 ac, ar;
-    BlockProj<T, NOISY, XLDS>::run(tx, d, wg, wn, tab_row0, blk, E, ac, ar);
-    const float b = (bias && ev) ? bias[tab_row0 + e] : 0.f;
+    BlockProj<T, NOISY, XLDS>::run(tx, d, tb, blk, E, ac, ar);
+    const float b = (bias && ev) ? bias[tb.row0 + e] : 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float c = ac[i] + b;
@@ -338,8 +387,8 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
   float ov[K1];
   int oe[K1];
   f32x16 cs, ss;
-  score_tile<T, K1, NOISY, XLDS>(tx, a.d, a.w_gate, a.w_noise, a.bias, 0, E, eps_row, Hs, ov, oe,
-                                 cs, ss);
+  const GateTabs tb{a.w_gate, a.w_noise, 0, (const bf16_t*)a.w_pack, 0, a.pack_nt};
+  score_tile<T, K1, NOISY, XLDS>(tx, a.d, tb, a.bias, E, eps_row, Hs, ov, oe, cs, ss);
   int ke[K1];
   float kg[K1], kth, k1th;
   kept_gates<K1>(ov, oe, a.k, E, ke, kg, &kth, &k1th);
@@ -445,8 +494,9 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
   float ov[K1];
   int oe[K1];
   f32x16 cs, ss;
-  score_tile<T, K1, NOISY, XLDS>(tx, a.d, a.w_gate, a.w_noise, nullptr, g * Eg, Eg, eps_row, Hs,
-                                 ov, oe, cs, ss);
+  const GateTabs tb{a.w_gate, a.w_noise, g * Eg, (const bf16_t*)a.w_pack,
+                    g * ((Eg + 31) / 32), a.pack_nt};
+  score_tile<T, K1, NOISY, XLDS>(tx, a.d, tb, nullptr, Eg, eps_row, Hs, ov, oe, cs, ss);
   const int row = tid / GATE_TPR;
   if (tid % GATE_TPR == 0 && row < n) {
     int ke[K1];
@@ -503,10 +553,11 @@ __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) 
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
+  const GateTabs tb{a.w_gate, a.w_noise, 0, (const bf16_t*)a.w_pack, 0, 2};
   for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
     const int e = blk + w * 32 + (lane & 31);
     f32x16 ac, ar;
-    BlockProj<T, true, XLDS>::run(tx, a.d, a.w_gate, a.w_noise, 0, blk, a.E, ac, ar);
+    BlockProj<T, true, XLDS>::run(tx, a.d, tb, blk, a.E, ac, ar);
     const float b = (a.bias && e < a.E) ? a.bias[e] : 0.f;
     f32x16 cs, ss;
 #pragma unroll
@@ -612,6 +663,45 @@ static hipError_t launch_group_t(const GateGroupArgs& a, int grid, hipStream_t s
 hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   return bf16 ? launch_group_t<bf16_t>(a, grid, s) : launch_group_t<float>(a, grid, s);
+}
+
+// packed[((((g*BG + b)*NG + G)*nt + t)*4 + j)*64 + l] (16 bytes each) =
+//   table t, row g*eg + min(32b + l%32, eg-1), columns 64G + 32(l/32) + 8j ..+7
+// with BG = ceil(eg/32), NG = d/64: the fragment lane l of the wave scoring
+// block b loads at step j of column group G.
+__global__ __launch_bounds__(256) void pack_gate_kernel(const bf16_t* wg, const bf16_t* wn,
+                                                        int ng, int eg, int d, int nt,
+                                                        bf16_t* out) {
+  const int BG = (eg + 31) / 32, NG = d / 64;
+  const int64_t n = (int64_t)ng * BG * NG * nt * 4 * 64;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  int64_t r = i;
+  const int l = (int)(r % 64); r /= 64;
+  const int j = (int)(r % 4); r /= 4;
+  const int t = (int)(r % nt); r /= nt;
+  const int G = (int)(r % NG); r /= NG;
+  const int b = (int)(r % BG);
+  const int g = (int)(r / BG);
+  const int64_t row = (int64_t)g * eg + min(32 * b + (l & 31), eg - 1);
+  const int col = 64 * G + 32 * (l >> 5) + 8 * j;
+  const bf16_t* src = (t == 0 ? wg : wn) + row * d + col;
+  *reinterpret_cast<u32x4*>(out + i * 8) = *reinterpret_cast<const u32x4*>(src);
+}
+
+bool gate_pack_supported(bool bf16, int d) { return bf16 && d > 0 && d % 64 == 0; }
+
+size_t gate_packed_bytes(int ng, int eg, int d, int nt) {
+  return sizeof(bf16_t) * (size_t)ng * (size_t)((eg + 31) / 32) * 32 * (size_t)d * nt;
+}
+
+hipError_t launch_pack_gate(const void* w_gate, const void* w_noise, int ng, int eg, int d, int nt,
+                            void* out, hipStream_t s) {
+  const int64_t n = (int64_t)ng * ((eg + 31) / 32) * (d / 64) * nt * 4 * 64;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const bf16_t*)w_gate, (const bf16_t*)w_noise, ng, eg, d, nt, (bf16_t*)out);
+  return hipGetLastError();
 }
 
 int load_partial_blocks(int64_t T) { return (int)((T + GATE_ROWS - 1) / GATE_ROWS); }

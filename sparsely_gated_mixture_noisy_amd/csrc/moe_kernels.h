@@ -20,8 +20,16 @@ struct GateFlatArgs {
   float* part;    // [ceil(T/32)][E] smooth-load partials (noisy, E <= 256) or null
   uint32_t* bits; // [ceil(T/32)][E] routing masks of the tile's tokens, or null
   float* imp_part = nullptr;  // [ceil(T/32)][E] gate sums of the tile's tokens (E <= 256) or null
+  const void* w_pack = nullptr;  // packed tables (bf16, launch_pack_gate) or null
+  int pack_nt = 0;               // tables in the packed form (1, or 2 with noise)
 };
 hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s);
+// Packed gate tables: groups ng of eg experts (flat gate: ng = 1, eg = E),
+// nt tables (w_gate, then w_noise when nt == 2), bf16, d % 64 == 0.
+bool gate_pack_supported(bool bf16, int d);
+size_t gate_packed_bytes(int ng, int eg, int d, int nt);
+hipError_t launch_pack_gate(const void* w_gate, const void* w_noise, int ng, int eg, int d, int nt,
+                            void* out, hipStream_t s);
 constexpr int GATE_FUSED_LOAD_MAX_E = 256;
 bool gate_fuses_load(int E);
 
@@ -37,6 +45,8 @@ struct GateGroupArgs {
   const float* gate_p;       // [T][kg] primary gates
   int32_t* idx;              // [T][kg*kpg] final experts
   float* gate;               // [T][kg*kpg] final gates
+  const void* w_pack = nullptr;  // packed secondary tables (G groups of Eg) or null
+  int pack_nt = 0;
 };
 hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStream_t s);
 
@@ -50,6 +60,7 @@ struct LoadArgs {
   int64_t T;
   int d, E, k;
   float* part;         // [ceil(T/32)][E]
+  const void* w_pack = nullptr;  // packed tables (nt = 2) or null
 };
 int load_partial_blocks(int64_t T);
 hipError_t launch_load_partial(const LoadArgs& a, bool bf16, hipStream_t s);

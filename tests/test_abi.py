@@ -88,3 +88,24 @@ def test_binding_raises_with_detail():
     with pytest.raises(L.MoEError) as ei:
         L._check(_gate_call(L.load(), cfg), "moe_gate")
     assert ei.value.status == L.MOE_ERR_INVALID_ARG
+
+
+def test_packed_table_sizes_and_rejections(lib):
+    """Packed gate tables: one 32-expert block per started 32 experts of a
+    group, both tables when noisy; none for fp32 gates."""
+    assert L.packed_gate_size(CONFIGS["flat256"]) == 8 * 32 * 512 * 2 * 2
+    assert L.packed_gate_size(CONFIGS["flat256"].replace(n_experts=40)) == 2 * 32 * 512 * 2 * 2
+    assert L.packed_gate_size(CONFIGS["hier4096"]) == 16 * 8 * 32 * 512 * 2 * 2
+    assert L.packed_gate_size(CONFIGS["mixtral"]) == 1 * 32 * 4096 * 1 * 2  # no noise table
+    assert L.packed_gate_size(CONFIGS["tiny"]) == 0
+    c = L.make_config(CONFIGS["tiny"])
+    p = L.moe_params(w_gate=FAKE, w_noise=FAKE)
+    assert lib.moe_pack_gate(ctypes.byref(c), ctypes.byref(p), FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    c = L.make_config(CONFIGS["flat256"])
+    assert lib.moe_pack_gate(ctypes.byref(c), ctypes.byref(p), FAKE + 8, None) == \
+        L.MOE_ERR_INVALID_ARG
+    # an unaligned packed table is refused by the gate before any launch
+    bad = L.moe_params(w_gate=FAKE, w_noise=FAKE, w_gate_packed=FAKE + 2)
+    assert _gate_call(L.load(), CONFIGS["flat256"], params=bad) == L.MOE_ERR_INVALID_ARG
+    bad = L.moe_params(w_gate=FAKE, w_noise=FAKE, w_gate_packed=FAKE)
+    assert _gate_call(L.load(), CONFIGS["tiny"], params=bad) == L.MOE_ERR_UNSUPPORTED

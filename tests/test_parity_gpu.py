@@ -247,3 +247,36 @@ def test_pack_rejects_unsupported_layers():
         assert L.packed_experts_size(cfg) == 0
         inp = make_inputs(cfg.replace(tokens=4), seed=0, device="cuda")
         assert L.pack_experts(cfg, inp) is None
+
+
+PACK_GATE_CASES = {
+    "flat256_t1000": CONFIGS["flat256"].replace(tokens=1000),
+    "flat_e40": CONFIGS["flat256"].replace(tokens=500, n_experts=40, top_k=3),
+    "zipf2048_t2000": CONFIGS["zipf2048"].replace(tokens=2000),
+    "hier_eg40": CONFIGS["hier4096"].replace(tokens=300, n_experts=16 * 40),
+    "mixtral_t64": CONFIGS["mixtral"].replace(tokens=64),
+}
+
+
+@pytest.mark.parametrize("name", list(PACK_GATE_CASES))
+def test_packed_gate_matches_unpacked_bitwise(name):
+    """The repacked gate tables hold the same values in the order the gate
+    kernels stream them: gate, smooth-load and whole-layer results are
+    bitwise those of the unpacked tables (expert counts that are not a
+    multiple of 32 exercise the padded last block)."""
+    cfg = PACK_GATE_CASES[name]
+    _say(f"[packed gate] {name}: {cfg}")
+    inp = make_inputs(cfg, seed=11, device="cuda")
+    gp = L.pack_gate(cfg, inp)
+    assert gp is not None and gp.numel() * 2 == L.packed_gate_size(cfg)
+    packed = dict(inp, w_gate_packed=gp)
+    a = L.gate(cfg, inp["x"], inp, inp)
+    b = L.gate(cfg, inp["x"], packed, inp)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert (u is None and v is None) or torch.equal(u, v)
+    fa = L.forward(cfg, inp["x"], inp, inp)
+    fb = L.forward(cfg, inp["x"], packed, inp)
+    torch.cuda.synchronize()
+    for key in ("y", "topk_idx", "topk_gate", "counts", "importance", "load", "balance"):
+        assert torch.equal(getattr(fa, key), getattr(fb, key)), key
