@@ -28,6 +28,7 @@ constexpr int GATE_WAVES = 8;
 constexpr int GATE_THREADS = 64 * GATE_WAVES;
 constexpr int GATE_BLOCK_E = 32 * GATE_WAVES;      // experts per projection block
 constexpr int GATE_TPR = GATE_THREADS / GATE_ROWS;  // selection lanes per row
+static_assert(GATE_TPR == 16, "a row's selection lanes form one 16-lane DPP row");
 constexpr int GATE_XLDS_MAX_D = 1024;               // input tile in LDS up to this d_model
 constexpr int GATE_RING = 16;                       // table k-steps in flight per wave
 constexpr int HLD = GATE_BLOCK_E + 1;               // LDS row stride of the score block
@@ -193,6 +194,36 @@ struct BlockProj<float, NOISY, XLDS> {
   }
 };
 
+// Cross-lane steps inside a 16-lane DPP row: the value of a partner lane.
+// XOR1 / XOR2 swap neighbours and pairs (quad permutations); HALF_MIRROR
+// pairs lane i with 7 - i of its half-row, MIRROR lane i with 15 - i.  Four
+// steps in this order combine all 16 lanes of a row with any commutative,
+// associative and idempotent operation (max, best-of).
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, dpp_f<DPP_XOR1>(m));
+  m = fmaxf(m, dpp_f<DPP_XOR2>(m));
+  m = fmaxf(m, dpp_f<DPP_HALF_MIRROR>(m));
+  return fmaxf(m, dpp_f<DPP_MIRROR>(m));
+}
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& bv, int& be) {
+  const float v2 = dpp_f<CTRL>(bv);
+  const int e2 = dpp_i<CTRL>(be);
+  if (ranks_before(v2, e2, bv, be)) {
+    bv = v2;
+    be = e2;
+  }
+}
+
 // Running top-K1 list of one lane (best first).
 template <int K1>
 struct TopList {
@@ -214,19 +245,18 @@ struct TopList {
       }
     }
   }
-  // Merge the lists of the GATE_TPR lanes of a row: every lane ends with the
-  // row's best K1 (value, expert) pairs in rank order.
+  // Merge the lists of the GATE_TPR (16) lanes of a row, one DPP row: every
+  // lane ends with the row's best K1 (value, expert) pairs in rank order.
+  // An expert sits in one lane's list only, so one lane pops per round.
   __device__ __forceinline__ void merge(float* ov, int* oe) {
 #pragma unroll
     for (int round = 0; round < K1; ++round) {
       float bv = v[0];
       int be = e[0];
-#pragma unroll
-      for (int off = 1; off < GATE_TPR; off <<= 1) {
-        float v2 = __shfl_xor(bv, off, GATE_TPR);
-        int e2 = __shfl_xor(be, off, GATE_TPR);
-        if (ranks_before(v2, e2, bv, be)) { bv = v2; be = e2; }
-      }
+      best_step<DPP_XOR1>(bv, be);
+      best_step<DPP_XOR2>(bv, be);
+      best_step<DPP_HALF_MIRROR>(bv, be);
+      best_step<DPP_MIRROR>(bv, be);
       ov[round] = bv;
       oe[round] = be;
       if (e[0] == be) {
@@ -345,8 +375,35 @@ __device__ void score_tile(const TileX<T>& tx, int d, const GateTabs& tb,
       Hs[acc_row(i, lane)][w * 32 + (lane & 31)] = h;
     }
     __syncthreads();
+    // lane `sub` of the row holds columns sub + 16q.  Only scores at or above
+    // tau, the K1-th largest of the row's 16 lane maxima, can be among the
+    // block's best K1 (K1 lanes hold a score >= tau); lanes whose maxima tie
+    // leave together, which only lowers tau.
     const int nb = min(GATE_BLOCK_E, E - blk);
-    for (int j = sub; j < nb; j += GATE_TPR) L.insert(Hs[row][j], blk + j);
+    float hv[GATE_BLOCK_E / GATE_TPR];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < GATE_BLOCK_E / GATE_TPR; ++q) {
+      const int j = sub + GATE_TPR * q;
+      hv[q] = j < nb ? Hs[row][j] : -INFINITY;
+      mx = fmaxf(mx, hv[q]);
+    }
+    float tau = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < K1; ++r) {
+      tau = row16_max(mx);
+      mx = mx == tau ? -INFINITY : mx;
+    }
+    uint32_t cand = 0u;
+#pragma unroll
+    for (int q = 0; q < GATE_BLOCK_E / GATE_TPR; ++q)
+      if (sub + GATE_TPR * q < nb && hv[q] >= tau) cand |= 1u << q;
+    while (cand) {
+      const int q = __ffs(cand) - 1;
+      cand &= cand - 1u;
+      const int j = sub + GATE_TPR * q;
+      L.insert(Hs[row][j], blk + j);
+    }
     __syncthreads();
   }
   L.merge(ov, oe);
