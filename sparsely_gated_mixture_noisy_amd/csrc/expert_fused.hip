@@ -15,12 +15,13 @@
 //   * eight waves, two per SIMD, so that one wave's MFMAs cover the other's
 //     waits on memory, LDS and barriers;
 //   * the hidden layer is produced 256 units at a time: each wave computes
-//     S = relu(X W1[32 units]^T) for all 96 rows (v_mfma_f32_32x32x16_bf16,
+//     S = relu(X W1[32 units]^T) for the tile's rows (v_mfma_f32_32x32x16_bf16,
 //     W1 fragments streamed from global memory into a register ring), writes
 //     it as bf16 to LDS, then every wave accumulates Y[:, its 64 columns] +=
-//     S W2[cols, 256 units]^T with W2 fragments streamed the same way;
-//   * Y (96 x 512 fp32) stays in registers across the hidden chunks and is
-//     written once, as bf16, through LDS for coalesced 16-byte stores;
+//     S W2[cols, 256 units]^T with W2 fragments streamed the same way; only
+//     the 32-row blocks that hold rows of the tile go through the MFMAs;
+//   * Y (up to 96 x 512 fp32) stays in registers across the hidden chunks and
+//     is written once, as bf16, through LDS for coalesced 16-byte stores;
 //   * the expert tables can be repacked once (moe_pack_experts) into the
 //     exact order the waves consume their 16-byte fragments, so that every
 //     wave-wide load reads 1 KB of contiguous memory instead of 32-byte pieces
@@ -87,23 +88,168 @@ struct Stream {
   }
 };
 
-template <int D, int MT, bool PACKED>
-__global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs a) {
+// One tile of m <= 32*MB rows of expert e, rows p0 .. p0+m-1 of the routed
+// order (input row s_src[r]).  Both layers run transposed on the MFMA: the
+// weight fragment is operand A and the activation fragment operand B, so an
+// accumulator lane holds four consecutive hidden units (first layer) or
+// output columns (second layer) of one row, which go to LDS as one 8-byte
+// store of two packed bf16 pairs.
+template <int D, int MB, bool PACKED>
+__device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, int m,
+                                           bf16_t* Xs, bf16_t* Ss, const int* s_src) {
   using S = Stream<D>;
-  constexpr int M = 32 * MT;     // rows per tile
   constexpr int XLD = D + 8;     // LDS row stride of the input tile (elements)
   constexpr int SLD = FZ_H + 8;  // LDS row stride of the hidden tile
   constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int XPT = M * CPR / FZ_THREADS;  // input chunks per thread
+  constexpr int XCH = 32 * MB * CPR;                             // input chunks of the tile
+  constexpr int XPT = (XCH + FZ_THREADS - 1) / FZ_THREADS;       // per thread
   constexpr int N1 = S::N1, NE = S::NE, NT2 = S::NT2, RING = FZ_RING;
   static_assert(NE % RING == 0 && N1 % RING == 0, "stream must be a multiple of the ring");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int fr = lane & 31, fk = (lane >> 5) * 8, q4 = (lane >> 5) * 4;
+  const int nchunks = a.h / FZ_H;
+  const bf16_t* W1e = a.w1 + (int64_t)e * a.h * D;
+  const bf16_t* W2e = a.w2 + (int64_t)e * D * a.h;
+  auto frag = [&](int hc, int n) -> u32x4 {
+    if constexpr (PACKED) {
+      return *reinterpret_cast<const u32x4*>(a.wp + S::packed(a.h, e, hc, w, n, lane));
+    } else {
+      int t;
+      const int64_t o = S::src(a.h, hc, w, n, lane, &t);
+      return *reinterpret_cast<const u32x4*>((t == 0 ? W1e : W2e) + o);
+    }
+  };
+
+  // gathered input rows (rows past m are zero) and the first RING weight
+  // fragments are requested together
+  u32x4 xv[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
+    xv[i] = (c < XCH && r < m) ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)s_src[r] * D + cc)
+                               : u32x4{0u, 0u, 0u, 0u};
+  }
+  // A ring of RING registers keeps RING weight loads in flight without
+  // draining between the two layers or between chunks: consuming entry n
+  // issues entry n + RING (of this chunk or the next one).
+  u32x4 ring[RING];
+#pragma unroll
+  for (int i = 0; i < RING; ++i) ring[i] = frag(0, i);
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
+    if (c < XCH) *reinterpret_cast<u32x4*>(Xs + r * XLD + cc) = xv[i];
+  }
+
+  f32x16 acc[MB][NT2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NT2; ++j) acc[i][j] = f32x16{};
+
+  __syncthreads();
+  for (int hc = 0; hc < nchunks; ++hc) {
+    const bool more = hc + 1 < nchunks;
+    // consume entry n of this chunk's stream and refill its ring slot
+    auto take = [&](int n) -> bf16x8 {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, ring[n % RING]);
+      const int nn = n + RING;
+      if (nn < NE) ring[n % RING] = frag(hc, nn);
+      else if (more) ring[n % RING] = frag(hc + 1, nn - NE);
+      return v;
+    };
+    // ---- first layer: S^T[32w .. +32 units][rows] = W1[units] X^T ----
+    f32x16 sa[MB];
+    bf16x8 xa[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      sa[i] = f32x16{};
+      xa[i] = *reinterpret_cast<const bf16x8*>(Xs + (32 * i + fr) * XLD + fk);
+    }
+#pragma unroll
+    for (int ks = 0; ks < S::KS1; ++ks) {
+      const bf16x8 b = take(ks);
+      bf16x8 av[MB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) av[i] = xa[i];
+      if (ks + 1 < S::KS1) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          xa[i] = *reinterpret_cast<const bf16x8*>(Xs + (32 * i + fr) * XLD + (ks + 1) * 16 + fk);
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i) sa[i] = mfma32(b, av[i], sa[i]);
+    }
+    // relu -> bf16 -> S[row][unit]: register group g holds units
+    // 8g + q4 .. +3 of row 32i + fr
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = cvt_pk_bf16(fmaxf(sa[i][4 * g], 0.f), fmaxf(sa[i][4 * g + 1], 0.f));
+        const uint32_t hi = cvt_pk_bf16(fmaxf(sa[i][4 * g + 2], 0.f), fmaxf(sa[i][4 * g + 3], 0.f));
+        *reinterpret_cast<uint2*>(Ss + (32 * i + fr) * SLD + w * S::U1 + 8 * g + q4) =
+            uint2{lo, hi};
+      }
+    __syncthreads();
+    // ---- second layer: Y^T[w*C2 .. +C2 cols][rows] += W2[cols, units] S^T ----
+    bf16x8 sv[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) sv[i] = *reinterpret_cast<const bf16x8*>(Ss + (32 * i + fr) * SLD + fk);
+#pragma unroll
+    for (int ks = 0; ks < S::KS2; ++ks) {
+      bf16x8 b[NT2];
+#pragma unroll
+      for (int j = 0; j < NT2; ++j) b[j] = take(N1 + ks * NT2 + j);
+      bf16x8 av[MB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) av[i] = sv[i];
+      if (ks + 1 < S::KS2) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          sv[i] = *reinterpret_cast<const bf16x8*>(Ss + (32 * i + fr) * SLD + (ks + 1) * 16 + fk);
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NT2; ++j) acc[i][j] = mfma32(b[j], av[i], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  // Y -> bf16 -> LDS (reusing the input tile) -> coalesced stores; register
+  // group g of acc[i][j] holds columns w*C2 + 32j + 8g + q4 .. +3 of row 32i + fr
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NT2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = cvt_pk_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+        const uint32_t hi = cvt_pk_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        *reinterpret_cast<uint2*>(Xs + (32 * i + fr) * XLD + w * S::C2 + 32 * j + 8 * g + q4) =
+            uint2{lo, hi};
+      }
+  __syncthreads();
+  for (int c = tid; c < m * CPR; c += FZ_THREADS) {
+    const int r = c / CPR, cc = (c % CPR) * 8;
+    *reinterpret_cast<u32x4*>(a.y + (int64_t)(p0 + r) * D + cc) =
+        *reinterpret_cast<const u32x4*>(Xs + r * XLD + cc);
+  }
+}
+
+template <int D, int MT, bool PACKED>
+__global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs a) {
+  constexpr int M = 32 * MT;     // rows per tile at most
+  constexpr int XLD = D + 8;
+  static_assert(MT == 3, "the tile body is instantiated for 1 .. 3 row blocks");
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
   bf16_t* Xs = lds;
   bf16_t* Ss = lds + M * XLD;
   __shared__ int s_info[3];
   __shared__ int s_src[M];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x;
   if (tid == 0) {
     const int Q = a.tiles[a.E];
     const int per = (Q + 7) / 8;
@@ -128,131 +274,14 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
     s_src[tid] = a.perm ? a.perm[p] / a.k : p;
   }
   __syncthreads();
-
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-  const int nchunks = a.h / FZ_H;
-  const bf16_t* W1e = a.w1 + (int64_t)e * a.h * D;
-  const bf16_t* W2e = a.w2 + (int64_t)e * D * a.h;
-  auto frag = [&](int hc, int n) -> u32x4 {
-    if constexpr (PACKED) {
-      return *reinterpret_cast<const u32x4*>(a.wp + S::packed(a.h, e, hc, w, n, lane));
-    } else {
-      int t;
-      const int64_t o = S::src(a.h, hc, w, n, lane, &t);
-      return *reinterpret_cast<const u32x4*>((t == 0 ? W1e : W2e) + o);
-    }
-  };
-
-  // gathered input rows (rows past m are zero) and the first RING weight
-  // fragments are requested together
-  u32x4 xv[XPT];
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
-    xv[i] = r < m ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)s_src[r] * D + cc)
-                  : u32x4{0u, 0u, 0u, 0u};
-  }
-  // A ring of RING registers keeps RING weight loads in flight without
-  // draining between the two layers or between chunks: consuming entry n
-  // issues entry n + RING (of this chunk or the next one).
-  u32x4 ring[RING];
-#pragma unroll
-  for (int i = 0; i < RING; ++i) ring[i] = frag(0, i);
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
-    *reinterpret_cast<u32x4*>(Xs + r * XLD + cc) = xv[i];
-  }
-
-  f32x16 acc[MT][NT2];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT2; ++j) acc[i][j] = f32x16{};
-
-  __syncthreads();
-  for (int hc = 0; hc < nchunks; ++hc) {
-    const bool more = hc + 1 < nchunks;
-    // consume entry n of this chunk's stream and refill its ring slot
-    auto take = [&](int n) -> bf16x8 {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, ring[n % RING]);
-      const int nn = n + RING;
-      if (nn < NE) ring[n % RING] = frag(hc, nn);
-      else if (more) ring[n % RING] = frag(hc + 1, nn - NE);
-      return v;
-    };
-    // ---- first layer: S[:, 32w .. +32) = relu(X W1[units]^T) ----
-    f32x16 sa[MT];
-    bf16x8 xa[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      sa[i] = f32x16{};
-      xa[i] = *reinterpret_cast<const bf16x8*>(Xs + (32 * i + fr) * XLD + fk);
-    }
-#pragma unroll
-    for (int ks = 0; ks < S::KS1; ++ks) {
-      const bf16x8 b = take(ks);
-      bf16x8 av[MT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) av[i] = xa[i];
-      if (ks + 1 < S::KS1) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-          xa[i] = *reinterpret_cast<const bf16x8*>(Xs + (32 * i + fr) * XLD + (ks + 1) * 16 + fk);
-      }
-#pragma unroll
-      for (int i = 0; i < MT; ++i) sa[i] = mfma32(av[i], b, sa[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        Ss[row * SLD + w * S::U1 + fr] = f32_to_bf16(fmaxf(sa[i][r], 0.f));
-      }
-    __syncthreads();
-    // ---- second layer: Y[:, w*C2 .. +C2) += S W2[cols, units]^T ----
-    bf16x8 sv[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) sv[i] = *reinterpret_cast<const bf16x8*>(Ss + (32 * i + fr) * SLD + fk);
-#pragma unroll
-    for (int ks = 0; ks < S::KS2; ++ks) {
-      bf16x8 b[NT2];
-#pragma unroll
-      for (int j = 0; j < NT2; ++j) b[j] = take(N1 + ks * NT2 + j);
-      bf16x8 av[MT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) av[i] = sv[i];
-      if (ks + 1 < S::KS2) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-          sv[i] = *reinterpret_cast<const bf16x8*>(Ss + (32 * i + fr) * SLD + (ks + 1) * 16 + fk);
-      }
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT2; ++j) acc[i][j] = mfma32(av[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-
-  // Y -> bf16 -> LDS (reusing the input tile) -> coalesced stores
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = w * S::C2 + j * 32 + fr;
-        Xs[row * XLD + col] = f32_to_bf16(acc[i][j][r]);
-      }
-  __syncthreads();
-  for (int c = tid; c < m * CPR; c += FZ_THREADS) {
-    const int r = c / CPR, cc = (c % CPR) * 8;
-    *reinterpret_cast<u32x4*>(a.y + (int64_t)(p0 + r) * D + cc) =
-        *reinterpret_cast<const u32x4*>(Xs + r * XLD + cc);
-  }
+  // only the 32-row blocks that hold rows run through the MFMAs
+  const int mb = (m + 31) / 32;
+  if (mb >= 3)
+    fused_tile<D, 3, PACKED>(a, e, p0, m, Xs, Ss, s_src);
+  else if (mb == 2)
+    fused_tile<D, 2, PACKED>(a, e, p0, m, Xs, Ss, s_src);
+  else
+    fused_tile<D, 1, PACKED>(a, e, p0, m, Xs, Ss, s_src);
 }
 
 bool fused_ffn_supported(int d, int h, int swiglu) {
