@@ -38,8 +38,8 @@ EXPERT_TRAFFIC = {
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "75ff4538defeaba9a44a30bfcec84f7a7679b069f12faec26e8113c0cae9ee4e",
-    "fetch_kib": 288660.0, "fetch_scale": 524288.0 / 262156.0,
+    "sources_sha256": "10503f5f3acdb976dbfffefaef17220d31d09a47b5c146d2e2bc79c479aa675c",
+    "fetch_kib": 289087.1, "fetch_scale": 524288.0 / 262156.0,
     "write_kib": 32768.0, "write_scale": 524288.0 / 524288.0,
 }
 
