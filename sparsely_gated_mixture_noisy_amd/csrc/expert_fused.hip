@@ -231,10 +231,11 @@ __device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, in
             uint2{lo, hi};
       }
   __syncthreads();
+  // streaming stores: the rows are read once, by the combine
   for (int c = tid; c < m * CPR; c += FZ_THREADS) {
     const int r = c / CPR, cc = (c % CPR) * 8;
-    *reinterpret_cast<u32x4*>(a.y + (int64_t)(p0 + r) * D + cc) =
-        *reinterpret_cast<const u32x4*>(Xs + r * XLD + cc);
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Xs + r * XLD + cc),
+                                reinterpret_cast<u32x4*>(a.y + (int64_t)(p0 + r) * D + cc));
   }
 }
 
