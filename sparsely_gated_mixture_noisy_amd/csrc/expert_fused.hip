@@ -88,6 +88,22 @@ struct Stream {
   }
 };
 
+// Weight fragment n of hidden chunk hc of expert e for the calling lane of
+// its wave (see Stream).
+template <int D, bool PACKED>
+__device__ __forceinline__ u32x4 fused_frag(const FusedArgs& a, int e, int hc, int n) {
+  using S = Stream<D>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if constexpr (PACKED) {
+    return *reinterpret_cast<const u32x4*>(a.wp + S::packed(a.h, e, hc, w, n, lane));
+  } else {
+    int t;
+    const int64_t o = S::src(a.h, hc, w, n, lane, &t);
+    const bf16_t* base = t == 0 ? a.w1 + (int64_t)e * a.h * D : a.w2 + (int64_t)e * D * a.h;
+    return *reinterpret_cast<const u32x4*>(base + o);
+  }
+}
+
 // One tile of m <= 32*MB rows of expert e, rows p0 .. p0+m-1 of the routed
 // order (input row s_src[r]).  Both layers run transposed on the MFMA: the
 // weight fragment is operand A and the activation fragment operand B, so an
@@ -96,7 +112,8 @@ struct Stream {
 // store of two packed bf16 pairs.
 template <int D, int MB, bool PACKED>
 __device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, int m,
-                                           bf16_t* Xs, bf16_t* Ss, const int* s_src) {
+                                           bf16_t* Xs, bf16_t* Ss, const int* s_src,
+                                           u32x4 (&ring)[FZ_RING]) {
   using S = Stream<D>;
   constexpr int XLD = D + 8;     // LDS row stride of the input tile (elements)
   constexpr int SLD = FZ_H + 8;  // LDS row stride of the hidden tile
@@ -108,20 +125,10 @@ __device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, in
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 31, fk = (lane >> 5) * 8, q4 = (lane >> 5) * 4;
   const int nchunks = a.h / FZ_H;
-  const bf16_t* W1e = a.w1 + (int64_t)e * a.h * D;
-  const bf16_t* W2e = a.w2 + (int64_t)e * D * a.h;
-  auto frag = [&](int hc, int n) -> u32x4 {
-    if constexpr (PACKED) {
-      return *reinterpret_cast<const u32x4*>(a.wp + S::packed(a.h, e, hc, w, n, lane));
-    } else {
-      int t;
-      const int64_t o = S::src(a.h, hc, w, n, lane, &t);
-      return *reinterpret_cast<const u32x4*>((t == 0 ? W1e : W2e) + o);
-    }
-  };
+  auto frag = [&](int hc, int n) -> u32x4 { return fused_frag<D, PACKED>(a, e, hc, n); };
 
-  // gathered input rows (rows past m are zero) and the first RING weight
-  // fragments are requested together
+  // gathered input rows (rows past m are zero); the ring already holds the
+  // requests for the first RING weight fragments
   u32x4 xv[XPT];
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
@@ -129,12 +136,6 @@ __device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, in
     xv[i] = (c < XCH && r < m) ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)s_src[r] * D + cc)
                                : u32x4{0u, 0u, 0u, 0u};
   }
-  // A ring of RING registers keeps RING weight loads in flight without
-  // draining between the two layers or between chunks: consuming entry n
-  // issues entry n + RING (of this chunk or the next one).
-  u32x4 ring[RING];
-#pragma unroll
-  for (int i = 0; i < RING; ++i) ring[i] = frag(0, i);
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int c = tid + i * FZ_THREADS, r = c / CPR, cc = (c % CPR) * 8;
@@ -267,9 +268,17 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
     s_info[2] = m;
   }
   __syncthreads();
-  const int e = s_info[0];
+  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
   if (e < 0) return;
-  const int p0 = s_info[1], m = s_info[2];
+  const int p0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+  const int m = __builtin_amdgcn_readfirstlane(s_info[2]);
+  // A ring of FZ_RING registers keeps that many weight loads in flight
+  // without draining between the two layers or between chunks: consuming
+  // entry n issues entry n + FZ_RING (of this chunk or the next one).  Its
+  // first requests go out before the input rows' gather.
+  u32x4 ring[FZ_RING];
+#pragma unroll
+  for (int i = 0; i < FZ_RING; ++i) ring[i] = fused_frag<D, PACKED>(a, e, 0, i);
   if (tid < M) {
     const int p = p0 + min(tid, m - 1);
     s_src[tid] = a.perm ? a.perm[p] / a.k : p;
@@ -278,11 +287,11 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
   // only the 32-row blocks that hold rows run through the MFMAs
   const int mb = (m + 31) / 32;
   if (mb >= 3)
-    fused_tile<D, 3, PACKED>(a, e, p0, m, Xs, Ss, s_src);
+    fused_tile<D, 3, PACKED>(a, e, p0, m, Xs, Ss, s_src, ring);
   else if (mb == 2)
-    fused_tile<D, 2, PACKED>(a, e, p0, m, Xs, Ss, s_src);
+    fused_tile<D, 2, PACKED>(a, e, p0, m, Xs, Ss, s_src, ring);
   else
-    fused_tile<D, 1, PACKED>(a, e, p0, m, Xs, Ss, s_src);
+    fused_tile<D, 1, PACKED>(a, e, p0, m, Xs, Ss, s_src, ring);
 }
 
 bool fused_ffn_supported(int d, int h, int swiglu) {
