@@ -80,8 +80,8 @@ hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float*
 // Balance statistics in one launch.  Workgroup (16 waves) b covers the 16
 // experts [16b, 16b+16).  Both sums run over 64 contiguous ranges of 32-token
 // blocks: each range is summed in ascending block order, then the 64 range
-// sums in range order (the same order in which the routing step reduces the
-// flat gate's per-block partials, so both give the same bits):
+// sums by a fixed butterfly (the same order in which the routing step reduces
+// the flat gate's per-block partials, so both give the same bits):
 //   importance[e]: wave w takes expert 16b + w, lane l range l, the block
 //                  sums adding the block's gates in token order;
 //   load[e]:       lane l of wave w takes expert 16b + l%16 and range
@@ -94,67 +94,58 @@ constexpr int BAL_THREADS = 1024;
 constexpr int BAL_EXPERTS = 16;
 
 __global__ __launch_bounds__(BAL_THREADS) void balance_kernel(BalanceArgs a) {
-  __shared__ float red[64][BAL_EXPERTS];
-  __shared__ float ired[BAL_EXPERTS][64];
+  __shared__ float red[BAL_EXPERTS][65];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e0 = blockIdx.x * BAL_EXPERTS;
   const int per = (a.blocks + 63) / 64;
   {
-    // importance of expert e0 + w; lane l sums the 32-token blocks
-    // [l*per, (l+1)*per): e's positions are in ascending token order, so the
-    // lane binary-searches its first one and walks on, adding each block's
-    // gates in row order into a block sum and the block sums in order
-    const int e = e0 + w;
-    float rs = 0.f;
-    if (e < a.E) {
-      const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
-      const int64_t tb0 = (int64_t)lane * per * 32, tb1 = tb0 + (int64_t)per * 32;
-      int lo = p0, hi = p1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a.perm[mid] / a.k < tb0) lo = mid + 1; else hi = mid;
-      }
-      float bs = 0.f;
-      int64_t cur = -1;
-      for (int q = lo; q < p1; ++q) {
-        const int as = a.perm[q];
-        const int64_t t = as / a.k;
-        if (t >= tb1) break;
-        if (t / 32 != cur) {
-          if (cur >= 0) rs += bs;
-          bs = 0.f;
-          cur = t / 32;
-        }
-        bs += a.gate[as];
-      }
-      if (cur >= 0) rs += bs;
-    }
-    ired[w][lane] = rs;
-  }
-  {
+    // load partials: lane l of wave w sums range 4w + l/16 of expert 16b + l%16
     const int le = lane % BAL_EXPERTS, range = 4 * w + lane / BAL_EXPERTS;
     const int e = e0 + le;
-    if (a.part) {
+    float s = 0.f;
+    if (a.part && e < a.E) {
       const int b0 = range * per, b1 = min(a.blocks, b0 + per);
-      float s = 0.f;
-      if (e < a.E)
-        for (int b = b0; b < b1; ++b) s += a.part[(int64_t)b * a.E + e];
-      red[range][le] = s;
+      for (int b = b0; b < b1; ++b) s += a.part[(int64_t)b * a.E + e];
     }
+    red[le][range] = s;
+  }
+  // importance of expert e0 + w; lane l sums the 32-token blocks
+  // [l*per, (l+1)*per): e's positions are in ascending token order, so the
+  // lane binary-searches its first one and walks on, adding each block's
+  // gates in row order into a block sum and the block sums in order
+  const int e = e0 + w;
+  float rs = 0.f;
+  if (e < a.E) {
+    const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
+    const int64_t tb0 = (int64_t)lane * per * 32, tb1 = tb0 + (int64_t)per * 32;
+    int lo = p0, hi = p1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.perm[mid] / a.k < tb0) lo = mid + 1; else hi = mid;
+    }
+    float bs = 0.f;
+    int64_t cur = -1;
+    for (int q = lo; q < p1; ++q) {
+      const int as = a.perm[q];
+      const int64_t t = as / a.k;
+      if (t >= tb1) break;
+      if (t / 32 != cur) {
+        if (cur >= 0) rs += bs;
+        bs = 0.f;
+        cur = t / 32;
+      }
+      bs += a.gate[as];
+    }
+    if (cur >= 0) rs += bs;
   }
   __syncthreads();
-  if (threadIdx.x < BAL_EXPERTS && e0 + threadIdx.x < a.E) {
-    const int ee = e0 + threadIdx.x;
-    float ti = 0.f;
-    for (int i = 0; i < 64; ++i) ti += ired[threadIdx.x][i];
-    a.importance[ee] = ti;
-    if (a.part) {
-      float t = 0.f;
-      for (int i = 0; i < 64; ++i) t += red[i][threadIdx.x];
-      a.load[ee] = t;
-    } else {
-      a.load[ee] = (float)(a.offsets[ee + 1] - a.offsets[ee]);
-    }
+  // the 64 range sums of expert e0 + w by the same butterfly as the routing
+  // step's reduction
+  const float ti = wave_sum(rs);
+  const float tl = wave_sum(red[w][lane]);
+  if (lane == 0 && e < a.E) {
+    a.importance[e] = ti;
+    a.load[e] = a.part ? tl : (float)(a.offsets[e + 1] - a.offsets[e]);
   }
 }
 

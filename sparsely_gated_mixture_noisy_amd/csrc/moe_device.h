@@ -119,35 +119,84 @@ __device__ __forceinline__ bool ranks_before(float v1, int e1, float v2, int e2)
   return v1 > v2 || (v1 == v2 && e1 < e2);
 }
 
-// Sum of one double per thread over a workgroup of NT threads (NT a power of
-// two), by a fixed tree in LDS: the result does not depend on scheduling.
-template <int NT>
-__device__ double block_sum_f64(double v) {
-  __shared__ double red[NT];
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = NT / 2; off > 0; off >>= 1) {
-    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-    __syncthreads();
+// Sum over the 64 lanes of a wave by a fixed xor butterfly (offsets 32 .. 1):
+// every lane ends with the same bits, and the order does not depend on
+// scheduling.
+template <typename F>
+__device__ __forceinline__ F wave_sum(F v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (integers).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
   }
-  const double r = red[0];
+  return v;
+}
+
+// Exclusive prefix sum of one int per thread over a workgroup of NT threads
+// (NT a multiple of 64); *total gets the sum.  One barrier pair.
+template <int NT>
+__device__ int block_excl_scan(int v, int* total) {
+  __shared__ int wsum[NT / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int x = wsum[i];
+    if (i < w) base += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// Sum of 256 slot values held by threads 0..255 of a workgroup of NT >= 256
+// threads: a butterfly inside each of the first four waves, then
+// (w0 + w1) + (w2 + w3).  The order is a function of the slots only, so any
+// NT gives the same bits.
+template <int NT>
+__device__ double sum256_f64(double v) {
+  static_assert(NT >= 256 && NT % 64 == 0, "needs the first four waves");
+  __shared__ double ws[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (w < 4) {
+    const double x = wave_sum(v);
+    if (lane == 0) ws[w] = x;
+  }
+  __syncthreads();
+  const double r = (ws[0] + ws[1]) + (ws[2] + ws[3]);
   __syncthreads();
   return r;
 }
 
 // Squared coefficient of variation of v[0..E): population variance / mean^2
-// in fp64 (0 when the mean is 0).  Called by all NT threads of a workgroup.
+// in fp64 (0 when the mean is 0).  Slot i < 256 sums v[i], v[i+256], ... in
+// order; the slots are added by sum256_f64.  Called by all NT threads.
 template <int NT>
 __device__ double cv2_of(const float* v, int E) {
+  const int tid = threadIdx.x;
   double s = 0.0;
-  for (int i = threadIdx.x; i < E; i += NT) s += (double)v[i];
-  const double mean = block_sum_f64<NT>(s) / E;
+  if (tid < 256)
+    for (int i = tid; i < E; i += 256) s += (double)v[i];
+  const double mean = sum256_f64<NT>(s) / E;
   double q = 0.0;
-  for (int i = threadIdx.x; i < E; i += NT) {
-    const double dv = (double)v[i] - mean;
-    q += dv * dv;
-  }
-  const double var = block_sum_f64<NT>(q) / E;
+  if (tid < 256)
+    for (int i = tid; i < E; i += 256) {
+      const double dv = (double)v[i] - mean;
+      q += dv * dv;
+    }
+  const double var = sum256_f64<NT>(q) / E;
   return mean == 0.0 ? 0.0 : var / (mean * mean);
 }
 

@@ -119,82 +119,70 @@ __global__ __launch_bounds__(256) void route_hist_kernel(RouteArgs a) {
 
 // Workgroup (16 waves) b covers the 16 experts [16b, 16b+16); lane l of wave
 // w takes expert 16b + l%16 and the (4w + l/16)-th of 64 contiguous ranges of
-// token blocks.
+// token blocks.  Then wave w scans (counts) and sums (importance, load) the
+// 64 range values of expert 16b + w, lane l holding range l.
 constexpr int SCAN_EXPERTS = 16;
+static_assert(SCAN_THREADS / 64 == SCAN_EXPERTS, "one wave per expert in the range pass");
 
 __global__ __launch_bounds__(SCAN_THREADS) void route_colscan_kernel(RouteArgs a) {
-  __shared__ int part[64][SCAN_EXPERTS];
+  __shared__ int pc[SCAN_EXPERTS][65];
+  __shared__ float pimp[SCAN_EXPERTS][65], pload[SCAN_EXPERTS][65];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int le = lane % SCAN_EXPERTS, range = 4 * w + lane / SCAN_EXPERTS;
   const int e = blockIdx.x * SCAN_EXPERTS + le;
   const int per = (a.NB + 63) / 64;
   const int b0 = range * per, b1 = min(a.NB, b0 + per);
+  const bool stats = a.importance != nullptr;
   int s = 0;
-  if (e < a.E)
-    for (int b = b0; b < b1; ++b) s += __popc(a.bits[(int64_t)b * a.E + e]);
-  part[range][le] = s;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < 64; ++i) {
-    if (i < range) base += part[i][le];
-    tot += part[i][le];
-  }
+  float si = 0.f, sl = 0.f;
   if (e < a.E) {
-    int run = base;
+    for (int b = b0; b < b1; ++b) {
+      const int64_t o = (int64_t)b * a.E + e;
+      s += __popc(a.bits[o]);
+      if (stats) {
+        si += a.imp_part[o];
+        if (a.load_part) sl += a.load_part[o];
+      }
+    }
+  }
+  pc[le][range] = s;
+  pimp[le][range] = si;
+  pload[le][range] = sl;
+  __syncthreads();
+  {
+    // importance and load: each range summed in ascending block order above,
+    // the 64 range sums by a fixed butterfly here
+    const int ew = blockIdx.x * SCAN_EXPERTS + w;
+    const int v = pc[w][lane];
+    const int incl = wave_incl_scan(v);
+    const int tot = __shfl(incl, 63, 64);
+    const float ti = wave_sum(pimp[w][lane]);
+    const float tl = wave_sum(pload[w][lane]);
+    pc[w][lane] = incl - v;  // exclusive base of range `lane` (only wave w touches row w)
+    if (lane == 0 && ew < a.E) {
+      a.counts[ew] = tot;
+      if (stats) {
+        a.importance[ew] = ti;
+        a.load[ew] = a.load_part ? tl : (float)tot;
+      }
+    }
+  }
+  __syncthreads();
+  if (e < a.E) {
+    int run = pc[le][range];
     for (int b = b0; b < b1; ++b) {
       const int64_t o = (int64_t)b * a.E + e;
       a.base[o] = run;
       run += __popc(a.bits[o]);
-    }
-    if (range == 0) a.counts[e] = tot;
-  }
-  if (a.importance) {
-    // importance and load of the same 16 experts: each range summed in
-    // ascending block order, then the 64 range sums in range order
-    __shared__ float pimp[64][SCAN_EXPERTS], pload[64][SCAN_EXPERTS];
-    float si = 0.f, sl = 0.f;
-    if (e < a.E) {
-      for (int b = b0; b < b1; ++b) {
-        si += a.imp_part[(int64_t)b * a.E + e];
-        if (a.load_part) sl += a.load_part[(int64_t)b * a.E + e];
-      }
-    }
-    pimp[range][le] = si;
-    pload[range][le] = sl;
-    __syncthreads();
-    if (range == 0 && e < a.E) {
-      float ti = 0.f, tl = 0.f;
-      for (int i = 0; i < 64; ++i) {
-        ti += pimp[i][le];
-        tl += pload[i][le];
-      }
-      a.importance[e] = ti;
-      a.load[e] = a.load_part ? tl : (float)tot;
     }
   }
 }
 
 constexpr int SCATTER_THREADS = 256;
 
-// Exclusive scan over the 256 thread sums in tsum (Hillis-Steele in LDS);
-// returns the thread's exclusive base; tsum[SCATTER_THREADS - 1] ends as the
-// total.  Called by all SCATTER_THREADS threads.
-__device__ int scan_thread_sums(int* tsum) {
-  const int tid = threadIdx.x;
-  __syncthreads();
-  for (int d = 1; d < SCATTER_THREADS; d <<= 1) {
-    const int v = tid >= d ? tsum[tid - d] : 0;
-    __syncthreads();
-    tsum[tid] += v;
-    __syncthreads();
-  }
-  return tid > 0 ? tsum[tid - 1] : 0;
-}
-
 // Exclusive scan of counts[0..E) into off[0..E] (LDS) by one workgroup of
 // SCATTER_THREADS threads: thread i owns a contiguous run of experts.
 __device__ void scan_counts(const int32_t* counts, int E, int* off) {
-  __shared__ int tsum[SCATTER_THREADS];
   const int tid = threadIdx.x;
   const int per = (E + SCATTER_THREADS - 1) / SCATTER_THREADS;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
@@ -203,10 +191,10 @@ __device__ void scan_counts(const int32_t* counts, int E, int* off) {
     off[e] = s;
     s += counts[e];
   }
-  tsum[tid] = s;
-  const int base = scan_thread_sums(tsum);
+  int total;
+  const int base = block_excl_scan<SCATTER_THREADS>(s, &total);
   for (int e = e0; e < e1; ++e) off[e] += base;
-  if (tid == SCATTER_THREADS - 1) off[E] = tsum[tid];
+  if (tid == 0) off[E] = total;
   __syncthreads();
 }
 
@@ -216,14 +204,13 @@ __device__ void scan_counts(const int32_t* counts, int E, int* off) {
 // desc[q] = {expert, first position, rows}, an expert's rows split into
 // near-equal tiles.
 __device__ void scatter_tile_map(const int* off, int E, int rows, int32_t* tiles, int32_t* desc) {
-  __shared__ int tsum[SCATTER_THREADS];
   const int tid = threadIdx.x;
   const int per = (E + SCATTER_THREADS - 1) / SCATTER_THREADS;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int s = 0;
   for (int e = e0; e < e1; ++e) s += (off[e + 1] - off[e] + rows - 1) / rows;
-  tsum[tid] = s;
-  int run = scan_thread_sums(tsum);
+  int total;
+  int run = block_excl_scan<SCATTER_THREADS>(s, &total);
   for (int e = e0; e < e1; ++e) {
     const int m = off[e + 1] - off[e], nt = (m + rows - 1) / rows;
     tiles[e] = run;
@@ -238,7 +225,7 @@ __device__ void scatter_tile_map(const int* off, int E, int rows, int32_t* tiles
     }
     run += nt;
   }
-  if (tid == SCATTER_THREADS - 1) tiles[E] = tsum[tid];
+  if (tid == 0) tiles[E] = total;
 }
 
 __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArgs a) {
