@@ -67,6 +67,17 @@ SMALL = {
     "hier4096_t300": CONFIGS["hier4096"].replace(tokens=300),
     "hier_g16_e64": CONFIGS["hier4096"].replace(tokens=700, n_experts=1024),
     "swiglu_bf16_small": CONFIGS["mixtral"].replace(tokens=200, d_model=512, d_hidden=1536),
+    # fused expert kernel with 2 and 8 hidden chunks of 256 units
+    "fused_h512": CONFIGS["flat256"].replace(tokens=600, d_hidden=512),
+    "fused_h2048": CONFIGS["flat256"].replace(tokens=400, d_hidden=2048),
+    # gate input tile in LDS at its largest d_model, and read from global above it
+    "gate_d1024": CONFIGS["flat256"].replace(tokens=300, d_model=1024, n_experts=64),
+    "gate_d1088": CONFIGS["flat256"].replace(tokens=300, d_model=1088, n_experts=40, top_k=3),
+    # the largest expert count and top-k the library takes
+    "e8192_k8": CONFIGS["flat256"].replace(tokens=200, d_model=64, d_hidden=128, n_experts=8192,
+                                           top_k=8),
+    "flat_k8": CONFIGS["flat256"].replace(tokens=300, top_k=8),
+    "flat_noise_free": CONFIGS["flat256"].replace(tokens=300, noisy=False),
 }
 
 
