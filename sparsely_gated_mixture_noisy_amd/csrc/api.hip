@@ -297,7 +297,8 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
 // Expert-stage tile rows of this configuration (0: no tile map needed).
 int expert_tile_rows(const moe_config* c) {
   if (c->dtype != MOE_BF16) return 0;
-  return ffn_tile_rows(true, c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
+  return ffn_tile_rows(true, c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU,
+                       c->tokens * c->top_k, c->n_experts);
 }
 
 // have_bits: the flat gate already wrote the routing masks.  with_tiles: also
@@ -373,8 +374,9 @@ moe_status do_ffn(const moe_config* c, const Layout& L, const void* x, const int
   if (f.A == 0) return MOE_OK;
   if (bf16 && !tiles_ready)
     MOE_TRY(hip_status(launch_tile_map(offsets, c->n_experts,
-                                       ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw), tiles,
-                                       desc, s),
+                                       ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw, f.A,
+                                                     c->n_experts),
+                                       tiles, desc, s),
                        "expert tiles"));
   return hip_status(launch_expert_ffn(f, bf16, sw, s), "experts");
 }

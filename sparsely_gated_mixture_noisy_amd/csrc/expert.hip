@@ -174,6 +174,184 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Large layers (on average >= GB_BM rows per expert): 256 x 128 output tiles,
+// K staged through LDS 64 at a time, four waves (one per SIMD) of 128 x 64
+// each.  Per 16-deep k-step a wave reads four activation and two (SwiGLU:
+// four) weight fragments for eight (sixteen) MFMAs, half the LDS traffic per
+// MFMA of the 128 x 128 kernel.  The MFMAs run transposed (weights in
+// operand A), so an accumulator lane holds four consecutive output columns of
+// one row and the epilogue stores them as 8 bytes.  Tiles are ordered in
+// windows of GB_WIN row tiles: consecutive workgroups (one per XCD, round
+// robin) take the window's row tiles against one column tile, then the next
+// column tile, so each XCD keeps one activation tile in its L2 while the
+// weight column tiles stream past.
+// ---------------------------------------------------------------------------
+constexpr int GB_BM = 256, GB_BN = 128, GB_BK = 64, GB_LD = GB_BK + 8, GB_WIN = 8;
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
+  constexpr bool SW = (EPI == EPI_SWIGLU);
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  bf16_t* As = smem;                          // [2][GB_BM][GB_LD]
+  bf16_t* Bs = As + 2 * GB_BM * GB_LD;        // [2][GB_BN][GB_LD]
+  bf16_t* B3s = Bs + 2 * GB_BN * GB_LD;       // [2][GB_BN][GB_LD], SwiGLU only
+  __shared__ int s_e, s_row0, s_m, s_ct;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) {
+    const int Q = g.tiles[g.E];
+    const int per_win = GB_WIN * g.ncol;
+    const int win = blockIdx.x / per_win, within = blockIdx.x % per_win;
+    const int q = win * GB_WIN + within % GB_WIN, ct = within / GB_WIN;
+    if (q < Q) {
+      const int e = expert_of_tile(g.tiles, g.E, q);
+      const int row0 = g.offsets[e] + (q - g.tiles[e]) * GB_BM;
+      s_e = e;
+      s_row0 = row0;
+      s_m = min(GB_BM, g.offsets[e + 1] - row0);
+      s_ct = ct;
+    } else {
+      s_e = -1;
+    }
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e < 0) return;
+  const int row0 = s_row0, m = s_m, n0 = s_ct * GB_BN;
+
+  // global -> LDS: thread t moves 16 bytes at k offset kc of rows t/8 + 32i
+  const int lr = tid >> 3, kc = (tid & 7) * 8;
+  const bf16_t* ap[8];
+  const bf16_t* bp[4];
+  const bf16_t* b3p[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = row0 + min(lr + 32 * i, m - 1);
+    const int64_t src = g.perm ? (int64_t)(g.perm[p] / g.k) : (int64_t)p;
+    ap[i] = g.A + src * g.lda + kc;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = min(n0 + lr + 32 * i, g.N - 1);
+    bp[i] = g.B + ((int64_t)e * g.N + n) * g.K + kc;
+    b3p[i] = SW ? g.B3 + ((int64_t)e * g.N + n) * g.K + kc : g.B;
+  }
+  u32x4 ra[8], rb[4], rb3[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0);
+      if constexpr (SW) rb3[i] = *reinterpret_cast<const u32x4*>(b3p[i] + k0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(As + (buf * GB_BM + lr + 32 * i) * GB_LD + kc) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(Bs + (buf * GB_BN + lr + 32 * i) * GB_LD + kc) = rb[i];
+      if constexpr (SW)
+        *reinterpret_cast<u32x4*>(B3s + (buf * GB_BN + lr + 32 * i) * GB_LD + kc) = rb3[i];
+    }
+  };
+
+  const int wm = w >> 1, wn = w & 1;  // wave tile: rows wm*128 .. +128, cols wn*64 .. +64
+  const bool active = wm * 128 < m;
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  f32x16 acc[4][2], acc3[SW ? 4 : 1][SW ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  if constexpr (SW) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc3[i][j] = f32x16{};
+  }
+
+  const int nk = g.K / GB_BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * GB_BK);
+    // every wave runs the MFMAs (rows past m hold copies of a valid row and are
+    // dropped at the store): a branch here would make the compiler keep a
+    // second copy of the accumulators
+    {
+      const bf16_t* Ab = As + (buf * GB_BM + wm * 128 + fr) * GB_LD + fk;
+      const bf16_t* Bb = Bs + (buf * GB_BN + wn * 64 + fr) * GB_LD + fk;
+      const bf16_t* B3b = B3s + (buf * GB_BN + wn * 64 + fr) * GB_LD + fk;
+      // operand fragments one 16-deep k-step ahead of the MFMAs, no further
+      bf16x8 af[2][4], bf[2][2], b3f[2][SW ? 2 : 1];
+      auto frags = [&](int ks, int sl) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[sl][i] = *reinterpret_cast<const bf16x8*>(Ab + i * 32 * GB_LD + ks);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bf[sl][j] = *reinterpret_cast<const bf16x8*>(Bb + j * 32 * GB_LD + ks);
+          if constexpr (SW) b3f[sl][j] = *reinterpret_cast<const bf16x8*>(B3b + j * 32 * GB_LD + ks);
+        }
+      };
+      frags(0, 0);
+#pragma unroll
+      for (int st = 0; st < GB_BK / 16; ++st) {
+        const int sl = st & 1;
+        if (st + 1 < GB_BK / 16) frags((st + 1) * 16, sl ^ 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[i][j] = mfma32(bf[sl][j], af[sl][i], acc[i][j]);
+            if constexpr (SW) acc3[i][j] = mfma32(b3f[sl][j], af[sl][i], acc3[i][j]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // register group q of acc[i][j] holds columns wn*64 + 32j + 8q + 4(lane/32) .. +3
+  // of row wm*128 + 32i + lane%32
+  const int q4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 128 + 32 * i + fr;
+    if (row >= m) continue;
+    bf16_t* crow = g.C + (int64_t)(row0 + row) * g.ldc;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * 64 + 32 * j + 8 * q + q4;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[i][j][4 * q + r];
+          if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+          if constexpr (EPI == EPI_SWIGLU) x = silu_f(x) * acc3[i][j][4 * q + r];
+          v[r] = x;
+        }
+        if (col + 3 < g.N) {
+          *reinterpret_cast<uint2*>(crow + col) = uint2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col + r < g.N) crow[col + r] = f32_to_bf16(v[r]);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: one thread per output element.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int p) {
@@ -219,9 +397,30 @@ __global__ __launch_bounds__(256) void ffn2_f32_kernel(FfnArgs a) {
   ((float*)a.y_sorted)[i] = s;
 }
 
-int ffn_tile_rows(bool bf16, int d, int h, int swiglu) {
+// The large-tile kernel pays off once the experts average a full tile of rows.
+static bool big_tiles(int64_t A, int E) { return A >= (int64_t)GB_BM * E; }
+
+int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E) {
   if (!bf16) return 1;
-  return fused_ffn_supported(d, h, swiglu) ? fused_ffn_tile_rows() : GM_BM;
+  if (fused_ffn_supported(d, h, swiglu)) return fused_ffn_tile_rows();
+  return big_tiles(A, E) ? GB_BM : GM_BM;
+}
+
+template <int EPI>
+static hipError_t launch_big(const GemmArgs& g, int64_t qmax, hipStream_t s) {
+  constexpr size_t lds =
+      sizeof(bf16_t) * (size_t)GB_LD * 2 * (GB_BM + GB_BN * (EPI == EPI_SWIGLU ? 2 : 1));
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    attr_done = true;
+  }
+  const int64_t wins = (qmax + GB_WIN - 1) / GB_WIN;
+  hipLaunchKernelGGL(grouped_gemm_big_kernel<EPI>, dim3((unsigned)(wins * GB_WIN * g.ncol)),
+                     dim3(256), lds, s, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_t s) {
@@ -234,8 +433,10 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
     return hipGetLastError();
   }
   if (fused_ffn_supported(a.d, a.h, swiglu)) return launch_fused_ffn(a, s);
+  const bool big = big_tiles(a.A, a.E);
+  const int bm = big ? GB_BM : GM_BM, bn = big ? GB_BN : GM_BN;
   // upper bound of tiles: each non-empty expert adds at most one partial tile
-  const int64_t qmax = (a.A + GM_BM - 1) / GM_BM + a.E;
+  const int64_t qmax = (a.A + bm - 1) / bm + a.E;
   GemmArgs g1;
   g1.A = (const bf16_t*)a.x;
   g1.lda = a.d;
@@ -250,13 +451,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
   g1.E = a.E;
   g1.C = (bf16_t*)a.hid;
   g1.ldc = a.h;
-  g1.ncol = (a.h + GM_BN - 1) / GM_BN;
-  if (swiglu)
-    hipLaunchKernelGGL(grouped_gemm_kernel<EPI_SWIGLU>, dim3((unsigned)(qmax * g1.ncol)), dim3(256),
-                       0, s, g1);
-  else
-    hipLaunchKernelGGL(grouped_gemm_kernel<EPI_RELU>, dim3((unsigned)(qmax * g1.ncol)), dim3(256), 0,
-                       s, g1);
+  g1.ncol = (a.h + bn - 1) / bn;
   GemmArgs g2 = g1;
   g2.A = (const bf16_t*)a.hid;
   g2.lda = a.h;
@@ -267,7 +462,18 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
   g2.K = a.h;
   g2.C = (bf16_t*)a.y_sorted;
   g2.ldc = a.d;
-  g2.ncol = (a.d + GM_BN - 1) / GM_BN;
+  g2.ncol = (a.d + bn - 1) / bn;
+  if (big) {
+    hipError_t err = swiglu ? launch_big<EPI_SWIGLU>(g1, qmax, s) : launch_big<EPI_RELU>(g1, qmax, s);
+    if (err != hipSuccess) return err;
+    return launch_big<EPI_NONE>(g2, qmax, s);
+  }
+  if (swiglu)
+    hipLaunchKernelGGL(grouped_gemm_kernel<EPI_SWIGLU>, dim3((unsigned)(qmax * g1.ncol)), dim3(256),
+                       0, s, g1);
+  else
+    hipLaunchKernelGGL(grouped_gemm_kernel<EPI_RELU>, dim3((unsigned)(qmax * g1.ncol)), dim3(256), 0,
+                       s, g1);
   hipLaunchKernelGGL(grouped_gemm_kernel<EPI_NONE>, dim3((unsigned)(qmax * g2.ncol)), dim3(256), 0,
                      s, g2);
   return hipGetLastError();

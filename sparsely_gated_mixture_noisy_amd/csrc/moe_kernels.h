@@ -121,7 +121,8 @@ struct FfnArgs {
   int64_t A;
   const void* wpacked;    // packed expert tables (fused path) or null
 };
-int ffn_tile_rows(bool bf16, int d, int h, int swiglu);
+// rows per tile of the expert stage for A routed rows over E experts
+int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E);
 // fused ReLU path (hidden layer kept on chip), d_model 512
 bool fused_ffn_supported(int d, int h, int swiglu);
 int fused_ffn_tile_rows();

@@ -78,6 +78,10 @@ SMALL = {
                                            top_k=8),
     "flat_k8": CONFIGS["flat256"].replace(tokens=300, top_k=8),
     "flat_noise_free": CONFIGS["flat256"].replace(tokens=300, noisy=False),
+    # the large-tile grouped GEMMs (>= 256 rows per expert on average), ragged tiles
+    "big_swiglu": CONFIGS["mixtral"].replace(tokens=1200, d_model=512, d_hidden=1536, n_experts=4),
+    "big_relu_d256": CONFIGS["flat256"].replace(tokens=1500, d_model=256, d_hidden=512,
+                                                n_experts=8, top_k=2),
 }
 
 
