@@ -178,23 +178,35 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 // K staged through LDS 64 at a time, four waves (one per SIMD) of 128 x 64
 // each.  Per 16-deep k-step a wave reads four activation and two (SwiGLU:
 // four) weight fragments for eight (sixteen) MFMAs, half the LDS traffic per
-// MFMA of the 128 x 128 kernel.  The MFMAs run transposed (weights in
-// operand A), so an accumulator lane holds four consecutive output columns of
-// one row and the epilogue stores them as 8 bytes.  Tiles are ordered in
-// windows of GB_WIN row tiles: consecutive workgroups (one per XCD, round
-// robin) take the window's row tiles against one column tile, then the next
-// column tile, so each XCD keeps one activation tile in its L2 while the
-// weight column tiles stream past.
+// MFMA of the 128 x 128 kernel.
+//   * Operand tiles go from global memory straight into LDS
+//     (global_load_lds_dwordx4: each wave-wide load fills 1 KB of LDS in lane
+//     order), with no staging registers and no LDS store pass.  A tile row is
+//     64 elements = 8 chunks of 16 bytes; chunk c of row R sits at slot
+//     R*8 + (c ^ ((R >> 1) & 7)), so the 16 rows a fragment read touches land
+//     in 16 different bank groups; each lane loads the chunk that belongs in
+//     its slot.
+//   * The MFMAs run transposed (weights in operand A), so an accumulator lane
+//     holds four consecutive output columns of one row and the epilogue
+//     stores them as 8 bytes.
+//   * Tiles go in windows of GB_WIN row tiles: consecutive workgroups (one
+//     per XCD, round robin) take the window's row tiles against one column
+//     tile, then the next column tile, so each XCD keeps one activation tile
+//     in its L2 while the weight column tiles stream past.
 // ---------------------------------------------------------------------------
-constexpr int GB_BM = 256, GB_BN = 128, GB_BK = 64, GB_LD = GB_BK + 8, GB_WIN = 8;
+constexpr int GB_BM = 256, GB_BN = 128, GB_BK = 64, GB_WIN = 8;
+
+// element offset of chunk c (8 elements) of row r in a swizzled operand tile
+__device__ __forceinline__ int gb_slot(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   constexpr bool SW = (EPI == EPI_SWIGLU);
+  constexpr int AT = GB_BM * GB_BK, BT = GB_BN * GB_BK;  // tile elements
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-  bf16_t* As = smem;                          // [2][GB_BM][GB_LD]
-  bf16_t* Bs = As + 2 * GB_BM * GB_LD;        // [2][GB_BN][GB_LD]
-  bf16_t* B3s = Bs + 2 * GB_BN * GB_LD;       // [2][GB_BN][GB_LD], SwiGLU only
+  bf16_t* As = smem;               // [2][AT]
+  bf16_t* Bs = As + 2 * AT;        // [2][BT]
+  bf16_t* B3s = Bs + 2 * BT;       // [2][BT], SwiGLU only
   __shared__ int s_e, s_row0, s_m, s_ct;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -215,52 +227,49 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     }
   }
   __syncthreads();
-  const int e = s_e;
+  const int e = __builtin_amdgcn_readfirstlane(s_e);
   if (e < 0) return;
-  const int row0 = s_row0, m = s_m, n0 = s_ct * GB_BN;
+  const int row0 = __builtin_amdgcn_readfirstlane(s_row0);
+  const int m = __builtin_amdgcn_readfirstlane(s_m);
+  const int n0 = __builtin_amdgcn_readfirstlane(s_ct) * GB_BN;
 
-  // global -> LDS: thread t moves 16 bytes at k offset kc of rows t/8 + 32i
-  const int lr = tid >> 3, kc = (tid & 7) * 8;
+  // Direct loads: wave w fills 1 KB blocks w*8 + j (A, j < 8) and w*4 + j
+  // (B, B3, j < 4); lane l of block b fills slot 64b + l: row (64b + l) / 8,
+  // chunk position l % 8, i.e. source chunk (l % 8) ^ ((row >> 1) & 7).
   const bf16_t* ap[8];
   const bf16_t* bp[4];
   const bf16_t* b3p[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = row0 + min(lr + 32 * i, m - 1);
+  for (int j = 0; j < 8; ++j) {
+    const int r = (w * 8 + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int p = row0 + min(r, m - 1);
     const int64_t src = g.perm ? (int64_t)(g.perm[p] / g.k) : (int64_t)p;
-    ap[i] = g.A + src * g.lda + kc;
+    ap[j] = g.A + src * g.lda + c * 8;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = min(n0 + lr + 32 * i, g.N - 1);
-    bp[i] = g.B + ((int64_t)e * g.N + n) * g.K + kc;
-    b3p[i] = SW ? g.B3 + ((int64_t)e * g.N + n) * g.K + kc : g.B;
+  for (int j = 0; j < 4; ++j) {
+    const int r = (w * 4 + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int n = min(n0 + r, g.N - 1);
+    bp[j] = g.B + ((int64_t)e * g.N + n) * g.K + c * 8;
+    b3p[j] = SW ? g.B3 + ((int64_t)e * g.N + n) * g.K + c * 8 : g.B;
   }
-  u32x4 ra[8], rb[4], rb3[4];
-  auto gload = [&](int k0) {
+  auto dma = [&](int k0, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0);
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(ap[j] + k0, As + buf * AT + (w * 8 + j) * 512, 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0);
-      if constexpr (SW) rb3[i] = *reinterpret_cast<const u32x4*>(b3p[i] + k0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(As + (buf * GB_BM + lr + 32 * i) * GB_LD + kc) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(Bs + (buf * GB_BN + lr + 32 * i) * GB_LD + kc) = rb[i];
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds(bp[j] + k0, Bs + buf * BT + (w * 4 + j) * 512, 16, 0, 0);
       if constexpr (SW)
-        *reinterpret_cast<u32x4*>(B3s + (buf * GB_BN + lr + 32 * i) * GB_LD + kc) = rb3[i];
+        __builtin_amdgcn_global_load_lds(b3p[j] + k0, B3s + buf * BT + (w * 4 + j) * 512, 16, 0, 0);
     }
   };
 
   const int wm = w >> 1, wn = w & 1;  // wave tile: rows wm*128 .. +128, cols wn*64 .. +64
   const bool active = wm * 128 < m;
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  const int fr = lane & 31, fh = lane >> 5;
   f32x16 acc[4][2], acc3[SW ? 4 : 1][SW ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -274,36 +283,38 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   }
 
   const int nk = g.K / GB_BK;
-  gload(0);
-  lstore(0);
+  dma(0, 0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GB_BK);
+    // the next K slice streams into the other buffer while this one is used
+    if (kt + 1 < nk) dma((kt + 1) * GB_BK, buf ^ 1);
     // every wave runs the MFMAs (rows past m hold copies of a valid row and are
     // dropped at the store): a branch here would make the compiler keep a
     // second copy of the accumulators
     {
-      const bf16_t* Ab = As + (buf * GB_BM + wm * 128 + fr) * GB_LD + fk;
-      const bf16_t* Bb = Bs + (buf * GB_BN + wn * 64 + fr) * GB_LD + fk;
-      const bf16_t* B3b = B3s + (buf * GB_BN + wn * 64 + fr) * GB_LD + fk;
+      const bf16_t* Ab = As + buf * AT;
+      const bf16_t* Bb = Bs + buf * BT;
+      const bf16_t* B3b = B3s + buf * BT;
       // operand fragments one 16-deep k-step ahead of the MFMAs, no further
       bf16x8 af[2][4], bf[2][2], b3f[2][SW ? 2 : 1];
-      auto frags = [&](int ks, int sl) {
+      auto frags = [&](int st, int sl) {
+        const int c = 2 * st + fh;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          af[sl][i] = *reinterpret_cast<const bf16x8*>(Ab + i * 32 * GB_LD + ks);
+          af[sl][i] = *reinterpret_cast<const bf16x8*>(Ab + gb_slot(wm * 128 + i * 32 + fr, c));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          bf[sl][j] = *reinterpret_cast<const bf16x8*>(Bb + j * 32 * GB_LD + ks);
-          if constexpr (SW) b3f[sl][j] = *reinterpret_cast<const bf16x8*>(B3b + j * 32 * GB_LD + ks);
+          bf[sl][j] = *reinterpret_cast<const bf16x8*>(Bb + gb_slot(wn * 64 + j * 32 + fr, c));
+          if constexpr (SW)
+            b3f[sl][j] = *reinterpret_cast<const bf16x8*>(B3b + gb_slot(wn * 64 + j * 32 + fr, c));
         }
       };
       frags(0, 0);
 #pragma unroll
       for (int st = 0; st < GB_BK / 16; ++st) {
         const int sl = st & 1;
-        if (st + 1 < GB_BK / 16) frags((st + 1) * 16, sl ^ 1);
+        if (st + 1 < GB_BK / 16) frags(st + 1, sl ^ 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -314,14 +325,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    // the next slice has landed (the barrier waits for the direct loads) and
+    // every wave is done with this one
     __syncthreads();
   }
 
   if (!active) return;
   // register group q of acc[i][j] holds columns wn*64 + 32j + 8q + 4(lane/32) .. +3
   // of row wm*128 + 32i + lane%32
-  const int q4 = (lane >> 5) * 4;
+  const int q4 = fh * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = wm * 128 + 32 * i + fr;
@@ -409,7 +421,7 @@ int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E) {
 template <int EPI>
 static hipError_t launch_big(const GemmArgs& g, int64_t qmax, hipStream_t s) {
   constexpr size_t lds =
-      sizeof(bf16_t) * (size_t)GB_LD * 2 * (GB_BM + GB_BN * (EPI == EPI_SWIGLU ? 2 : 1));
+      sizeof(bf16_t) * (size_t)GB_BK * 2 * (GB_BM + GB_BN * (EPI == EPI_SWIGLU ? 2 : 1));
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI>,
