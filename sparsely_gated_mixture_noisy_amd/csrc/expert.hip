@@ -366,6 +366,25 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // fp32 path: one thread per output element.
 // ---------------------------------------------------------------------------
+// sum_c a[c] b[c] in c order, 16-byte loads when both rows allow them
+__device__ __forceinline__ float dot_f32(const float* a, const float* b, int n) {
+  float s = 0.f;
+  int c = 0;
+  if (((n | (int)((uintptr_t)a | (uintptr_t)b)) & 3) == 0 &&
+      (((uintptr_t)a | (uintptr_t)b) & 15) == 0) {
+    for (; c < n; c += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(a + c);
+      const float4 y = *reinterpret_cast<const float4*>(b + c);
+      s = fmaf(x.x, y.x, s);
+      s = fmaf(x.y, y.y, s);
+      s = fmaf(x.z, y.z, s);
+      s = fmaf(x.w, y.w, s);
+    }
+  }
+  for (; c < n; ++c) s = fmaf(a[c], b[c], s);
+  return s;
+}
+
 __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int p) {
   int lo = 0, hi = E - 1;
   while (lo < hi) {
@@ -383,13 +402,11 @@ __global__ __launch_bounds__(256) void ffn1_f32_kernel(FfnArgs a, int swiglu) {
   const int64_t src = a.perm ? (int64_t)(a.perm[p] / a.k) : (int64_t)p;
   const float* xr = (const float*)a.x + src * a.d;
   const float* w1 = (const float*)a.w1 + ((int64_t)e * a.h + j) * a.d;
-  float s = 0.f;
-  for (int c = 0; c < a.d; ++c) s = fmaf(xr[c], w1[c], s);
+  const float* w3 = swiglu ? (const float*)a.w3 + ((int64_t)e * a.h + j) * a.d : w1;
+  const float s = dot_f32(xr, w1, a.d);
   float v;
   if (swiglu) {
-    const float* w3 = (const float*)a.w3 + ((int64_t)e * a.h + j) * a.d;
-    float u = 0.f;
-    for (int c = 0; c < a.d; ++c) u = fmaf(xr[c], w3[c], u);
+    const float u = dot_f32(xr, w3, a.d);
     v = silu_f(s) * u;
   } else {
     v = fmaxf(s, 0.f);
@@ -404,9 +421,7 @@ __global__ __launch_bounds__(256) void ffn2_f32_kernel(FfnArgs a) {
   const int e = expert_of_row(a.offsets, a.E, p);
   const float* hr = (const float*)a.hid + (int64_t)p * a.h;
   const float* w2 = (const float*)a.w2 + ((int64_t)e * a.d + n) * a.h;
-  float s = 0.f;
-  for (int c = 0; c < a.h; ++c) s = fmaf(hr[c], w2[c], s);
-  ((float*)a.y_sorted)[i] = s;
+  ((float*)a.y_sorted)[i] = dot_f32(hr, w2, a.h);
 }
 
 // The large-tile kernel pays off once the experts average a full tile of rows.
