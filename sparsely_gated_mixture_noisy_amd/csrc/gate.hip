@@ -6,16 +6,19 @@
 //   H_e     = clean_e + eps_e * softplus(x . W_noise[e])   (noisy gate)
 //   keep the k largest H_e (ties: lower e), softmax over the kept ones.
 //
-// A workgroup (8 waves) scores a tile of 32 rows against the experts in
-// blocks of 256: wave w computes the clean and the raw-noise scores of
-// experts blk + 32w .. +31 for all 32 rows with v_mfma_f32_32x32x16_bf16 (one
-// LDS input fragment feeds both tables' MFMAs; the table rows stream from
-// global memory through a register ring).  The scores stay in the MFMA
-// accumulator layout: lane l holds expert (l mod 32) of its wave for the 16
-// tile rows acc_row(i, l).  The noisy scores go through LDS to the selection
-// step, where 16 lanes per row keep running top-(k+1) lists that are merged
-// with lane shuffles.  For the smooth load the clean scores and noise scales
-// never leave the registers.
+// A workgroup (8 waves) scores a tile of 32 rows (64 for large expert
+// counts: RB = 2 blocks of 32, so that every table fragment fetched serves
+// twice the rows) against the experts in blocks of 256: wave w computes the
+// clean and the raw-noise scores of experts blk + 32w .. +31 for all the rows
+// with v_mfma_f32_32x32x16_bf16 (one LDS input fragment feeds both tables'
+// MFMAs; the table rows stream from global memory through a register ring).
+// The scores stay in the MFMA accumulator layout: lane l holds expert
+// (l mod 32) of its wave for the 16 rows acc_row(i, l) of each 32-row block.
+// The noisy scores go through LDS to the selection step, where 16 (RB = 2:
+// 8) lanes per row keep running top-(k+1) lists merged over DPP rows.  For
+// the smooth load the clean scores and noise scales never leave the
+// registers.  Outputs that feed the routing and the balance statistics (masks,
+// partial sums) are written per 32-token block whatever the tile size.
 #include <algorithm>
 
 #include "moe_device.h"
@@ -27,11 +30,18 @@ constexpr int GATE_ROWS = 32;
 constexpr int GATE_WAVES = 8;
 constexpr int GATE_THREADS = 64 * GATE_WAVES;
 constexpr int GATE_BLOCK_E = 32 * GATE_WAVES;      // experts per projection block
-constexpr int GATE_TPR = GATE_THREADS / GATE_ROWS;  // selection lanes per row
-static_assert(GATE_TPR == 16, "a row's selection lanes form one 16-lane DPP row");
 constexpr int GATE_XLDS_MAX_D = 1024;               // input tile in LDS up to this d_model
 constexpr int GATE_RING = 16;                       // table k-steps in flight per wave
 constexpr int HLD = GATE_BLOCK_E + 1;               // LDS row stride of the score block
+
+// A tile of RB blocks of 32 rows.
+template <int RB>
+struct GateTile {
+  static constexpr int R = GATE_ROWS * RB;           // rows
+  static constexpr int TPR = GATE_THREADS / R;       // selection lanes per row (16 or 8)
+  static constexpr int NQ = GATE_BLOCK_E / TPR;      // scores per lane per expert block
+  static_assert(TPR == 16 || TPR == 8, "a row's selection lanes lie inside one DPP row");
+};
 
 // Tile row held in accumulator register i of lane l (32x32 MFMA layout).
 __device__ __forceinline__ int acc_row(int i, int lane) {
@@ -62,11 +72,11 @@ struct GateTabs {
   int pk_nt;
 };
 
-// Copy the 32 input rows of a tile to LDS (bf16, d % 8 == 0).
-__device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* rows, bf16_t* Xs,
-                                            int xld) {
+// Copy the nr input rows of a tile to LDS (bf16, d % 8 == 0).
+__device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* rows, int nr,
+                                            bf16_t* Xs, int xld) {
   const int cpr = d / 8;
-  for (int c = threadIdx.x; c < GATE_ROWS * cpr; c += GATE_THREADS) {
+  for (int c = threadIdx.x; c < nr * cpr; c += GATE_THREADS) {
     const int r = c / cpr, cc = (c % cpr) * 8;
     *reinterpret_cast<u32x4*>(Xs + r * xld + cc) =
         *reinterpret_cast<const u32x4*>(x + (int64_t)rows[r] * d + cc);
@@ -78,7 +88,7 @@ __device__ __forceinline__ void load_x_tile(const bf16_t* x, int d, const int* r
 // e = blk + 32 * wave + (lane & 31).  Columns past E read a valid table row
 // and are never used; waves with no valid column skip the MFMAs.  XLDS: the
 // input rows are in the LDS tile Xs (bf16 only).
-template <typename T, bool NOISY, bool XLDS>
+template <typename T, bool NOISY, bool XLDS, int RB = 1>
 struct BlockProj;
 
 // bf16: the contraction runs over groups of 64 columns.  Lane (c, h) of a
@@ -89,18 +99,22 @@ struct BlockProj;
 // of the columns, the same for both operands, so every product term appears
 // exactly once; the four loads of a piece run over whole cache lines back to
 // back.  A ring of GATE_RING / 4 groups per table stays in flight.
-template <bool NOISY, bool XLDS>
-struct BlockProj<bf16_t, NOISY, XLDS> {
-  static constexpr int RG = GATE_RING / 4;  // groups in flight per table
+template <bool NOISY, bool XLDS, int RB>
+struct BlockProj<bf16_t, NOISY, XLDS, RB> {
+  static constexpr int RG = RB == 1 ? GATE_RING / 4 : 2;  // groups in flight per table
   static __device__ __forceinline__ u32x4 ld(const bf16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
   }
   static __device__ __forceinline__ void run(const TileX<bf16_t>& tx, int d, const GateTabs& tb,
-                                             int blk, int E, f32x16& ac, f32x16& ar) {
+                                             int blk, int E, f32x16 (&ac)[RB],
+                                             f32x16 (&ar)[RB]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c = lane & 31, kh = (lane >> 5) * 32;
-    ac = f32x16{};
-    ar = f32x16{};
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      ac[i] = f32x16{};
+      ar[i] = f32x16{};
+    }
     if (blk + w * 32 >= E) return;
     const int NG = d / 64;
     // table piece j of column group G sits at pg + G * gs + j * js
@@ -119,7 +133,11 @@ struct BlockProj<bf16_t, NOISY, XLDS> {
       gs = 64;
       js = 8;
     }
-    const bf16_t* pa = XLDS ? tx.Xs + c * tx.xld + kh : tx.x + (int64_t)tx.rows[c] * d + kh;
+    const bf16_t* pa[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      pa[i] = XLDS ? tx.Xs + (32 * i + c) * tx.xld + kh
+                   : tx.x + (int64_t)tx.rows[32 * i + c] * d + kh;
     u32x4 rg[RG][4], rn[RG][4];
 #pragma unroll
     for (int sl = 0; sl < RG; ++sl) {
@@ -136,9 +154,12 @@ struct BlockProj<bf16_t, NOISY, XLDS> {
       for (int sl = 0; sl < RG; ++sl) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, ld(pa + (g + sl) * 64 + j * 8));
-          ac = mfma32(a, __builtin_bit_cast(bf16x8, rg[sl][j]), ac);
-          if (NOISY) ar = mfma32(a, __builtin_bit_cast(bf16x8, rn[sl][j]), ar);
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, ld(pa[i] + (g + sl) * 64 + j * 8));
+            ac[i] = mfma32(a, __builtin_bit_cast(bf16x8, rg[sl][j]), ac[i]);
+            if (NOISY) ar[i] = mfma32(a, __builtin_bit_cast(bf16x8, rn[sl][j]), ar[i]);
+          }
         }
         // refill the slot with the group RG further on (the last one again
         // past the end)
@@ -159,11 +180,14 @@ struct BlockProj<bf16_t, NOISY, XLDS> {
       const bool live = g + sl < NG;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x4 av = ld(pa + G * 64 + j * 8);
-        if (!live) av = u32x4{0u, 0u, 0u, 0u};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-        ac = mfma32(a, __builtin_bit_cast(bf16x8, rg[sl][j]), ac);
-        if (NOISY) ar = mfma32(a, __builtin_bit_cast(bf16x8, rn[sl][j]), ar);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          u32x4 av = ld(pa[i] + G * 64 + j * 8);
+          if (!live) av = u32x4{0u, 0u, 0u, 0u};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+          ac[i] = mfma32(a, __builtin_bit_cast(bf16x8, rg[sl][j]), ac[i]);
+          if (NOISY) ar[i] = mfma32(a, __builtin_bit_cast(bf16x8, rn[sl][j]), ar[i]);
+        }
       }
     }
   }
@@ -173,10 +197,13 @@ struct BlockProj<bf16_t, NOISY, XLDS> {
 // the 16 rows (16 independent chains) and, when d % 4 == 0, four at a time on
 // 16-byte loads.
 template <bool NOISY, bool XLDS>
-struct BlockProj<float, NOISY, XLDS> {
+struct BlockProj<float, NOISY, XLDS, 1> {
   static __device__ __forceinline__ void run(const TileX<float>& tx, int d, const GateTabs& tb,
-                                             int blk, int E, f32x16& ac, f32x16& ar) {
+                                             int blk, int E, f32x16 (&acs)[1],
+                                             f32x16 (&ars)[1]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    f32x16& ac = acs[0];
+    f32x16& ar = ars[0];
     ac = f32x16{};
     ar = f32x16{};
     if (blk + w * 32 >= E) return;
@@ -239,11 +266,15 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
 }
-__device__ __forceinline__ float row16_max(float m) {
+// max over the TPR (16 or 8) lanes of a row (8 lanes: a half DPP row, which
+// the first three steps cover)
+template <int TPR>
+__device__ __forceinline__ float row_max(float m) {
   m = fmaxf(m, dpp_f<DPP_XOR1>(m));
   m = fmaxf(m, dpp_f<DPP_XOR2>(m));
   m = fmaxf(m, dpp_f<DPP_HALF_MIRROR>(m));
-  return fmaxf(m, dpp_f<DPP_MIRROR>(m));
+  if constexpr (TPR == 16) m = fmaxf(m, dpp_f<DPP_MIRROR>(m));
+  return m;
 }
 template <int CTRL>
 __device__ __forceinline__ void best_step(float& bv, int& be) {
@@ -276,9 +307,10 @@ struct TopList {
       }
     }
   }
-  // Merge the lists of the GATE_TPR (16) lanes of a row, one DPP row: every
-  // lane ends with the row's best K1 (value, expert) pairs in rank order.
-  // An expert sits in one lane's list only, so one lane pops per round.
+  // Merge the lists of the TPR (16 or 8) lanes of a row, inside one DPP row:
+  // every lane ends with the row's best K1 (value, expert) pairs in rank
+  // order.  An expert sits in one lane's list only, so one lane pops per round.
+  template <int TPR>
   __device__ __forceinline__ void merge(float* ov, int* oe) {
 #pragma unroll
     for (int round = 0; round < K1; ++round) {
@@ -287,7 +319,7 @@ struct TopList {
       best_step<DPP_XOR1>(bv, be);
       best_step<DPP_XOR2>(bv, be);
       best_step<DPP_HALF_MIRROR>(bv, be);
-      best_step<DPP_MIRROR>(bv, be);
+      if constexpr (TPR == 16) best_step<DPP_MIRROR>(bv, be);
       ov[round] = bv;
       oe[round] = be;
       if (e[0] == be) {
@@ -368,121 +400,133 @@ __device__ __forceinline__ float load_column_sum(const f32x16& clean, const f32x
   return s + __shfl_xor(s, 32, 64);
 }
 
-// The scoring and selection of one 32-row tile against experts [0, E) of a
-// table block (tb).  eps_row(r) gives the
-// noise row of tile row r (experts contiguous).  On return every lane of a
-// row's group holds the row's top-K1 in ov/oe, and cs/ss the clean scores
-// (bias included) and noise scales of the last expert block.
-template <typename T, int K1, bool NOISY, bool XLDS, typename EpsRow>
+// The scoring and selection of one tile of RB 32-row blocks against experts
+// [0, E) of a table block (tb).  eps_row(r) gives the noise row of tile row r
+// (experts contiguous); Hs is the R x HLD score block in LDS.  On return every
+// lane of a row's group holds the row's top-K1 in ov/oe, and cs/ss the clean
+// scores (bias included) and noise scales of the last expert block.
+template <typename T, int K1, bool NOISY, bool XLDS, int RB, typename EpsRow>
 __device__ void score_tile(const TileX<T>& tx, int d, const GateTabs& tb,
-                           const float* __restrict__ bias, int E, EpsRow eps_row,
-                           float (*Hs)[HLD], float* ov, int* oe, f32x16& cs, f32x16& ss) {
+                           const float* __restrict__ bias, int E, EpsRow eps_row, float* Hs,
+                           float* ov, int* oe, f32x16 (&cs)[RB], f32x16 (&ss)[RB]) {
+  using GT = GateTile<RB>;
+  constexpr int TPR = GT::TPR, NQ = GT::NQ;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int row = tid / GATE_TPR, sub = tid % GATE_TPR;
+  const int row = tid / TPR, sub = tid % TPR;
   TopList<K1> L;
   L.init();
   for (int blk = 0; blk < E; blk += GATE_BLOCK_E) {
     const int e = blk + w * 32 + (lane & 31);
     const bool ev = e < E;
-    // noise of this lane's 16 (row, expert) pairs, requested before the MFMAs
-    float ep[16];
+    // noise of this lane's (row, expert) pairs, requested before the MFMAs
+    float ep[RB][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ep[i] = (NOISY && ev) ? eps_row(acc_row(i, lane))[e] : 0.f;
-    f32x16 ac, ar;
-    BlockProj<T, NOISY, XLDS>::run(tx, d, tb, blk, E, ac, ar);
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ep[i][r] = (NOISY && ev) ? eps_row(32 * i + acc_row(r, lane))[e] : 0.f;
+    f32x16 ac[RB], ar[RB];
+    BlockProj<T, NOISY, XLDS, RB>::run(tx, d, tb, blk, E, ac, ar);
     const float b = (bias && ev) ? bias[tb.row0 + e] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float c = ac[i] + b;
-      float h = c;
-      if (NOISY) {
-        const float sp = softplus_f(ar[i]);
-        h = c + ep[i] * sp;
-        ss[i] = sp;
-      } else {
-        ss[i] = 0.f;
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float c = ac[i][r] + b;
+        float h = c;
+        if (NOISY) {
+          const float sp = softplus_f(ar[i][r]);
+          h = c + ep[i][r] * sp;
+          ss[i][r] = sp;
+        } else {
+          ss[i][r] = 0.f;
+        }
+        cs[i][r] = c;
+        Hs[(32 * i + acc_row(r, lane)) * HLD + w * 32 + (lane & 31)] = h;
       }
-      cs[i] = c;
-      Hs[acc_row(i, lane)][w * 32 + (lane & 31)] = h;
-    }
     __syncthreads();
-    // lane `sub` of the row holds columns sub + 16q.  Only scores at or above
-    // tau, the K1-th largest of the row's 16 lane maxima, can be among the
+    // lane `sub` of the row holds columns sub + TPR*q.  Only scores at or above
+    // tau, the K1-th largest of the row's TPR lane maxima, can be among the
     // block's best K1 (K1 lanes hold a score >= tau); lanes whose maxima tie
     // leave together, which only lowers tau.
     const int nb = min(GATE_BLOCK_E, E - blk);
-    float hv[GATE_BLOCK_E / GATE_TPR];
+    float hv[NQ];
     float mx = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < GATE_BLOCK_E / GATE_TPR; ++q) {
-      const int j = sub + GATE_TPR * q;
-      hv[q] = j < nb ? Hs[row][j] : -INFINITY;
+    for (int q = 0; q < NQ; ++q) {
+      const int j = sub + TPR * q;
+      hv[q] = j < nb ? Hs[row * HLD + j] : -INFINITY;
       mx = fmaxf(mx, hv[q]);
     }
     float tau = -INFINITY;
 #pragma unroll
     for (int r = 0; r < K1; ++r) {
-      tau = row16_max(mx);
+      tau = row_max<TPR>(mx);
       mx = mx == tau ? -INFINITY : mx;
     }
     uint32_t cand = 0u;
 #pragma unroll
-    for (int q = 0; q < GATE_BLOCK_E / GATE_TPR; ++q)
-      if (sub + GATE_TPR * q < nb && hv[q] >= tau) cand |= 1u << q;
+    for (int q = 0; q < NQ; ++q)
+      if (sub + TPR * q < nb && hv[q] >= tau) cand |= 1u << q;
     while (cand) {
       const int q = __ffs(cand) - 1;
       cand &= cand - 1u;
-      const int j = sub + GATE_TPR * q;
-      L.insert(Hs[row][j], blk + j);
+      const int j = sub + TPR * q;
+      L.insert(Hs[row * HLD + j], blk + j);
     }
     __syncthreads();
   }
-  L.merge(ov, oe);
+  L.template merge<TPR>(ov, oe);
 }
 
 // ---------------------------------------------------------------------------
-// Flat gate: tile = 32 consecutive tokens.  With a.part set (noisy gate,
-// E <= GATE_FUSED_LOAD_MAX_E) the kernel also writes the tile's row of
-// smooth-load partial sums; with a.imp_part (E <= GATE_FUSED_LOAD_MAX_E) its
-// row of gate sums per expert (rows in ascending order); with a.bits the
-// tile's routing masks.  All use the masks sb[E] in LDS (bit r of sb[e]:
-// tile row r keeps expert e).
+// Flat gate: tile = R = 32*RB consecutive tokens.  With a.part set (noisy
+// gate, E <= GATE_FUSED_LOAD_MAX_E) the kernel also writes the smooth-load
+// partial sums of each of its 32-token blocks; with a.imp_part (E <=
+// GATE_FUSED_LOAD_MAX_E) their gate sums per expert (rows in ascending order);
+// with a.bits their routing masks.  All use the masks sb[RB][E] in LDS (bit r
+// of sb[i][e]: row 32i + r keeps expert e).
+// Dynamic LDS: input tile (XLDS), score block Hs[R][HLD], masks.
 // ---------------------------------------------------------------------------
-template <typename T, int K1, bool NOISY, bool XLDS>
+template <typename T, int K1, bool NOISY, bool XLDS, int RB>
 __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a) {
-  __shared__ float Hs[GATE_ROWS][HLD];
-  __shared__ int rows[GATE_ROWS];
-  __shared__ RowThr thr[GATE_ROWS];
-  __shared__ int kle[GATE_ROWS][8];    // kept experts of each row
-  __shared__ float klg[GATE_ROWS][8];  // and their gates
+  using GT = GateTile<RB>;
+  constexpr int R = GT::R, TPR = GT::TPR;
+  __shared__ int rows[R];
+  __shared__ RowThr thr[R];
+  __shared__ int kle[R][8];    // kept experts of each row
+  __shared__ float klg[R][8];  // and their gates
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  const int64_t t0 = (int64_t)blockIdx.x * R;
+  const int64_t nblk = (a.T + GATE_ROWS - 1) / GATE_ROWS;  // 32-token blocks of the batch
   const int E = a.E;
-  if (tid < GATE_ROWS) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
+  if (tid < R) rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
   const int xld = a.d + 8;
+  const size_t xbytes = XLDS ? sizeof(bf16_t) * R * xld : 0;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
+  float* Hs = reinterpret_cast<float*>(dyn + xbytes);
+  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + xbytes + sizeof(float) * R * HLD);
   const bool masks = a.bits || (NOISY && a.part) || a.imp_part;
-  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
   if (masks)
-    for (int i = tid; i < E; i += GATE_THREADS) sb[i] = 0u;
+    for (int i = tid; i < RB * E; i += GATE_THREADS) sb[i] = 0u;
   __syncthreads();
-  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, R, Xs, xld);
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const float* eps = a.eps;
   auto eps_row = [&](int r) -> const float* { return eps + (int64_t)rows[r] * E; };
   float ov[K1];
   int oe[K1];
-  f32x16 cs, ss;
+  f32x16 cs[RB], ss[RB];
   const GateTabs tb{a.w_gate, a.w_noise, 0, (const bf16_t*)a.w_pack, 0, a.pack_nt};
-  score_tile<T, K1, NOISY, XLDS>(tx, a.d, tb, a.bias, E, eps_row, Hs, ov, oe, cs, ss);
+  score_tile<T, K1, NOISY, XLDS, RB>(tx, a.d, tb, a.bias, E, eps_row, Hs, ov, oe, cs, ss);
   int ke[K1];
   float kg[K1], kth, k1th;
   kept_gates<K1>(ov, oe, a.k, E, ke, kg, &kth, &k1th);
-  const int row = tid / GATE_TPR;
+  const int row = tid / TPR;
   const int64_t t = t0 + row;
-  if (tid % GATE_TPR == 0) {
+  if (tid % TPR == 0) {
     if (t < a.T) {
 #pragma unroll
       for (int j = 0; j < K1; ++j) {
@@ -498,7 +542,8 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
       if (masks) {
 #pragma unroll
         for (int j = 0; j < K1; ++j)
-          if (j < a.k && (unsigned)ke[j] < (unsigned)E) atomicOr(&sb[ke[j]], 1u << row);
+          if (j < a.k && (unsigned)ke[j] < (unsigned)E)
+            atomicOr(&sb[(row >> 5) * E + ke[j]], 1u << (row & 31));
       }
     }
     thr[row].kth = kth;
@@ -512,27 +557,32 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
     }
   }
   if (masks) __syncthreads();
-  if (a.imp_part) {
-    for (int e = tid; e < E; e += GATE_THREADS) {
-      uint32_t m = sb[e];
-      float s = 0.f;
-      while (m) {
-        const int r = __ffs(m) - 1;
-        m &= m - 1u;
-        for (int j = 0; j < a.k; ++j)
-          if (kle[r][j] == e) s += klg[r][j];
+#pragma unroll
+  for (int hb = 0; hb < RB; ++hb) {
+    const int64_t blk = (int64_t)blockIdx.x * RB + hb;  // 32-token block
+    if (blk >= nblk) break;
+    if (a.imp_part) {
+      for (int e = tid; e < E; e += GATE_THREADS) {
+        uint32_t m = sb[hb * E + e];
+        float s = 0.f;
+        while (m) {
+          const int r = 32 * hb + __ffs(m) - 1;
+          m &= m - 1u;
+          for (int j = 0; j < a.k; ++j)
+            if (kle[r][j] == e) s += klg[r][j];
+        }
+        a.imp_part[blk * E + e] = s;
       }
-      a.imp_part[(int64_t)blockIdx.x * E + e] = s;
     }
-  }
-  if (a.bits)
-    for (int i = tid; i < E; i += GATE_THREADS) a.bits[(int64_t)blockIdx.x * E + i] = sb[i];
-  if (NOISY && a.part) {
-    const int e = (tid >> 6) * 32 + (lane & 31);
-    const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
-    const uint32_t kept = e < E ? sb[e] : 0u;
-    const float s = load_column_sum(cs, ss, kept, thr, valid);
-    if (lane < 32 && e < E) a.part[(int64_t)blockIdx.x * E + e] = s;
+    if (a.bits)
+      for (int i = tid; i < E; i += GATE_THREADS) a.bits[blk * E + i] = sb[hb * E + i];
+    if (NOISY && a.part) {
+      const int e = (tid >> 6) * 32 + (lane & 31);
+      const int valid = (int)max<int64_t>(0, min<int64_t>(GATE_ROWS, a.T - blk * GATE_ROWS));
+      const uint32_t kept = e < E ? sb[hb * E + e] : 0u;
+      const float s = load_column_sum(cs[hb], ss[hb], kept, thr + 32 * hb, valid);
+      if (lane < 32 && e < E) a.part[blk * E + e] = s;
+    }
   }
 }
 
@@ -541,10 +591,11 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
 // one group g, taken from the group routing (perm_g, offsets_g); tile i of
 // group g covers positions offsets_g[g] + 32*(i - tiles_g[g]) onward.
 // Writes the final experts g*Eg + j and gates gate_p * gate_s directly.
+// Dynamic LDS: input tile (XLDS), score block Hs[32][HLD].
 // ---------------------------------------------------------------------------
 template <typename T, int K1, bool NOISY, bool XLDS>
 __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs a) {
-  __shared__ float Hs[GATE_ROWS][HLD];
+  constexpr int TPR = GateTile<1>::TPR;
   __shared__ int rows[GATE_ROWS];
   __shared__ int asg[GATE_ROWS];
   __shared__ int s_g, s_p0, s_n;
@@ -572,8 +623,10 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
   }
   __syncthreads();
   const int xld = a.d + 8;
+  const size_t xbytes = XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
-  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  float* Hs = reinterpret_cast<float*>(dyn + xbytes);
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, GATE_ROWS, Xs, xld);
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const int Eg = a.Eg, G = a.G;
@@ -581,12 +634,12 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
   auto eps_row = [&](int r) -> const float* { return eps + ((int64_t)rows[r] * G + g) * Eg; };
   float ov[K1];
   int oe[K1];
-  f32x16 cs, ss;
+  f32x16 cs[1], ss[1];
   const GateTabs tb{a.w_gate, a.w_noise, g * Eg, (const bf16_t*)a.w_pack,
                     g * ((Eg + 31) / 32), a.pack_nt};
-  score_tile<T, K1, NOISY, XLDS>(tx, a.d, tb, nullptr, Eg, eps_row, Hs, ov, oe, cs, ss);
-  const int row = tid / GATE_TPR;
-  if (tid % GATE_TPR == 0 && row < n) {
+  score_tile<T, K1, NOISY, XLDS, 1>(tx, a.d, tb, nullptr, Eg, eps_row, Hs, ov, oe, cs, ss);
+  const int row = tid / TPR;
+  if (tid % TPR == 0 && row < n) {
     int ke[K1];
     float kg[K1], kth, k1th;
     kept_gates<K1>(ov, oe, a.kpg, Eg, ke, kg, &kth, &k1th);
@@ -607,24 +660,28 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
 
 // ---------------------------------------------------------------------------
 // Smooth load estimate (flat noisy gate), recomputing the projections from
-// the gate's thresholds.  Workgroup b covers tokens [32b, 32b+32) and writes
-//   part[b][e] = sum over its rows of
+// the gate's thresholds.  Workgroup b covers tokens [R b, R b + R), R = 32*RB,
+// and writes for each of its 32-token blocks c
+//   part[c][e] = sum over the block's rows of
 //                Phi((clean[t,e] - theta[t,e]) / softplus(raw[t,e]))
 // with theta = thr[t][1] if e is kept by t, else thr[t][0]: the same terms,
 // in the same order, as the gate kernel's fused variant.
+// Dynamic LDS: input tile (XLDS), masks sb[RB][E].
 // ---------------------------------------------------------------------------
-template <typename T, bool XLDS>
+template <typename T, bool XLDS, int RB>
 __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) {
-  __shared__ int rows[GATE_ROWS];
-  __shared__ RowThr thr[GATE_ROWS];
+  constexpr int R = GateTile<RB>::R;
+  __shared__ int rows[R];
+  __shared__ RowThr thr[R];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  const int64_t t0 = (int64_t)blockIdx.x * R;
+  const int64_t nblk = (a.T + GATE_ROWS - 1) / GATE_ROWS;
   const int xld = a.d + 8;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
-  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
-  for (int i = tid; i < a.E; i += GATE_THREADS) sb[i] = 0u;
-  if (tid < GATE_ROWS) {
+  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * R * xld : 0));
+  for (int i = tid; i < RB * a.E; i += GATE_THREADS) sb[i] = 0u;
+  if (tid < R) {
     const int r = (int)min<int64_t>(t0 + tid, a.T - 1);
     rows[tid] = r;
     thr[tid].kth = a.thr[2 * (int64_t)r];
@@ -632,40 +689,48 @@ __global__ __launch_bounds__(GATE_THREADS) void load_partial_kernel(LoadArgs a) 
   }
   __syncthreads();
   // kept-expert masks of the tile's valid rows
-  for (int i = tid; i < GATE_ROWS * a.k; i += GATE_THREADS) {
+  for (int i = tid; i < R * a.k; i += GATE_THREADS) {
     const int r = i / a.k;
     const int e = t0 + r < a.T ? a.idx[(t0 + r) * a.k + i % a.k] : -1;
-    if ((unsigned)e < (unsigned)a.E) atomicOr(&sb[e], 1u << r);
+    if ((unsigned)e < (unsigned)a.E) atomicOr(&sb[(r >> 5) * a.E + e], 1u << (r & 31));
   }
-  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, Xs, xld);
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, R, Xs, xld);
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
-  const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
   const GateTabs tb{a.w_gate, a.w_noise, 0, (const bf16_t*)a.w_pack, 0, 2};
   for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
     const int e = blk + w * 32 + (lane & 31);
-    f32x16 ac, ar;
-    BlockProj<T, true, XLDS>::run(tx, a.d, tb, blk, a.E, ac, ar);
+    f32x16 ac[RB], ar[RB];
+    BlockProj<T, true, XLDS, RB>::run(tx, a.d, tb, blk, a.E, ac, ar);
     const float b = (a.bias && e < a.E) ? a.bias[e] : 0.f;
-    f32x16 cs, ss;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      cs[i] = ac[i] + b;
-      ss[i] = softplus_f(ar[i]);
+    for (int hb = 0; hb < RB; ++hb) {
+      const int64_t cb = (int64_t)blockIdx.x * RB + hb;  // 32-token block
+      f32x16 cs, ss;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        cs[i] = ac[hb][i] + b;
+        ss[i] = softplus_f(ar[hb][i]);
+      }
+      const int valid = (int)max<int64_t>(0, min<int64_t>(GATE_ROWS, a.T - cb * GATE_ROWS));
+      const uint32_t kept = e < a.E ? sb[hb * a.E + e] : 0u;
+      const float s = load_column_sum(cs, ss, kept, thr + 32 * hb, valid);
+      if (lane < 32 && e < a.E && cb < nblk) a.part[cb * a.E + e] = s;
     }
-    const uint32_t kept = e < a.E ? sb[e] : 0u;
-    const float s = load_column_sum(cs, ss, kept, thr, valid);
-    if (lane < 32 && e < a.E) a.part[(int64_t)blockIdx.x * a.E + e] = s;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-static size_t xtile_bytes(bool bf16, int d) {
-  return (bf16 && d <= GATE_XLDS_MAX_D) ? sizeof(bf16_t) * GATE_ROWS * (size_t)(d + 8) : 0;
+static bool xtile_in_lds(bool bf16, int d) { return bf16 && d <= GATE_XLDS_MAX_D; }
+
+static size_t xtile_bytes(bool bf16, int d, int rows) {
+  return xtile_in_lds(bf16, d) ? sizeof(bf16_t) * rows * (size_t)(d + 8) : 0;
 }
 
+// Dynamic LDS the kernels may take (the static arrays come on top).
+constexpr size_t GATE_DYN_LDS_MAX = 150 * 1024;
 
 // Raise a kernel's dynamic LDS limit when needed; `done` caches the largest
 // size already granted to that kernel.
@@ -678,37 +743,60 @@ static hipError_t set_lds(K kernel, size_t bytes, size_t* done) {
   return err;
 }
 
-static bool xtile_in_lds(bool bf16, int d) { return bf16 && d <= GATE_XLDS_MAX_D; }
+// Tiles of 64 rows for large expert counts (each table fragment serves twice
+// the rows), when the input tile is in LDS and everything fits.
+static size_t flat_lds(bool bf16, int d, int E, bool masks, int rb) {
+  return xtile_bytes(bf16, d, 32 * rb) + sizeof(float) * 32 * rb * HLD +
+         (masks ? sizeof(uint32_t) * (size_t)rb * E : 0);
+}
+static int flat_rb(bool bf16, int d, int E, bool masks) {
+  return (xtile_in_lds(bf16, d) && E >= 2 * GATE_BLOCK_E &&
+          flat_lds(bf16, d, E, masks, 2) <= GATE_DYN_LDS_MAX) ? 2 : 1;
+}
+static size_t load_lds(bool bf16, int d, int E, int rb) {
+  return xtile_bytes(bf16, d, 32 * rb) + sizeof(uint32_t) * (size_t)rb * E;
+}
+static int load_rb(bool bf16, int d, int E) {
+  return (xtile_in_lds(bf16, d) && E >= 2 * GATE_BLOCK_E &&
+          load_lds(bf16, d, E, 2) <= GATE_DYN_LDS_MAX) ? 2 : 1;
+}
 
-template <typename T, int K1, bool NOISY, bool XLDS>
+template <typename T, int K1, bool NOISY, bool XLDS, int RB>
 static hipError_t launch_flat_v(const GateFlatArgs& a, size_t sh, hipStream_t s) {
   static size_t granted = 0;
-  hipError_t err = set_lds(gate_flat_kernel<T, K1, NOISY, XLDS>, sh, &granted);
+  hipError_t err = set_lds(gate_flat_kernel<T, K1, NOISY, XLDS, RB>, sh, &granted);
   if (err != hipSuccess) return err;
-  dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
-  hipLaunchKernelGGL((gate_flat_kernel<T, K1, NOISY, XLDS>), grid, dim3(GATE_THREADS), sh, s, a);
+  constexpr int R = GateTile<RB>::R;
+  dim3 grid((unsigned)((a.T + R - 1) / R));
+  hipLaunchKernelGGL((gate_flat_kernel<T, K1, NOISY, XLDS, RB>), grid, dim3(GATE_THREADS), sh, s,
+                     a);
   return hipGetLastError();
 }
 
-template <typename T, int K1>
-static hipError_t launch_flat_k(const GateFlatArgs& a, size_t sh, bool noisy, hipStream_t s) {
+template <typename T, int K1, bool NOISY>
+static hipError_t launch_flat_n(const GateFlatArgs& a, bool masks, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (xtile_in_lds(true, a.d))
-      return noisy ? launch_flat_v<T, K1, true, true>(a, sh, s)
-                   : launch_flat_v<T, K1, false, true>(a, sh, s);
+    if (xtile_in_lds(true, a.d)) {
+      if (flat_rb(true, a.d, a.E, masks) == 2)
+        return launch_flat_v<T, K1, NOISY, true, 2>(a, flat_lds(true, a.d, a.E, masks, 2), s);
+      return launch_flat_v<T, K1, NOISY, true, 1>(a, flat_lds(true, a.d, a.E, masks, 1), s);
+    }
   }
-  return noisy ? launch_flat_v<T, K1, true, false>(a, sh, s)
-               : launch_flat_v<T, K1, false, false>(a, sh, s);
+  return launch_flat_v<T, K1, NOISY, false, 1>(a, flat_lds(sizeof(T) == 2, a.d, a.E, masks, 1), s);
+}
+
+template <typename T, int K1>
+static hipError_t launch_flat_k(const GateFlatArgs& a, bool noisy, hipStream_t s) {
+  const bool masks = a.bits || (noisy && a.part) || a.imp_part;
+  return noisy ? launch_flat_n<T, K1, true>(a, masks, s) : launch_flat_n<T, K1, false>(a, masks, s);
 }
 
 template <typename T>
 static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
   const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
-  size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
-  if (a.bits || (noisy && a.part) || a.imp_part) sh += sizeof(uint32_t) * (size_t)a.E;
-  if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, sh, noisy, s);
-  if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, sh, noisy, s);
-  return launch_flat_k<T, 9>(a, sh, noisy, s);
+  if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, noisy, s);
+  if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, noisy, s);
+  return launch_flat_k<T, 9>(a, noisy, s);
 }
 
 bool gate_fuses_load(int E) { return E <= GATE_FUSED_LOAD_MAX_E; }
@@ -742,7 +830,7 @@ static hipError_t launch_group_k(const GateGroupArgs& a, int grid, size_t sh, hi
 
 template <typename T>
 static hipError_t launch_group_t(const GateGroupArgs& a, int grid, hipStream_t s) {
-  const size_t sh = xtile_bytes(sizeof(T) == 2, a.d);
+  const size_t sh = xtile_bytes(sizeof(T) == 2, a.d, GATE_ROWS) + sizeof(float) * GATE_ROWS * HLD;
   if (a.kpg + 1 <= 3) return launch_group_k<T, 3>(a, grid, sh, s);
   if (a.kpg + 1 <= 5) return launch_group_k<T, 5>(a, grid, sh, s);
   return launch_group_k<T, 9>(a, grid, sh, s);
@@ -794,22 +882,25 @@ hipError_t launch_pack_gate(const void* w_gate, const void* w_noise, int ng, int
 
 int load_partial_blocks(int64_t T) { return (int)((T + GATE_ROWS - 1) / GATE_ROWS); }
 
-template <typename T, bool XLDS>
-static hipError_t launch_load_v(const LoadArgs& a, int blocks, size_t sh, hipStream_t s) {
+template <typename T, bool XLDS, int RB>
+static hipError_t launch_load_v(const LoadArgs& a, size_t sh, hipStream_t s) {
   static size_t granted = 0;
-  hipError_t err = set_lds(load_partial_kernel<T, XLDS>, sh, &granted);
+  hipError_t err = set_lds(load_partial_kernel<T, XLDS, RB>, sh, &granted);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((load_partial_kernel<T, XLDS>), dim3(blocks), dim3(GATE_THREADS), sh, s, a);
+  constexpr int R = GateTile<RB>::R;
+  hipLaunchKernelGGL((load_partial_kernel<T, XLDS, RB>), dim3((unsigned)((a.T + R - 1) / R)),
+                     dim3(GATE_THREADS), sh, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_load_partial(const LoadArgs& a, bool bf16, hipStream_t s) {
-  const int blocks = load_partial_blocks(a.T);
-  if (blocks == 0) return hipSuccess;
-  const size_t sh = xtile_bytes(bf16, a.d) + sizeof(uint32_t) * (size_t)a.E;
-  if (!bf16) return launch_load_v<float, false>(a, blocks, sh, s);
-  return xtile_in_lds(true, a.d) ? launch_load_v<bf16_t, true>(a, blocks, sh, s)
-                                 : launch_load_v<bf16_t, false>(a, blocks, sh, s);
+  if (a.T == 0) return hipSuccess;
+  if (!bf16) return launch_load_v<float, false, 1>(a, load_lds(false, a.d, a.E, 1), s);
+  if (!xtile_in_lds(true, a.d))
+    return launch_load_v<bf16_t, false, 1>(a, load_lds(true, a.d, a.E, 1), s);
+  if (load_rb(true, a.d, a.E) == 2)
+    return launch_load_v<bf16_t, true, 2>(a, load_lds(true, a.d, a.E, 2), s);
+  return launch_load_v<bf16_t, true, 1>(a, load_lds(true, a.d, a.E, 1), s);
 }
 
 }  // namespace moe
