@@ -1,0 +1,271 @@
+"""Evidence that the oracle's pins have teeth: each case plants one plausible
+mistake in the oracle (a dropped term, a flipped sign, a wrong index or
+tie-break, a transposed operand, an off-by-one rank, a different variance) and
+checks that the pins named beside it fail on the planted oracle.  The mistakes
+live in this file only; the oracle itself is patched for the duration of one
+test and restored by pytest.  CPU only."""
+import importlib.util
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import oracle.moe_oracle as om
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_spec = importlib.util.spec_from_file_location("_oracle_pins", os.path.join(_HERE, "test_oracle_pins.py"))
+pins = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(pins)
+
+_orig = {name: getattr(om, name) for name in dir(om) if not name.startswith("__")}
+
+
+def _cases(fn):
+    """Argument tuples of a pin: one per parametrize value, else one empty."""
+    for mark in getattr(fn, "pytestmark", []):
+        if mark.name == "parametrize":
+            return [(v,) for v in mark.args[1]]
+    return [()]
+
+
+def _pin_fails(name):
+    fn = getattr(pins, name)
+    for args in _cases(fn):
+        try:
+            fn(*args)
+        except Exception:  # an assertion or a crash: either way the pin rejects it
+            return True
+    return False
+
+
+def _top_k_from_order(H, order, k):
+    """The remainder of KeepTopK once a descending order is chosen."""
+    T, E = H.shape
+    idx = np.sort(order[:, :k], axis=1).astype(np.int32)
+    rows = np.arange(T)
+    kth = H[rows, order[:, k - 1]] if T else np.zeros(0)
+    k1th = H[rows, order[:, k]] if (T and k < E) else np.full(T, -np.inf)
+    with np.errstate(invalid="ignore"):
+        return idx, kth, k1th, kth - k1th
+
+
+# ------------------------------------------------------------ mistakes ----
+
+def noise_term_dropped(x, w_gate, w_noise=None, bias=None, eps=None):
+    clean, sp, _ = _orig["noisy_logits"](x, w_gate, w_noise, bias, eps)
+    return clean, sp, clean.copy()
+
+
+def bias_dropped(x, w_gate, w_noise=None, bias=None, eps=None):
+    return _orig["noisy_logits"](x, w_gate, w_noise, None, eps)
+
+
+def noise_scale_from_clean_table(x, w_gate, w_noise=None, bias=None, eps=None):
+    return _orig["noisy_logits"](x, w_gate, w_gate if w_noise is not None else None, bias, eps)
+
+
+def softplus_sign_flipped(z):
+    z = np.asarray(z, dtype=np.float64)
+    return np.maximum(-z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def softplus_linear_part_dropped(z):
+    z = np.asarray(z, dtype=np.float64)
+    return np.log1p(np.exp(-np.abs(z)))
+
+
+def cdf_argument_sign_flipped(z):
+    return 0.5 * scipy.special.erfc(np.asarray(z, dtype=np.float64) / math.sqrt(2.0))
+
+
+def cdf_without_root_two(z):
+    return 0.5 * scipy.special.erfc(-np.asarray(z, dtype=np.float64))
+
+
+def silu_with_negated_sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z * (0.5 * (1.0 - np.tanh(0.5 * z)))
+
+
+def ties_to_higher_index(H, k):
+    H = np.asarray(H, dtype=np.float64)
+    E = H.shape[1]
+    order = E - 1 - np.argsort(-H[:, ::-1], axis=1, kind="stable")
+    return _top_k_from_order(H, order, k)
+
+
+def kth_and_k1th_swapped(H, k):
+    idx, kth, k1th, margin = _orig["keep_top_k"](H, k)
+    return idx, k1th, kth, margin
+
+
+def kept_in_score_order(H, k):
+    H = np.asarray(H, dtype=np.float64)
+    order = np.argsort(-H, axis=1, kind="stable")
+    idx, kth, k1th, margin = _top_k_from_order(H, order, k)
+    return order[:, :k].astype(np.int32), kth, k1th, margin
+
+
+def softmax_over_all_experts(H, idx):
+    H = np.asarray(H, dtype=np.float64)
+    if H.shape[0] == 0:
+        return np.zeros(idx.shape)
+    P = scipy.special.softmax(H, axis=1)
+    return np.take_along_axis(P, idx.astype(np.int64), axis=1)
+
+
+def route_tokens_descending(idx, n_experts):
+    T, k = idx.shape
+    counts, offsets, _, _ = _orig["route"](idx, n_experts)
+    fill = offsets[:-1].astype(np.int64).copy()
+    perm = np.zeros(T * k, dtype=np.int32)
+    inv = np.zeros(T * k, dtype=np.int32)
+    for t in reversed(range(T)):
+        for s in range(k):
+            p = fill[idx[t, s]]
+            fill[idx[t, s]] += 1
+            perm[p] = t * k + s
+            inv[t * k + s] = p
+    return counts, offsets, perm, inv
+
+
+def route_inclusive_offsets(idx, n_experts):
+    counts, offsets, perm, inv = _orig["route"](idx, n_experts)
+    return counts, np.append(offsets[1:], offsets[-1]).astype(np.int32), perm, inv
+
+
+def expert_without_relu(X, w1_e, w2_e):
+    X = om._f64(X)
+    return (X @ om._f64(w1_e).T) @ om._f64(w2_e).T
+
+
+def swiglu_gate_and_up_swapped(X, w1_e, w3_e, w2_e):
+    return _orig["expert_swiglu"](X, w3_e, w1_e, w2_e)
+
+
+def experts_fed_assignment_index(x, perm, offsets, k, w1, w2, w3=None):
+    """Rows gathered by assignment number t*k+s instead of token t."""
+    x = om._f64(x)
+    E = len(offsets) - 1
+    y = np.zeros((int(offsets[-1]), om._f64(w2[0]).shape[0]))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y[lo:hi] = om.expert_apply(x[np.asarray(perm[lo:hi]) % x.shape[0]], e, w1, w2, w3)
+    return y
+
+
+def combine_without_gates(y_sorted, inv, gates):
+    return _orig["combine"](y_sorted, inv, np.ones_like(np.asarray(gates, dtype=np.float64)))
+
+
+def combine_through_perm(y_sorted, inv, gates):
+    perm = np.argsort(np.asarray(inv))   # the inverse of inv, used where inv belongs
+    return _orig["combine"](y_sorted, perm, gates)
+
+
+def cv2_sample_variance(v):
+    v = np.asarray(v, dtype=np.float64)
+    if v.size < 2 or v.mean() == 0.0:
+        return 0.0
+    return float(v.var(ddof=1) / v.mean() ** 2)
+
+
+def cv2_not_squared_mean(v):
+    v = np.asarray(v, dtype=np.float64)
+    if v.size == 0 or v.mean() == 0.0:
+        return 0.0
+    return float(v.var() / abs(v.mean()))
+
+
+def importance_counts_rows(idx, gates, n_experts):
+    return _orig["importance"](idx, np.ones_like(gates), n_experts)
+
+
+def load_theta_swapped(clean, sp, H, idx, kth, k1th):
+    return _orig["load_estimate"](clean, sp, H, idx, k1th, kth)
+
+
+def load_without_noise_scale(clean, sp, H, idx, kth, k1th):
+    return _orig["load_estimate"](clean, np.ones_like(sp), H, idx, kth, k1th)
+
+
+def loss_weights_swapped(n_experts, idx, gates, counts, gate_info=None,
+                         w_importance=1.0, w_load=1.0):
+    return _orig["balance_stats"](n_experts, idx, gates, counts, gate_info, w_load, w_importance)
+
+
+def hier_primary_gate_only(x, w_gate_p, w_noise_p, eps_p, w_gate, w_noise, eps,
+                           n_groups, k_groups, k_per_group):
+    h = _orig["hier_gate"](x, w_gate_p, w_noise_p, eps_p, w_gate, w_noise, eps,
+                           n_groups, k_groups, k_per_group)
+    h["gates"] = np.repeat(h["primary"]["gates"], k_per_group, axis=1)
+    return h
+
+
+def hier_expert_index_transposed(x, w_gate_p, w_noise_p, eps_p, w_gate, w_noise, eps,
+                                 n_groups, k_groups, k_per_group):
+    """Global expert j*n_groups + g instead of g*Eg + j."""
+    h = _orig["hier_gate"](x, w_gate_p, w_noise_p, eps_p, w_gate, w_noise, eps,
+                           n_groups, k_groups, k_per_group)
+    Eg = om._f64(w_gate).shape[0] // n_groups
+    g, j = h["idx"] // Eg, h["idx"] % Eg
+    h["idx"] = (j * n_groups + g).astype(np.int32)
+    return h
+
+
+# (function patched, mistake, pins that must reject it)
+MUTATIONS = [
+    ("noisy_logits", noise_term_dropped, ["test_noisy_logits_hand_example"]),
+    ("noisy_logits", bias_dropped, ["test_noisy_logits_hand_example"]),
+    ("noisy_logits", noise_scale_from_clean_table, ["test_noisy_logits_hand_example"]),
+    ("softplus", softplus_sign_flipped, ["test_softplus_closed_forms", "test_noisy_logits_hand_example"]),
+    ("softplus", softplus_linear_part_dropped, ["test_softplus_closed_forms", "test_noisy_logits_hand_example"]),
+    ("normal_cdf", cdf_argument_sign_flipped, ["test_normal_cdf_closed_forms", "test_load_estimate_monte_carlo"]),
+    ("normal_cdf", cdf_without_root_two, ["test_normal_cdf_closed_forms", "test_load_two_experts_top1_closed_form"]),
+    ("silu", silu_with_negated_sigmoid, ["test_silu_closed_forms", "test_single_expert_swiglu_matches_torch"]),
+    ("keep_top_k", ties_to_higher_index, ["test_ties_prefer_lower_index",
+                                          "test_zero_tables_give_uniform_gates_and_lowest_index_ties"]),
+    ("keep_top_k", kth_and_k1th_swapped, ["test_top_k_equals_brute_force_best_subset",
+                                          "test_load_estimate_monte_carlo"]),
+    ("keep_top_k", kept_in_score_order, ["test_top_k_equals_brute_force_best_subset",
+                                         "test_gate_invariants_random"]),
+    ("kept_softmax", softmax_over_all_experts, ["test_worked_example_from_the_lesson_page",
+                                                "test_gate_invariants_random"]),
+    ("route", route_tokens_descending, ["test_route_hand_example", "test_route_invariants_random"]),
+    ("route", route_inclusive_offsets, ["test_route_hand_example", "test_route_invariants_random"]),
+    ("expert_relu", expert_without_relu, ["test_single_expert_is_a_plain_relu_ffn",
+                                          "test_dense_mixture_when_k_equals_E"]),
+    ("expert_swiglu", swiglu_gate_and_up_swapped, ["test_single_expert_swiglu_matches_torch"]),
+    ("run_experts", experts_fed_assignment_index, ["test_sparse_layer_equals_dense_brute_force",
+                                                   "test_dense_mixture_when_k_equals_E"]),
+    ("combine", combine_without_gates, ["test_combine_hand_example",
+                                        "test_sparse_layer_equals_dense_brute_force"]),
+    ("combine", combine_through_perm, ["test_combine_hand_example",
+                                       "test_sparse_layer_equals_dense_brute_force"]),
+    ("cv_squared", cv2_sample_variance, ["test_cv_squared_closed_forms"]),
+    ("cv_squared", cv2_not_squared_mean, ["test_cv_squared_closed_forms"]),
+    ("importance", importance_counts_rows, ["test_importance_sums_to_token_count"]),
+    ("load_estimate", load_theta_swapped, ["test_load_two_experts_top1_closed_form",
+                                           "test_load_estimate_monte_carlo"]),
+    ("load_estimate", load_without_noise_scale, ["test_load_two_experts_top1_closed_form"]),
+    ("balance_stats", loss_weights_swapped, ["test_balance_loss_weights"]),
+    ("hier_gate", hier_primary_gate_only, ["test_hierarchy_constructed_case",
+                                           "test_hierarchy_invariants_random"]),
+    ("hier_gate", hier_expert_index_transposed, ["test_hierarchy_constructed_case",
+                                                 "test_hierarchy_invariants_random"]),
+]
+
+
+@pytest.mark.parametrize("target,mistake,catchers", MUTATIONS,
+                         ids=[m[1].__name__ for m in MUTATIONS])
+def test_pins_reject_planted_mistake(monkeypatch, target, mistake, catchers):
+    for name in catchers:
+        assert not _pin_fails(name), f"{name} fails on the unplanted oracle"
+    monkeypatch.setattr(om, target, mistake)
+    monkeypatch.setattr(oracle, target, mistake)
+    missed = [name for name in catchers if not _pin_fails(name)]
+    assert not missed, f"planted {mistake.__name__} in {target} passes {missed}"
