@@ -10,4 +10,6 @@ from .moe_oracle import (cv_squared, combine, dense_forward, dense_gates,  # noq
                          hier_gate, importance, keep_top_k, kept_softmax,
                          load_estimate, noisy_logits, normal_cdf, route,
                          run_experts, silu, softplus, token_outputs,
-                         balance_stats)
+                         balance_stats, backward, cv_squared_grad, rank_experts,
+                         expert_relu_backward, expert_swiglu_backward, normal_pdf,
+                         sigmoid)

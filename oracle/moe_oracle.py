@@ -44,6 +44,12 @@ the design notes):
   * the SwiGLU expert is (silu(X W_gate) * (X W_up)) W_down, no biases.
   * parity unpinned: the hierarchical load (reported as hard counts per
     expert) has no page formula.
+  * backward pass (flat gate only): the objective is sum(dy * y) +
+    w_imp CV^2(Importance) + w_load CV^2(Load); the kept set and the experts
+    ranked k-th and (k+1)-th are held fixed (the choice itself has no
+    gradient), so the threshold theta of the smooth load passes its gradient
+    to the score of the expert it was read from; noise-free gating has a
+    hard load and no load gradient.
 
 Array layouts follow the library's: x [T][d]; w_gate, w_noise [E][d] (the
 pages' d x n table stored transposed); w1 [E][h][d]; w3 [E][h][d]; w2 [E][d][h].
@@ -421,3 +427,177 @@ def dense_forward(inp: Dict, cfg) -> np.ndarray:
     for e in range(cfg.n_experts):
         y += G[:, e:e + 1] * expert_apply(x, e, w1, w2, w3)
     return y
+
+
+# ---------------------------------------------------------------------------
+# Backward pass  [Reading note, sections 问题是什么 and 方法怎么做; Paper card,
+# sections 瓶颈 and 方法适配; Mixtral page, section 核心概念]
+#
+# The objective is L = sum(dy * y) + w_imp * CV^2(Importance) + w_load *
+# CV^2(Load): dy is the gradient that flows into the layer output from above,
+# and the two balance losses are added to the training objective with the
+# caller's weights.  The choice of the kept experts is a discrete step with no
+# gradient (the reading note's point that a hard choice is not
+# differentiable): the kept set, and which expert holds the k-th and (k+1)-th
+# score, are held fixed, and gradients flow through the softmax weights of the
+# kept scores, the noisy scores, the smooth load estimate and the experts.
+# Hidden activations are recomputed from the inputs (the paper card's
+# activation recomputation) rather than saved.
+# ---------------------------------------------------------------------------
+
+def sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * (1.0 + np.tanh(0.5 * z))
+
+
+def normal_pdf(z):
+    """phi(z) = exp(-z^2 / 2) / sqrt(2 pi), the derivative of Phi."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def cv_squared_grad(v) -> np.ndarray:
+    """Gradient of CV^2(v) = Var(v) / mean(v)^2 (population variance) with
+    respect to each v_i: 2 / (n m^2) * (v_i - m - Var / m); zero when the mean
+    is zero (where CV^2 is defined as 0)."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.size
+    if n == 0:
+        return np.zeros(0)
+    m = v.mean()
+    if m == 0.0:
+        return np.zeros(n)
+    var = ((v - m) ** 2).mean()
+    return 2.0 / (n * m * m) * (v - m - var / m)
+
+
+def rank_experts(H: np.ndarray, k: int):
+    """The experts ranked k-th and (k+1)-th by (score descending, index
+    ascending), the ones whose scores are the thresholds kth and k1th of
+    keep_top_k; -1 where there is no (k+1)-th (k == E)."""
+    H = np.asarray(H, dtype=np.float64)
+    T, E = H.shape
+    order = np.argsort(-H, axis=1, kind="stable")
+    jk = order[:, k - 1] if T else np.zeros(0, dtype=np.int64)
+    jk1 = order[:, k] if (T and k < E) else np.full(T, -1)
+    return jk, jk1
+
+
+def expert_relu_backward(X, w1_e, w2_e, dY):
+    """E(X) = max(X W1^T, 0) W2^T.  Returns dX, dW1 [h][d], dW2 [d][h]."""
+    X, w1_e, w2_e, dY = _f64(X), _f64(w1_e), _f64(w2_e), _f64(dY)
+    P = X @ w1_e.T
+    hid = np.maximum(P, 0.0)
+    dhid = dY @ w2_e
+    dP = dhid * (P > 0.0)
+    return dP @ w1_e, dP.T @ X, dY.T @ hid
+
+
+def expert_swiglu_backward(X, w1_e, w3_e, w2_e, dY):
+    """E(X) = (silu(X W1^T) * (X W3^T)) W2^T.  Returns dX, dW1, dW3, dW2.
+    silu'(a) = s (1 + a (1 - s)) with s = sigmoid(a)."""
+    X, w1_e, w3_e, w2_e, dY = _f64(X), _f64(w1_e), _f64(w3_e), _f64(w2_e), _f64(dY)
+    a = X @ w1_e.T
+    b = X @ w3_e.T
+    s = sigmoid(a)
+    hid = a * s * b
+    dhid = dY @ w2_e
+    da = dhid * b * s * (1.0 + a * (1.0 - s))
+    db = dhid * a * s
+    return da @ w1_e + db @ w3_e, da.T @ X, db.T @ X, dY.T @ hid
+
+
+def backward(inp: Dict, cfg, dy, w_importance=1.0, w_load=1.0) -> Dict:
+    """Gradients of L (see above) for the flat gate, ReLU or SwiGLU experts.
+
+    Returns dx [T][d], dw_gate [E][d], dw_noise [E][d] (None without noise),
+    dbias [E], dw1 [E][h][d], dw3 (SwiGLU, else None), dw2 [E][d][h], and the
+    intermediates dgate [T][k] (gradient of the kept gates) and dH [T][E]
+    (gradient of the noisy scores).
+    """
+    if cfg.n_groups:
+        raise NotImplementedError("the backward pass covers the flat gate")
+    x = _f64(inp["x"])
+    dy = _f64(dy)
+    fw = forward(inp, cfg, w_importance, w_load)
+    g = fw["gate_info"]
+    idx, gates, inv = fw["idx"], fw["gates"], fw["inv"]
+    T, k = idx.shape
+    E = cfg.n_experts
+    rows = np.arange(T)
+
+    # combine: y_t = sum_s gate[t,s] * y_sorted[inv[t,s]]
+    y_rows = fw["y_sorted"][inv.reshape(T, k)]            # [T][k][d]
+    dgate = np.einsum("tsd,td->ts", y_rows, dy) if T else np.zeros((0, k))
+    # importance: d Importance_e / d G[t,e] = 1 for every kept (t, e)
+    dgate = dgate + w_importance * cv_squared_grad(fw["importance"])[idx]
+    # softmax over the kept scores
+    dH_kept = gates * (dgate - (gates * dgate).sum(axis=1, keepdims=True))
+    dH = np.zeros((T, E))
+    for s in range(k):
+        dH[rows, idx[:, s]] += dH_kept[:, s]
+
+    clean, sp, H = g["clean"], g["sp"], g["H"]
+    dclean = np.zeros((T, E))
+    dsp = np.zeros((T, E))
+    if sp is not None:
+        # smooth load: Load_e = sum_t Phi(z), z = (clean - theta) / sp, theta the
+        # k-th largest score among the other experts, the score of the expert
+        # ranked k+1 when e is kept and of the one ranked k otherwise
+        kept = np.zeros((T, E), dtype=bool)
+        for s in range(k):
+            kept[rows, idx[:, s]] = True
+        jk, jk1 = rank_experts(H, k)
+        theta = np.where(kept, g["k1th"][:, None], g["kth"][:, None])
+        with np.errstate(invalid="ignore"):
+            z = (clean - theta) / sp
+        dload = w_load * cv_squared_grad(fw["load"])
+        dz = dload[None, :] * np.where(np.isfinite(z), normal_pdf(np.where(np.isfinite(z), z, 0.0)), 0.0)
+        zf = np.where(np.isfinite(z), z, 0.0)
+        dclean += dz / sp
+        dsp += -dz * zf / sp
+        dtheta = -dz / sp
+        dH[rows, jk] += np.where(kept, 0.0, dtheta).sum(axis=1)
+        has_k1 = jk1 >= 0
+        dH[rows[has_k1], jk1[has_k1]] += np.where(kept, dtheta, 0.0).sum(axis=1)[has_k1]
+        # H = clean + eps * sp
+        dclean += dH
+        dsp += dH * _f64(inp["eps"])
+        raw = x @ _f64(inp["w_noise"]).T
+        draw = dsp * sigmoid(raw)
+    else:
+        dclean += dH
+        draw = None
+
+    # clean = x W_g^T + bias, raw = x W_noise^T
+    dw_gate = dclean.T @ x
+    dw_noise = draw.T @ x if draw is not None else None
+    dbias = dclean.sum(axis=0)
+    dx = dclean @ _f64(inp["w_gate"])
+    if draw is not None:
+        dx = dx + draw @ _f64(inp["w_noise"])
+
+    # experts: the rows of expert e are the tokens perm[p] // k, and the
+    # gradient flowing into row p is gate[t,s] * dy[t]
+    w1, w2 = _f64(inp["w1"]), _f64(inp["w2"])
+    w3 = _f64(inp.get("w3"))
+    perm, offsets = fw["perm"], fw["offsets"]
+    dw1 = np.zeros_like(w1)
+    dw2 = np.zeros_like(w2)
+    dw3 = np.zeros_like(w3) if w3 is not None else None
+    flat_gates = gates.reshape(-1)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        a = perm[lo:hi]
+        toks = a // k
+        X = x[toks]
+        dY = flat_gates[a][:, None] * dy[toks]
+        if w3 is None:
+            dX, dw1[e], dw2[e] = expert_relu_backward(X, w1[e], w2[e], dY)
+        else:
+            dX, dw1[e], dw3[e], dw2[e] = expert_swiglu_backward(X, w1[e], w3[e], w2[e], dY)
+        np.add.at(dx, toks, dX)
+    return dict(dx=dx, dw_gate=dw_gate, dw_noise=dw_noise, dbias=dbias, dw1=dw1,
+                dw3=dw3, dw2=dw2, dgate=dgate, dH=dH, forward=fw)

@@ -29,7 +29,7 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-__all__ = ["MoEConfig", "CONFIGS", "make_inputs", "stream_seed"]
+__all__ = ["MoEConfig", "CONFIGS", "make_inputs", "make_upstream", "stream_seed"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -190,3 +190,10 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu",
                      if cfg.ffn == "swiglu" else None)
         out["w2"] = _expert_table(E, d, h, s2, device, seed, "w2", dt)
     return out
+
+
+def make_upstream(cfg: MoEConfig, seed: int = 0, device="cpu") -> torch.Tensor:
+    """The gradient flowing into the layer output from above, dy [T][d] ~ N(0,1)
+    in the layer's dtype, for the backward pass."""
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    return _normal((cfg.tokens, cfg.d_model), 1.0, device, seed, "dy", dt)

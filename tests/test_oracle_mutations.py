@@ -16,9 +16,17 @@ import oracle
 import oracle.moe_oracle as om
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_spec = importlib.util.spec_from_file_location("_oracle_pins", os.path.join(_HERE, "test_oracle_pins.py"))
-pins = importlib.util.module_from_spec(_spec)
-_spec.loader.exec_module(pins)
+
+
+def _load(name):
+    spec = importlib.util.spec_from_file_location("_" + name, os.path.join(_HERE, name + ".py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+pins = _load("test_oracle_pins")
+bpins = _load("test_oracle_backward_pins")
 
 _orig = {name: getattr(om, name) for name in dir(om) if not name.startswith("__")}
 
@@ -32,7 +40,7 @@ def _cases(fn):
 
 
 def _pin_fails(name):
-    fn = getattr(pins, name)
+    fn = getattr(pins, name, None) or getattr(bpins, name)
     for args in _cases(fn):
         try:
             fn(*args)
@@ -217,6 +225,49 @@ def hier_expert_index_transposed(x, w_gate_p, w_noise_p, eps_p, w_gate, w_noise,
     return h
 
 
+def cv2_grad_without_mean_term(v):
+    v = np.asarray(v, dtype=np.float64)
+    if v.size == 0 or v.mean() == 0.0:
+        return np.zeros(v.size)
+    m = v.mean()
+    return 2.0 / (v.size * m * m) * (v - m)
+
+
+def pdf_without_normalisation(z):
+    z = np.asarray(z, dtype=np.float64)
+    return np.exp(-0.5 * z * z)
+
+
+def rank_k_and_k1_swapped(H, k):
+    jk, jk1 = _orig["rank_experts"](H, k)
+    return np.where(jk1 >= 0, jk1, jk), np.where(jk1 >= 0, jk, -1)
+
+
+def relu_backward_weights_from_pre_activation(X, w1_e, w2_e, dY):
+    dX, dW1, _ = _orig["expert_relu_backward"](X, w1_e, w2_e, dY)
+    X, w1_e, dY = om._f64(X), om._f64(w1_e), om._f64(dY)
+    return dX, dW1, dY.T @ (X @ w1_e.T)
+
+
+def relu_backward_without_mask(X, w1_e, w2_e, dY):
+    X, w1_e, w2_e, dY = om._f64(X), om._f64(w1_e), om._f64(w2_e), om._f64(dY)
+    dP = dY @ w2_e
+    return dP @ w1_e, dP.T @ X, dY.T @ np.maximum(X @ w1_e.T, 0.0)
+
+
+def swiglu_backward_sigmoid_as_silu_derivative(X, w1_e, w3_e, w2_e, dY):
+    X, w1_e, w3_e, w2_e, dY = (om._f64(a) for a in (X, w1_e, w3_e, w2_e, dY))
+    a, b = X @ w1_e.T, X @ w3_e.T
+    s = om.sigmoid(a)
+    dhid = dY @ w2_e
+    da, db = dhid * b * s, dhid * a * s
+    return da @ w1_e + db @ w3_e, da.T @ X, db.T @ X, dY.T @ (a * s * b)
+
+
+def noise_scale_slope_one(z):
+    return np.ones_like(np.asarray(z, dtype=np.float64))
+
+
 # (function patched, mistake, pins that must reject it)
 MUTATIONS = [
     ("noisy_logits", noise_term_dropped, ["test_noisy_logits_hand_example"]),
@@ -257,6 +308,26 @@ MUTATIONS = [
                                            "test_hierarchy_invariants_random"]),
     ("hier_gate", hier_expert_index_transposed, ["test_hierarchy_constructed_case",
                                                  "test_hierarchy_invariants_random"]),
+    # backward
+    ("cv_squared_grad", cv2_grad_without_mean_term, ["test_cv_squared_gradient_closed_forms",
+                                                     "test_gradients_match_central_differences"]),
+    ("normal_pdf", pdf_without_normalisation, ["test_normal_pdf_and_sigmoid_closed_forms",
+                                               "test_gradients_match_central_differences"]),
+    ("rank_experts", rank_k_and_k1_swapped, ["test_rank_experts_follow_the_tie_break",
+                                             "test_gradients_match_central_differences"]),
+    ("expert_relu_backward", relu_backward_weights_from_pre_activation,
+     ["test_single_expert_backward_matches_torch_autograd",
+      "test_expert_backward_matches_torch_on_random_rows",
+      "test_gradients_match_central_differences"]),
+    ("expert_relu_backward", relu_backward_without_mask,
+     ["test_single_expert_backward_matches_torch_autograd",
+      "test_dense_mixture_backward_matches_torch_autograd"]),
+    ("expert_swiglu_backward", swiglu_backward_sigmoid_as_silu_derivative,
+     ["test_single_expert_backward_matches_torch_autograd",
+      "test_expert_backward_matches_torch_on_random_rows",
+      "test_gradients_match_central_differences"]),
+    ("sigmoid", noise_scale_slope_one, ["test_normal_pdf_and_sigmoid_closed_forms",
+                                        "test_gradients_match_central_differences"]),
 ]
 
 
