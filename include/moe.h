@@ -1,6 +1,7 @@
 /*
- * moe.h -- C ABI of libmoe, the forward pass of the sparsely-gated noisy
- * top-k Mixture-of-Experts layer on one AMD Instinct MI355X (gfx950).
+ * moe.h -- C ABI of libmoe, the forward and backward passes of the
+ * sparsely-gated noisy top-k Mixture-of-Experts layer on one AMD Instinct
+ * MI355X (gfx950).
  *
  * The layer, as the pages on Shazeer et al. 2017 describe it:
  *   - "MoE:稀疏门控混合专家" (nengyongai.cn), section 二: one MoE layer is
@@ -227,7 +228,8 @@ moe_status moe_balance_loss(const moe_config* cfg, const void* x,
                             void* stream);
 
 /* Outputs of moe_forward.  y is required; the rest are nullable (the
- * library then keeps them in the workspace). */
+ * library then keeps them in the workspace).  The last five are what
+ * moe_backward reads back (see moe_saved). */
 typedef struct moe_outputs {
   void* y;            /* [T][d] */
   int32_t* topk_idx;  /* [T][k] */
@@ -236,6 +238,11 @@ typedef struct moe_outputs {
   float* importance;  /* [E]; balance statistics are computed only when */
   float* load;        /* [E]; `balance` is non-NULL */
   float* balance;     /* [3]: cv2 importance, cv2 load, weighted loss */
+  float* thr;         /* [T][2] flat gate: k-th and (k+1)-th noisy score */
+  int32_t* offsets;   /* [E+1] routing offsets */
+  int32_t* perm;      /* [A] routing permutation */
+  int32_t* inv;       /* [A] its inverse */
+  void* y_sorted;     /* [A][d] expert outputs in routed order */
 } moe_outputs;
 
 /* The whole layer: gate -> route -> experts -> combine (-> balance). */
@@ -243,6 +250,64 @@ moe_status moe_forward(const moe_config* cfg, const void* x,
                        const moe_params* p, const moe_noise* noise,
                        float w_importance, float w_load, moe_outputs* out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Backward pass -------------------------------------------------------
+ * Gradients of L = sum(dy * y) + w_importance * CV^2(importance) +
+ * w_load * CV^2(load) for the flat gate (n_groups == 0), ReLU or SwiGLU
+ * experts, bf16 or fp32.  dy is the gradient flowing into y from above; the
+ * balance losses are those moe_balance_loss defines, added to the objective
+ * with the given weights.  The choice of kept experts has no gradient (the
+ * reading note "Outrageously Large Neural Networks — MoE 怎样让模型“很大但
+ * 不每次全算”", section 问题是什么): the kept set and the experts ranked k-th
+ * and (k+1)-th are held fixed, and gradients flow through the softmax over the
+ * kept scores, the noisy scores (section 方法怎么做: the learnable noise), the
+ * smooth load estimate (whose threshold passes its gradient to the score it
+ * was read from) and the experts.  Hidden activations are recomputed, not
+ * saved (paper card, section 瓶颈: activation recomputation).
+ *
+ * Tensors saved from the forward pass of the same inputs (moe_forward with
+ * the matching moe_outputs fields, or the staged calls). */
+typedef struct moe_saved {
+  const int32_t* topk_idx;  /* [T][k] */
+  const float* topk_gate;   /* [T][k] */
+  const float* thr;         /* [T][2]; needed when noisy and w_load != 0 */
+  const int32_t* offsets;   /* [E+1] */
+  const int32_t* perm;      /* [A] */
+  const int32_t* inv;       /* [A] */
+  const void* y_sorted;     /* [A][d] */
+  const float* importance;  /* [E]; needed when w_importance != 0 */
+  const float* load;        /* [E]; needed when noisy and w_load != 0 */
+} moe_saved;
+
+/* Gradient outputs.  dx is required; the others are nullable (not
+ * computed).  Element type: cfg dtype, except dbias (float32).  Experts
+ * that receive no rows get zero table gradients. */
+typedef struct moe_grads {
+  void* dx;        /* [T][d] */
+  void* dw_gate;   /* [E][d] */
+  void* dw_noise;  /* [E][d] (noisy only) */
+  float* dbias;    /* [E] */
+  void* dw1;       /* [E][h][d] */
+  void* dw3;       /* [E][h][d] (SwiGLU only) */
+  void* dw2;       /* [E][d][h] */
+} moe_grads;
+
+/* Bytes of workspace moe_backward needs for this configuration (0 when the
+ * configuration has no backward pass: the hierarchy). */
+size_t moe_backward_workspace_size(const moe_config* cfg);
+
+/* The backward pass.  x, p (w_gate, w_noise, bias, w1, w2, w3; packed tables
+ * are optional for the gate and not used for the experts, whose unpacked
+ * w1 / w2 / w3 are required), noise (eps, when noisy) and `saved` are the
+ * forward's inputs and saved tensors; dy [T][d] is in the cfg dtype.
+ * Returns MOE_ERR_UNSUPPORTED for the hierarchy.  bf16: products on MFMA
+ * with fp32 accumulation; fp32 operands (score gradients) and gate-scaled
+ * output gradients are rounded to bf16 as they enter a product, the hidden
+ * activation and its gradients are rounded to bf16 between products. */
+moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* p,
+                        const moe_noise* noise, const moe_saved* saved, const void* dy,
+                        float w_importance, float w_load, moe_grads* grads, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(int status);

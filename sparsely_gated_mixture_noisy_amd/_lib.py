@@ -56,7 +56,19 @@ class moe_noise(ctypes.Structure):
 
 class moe_outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("y", "topk_idx", "topk_gate", "counts", "importance", "load", "balance")]
+                ("y", "topk_idx", "topk_gate", "counts", "importance", "load", "balance",
+                 "thr", "offsets", "perm", "inv", "y_sorted")]
+
+
+class moe_saved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_gate", "thr", "offsets", "perm", "inv", "y_sorted",
+                 "importance", "load")]
+
+
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw3", "dw2")]
 
 
 _P = ctypes.c_void_p
@@ -81,6 +93,11 @@ _SIGS = {
     "moe_packed_gate_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config)]),
     "moe_pack_gate": (ctypes.c_int, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_params),
                                      _P, _P]),
+    "moe_backward_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config)]),
+    "moe_backward": (ctypes.c_int, [ctypes.POINTER(moe_config), _P, ctypes.POINTER(moe_params),
+                                    ctypes.POINTER(moe_noise), ctypes.POINTER(moe_saved), _P,
+                                    ctypes.c_float, ctypes.c_float, ctypes.POINTER(moe_grads), _P,
+                                    ctypes.c_size_t, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -280,9 +297,10 @@ def balance_loss(cfg: MoEConfig, x, params, idx, gates, thr, perm, offsets, w_im
 
 
 class ForwardOut:
-    """Output tensors of one moe_forward call."""
+    """Output tensors of one moe_forward call; with save=True also the tensors
+    the backward pass reads (thresholds, routing, expert outputs)."""
 
-    def __init__(self, cfg: MoEConfig, T: int, device, balance: bool):
+    def __init__(self, cfg: MoEConfig, T: int, device, balance: bool, save: bool = False):
         self.y = torch.empty((T, cfg.d_model), dtype=_act_dtype(cfg), device=device)
         self.topk_idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=device)
         self.topk_gate = torch.empty((T, cfg.top_k), dtype=torch.float32, device=device)
@@ -292,12 +310,31 @@ class ForwardOut:
         self.load = (torch.empty(cfg.n_experts, dtype=torch.float32, device=device)
                      if balance else None)
         self.balance = torch.empty(3, dtype=torch.float32, device=device) if balance else None
+        A = T * cfg.top_k
+        flat = not cfg.hierarchical
+        self.thr = (torch.empty((T, 2), dtype=torch.float32, device=device)
+                    if save and flat else None)
+        self.offsets = (torch.empty(cfg.n_experts + 1, dtype=torch.int32, device=device)
+                        if save else None)
+        self.perm = torch.empty(A, dtype=torch.int32, device=device) if save else None
+        self.inv = torch.empty(A, dtype=torch.int32, device=device) if save else None
+        self.y_sorted = (torch.empty((A, cfg.d_model), dtype=_act_dtype(cfg), device=device)
+                         if save else None)
 
     def struct(self) -> moe_outputs:
         return moe_outputs(y=_ptr(self.y), topk_idx=_ptr(self.topk_idx),
                            topk_gate=_ptr(self.topk_gate), counts=_ptr(self.counts),
                            importance=_ptr(self.importance), load=_ptr(self.load),
-                           balance=_ptr(self.balance))
+                           balance=_ptr(self.balance), thr=_ptr(self.thr),
+                           offsets=_ptr(self.offsets), perm=_ptr(self.perm), inv=_ptr(self.inv),
+                           y_sorted=_ptr(self.y_sorted))
+
+    def saved(self) -> moe_saved:
+        """The moe_saved view of these outputs (needs save=True)."""
+        return moe_saved(topk_idx=_ptr(self.topk_idx), topk_gate=_ptr(self.topk_gate),
+                         thr=_ptr(self.thr), offsets=_ptr(self.offsets), perm=_ptr(self.perm),
+                         inv=_ptr(self.inv), y_sorted=_ptr(self.y_sorted),
+                         importance=_ptr(self.importance), load=_ptr(self.load))
 
 
 class Forward:
@@ -305,12 +342,13 @@ class Forward:
     repeated calls (benchmarks, graph capture) only cross into the library."""
 
     def __init__(self, cfg: MoEConfig, x, params, noise, w_importance=1.0, w_load=1.0,
-                 balance=True, ws: Optional[Workspace] = None, out: Optional[ForwardOut] = None):
+                 balance=True, ws: Optional[Workspace] = None, out: Optional[ForwardOut] = None,
+                 save: bool = False):
         T = x.shape[0]
         self.cfg = cfg
         self._keep = (x, params, noise)
         self.ws = ws or workspace(cfg, T, x.device)
-        self.out = out or ForwardOut(cfg, T, x.device, balance)
+        self.out = out or ForwardOut(cfg, T, x.device, balance, save)
         self._c = make_config(cfg, T)
         self._p = make_params(params)
         self._n = make_noise(noise)
@@ -327,5 +365,62 @@ class Forward:
 
 
 def forward(cfg: MoEConfig, x, params, noise, w_importance=1.0, w_load=1.0, balance=True,
-            ws: Optional[Workspace] = None) -> ForwardOut:
-    return Forward(cfg, x, params, noise, w_importance, w_load, balance, ws)()
+            ws: Optional[Workspace] = None, save: bool = False) -> ForwardOut:
+    return Forward(cfg, x, params, noise, w_importance, w_load, balance, ws, save=save)()
+
+
+def backward_workspace_size(cfg: MoEConfig, tokens: Optional[int] = None) -> int:
+    c = make_config(cfg, tokens)
+    return int(load().moe_backward_workspace_size(ctypes.byref(c)))
+
+
+class Grads:
+    """Gradient tensors of one moe_backward call."""
+
+    def __init__(self, cfg: MoEConfig, T: int, device, tables: bool = True):
+        dt = _act_dtype(cfg)
+        E, d, h = cfg.n_experts, cfg.d_model, cfg.d_hidden
+        self.dx = torch.empty((T, d), dtype=dt, device=device)
+        self.dw_gate = torch.empty((E, d), dtype=dt, device=device) if tables else None
+        self.dw_noise = (torch.empty((E, d), dtype=dt, device=device)
+                         if tables and cfg.noisy else None)
+        self.dbias = torch.empty(E, dtype=torch.float32, device=device) if tables else None
+        self.dw1 = torch.empty((E, h, d), dtype=dt, device=device) if tables else None
+        self.dw3 = (torch.empty((E, h, d), dtype=dt, device=device)
+                    if tables and cfg.ffn == "swiglu" else None)
+        self.dw2 = torch.empty((E, d, h), dtype=dt, device=device) if tables else None
+
+    def struct(self) -> moe_grads:
+        return moe_grads(**{n: _ptr(getattr(self, n)) for n, _ in moe_grads._fields_})
+
+
+class Backward:
+    """A prepared moe_backward call for the tensors a saving forward produced."""
+
+    def __init__(self, cfg: MoEConfig, x, params, noise, fwd: ForwardOut, dy,
+                 w_importance=1.0, w_load=1.0, ws: Optional[Workspace] = None,
+                 grads: Optional[Grads] = None):
+        T = x.shape[0]
+        self._keep = (x, params, noise, fwd, dy)
+        self.ws = ws or Workspace(backward_workspace_size(cfg, T), x.device)
+        self.grads = grads or Grads(cfg, T, x.device)
+        self._c = make_config(cfg, T)
+        self._p = make_params(params)
+        self._n = make_noise(noise)
+        self._s = fwd.saved()
+        self._g = self.grads.struct()
+        self._x, self._dy = _ptr(x), _ptr(dy)
+        self._wi, self._wl = float(w_importance), float(w_load)
+        self._fn = load().moe_backward
+
+    def __call__(self) -> Grads:
+        _check(self._fn(ctypes.byref(self._c), self._x, ctypes.byref(self._p),
+                        ctypes.byref(self._n), ctypes.byref(self._s), self._dy, self._wi,
+                        self._wl, ctypes.byref(self._g), self.ws.ptr, self.ws.nbytes, _stream()),
+               "moe_backward")
+        return self.grads
+
+
+def backward(cfg: MoEConfig, x, params, noise, fwd: ForwardOut, dy, w_importance=1.0,
+             w_load=1.0, ws: Optional[Workspace] = None) -> Grads:
+    return Backward(cfg, x, params, noise, fwd, dy, w_importance, w_load, ws)()

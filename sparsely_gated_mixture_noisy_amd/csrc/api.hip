@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/moe.h"
@@ -422,6 +423,280 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
   return hip_status(launch_balance(b, s), "balance");
 }
 
+
+// ---- backward layout and launch order ----------------------------------------
+
+struct BwLayout {
+  size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, hid, dp, db, dxs, part_g,
+      part_n;
+  size_t total;
+  int nblk, nchunk;
+  int64_t kchunk;
+};
+
+BwLayout bw_layout(const moe_config* c) {
+  BwLayout L;
+  const int64_t T = c->tokens, A = T * c->top_k;
+  const int E = c->n_experts, d = c->d_model, h = c->d_hidden;
+  const size_t es = elem_size(c);
+  const bool sw = c->ffn == MOE_FFN_SWIGLU;
+  L.nblk = (int)((T + 31) / 32);
+  // gate-table products: K = tokens split into chunks, enough workgroups
+  const int64_t tiles_mn = ((E + 127) / 128) * (int64_t)((d + 127) / 128);
+  int64_t nch = (1024 + tiles_mn - 1) / tiles_mn;
+  nch = std::min<int64_t>(nch, std::max<int64_t>(1, (T + 255) / 256));
+  nch = std::max<int64_t>(nch, 1);
+  int64_t kc = (T + nch - 1) / nch;
+  kc = std::max<int64_t>(32, (kc + 31) / 32 * 32);
+  L.kchunk = kc;
+  L.nchunk = (int)std::max<int64_t>(1, (T + kc - 1) / kc);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.dimp = take(4 * (size_t)E);
+  L.dload = take(4 * (size_t)E);
+  L.dhk = take(4 * (size_t)A);
+  L.rinfo = take(16 * (size_t)T);
+  L.dclean = take(4 * (size_t)T * E);
+  L.draw = take(c->noisy ? 4 * (size_t)T * E : 0);
+  L.dbias_part = take(4 * (size_t)L.nblk * E);
+  L.dxg = take(4 * (size_t)T * d);
+  L.tiles = take(4 * (size_t)(E + 1));
+  L.hid = take(es * (size_t)A * h);
+  L.dp = take(es * (size_t)A * h);
+  L.db = take(sw ? es * (size_t)A * h : 0);
+  L.dxs = take(4 * (size_t)A * d);
+  L.part_g = take(4 * (size_t)L.nchunk * E * d);
+  L.part_n = take(c->noisy ? 4 * (size_t)L.nchunk * E * d : 0);
+  L.total = o;
+  return L;
+}
+
+BwOp op_rows(const void* ptr, int64_t ld, bool f32, const int32_t* gather = nullptr, int gk = 1,
+             const float* scale = nullptr) {
+  BwOp o;
+  o.p = ptr;
+  o.ld = ld;
+  o.f32 = f32 ? 1 : 0;
+  o.kmajor = 1;
+  o.gather = gather;
+  o.gk = gk;
+  o.scale = scale;
+  return o;
+}
+
+BwOp op_cols(const void* ptr, int64_t ld, bool f32, const int32_t* gather = nullptr, int gk = 1,
+             const float* scale = nullptr) {
+  BwOp o = op_rows(ptr, ld, f32, gather, gk, scale);
+  o.kmajor = 0;
+  return o;
+}
+
+BwOp per_expert(BwOp o, int64_t estride) {
+  o.estride = estride;
+  return o;
+}
+
+BwOp low_half(BwOp o) {
+  o.lo = 1;
+  return o;
+}
+
+void add_pair(BwGemm& q, const BwOp& a, const BwOp& b) {
+  q.sa[q.nextra] = a;
+  q.sb[q.nextra] = b;
+  ++q.nextra;
+}
+
+moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, const moe_params* p,
+                       const moe_noise* n, const moe_saved* sv, const void* dy, float wi,
+                       float wl, moe_grads* g, void* ws, hipStream_t s) {
+  const int64_t T = c->tokens, A = T * c->top_k;
+  const int E = c->n_experts, d = c->d_model, h = c->d_hidden, k = c->top_k;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool f32 = !bf16;
+  const bool noisy = c->noisy != 0;
+  const bool sw = c->ffn == MOE_FFN_SWIGLU;
+  float* dimp = at<float>(ws, L.dimp);
+  float* dload = at<float>(ws, L.dload);
+  // 1. CV^2 gradients of the two balance losses
+  const bool use_imp = wi != 0.f && T > 0;
+  const bool smooth = noisy && wl != 0.f && T > 0;
+  MOE_TRY(hip_status(launch_bw_cv2_grad(use_imp ? sv->importance : nullptr,
+                                        smooth ? sv->load : nullptr, E, wi, wl, dimp, dload, s),
+                     "backward cv2"));
+  // 2. kept-gate gradients through the combine and the importance loss
+  float* dhk = at<float>(ws, L.dhk);
+  if (T > 0) {
+    BwGateOutArgs go;
+    go.y_sorted = sv->y_sorted;
+    go.inv = sv->inv;
+    go.idx = sv->topk_idx;
+    go.gate = sv->topk_gate;
+    go.dy = dy;
+    go.dimp = use_imp ? dimp : nullptr;
+    go.T = T;
+    go.k = k;
+    go.d = d;
+    go.dhk = dhk;
+    MOE_TRY(hip_status(launch_bw_gate_out(go, bf16, s), "backward gate outputs"));
+  }
+  // 3. score gradients per (token, expert)
+  float* dclean = at<float>(ws, L.dclean);
+  float* draw = noisy ? at<float>(ws, L.draw) : nullptr;
+  float* dbias_part = at<float>(ws, L.dbias_part);
+  BwGateArgs ga;
+  ga.x = x;
+  ga.w_gate = p->w_gate;
+  ga.w_noise = noisy ? p->w_noise : nullptr;
+  ga.bias = p->bias;
+  ga.eps = noisy && n ? n->eps : nullptr;
+  ga.w_pack = p->w_gate_packed;
+  ga.pack_nt = gate_pack_tables(c);
+  ga.idx = sv->topk_idx;
+  ga.thr = smooth ? sv->thr : nullptr;
+  ga.dload = smooth ? dload : nullptr;
+  ga.dhk = dhk;
+  ga.T = T;
+  ga.d = d;
+  ga.E = E;
+  ga.k = k;
+  ga.rinfo = at<int32_t>(ws, L.rinfo);
+  ga.dclean = dclean;
+  ga.draw = draw;
+  ga.dbias_part = dbias_part;
+  MOE_TRY(hip_status(launch_bw_gate(ga, bf16, s), "backward gate"));
+  if (g->dbias)
+    MOE_TRY(hip_status(launch_bw_sum_rows(dbias_part, L.nblk, E, g->dbias, s), "backward dbias"));
+  // 4. gate-table products
+  float* dxg = at<float>(ws, L.dxg);
+  if (T > 0) {
+    BwGemm q;
+    q.mode = BW_PLAIN;
+    q.a = op_rows(dclean, E, true);
+    q.b = op_cols(p->w_gate, d, f32);
+    // bf16 products carry the fp32 score gradients as hi + lo halves
+    if (bf16) add_pair(q, low_half(q.a), q.b);
+    if (noisy) {
+      add_pair(q, op_rows(draw, E, true), op_cols(p->w_noise, d, f32));
+      if (bf16) add_pair(q, low_half(op_rows(draw, E, true)), op_cols(p->w_noise, d, f32));
+    }
+    q.M = T;
+    q.N = d;
+    q.K = E;
+    q.kchunk = E;
+    q.C = dxg;
+    q.c_f32 = 1;
+    q.ldc = d;
+    const int64_t grid = ((T + 127) / 128) * ((d + 127) / 128);
+    MOE_TRY(hip_status(launch_bw_gemm(q, bf16, grid, s), "backward dx gate"));
+  }
+  for (int tab = 0; tab < 2; ++tab) {
+    void* out = tab == 0 ? g->dw_gate : g->dw_noise;
+    if (!out) continue;
+    float* part = at<float>(ws, tab == 0 ? L.part_g : L.part_n);
+    BwGemm q;
+    q.mode = BW_PLAIN;
+    q.a = op_cols(tab == 0 ? dclean : draw, E, true);
+    q.b = op_cols(x, d, f32);
+    if (bf16) add_pair(q, low_half(q.a), q.b);
+    q.M = E;
+    q.N = d;
+    q.K = T;
+    q.kchunk = L.kchunk;
+    q.C = part;
+    q.c_f32 = 1;
+    q.ldc = d;
+    q.c_chunk = (int64_t)E * d;
+    const int64_t grid = (int64_t)L.nchunk * ((E + 127) / 128) * ((d + 127) / 128);
+    MOE_TRY(hip_status(launch_bw_gemm(q, bf16, grid, s), "backward gate tables"));
+    MOE_TRY(hip_status(launch_bw_sum_chunks(part, L.nchunk, (int64_t)E * d, bf16, out, s),
+                       "backward gate table sum"));
+  }
+  // 5. experts
+  void* hid = at<void>(ws, L.hid);
+  void* dp = at<void>(ws, L.dp);
+  void* db = sw ? at<void>(ws, L.db) : nullptr;
+  float* dxs = at<float>(ws, L.dxs);
+  const int64_t hd = (int64_t)h * d;
+  if (A > 0) {
+    int32_t* tiles = at<int32_t>(ws, L.tiles);
+    MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, s),
+                       "backward tiles"));
+    const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
+    // hidden layer recomputed with its gradient
+    BwGemm q;
+    q.mode = BW_POS;
+    q.epi = sw ? BW_EPI_SWIGLU : BW_EPI_RELU;
+    q.a = op_rows(x, d, f32, sv->perm, k);
+    q.b = per_expert(op_rows(p->w1, d, f32), hd);
+    q.a1 = op_rows(dy, d, f32, sv->perm, k, sv->topk_gate);
+    q.b1 = per_expert(op_cols(p->w2, h, f32), hd);
+    if (sw) q.b3 = per_expert(op_rows(p->w3, d, f32), hd);
+    q.M = A;
+    q.N = h;
+    q.K = d;
+    q.offsets = sv->offsets;
+    q.tiles = tiles;
+    q.E = E;
+    q.C = hid;
+    q.C2 = dp;
+    q.C3 = db;
+    MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
+                       "backward hidden"));
+    // dX = dP W1 (+ dB W3), per routed row
+    BwGemm r;
+    r.mode = BW_POS;
+    r.a = op_rows(dp, h, f32);
+    r.b = per_expert(op_cols(p->w1, d, f32), hd);
+    if (sw) add_pair(r, op_rows(db, h, f32), per_expert(op_cols(p->w3, d, f32), hd));
+    r.M = A;
+    r.N = d;
+    r.K = h;
+    r.offsets = sv->offsets;
+    r.tiles = tiles;
+    r.E = E;
+    r.C = dxs;
+    r.c_f32 = 1;
+    r.ldc = d;
+    MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((d + 127) / 128), s),
+                       "backward expert dx"));
+  }
+  // table gradients, one problem per expert over its rows (zero without rows)
+  auto wgrad = [&](void* out, BwOp a, BwOp b, int64_t M, int64_t N, const char* what) {
+    if (!out) return MOE_OK;
+    BwGemm q;
+    q.mode = BW_WGT;
+    q.a = a;
+    q.b = b;
+    q.M = M;
+    q.N = N;
+    q.offsets = sv->offsets;
+    q.E = E;
+    q.C = out;
+    q.c_f32 = f32 ? 1 : 0;
+    q.ldc = N;
+    q.c_estride = M * N;
+    const int64_t grid = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
+    return hip_status(launch_bw_gemm(q, bf16, grid, s), what);
+  };
+  MOE_TRY(wgrad(g->dw1, op_cols(dp, h, f32), op_cols(x, d, f32, sv->perm, k), h, d,
+                "backward dw1"));
+  if (sw)
+    MOE_TRY(wgrad(g->dw3, op_cols(db, h, f32), op_cols(x, d, f32, sv->perm, k), h, d,
+                  "backward dw3"));
+  MOE_TRY(wgrad(g->dw2, op_cols(dy, d, f32, sv->perm, k, sv->topk_gate), op_cols(hid, h, f32), d,
+                h, "backward dw2"));
+  // 6. dx
+  if (T > 0)
+    MOE_TRY(hip_status(launch_bw_assemble_dx(dxg, dxs, sv->inv, T, k, d, bf16, g->dx, s),
+                       "backward dx"));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -575,10 +850,10 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   int32_t* idx = out->topk_idx ? out->topk_idx : at<int32_t>(ws, L.idx);
   float* gate = out->topk_gate ? out->topk_gate : at<float>(ws, L.gate);
   int32_t* counts = out->counts ? out->counts : at<int32_t>(ws, L.counts);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* perm = at<int32_t>(ws, L.perm);
-  int32_t* inv = at<int32_t>(ws, L.inv);
-  void* y_sorted = at<void>(ws, L.ysorted);
+  int32_t* offsets = out->offsets ? out->offsets : at<int32_t>(ws, L.offsets);
+  int32_t* perm = out->perm ? out->perm : at<int32_t>(ws, L.perm);
+  int32_t* inv = out->inv ? out->inv : at<int32_t>(ws, L.inv);
+  void* y_sorted = out->y_sorted ? out->y_sorted : at<void>(ws, L.ysorted);
   const bool balance = out->balance != nullptr;
   const bool smooth = balance && cfg->n_groups == 0 && cfg->noisy && cfg->tokens > 0;
   // the flat gate writes the routing masks; the routing step builds the
@@ -591,8 +866,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   // small expert counts: the gate kernel writes per-tile importance (and
   // smooth-load) partials and the routing step reduces them
   const bool fused_stats = balance && flat && gate_fuses_load(cfg->n_experts);
-  // thresholds for the smooth-load recompute kernel
-  float* thr = smooth && !fused_stats ? at<float>(ws, L.thr) : nullptr;
+  // thresholds for the smooth-load recompute kernel (or for the caller)
+  if (out->thr && cfg->n_groups > 0) return fail(MOE_ERR_INVALID_ARG, "thr is for the flat gate only");
+  float* thr = out->thr ? out->thr : (smooth && !fused_stats ? at<float>(ws, L.thr) : nullptr);
   RouteStats st;
   float* part = nullptr;
   if (fused_stats) {
@@ -615,6 +891,64 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   if (balance && !fused_stats)
     MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, perm, offsets, w_importance, w_load, imp,
                        load, out->balance, false, ws, s));
+  return ok();
+}
+
+// ---- backward ---------------------------------------------------------------
+
+size_t moe_backward_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK || cfg->n_groups > 0) return 0;
+  return bw_layout(cfg).total;
+}
+
+moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* p,
+                        const moe_noise* noise, const moe_saved* sv, const void* dy,
+                        float w_importance, float w_load, moe_grads* g, void* ws,
+                        size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg));
+  if (cfg->n_groups > 0)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass covers the flat gate only");
+  if (!p || !sv || !g) return fail(MOE_ERR_INVALID_ARG, "params / saved / grads is NULL");
+  const int64_t T = cfg->tokens;
+  const bool rows = T > 0;
+  const bool noisy = cfg->noisy != 0;
+  const bool sw = cfg->ffn == MOE_FFN_SWIGLU;
+  if (!p->w_gate || (noisy && !p->w_noise))
+    return fail(MOE_ERR_INVALID_ARG, "w_gate / w_noise is NULL");
+  if (!p->w1 || !p->w2 || (sw && !p->w3))
+    return fail(MOE_ERR_INVALID_ARG, "the backward pass needs the unpacked w1 / w2 (/ w3)");
+  if (p->w_gate_packed) {
+    if (!gate_packable(cfg))
+      return fail(MOE_ERR_UNSUPPORTED, "packed gate tables need bf16 and d_model %% 64 == 0");
+    if (reinterpret_cast<uintptr_t>(p->w_gate_packed) & 15)
+      return fail(MOE_ERR_INVALID_ARG, "w_gate_packed must be 16-byte aligned");
+  }
+  if (!g->dx && rows) return fail(MOE_ERR_INVALID_ARG, "grads->dx is NULL");
+  if (g->dw_noise && !noisy) return fail(MOE_ERR_INVALID_ARG, "dw_noise needs a noisy gate");
+  if (g->dw3 && !sw) return fail(MOE_ERR_INVALID_ARG, "dw3 needs SwiGLU experts");
+  if (!sv->offsets) return fail(MOE_ERR_INVALID_ARG, "saved offsets is NULL");
+  if (rows) {
+    if (!x || !dy) return fail(MOE_ERR_INVALID_ARG, "x / dy is NULL");
+    if (noisy && (!noise || !noise->eps)) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps");
+    if (!sv->topk_idx || !sv->topk_gate || !sv->perm || !sv->inv || !sv->y_sorted)
+      return fail(MOE_ERR_INVALID_ARG, "saved topk_idx / topk_gate / perm / inv / y_sorted is NULL");
+    if (w_importance != 0.f && !sv->importance)
+      return fail(MOE_ERR_INVALID_ARG, "w_importance != 0 needs saved importance");
+    if (noisy && w_load != 0.f && (!sv->load || !sv->thr))
+      return fail(MOE_ERR_INVALID_ARG, "w_load != 0 with noise needs saved load and thr");
+  }
+  const BwLayout L = bw_layout(cfg);
+  if (L.total > 0) {
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+    if (reinterpret_cast<uintptr_t>(ws) & 255)
+      return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < L.total)
+      return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+  }
+  if (bw_gate_lds_bytes(cfg->dtype == MOE_BF16, cfg->d_model, cfg->n_experts) > 150 * 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts / d_model too large for the backward gate tile");
+  MOE_TRY(do_backward(cfg, L, x, p, noise, sv, dy, w_importance, w_load, g, ws,
+                      (hipStream_t)stream));
   return ok();
 }
 

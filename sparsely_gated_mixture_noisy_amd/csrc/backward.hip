@@ -1,0 +1,839 @@
+// Backward pass of the MoE layer with the flat gate: the gradients of
+//   L = sum(dy * y) + w_imp * CV^2(Importance) + w_load * CV^2(Load)
+// with respect to x, the gate tables and bias, and the expert tables.
+//
+// Pages: the reading note ("Outrageously Large Neural Networks — MoE 怎样让模型
+// “很大但不每次全算”", sections 问题是什么 and 方法怎么做) says the hard choice of
+// experts has no gradient and that the learnable noise lets more experts
+// receive one; the paper card (ai-papers.xuzou.cn, sections 瓶颈 and 方法适配)
+// names activation recomputation for the backward pass and the importance and
+// load losses.  The kept set and the experts ranked k-th and (k+1)-th are held
+// fixed; gradients flow through the kept softmax, the noisy scores, the smooth
+// load estimate and the experts.
+//
+// Steps (one stream, in this order):
+//   cv2 grad   dImp = w_imp dCV^2/dImportance, dLoad = w_load dCV^2/dLoad
+//   gate out   dg[t,s] = dy_t . y_sorted[inv[t,s]] + dImp[e]; softmax
+//              backward over the kept scores -> dHk[t,s]
+//   gate rank  per token: which experts are ranked k-th and (k+1)-th, and the
+//              sums of the threshold gradients that flow to their scores
+//   gate grad  per (token, expert): dclean, draw (noise pre-activation), and
+//              per-32-token partial sums of dclean (the bias gradient)
+//   products   dx_gate = dclean W_g + draw W_noise;  dW_g = dclean^T x,
+//              dW_noise = draw^T x (split over tokens, then summed in order)
+//   experts    recompute the hidden layer, dHid = dY W2, its mask or SwiGLU
+//              factors; dX = dP W1 (+ dB W3); dW1 = dP^T X; dW2 = dY^T Hid
+//   assemble   dx_t = dx_gate_t + sum_s dX[inv[t,s]]
+//
+// bf16 layers: products run on MFMA (v_mfma_f32_32x32x16_bf16) with fp32
+// accumulation; operands that are fp32 (dclean, draw) or scaled (gate * dy)
+// are rounded to bf16 as they enter a product, the hidden activation and its
+// gradients are rounded to bf16 between products, outputs are rounded to the
+// layer's dtype.  fp32 layers use plain fp32 FMA loops.  Every sum runs in a
+// fixed order: the results are deterministic.
+#include "gate_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// CV^2 gradients: g_i = w * 2 / (n m^2) * (v_i - m - var / m), fp64
+// reductions in a fixed order; 0 when the mean is 0 or v is absent.
+// ---------------------------------------------------------------------------
+__device__ void cv2_grad_block(const float* v, int E, float wgt, float* g) {
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  for (int i = tid; i < E; i += 256) s += (double)v[i];
+  const double mean = sum256_f64<256>(s) / E;
+  double q = 0.0;
+  for (int i = tid; i < E; i += 256) {
+    const double dv = (double)v[i] - mean;
+    q += dv * dv;
+  }
+  const double var = sum256_f64<256>(q) / E;
+  for (int i = tid; i < E; i += 256) {
+    double r = 0.0;
+    if (mean != 0.0) r = 2.0 / ((double)E * mean * mean) * ((double)v[i] - mean - var / mean);
+    g[i] = (float)((double)wgt * r);
+  }
+}
+
+__global__ __launch_bounds__(256) void bw_cv2_grad_kernel(const float* imp, const float* load,
+                                                          int E, float wi, float wl, float* dimp,
+                                                          float* dload) {
+  if (imp) {
+    cv2_grad_block(imp, E, wi, dimp);
+  } else {
+    for (int i = threadIdx.x; i < E; i += 256) dimp[i] = 0.f;
+  }
+  if (load) {
+    cv2_grad_block(load, E, wl, dload);
+  } else {
+    for (int i = threadIdx.x; i < E; i += 256) dload[i] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gate outputs: one wave per token.  dg[s] = dy_t . y_sorted[inv[t*k+s]]
+// (lanes over d, then a fixed butterfly) + dImp[idx[t,s]]; then
+// dHk[t,s] = g_s (dg_s - sum_j g_j dg_j).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bw_gate_out_kernel(BwGateOutArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const T* dy = (const T*)a.dy + t * a.d;
+  const T* ys = (const T*)a.y_sorted;
+  float dg[8], g[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    dg[s] = 0.f;
+    g[s] = 0.f;
+    if (s < a.k) {
+      const int64_t p = a.inv[t * a.k + s];
+      const T* yr = ys + p * a.d;
+      float acc = 0.f;
+      for (int c = lane; c < a.d; c += 64) acc = fmaf(Elem<T>::load(dy, c), Elem<T>::load(yr, c), acc);
+      dg[s] = wave_sum(acc);
+      if (a.dimp) dg[s] += a.dimp[a.idx[t * a.k + s]];
+      g[s] = a.gate[t * a.k + s];
+    }
+  }
+  float sdot = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) sdot = fmaf(g[s], dg[s], sdot);
+  if (lane < a.k) {
+    float v = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s == lane) v = g[s] * (dg[s] - sdot);
+    a.dhk[t * a.k + lane] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gate score tiles (32 tokens, eight waves, experts in blocks of 256): the
+// forward's projection recomputes clean = x W_g^T + b, raw = x W_noise^T and
+// H for the lane's (row, expert) pairs in the MFMA accumulator layout (lane l
+// of wave w: expert blk + 32w + l%32, rows acc_row(i, l)).
+// ---------------------------------------------------------------------------
+struct RankBest {
+  float v;
+  int e;
+};
+// a ranks before b: larger score, then lower index
+__device__ __forceinline__ bool rb_before(const RankBest& a, const RankBest& b) {
+  return ranks_before(a.v, a.e, b.v, b.e);
+}
+__device__ __forceinline__ RankBest rb_xor(const RankBest& r, int off) {
+  return RankBest{__shfl_xor(r.v, off, 64), __shfl_xor(r.e, off, 64)};
+}
+
+// The gate tile's shared set-up: rows, the x tile, kept masks (bit r of
+// sb[e]: tile row r keeps expert e), kept experts per row, thresholds.
+struct BwTileShared {
+  int rows[GATE_ROWS];
+  int kle[GATE_ROWS][8];
+  float kth[GATE_ROWS], k1th[GATE_ROWS];
+};
+
+template <typename T, bool XLDS>
+__device__ void bw_tile_setup(const BwGateArgs& a, BwTileShared& sh, uint32_t* sb, bf16_t* Xs,
+                              int xld) {
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  if (tid < GATE_ROWS) sh.rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
+  for (int i = tid; i < a.E; i += GATE_THREADS) sb[i] = 0u;
+  __syncthreads();
+  if (tid < GATE_ROWS) {
+    const int64_t t = t0 + tid;
+    const bool valid = t < a.T;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      int e = -1;
+      if (valid && s < a.k) e = a.idx[t * a.k + s];
+      sh.kle[tid][s] = e;
+      if (e >= 0) atomicOr(&sb[e], 1u << tid);
+    }
+    sh.kth[tid] = (valid && a.thr) ? a.thr[2 * t] : 0.f;
+    sh.k1th[tid] = (valid && a.thr) ? a.thr[2 * t + 1] : 0.f;
+  }
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, sh.rows, GATE_ROWS, Xs, xld);
+  __syncthreads();
+}
+
+// Scores of one expert block for the lane: clean (bias included), sp, H, raw.
+template <typename T, bool NOISY, bool XLDS>
+__device__ __forceinline__ void bw_block_scores(const BwGateArgs& a, const BwTileShared& sh,
+                                                const bf16_t* Xs, int xld, int blk, f32x16& cs,
+                                                f32x16& ss, f32x16& hs, f32x16& rs, f32x16& es) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blk + w * 32 + (lane & 31);
+  const bool ev = e < a.E;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    es[r] = (NOISY && ev) ? a.eps[(int64_t)sh.rows[acc_row(r, lane)] * a.E + e] : 0.f;
+  const TileX<T> tx{(const T*)a.x, sh.rows, XLDS ? Xs : nullptr, xld};
+  const GateTabs tb{a.w_gate, a.w_noise, 0, (const bf16_t*)a.w_pack, 0, a.pack_nt};
+  f32x16 ac[1], ar[1];
+  BlockProj<T, NOISY, XLDS, 1>::run(tx, a.d, tb, blk, a.E, ac, ar);
+  const float b = (a.bias && ev) ? a.bias[e] : 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float c = ac[0][r] + b;
+    cs[r] = c;
+    if (NOISY) {
+      const float sp = softplus_f(ar[0][r]);
+      ss[r] = sp;
+      hs[r] = noisy_score(c, es[r], sp);
+      rs[r] = ar[0][r];
+    } else {
+      ss[r] = 0.f;
+      hs[r] = c;
+      rs[r] = 0.f;
+    }
+  }
+}
+
+// phi(z) = exp(-z^2/2) / sqrt(2 pi); z = +-inf gives 0
+__device__ __forceinline__ float normal_pdf_f(float z) {
+  return 0.3989422804014327f * exp2_hw(-0.5f * z * z * 1.4426950408889634f);
+}
+
+template <typename T, bool NOISY, bool XLDS>
+__global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a) {
+  __shared__ BwTileShared sh;
+  __shared__ RankBest wk[GATE_WAVES][GATE_ROWS], bn[GATE_WAVES][GATE_ROWS];
+  __shared__ float wsk[GATE_WAVES][GATE_ROWS], wsn[GATE_WAVES][GATE_ROWS];
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+  const int xld = a.d + 8;
+  bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
+  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
+  bw_tile_setup<T, XLDS>(a, sh, sb, Xs, xld);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool smooth = NOISY && a.dload != nullptr;
+  RankBest worst_kept[16], best_drop[16];
+  float s_kept[16], s_drop[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    worst_kept[r] = RankBest{INFINITY, -1};
+    best_drop[r] = RankBest{-INFINITY, 0x7fffffff};
+    s_kept[r] = 0.f;
+    s_drop[r] = 0.f;
+  }
+  for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
+    f32x16 cs, ss, hs, rs, es;
+    bw_block_scores<T, NOISY, XLDS>(a, sh, Xs, xld, blk, cs, ss, hs, rs, es);
+    const int e = blk + w * 32 + (lane & 31);
+    if (e < a.E) {
+      const uint32_t km = sb[e];
+      const float dl = smooth ? a.dload[e] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, lane);
+        const bool kept = (km >> row) & 1u;
+        const RankBest cur{hs[r], e};
+        if (kept) {
+          if (rb_before(worst_kept[r], cur)) worst_kept[r] = cur;
+        } else {
+          if (rb_before(cur, best_drop[r])) best_drop[r] = cur;
+        }
+        if (smooth) {
+          const float th = kept ? sh.k1th[row] : sh.kth[row];
+          const float isp = rcp_hw(ss[r]);
+          const float z = (cs[r] - th) * isp;
+          const float dt = (z == INFINITY || z == -INFINITY) ? 0.f : -dl * normal_pdf_f(z) * isp;
+          if (kept) s_kept[r] += dt;
+          else s_drop[r] += dt;
+        }
+      }
+    }
+  }
+  // across the 32 lanes of a half-wave (the experts of one row)
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const RankBest ok = rb_xor(worst_kept[r], off);
+      if (rb_before(worst_kept[r], ok)) worst_kept[r] = ok;
+      const RankBest od = rb_xor(best_drop[r], off);
+      if (rb_before(od, best_drop[r])) best_drop[r] = od;
+      s_kept[r] += __shfl_xor(s_kept[r], off, 64);
+      s_drop[r] += __shfl_xor(s_drop[r], off, 64);
+    }
+  }
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = acc_row(r, lane);
+      wk[w][row] = worst_kept[r];
+      bn[w][row] = best_drop[r];
+      wsk[w][row] = s_kept[r];
+      wsn[w][row] = s_drop[r];
+    }
+  }
+  __syncthreads();
+  // across the eight waves, in wave order
+  if (tid < GATE_ROWS) {
+    const int64_t t = (int64_t)blockIdx.x * GATE_ROWS + tid;
+    RankBest k0 = wk[0][tid], d0 = bn[0][tid];
+    float sk = wsk[0][tid], sd = wsn[0][tid];
+    for (int i = 1; i < GATE_WAVES; ++i) {
+      if (rb_before(k0, wk[i][tid])) k0 = wk[i][tid];
+      if (rb_before(bn[i][tid], d0)) d0 = bn[i][tid];
+      sk += wsk[i][tid];
+      sd += wsn[i][tid];
+    }
+    if (t < a.T) {
+      int4 out;
+      out.x = k0.e;                                   // expert ranked k-th
+      out.y = d0.e == 0x7fffffff ? -1 : d0.e;         // ranked k+1-th (none: -1)
+      out.z = __float_as_int(sd);                     // gradient to the k-th score
+      out.w = __float_as_int(sk);                     // gradient to the (k+1)-th score
+      reinterpret_cast<int4*>(a.rinfo)[t] = out;
+    }
+  }
+}
+
+template <typename T, bool NOISY, bool XLDS>
+__global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a) {
+  __shared__ BwTileShared sh;
+  __shared__ int4 ri[GATE_ROWS];
+  __shared__ float dhk[GATE_ROWS][8];
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+  const int xld = a.d + 8;
+  bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
+  uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  if (tid < GATE_ROWS) {
+    const int64_t t = min<int64_t>(t0 + tid, a.T - 1);
+    ri[tid] = reinterpret_cast<const int4*>(a.rinfo)[t];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dhk[tid][s] = s < a.k ? a.dhk[t * a.k + s] : 0.f;
+  }
+  bw_tile_setup<T, XLDS>(a, sh, sb, Xs, xld);
+  const bool smooth = NOISY && a.dload != nullptr;
+  const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
+  for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
+    f32x16 cs, ss, hs, rs, es;
+    bw_block_scores<T, NOISY, XLDS>(a, sh, Xs, xld, blk, cs, ss, hs, rs, es);
+    const int e = blk + w * 32 + (lane & 31);
+    float bsum = 0.f;
+    if (e < a.E) {
+      const uint32_t km = sb[e];
+      const float dl = smooth ? a.dload[e] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, lane);
+        const bool kept = (km >> row) & 1u;
+        float dh = 0.f;
+        if (kept) {
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+            if (sh.kle[row][s] == e) dh = dhk[row][s];
+        }
+        const int4 rw = ri[row];
+        if (e == rw.x) dh += __int_as_float(rw.z);
+        if (e == rw.y) dh += __int_as_float(rw.w);
+        float dc = dh;
+        if (NOISY) {
+          float dsp = dh * es[r];
+          if (smooth) {
+            const float th = kept ? sh.k1th[row] : sh.kth[row];
+            const float isp = rcp_hw(ss[r]);
+            const float z = (cs[r] - th) * isp;
+            if (z != INFINITY && z != -INFINITY) {
+              const float dz = dl * normal_pdf_f(z);
+              dc += dz * isp;
+              dsp -= dz * z * isp;
+            }
+          }
+          // d softplus(raw) / d raw = sigmoid(raw)
+          const float sg = rcp_hw(1.0f + exp2_hw(-rs[r] * 1.4426950408889634f));
+          if (row < valid) a.draw[(t0 + row) * a.E + e] = dsp * sg;
+        }
+        if (row < valid) a.dclean[(t0 + row) * a.E + e] = dc;
+        bsum += row < valid ? dc : 0.f;
+      }
+    }
+    bsum += __shfl_xor(bsum, 32, 64);
+    if (lane < 32 && e < a.E) a.dbias_part[(int64_t)blockIdx.x * a.E + e] = bsum;
+  }
+}
+
+// dbias[e] = sum over 32-token blocks of the partials, in block order
+__global__ __launch_bounds__(256) void bw_sum_rows_kernel(const float* part, int64_t nrow,
+                                                          int64_t ncol, float* out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= ncol) return;
+  float s = 0.f;
+  for (int64_t r = 0; r < nrow; ++r) s += part[r * ncol + c];
+  out[c] = s;
+}
+
+// out[i] = cast(sum over chunks of part[chunk][i]) in chunk order
+template <typename TO>
+__global__ __launch_bounds__(256) void bw_sum_chunks_kernel(const float* part, int nchunk,
+                                                            int64_t n, TO* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int c = 0; c < nchunk; ++c) s += part[(int64_t)c * n + i];
+  Elem<TO>::store(out, i, s);
+}
+
+// dx[t][c] = dx_gate[t][c] + sum_s dxs[inv[t*k+s]][c], slots in order
+template <typename TO>
+__global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, const float* dxs,
+                                                             const int32_t* inv, int64_t T, int k,
+                                                             int d, TO* dx) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * d) return;
+  const int64_t t = i / d;
+  const int c = (int)(i % d);
+  float v = dxg[i];
+  for (int s = 0; s < k; ++s) v += dxs[(int64_t)inv[t * k + s] * d + c];
+  Elem<TO>::store(dx, i, v);
+}
+
+// ---------------------------------------------------------------------------
+// Products.  C[m][n] = sum_k A(m, k) B(n, k) for each problem (an expert, or
+// the single gate problem), operands described by BwOp:
+//   kmajor: element (r, k) at p + e*estride + src(r)*ld + k
+//   else:   element (r, k) at p + e*estride + src(k)*ld + r
+// with src(i) = gather ? gather[i] / gk : i, times scale[gather ? gather[i] :
+// i] when scale is set.  Geometry (BwGemm::mode):
+//   POS   rows m are the positions of expert e (absolute, offsets[e] ..), K
+//         fixed; grid = row tiles of the tile map x column tiles
+//   WGT   M, N fixed per expert, k runs over the positions of expert e
+//   PLAIN one problem; grid = row tiles x column tiles x K chunks
+// ---------------------------------------------------------------------------
+constexpr int BG_BM = 128, BG_BN = 128, BG_BK = 32, BG_LD = BG_BK + 8;
+
+__device__ __forceinline__ int bw_src(const BwOp& o, int64_t i) {
+  return o.gather ? o.gather[i] / o.gk : (int)i;
+}
+__device__ __forceinline__ float bw_scale(const BwOp& o, int64_t i) {
+  return o.scale ? o.scale[o.gather ? o.gather[i] : i] : 1.0f;
+}
+__device__ __forceinline__ float bw_elem(const BwOp& o, int e, int64_t r, int64_t k) {
+  const int64_t base = (int64_t)e * o.estride;
+  int64_t off;
+  float s;
+  if (o.kmajor) {
+    off = base + (int64_t)bw_src(o, r) * o.ld + k;
+    s = bw_scale(o, r);
+  } else {
+    off = base + (int64_t)bw_src(o, k) * o.ld + r;
+    s = bw_scale(o, k);
+  }
+  const float v = o.f32 ? ((const float*)o.p)[off] : bf16_to_f32(((const bf16_t*)o.p)[off]);
+  return v * s;
+}
+
+// The part of v an operand carries into a bf16 product: v itself (rounded to
+// bf16 by the caller), or with `lo` the residual v - bf16(v), exact in fp32,
+// so that a hi pass and a lo pass together carry about 16 significant bits.
+__device__ __forceinline__ float bw_part(const BwOp& o, float v) {
+  if (!o.lo) return v;
+  const uint32_t hi = cvt_pk_bf16(v, 0.f) << 16;
+  return v - __uint_as_float(hi);
+}
+
+// Fill the LDS tile S[BG_BM][BG_LD] with rows r0 .. r0+127 (valid below R),
+// k = k0 .. k0+31 (valid below K) of operand o, as bf16; 256 threads.
+__device__ __forceinline__ void bw_fill(const BwOp& o, int e, int64_t r0, int64_t R, int64_t k0,
+                                        int64_t K, bf16_t (*S)[BG_LD]) {
+  const int tid = threadIdx.x;
+  if (o.kmajor) {
+    // two 8-element k chunks per thread: rows tid/4 and +64, chunk (tid%4)*8
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = (tid >> 2) + 64 * i, kc = (tid & 3) * 8;
+      const int64_t r = r0 + rr, k = k0 + kc;
+      u32x4 out = {0u, 0u, 0u, 0u};
+      if (r < R && k < K) {
+        const int64_t base = (int64_t)e * o.estride + (int64_t)bw_src(o, r) * o.ld;
+        const float s = bw_scale(o, r);
+        float v[8];
+        // whole 16-byte (bf16) or 2 x 16-byte (fp32) pieces when the row
+        // stride keeps them aligned
+        if (k + 8 <= K && !o.f32 && !o.scale && (o.ld & 7) == 0) {
+          out = *reinterpret_cast<const u32x4*>((const bf16_t*)o.p + base + k);
+        } else {
+          if (k + 8 <= K && o.f32 && (o.ld & 3) == 0) {
+            const float4 a = *reinterpret_cast<const float4*>((const float*)o.p + base + k);
+            const float4 b = *reinterpret_cast<const float4*>((const float*)o.p + base + k + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              v[j] = 0.f;
+              if (k + j < K)
+                v[j] = o.f32 ? ((const float*)o.p)[base + k + j]
+                             : bf16_to_f32(((const bf16_t*)o.p)[base + k + j]);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = bw_part(o, v[j] * s);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) out[j] = cvt_pk_bf16(v[2 * j], v[2 * j + 1]);
+        }
+      }
+      *reinterpret_cast<u32x4*>(&S[rr][kc]) = out;
+    }
+  } else {
+    // two rows x 8 k per thread: rows 2*(tid%64) .. +1, k chunk (tid/64)*8
+    const int rr = (tid & 63) * 2, kc = (tid >> 6) * 8;
+    const int64_t r = r0 + rr;
+    float v0[8], v1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v0[j] = 0.f;
+      v1[j] = 0.f;
+      const int64_t k = k0 + kc + j;
+      if (k < K && r < R) {
+        const int64_t base = (int64_t)e * o.estride + (int64_t)bw_src(o, k) * o.ld + r;
+        const float s = bw_scale(o, k);
+        if (r + 1 < R && (o.ld & 1) == 0) {
+          // the pair (r, r + 1) in one 8-byte (fp32) or 4-byte (bf16) load
+          if (o.f32) {
+            const float2 a = *reinterpret_cast<const float2*>((const float*)o.p + base);
+            v0[j] = a.x * s;
+            v1[j] = a.y * s;
+          } else {
+            const uint32_t u = *reinterpret_cast<const uint32_t*>((const bf16_t*)o.p + base);
+            v0[j] = __uint_as_float(u << 16) * s;
+            v1[j] = __uint_as_float(u & 0xffff0000u) * s;
+          }
+        } else {
+          v0[j] = (o.f32 ? ((const float*)o.p)[base] : bf16_to_f32(((const bf16_t*)o.p)[base])) * s;
+          if (r + 1 < R)
+            v1[j] = (o.f32 ? ((const float*)o.p)[base + 1]
+                           : bf16_to_f32(((const bf16_t*)o.p)[base + 1])) * s;
+        }
+      }
+    }
+    u32x4 o0, o1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v0[j] = bw_part(o, v0[j]);
+      v1[j] = bw_part(o, v1[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o0[j] = cvt_pk_bf16(v0[2 * j], v0[2 * j + 1]);
+      o1[j] = cvt_pk_bf16(v1[2 * j], v1[2 * j + 1]);
+    }
+    *reinterpret_cast<u32x4*>(&S[rr][kc]) = o0;
+    *reinterpret_cast<u32x4*>(&S[rr + 1][kc]) = o1;
+  }
+}
+
+// Which problem, rows, columns and K range a workgroup covers.
+struct BwTile {
+  int e;
+  int64_t m0, M;   // rows m0 .. M-1 (absolute positions in POS mode)
+  int64_t n0, N;
+  int64_t k0, K;   // k range [k0, K) (absolute positions in WGT mode)
+  int chunk;
+};
+
+__device__ __forceinline__ bool bw_tile_of(const BwGemm& g, BwTile* t) {
+  const int bid = blockIdx.x;
+  if (g.mode == BW_POS) {
+    const int q = bid / g.ncol, ct = bid % g.ncol;
+    const int Q = g.tiles[g.E];
+    if (q >= Q) return false;
+    int lo = 0, hi = g.E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.tiles[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    t->e = lo;
+    t->m0 = g.offsets[lo] + (int64_t)(q - g.tiles[lo]) * BG_BM;
+    t->M = g.offsets[lo + 1];
+    t->n0 = (int64_t)ct * BG_BN;
+    t->N = g.N;
+    t->k0 = 0;
+    t->K = g.K;
+    t->chunk = 0;
+  } else if (g.mode == BW_WGT) {
+    const int per = g.nrow * g.ncol;
+    const int e = bid / per, rem = bid % per;
+    t->e = e;
+    t->m0 = (int64_t)(rem / g.ncol) * BG_BM;
+    t->M = g.M;
+    t->n0 = (int64_t)(rem % g.ncol) * BG_BN;
+    t->N = g.N;
+    t->k0 = g.offsets[e];
+    t->K = g.offsets[e + 1];
+    t->chunk = 0;
+  } else {
+    const int per = g.nrow * g.ncol;
+    const int c = bid / per, rem = bid % per;
+    t->e = 0;
+    t->m0 = (int64_t)(rem / g.ncol) * BG_BM;
+    t->M = g.M;
+    t->n0 = (int64_t)(rem % g.ncol) * BG_BN;
+    t->N = g.N;
+    t->k0 = (int64_t)c * g.kchunk;
+    t->K = min<int64_t>(g.K, t->k0 + g.kchunk);
+    t->chunk = c;
+  }
+  return true;
+}
+
+// Output element (m, n) of a plain product.
+__device__ __forceinline__ void bw_store(const BwGemm& g, const BwTile& t, int64_t m, int64_t n,
+                                         float v) {
+  const int64_t i = (int64_t)t.e * g.c_estride + (int64_t)t.chunk * g.c_chunk + m * g.ldc + n;
+  if (g.c_f32) ((float*)g.C)[i] = v;
+  else ((bf16_t*)g.C)[i] = f32_to_bf16(v);
+}
+
+// The expert-hidden epilogue: acc[0] = X W1^T (pre-activation a), acc[1] =
+// dY W2 (dHid), acc[2] = X W3^T (SwiGLU b).  ReLU writes Hid = relu(a) and dP
+// = dHid * (a > 0); SwiGLU writes Hid = silu(a) b, dA = dHid b silu'(a), dB =
+// dHid silu(a).  All [A][N] bf16.
+__device__ __forceinline__ void bw_hidden_store(const BwGemm& g, int64_t m, int64_t n, float a,
+                                                float dh, float b) {
+  const int64_t i = m * g.N + n;
+  bf16_t* hid = (bf16_t*)g.C;
+  bf16_t* d1 = (bf16_t*)g.C2;
+  if (g.epi == BW_EPI_RELU) {
+    hid[i] = f32_to_bf16(fmaxf(a, 0.f));
+    d1[i] = f32_to_bf16(a > 0.f ? dh : 0.f);
+  } else {
+    const float sg = 1.0f / (1.0f + expf(-a));
+    const float sl = a * sg;
+    hid[i] = f32_to_bf16(sl * b);
+    d1[i] = f32_to_bf16(dh * b * sg * (1.0f + a * (1.0f - sg)));
+    ((bf16_t*)g.C3)[i] = f32_to_bf16(dh * sl);
+  }
+}
+
+// bf16 MFMA product: 128 x 128 tile, four waves of 64 x 64, K in slices of
+// 32 staged through LDS (the next slice's loads in flight during the MFMAs).
+// NPROD products share the tile (the hidden epilogue: 2 for ReLU, 3 for
+// SwiGLU); plain products may add further operand pairs (sa/sb) over the
+// same K range.
+template <int NPROD>
+__global__ __launch_bounds__(256) void bw_gemm_mfma_kernel(BwGemm g) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[NPROD][BG_BM][BG_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[NPROD][BG_BN][BG_LD];
+  BwTile t;
+  if (!bw_tile_of(g, &t)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1, fr = lane & 31, fk = (lane >> 5) * 8;
+  f32x16 acc[NPROD][2][2];
+#pragma unroll
+  for (int p = 0; p < NPROD; ++p)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[p][i][j] = f32x16{};
+  const int nseg = 1 + g.nextra;
+  for (int seg = 0; seg < nseg; ++seg) {
+    for (int64_t k0 = t.k0; k0 < t.K; k0 += BG_BK) {
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < NPROD; ++p) {
+        const BwOp& A = seg ? g.sa[seg - 1] : (p == 0 ? g.a : p == 1 ? g.a1 : g.a);
+        const BwOp& B = seg ? g.sb[seg - 1] : (p == 0 ? g.b : p == 1 ? g.b1 : g.b3);
+        bw_fill(A, t.e, t.m0, t.M, k0, t.K, As[p]);
+        bw_fill(B, t.e, t.n0, t.N, k0, t.K, Bs[p]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < BG_BK; ks += 16) {
+#pragma unroll
+        for (int p = 0; p < NPROD; ++p) {
+          bf16x8 af[2], bf[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            af[i] = *reinterpret_cast<const bf16x8*>(&As[p][wm * 64 + i * 32 + fr][ks + fk]);
+            bf[i] = *reinterpret_cast<const bf16x8*>(&Bs[p][wn * 64 + i * 32 + fr][ks + fk]);
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[p][i][j] = mfma32(af[i], bf[j], acc[p][i][j]);
+        }
+      }
+    }
+  }
+  // accumulator register r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = t.m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t n = t.n0 + wn * 64 + j * 32 + fr;
+        if (m >= t.M || n >= t.N) continue;
+        if constexpr (NPROD == 1) {
+          bw_store(g, t, m, n, acc[0][i][j][r]);
+        } else if constexpr (NPROD == 2) {
+          bw_hidden_store(g, m, n, acc[0][i][j][r], acc[1][i][j][r], 0.f);
+        } else {
+          bw_hidden_store(g, m, n, acc[0][i][j][r], acc[1][i][j][r], acc[2][i][j][r]);
+        }
+      }
+}
+
+// fp32 products: one thread per output element, plain FMA over k in order.
+__global__ __launch_bounds__(256) void bw_gemm_scalar_kernel(BwGemm g) {
+  // the tile geometry of the MFMA kernel, 256 threads over a 128 x 128 tile
+  BwTile t;
+  if (!bw_tile_of(g, &t)) return;
+  const bool hidden = g.epi != BW_EPI_NONE;
+  const bool sw = g.epi == BW_EPI_SWIGLU;
+  for (int idx = threadIdx.x; idx < BG_BM * BG_BN; idx += 256) {
+    const int64_t m = t.m0 + idx / BG_BN, n = t.n0 + idx % BG_BN;
+    if (m >= t.M || n >= t.N) continue;
+    const int nseg = 1 + g.nextra;
+    float s0 = 0.f, s1 = 0.f, s3 = 0.f;
+    for (int seg = 0; seg < nseg; ++seg) {
+      const BwOp& A = seg ? g.sa[seg - 1] : g.a;
+      const BwOp& B = seg ? g.sb[seg - 1] : g.b;
+      if (A.lo) continue;  // fp32 products take fp32 operands whole
+      for (int64_t k = t.k0; k < t.K; ++k) {
+        s0 = fmaf(bw_elem(A, t.e, m, k), bw_elem(B, t.e, n, k), s0);
+        if (hidden) s1 = fmaf(bw_elem(g.a1, t.e, m, k), bw_elem(g.b1, t.e, n, k), s1);
+        if (sw) s3 = fmaf(bw_elem(g.a, t.e, m, k), bw_elem(g.b3, t.e, n, k), s3);
+      }
+    }
+    if (!hidden) {
+      bw_store(g, t, m, n, s0);
+    } else {
+      const int64_t i = m * g.N + n;
+      float* hid = (float*)g.C;
+      float* d1 = (float*)g.C2;
+      if (!sw) {
+        hid[i] = fmaxf(s0, 0.f);
+        d1[i] = s0 > 0.f ? s1 : 0.f;
+      } else {
+        const float sg = 1.0f / (1.0f + expf(-s0));
+        hid[i] = s0 * sg * s3;
+        d1[i] = s1 * s3 * sg * (1.0f + s0 * (1.0f - sg));
+        ((float*)g.C3)[i] = s1 * s0 * sg;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_bw_cv2_grad(const float* imp, const float* load, int E, float wi, float wl,
+                              float* dimp, float* dload, hipStream_t s) {
+  hipLaunchKernelGGL(bw_cv2_grad_kernel, dim3(1), dim3(256), 0, s, imp, load, E, wi, wl, dimp,
+                     dload);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_gate_out(const BwGateOutArgs& a, bool bf16, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.T + 3) / 4));
+  if (bf16) hipLaunchKernelGGL(bw_gate_out_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(bw_gate_out_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+static size_t bw_gate_lds(bool xlds, int d, int E) {
+  return (xlds ? sizeof(bf16_t) * GATE_ROWS * (d + 8) : 0) + sizeof(uint32_t) * (size_t)E;
+}
+
+template <typename K>
+static hipError_t bw_set_lds(K kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+template <typename T, bool NOISY, bool XLDS>
+static hipError_t launch_bw_gate_v(const BwGateArgs& a, hipStream_t s) {
+  const size_t lds = bw_gate_lds(XLDS, a.d, a.E);
+  hipError_t err = bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS>, lds);
+  if (err != hipSuccess) return err;
+  err = bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS>, lds);
+  if (err != hipSuccess) return err;
+  const dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
+  hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS>), grid, dim3(GATE_THREADS), lds, s, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((bw_gate_grad_kernel<T, NOISY, XLDS>), grid, dim3(GATE_THREADS), lds, s, a);
+  return hipGetLastError();
+}
+
+size_t bw_gate_lds_bytes(bool bf16, int d, int E) {
+  return bw_gate_lds(bf16 && d <= GATE_XLDS_MAX_D, d, E);
+}
+
+hipError_t launch_bw_gate(const BwGateArgs& a, bool bf16, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const bool noisy = a.w_noise != nullptr;
+  if (bf16) {
+    if (a.d <= GATE_XLDS_MAX_D)
+      return noisy ? launch_bw_gate_v<bf16_t, true, true>(a, s)
+                   : launch_bw_gate_v<bf16_t, false, true>(a, s);
+    return noisy ? launch_bw_gate_v<bf16_t, true, false>(a, s)
+                 : launch_bw_gate_v<bf16_t, false, false>(a, s);
+  }
+  return noisy ? launch_bw_gate_v<float, true, false>(a, s)
+               : launch_bw_gate_v<float, false, false>(a, s);
+}
+
+hipError_t launch_bw_sum_rows(const float* part, int64_t nrow, int64_t ncol, float* out,
+                              hipStream_t s) {
+  if (ncol == 0) return hipSuccess;
+  hipLaunchKernelGGL(bw_sum_rows_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
+                     part, nrow, ncol, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_sum_chunks(const float* part, int nchunk, int64_t n, bool bf16, void* out,
+                                hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16) hipLaunchKernelGGL(bw_sum_chunks_kernel<bf16_t>, grid, dim3(256), 0, s, part, nchunk, n, (bf16_t*)out);
+  else hipLaunchKernelGGL(bw_sum_chunks_kernel<float>, grid, dim3(256), 0, s, part, nchunk, n, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_assemble_dx(const float* dxg, const float* dxs, const int32_t* inv, int64_t T,
+                                 int k, int d, bool bf16, void* dx, hipStream_t s) {
+  const int64_t n = T * d;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(bw_assemble_dx_kernel<bf16_t>, grid, dim3(256), 0, s, dxg, dxs, inv, T, k, d, (bf16_t*)dx);
+  else
+    hipLaunchKernelGGL(bw_assemble_dx_kernel<float>, grid, dim3(256), 0, s, dxg, dxs, inv, T, k, d, (float*)dx);
+  return hipGetLastError();
+}
+
+int bw_tile_rows() { return BG_BM; }
+
+hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
+  g.ncol = (int)((g.N + BG_BN - 1) / BG_BN);
+  g.nrow = (int)((g.M + BG_BM - 1) / BG_BM);
+  if (grid <= 0 || g.ncol == 0) return hipSuccess;
+  if (!bf16) {
+    hipLaunchKernelGGL(bw_gemm_scalar_kernel, dim3((unsigned)grid), dim3(256), 0, s, g);
+  } else if (g.epi == BW_EPI_NONE) {
+    hipLaunchKernelGGL(bw_gemm_mfma_kernel<1>, dim3((unsigned)grid), dim3(256), 0, s, g);
+  } else if (g.epi == BW_EPI_RELU) {
+    hipLaunchKernelGGL(bw_gemm_mfma_kernel<2>, dim3((unsigned)grid), dim3(256), 0, s, g);
+  } else {
+    hipLaunchKernelGGL(bw_gemm_mfma_kernel<3>, dim3((unsigned)grid), dim3(256), 0, s, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

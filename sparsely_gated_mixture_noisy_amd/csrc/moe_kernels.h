@@ -150,4 +150,88 @@ struct BalanceArgs {
 };
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
 
+// -------------------------------------------------------------- backward ---
+hipError_t launch_bw_cv2_grad(const float* imp, const float* load, int E, float wi, float wl,
+                              float* dimp, float* dload, hipStream_t s);
+
+struct BwGateOutArgs {
+  const void* y_sorted;  // [A][d]
+  const int32_t* inv;    // [A]
+  const int32_t* idx;    // [T][k]
+  const float* gate;     // [T][k]
+  const void* dy;        // [T][d]
+  const float* dimp;     // [E] or null
+  int64_t T;
+  int k, d;
+  float* dhk;            // [T][k] gradient of the kept noisy scores
+};
+hipError_t launch_bw_gate_out(const BwGateOutArgs& a, bool bf16, hipStream_t s);
+
+struct BwGateArgs {
+  const void* x;
+  const void* w_gate;
+  const void* w_noise;   // null: noise-free gate
+  const float* bias;
+  const float* eps;      // [T][E] (noisy)
+  const void* w_pack = nullptr;
+  int pack_nt = 0;
+  const int32_t* idx;    // [T][k]
+  const float* thr;      // [T][2] (smooth load) or null
+  const float* dload;    // [E] load-loss gradient or null (no smooth-load term)
+  const float* dhk;      // [T][k]
+  int64_t T;
+  int d, E, k;
+  int32_t* rinfo;        // [T][4]: expert ranked k, k+1 (-1: none), their score gradients
+  float* dclean;         // [T][E]
+  float* draw;           // [T][E] (noisy)
+  float* dbias_part;     // [ceil(T/32)][E]
+};
+size_t bw_gate_lds_bytes(bool bf16, int d, int E);
+hipError_t launch_bw_gate(const BwGateArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bw_sum_rows(const float* part, int64_t nrow, int64_t ncol, float* out,
+                              hipStream_t s);
+hipError_t launch_bw_sum_chunks(const float* part, int nchunk, int64_t n, bool bf16, void* out,
+                                hipStream_t s);
+hipError_t launch_bw_assemble_dx(const float* dxg, const float* dxs, const int32_t* inv, int64_t T,
+                                 int k, int d, bool bf16, void* dx, hipStream_t s);
+
+// Operand of a backward product: element (r, k) of an R x K matrix.
+struct BwOp {
+  const void* p = nullptr;
+  int64_t estride = 0;          // elements per problem (expert)
+  int64_t ld = 0;
+  int f32 = 0;                  // fp32 source (else bf16)
+  int kmajor = 1;               // 1: (r, k) at src(r)*ld + k; 0: at src(k)*ld + r
+  const int32_t* gather = nullptr;  // src(i) = gather[i] / gk
+  int gk = 1;
+  const float* scale = nullptr;     // times scale[gather[i]] (or scale[i])
+  int lo = 0;                   // bf16 products: the residual v - bf16(v) of each value
+};
+enum { BW_POS = 0, BW_WGT = 1, BW_PLAIN = 2 };
+enum { BW_EPI_NONE = 0, BW_EPI_RELU = 1, BW_EPI_SWIGLU = 2 };
+struct BwGemm {
+  int mode = BW_PLAIN;
+  int epi = BW_EPI_NONE;
+  BwOp a, b;          // product 0 (and the SwiGLU b-factor's A operand)
+  BwOp a1, b1;        // product 1 of the hidden epilogue (dY, W2^T)
+  BwOp b3;            // product 2 of the SwiGLU epilogue (X, W3)
+  // further operand pairs added to product 0 over the same K range (plain
+  // products): a second table, or the low halves of fp32 operands
+  BwOp sa[3], sb[3];
+  int nextra = 0;
+  int64_t M = 0, N = 0, K = 0;
+  int64_t kchunk = 0;           // PLAIN: K per chunk (grid covers the chunks)
+  const int32_t* offsets = nullptr;  // [E+1]
+  const int32_t* tiles = nullptr;    // POS: [E+1] row tiles of bw_tile_rows()
+  int E = 0;
+  void* C = nullptr;            // plain: output; hidden: Hid [A][N]
+  void* C2 = nullptr;           // hidden: dP (ReLU) or dA (SwiGLU)
+  void* C3 = nullptr;           // SwiGLU: dB
+  int c_f32 = 1;
+  int64_t ldc = 0, c_estride = 0, c_chunk = 0;
+  int nrow = 0, ncol = 0;       // set by the launcher
+};
+int bw_tile_rows();
+hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s);
+
 }  // namespace moe
