@@ -38,7 +38,7 @@ EXPERT_TRAFFIC = {
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "c93c9c32c791d4637c8b6187420051c6ef14f8ecfd5a1d2e544124fc6c3ced43",
+    "sources_sha256": "95b6d549653b46f36106f5e50c500bbbfcae82e87044ee1065626a73ec9d2c4a",
     "fetch_kib": 288812.2, "fetch_scale": 524288.0 / 262156.0,
     "write_kib": 32768.0, "write_scale": 524288.0 / 524288.0,
 }
