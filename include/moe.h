@@ -300,7 +300,8 @@ size_t moe_backward_workspace_size(const moe_config* cfg);
  * are optional for the gate and not used for the experts, whose unpacked
  * w1 / w2 / w3 are required), noise (eps, when noisy) and `saved` are the
  * forward's inputs and saved tensors; dy [T][d] is in the cfg dtype.
- * Returns MOE_ERR_UNSUPPORTED for the hierarchy.  bf16: products on MFMA
+ * Returns MOE_ERR_UNSUPPORTED for the hierarchy, and for fp32 layers whose
+ * d_model or d_hidden is not a multiple of 4.  bf16: products on MFMA
  * with fp32 accumulation; fp32 operands (score gradients) and gate-scaled
  * output gradients are rounded to bf16 as they enter a product, the hidden
  * activation and its gradients are rounded to bf16 between products. */

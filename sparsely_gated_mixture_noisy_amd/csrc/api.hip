@@ -428,7 +428,7 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
 
 struct BwLayout {
   size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, hid, dp, db, dxs, part_g,
-      part_n;
+      part_n, xs, dys;
   size_t total;
   int nblk, nchunk;
   int64_t kchunk;
@@ -471,27 +471,24 @@ BwLayout bw_layout(const moe_config* c) {
   L.dxs = take(4 * (size_t)A * d);
   L.part_g = take(4 * (size_t)L.nchunk * E * d);
   L.part_n = take(c->noisy ? 4 * (size_t)L.nchunk * E * d : 0);
+  L.xs = take(es * (size_t)A * d);
+  L.dys = take(es * (size_t)A * d);
   L.total = o;
   return L;
 }
 
-BwOp op_rows(const void* ptr, int64_t ld, bool f32, const int32_t* gather = nullptr, int gk = 1,
-             const float* scale = nullptr) {
+// Operands: rows (element (r, k) at r*ld + k) or columns (at k*ld + r).
+BwOp op_rows(const void* ptr, int64_t ld, bool f32) {
   BwOp o;
   o.p = ptr;
   o.ld = ld;
-  o.f32 = f32 ? 1 : 0;
-  o.kmajor = 1;
-  o.gather = gather;
-  o.gk = gk;
-  o.scale = scale;
+  o.kind = f32 ? BW_KF : BW_KB;
   return o;
 }
 
-BwOp op_cols(const void* ptr, int64_t ld, bool f32, const int32_t* gather = nullptr, int gk = 1,
-             const float* scale = nullptr) {
-  BwOp o = op_rows(ptr, ld, f32, gather, gk, scale);
-  o.kmajor = 0;
+BwOp op_cols(const void* ptr, int64_t ld, bool f32) {
+  BwOp o = op_rows(ptr, ld, f32);
+  o.kind = f32 ? BW_TF : BW_TB;
   return o;
 }
 
@@ -505,10 +502,19 @@ BwOp low_half(BwOp o) {
   return o;
 }
 
+// a product with one operand pair; add_pair appends pairs summed into it
+BwGemm product(const BwOp& a, const BwOp& b) {
+  BwGemm q;
+  q.a[0] = a;
+  q.b[0] = b;
+  q.npair = 1;
+  return q;
+}
+
 void add_pair(BwGemm& q, const BwOp& a, const BwOp& b) {
-  q.sa[q.nextra] = a;
-  q.sb[q.nextra] = b;
-  ++q.nextra;
+  q.a[q.npair] = a;
+  q.b[q.npair] = b;
+  ++q.npair;
 }
 
 moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, const moe_params* p,
@@ -574,12 +580,10 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   // 4. gate-table products
   float* dxg = at<float>(ws, L.dxg);
   if (T > 0) {
-    BwGemm q;
+    BwGemm q = product(op_rows(dclean, E, true), op_cols(p->w_gate, d, f32));
     q.mode = BW_PLAIN;
-    q.a = op_rows(dclean, E, true);
-    q.b = op_cols(p->w_gate, d, f32);
     // bf16 products carry the fp32 score gradients as hi + lo halves
-    if (bf16) add_pair(q, low_half(q.a), q.b);
+    if (bf16) add_pair(q, low_half(q.a[0]), q.b[0]);
     if (noisy) {
       add_pair(q, op_rows(draw, E, true), op_cols(p->w_noise, d, f32));
       if (bf16) add_pair(q, low_half(op_rows(draw, E, true)), op_cols(p->w_noise, d, f32));
@@ -598,11 +602,9 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     void* out = tab == 0 ? g->dw_gate : g->dw_noise;
     if (!out) continue;
     float* part = at<float>(ws, tab == 0 ? L.part_g : L.part_n);
-    BwGemm q;
+    BwGemm q = product(op_cols(tab == 0 ? dclean : draw, E, true), op_cols(x, d, f32));
     q.mode = BW_PLAIN;
-    q.a = op_cols(tab == 0 ? dclean : draw, E, true);
-    q.b = op_cols(x, d, f32);
-    if (bf16) add_pair(q, low_half(q.a), q.b);
+    if (bf16) add_pair(q, low_half(q.a[0]), q.b[0]);
     q.M = E;
     q.N = d;
     q.K = T;
@@ -622,20 +624,27 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   void* db = sw ? at<void>(ws, L.db) : nullptr;
   float* dxs = at<float>(ws, L.dxs);
   const int64_t hd = (int64_t)h * d;
+  // the routed rows of x and the gate-scaled output gradients, in expert order
+  void* xs = at<void>(ws, L.xs);
+  void* dys = at<void>(ws, L.dys);
+  if (A > 0) {
+    MOE_TRY(hip_status(launch_bw_gather_rows(x, sv->perm, k, nullptr, A, d, bf16, xs, s),
+                       "backward gather x"));
+    MOE_TRY(hip_status(launch_bw_gather_rows(dy, sv->perm, k, sv->topk_gate, A, d, bf16, dys, s),
+                       "backward gather dy"));
+  }
   if (A > 0) {
     int32_t* tiles = at<int32_t>(ws, L.tiles);
     MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, s),
                        "backward tiles"));
     const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
     // hidden layer recomputed with its gradient
-    BwGemm q;
+    BwGemm q = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
     q.mode = BW_POS;
     q.epi = sw ? BW_EPI_SWIGLU : BW_EPI_RELU;
-    q.a = op_rows(x, d, f32, sv->perm, k);
-    q.b = per_expert(op_rows(p->w1, d, f32), hd);
-    q.a1 = op_rows(dy, d, f32, sv->perm, k, sv->topk_gate);
-    q.b1 = per_expert(op_cols(p->w2, h, f32), hd);
-    if (sw) q.b3 = per_expert(op_rows(p->w3, d, f32), hd);
+    q.a[1] = op_rows(dys, d, f32);
+    q.b[1] = per_expert(op_cols(p->w2, h, f32), hd);
+    if (sw) q.b[2] = per_expert(op_rows(p->w3, d, f32), hd);
     q.M = A;
     q.N = h;
     q.K = d;
@@ -648,10 +657,8 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
                        "backward hidden"));
     // dX = dP W1 (+ dB W3), per routed row
-    BwGemm r;
+    BwGemm r = product(op_rows(dp, h, f32), per_expert(op_cols(p->w1, d, f32), hd));
     r.mode = BW_POS;
-    r.a = op_rows(dp, h, f32);
-    r.b = per_expert(op_cols(p->w1, d, f32), hd);
     if (sw) add_pair(r, op_rows(db, h, f32), per_expert(op_cols(p->w3, d, f32), hd));
     r.M = A;
     r.N = d;
@@ -668,10 +675,8 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   // table gradients, one problem per expert over its rows (zero without rows)
   auto wgrad = [&](void* out, BwOp a, BwOp b, int64_t M, int64_t N, const char* what) {
     if (!out) return MOE_OK;
-    BwGemm q;
+    BwGemm q = product(a, b);
     q.mode = BW_WGT;
-    q.a = a;
-    q.b = b;
     q.M = M;
     q.N = N;
     q.offsets = sv->offsets;
@@ -683,13 +688,9 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     const int64_t grid = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
     return hip_status(launch_bw_gemm(q, bf16, grid, s), what);
   };
-  MOE_TRY(wgrad(g->dw1, op_cols(dp, h, f32), op_cols(x, d, f32, sv->perm, k), h, d,
-                "backward dw1"));
-  if (sw)
-    MOE_TRY(wgrad(g->dw3, op_cols(db, h, f32), op_cols(x, d, f32, sv->perm, k), h, d,
-                  "backward dw3"));
-  MOE_TRY(wgrad(g->dw2, op_cols(dy, d, f32, sv->perm, k, sv->topk_gate), op_cols(hid, h, f32), d,
-                h, "backward dw2"));
+  MOE_TRY(wgrad(g->dw1, op_cols(dp, h, f32), op_cols(xs, d, f32), h, d, "backward dw1"));
+  if (sw) MOE_TRY(wgrad(g->dw3, op_cols(db, h, f32), op_cols(xs, d, f32), h, d, "backward dw3"));
+  MOE_TRY(wgrad(g->dw2, op_cols(dys, d, f32), op_cols(hid, h, f32), d, h, "backward dw2"));
   // 6. dx
   if (T > 0)
     MOE_TRY(hip_status(launch_bw_assemble_dx(dxg, dxs, sv->inv, T, k, d, bf16, g->dx, s),
@@ -945,6 +946,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* 
     if (ws_bytes < L.total)
       return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
   }
+  if (cfg->dtype == MOE_F32 && (cfg->d_model % 4 != 0 || cfg->d_hidden % 4 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "the fp32 backward pass needs d_model and d_hidden multiples of 4");
   if (bw_gate_lds_bytes(cfg->dtype == MOE_BF16, cfg->d_model, cfg->n_experts) > 150 * 1024)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts / d_model too large for the backward gate tile");
   MOE_TRY(do_backward(cfg, L, x, p, noise, sv, dy, w_importance, w_load, g, ws,

@@ -94,7 +94,29 @@ __global__ __launch_bounds__(256) void bw_gate_out_kernel(BwGateOutArgs a) {
       const int64_t p = a.inv[t * a.k + s];
       const T* yr = ys + p * a.d;
       float acc = 0.f;
-      for (int c = lane; c < a.d; c += 64) acc = fmaf(Elem<T>::load(dy, c), Elem<T>::load(yr, c), acc);
+      if ((a.d & 3) == 0) {
+        // four elements per lane and step: 8-byte (bf16) or 16-byte (fp32) loads
+        for (int c = lane * 4; c < a.d; c += 256) {
+          float u[4], v[4];
+          if constexpr (sizeof(T) == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(dy + c);
+            const uint2 y = *reinterpret_cast<const uint2*>(yr + c);
+            u[0] = __uint_as_float(x.x << 16); u[1] = __uint_as_float(x.x & 0xffff0000u);
+            u[2] = __uint_as_float(x.y << 16); u[3] = __uint_as_float(x.y & 0xffff0000u);
+            v[0] = __uint_as_float(y.x << 16); v[1] = __uint_as_float(y.x & 0xffff0000u);
+            v[2] = __uint_as_float(y.y << 16); v[3] = __uint_as_float(y.y & 0xffff0000u);
+          } else {
+            const float4 x = *reinterpret_cast<const float4*>(dy + c);
+            const float4 y = *reinterpret_cast<const float4*>(yr + c);
+            u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
+            v[0] = y.x; v[1] = y.y; v[2] = y.z; v[3] = y.w;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = fmaf(u[j], v[j], acc);
+        }
+      } else {
+        for (int c = lane; c < a.d; c += 64) acc = fmaf(Elem<T>::load(dy, c), Elem<T>::load(yr, c), acc);
+      }
       dg[s] = wave_sum(acc);
       if (a.dimp) dg[s] += a.dimp[a.idx[t * a.k + s]];
       g[s] = a.gate[t * a.k + s];
@@ -363,14 +385,24 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
   }
 }
 
-// dbias[e] = sum over 32-token blocks of the partials, in block order
-__global__ __launch_bounds__(256) void bw_sum_rows_kernel(const float* part, int64_t nrow,
-                                                          int64_t ncol, float* out) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= ncol) return;
+// out[c] = sum over rows r of part[r][c]: 64 columns per workgroup, wave w
+// sums rows w, w+16, ... in order, then the 16 wave sums are added in wave
+// order.
+__global__ __launch_bounds__(1024) void bw_sum_rows_kernel(const float* part, int64_t nrow,
+                                                           int64_t ncol, float* out) {
+  __shared__ float ws[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int64_t r = 0; r < nrow; ++r) s += part[r * ncol + c];
-  out[c] = s;
+  if (c < ncol)
+    for (int64_t r = w; r < nrow; r += 16) s += part[r * ncol + c];
+  ws[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && c < ncol) {
+    float t = 0.f;
+    for (int i = 0; i < 16; ++i) t += ws[i][lane];
+    out[c] = t;
+  }
 }
 
 // out[i] = cast(sum over chunks of part[chunk][i]) in chunk order
@@ -384,18 +416,58 @@ __global__ __launch_bounds__(256) void bw_sum_chunks_kernel(const float* part, i
   Elem<TO>::store(out, i, s);
 }
 
-// dx[t][c] = dx_gate[t][c] + sum_s dxs[inv[t*k+s]][c], slots in order
+// out[p][c] = src[perm[p] / k][c] (times scale[perm[p]] when scale is set),
+// rounded to the layer's type: the routed rows in expert order, 8 elements
+// (bf16) or 4 (fp32) per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void bw_gather_rows_kernel(const T* src, const int32_t* perm,
+                                                             int k, const float* scale, int64_t A,
+                                                             int d, T* out) {
+  constexpr int V = sizeof(T) == 2 ? 8 : 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = d / V;
+  if (i >= A * per) return;
+  const int64_t p = i / per;
+  const int c = (int)(i % per) * V;
+  const int a = perm[p];
+  const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)(a / k) * d + c);
+  u32x4 o = v;
+  if (scale) {
+    const float sc = scale[a];
+    if constexpr (V == 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = cvt_pk_bf16(__uint_as_float(v[j] << 16) * sc, __uint_as_float(v[j] & 0xffff0000u) * sc);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = __float_as_uint(__uint_as_float(v[j]) * sc);
+    }
+  }
+  *reinterpret_cast<u32x4*>(out + p * d + c) = o;
+}
+
+// dx[t][c] = dx_gate[t][c] + sum_s dxs[inv[t*k+s]][c], slots in order; four
+// columns per thread (d % 4 == 0)
 template <typename TO>
 __global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, const float* dxs,
                                                              const int32_t* inv, int64_t T, int k,
                                                              int d, TO* dx) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= T * d) return;
   const int64_t t = i / d;
   const int c = (int)(i % d);
-  float v = dxg[i];
-  for (int s = 0; s < k; ++s) v += dxs[(int64_t)inv[t * k + s] * d + c];
-  Elem<TO>::store(dx, i, v);
+  float4 v = *reinterpret_cast<const float4*>(dxg + i);
+  for (int s = 0; s < k; ++s) {
+    const float4 u = *reinterpret_cast<const float4*>(dxs + (int64_t)inv[t * k + s] * d + c);
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+  Elem<TO>::store(dx, i, v.x);
+  Elem<TO>::store(dx, i + 1, v.y);
+  Elem<TO>::store(dx, i + 2, v.z);
+  Elem<TO>::store(dx, i + 3, v.w);
 }
 
 // ---------------------------------------------------------------------------
@@ -410,128 +482,179 @@ __global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, c
 //   WGT   M, N fixed per expert, k runs over the positions of expert e
 //   PLAIN one problem; grid = row tiles x column tiles x K chunks
 // ---------------------------------------------------------------------------
-constexpr int BG_BM = 128, BG_BN = 128, BG_BK = 32, BG_LD = BG_BK + 8;
+constexpr int BG_BM = 128, BG_BN = 128;
 
-__device__ __forceinline__ int bw_src(const BwOp& o, int64_t i) {
-  return o.gather ? o.gather[i] / o.gk : (int)i;
-}
-__device__ __forceinline__ float bw_scale(const BwOp& o, int64_t i) {
-  return o.scale ? o.scale[o.gather ? o.gather[i] : i] : 1.0f;
+__device__ __forceinline__ bool bw_kmajor(const BwOp& o) {
+  return o.kind == BW_KB || o.kind == BW_KF;
 }
 __device__ __forceinline__ float bw_elem(const BwOp& o, int e, int64_t r, int64_t k) {
-  const int64_t base = (int64_t)e * o.estride;
-  int64_t off;
-  float s;
-  if (o.kmajor) {
-    off = base + (int64_t)bw_src(o, r) * o.ld + k;
-    s = bw_scale(o, r);
-  } else {
-    off = base + (int64_t)bw_src(o, k) * o.ld + r;
-    s = bw_scale(o, k);
-  }
-  const float v = o.f32 ? ((const float*)o.p)[off] : bf16_to_f32(((const bf16_t*)o.p)[off]);
-  return v * s;
+  const int64_t off = (int64_t)e * o.estride + (bw_kmajor(o) ? r * o.ld + k : k * o.ld + r);
+  const bool f32 = o.kind == BW_KF || o.kind == BW_TF;
+  return f32 ? ((const float*)o.p)[off] : bf16_to_f32(((const bf16_t*)o.p)[off]);
 }
 
 // The part of v an operand carries into a bf16 product: v itself (rounded to
 // bf16 by the caller), or with `lo` the residual v - bf16(v), exact in fp32,
 // so that a hi pass and a lo pass together carry about 16 significant bits.
-__device__ __forceinline__ float bw_part(const BwOp& o, float v) {
-  if (!o.lo) return v;
+__device__ __forceinline__ float bw_part(int lo, float v) {
+  if (!lo) return v;
   const uint32_t hi = cvt_pk_bf16(v, 0.f) << 16;
   return v - __uint_as_float(hi);
 }
 
-// Fill the LDS tile S[BG_BM][BG_LD] with rows r0 .. r0+127 (valid below R),
-// k = k0 .. k0+31 (valid below K) of operand o, as bf16; 256 threads.
-__device__ __forceinline__ void bw_fill(const BwOp& o, int e, int64_t r0, int64_t R, int64_t k0,
-                                        int64_t K, bf16_t (*S)[BG_LD]) {
-  const int tid = threadIdx.x;
-  if (o.kmajor) {
-    // two 8-element k chunks per thread: rows tid/4 and +64, chunk (tid%4)*8
+// An LDS operand tile: 128 rows of BK bf16 k values (+8 of padding).
+template <int BK>
+using BwTileT = bf16_t[BG_BM][BK + 8];
+
+// Column of element (row, k) in a tile.  64-wide slices swap their 16-byte
+// chunks by row, chunk ^ ((row >> 4) & 7): the fragment reads of the MFMAs
+// stay free of bank conflicts and the 4-row pieces written by the transposing
+// loader conflict 2-way instead of 8-way.
+template <int BK>
+__device__ __forceinline__ int bw_col(int row, int k) {
+  if constexpr (BK == 64) return (((k >> 3) ^ ((row >> 4) & 7)) << 3) | (k & 7);
+  return k;
+}
+
+// Loaders of one K slice (BK) of 128 rows of an operand, by kind: load()
+// issues the global reads into registers (one slice ahead), put() writes them
+// to an LDS tile as bf16 [row][k].  Thread t covers
+//   KB, KF: 16-byte k pieces: rows t/(BK/8) + (2048/BK) i, k = (t%(BK/8))*8 .. +7
+//   TB, TF: 4-row pieces: rows (t%32)*4 .. +3, k = (t/32)*4 + 32 j .. +3
+template <int KIND, int BK> struct BwLd;
+
+template <int BK> struct BwLd<BW_KB, BK> {
+  static constexpr int CPR = BK / 8, NI = BK / 16;  // pieces per row, per thread
+  struct Raw { u32x4 v[NI]; };
+  static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
+                                              int64_t k0, int64_t K, Raw& raw) {
+    const int tid = threadIdx.x;
+    const bf16_t* p = (const bf16_t*)o.p + (int64_t)e * o.estride;
+    const int64_t k = k0 + (tid % CPR) * 8;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t r = r0 + tid / CPR + (256 / CPR) * i;
+      raw.v[i] = (r < R && k < K) ? *reinterpret_cast<const u32x4*>(p + r * o.ld + k)
+                                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  static __device__ __forceinline__ void put(const BwOp&, const Raw& raw, BwTileT<BK>& S) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = tid / CPR + (256 / CPR) * i;
+      *reinterpret_cast<u32x4*>(&S[row][bw_col<BK>(row, (tid % CPR) * 8)]) = raw.v[i];
+    }
+  }
+};
+
+template <int BK> struct BwLd<BW_TB, BK> {
+  static constexpr int NJ = BK / 32;  // 4-k groups per thread
+  struct Raw { uint2 v[NJ][4]; };
+  static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
+                                              int64_t k0, int64_t K, Raw& raw) {
+    const int tid = threadIdx.x;
+    const bf16_t* p = (const bf16_t*)o.p + (int64_t)e * o.estride;
+    const int64_t r = r0 + (tid & 31) * 4;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t k = k0 + (tid >> 5) * 4 + 32 * jj + j;
+        raw.v[jj][j] = (r < R && k < K) ? *reinterpret_cast<const uint2*>(p + k * o.ld + r)
+                                        : uint2{0u, 0u};
+      }
+  }
+  static __device__ __forceinline__ void put(const BwOp&, const Raw& raw, BwTileT<BK>& S) {
+    const int tid = threadIdx.x;
+    const int rr = (tid & 31) * 4;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int kq = (tid >> 5) * 4 + 32 * jj;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // row q of the four 4-row pieces: its bf16 half of each piece
+        const int wd = q >> 1, sh = (q & 1) * 16;
+        uint32_t a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = ((wd ? raw.v[jj][j].y : raw.v[jj][j].x) >> sh) & 0xffffu;
+        *reinterpret_cast<uint2*>(&S[rr + q][bw_col<BK>(rr + q, kq)]) =
+            uint2{a[0] | (a[1] << 16), a[2] | (a[3] << 16)};
+      }
+    }
+  }
+};
+
+template <int BK> struct BwLd<BW_KF, BK> {
+  static_assert(BK == 32, "fp32 operands use 32-wide slices");
+  struct Raw { float v[2][8]; };
+  static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
+                                              int64_t k0, int64_t K, Raw& raw) {
+    const int tid = threadIdx.x;
+    const float* p = (const float*)o.p + (int64_t)e * o.estride;
+    const int64_t k = k0 + (tid & 3) * 8;
+    const bool vec = (o.ld & 3) == 0 && k + 8 <= K;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int rr = (tid >> 2) + 64 * i, kc = (tid & 3) * 8;
-      const int64_t r = r0 + rr, k = k0 + kc;
-      u32x4 out = {0u, 0u, 0u, 0u};
-      if (r < R && k < K) {
-        const int64_t base = (int64_t)e * o.estride + (int64_t)bw_src(o, r) * o.ld;
-        const float s = bw_scale(o, r);
-        float v[8];
-        // whole 16-byte (bf16) or 2 x 16-byte (fp32) pieces when the row
-        // stride keeps them aligned
-        if (k + 8 <= K && !o.f32 && !o.scale && (o.ld & 7) == 0) {
-          out = *reinterpret_cast<const u32x4*>((const bf16_t*)o.p + base + k);
-        } else {
-          if (k + 8 <= K && o.f32 && (o.ld & 3) == 0) {
-            const float4 a = *reinterpret_cast<const float4*>((const float*)o.p + base + k);
-            const float4 b = *reinterpret_cast<const float4*>((const float*)o.p + base + k + 4);
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-          } else {
+      const int64_t r = r0 + (tid >> 2) + 64 * i;
+      const float* q = p + (r < R ? r : 0) * o.ld + k;
+      if (r < R && vec) {
+        const float4 a = *reinterpret_cast<const float4*>(q);
+        const float4 b = *reinterpret_cast<const float4*>(q + 4);
+        raw.v[i][0] = a.x; raw.v[i][1] = a.y; raw.v[i][2] = a.z; raw.v[i][3] = a.w;
+        raw.v[i][4] = b.x; raw.v[i][5] = b.y; raw.v[i][6] = b.z; raw.v[i][7] = b.w;
+      } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              v[j] = 0.f;
-              if (k + j < K)
-                v[j] = o.f32 ? ((const float*)o.p)[base + k + j]
-                             : bf16_to_f32(((const bf16_t*)o.p)[base + k + j]);
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = bw_part(o, v[j] * s);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) out[j] = cvt_pk_bf16(v[2 * j], v[2 * j + 1]);
-        }
-      }
-      *reinterpret_cast<u32x4*>(&S[rr][kc]) = out;
-    }
-  } else {
-    // two rows x 8 k per thread: rows 2*(tid%64) .. +1, k chunk (tid/64)*8
-    const int rr = (tid & 63) * 2, kc = (tid >> 6) * 8;
-    const int64_t r = r0 + rr;
-    float v0[8], v1[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v0[j] = 0.f;
-      v1[j] = 0.f;
-      const int64_t k = k0 + kc + j;
-      if (k < K && r < R) {
-        const int64_t base = (int64_t)e * o.estride + (int64_t)bw_src(o, k) * o.ld + r;
-        const float s = bw_scale(o, k);
-        if (r + 1 < R && (o.ld & 1) == 0) {
-          // the pair (r, r + 1) in one 8-byte (fp32) or 4-byte (bf16) load
-          if (o.f32) {
-            const float2 a = *reinterpret_cast<const float2*>((const float*)o.p + base);
-            v0[j] = a.x * s;
-            v1[j] = a.y * s;
-          } else {
-            const uint32_t u = *reinterpret_cast<const uint32_t*>((const bf16_t*)o.p + base);
-            v0[j] = __uint_as_float(u << 16) * s;
-            v1[j] = __uint_as_float(u & 0xffff0000u) * s;
-          }
-        } else {
-          v0[j] = (o.f32 ? ((const float*)o.p)[base] : bf16_to_f32(((const bf16_t*)o.p)[base])) * s;
-          if (r + 1 < R)
-            v1[j] = (o.f32 ? ((const float*)o.p)[base + 1]
-                           : bf16_to_f32(((const bf16_t*)o.p)[base + 1])) * s;
-        }
+        for (int j = 0; j < 8; ++j) raw.v[i][j] = (r < R && k + j < K) ? q[j] : 0.f;
       }
     }
-    u32x4 o0, o1;
+  }
+  static __device__ __forceinline__ void put(const BwOp& o, const Raw& raw, BwTileT<BK>& S) {
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v0[j] = bw_part(o, v0[j]);
-      v1[j] = bw_part(o, v1[j]);
+    for (int i = 0; i < 2; ++i) {
+      u32x4 out;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        out[j] = cvt_pk_bf16(bw_part(o.lo, raw.v[i][2 * j]), bw_part(o.lo, raw.v[i][2 * j + 1]));
+      *reinterpret_cast<u32x4*>(&S[(tid >> 2) + 64 * i][(tid & 3) * 8]) = out;
     }
+  }
+};
+
+template <int BK> struct BwLd<BW_TF, BK> {
+  static_assert(BK == 32, "fp32 operands use 32-wide slices");
+  struct Raw { float v[4][4]; };  // [k][row]
+  static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
+                                              int64_t k0, int64_t K, Raw& raw) {
+    const int tid = threadIdx.x;
+    const float* p = (const float*)o.p + (int64_t)e * o.estride;
+    const int64_t r = r0 + (tid & 31) * 4, kq = k0 + (tid >> 5) * 4;
+    const bool vec = (o.ld & 3) == 0 && r + 4 <= R;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      o0[j] = cvt_pk_bf16(v0[2 * j], v0[2 * j + 1]);
-      o1[j] = cvt_pk_bf16(v1[2 * j], v1[2 * j + 1]);
+      const int64_t k = kq + j;
+      const float* q = p + (k < K ? k : 0) * o.ld + r;
+      if (k < K && vec) {
+        const float4 a = *reinterpret_cast<const float4*>(q);
+        raw.v[j][0] = a.x; raw.v[j][1] = a.y; raw.v[j][2] = a.z; raw.v[j][3] = a.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) raw.v[j][c] = (k < K && r + c < R) ? q[c] : 0.f;
+      }
     }
-    *reinterpret_cast<u32x4*>(&S[rr][kc]) = o0;
-    *reinterpret_cast<u32x4*>(&S[rr + 1][kc]) = o1;
   }
-}
+  static __device__ __forceinline__ void put(const BwOp& o, const Raw& raw, BwTileT<BK>& S) {
+    const int tid = threadIdx.x;
+    const int rr = (tid & 31) * 4, kq = (tid >> 5) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t x = cvt_pk_bf16(bw_part(o.lo, raw.v[0][c]), bw_part(o.lo, raw.v[1][c]));
+      const uint32_t y = cvt_pk_bf16(bw_part(o.lo, raw.v[2][c]), bw_part(o.lo, raw.v[3][c]));
+      *reinterpret_cast<uint2*>(&S[rr + c][kq]) = uint2{x, y};
+    }
+  }
+};
 
 // Which problem, rows, columns and K range a workgroup covers.
 struct BwTile {
@@ -616,19 +739,31 @@ __device__ __forceinline__ void bw_hidden_store(const BwGemm& g, int64_t m, int6
   }
 }
 
-// bf16 MFMA product: 128 x 128 tile, four waves of 64 x 64, K in slices of
-// 32 staged through LDS (the next slice's loads in flight during the MFMAs).
-// NPROD products share the tile (the hidden epilogue: 2 for ReLU, 3 for
-// SwiGLU); plain products may add further operand pairs (sa/sb) over the
-// same K range.
-template <int NPROD>
-__global__ __launch_bounds__(256) void bw_gemm_mfma_kernel(BwGemm g) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[NPROD][BG_BM][BG_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[NPROD][BG_BN][BG_LD];
+// LDS bytes of the staged output tile: NOUT tiles of 128 x (128 + pad) of
+// the output type.
+constexpr int BG_CLD_B = BG_BN + 8;   // bf16 row stride
+constexpr int BG_CLD_F = BG_BN + 4;   // fp32 row stride
+
+// bf16 MFMA product: 128 x 128 tile, four waves of 64 x 64, K in slices of BK
+// through two LDS buffers: the global loads of slice s+1 are in flight during
+// the MFMAs of slice s and land in the other buffer afterwards (one barrier
+// per slice).  NPROD products share the tile: plain products (NPROD = 1) sum
+// their npair operand pairs into one accumulator, the hidden epilogue runs 2
+// (ReLU) or 3 (SwiGLU) products.  Operand kinds are template arguments: KA
+// for every A operand, KB0 for the B operands except that of product 1 (KB1).
+// The results go through LDS and leave as 16-byte row pieces.
+template <int NPROD, int KA, int KB0, int KB1, int BK>
+__global__ __launch_bounds__(256, 1) void bw_gemm_mfma_kernel(BwGemm g) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t bw_lds[];
+  using Tile = BwTileT<BK>;
+  Tile* tiles = reinterpret_cast<Tile*>(bw_lds);  // [2 buffers][2 * NPROD operands]
   BwTile t;
   if (!bw_tile_of(g, &t)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1, fr = lane & 31, fk = (lane >> 5) * 8;
+  using LA = BwLd<KA, BK>;
+  using LB0 = BwLd<KB0, BK>;
+  using LB1 = BwLd<KB1, BK>;
   f32x16 acc[NPROD][2][2];
 #pragma unroll
   for (int p = 0; p < NPROD; ++p)
@@ -636,54 +771,172 @@ __global__ __launch_bounds__(256) void bw_gemm_mfma_kernel(BwGemm g) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[p][i][j] = f32x16{};
-  const int nseg = 1 + g.nextra;
-  for (int seg = 0; seg < nseg; ++seg) {
-    for (int64_t k0 = t.k0; k0 < t.K; k0 += BG_BK) {
-      __syncthreads();
-#pragma unroll
-      for (int p = 0; p < NPROD; ++p) {
-        const BwOp& A = seg ? g.sa[seg - 1] : (p == 0 ? g.a : p == 1 ? g.a1 : g.a);
-        const BwOp& B = seg ? g.sb[seg - 1] : (p == 0 ? g.b : p == 1 ? g.b1 : g.b3);
-        bw_fill(A, t.e, t.m0, t.M, k0, t.K, As[p]);
-        bw_fill(B, t.e, t.n0, t.N, k0, t.K, Bs[p]);
+  const int64_t nk = (t.K - t.k0 + BK - 1) / BK;
+  const int nseg = NPROD == 1 ? g.npair : 1;
+  for (int seg = 0; seg < nseg && nk > 0; ++seg) {
+    const BwOp& A0 = g.a[seg];
+    const BwOp& B0 = g.b[seg];
+    const BwOp& A1 = g.a[1];
+    const BwOp& B1 = g.b[1];
+    const BwOp& B2 = g.b[2];
+    typename LA::Raw ra0, ra1;
+    typename LB0::Raw rb0, rb2;
+    typename LB1::Raw rb1;
+    auto load_all = [&](int64_t k0) {
+      LA::load(A0, t.e, t.m0, t.M, k0, t.K, ra0);
+      LB0::load(B0, t.e, t.n0, t.N, k0, t.K, rb0);
+      if constexpr (NPROD >= 2) {
+        LA::load(A1, t.e, t.m0, t.M, k0, t.K, ra1);
+        LB1::load(B1, t.e, t.n0, t.N, k0, t.K, rb1);
       }
-      __syncthreads();
+      if constexpr (NPROD == 3) LB0::load(B2, t.e, t.n0, t.N, k0, t.K, rb2);
+    };
+    auto put_all = [&](Tile* T) {
+      LA::put(A0, ra0, T[0]);
+      LB0::put(B0, rb0, T[1]);
+      if constexpr (NPROD >= 2) {
+        LA::put(A1, ra1, T[2]);
+        LB1::put(B1, rb1, T[3]);
+      }
+      if constexpr (NPROD == 3) LB0::put(B2, rb2, T[5]);
+    };
+    __syncthreads();  // the previous segment's last reads are done
+    load_all(t.k0);
+    put_all(tiles);
+    __syncthreads();
+    for (int64_t s = 0; s < nk; ++s) {
+      const int cur = (int)(s & 1);
+      Tile* T0 = tiles + cur * 2 * NPROD;
+      Tile* T1 = tiles + (cur ^ 1) * 2 * NPROD;
+      const bool more = s + 1 < nk;
+      if (more) load_all(t.k0 + (s + 1) * BK);
 #pragma unroll
-      for (int ks = 0; ks < BG_BK; ks += 16) {
+      for (int ks = 0; ks < BK; ks += 16) {
 #pragma unroll
         for (int p = 0; p < NPROD; ++p) {
+          // product 2 (SwiGLU up) shares product 0's A tile
+          const int ta = p == 2 ? 0 : 2 * p;
           bf16x8 af[2], bf[2];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            af[i] = *reinterpret_cast<const bf16x8*>(&As[p][wm * 64 + i * 32 + fr][ks + fk]);
-            bf[i] = *reinterpret_cast<const bf16x8*>(&Bs[p][wn * 64 + i * 32 + fr][ks + fk]);
+            const int ra = wm * 64 + i * 32 + fr, rb = wn * 64 + i * 32 + fr;
+            af[i] = *reinterpret_cast<const bf16x8*>(&T0[ta][ra][bw_col<BK>(ra, ks + fk)]);
+            bf[i] = *reinterpret_cast<const bf16x8*>(&T0[2 * p + 1][rb][bw_col<BK>(rb, ks + fk)]);
           }
+          // B as the first operand: the accumulators hold C^T, so that a lane
+          // holds four consecutive columns of one row
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[p][i][j] = mfma32(af[i], bf[j], acc[p][i][j]);
+            for (int j = 0; j < 2; ++j) acc[p][i][j] = mfma32(bf[j], af[i], acc[p][i][j]);
         }
+      }
+      if (more) put_all(T1);
+      __syncthreads();
+    }
+  }
+  __syncthreads();  // operand tiles free: the output tiles take their place
+  // accumulator register r of lane l holds C[row l%32][column 8*(r/4) +
+  // 4*(l/32) + r%4] of the wave's (i, j) block: register group g is four
+  // consecutive columns of one row
+  const int erow = lane & 31, ecol = 4 * (lane >> 5);
+  if constexpr (NPROD == 1) {
+    if (g.c_f32) {
+      float (*Cs)[BG_CLD_F] = reinterpret_cast<float (*)[BG_CLD_F]>(bw_lds);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(&Cs[wm * 64 + i * 32 + erow][wn * 64 + j * 32 + 8 * q + ecol]) =
+                float4{acc[0][i][j][4 * q], acc[0][i][j][4 * q + 1], acc[0][i][j][4 * q + 2],
+                       acc[0][i][j][4 * q + 3]};
+      __syncthreads();
+      float* C = (float*)g.C + (int64_t)t.e * g.c_estride + (int64_t)t.chunk * g.c_chunk;
+      for (int c = tid; c < BG_BM * (BG_BN / 4); c += 256) {
+        const int rr = c / (BG_BN / 4), cc = (c % (BG_BN / 4)) * 4;
+        const int64_t m = t.m0 + rr, n = t.n0 + cc;
+        if (m < t.M && n < t.N)
+          *reinterpret_cast<float4*>(C + m * g.ldc + n) = *reinterpret_cast<const float4*>(&Cs[rr][cc]);
+      }
+    } else {
+      bf16_t (*Cs)[BG_CLD_B] = reinterpret_cast<bf16_t (*)[BG_CLD_B]>(bw_lds);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint2*>(&Cs[wm * 64 + i * 32 + erow][wn * 64 + j * 32 + 8 * q + ecol]) =
+                uint2{cvt_pk_bf16(acc[0][i][j][4 * q], acc[0][i][j][4 * q + 1]),
+                      cvt_pk_bf16(acc[0][i][j][4 * q + 2], acc[0][i][j][4 * q + 3])};
+      __syncthreads();
+      bf16_t* C = (bf16_t*)g.C + (int64_t)t.e * g.c_estride + (int64_t)t.chunk * g.c_chunk;
+      for (int c = tid; c < BG_BM * (BG_BN / 8); c += 256) {
+        const int rr = c / (BG_BN / 8), cc = (c % (BG_BN / 8)) * 8;
+        const int64_t m = t.m0 + rr, n = t.n0 + cc;
+        if (m < t.M && n < t.N)
+          *reinterpret_cast<u32x4*>(C + m * g.ldc + n) = *reinterpret_cast<const u32x4*>(&Cs[rr][cc]);
+      }
+    }
+  } else {
+    // Hid, dP (ReLU) or Hid, dA, dB (SwiGLU), each [A][N] bf16
+    constexpr int NOUT = NPROD;
+    bf16_t (*Cs)[BG_BM][BG_CLD_B] = reinterpret_cast<bf16_t (*)[BG_BM][BG_CLD_B]>(bw_lds);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = wm * 64 + i * 32 + erow, cc = wn * 64 + j * 32 + 8 * q + ecol;
+          float o0[4], o1[4], o2[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float a = acc[0][i][j][4 * q + u], dh = acc[1][i][j][4 * q + u];
+            if constexpr (NPROD == 2) {
+              o0[u] = fmaxf(a, 0.f);
+              o1[u] = a > 0.f ? dh : 0.f;
+              o2[u] = 0.f;
+            } else {
+              const float b = acc[2][i][j][4 * q + u];
+              const float sg = 1.0f / (1.0f + expf(-a));
+              const float sl = a * sg;
+              o0[u] = sl * b;
+              o1[u] = dh * b * sg * (1.0f + a * (1.0f - sg));
+              o2[u] = dh * sl;
+            }
+          }
+          *reinterpret_cast<uint2*>(&Cs[0][rr][cc]) =
+              uint2{cvt_pk_bf16(o0[0], o0[1]), cvt_pk_bf16(o0[2], o0[3])};
+          *reinterpret_cast<uint2*>(&Cs[1][rr][cc]) =
+              uint2{cvt_pk_bf16(o1[0], o1[1]), cvt_pk_bf16(o1[2], o1[3])};
+          if constexpr (NOUT == 3)
+            *reinterpret_cast<uint2*>(&Cs[2][rr][cc]) =
+                uint2{cvt_pk_bf16(o2[0], o2[1]), cvt_pk_bf16(o2[2], o2[3])};
+        }
+    __syncthreads();
+    for (int c = tid; c < BG_BM * (BG_BN / 8); c += 256) {
+      const int rr = c / (BG_BN / 8), cc = (c % (BG_BN / 8)) * 8;
+      const int64_t m = t.m0 + rr, n = t.n0 + cc;
+      if (m < t.M && n < t.N) {
+        const int64_t o = m * g.N + n;
+        *reinterpret_cast<u32x4*>((bf16_t*)g.C + o) = *reinterpret_cast<const u32x4*>(&Cs[0][rr][cc]);
+        *reinterpret_cast<u32x4*>((bf16_t*)g.C2 + o) = *reinterpret_cast<const u32x4*>(&Cs[1][rr][cc]);
+        if constexpr (NOUT == 3)
+          *reinterpret_cast<u32x4*>((bf16_t*)g.C3 + o) = *reinterpret_cast<const u32x4*>(&Cs[2][rr][cc]);
       }
     }
   }
-  // accumulator register r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = t.m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t n = t.n0 + wn * 64 + j * 32 + fr;
-        if (m >= t.M || n >= t.N) continue;
-        if constexpr (NPROD == 1) {
-          bw_store(g, t, m, n, acc[0][i][j][r]);
-        } else if constexpr (NPROD == 2) {
-          bw_hidden_store(g, m, n, acc[0][i][j][r], acc[1][i][j][r], 0.f);
-        } else {
-          bw_hidden_store(g, m, n, acc[0][i][j][r], acc[1][i][j][r], acc[2][i][j][r]);
-        }
-      }
+}
+
+template <int NPROD, int BK>
+static size_t bw_gemm_lds() {
+  const size_t ops = sizeof(bf16_t) * 2 * 2 * NPROD * BG_BM * (BK + 8);
+  const size_t outs = NPROD == 1 ? sizeof(float) * BG_BM * BG_CLD_F
+                                 : sizeof(bf16_t) * NPROD * BG_BM * BG_CLD_B;
+  return ops > outs ? ops : outs;
 }
 
 // fp32 products: one thread per output element, plain FMA over k in order.
@@ -696,16 +949,16 @@ __global__ __launch_bounds__(256) void bw_gemm_scalar_kernel(BwGemm g) {
   for (int idx = threadIdx.x; idx < BG_BM * BG_BN; idx += 256) {
     const int64_t m = t.m0 + idx / BG_BN, n = t.n0 + idx % BG_BN;
     if (m >= t.M || n >= t.N) continue;
-    const int nseg = 1 + g.nextra;
+    const int nseg = hidden ? 1 : g.npair;
     float s0 = 0.f, s1 = 0.f, s3 = 0.f;
     for (int seg = 0; seg < nseg; ++seg) {
-      const BwOp& A = seg ? g.sa[seg - 1] : g.a;
-      const BwOp& B = seg ? g.sb[seg - 1] : g.b;
+      const BwOp& A = g.a[seg];
+      const BwOp& B = g.b[seg];
       if (A.lo) continue;  // fp32 products take fp32 operands whole
       for (int64_t k = t.k0; k < t.K; ++k) {
         s0 = fmaf(bw_elem(A, t.e, m, k), bw_elem(B, t.e, n, k), s0);
-        if (hidden) s1 = fmaf(bw_elem(g.a1, t.e, m, k), bw_elem(g.b1, t.e, n, k), s1);
-        if (sw) s3 = fmaf(bw_elem(g.a, t.e, m, k), bw_elem(g.b3, t.e, n, k), s3);
+        if (hidden) s1 = fmaf(bw_elem(g.a[1], t.e, m, k), bw_elem(g.b[1], t.e, n, k), s1);
+        if (sw) s3 = fmaf(bw_elem(g.a[0], t.e, m, k), bw_elem(g.b[2], t.e, n, k), s3);
       }
     }
     if (!hidden) {
@@ -792,7 +1045,7 @@ hipError_t launch_bw_gate(const BwGateArgs& a, bool bf16, hipStream_t s) {
 hipError_t launch_bw_sum_rows(const float* part, int64_t nrow, int64_t ncol, float* out,
                               hipStream_t s) {
   if (ncol == 0) return hipSuccess;
-  hipLaunchKernelGGL(bw_sum_rows_kernel, dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(bw_sum_rows_kernel, dim3((unsigned)((ncol + 63) / 64)), dim3(1024), 0, s,
                      part, nrow, ncol, out);
   return hipGetLastError();
 }
@@ -808,7 +1061,7 @@ hipError_t launch_bw_sum_chunks(const float* part, int nchunk, int64_t n, bool b
 
 hipError_t launch_bw_assemble_dx(const float* dxg, const float* dxs, const int32_t* inv, int64_t T,
                                  int k, int d, bool bf16, void* dx, hipStream_t s) {
-  const int64_t n = T * d;
+  const int64_t n = T * d / 4;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (bf16)
@@ -818,7 +1071,30 @@ hipError_t launch_bw_assemble_dx(const float* dxg, const float* dxs, const int32
   return hipGetLastError();
 }
 
+hipError_t launch_bw_gather_rows(const void* src, const int32_t* perm, int k, const float* scale,
+                                 int64_t A, int d, bool bf16, void* out, hipStream_t s) {
+  const int V = bf16 ? 8 : 4;
+  const int64_t n = A * (d / V);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(bw_gather_rows_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)src, perm, k, scale, A, d, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL(bw_gather_rows_kernel<float>, grid, dim3(256), 0, s, (const float*)src, perm, k, scale, A, d, (float*)out);
+  return hipGetLastError();
+}
+
 int bw_tile_rows() { return BG_BM; }
+
+template <int NPROD, int KA, int KB0, int KB1, int BK>
+static hipError_t launch_bw_mfma(const BwGemm& g, int64_t grid, hipStream_t s) {
+  auto kern = bw_gemm_mfma_kernel<NPROD, KA, KB0, KB1, BK>;
+  const size_t lds = bw_gemm_lds<NPROD, BK>();
+  hipError_t err = bw_set_lds(kern, lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
   g.ncol = (int)((g.N + BG_BN - 1) / BG_BN);
@@ -826,14 +1102,18 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
   if (grid <= 0 || g.ncol == 0) return hipSuccess;
   if (!bf16) {
     hipLaunchKernelGGL(bw_gemm_scalar_kernel, dim3((unsigned)grid), dim3(256), 0, s, g);
-  } else if (g.epi == BW_EPI_NONE) {
-    hipLaunchKernelGGL(bw_gemm_mfma_kernel<1>, dim3((unsigned)grid), dim3(256), 0, s, g);
-  } else if (g.epi == BW_EPI_RELU) {
-    hipLaunchKernelGGL(bw_gemm_mfma_kernel<2>, dim3((unsigned)grid), dim3(256), 0, s, g);
-  } else {
-    hipLaunchKernelGGL(bw_gemm_mfma_kernel<3>, dim3((unsigned)grid), dim3(256), 0, s, g);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  if (g.epi == BW_EPI_RELU) return launch_bw_mfma<2, BW_KB, BW_KB, BW_TB, 64>(g, grid, s);
+  if (g.epi == BW_EPI_SWIGLU) return launch_bw_mfma<3, BW_KB, BW_KB, BW_TB, 32>(g, grid, s);
+  const int ka = g.a[0].kind, kb = g.b[0].kind;
+  if (kb != BW_TB) return hipErrorInvalidValue;
+  switch (ka) {
+    case BW_KB: return launch_bw_mfma<1, BW_KB, BW_TB, BW_TB, 64>(g, grid, s);
+    case BW_TB: return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64>(g, grid, s);
+    case BW_KF: return launch_bw_mfma<1, BW_KF, BW_TB, BW_TB, 32>(g, grid, s);
+    default: return launch_bw_mfma<1, BW_TF, BW_TB, BW_TB, 32>(g, grid, s);
+  }
 }
 
 }  // namespace moe

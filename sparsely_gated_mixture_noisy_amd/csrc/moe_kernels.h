@@ -195,16 +195,16 @@ hipError_t launch_bw_sum_chunks(const float* part, int nchunk, int64_t n, bool b
 hipError_t launch_bw_assemble_dx(const float* dxg, const float* dxs, const int32_t* inv, int64_t T,
                                  int k, int d, bool bf16, void* dx, hipStream_t s);
 
-// Operand of a backward product: element (r, k) of an R x K matrix.
+// Operand of a backward product: element (r, k) of an R x K matrix, for
+// problem (expert) e at p + e*estride + (kind KB/KF: r*ld + k; TB/TF:
+// k*ld + r); B = bf16, F = fp32.  Kinds KB and TB need K % 8 == 0 (KB) and
+// R % 4 == 0 (TB) and ld % 8 == 0.
+enum { BW_KB = 0, BW_TB = 1, BW_KF = 2, BW_TF = 3 };
 struct BwOp {
   const void* p = nullptr;
-  int64_t estride = 0;          // elements per problem (expert)
+  int64_t estride = 0;
   int64_t ld = 0;
-  int f32 = 0;                  // fp32 source (else bf16)
-  int kmajor = 1;               // 1: (r, k) at src(r)*ld + k; 0: at src(k)*ld + r
-  const int32_t* gather = nullptr;  // src(i) = gather[i] / gk
-  int gk = 1;
-  const float* scale = nullptr;     // times scale[gather[i]] (or scale[i])
+  int kind = BW_KB;
   int lo = 0;                   // bf16 products: the residual v - bf16(v) of each value
 };
 enum { BW_POS = 0, BW_WGT = 1, BW_PLAIN = 2 };
@@ -212,13 +212,11 @@ enum { BW_EPI_NONE = 0, BW_EPI_RELU = 1, BW_EPI_SWIGLU = 2 };
 struct BwGemm {
   int mode = BW_PLAIN;
   int epi = BW_EPI_NONE;
-  BwOp a, b;          // product 0 (and the SwiGLU b-factor's A operand)
-  BwOp a1, b1;        // product 1 of the hidden epilogue (dY, W2^T)
-  BwOp b3;            // product 2 of the SwiGLU epilogue (X, W3)
-  // further operand pairs added to product 0 over the same K range (plain
-  // products): a second table, or the low halves of fp32 operands
-  BwOp sa[3], sb[3];
-  int nextra = 0;
+  // plain: C = sum over the npair pairs of a[i] b[i]^T (same kinds for every
+  // pair: a second table, or the low halves of fp32 operands); hidden:
+  // (a[0], b[0]) = (X, W1), (a[1], b[1]) = (dY, W2^T), (a[0], b[2]) = (X, W3)
+  BwOp a[4], b[4];
+  int npair = 1;
   int64_t M = 0, N = 0, K = 0;
   int64_t kchunk = 0;           // PLAIN: K per chunk (grid covers the chunks)
   const int32_t* offsets = nullptr;  // [E+1]
@@ -231,6 +229,9 @@ struct BwGemm {
   int64_t ldc = 0, c_estride = 0, c_chunk = 0;
   int nrow = 0, ncol = 0;       // set by the launcher
 };
+// out[p] = src[perm[p] / k] (times scale[perm[p]]), d % 8 == 0 (bf16) or % 4 (fp32)
+hipError_t launch_bw_gather_rows(const void* src, const int32_t* perm, int k, const float* scale,
+                                 int64_t A, int d, bool bf16, void* out, hipStream_t s);
 int bw_tile_rows();
 hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s);
 
