@@ -157,3 +157,88 @@ def test_backward_rejects_hierarchy_and_missing_inputs():
     with pytest.raises(L.MoEError) as e:
         L.backward(flat, inp["x"], inp, inp, fwd, dy)
     assert e.value.status == L.MOE_ERR_INVALID_ARG
+
+
+def test_backward_flat256_full_size_sampled():
+    """The full paper-shaped layer (8192 tokens, 256 experts, 512 -> 1024 ->
+    512, k = 4, noisy), in the launch configuration the timings use.  The
+    oracle computes, one by one: the table gradients of sampled experts
+    (from those experts' rows only) and the input gradients of sampled
+    tokens (from their own slots; the load-loss and importance gradients
+    need only the per-expert statistics, which the oracle computes over all
+    tokens).  Tokens whose scores around the threshold are within 1e-5 are
+    not sampled, nor experts that hold such a token."""
+    cfg = CONFIGS["flat256"]
+    wi, wl = 1.0, 1.0
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    cpu = {key: (v.to("cpu") if v is not None else None) for key, v in inp.items()}
+    dy = make_upstream(cfg, seed=0, device="cuda")
+    _say("[backward] flat256 full size: forward + backward on the GPU")
+    fwd = L.forward(cfg, inp["x"], inp, inp, wi, wl, balance=True, save=True)
+    g = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
+    torch.cuda.synchronize()
+    _say("[backward] oracle gate and statistics")
+    x = cpu["x"].double().numpy()
+    dyn = dy.to("cpu").double().numpy()
+    gi = oracle.gate(cpu, cfg)
+    T, k, E = cfg.tokens, cfg.top_k, cfg.n_experts
+    idx, gates = gi["idx"], gi["gates"]
+    assert (np_(fwd.topk_idx) == idx).all()
+    counts, offsets, perm, inv = oracle.route(idx, E)
+    imp = oracle.importance(idx, gates, E)
+    load = oracle.load_estimate(gi["clean"], gi["sp"], gi["H"], idx, gi["kth"], gi["k1th"])
+    dimp = wi * oracle.cv_squared_grad(imp)
+    dload = wl * oracle.cv_squared_grad(load)
+    srt = -np.sort(-gi["H"], axis=1)
+    risky = ((srt[:, k - 2:k + 1] - srt[:, k - 1:k + 2]) < GAP).any(axis=1)
+    w1 = cpu["w1"].double().numpy()
+    w2 = cpu["w2"].double().numpy()
+    rng = np.random.default_rng(1)
+
+    # table gradients of sampled experts
+    risky_e = set(idx[risky].reshape(-1).tolist())
+    cand = [e for e in range(E) if e not in risky_e and counts[e] > 0]
+    for e in rng.choice(cand, size=6, replace=False):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        toks = rows // k
+        dY = gates.reshape(-1)[rows][:, None] * dyn[toks]
+        _, dw1, dw2 = oracle.expert_relu_backward(x[toks], w1[e], w2[e], dY)
+        _check(f"dw1[{e}]", g.dw1[e], dw1, RTOL["bf16"], FRO["bf16"])
+        _check(f"dw2[{e}]", g.dw2[e], dw2, RTOL["bf16"], FRO["bf16"])
+
+    # input gradients of sampled tokens: expert part + gate part
+    jk, jk1 = oracle.rank_experts(gi["H"], k)
+    wg = cpu["w_gate"].double().numpy()
+    wn = cpu["w_noise"].double().numpy()
+    eps = cpu["eps"].double().numpy()
+    toks = rng.choice(np.nonzero(~risky)[0], size=24, replace=False)
+    dx_ref = np.zeros((toks.size, cfg.d_model))
+    for n, t in enumerate(toks):
+        xt = x[t:t + 1]
+        dg = np.zeros(k)
+        dxe = np.zeros(cfg.d_model)
+        for s in range(k):
+            e = idx[t, s]
+            y_e = oracle.expert_relu(xt, w1[e], w2[e])[0]
+            dg[s] = y_e @ dyn[t] + dimp[e]
+            dX, _, _ = oracle.expert_relu_backward(xt, w1[e], w2[e], gates[t, s] * dyn[t:t + 1])
+            dxe += dX[0]
+        dH = np.zeros(E)
+        dH[idx[t]] = gates[t] * (dg - gates[t] @ dg)
+        kept = np.zeros(E, dtype=bool)
+        kept[idx[t]] = True
+        theta = np.where(kept, gi["k1th"][t], gi["kth"][t])
+        sp = gi["sp"][t]
+        z = (gi["clean"][t] - theta) / sp
+        dz = dload * oracle.normal_pdf(z)
+        dclean = dz / sp
+        dsp = -dz * z / sp
+        dtheta = -dz / sp
+        dH[jk[t]] += dtheta[~kept].sum()
+        dH[jk1[t]] += dtheta[kept].sum()
+        dclean = dclean + dH
+        dsp = dsp + dH * eps[t]
+        draw = dsp * oracle.sigmoid(xt[0] @ wn.T)
+        dx_ref[n] = dxe + dclean @ wg + draw @ wn
+    got = np_(g.dx)[toks]
+    _check("dx[sampled]", got, dx_ref, RTOL["bf16"], FRO["bf16"])
