@@ -157,6 +157,54 @@ def expert_work(cfg, counts):
     return flops, wbytes + abytes, hit
 
 
+def backward_work(cfg, hit):
+    """Algorithmic flops and HBM bytes of one backward pass: the hidden layer
+    recomputed and four more products per routed row (dHid, dX and the two
+    table gradients); the tables of every hit expert read once and their
+    gradients written once, x, dy, the saved expert outputs and the noise
+    read once, dx written once (gate tables and index arrays are small)."""
+    A = cfg.tokens * cfg.top_k
+    el = 2 if cfg.dtype == "bf16" else 4
+    mats = 3 if cfg.ffn == "swiglu" else 2
+    prods = 7 if cfg.ffn == "swiglu" else 5
+    flops = 2.0 * A * cfg.d_model * cfg.d_hidden * prods
+    tables = 2 * hit * mats * cfg.d_model * cfg.d_hidden * el
+    acts = (3 * cfg.tokens + A) * cfg.d_model * el
+    noise = cfg.tokens * cfg.n_experts * 4 if cfg.noisy else 0
+    return flops, tables + acts + noise
+
+
+def backward_line(L, cfg, inp, fwd_ms, steps, warmup, hit):
+    """moe_backward timed on the forward's saved tensors (HIP events around
+    `steps` calls after `warmup`), with the gradients of sum(dy * y) + CV^2
+    losses of weight 1 for a seeded dy."""
+    import torch
+    from sparsely_gated_mixture_noisy_amd.inputs import make_upstream
+    dy = make_upstream(cfg, seed=0, device="cuda")
+    saved = L.Forward(cfg, inp["x"], inp, inp, balance=True, save=True)()
+    bwd = L.Backward(cfg, inp["x"], inp, inp, saved, dy)
+    for _ in range(max(1, warmup)):
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / steps
+    print(f"[bench] moe_backward {bms:.4f} ms/step", file=sys.stderr, flush=True)
+    flops, nbytes = backward_work(cfg, hit)
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    return {"ms_per_step": bms, "tokens_per_s": cfg.tokens / (bms * 1e-3),
+            "train_step_tokens_per_s": cfg.tokens / ((bms + fwd_ms) * 1e-3),
+            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "flops": flops, "mfma_frac": flops / (bms * 1e-3) / 1e12 / peak_tf,
+            "note": "gradients of x, gate tables, bias and expert tables; "
+                    "forward tensors saved by moe_forward"}
+
+
 def cpu_baseline(cfg, inp, budget_s):
     """The oracle, as it is, on the first S tokens of the same inputs."""
     import numpy as np
@@ -205,6 +253,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement (reported beside the forward)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer (device to device) a few times and exit: "
                          "the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -302,6 +352,9 @@ def main():
         res["expert_mfma_frac"] = tflops / peak_tf
         res["experts_hit"] = hit
     res["counts_max_over_mean"] = float(counts.max() / max(counts.mean(), 1e-9))
+    if not args.no_backward and not cfg.hierarchical:
+        res["backward"] = backward_line(L, cfg, inp, fwd_ms=ms, steps=args.steps,
+                                        warmup=args.warmup, hit=hit)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(res), flush=True)
