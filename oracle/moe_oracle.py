@@ -220,27 +220,34 @@ def hier_gate(x, w_gate_p, w_noise_p, eps_p, w_gate, w_noise, eps,
 # Routing: group the (token, slot) pairs by expert  [Paper card, section 瓶颈]
 # ---------------------------------------------------------------------------
 
-def route(idx: np.ndarray, n_experts: int):
+def route(idx: np.ndarray, n_experts: int, capacity: int = 0):
     """Stable grouping of the T*k (token, slot) assignments by expert.
 
-    counts[e]  number of assignments to expert e;
+    counts[e]  number of assignments to expert e (kept ones, with a capacity);
     offsets    exclusive prefix sum of counts, length E+1;
     perm[p]    the assignment t*k+s placed at position p: expert-contiguous,
-               tokens ascending inside each expert;
-    inv[t*k+s] the position p of that assignment (inverse of perm).
+               tokens ascending inside each expert (length offsets[E]);
+    inv[t*k+s] the position p of that assignment (inverse of perm), or -1.
+
+    With capacity > 0 an expert keeps only the first `capacity` assignments
+    that reach it in token order; the later ones are dropped (inv = -1).
+    [Mixtral page, section 核心概念: a per-expert buffer limit, overflow dropped]
     """
     T, k = idx.shape
     counts = np.zeros(n_experts, dtype=np.int64)
     for e in idx.reshape(-1):
-        counts[e] += 1
+        if capacity <= 0 or counts[e] < capacity:
+            counts[e] += 1
     offsets = np.zeros(n_experts + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
     fill = offsets[:-1].copy()
-    perm = np.zeros(T * k, dtype=np.int64)
-    inv = np.zeros(T * k, dtype=np.int64)
+    perm = np.zeros(int(offsets[-1]), dtype=np.int64)
+    inv = np.full(T * k, -1, dtype=np.int64)
     for t in range(T):
         for s in range(k):
             e = idx[t, s]
+            if fill[e] == offsets[e + 1]:
+                continue  # expert e is full
             p = fill[e]
             fill[e] += 1
             perm[p] = t * k + s
@@ -294,13 +301,16 @@ def run_experts(x, perm, offsets, k, w1, w2, w3=None) -> np.ndarray:
 
 def combine(y_sorted, inv, gates) -> np.ndarray:
     """y_t = sum over slots s of gate[t,s] * y_sorted[inv[t*k+s]], slots in
-    ascending order.  [MoE lesson, section 二: y = sum_i G(x)_i E_i(x)]"""
+    ascending order; a slot dropped by a capacity (inv = -1) adds nothing.
+    [MoE lesson, section 二: y = sum_i G(x)_i E_i(x)]"""
     gates = np.asarray(gates, dtype=np.float64)
     T, k = gates.shape
     d = y_sorted.shape[1] if y_sorted.ndim == 2 else 0
     y = np.zeros((T, d))
+    inv2 = np.asarray(inv).reshape(T, k)
     for s in range(k):
-        y += gates[:, s:s + 1] * y_sorted[inv.reshape(T, k)[:, s]]
+        kept = inv2[:, s] >= 0
+        y[kept] += gates[kept, s:s + 1] * y_sorted[inv2[kept, s]]
     return y
 
 
@@ -379,9 +389,12 @@ def forward(inp: Dict, cfg, w_importance=1.0, w_load=1.0,
     Returns every intermediate the HIP path exposes."""
     g = gate(inp, cfg)
     idx, gates = g["idx"], g["gates"]
-    counts, offsets, perm, inv = route(idx, cfg.n_experts)
+    capacity = getattr(cfg, "capacity", 0)
+    counts, offsets, perm, inv = route(idx, cfg.n_experts, capacity)
     out = dict(idx=idx, gates=gates, margin=g["margin"], counts=counts,
                offsets=offsets, perm=perm, inv=inv, gate_info=g)
+    # the balance statistics describe the gate's choice, before any drop
+    gate_counts = route(idx, cfg.n_experts)[0] if capacity > 0 else counts
     if with_experts:
         w1 = _f64(inp["w1"])
         w2 = _f64(inp["w2"])
@@ -389,7 +402,7 @@ def forward(inp: Dict, cfg, w_importance=1.0, w_load=1.0,
         y_sorted = run_experts(inp["x"], perm, offsets, cfg.top_k, w1, w2, w3)
         out["y_sorted"] = y_sorted
         out["y"] = combine(y_sorted, inv, gates)
-    out.update(balance_stats(cfg.n_experts, idx, gates, counts,
+    out.update(balance_stats(cfg.n_experts, idx, gates, gate_counts,
                              None if cfg.n_groups else g, w_importance, w_load))
     return out
 
@@ -526,8 +539,11 @@ def backward(inp: Dict, cfg, dy, w_importance=1.0, w_load=1.0) -> Dict:
     E = cfg.n_experts
     rows = np.arange(T)
 
-    # combine: y_t = sum_s gate[t,s] * y_sorted[inv[t,s]]
-    y_rows = fw["y_sorted"][inv.reshape(T, k)]            # [T][k][d]
+    # combine: y_t = sum over the kept slots of gate[t,s] * y_sorted[inv[t,s]]
+    inv2 = inv.reshape(T, k)
+    y_rows = np.zeros((T, k, dy.shape[1]))
+    kept_slot = inv2 >= 0
+    y_rows[kept_slot] = fw["y_sorted"][inv2[kept_slot]]   # dropped slots add nothing
     dgate = np.einsum("tsd,td->ts", y_rows, dy) if T else np.zeros((0, k))
     # importance: d Importance_e / d G[t,e] = 1 for every kept (t, e)
     dgate = dgate + w_importance * cv_squared_grad(fw["importance"])[idx]

@@ -55,6 +55,7 @@ class MoEConfig:
     k_per_group: int = 0
     bias: str = "none"         # "none" or "zipf"
     gate_std: float = 0.02
+    capacity: int = 0          # rows an expert takes at most (0: no limit)
 
     @property
     def hierarchical(self) -> bool:

@@ -27,6 +27,7 @@ def _load(name):
 
 pins = _load("test_oracle_pins")
 bpins = _load("test_oracle_backward_pins")
+cpins = _load("test_oracle_capacity_pins")
 
 _orig = {name: getattr(om, name) for name in dir(om) if not name.startswith("__")}
 
@@ -40,7 +41,7 @@ def _cases(fn):
 
 
 def _pin_fails(name):
-    fn = getattr(pins, name, None) or getattr(bpins, name)
+    fn = getattr(pins, name, None) or getattr(bpins, name, None) or getattr(cpins, name)
     for args in _cases(fn):
         try:
             fn(*args)
@@ -123,6 +124,39 @@ def softmax_over_all_experts(H, idx):
         return np.zeros(idx.shape)
     P = scipy.special.softmax(H, axis=1)
     return np.take_along_axis(P, idx.astype(np.int64), axis=1)
+
+
+def route_capacity_keeps_latest(idx, n_experts, capacity=0):
+    """Keeps the last `capacity` tokens of an expert instead of the first."""
+    if capacity <= 0:
+        return _orig["route"](idx, n_experts)
+    T, k = idx.shape
+    flipped = idx[::-1]
+    counts, offsets, perm_f, inv_f = _orig["route"](flipped, n_experts, capacity)
+    inv = np.full(T * k, -1, dtype=np.int32)
+    perm = np.zeros_like(perm_f)
+    for a_f in range(T * k):
+        t_f, s_ = divmod(a_f, k)
+        if inv_f[a_f] >= 0:
+            a = (T - 1 - t_f) * k + s_
+            inv[a] = inv_f[a_f]
+            perm[inv_f[a_f]] = a
+    return counts, offsets, perm, inv
+
+
+def route_capacity_off_by_one(idx, n_experts, capacity=0):
+    return _orig["route"](idx, n_experts, capacity + 1 if capacity > 0 else 0)
+
+
+def combine_dropped_slot_reads_last_row(y_sorted, inv, gates):
+    """A dropped slot (-1) indexes the last routed row instead of adding nothing."""
+    gates = np.asarray(gates, dtype=np.float64)
+    T, k = gates.shape
+    y = np.zeros((T, y_sorted.shape[1]))
+    inv2 = np.asarray(inv).reshape(T, k)
+    for s_ in range(k):
+        y += gates[:, s_:s_ + 1] * y_sorted[inv2[:, s_]]
+    return y
 
 
 def route_tokens_descending(idx, n_experts):
@@ -308,6 +342,13 @@ MUTATIONS = [
                                            "test_hierarchy_invariants_random"]),
     ("hier_gate", hier_expert_index_transposed, ["test_hierarchy_constructed_case",
                                                  "test_hierarchy_invariants_random"]),
+    # capacity
+    ("route", route_capacity_keeps_latest, ["test_route_capacity_hand_example",
+                                            "test_capacity_invariants_random",
+                                            "test_capacity_layer_equals_brute_force"]),
+    ("route", route_capacity_off_by_one, ["test_route_capacity_hand_example",
+                                          "test_capacity_invariants_random"]),
+    ("combine", combine_dropped_slot_reads_last_row, ["test_capacity_layer_equals_brute_force"]),
     # backward
     ("cv_squared_grad", cv2_grad_without_mean_term, ["test_cv_squared_gradient_closed_forms",
                                                      "test_gradients_match_central_differences"]),
