@@ -79,6 +79,13 @@ typedef struct moe_config {
   int32_t noisy;       /* 1 = noisy gating (noise tables and eps given) */
   int32_t ffn;         /* moe_ffn */
   int32_t dtype;       /* moe_dtype */
+  int32_t capacity;    /* 0 = none; else rows an expert takes at most: the
+                          first `capacity` assignments in token order are
+                          kept and the rest dropped (a capacity factor with
+                          overflow drop, "MoE 混合专家：参数大、计算省",
+                          section 核心概念).  A dropped assignment adds nothing
+                          to y; gates are not renormalized; the balance
+                          statistics stay those of the gate's choice. */
 } moe_config;
 
 /* Gate and expert parameters.  Tables hold one ROW per output unit (the
@@ -151,6 +158,9 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
  *             expert (stable)
  *   inv       [A] int32 out: inv[a] = position of assignment a
  *   x, x_sorted  nullable pair: when both are given, x_sorted[p] = x[perm[p]/k]
+ * With cfg->capacity > 0: counts and offsets count the kept rows only,
+ * inv[a] = -1 for a dropped assignment, and perm[p] = 0 for the positions
+ * p >= offsets[E] that no kept assignment takes.
  * Out-of-range expert ids in topk_idx are undefined behaviour. */
 moe_status moe_route(const moe_config* cfg, const int32_t* topk_idx,
                      int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -201,7 +211,8 @@ moe_status moe_pack_gate(const moe_config* cfg, const moe_params* p, void* packe
 
 /* Combine: y[t] = sum over slots s (ascending) of
  * topk_gate[t][s] * y_sorted[inv[t*k+s]], accumulated in fp32
- * (lesson page, section 二).  y [T][d] out (cfg dtype). */
+ * (lesson page, section 二); slots with inv = -1 (dropped by a capacity)
+ * add nothing.  y [T][d] out (cfg dtype). */
 moe_status moe_combine(const moe_config* cfg, const void* y_sorted,
                        const int32_t* inv, const float* topk_gate, void* y,
                        void* stream);
@@ -217,7 +228,8 @@ moe_status moe_combine(const moe_config* cfg, const void* y_sorted,
  *   out[2] = w_importance * out[0] + w_load * out[1]
  * CV^2 = population variance / mean^2 (0 when the mean is 0).
  * Inputs: x, p (w_gate, w_noise, bias) and thr are used only for the smooth
- * load; perm/offsets from moe_route; topk_idx/topk_gate/thr from moe_gate.
+ * load; perm/offsets from moe_route without a capacity (the statistics
+ * describe the gate's choice); topk_idx/topk_gate/thr from moe_gate.
  * importance, load [E] f32 out; out [3] f32 out. */
 moe_status moe_balance_loss(const moe_config* cfg, const void* x,
                             const moe_params* p, const int32_t* topk_idx,

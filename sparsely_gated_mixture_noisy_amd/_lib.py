@@ -41,7 +41,8 @@ class moe_config(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("d_hidden", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("k_groups", ctypes.c_int32), ("k_per_group", ctypes.c_int32),
-                ("noisy", ctypes.c_int32), ("ffn", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("noisy", ctypes.c_int32), ("ffn", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("capacity", ctypes.c_int32)]
 
 
 class moe_params(ctypes.Structure):
@@ -142,7 +143,7 @@ def make_config(cfg: MoEConfig, tokens: Optional[int] = None) -> moe_config:
         n_groups=cfg.n_groups, k_groups=cfg.k_groups, k_per_group=cfg.k_per_group,
         noisy=1 if cfg.noisy else 0,
         ffn=MOE_FFN_SWIGLU if cfg.ffn == "swiglu" else MOE_FFN_RELU,
-        dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+        dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32, capacity=cfg.capacity)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

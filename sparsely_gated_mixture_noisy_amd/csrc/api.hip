@@ -44,6 +44,7 @@ struct Layout {
   size_t idx, gate, thr, counts, offsets, perm, inv, bits, base, tiles, desc, hid, ysorted, part,
       imp_part, imp, load;
   size_t idx_p, gate_p, counts_g, offsets_g, perm_g, inv_g, bits_g, base_g, tiles_g;
+  size_t counts_u, offsets_u, perm_u, inv_u;
   size_t total;
   int nb, load_blocks;
 };
@@ -90,6 +91,12 @@ Layout layout(const moe_config* c) {
   L.bits_g = take(4 * (size_t)L.nb * G);
   L.base_g = take(4 * (size_t)L.nb * G);
   L.tiles_g = take(4 * (size_t)(G + 1));
+  // the routing without the capacity, for the balance statistics
+  const bool cap = c->capacity > 0;
+  L.counts_u = take(cap ? 4 * (size_t)E : 0);
+  L.offsets_u = take(cap ? 4 * (size_t)(E + 1) : 0);
+  L.perm_u = take(cap ? 4 * (size_t)A : 0);
+  L.inv_u = take(cap ? 4 * (size_t)A : 0);
   L.total = o;
   return L;
 }
@@ -111,6 +118,7 @@ moe_status check_config(const moe_config* c) {
   if (c->ffn != MOE_FFN_RELU && c->ffn != MOE_FFN_SWIGLU)
     return fail(MOE_ERR_INVALID_ARG, "unknown ffn %d", c->ffn);
   if (c->noisy != 0 && c->noisy != 1) return fail(MOE_ERR_INVALID_ARG, "noisy must be 0 or 1");
+  if (c->capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity < 0");
   if (c->n_groups < 0) return fail(MOE_ERR_INVALID_ARG, "n_groups < 0");
   if (c->n_groups > 0) {
     const int G = c->n_groups;
@@ -315,8 +323,10 @@ struct RouteStats {
 
 moe_status do_route(const moe_config* c, const Layout& L, const int32_t* idx, int32_t* counts,
                     int32_t* offsets, int32_t* perm, int32_t* inv, bool have_bits,
-                    bool with_tiles, void* ws, hipStream_t s, const RouteStats& st = RouteStats()) {
+                    bool with_tiles, void* ws, hipStream_t s, const RouteStats& st = RouteStats(),
+                    bool capped = true) {
   RouteArgs r;
+  r.capacity = capped ? c->capacity : 0;
   r.idx = idx;
   r.T = c->tokens;
   r.k = c->top_k;
@@ -889,9 +899,22 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   MOE_TRY(hip_status(launch_combine(y_sorted, inv, gate, cfg->tokens, cfg->top_k, cfg->d_model,
                                     cfg->dtype == MOE_BF16, out->y, s),
                      "combine"));
-  if (balance && !fused_stats)
-    MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, perm, offsets, w_importance, w_load, imp,
-                       load, out->balance, false, ws, s));
+  if (balance && !fused_stats) {
+    // the statistics describe the gate's choice: with a capacity they walk
+    // the routing without it
+    const int32_t* bperm = perm;
+    const int32_t* boff = offsets;
+    if (cfg->capacity > 0 && cfg->tokens > 0) {
+      int32_t* perm_u = at<int32_t>(ws, L.perm_u);
+      int32_t* off_u = at<int32_t>(ws, L.offsets_u);
+      MOE_TRY(do_route(cfg, L, idx, at<int32_t>(ws, L.counts_u), off_u, perm_u,
+                       at<int32_t>(ws, L.inv_u), false, false, ws, s, RouteStats(), false));
+      bperm = perm_u;
+      boff = off_u;
+    }
+    MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, bperm, boff, w_importance, w_load, imp, load,
+                       out->balance, false, ws, s));
+  }
   return ok();
 }
 

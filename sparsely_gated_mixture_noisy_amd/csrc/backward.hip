@@ -92,8 +92,10 @@ __global__ __launch_bounds__(256) void bw_gate_out_kernel(BwGateOutArgs a) {
     g[s] = 0.f;
     if (s < a.k) {
       const int64_t p = a.inv[t * a.k + s];
-      const T* yr = ys + p * a.d;
+      const T* yr = ys + (p < 0 ? 0 : p) * a.d;
       float acc = 0.f;
+      // a slot dropped by a capacity (inv = -1) contributes nothing to y
+      if (p >= 0) {
       if ((a.d & 3) == 0) {
         // four elements per lane and step: 8-byte (bf16) or 16-byte (fp32) loads
         for (int c = lane * 4; c < a.d; c += 256) {
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(256) void bw_gate_out_kernel(BwGateOutArgs a) {
         }
       } else {
         for (int c = lane; c < a.d; c += 64) acc = fmaf(Elem<T>::load(dy, c), Elem<T>::load(yr, c), acc);
+      }
       }
       dg[s] = wave_sum(acc);
       if (a.dimp) dg[s] += a.dimp[a.idx[t * a.k + s]];
@@ -458,7 +461,9 @@ __global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, c
   const int c = (int)(i % d);
   float4 v = *reinterpret_cast<const float4*>(dxg + i);
   for (int s = 0; s < k; ++s) {
-    const float4 u = *reinterpret_cast<const float4*>(dxs + (int64_t)inv[t * k + s] * d + c);
+    const int p = inv[t * k + s];
+    if (p < 0) continue;  // dropped by a capacity
+    const float4 u = *reinterpret_cast<const float4*>(dxs + (int64_t)p * d + c);
     v.x += u.x;
     v.y += u.y;
     v.z += u.z;

@@ -2,7 +2,8 @@
 //
 // Combine ("MoE:稀疏门控混合专家", nengyongai.cn, section 二):
 //   y_t = sum over the token's kept slots s (ascending) of
-//         gate[t][s] * y_sorted[inv[t*k + s]],  fp32 accumulation.
+//         gate[t][s] * y_sorted[inv[t*k + s]],  fp32 accumulation;
+//   slots that an expert's capacity dropped (inv = -1) add nothing.
 // One wave per token; each lane owns 16-byte column chunks of the row.
 //
 // Balance statistics ("Outrageously Large Neural Networks — MoE ..." reading
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ ys,
       for (int j = 0; j < V; ++j) acc[j] = 0.f;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        if (s < k) {
+        if (s < k && rows[s] >= 0) {
           const T* src = ys + (int64_t)rows[s] * d + c;
           u32x4 raw = *reinterpret_cast<const u32x4*>(src);
           const T* vals = reinterpret_cast<const T*>(&raw);
@@ -57,7 +58,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ ys,
   } else {
     for (int c = lane; c < d; c += 64) {
       float acc = 0.f;
-      for (int s = 0; s < k; ++s) acc = fmaf(g[s], Elem<T>::load(ys, (int64_t)rows[s] * d + c), acc);
+      for (int s = 0; s < k; ++s)
+        if (rows[s] >= 0) acc = fmaf(g[s], Elem<T>::load(ys, (int64_t)rows[s] * d + c), acc);
       Elem<T>::store(y, t * d + c, acc);
     }
   }

@@ -90,6 +90,10 @@ struct RouteArgs {
   float* load = nullptr;             // [E]
   float* bal_out = nullptr;          // [3]: CV^2(importance), CV^2(load), weighted sum
   float w_imp = 0.f, w_load = 0.f;
+  // > 0: an expert keeps its first `capacity` assignments (token order); the
+  // rest get inv = -1 and no position; counts / offsets count kept rows;
+  // perm past offsets[E] holds 0.  The statistics above stay pre-drop.
+  int capacity = 0;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);

@@ -19,7 +19,8 @@
 //                  and no workgroup has to wait for another); workgroup 0
 //                  also writes offsets and, when asked, the expert stage's
 //                  tile map; pos = offsets[e] + base[b][e] + in-block rank,
-//                  perm[pos] = a, inv[a] = pos
+//                  perm[pos] = a, inv[a] = pos; with a capacity, ranks at or
+//                  past it are dropped (inv[a] = -1) and counts are capped
 // With balance partials (per-block gate sums and smooth-load terms from the
 // flat gate), route_colscan also reduces them to importance[e] and load[e],
 // and workgroup 0 of route_scatter turns those into the CV^2 values.
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void route_colscan_kernel(RouteArgs a
     const float tl = wave_sum(pload[w][lane]);
     pc[w][lane] = incl - v;  // exclusive base of range `lane` (only wave w touches row w)
     if (lane == 0 && ew < a.E) {
-      a.counts[ew] = tot;
+      a.counts[ew] = a.capacity > 0 ? min(tot, a.capacity) : tot;
       if (stats) {
         a.importance[ew] = ti;
         a.load[ew] = a.load_part ? tl : (float)tot;
@@ -253,9 +254,22 @@ __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArg
     const int64_t as = t0 * a.k + i;
     const int e = a.idx[as];
     const int64_t o = (int64_t)b * a.E + e;
-    const int pos = off[e] + a.base[o] + __popc(a.bits[o] & ((1u << tl) - 1u));
+    const int rank = a.base[o] + __popc(a.bits[o] & ((1u << tl) - 1u));
+    if (a.capacity > 0 && rank >= a.capacity) {
+      a.inv[as] = -1;  // past the expert's capacity: dropped
+      continue;
+    }
+    const int pos = off[e] + rank;
     a.perm[pos] = (int32_t)as;
     a.inv[as] = pos;
+  }
+  if (a.capacity > 0) {
+    // positions no kept assignment took: a valid index, so that row gathers
+    // over all T*k positions stay in bounds
+    const int64_t A = a.T * a.k;
+    for (int64_t p = off[a.E] + (int64_t)b * SCATTER_THREADS + tid; p < A;
+         p += (int64_t)gridDim.x * SCATTER_THREADS)
+      a.perm[p] = 0;
   }
 }
 

@@ -100,6 +100,10 @@ CASES = {
                                                       d_hidden=320, noisy=False, top_k=3),
                            1.2, 0.0),
     "bf16_flat256_t512": (CONFIGS["flat256"].replace(tokens=512), 1.0, 1.0),
+    # experts capped at 6 rows: dropped slots add nothing to y or dx
+    "bf16_capacity6": (CONFIGS["flat256"].replace(tokens=300, n_experts=24, d_model=128,
+                                                  d_hidden=256, capacity=6), 0.7, 1.2),
+    "tiny_capacity40": (CONFIGS["tiny"].replace(capacity=40), 0.5, 0.5),
 }
 
 

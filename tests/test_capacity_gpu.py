@@ -1,0 +1,90 @@
+"""Parity of capacity-constrained routing on the GPU (moe_config.capacity: an
+expert takes at most `capacity` rows, the first ones in token order, and the
+later assignments are dropped; "MoE 混合专家：参数大、计算省", section 核心概念)
+with the CPU oracle, through the staged entry points and moe_forward.
+
+Routing (counts, offsets, the kept part of perm, inv with -1 for dropped
+assignments) must be bit-exact, perm past offsets[E] must hold 0, outputs
+within the layer bar, and the balance statistics must be those of the gate's
+choice (before the drop).  Inputs come from the first seed with no token
+whose k-th vs (k+1)-th score margin is below 1e-4, since one changed choice
+would move the drop of every later token of that expert."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_check import check_balance, check_close, check_gate, excluded, np_
+from sparsely_gated_mixture_noisy_amd import _lib as L
+from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+CASES = {
+    "tiny_cap40": CONFIGS["tiny"].replace(capacity=40),
+    "flat256_t1000_cap10": CONFIGS["flat256"].replace(tokens=1000, capacity=10),
+    "flat256_t1000_cap10_packed": CONFIGS["flat256"].replace(tokens=1000, capacity=10),
+    "zipf_t500_cap3": CONFIGS["zipf2048"].replace(tokens=500, capacity=3),
+    "hier_t300_cap1": CONFIGS["hier4096"].replace(tokens=300, capacity=1),
+    "swiglu_cap30": CONFIGS["mixtral"].replace(tokens=200, d_model=512, d_hidden=1536, capacity=30),
+    "cap_above_every_count": CONFIGS["flat256"].replace(tokens=300, capacity=10 ** 6),
+}
+
+
+def _inputs(cfg, name):
+    for seed in range(12):
+        inp = make_inputs(cfg, seed=seed, device="cuda")
+        cpu = {k: (v.to("cpu") if v is not None else None) for k, v in inp.items()}
+        ref = oracle.forward(cpu, cfg)
+        if not excluded(ref).any():
+            if name.endswith("_packed"):
+                inp = dict(inp, w_packed=L.pack_experts(cfg, inp))
+            return seed, inp, ref
+    pytest.fail("no seed without near-tied scores")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_capacity_layer(name):
+    cfg = CASES[name]
+    seed, inp, ref = _inputs(cfg, name)
+    _say(f"[capacity] {name} seed {seed}: {cfg}")
+    x = inp["x"]
+    T, k, E = cfg.tokens, cfg.top_k, cfg.n_experts
+    ws = L.workspace(cfg, T)
+    idx, gate, thr = L.gate(cfg, x, inp, inp, ws=ws)
+    counts, offsets, perm, inv, _ = L.route(cfg, idx, ws=ws)
+    ys = L.expert_ffn(cfg, x, perm, offsets, inp, ws=ws)
+    y = L.combine(cfg, ys, inv, gate)
+    torch.cuda.synchronize()
+    excl = np.zeros(T, dtype=bool)
+    check_gate(idx, gate, ref, excl, thr=thr)
+    counts, offsets, perm, inv = np_(counts), np_(offsets), np_(perm), np_(inv)
+    ak = int(offsets[-1])
+    assert (counts == ref["counts"]).all() and (offsets == ref["offsets"]).all()
+    assert (perm[:ak] == ref["perm"]).all() and (inv == ref["inv"]).all()
+    assert (perm[ak:] == 0).all()
+    dropped = int((inv < 0).sum())
+    if cfg.capacity < 10 ** 6:
+        assert dropped > 0, "the case must drop assignments"
+    else:
+        assert dropped == 0
+    worst = check_close(y, ref["y"], RTOL[cfg.dtype])
+    # the whole layer in one call gives the same bits, and statistics of the
+    # gate's choice
+    fo = L.forward(cfg, x, inp, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fo.y, y) and torch.equal(fo.topk_idx, idx)
+    assert (np_(fo.counts) == counts).all()
+    check_balance(fo.importance, fo.load, fo.balance, ref, excl, ref["idx"],
+                  smooth=(cfg.noisy and not cfg.hierarchical))
+    _say(f"[capacity] {name}: ok dropped={dropped} of {T * k} worst_y={worst:.2e}")
