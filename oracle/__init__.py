@@ -12,4 +12,4 @@ from .moe_oracle import (cv_squared, combine, dense_forward, dense_gates,  # noq
                          run_experts, silu, softplus, token_outputs,
                          balance_stats, backward, cv_squared_grad, rank_experts,
                          expert_relu_backward, expert_swiglu_backward, normal_pdf,
-                         sigmoid)
+                         sigmoid, philox4x32_10, uniform23, philox_normals, draw_noise)

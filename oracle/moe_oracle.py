@@ -617,3 +617,79 @@ def backward(inp: Dict, cfg, dy, w_importance=1.0, w_load=1.0) -> Dict:
         np.add.at(dx, toks, dX)
     return dict(dx=dx, dw_gate=dw_gate, dw_noise=dw_noise, dbias=dbias, dw1=dw1,
                 dw3=dw3, dw2=dw2, dgate=dgate, dH=dH, forward=fw)
+
+
+# ---------------------------------------------------------------------------
+# Noise drawn from a counter-based generator  [MoE lesson, section 四: a fresh
+# standard-normal draw per call]
+#
+# Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
+# Easy as 1, 2, 3", SC 2011): a 128-bit counter and a 64-bit key; ten rounds,
+# each multiplying counter words 0 and 2 by two fixed 32-bit constants and
+# mixing the high halves with the other words and the key, the key then
+# bumped by two Weyl constants.  Element i of a noise row `row` (group `sub`,
+# stream `stream`: 0 flat / secondary, 1 primary) takes the Philox output of
+# counter (i // 4, row, sub, stream) under key (seed low, seed high): words
+# (0, 1) feed elements 4q, 4q+1 and words (2, 3) elements 4q+2, 4q+3 through
+# the Box-Muller transform r = sqrt(-2 ln u_a), n = r cos(2 pi u_b) (even
+# element) or r sin(2 pi u_b) (odd), u = (top 23 bits + 1/2) / 2^23, which
+# float32 holds exactly.
+# ---------------------------------------------------------------------------
+
+PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57
+PHILOX_W0, PHILOX_W1 = 0x9E3779B9, 0xBB67AE85
+
+
+def philox4x32_10(ctr, key):
+    """ctr: uint [..., 4], key: uint [..., 2] (broadcast) -> uint32 [..., 4]."""
+    c = [np.asarray(ctr, dtype=np.uint64)[..., i] & 0xFFFFFFFF for i in range(4)]
+    key = np.asarray(key, dtype=np.uint64)
+    k0, k1 = key[..., 0] & 0xFFFFFFFF, key[..., 1] & 0xFFFFFFFF
+    mask = np.uint64(0xFFFFFFFF)
+    for _ in range(10):
+        p0 = np.uint64(PHILOX_M0) * c[0]
+        p1 = np.uint64(PHILOX_M1) * c[2]
+        hi0, lo0 = p0 >> np.uint64(32), p0 & mask
+        hi1, lo1 = p1 >> np.uint64(32), p1 & mask
+        c = [(hi1 ^ c[1] ^ k0) & mask, lo1, (hi0 ^ c[3] ^ k1) & mask, lo0]
+        k0 = (k0 + np.uint64(PHILOX_W0)) & mask
+        k1 = (k1 + np.uint64(PHILOX_W1)) & mask
+    return np.stack(c, axis=-1).astype(np.uint32)
+
+
+def uniform23(x):
+    """(top 23 bits of x + 1/2) / 2^23: in (0, 1), exact in float32."""
+    return ((np.asarray(x, dtype=np.uint32) >> np.uint32(9)).astype(np.float64) + 0.5) * 2.0 ** -23
+
+
+def philox_normals(rows, n, seed, sub=0, stream=0):
+    """Standard normals [len(rows)][n] of the given noise rows (see above)."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    i = np.arange(n, dtype=np.uint64)
+    q = i >> np.uint64(2)
+    ctr = np.zeros((rows.size, n, 4), dtype=np.uint64)
+    ctr[..., 0] = q[None, :]
+    ctr[..., 1] = rows[:, None]
+    ctr[..., 2] = np.uint64(sub)
+    ctr[..., 3] = np.uint64(stream)
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint64)
+    out = philox4x32_10(ctr, key)
+    j = (i & np.uint64(3)).astype(np.int64)
+    pair = j >> 1
+    xa = np.where(pair == 0, out[..., 0], out[..., 2])
+    xb = np.where(pair == 0, out[..., 1], out[..., 3])
+    r = np.sqrt(-2.0 * np.log(uniform23(xa)))
+    ang = 2.0 * math.pi * uniform23(xb)
+    return np.where((j & 1) == 0, r * np.cos(ang), r * np.sin(ang))
+
+
+def draw_noise(cfg, seed) -> Dict:
+    """The noise tensors of one layer call drawn from `seed`: eps [T][E]
+    (flat), or eps_p [T][G] and eps [T][G][Eg] (hierarchy)."""
+    T = cfg.tokens
+    rows = np.arange(T)
+    if not cfg.n_groups:
+        return dict(eps=philox_normals(rows, cfg.n_experts, seed, 0, 0), eps_p=None)
+    G, Eg = cfg.n_groups, cfg.n_experts // cfg.n_groups
+    eps = np.stack([philox_normals(rows, Eg, seed, g, 0) for g in range(G)], axis=1)
+    return dict(eps=eps, eps_p=philox_normals(rows, G, seed, 0, 1))

@@ -28,6 +28,7 @@ def _load(name):
 pins = _load("test_oracle_pins")
 bpins = _load("test_oracle_backward_pins")
 cpins = _load("test_oracle_capacity_pins")
+npins = _load("test_oracle_noise_pins")
 
 _orig = {name: getattr(om, name) for name in dir(om) if not name.startswith("__")}
 
@@ -41,7 +42,8 @@ def _cases(fn):
 
 
 def _pin_fails(name):
-    fn = getattr(pins, name, None) or getattr(bpins, name, None) or getattr(cpins, name)
+    fn = (getattr(pins, name, None) or getattr(bpins, name, None) or getattr(cpins, name, None)
+          or getattr(npins, name))
     for args in _cases(fn):
         try:
             fn(*args)
@@ -157,6 +159,37 @@ def combine_dropped_slot_reads_last_row(y_sorted, inv, gates):
     for s_ in range(k):
         y += gates[:, s_:s_ + 1] * y_sorted[inv2[:, s_]]
     return y
+
+
+def philox_without_key_bump(ctr, key):
+    """Ten rounds that reuse the first round key."""
+    c = [np.asarray(ctr, dtype=np.uint64)[..., i] for i in range(4)]
+    key = np.asarray(key, dtype=np.uint64)
+    k0, k1 = key[..., 0], key[..., 1]
+    mask = np.uint64(0xFFFFFFFF)
+    for _ in range(10):
+        p0 = np.uint64(om.PHILOX_M0) * c[0]
+        p1 = np.uint64(om.PHILOX_M1) * c[2]
+        c = [((p1 >> np.uint64(32)) ^ c[1] ^ k0) & mask, p1 & mask,
+             ((p0 >> np.uint64(32)) ^ c[3] ^ k1) & mask, p0 & mask]
+    return np.stack(c, axis=-1).astype(np.uint32)
+
+
+def philox_words_of_product_swapped(ctr, key):
+    out = _orig["philox4x32_10"](ctr, key)
+    return out[..., [1, 0, 3, 2]]
+
+
+def uniform_from_24_bits(x):
+    return ((np.asarray(x, dtype=np.uint32) >> np.uint32(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+
+
+def normals_sin_and_cos_swapped(rows, n, seed, sub=0, stream=0):
+    z = _orig["philox_normals"](rows, n, seed, sub, stream)
+    m = n - n % 2
+    out = z.copy()
+    out[:, 0:m:2], out[:, 1:m:2] = z[:, 1:m:2], z[:, 0:m:2]
+    return out
 
 
 def route_tokens_descending(idx, n_experts):
@@ -349,6 +382,12 @@ MUTATIONS = [
     ("route", route_capacity_off_by_one, ["test_route_capacity_hand_example",
                                           "test_capacity_invariants_random"]),
     ("combine", combine_dropped_slot_reads_last_row, ["test_capacity_layer_equals_brute_force"]),
+    # counter-based noise
+    ("philox4x32_10", philox_without_key_bump, ["test_philox_known_answers"]),
+    ("philox4x32_10", philox_words_of_product_swapped, ["test_philox_known_answers",
+                                                        "test_normals_follow_the_counter_layout"]),
+    ("uniform23", uniform_from_24_bits, ["test_uniform23_range_and_exactness"]),
+    ("philox_normals", normals_sin_and_cos_swapped, ["test_normals_follow_the_counter_layout"]),
     # backward
     ("cv_squared_grad", cv2_grad_without_mean_term, ["test_cv_squared_gradient_closed_forms",
                                                      "test_gradients_match_central_differences"]),

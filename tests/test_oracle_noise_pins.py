@@ -1,0 +1,74 @@
+"""Pins of the oracle's counter-based noise: Philox4x32-10 against the
+known-answer vectors published with its reference implementation, the
+23-bit uniforms, and the Box-Muller normals against the standard normal
+distribution (moments and a Kolmogorov-Smirnov test).  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import scipy.stats
+
+import oracle
+from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_philox_known_answers():
+    with open(os.path.join(GOLDEN, "philox_kat.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    for v in g["vectors"]:
+        ctr = np.array([int(h, 16) for h in v["ctr"]], dtype=np.uint64)
+        key = np.array([int(h, 16) for h in v["key"]], dtype=np.uint64)
+        out = oracle.philox4x32_10(ctr, key)
+        assert [f"{int(w):08x}" for w in out] == v["out"]
+
+
+def test_uniform23_range_and_exactness():
+    x = np.array([0, 511, 512, 0xFFFFFFFF, 0x80000000], dtype=np.uint32)
+    u = oracle.uniform23(x)
+    assert u[0] == u[1] == 0.5 * 2.0 ** -23
+    assert u[2] == 1.5 * 2.0 ** -23
+    assert u[3] == 1.0 - 0.5 * 2.0 ** -23
+    assert u[4] == 0.5 + 0.5 * 2.0 ** -23
+    rng = np.random.default_rng(0)
+    u = oracle.uniform23(rng.integers(0, 2 ** 32, 100000, dtype=np.uint64).astype(np.uint32))
+    assert (u.astype(np.float32).astype(np.float64) == u).all()       # exact in float32
+    assert ((u > 0) & (u < 1)).all()
+
+
+def test_normals_are_standard():
+    z = oracle.philox_normals(np.arange(400), 500, seed=12345).ravel()
+    assert abs(z.mean()) < 4 / math.sqrt(z.size)
+    assert abs(z.var() - 1.0) < 6 * math.sqrt(2.0 / z.size)
+    assert scipy.stats.kstest(z, "norm").pvalue > 1e-3
+    # the cos and sin halves of each pair are uncorrelated
+    zz = z.reshape(-1, 2)
+    assert abs(np.corrcoef(zz[:, 0], zz[:, 1])[0, 1]) < 5 / math.sqrt(zz.shape[0])
+
+
+def test_normals_follow_the_counter_layout():
+    """Element i of row t is word pair (i % 4) // 2 of counter (i // 4, t,
+    sub, stream); streams, groups, rows and seeds give different draws."""
+    seed = (7 << 32) | 99
+    z = oracle.philox_normals([5], 8, seed)[0]
+    w = oracle.philox4x32_10(np.array([1, 5, 0, 0], dtype=np.uint64),
+                             np.array([99, 7], dtype=np.uint64))
+    r = math.sqrt(-2.0 * math.log(oracle.uniform23(w[0])))
+    a = 2.0 * math.pi * oracle.uniform23(w[1])
+    assert abs(z[4] - r * math.cos(a)) < 1e-12 and abs(z[5] - r * math.sin(a)) < 1e-12
+    base = oracle.philox_normals([5], 8, seed)
+    for other in (oracle.philox_normals([6], 8, seed), oracle.philox_normals([5], 8, seed + 1),
+                  oracle.philox_normals([5], 8, seed, sub=1),
+                  oracle.philox_normals([5], 8, seed, stream=1)):
+        assert not np.allclose(other, base)
+
+
+def test_draw_noise_shapes():
+    flat = oracle.draw_noise(CONFIGS["tiny"].replace(tokens=10), seed=3)
+    assert flat["eps"].shape == (10, 8) and flat["eps_p"] is None
+    hc = CONFIGS["hier4096"].replace(tokens=6, n_experts=32, n_groups=4)
+    h = oracle.draw_noise(hc, seed=3)
+    assert h["eps"].shape == (6, 4, 8) and h["eps_p"].shape == (6, 4)
+    assert np.allclose(h["eps"][:, 2, :], oracle.philox_normals(np.arange(6), 8, 3, sub=2))
