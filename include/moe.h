@@ -121,14 +121,34 @@ typedef struct moe_params {
   const void* w_gate_packed;
 } moe_params;
 
-/* Noise draws, float32 ~ N(0,1), supplied by the caller (NULL = no noise).
+/* Noise draws, float32 ~ N(0,1), supplied by the caller (NULL = no noise),
+ * or drawn inside the kernels:
  *   eps    flat: [T][E];  hierarchy: [T][G][Eg], only the slices of the
  *          groups a token keeps are read
- *   eps_p  hierarchy: [T][G] primary noise */
+ *   eps_p  hierarchy: [T][G] primary noise
+ *   in_kernel  1: eps / eps_p are not read; every kernel that needs a draw
+ *          makes it from a counter-based generator keyed by `seed`:
+ *          Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random
+ *          Numbers: As Easy as 1, 2, 3", SC 2011).  Element j of the noise
+ *          row of token t takes counter (j/4, t, g, stream) (g: the group of
+ *          the hierarchy's secondary noise, else 0; stream 1 for eps_p, else
+ *          0); output words (0,1) serve elements 4q, 4q+1 and (2,3) elements
+ *          4q+2, 4q+3 through Box-Muller, r = sqrt(-2 ln u_a) times
+ *          cos(2 pi u_b) (even j) or sin(2 pi u_b) (odd j), with
+ *          u = (top 23 bits + 1/2) / 2^23.  moe_draw_noise writes the same
+ *          draws out.  A fresh seed per call gives the fresh draw the lesson
+ *          page's section 四 asks for. */
 typedef struct moe_noise {
   const float* eps;
   const float* eps_p;
+  uint64_t seed;
+  int32_t in_kernel;
 } moe_noise;
+
+/* The generator's draws for `seed` written out: eps [T][E] (flat) or
+ * [T][G][Eg] (hierarchy) and eps_p [T][G] (hierarchy), either nullable. */
+moe_status moe_draw_noise(const moe_config* cfg, uint64_t seed, float* eps, float* eps_p,
+                          void* stream);
 
 /* Bytes of workspace needed by any entry point for this configuration. */
 size_t moe_workspace_size(const moe_config* cfg);

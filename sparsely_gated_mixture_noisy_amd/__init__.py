@@ -8,6 +8,6 @@ its absence is an error.
 """
 from .inputs import CONFIGS, MoEConfig, make_inputs, make_upstream  # noqa: F401
 from ._lib import (Backward, Forward, ForwardOut, Grads, MoEError, Workspace,  # noqa: F401
-                   backward, backward_workspace_size, balance_loss,
+                   backward, backward_workspace_size, balance_loss, draw_noise,
                    combine, expert_ffn, forward, gate, load, pack_experts, pack_gate,
                    packed_experts_size, packed_gate_size, route, workspace, workspace_size)

@@ -52,7 +52,8 @@ class moe_params(ctypes.Structure):
 
 
 class moe_noise(ctypes.Structure):
-    _fields_ = [("eps", ctypes.c_void_p), ("eps_p", ctypes.c_void_p)]
+    _fields_ = [("eps", ctypes.c_void_p), ("eps_p", ctypes.c_void_p),
+                ("seed", ctypes.c_uint64), ("in_kernel", ctypes.c_int32)]
 
 
 class moe_outputs(ctypes.Structure):
@@ -99,6 +100,7 @@ _SIGS = {
                                     ctypes.POINTER(moe_noise), ctypes.POINTER(moe_saved), _P,
                                     ctypes.c_float, ctypes.c_float, ctypes.POINTER(moe_grads), _P,
                                     ctypes.c_size_t, _P]),
+    "moe_draw_noise": (ctypes.c_int, [ctypes.POINTER(moe_config), ctypes.c_uint64, _P, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -163,7 +165,28 @@ def make_params(p: Dict[str, Optional[torch.Tensor]]) -> moe_params:
 
 
 def make_noise(p: Dict[str, Optional[torch.Tensor]]) -> moe_noise:
-    return moe_noise(eps=_ptr(p.get("eps")), eps_p=_ptr(p.get("eps_p")))
+    """The noise tensors of p, or, when p holds "noise_seed", noise drawn
+    inside the kernels from that seed (the tensors are then not read)."""
+    seed = p.get("noise_seed")
+    if seed is not None:
+        return moe_noise(eps=None, eps_p=None, seed=int(seed), in_kernel=1)
+    return moe_noise(eps=_ptr(p.get("eps")), eps_p=_ptr(p.get("eps_p")), seed=0, in_kernel=0)
+
+
+def draw_noise(cfg: MoEConfig, seed: int, tokens: Optional[int] = None, device="cuda"):
+    """The generator's draws for `seed` as tensors: (eps, eps_p)."""
+    T = cfg.tokens if tokens is None else tokens
+    if cfg.hierarchical:
+        eps = torch.empty((T, cfg.n_groups, cfg.experts_per_group), dtype=torch.float32,
+                          device=device)
+        eps_p = torch.empty((T, cfg.n_groups), dtype=torch.float32, device=device)
+    else:
+        eps = torch.empty((T, cfg.n_experts), dtype=torch.float32, device=device)
+        eps_p = None
+    c = make_config(cfg, T)
+    _check(load().moe_draw_noise(ctypes.byref(c), int(seed), _ptr(eps), _ptr(eps_p), _stream()),
+           "moe_draw_noise")
+    return eps, eps_p
 
 
 def packed_experts_size(cfg: MoEConfig) -> int:

@@ -158,6 +158,23 @@ bool gate_packable(const moe_config* c) {
 int gate_pack_groups(const moe_config* c) { return c->n_groups > 0 ? c->n_groups : 1; }
 int gate_pack_tables(const moe_config* c) { return c->noisy ? 2 : 1; }
 
+// The noise source of a kernel: the generator when the caller asks for it,
+// else the caller's tensor (stream 1: the hierarchy's primary noise).
+NoiseSrc noise_src(const moe_noise* n, const float* eps, int stream) {
+  NoiseSrc s;
+  if (n && n->in_kernel) {
+    s.gen = 1;
+    s.k0 = (uint32_t)(n->seed & 0xFFFFFFFFu);
+    s.k1 = (uint32_t)(n->seed >> 32);
+    s.stream = stream;
+  } else {
+    s.eps = eps;
+  }
+  return s;
+}
+
+bool has_noise(const moe_noise* n, const float* eps) { return (n && n->in_kernel) || eps; }
+
 moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_params* p,
                              const moe_noise* n) {
   if (!x && c->tokens > 0) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
@@ -166,7 +183,8 @@ moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_param
   // an empty batch reads no activations and no noise
   const bool rows = c->tokens > 0;
   if (c->noisy) {
-    if (rows && (!n || !n->eps)) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps");
+    if (rows && !has_noise(n, n ? n->eps : nullptr))
+      return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps (or noise drawn in the kernels)");
     if (!p->w_noise) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs w_noise");
   }
   if (p->w_gate_packed) {
@@ -178,7 +196,7 @@ moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_param
   if (c->n_groups > 0) {
     if (!p->w_gate_p) return fail(MOE_ERR_INVALID_ARG, "hierarchy needs w_gate_p");
     if (p->bias) return fail(MOE_ERR_UNSUPPORTED, "bias is supported by the flat gate only");
-    if (c->noisy && ((rows && !n->eps_p) || !p->w_noise_p))
+    if (c->noisy && ((rows && !has_noise(n, n->eps_p)) || !p->w_noise_p))
       return fail(MOE_ERR_INVALID_ARG, "noisy hierarchy needs eps_p and w_noise_p");
   }
   return MOE_OK;
@@ -228,7 +246,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
     a.w_gate = p->w_gate;
     a.w_noise = noisy ? p->w_noise : nullptr;
     a.bias = p->bias;
-    a.eps = noisy ? n->eps : nullptr;
+    a.noise = noisy ? noise_src(n, n->eps, 0) : NoiseSrc();
     a.T = c->tokens;
     a.d = c->d_model;
     a.E = c->n_experts;
@@ -251,7 +269,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   a.w_gate = p->w_gate_p;
   a.w_noise = noisy ? p->w_noise_p : nullptr;
   a.bias = nullptr;
-  a.eps = noisy ? n->eps_p : nullptr;
+  a.noise = noisy ? noise_src(n, n->eps_p, 1) : NoiseSrc();
   a.T = c->tokens;
   a.d = c->d_model;
   a.E = G;
@@ -285,7 +303,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   ga.x = x;
   ga.w_gate = p->w_gate;
   ga.w_noise = noisy ? p->w_noise : nullptr;
-  ga.eps = noisy ? n->eps : nullptr;
+  ga.noise = noisy ? noise_src(n, n->eps, 0) : NoiseSrc();
   ga.d = c->d_model;
   ga.G = G;
   ga.Eg = c->n_experts / G;
@@ -569,7 +587,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   ga.w_gate = p->w_gate;
   ga.w_noise = noisy ? p->w_noise : nullptr;
   ga.bias = p->bias;
-  ga.eps = noisy && n ? n->eps : nullptr;
+  ga.noise = noisy && n ? noise_src(n, n->eps, 0) : NoiseSrc();
   ga.w_pack = p->w_gate_packed;
   ga.pack_nt = gate_pack_tables(c);
   ga.idx = sv->topk_idx;
@@ -918,6 +936,16 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
   return ok();
 }
 
+moe_status moe_draw_noise(const moe_config* cfg, uint64_t seed, float* eps, float* eps_p,
+                          void* stream) {
+  MOE_TRY(check_config(cfg));
+  if (eps_p && cfg->n_groups == 0) return fail(MOE_ERR_INVALID_ARG, "eps_p is for the hierarchy");
+  MOE_TRY(hip_status(launch_draw_noise(cfg->tokens, cfg->n_experts, cfg->n_groups, seed, eps, eps_p,
+                                       (hipStream_t)stream),
+                     "draw noise"));
+  return ok();
+}
+
 // ---- backward ---------------------------------------------------------------
 
 size_t moe_backward_workspace_size(const moe_config* cfg) {
@@ -953,7 +981,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* 
   if (!sv->offsets) return fail(MOE_ERR_INVALID_ARG, "saved offsets is NULL");
   if (rows) {
     if (!x || !dy) return fail(MOE_ERR_INVALID_ARG, "x / dy is NULL");
-    if (noisy && (!noise || !noise->eps)) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps");
+    if (noisy && !has_noise(noise, noise ? noise->eps : nullptr))
+      return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps (or noise drawn in the kernels)");
     if (!sv->topk_idx || !sv->topk_gate || !sv->perm || !sv->inv || !sv->y_sorted)
       return fail(MOE_ERR_INVALID_ARG, "saved topk_idx / topk_gate / perm / inv / y_sorted is NULL");
     if (w_importance != 0.f && !sv->importance)

@@ -196,9 +196,15 @@ __device__ __forceinline__ void bw_block_scores(const BwGateArgs& a, const BwTil
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e = blk + w * 32 + (lane & 31);
   const bool ev = e < a.E;
+  if (NOISY) {
+    float ev16[16];
+    a.noise.rows16(0, 1, e, a.E, [&](int r) { return sh.rows[acc_row(r, lane)]; }, ev16);
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    es[r] = (NOISY && ev) ? a.eps[(int64_t)sh.rows[acc_row(r, lane)] * a.E + e] : 0.f;
+    for (int r = 0; r < 16; ++r) es[r] = ev ? ev16[r] : 0.f;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) es[r] = 0.f;
+  }
   const TileX<T> tx{(const T*)a.x, sh.rows, XLDS ? Xs : nullptr, xld};
   const GateTabs tb{a.w_gate, a.w_noise, 0, (const bf16_t*)a.w_pack, 0, a.pack_nt};
   f32x16 ac[1], ar[1];

@@ -141,13 +141,14 @@ __device__ __forceinline__ float load_column_sum(const f32x16& clean, const f32x
 }
 
 // The scoring and selection of one tile of RB 32-row blocks against experts
-// [0, E) of a table block (tb).  eps_row(r) gives the noise row of tile row r
+// [0, E) of a table block (tb).  eps_at(i, e, out) gives the noise of expert
+// e for the 16 accumulator rows of block i (all lanes call it together)
 // (experts contiguous); Hs is the R x HLD score block in LDS.  On return every
 // lane of a row's group holds the row's top-K1 in ov/oe, and cs/ss the clean
 // scores (bias included) and noise scales of the last expert block.
 template <typename T, int K1, bool NOISY, bool XLDS, int RB, typename EpsRow>
 __device__ void score_tile(const TileX<T>& tx, int d, const GateTabs& tb,
-                           const float* __restrict__ bias, int E, EpsRow eps_row, float* Hs,
+                           const float* __restrict__ bias, int E, EpsRow eps_at, float* Hs,
                            float* ov, int* oe, f32x16 (&cs)[RB], f32x16 (&ss)[RB]) {
   using GT = GateTile<RB>;
   constexpr int TPR = GT::TPR, NQ = GT::NQ;
@@ -161,10 +162,14 @@ __device__ void score_tile(const TileX<T>& tx, int d, const GateTabs& tb,
     // noise of this lane's (row, expert) pairs, requested before the MFMAs
     float ep[RB][16];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < RB; ++i) {
+      if (NOISY) {
+        eps_at(i, e, ep[i]);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ep[i][r] = (NOISY && ev) ? eps_row(32 * i + acc_row(r, lane))[e] : 0.f;
+        for (int r = 0; r < 16; ++r) ep[i][r] = 0.f;
+      }
+    }
     f32x16 ac[RB], ar[RB];
     BlockProj<T, NOISY, XLDS, RB>::run(tx, d, tb, blk, E, ac, ar);
     const float b = (bias && ev) ? bias[tb.row0 + e] : 0.f;
@@ -254,8 +259,10 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
   if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, R, Xs, xld);
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
-  const float* eps = a.eps;
-  auto eps_row = [&](int r) -> const float* { return eps + (int64_t)rows[r] * E; };
+  const NoiseSrc& noise = a.noise;
+  auto eps_row = [&](int i, int e, float (&out)[16]) {
+    noise.rows16(0, 1, e, E, [&](int r) { return rows[32 * i + acc_row(r, threadIdx.x & 63)]; }, out);
+  };
   float ov[K1];
   int oe[K1];
   f32x16 cs[RB], ss[RB];
@@ -370,8 +377,10 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const int Eg = a.Eg, G = a.G;
-  const float* eps = a.eps;
-  auto eps_row = [&](int r) -> const float* { return eps + ((int64_t)rows[r] * G + g) * Eg; };
+  const NoiseSrc& noise = a.noise;
+  auto eps_row = [&](int i, int j, float (&out)[16]) {
+    noise.rows16(g, G, j, Eg, [&](int r) { return rows[32 * i + acc_row(r, threadIdx.x & 63)]; }, out);
+  };
   float ov[K1];
   int oe[K1];
   f32x16 cs[1], ss[1];
@@ -533,7 +542,7 @@ static hipError_t launch_flat_k(const GateFlatArgs& a, bool noisy, hipStream_t s
 
 template <typename T>
 static hipError_t launch_flat_t(const GateFlatArgs& a, hipStream_t s) {
-  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
+  const bool noisy = a.noise.on() && a.w_noise != nullptr;
   if (a.k + 1 <= 3) return launch_flat_k<T, 3>(a, noisy, s);
   if (a.k + 1 <= 5) return launch_flat_k<T, 5>(a, noisy, s);
   return launch_flat_k<T, 9>(a, noisy, s);
@@ -558,7 +567,7 @@ static hipError_t launch_group_v(const GateGroupArgs& a, int grid, size_t sh, hi
 
 template <typename T, int K1>
 static hipError_t launch_group_k(const GateGroupArgs& a, int grid, size_t sh, hipStream_t s) {
-  const bool noisy = a.eps != nullptr && a.w_noise != nullptr;
+  const bool noisy = a.noise.on() && a.w_noise != nullptr;
   if constexpr (sizeof(T) == 2) {
     if (xtile_in_lds(true, a.d))
       return noisy ? launch_group_v<T, K1, true, true>(a, grid, sh, s)

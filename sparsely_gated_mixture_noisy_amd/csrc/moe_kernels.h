@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "noise.h"
+
 namespace moe {
 
 // ----------------------------------------------------------------- gate ----
@@ -11,7 +13,7 @@ struct GateFlatArgs {
   const void* w_gate;   // [E][d]
   const void* w_noise;  // [E][d] or null
   const float* bias;    // [E] or null
-  const float* eps;     // [T][E] or null
+  NoiseSrc noise;       // [T][E] tensor or generator; off: noise-free
   int64_t T;
   int d, E, k;
   int32_t* idx;   // [T][k]
@@ -37,7 +39,7 @@ struct GateGroupArgs {
   const void* x;
   const void* w_gate;   // [E][d], group g = rows g*Eg ..
   const void* w_noise;  // [E][d] or null
-  const float* eps;     // [T][G][Eg] or null
+  NoiseSrc noise;       // [T][G][Eg] tensor or generator; off: noise-free
   int d, G, Eg, kg, kpg;
   const int32_t* perm_g;     // group routing of the primary selection
   const int32_t* offsets_g;  // [G+1]
@@ -176,7 +178,7 @@ struct BwGateArgs {
   const void* w_gate;
   const void* w_noise;   // null: noise-free gate
   const float* bias;
-  const float* eps;      // [T][E] (noisy)
+  NoiseSrc noise;        // [T][E] tensor or generator (noisy)
   const void* w_pack = nullptr;
   int pack_nt = 0;
   const int32_t* idx;    // [T][k]
@@ -239,4 +241,11 @@ hipError_t launch_bw_gather_rows(const void* src, const int32_t* perm, int k, co
 int bw_tile_rows();
 hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s);
 
+}  // namespace moe
+
+namespace moe {
+// eps [T][E] (flat) or eps [T][G][Eg] and eps_p [T][G] (hierarchy, G > 0)
+// drawn from the generator; either may be null
+hipError_t launch_draw_noise(int64_t T, int E, int G, uint64_t seed, float* eps, float* eps_p,
+                             hipStream_t s);
 }  // namespace moe

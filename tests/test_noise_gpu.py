@@ -1,0 +1,105 @@
+"""Noise drawn inside the kernels (moe_noise.in_kernel) from the
+counter-based generator, against the oracle's own implementation of the same
+generator (Philox4x32-10 and Box-Muller, written from their published
+definitions; the two share no code).
+
+Bar: the draws written out by moe_draw_noise within 4e-6 (1 + |z|) of the
+oracle's fp64 ones (fp32 logarithm, square root and sine / cosine); layers
+gated by in-kernel noise meet the forward parity bar against the oracle fed
+its own draws; and drawing inside the kernels gives bitwise the results of
+reading the drawn tensors."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_check import (check_balance, check_close, check_gate, check_routing, excluded, np_)
+from sparsely_gated_mixture_noisy_amd import _lib as L
+from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs, make_upstream
+
+pytestmark = pytest.mark.gpu
+
+SEED = (0x5EED << 32) | 0x1234ABCD
+RTOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("name", ["flat", "hier"])
+def test_drawn_noise_matches_oracle(name):
+    cfg = (CONFIGS["flat256"].replace(tokens=600) if name == "flat"
+           else CONFIGS["hier4096"].replace(tokens=120))
+    eps, eps_p = L.draw_noise(cfg, SEED)
+    torch.cuda.synchronize()
+    ref = oracle.draw_noise(cfg, SEED)
+    for got, r in ((eps, ref["eps"]), (eps_p, ref["eps_p"])):
+        if r is None:
+            assert got is None
+            continue
+        g = np_(got).astype(np.float64)
+        assert g.shape == r.shape
+        err = np.abs(g - r)
+        assert (err <= 4e-6 * (1.0 + np.abs(r))).all(), f"max err {err.max():.3e}"
+    z = np_(eps).ravel()
+    assert abs(z.mean()) < 0.01 and abs(z.std() - 1.0) < 0.01
+
+
+CASES = {
+    "tiny": CONFIGS["tiny"],
+    "flat256_t1000": CONFIGS["flat256"].replace(tokens=1000),
+    "zipf_t600": CONFIGS["zipf2048"].replace(tokens=600),
+    "hier_t300": CONFIGS["hier4096"].replace(tokens=300),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_with_in_kernel_noise(name):
+    cfg = CASES[name]
+    _say(f"[noise] {name}: {cfg}")
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    gen = dict(inp, eps=None, eps_p=None, noise_seed=SEED)
+    out = L.forward(cfg, inp["x"], gen, gen)
+    torch.cuda.synchronize()
+    # the oracle with its own draws of the same generator
+    cpu = {k: (v.to("cpu") if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    drawn = oracle.draw_noise(cfg, SEED)
+    cpu["eps"] = drawn["eps"]
+    cpu["eps_p"] = drawn["eps_p"]
+    ref = oracle.forward(cpu, cfg)
+    excl = excluded(ref)
+    check_gate(out.topk_idx, out.topk_gate, ref, excl)
+    rows = np.nonzero(~excl)[0]
+    worst = check_close(out.y, ref["y"], RTOL[cfg.dtype], rows=rows)
+    check_balance(out.importance, out.load, out.balance, ref, excl, ref["idx"],
+                  smooth=(cfg.noisy and not cfg.hierarchical))
+    # drawing inside the kernels = reading the same draws from tensors
+    eps, eps_p = L.draw_noise(cfg, SEED)
+    tens = dict(inp, eps=eps, eps_p=eps_p)
+    out2 = L.forward(cfg, inp["x"], tens, tens)
+    torch.cuda.synchronize()
+    for a, b in ((out.topk_idx, out2.topk_idx), (out.topk_gate, out2.topk_gate), (out.y, out2.y),
+                 (out.balance, out2.balance)):
+        assert torch.equal(a, b)
+    _say(f"[noise] {name}: ok excluded={int(excl.sum())} worst_y={worst:.2e}")
+
+
+def test_backward_with_in_kernel_noise():
+    """The backward recomputes the noisy scores with the same in-kernel draws."""
+    cfg = CONFIGS["flat256"].replace(tokens=300, n_experts=24, d_model=128, d_hidden=256)
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    gen = dict(inp, eps=None, noise_seed=SEED)
+    dy = make_upstream(cfg, seed=0, device="cuda")
+    fwd = L.forward(cfg, inp["x"], gen, gen, save=True)
+    g_gen = L.backward(cfg, inp["x"], gen, gen, fwd, dy)
+    eps, _ = L.draw_noise(cfg, SEED)
+    tens = dict(inp, eps=eps)
+    fwd2 = L.forward(cfg, inp["x"], tens, tens, save=True)
+    g_ten = L.backward(cfg, inp["x"], tens, tens, fwd2, dy)
+    torch.cuda.synchronize()
+    for key in ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw2"):
+        assert torch.equal(getattr(g_gen, key), getattr(g_ten, key)), key
