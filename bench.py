@@ -38,7 +38,7 @@ EXPERT_TRAFFIC = {
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "95b6d549653b46f36106f5e50c500bbbfcae82e87044ee1065626a73ec9d2c4a",
+    "sources_sha256": "d902b71f0c2d9cc29dbf44848f1e4d3ff3fff40f6215281d1b21006ec8427acf",
     "fetch_kib": 288812.2, "fetch_scale": 524288.0 / 262156.0,
     "write_kib": 32768.0, "write_scale": 524288.0 / 524288.0,
 }
