@@ -174,7 +174,7 @@ def backward_work(cfg, hit):
     return flops, tables + acts + noise
 
 
-def backward_line(L, cfg, inp, fwd_ms, steps, warmup, hit):
+def backward_line(L, cfg, inp, fwd_ms, steps, warmup, hit, cpu_budget=0.0):
     """moe_backward timed on the forward's saved tensors (HIP events around
     `steps` calls after `warmup`), with the gradients of sum(dy * y) + CV^2
     losses of weight 1 for a seeded dy."""
@@ -197,12 +197,47 @@ def backward_line(L, cfg, inp, fwd_ms, steps, warmup, hit):
     print(f"[bench] moe_backward {bms:.4f} ms/step", file=sys.stderr, flush=True)
     flops, nbytes = backward_work(cfg, hit)
     peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-    return {"ms_per_step": bms, "tokens_per_s": cfg.tokens / (bms * 1e-3),
+    line = {"ms_per_step": bms, "tokens_per_s": cfg.tokens / (bms * 1e-3),
             "train_step_tokens_per_s": cfg.tokens / ((bms + fwd_ms) * 1e-3),
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "flops": flops, "mfma_frac": flops / (bms * 1e-3) / 1e12 / peak_tf,
             "note": "gradients of x, gate tables, bias and expert tables; "
                     "forward tensors saved by moe_forward"}
+    if cpu_budget > 0:
+        line["cpu_baseline"] = cpu_backward_baseline(cfg, inp, dy, cpu_budget)
+    return line
+
+
+def cpu_backward_baseline(cfg, inp, dy, budget_s):
+    """The oracle's backward (which runs its own forward first), as it is, on
+    the first S tokens of the same inputs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cpu = {k: (v.detach().cpu() if v is not None else None) for k, v in inp.items()}
+    w = {k: (oracle.moe_oracle._f64(cpu[k]) if cpu.get(k) is not None else None)
+         for k in ("w1", "w2", "w3")}
+    dyc = dy.detach().cpu()
+    S = min(cfg.tokens, 256)
+    while True:
+        sample = dict(cpu)
+        for k in ("x", "eps"):
+            if sample.get(k) is not None:
+                sample[k] = sample[k][:S]
+        sample.update(w)
+        c = cfg.replace(tokens=S)
+        t0 = time.perf_counter()
+        oracle.backward(sample, c, dyc[:S], 1.0, 1.0)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or S >= cfg.tokens:
+            break
+        S = min(cfg.tokens, S * 2)
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.tokens} tokens, oracle backward (its forward "
+                      f"included), fp64 numpy, {dt:.2f} s"}
 
 
 def cpu_baseline(cfg, inp, budget_s):
@@ -248,7 +283,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; about 40 ms of work lets the clocks settle")
     ap.add_argument("--config", default="flat256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -353,8 +389,9 @@ def main():
         res["experts_hit"] = hit
     res["counts_max_over_mean"] = float(counts.max() / max(counts.mean(), 1e-9))
     if not args.no_backward and not cfg.hierarchical:
-        res["backward"] = backward_line(L, cfg, inp, fwd_ms=ms, steps=args.steps,
-                                        warmup=args.warmup, hit=hit)
+        res["backward"] = backward_line(
+            L, cfg, inp, fwd_ms=ms, steps=args.steps, warmup=args.warmup, hit=hit,
+            cpu_budget=0.0 if args.no_cpu_baseline else args.cpu_budget / 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(res), flush=True)
