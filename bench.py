@@ -157,6 +157,32 @@ def expert_work(cfg, counts):
     return flops, wbytes + abytes, hit
 
 
+def stage_bytes(cfg):
+    """Algorithmic HBM bytes of the gate, route and combine stages: what each
+    must read once and write once, with no intermediate of this library.
+    gate: x, the noise it reads (hierarchy: the primary noise and the chosen
+    groups' secondary noise), the gate tables once, bias, and idx, gates and
+    thr written.  route: idx read; counts, offsets, perm and inv written.
+    combine: the routed expert outputs, inv and the gates read, y written."""
+    T, d, E, k = cfg.tokens, cfg.d_model, cfg.n_experts, cfg.top_k
+    A = T * k
+    el = 2 if cfg.dtype == "bf16" else 4
+    tabs = 2 if cfg.noisy else 1
+    if cfg.hierarchical:
+        G, Eg = cfg.n_groups, cfg.experts_per_group
+        tables = tabs * d * (G + G * Eg) * el
+        noise = (T * G + T * cfg.k_groups * Eg) * 4 if cfg.noisy else 0
+        thr = 0
+    else:
+        tables = tabs * d * E * el
+        noise = T * E * 4 if cfg.noisy else 0
+        thr = T * 2 * 4
+    gate = T * d * el + noise + tables + E * 4 + A * 8 + thr
+    route = A * 4 + (2 * E + 1) * 4 + A * 8
+    combine = A * d * el + A * 8 + T * d * el
+    return {"gate": gate, "route": route, "combine": combine}
+
+
 def backward_work(cfg, hit):
     """Algorithmic flops and HBM bytes of one backward pass: the hidden layer
     recomputed and four more products per routed row (dHid, dX and the two
@@ -384,6 +410,11 @@ def main():
                            "kernel": "expert FFN stage (moe_expert_ffn)",
                            "bytes_per_launch": ebytes}
         res["stages_ms"] = stages
+        sb = stage_bytes(cfg)
+        res["stages_hbm"] = {
+            name: {"bytes": b, "gbs": b / (stages[name] * 1e-3) / 1e9,
+                   "frac": b / (stages[name] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            for name, b in sb.items()}
         res["expert_tflops"] = tflops
         res["expert_mfma_frac"] = tflops / peak_tf
         res["experts_hit"] = hit
