@@ -44,12 +44,14 @@ the design notes):
   * the SwiGLU expert is (silu(X W_gate) * (X W_up)) W_down, no biases.
   * parity unpinned: the hierarchical load (reported as hard counts per
     expert) has no page formula.
-  * backward pass (flat gate only): the objective is sum(dy * y) +
-    w_imp CV^2(Importance) + w_load CV^2(Load); the kept set and the experts
-    ranked k-th and (k+1)-th are held fixed (the choice itself has no
-    gradient), so the threshold theta of the smooth load passes its gradient
-    to the score of the expert it was read from; noise-free gating has a
-    hard load and no load gradient.
+  * backward pass: the objective is sum(dy * y) + w_imp CV^2(Importance) +
+    w_load CV^2(Load); the kept set and the experts ranked k-th and (k+1)-th
+    are held fixed (the choice itself has no gradient), so the threshold
+    theta of the smooth load passes its gradient to the score of the expert
+    it was read from; noise-free gating and the hierarchy have a hard load
+    and no load gradient; in the hierarchy the product of the two levels'
+    gates passes its gradient to each level, which then differentiates like
+    a flat gate over its kept scores.
 
 Array layouts follow the library's: x [T][d]; w_gate, w_noise [E][d] (the
 pages' d x n table stored transposed); w1 [E][h][d]; w3 [E][h][d]; w2 [E][d][h].
@@ -521,23 +523,22 @@ def expert_swiglu_backward(X, w1_e, w3_e, w2_e, dY):
 
 
 def backward(inp: Dict, cfg, dy, w_importance=1.0, w_load=1.0) -> Dict:
-    """Gradients of L (see above) for the flat gate, ReLU or SwiGLU experts.
+    """Gradients of L (see above), flat or hierarchical gate, ReLU or SwiGLU
+    experts.
 
     Returns dx [T][d], dw_gate [E][d], dw_noise [E][d] (None without noise),
-    dbias [E], dw1 [E][h][d], dw3 (SwiGLU, else None), dw2 [E][d][h], and the
-    intermediates dgate [T][k] (gradient of the kept gates) and dH [T][E]
-    (gradient of the noisy scores).
+    dbias [E] (None for the hierarchy, which has no bias), dw1 [E][h][d], dw3
+    (SwiGLU, else None), dw2 [E][d][h], for the hierarchy dw_gate_p [G][d] and
+    dw_noise_p [G][d], and the intermediates dgate [T][k] (gradient of the
+    kept gates) and dH [T][E] (gradient of the noisy scores; the hierarchy
+    adds dH_p [T][G]).
     """
-    if cfg.n_groups:
-        raise NotImplementedError("the backward pass covers the flat gate")
     x = _f64(inp["x"])
     dy = _f64(dy)
     fw = forward(inp, cfg, w_importance, w_load)
     g = fw["gate_info"]
     idx, gates, inv = fw["idx"], fw["gates"], fw["inv"]
     T, k = idx.shape
-    E = cfg.n_experts
-    rows = np.arange(T)
 
     # combine: y_t = sum over the kept slots of gate[t,s] * y_sorted[inv[t,s]]
     inv2 = inv.reshape(T, k)
@@ -547,6 +548,23 @@ def backward(inp: Dict, cfg, dy, w_importance=1.0, w_load=1.0) -> Dict:
     dgate = np.einsum("tsd,td->ts", y_rows, dy) if T else np.zeros((0, k))
     # importance: d Importance_e / d G[t,e] = 1 for every kept (t, e)
     dgate = dgate + w_importance * cv_squared_grad(fw["importance"])[idx]
+    if cfg.n_groups:
+        res = _hier_gate_backward(inp, cfg, x, g, dgate)
+    else:
+        res = _flat_gate_backward(inp, cfg, x, fw, dgate, w_load)
+    dx = res.pop("dx")
+    _expert_backward(inp, cfg, x, dy, fw, dx, res)
+    return dict(dx=dx, dgate=dgate, forward=fw, **res)
+
+
+def _flat_gate_backward(inp, cfg, x, fw, dgate, w_load):
+    """The flat gate's share: softmax over the kept scores, the smooth load,
+    the noisy score, the two projections and the bias."""
+    g = fw["gate_info"]
+    idx, gates = fw["idx"], fw["gates"]
+    T, k = idx.shape
+    E = cfg.n_experts
+    rows = np.arange(T)
     # softmax over the kept scores
     dH_kept = gates * (dgate - (gates * dgate).sum(axis=1, keepdims=True))
     dH = np.zeros((T, E))
@@ -592,9 +610,77 @@ def backward(inp: Dict, cfg, dy, w_importance=1.0, w_load=1.0) -> Dict:
     dx = dclean @ _f64(inp["w_gate"])
     if draw is not None:
         dx = dx + draw @ _f64(inp["w_noise"])
+    return dict(dx=dx, dw_gate=dw_gate, dw_noise=dw_noise, dbias=dbias, dH=dH)
 
-    # experts: the rows of expert e are the tokens perm[p] // k, and the
-    # gradient flowing into row p is gate[t,s] * dy[t]
+
+def _hier_gate_backward(inp, cfg, x, g, dgate):
+    """The hierarchy's share.  A kept gate is gp[a] * gs[a, b]: the primary
+    softmax weight of kept group a times the secondary softmax weight of its
+    kept expert b, so d gs[a, b] = dgate * gp[a] and d gp[a] = sum over b of
+    dgate * gs[a, b]; each level then differentiates like a flat gate over its
+    kept scores (softmax, noisy score, projections).  The hierarchy's load is
+    a hard count, so no load gradient reaches either level."""
+    T, k = g["idx"].shape
+    E, G = cfg.n_experts, cfg.n_groups
+    Eg, kg, kpg = E // G, cfg.k_groups, cfg.k_per_group
+    prim = g["primary"]
+    wg, wn = _f64(inp["w_gate"]), _f64(inp.get("w_noise"))
+    wgp, wnp = _f64(inp["w_gate_p"]), _f64(inp.get("w_noise_p"))
+    eps, eps_p = _f64(inp.get("eps")), _f64(inp.get("eps_p"))
+    noisy = wn is not None and eps is not None
+    noisy_p = wnp is not None and eps_p is not None
+    dclean_p = np.zeros((T, G))
+    draw_p = np.zeros((T, G))
+    dclean = np.zeros((T, E))
+    draw = np.zeros((T, E))
+    for t in range(T):
+        gp = prim["gates"][t]                       # [kg], kept groups ascending
+        dgp = np.zeros(kg)
+        for a in range(kg):
+            grp = int(prim["idx"][t, a])
+            sub = slice(grp * Eg, (grp + 1) * Eg)
+            sec = flat_gate(x[t:t + 1], wg[sub], None if not noisy else wn[sub], None,
+                            None if not noisy else eps[t:t + 1, grp, :], kpg)
+            gs = sec["gates"][0]                    # [kpg], kept experts ascending
+            dg = dgate[t, a * kpg:(a + 1) * kpg]
+            dgp[a] = (dg * gs).sum()
+            dgs = dg * gp[a]
+            dHs = gs * (dgs - (gs * dgs).sum())
+            for b in range(kpg):
+                j = int(sec["idx"][0, b])
+                e = grp * Eg + j
+                dclean[t, e] += dHs[b]
+                if noisy:
+                    # H = clean + eps * softplus(raw): d raw = dH * eps * sigmoid(raw)
+                    raw = float(x[t] @ wn[e])
+                    draw[t, e] += dHs[b] * eps[t, grp, j] * sigmoid(raw)
+        dHp = gp * (dgp - (gp * dgp).sum())
+        for a in range(kg):
+            grp = int(prim["idx"][t, a])
+            dclean_p[t, grp] += dHp[a]
+            if noisy_p:
+                raw = float(x[t] @ wnp[grp])
+                draw_p[t, grp] += dHp[a] * eps_p[t, grp] * sigmoid(raw)
+    dx = dclean_p @ wgp + dclean @ wg
+    res = dict(dw_gate_p=dclean_p.T @ x, dw_gate=dclean.T @ x, dbias=None,
+               dH=dclean, dH_p=dclean_p, dw_noise=None, dw_noise_p=None)
+    if noisy:
+        dx = dx + draw @ wn
+        res["dw_noise"] = draw.T @ x
+    if noisy_p:
+        dx = dx + draw_p @ wnp
+        res["dw_noise_p"] = draw_p.T @ x
+    res["dx"] = dx
+    return res
+
+
+def _expert_backward(inp, cfg, x, dy, fw, dx, res):
+    """The experts' share, added into dx; writes dw1, dw2 (dw3) into res.
+    The rows of expert e are the tokens perm[p] // k, and the gradient
+    flowing into row p is gate[t,s] * dy[t]."""
+    gates = fw["gates"]
+    k = gates.shape[1]
+    E = cfg.n_experts
     w1, w2 = _f64(inp["w1"]), _f64(inp["w2"])
     w3 = _f64(inp.get("w3"))
     perm, offsets = fw["perm"], fw["offsets"]
@@ -615,8 +701,7 @@ def backward(inp: Dict, cfg, dy, w_importance=1.0, w_load=1.0) -> Dict:
         else:
             dX, dw1[e], dw3[e], dw2[e] = expert_swiglu_backward(X, w1[e], w3[e], w2[e], dY)
         np.add.at(dx, toks, dX)
-    return dict(dx=dx, dw_gate=dw_gate, dw_noise=dw_noise, dbias=dbias, dw1=dw1,
-                dw3=dw3, dw2=dw2, dgate=dgate, dH=dH, forward=fw)
+    res.update(dw1=dw1, dw2=dw2, dw3=dw3)
 
 
 # ---------------------------------------------------------------------------

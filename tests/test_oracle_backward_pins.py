@@ -198,3 +198,83 @@ def test_normal_pdf_and_sigmoid_closed_forms():
     num = (oracle.normal_cdf(z + h) - oracle.normal_cdf(z - h)) / (2 * h)
     assert np.allclose(oracle.normal_pdf(z), num, rtol=1e-7, atol=1e-10)
     assert np.allclose(oracle.sigmoid(z), 1.0 / (1.0 + np.exp(-z)), rtol=1e-14)
+
+
+HIER_FD_CASES = [
+    dict(ffn="relu", noisy=True, wi=0.7, wl=1.0),
+    dict(ffn="swiglu", noisy=False, wi=1.1, wl=0.0),
+    dict(ffn="relu", noisy=True, wi=0.0, wl=0.0, k_groups=1, k_per_group=3),
+    dict(ffn="relu", noisy=True, wi=0.5, wl=0.0, k_groups=3, k_per_group=1, capacity=3),
+]
+
+
+def _hier_cfg(**kw):
+    base = dict(name="bwh", tokens=6, d_model=5, n_experts=12, d_hidden=7, noisy=True,
+                dtype="f32", gate_std=0.6, n_groups=3, k_groups=2, k_per_group=2)
+    base.update(kw)
+    base["top_k"] = base["k_groups"] * base["k_per_group"]
+    return MoEConfig(**base)
+
+
+@pytest.mark.parametrize("case", HIER_FD_CASES,
+                         ids=lambda c: "-".join(f"{k}={v}" for k, v in c.items()))
+def test_hier_gradients_match_central_differences(case):
+    """The hierarchy: every gradient, both levels' tables included, equals
+    the central difference of the oracle's forward objective (whose hard
+    load does not move under a small perturbation)."""
+    case = dict(case)
+    wi, wl = case.pop("wi"), case.pop("wl")
+    cfg = _hier_cfg(**case)
+    for seed in range(80):
+        inp = _np_inputs(cfg, seed)
+        if _min_margin(inp, cfg) > 5e-3:
+            break
+    else:
+        pytest.fail("no seed with well-separated scores")
+    dy = make_upstream(cfg, seed=seed).double().numpy()
+    bw = oracle.backward(inp, cfg, dy, wi, wl)
+    assert bw["dbias"] is None
+    h = 1e-6
+    names = [("x", "dx"), ("w_gate", "dw_gate"), ("w_gate_p", "dw_gate_p"), ("w1", "dw1"),
+             ("w2", "dw2")]
+    if cfg.noisy:
+        names += [("w_noise", "dw_noise"), ("w_noise_p", "dw_noise_p")]
+    if cfg.ffn == "swiglu":
+        names.append(("w3", "dw3"))
+    for key, gkey in names:
+        base = inp[key]
+        num = np.zeros_like(base)
+        for i in np.ndindex(base.shape):
+            old = base[i]
+            base[i] = old + h
+            fp = _objective(inp, cfg, dy, wi, wl)
+            base[i] = old - h
+            fm = _objective(inp, cfg, dy, wi, wl)
+            base[i] = old
+            num[i] = (fp - fm) / (2 * h)
+        ana = bw[gkey]
+        scale = max(1.0, np.abs(num).max())
+        assert np.allclose(ana, num, rtol=1e-5, atol=1e-6 * scale), (key, np.abs(ana - num).max())
+
+
+def test_hier_with_one_group_is_the_flat_gate():
+    """One group kept out of one: the primary gate is 1 and has no gradient,
+    and the layer is the flat gate over the group's experts, so every
+    gradient equals the flat backward's (load weight 0: the hierarchy's load
+    is a hard count, the flat noisy gate's a smooth estimate)."""
+    for noisy in (True, False):
+        hcfg = _hier_cfg(n_groups=1, k_groups=1, k_per_group=2, n_experts=5, noisy=noisy)
+        inp = _np_inputs(hcfg, 4)
+        fcfg = _cfg(n_experts=5, top_k=2, noisy=noisy)
+        finp = dict(inp, bias=np.zeros(5), eps=None if inp["eps"] is None else inp["eps"][:, 0, :])
+        dy = make_upstream(hcfg, seed=4).double().numpy()
+        hb = oracle.backward(inp, hcfg, dy, 0.6, 0.0)
+        fb = oracle.backward(finp, fcfg, dy, 0.6, 0.0)
+        for key in ("dx", "dw_gate", "dw_noise", "dw1", "dw2"):
+            if fb[key] is None:
+                assert hb[key] is None
+                continue
+            assert np.allclose(hb[key], fb[key], rtol=1e-12, atol=1e-12), key
+        assert np.allclose(hb["dw_gate_p"], 0.0, atol=1e-12)
+        if noisy:
+            assert np.allclose(hb["dw_noise_p"], 0.0, atol=1e-12)
