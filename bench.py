@@ -38,7 +38,7 @@ EXPERT_TRAFFIC = {
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "d902b71f0c2d9cc29dbf44848f1e4d3ff3fff40f6215281d1b21006ec8427acf",
+    "sources_sha256": "6735a7185c71e1065cd63277267c93032bf595aac16ea1229ff14c2ca7598253",
     "fetch_kib": 288812.2, "fetch_scale": 524288.0 / 262156.0,
     "write_kib": 32768.0, "write_scale": 524288.0 / 524288.0,
 }
@@ -196,7 +196,12 @@ def backward_work(cfg, hit):
     flops = 2.0 * A * cfg.d_model * cfg.d_hidden * prods
     tables = 2 * hit * mats * cfg.d_model * cfg.d_hidden * el
     acts = (3 * cfg.tokens + A) * cfg.d_model * el
-    noise = cfg.tokens * cfg.n_experts * 4 if cfg.noisy else 0
+    if not cfg.noisy:
+        noise = 0
+    elif cfg.hierarchical:  # the draws of the kept groups and kept experts
+        noise = cfg.tokens * (cfg.k_groups + A // cfg.tokens) * 4
+    else:
+        noise = cfg.tokens * cfg.n_experts * 4
     return flops, tables + acts + noise
 
 
@@ -250,7 +255,7 @@ def cpu_backward_baseline(cfg, inp, dy, budget_s):
     S = min(cfg.tokens, 256)
     while True:
         sample = dict(cpu)
-        for k in ("x", "eps"):
+        for k in ("x", "eps", "eps_p"):
             if sample.get(k) is not None:
                 sample[k] = sample[k][:S]
         sample.update(w)
@@ -419,7 +424,7 @@ def main():
         res["expert_mfma_frac"] = tflops / peak_tf
         res["experts_hit"] = hit
     res["counts_max_over_mean"] = float(counts.max() / max(counts.mean(), 1e-9))
-    if not args.no_backward and not cfg.hierarchical:
+    if not args.no_backward:
         res["backward"] = backward_line(
             L, cfg, inp, fwd_ms=ms, steps=args.steps, warmup=args.warmup, hit=hit,
             cpu_budget=0.0 if args.no_cpu_baseline else args.cpu_budget / 2)

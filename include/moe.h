@@ -285,7 +285,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x,
 
 /* ---- Backward pass -------------------------------------------------------
  * Gradients of L = sum(dy * y) + w_importance * CV^2(importance) +
- * w_load * CV^2(load) for the flat gate (n_groups == 0), ReLU or SwiGLU
+ * w_load * CV^2(load) for the flat gate or the hierarchy, ReLU or SwiGLU
  * experts, bf16 or fp32.  dy is the gradient flowing into y from above; the
  * balance losses are those moe_balance_loss defines, added to the objective
  * with the given weights.  The choice of kept experts has no gradient (the
@@ -295,7 +295,13 @@ moe_status moe_forward(const moe_config* cfg, const void* x,
  * kept scores, the noisy scores (section 方法怎么做: the learnable noise), the
  * smooth load estimate (whose threshold passes its gradient to the score it
  * was read from) and the experts.  Hidden activations are recomputed, not
- * saved (paper card, section 瓶颈: activation recomputation).
+ * saved (paper card, section 瓶颈: activation recomputation).  In the
+ * hierarchy a kept gate is the product of the primary (group) and secondary
+ * (expert) softmax weights; the product passes its gradient to both levels,
+ * each of which then differentiates like a flat gate over its kept scores.
+ * The hierarchy's load is a hard count, so w_load adds no gradient there, and
+ * the secondary tables' gradients cover every kept (token, expert) pair of
+ * the gate's choice, dropped by a capacity or not.
  *
  * Tensors saved from the forward pass of the same inputs (moe_forward with
  * the matching moe_outputs fields, or the staged calls). */
@@ -318,22 +324,26 @@ typedef struct moe_grads {
   void* dx;        /* [T][d] */
   void* dw_gate;   /* [E][d] */
   void* dw_noise;  /* [E][d] (noisy only) */
-  float* dbias;    /* [E] */
+  float* dbias;    /* [E] (flat gate only) */
   void* dw1;       /* [E][h][d] */
   void* dw3;       /* [E][h][d] (SwiGLU only) */
   void* dw2;       /* [E][d][h] */
+  void* dw_gate_p;   /* [G][d] (hierarchy only) */
+  void* dw_noise_p;  /* [G][d] (hierarchy and noisy only) */
 } moe_grads;
 
-/* Bytes of workspace moe_backward needs for this configuration (0 when the
- * configuration has no backward pass: the hierarchy). */
+/* Bytes of workspace moe_backward needs for this configuration (0 for an
+ * invalid configuration). */
 size_t moe_backward_workspace_size(const moe_config* cfg);
 
-/* The backward pass.  x, p (w_gate, w_noise, bias, w1, w2, w3; packed tables
- * are optional for the gate and not used for the experts, whose unpacked
- * w1 / w2 / w3 are required), noise (eps, when noisy) and `saved` are the
- * forward's inputs and saved tensors; dy [T][d] is in the cfg dtype.
- * Returns MOE_ERR_UNSUPPORTED for the hierarchy, and for fp32 layers whose
- * d_model or d_hidden is not a multiple of 4.  bf16: products on MFMA
+/* The backward pass.  x, p (w_gate, w_noise, bias, w1, w2, w3, and for the
+ * hierarchy w_gate_p, w_noise_p; packed tables are optional for the gate and
+ * not used for the experts, whose unpacked w1 / w2 / w3 are required), noise
+ * (eps, and eps_p for the hierarchy, when noisy) and `saved` are the
+ * forward's inputs and saved tensors (thr is not needed by the hierarchy);
+ * dy [T][d] is in the cfg dtype.  Returns MOE_ERR_UNSUPPORTED for fp32
+ * layers whose d_model or d_hidden is not a multiple of 4.  The hierarchy's
+ * gate side runs in fp32 arithmetic for both dtypes.  bf16: products on MFMA
  * with fp32 accumulation; fp32 operands (score gradients) and gate-scaled
  * output gradients are rounded to bf16 as they enter a product, the hidden
  * activation and its gradients are rounded to bf16 between products. */

@@ -70,7 +70,8 @@ class moe_saved(ctypes.Structure):
 
 class moe_grads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw3", "dw2")]
+                ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw3", "dw2", "dw_gate_p",
+                 "dw_noise_p")]
 
 
 _P = ctypes.c_void_p
@@ -408,11 +409,17 @@ class Grads:
         self.dw_gate = torch.empty((E, d), dtype=dt, device=device) if tables else None
         self.dw_noise = (torch.empty((E, d), dtype=dt, device=device)
                          if tables and cfg.noisy else None)
-        self.dbias = torch.empty(E, dtype=torch.float32, device=device) if tables else None
+        hier = cfg.hierarchical
+        self.dbias = (torch.empty(E, dtype=torch.float32, device=device)
+                      if tables and not hier else None)
         self.dw1 = torch.empty((E, h, d), dtype=dt, device=device) if tables else None
         self.dw3 = (torch.empty((E, h, d), dtype=dt, device=device)
                     if tables and cfg.ffn == "swiglu" else None)
         self.dw2 = torch.empty((E, d, h), dtype=dt, device=device) if tables else None
+        G = cfg.n_groups
+        self.dw_gate_p = torch.empty((G, d), dtype=dt, device=device) if tables and hier else None
+        self.dw_noise_p = (torch.empty((G, d), dtype=dt, device=device)
+                           if tables and hier and cfg.noisy else None)
 
     def struct(self) -> moe_grads:
         return moe_grads(**{n: _ptr(getattr(self, n)) for n, _ in moe_grads._fields_})

@@ -457,8 +457,11 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
 struct BwLayout {
   size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, hid, dp, db, dxs, part_g,
       part_n, xs, dys;
+  // hierarchy: per-slot and per-group score gradients, and the routing
+  // without capacity (when the forward capped it) for the secondary tables
+  size_t cs, ns, dcp, drp, r_bits, r_base, r_counts, r_offsets, r_perm, r_inv;
   size_t total;
-  int nblk, nchunk;
+  int nblk, nchunk, nb;
   int64_t kchunk;
 };
 
@@ -468,9 +471,14 @@ BwLayout bw_layout(const moe_config* c) {
   const int E = c->n_experts, d = c->d_model, h = c->d_hidden;
   const size_t es = elem_size(c);
   const bool sw = c->ffn == MOE_FFN_SWIGLU;
+  const bool hier = c->n_groups > 0;
+  const int G = hier ? c->n_groups : 0;
+  // rows of the dense gate-table products: the experts, or the hierarchy's groups
+  const int Etab = hier ? G : E;
   L.nblk = (int)((T + 31) / 32);
+  L.nb = (int)((T + ROUTE_BLOCK_TOKENS - 1) / ROUTE_BLOCK_TOKENS);
   // gate-table products: K = tokens split into chunks, enough workgroups
-  const int64_t tiles_mn = ((E + 127) / 128) * (int64_t)((d + 127) / 128);
+  const int64_t tiles_mn = ((Etab + 127) / 128) * (int64_t)((d + 127) / 128);
   int64_t nch = (1024 + tiles_mn - 1) / tiles_mn;
   nch = std::min<int64_t>(nch, std::max<int64_t>(1, (T + 255) / 256));
   nch = std::max<int64_t>(nch, 1);
@@ -484,21 +492,33 @@ BwLayout bw_layout(const moe_config* c) {
     o = align256(o + bytes);
     return at;
   };
+  const bool flat = !hier;
   L.dimp = take(4 * (size_t)E);
   L.dload = take(4 * (size_t)E);
-  L.dhk = take(4 * (size_t)A);
-  L.rinfo = take(16 * (size_t)T);
-  L.dclean = take(4 * (size_t)T * E);
-  L.draw = take(c->noisy ? 4 * (size_t)T * E : 0);
-  L.dbias_part = take(4 * (size_t)L.nblk * E);
+  L.dhk = take(flat ? 4 * (size_t)A : 0);
+  L.rinfo = take(flat ? 16 * (size_t)T : 0);
+  L.dclean = take(flat ? 4 * (size_t)T * E : 0);
+  L.draw = take(flat && c->noisy ? 4 * (size_t)T * E : 0);
+  L.dbias_part = take(flat ? 4 * (size_t)L.nblk * E : 0);
+  L.cs = take(hier ? 4 * (size_t)A : 0);
+  L.ns = take(hier && c->noisy ? 4 * (size_t)A : 0);
+  L.dcp = take(hier ? 4 * (size_t)T * G : 0);
+  L.drp = take(hier && c->noisy ? 4 * (size_t)T * G : 0);
+  const bool reroute = hier && c->capacity > 0;
+  L.r_bits = take(reroute ? 4 * (size_t)L.nb * E : 0);
+  L.r_base = take(reroute ? 4 * (size_t)L.nb * E : 0);
+  L.r_counts = take(reroute ? 4 * (size_t)E : 0);
+  L.r_offsets = take(reroute ? 4 * (size_t)(E + 1) : 0);
+  L.r_perm = take(reroute ? 4 * (size_t)A : 0);
+  L.r_inv = take(reroute ? 4 * (size_t)A : 0);
   L.dxg = take(4 * (size_t)T * d);
   L.tiles = take(4 * (size_t)(E + 1));
   L.hid = take(es * (size_t)A * h);
   L.dp = take(es * (size_t)A * h);
   L.db = take(sw ? es * (size_t)A * h : 0);
   L.dxs = take(4 * (size_t)A * d);
-  L.part_g = take(4 * (size_t)L.nchunk * E * d);
-  L.part_n = take(c->noisy ? 4 * (size_t)L.nchunk * E * d : 0);
+  L.part_g = take(4 * (size_t)L.nchunk * Etab * d);
+  L.part_n = take(c->noisy ? 4 * (size_t)L.nchunk * Etab * d : 0);
   L.xs = take(es * (size_t)A * d);
   L.dys = take(es * (size_t)A * d);
   L.total = o;
@@ -545,6 +565,111 @@ void add_pair(BwGemm& q, const BwOp& a, const BwOp& b) {
   ++q.npair;
 }
 
+// A gate table's gradient: out[rows][d] = coef^T x for coef [T][rows] fp32,
+// the tokens split into chunks whose partial products are summed in order.
+moe_status gate_table_grad(const moe_config* c, const BwLayout& L, const void* x,
+                           const float* coef, int rows, void* out, float* part, hipStream_t s) {
+  if (!out) return MOE_OK;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool f32 = !bf16;
+  const int d = c->d_model;
+  BwGemm q = product(op_cols(coef, rows, true), op_cols(x, d, f32));
+  q.mode = BW_PLAIN;
+  // bf16 products carry the fp32 score gradients as hi + lo halves
+  if (bf16) add_pair(q, low_half(q.a[0]), q.b[0]);
+  q.M = rows;
+  q.N = d;
+  q.K = c->tokens;
+  q.kchunk = L.kchunk;
+  q.C = part;
+  q.c_f32 = 1;
+  q.ldc = d;
+  q.c_chunk = (int64_t)rows * d;
+  const int64_t grid = (int64_t)L.nchunk * ((rows + 127) / 128) * ((d + 127) / 128);
+  MOE_TRY(hip_status(launch_bw_gemm(q, bf16, grid, s), "backward gate tables"));
+  return hip_status(launch_bw_sum_chunks(part, L.nchunk, (int64_t)rows * d, bf16, out, s),
+                    "backward gate table sum");
+}
+
+// The hierarchy's gate side: score gradients of both levels and dx's share
+// (one wave per token), the primary tables as dense products over tokens,
+// the secondary tables as per-expert sums over the routed rows of the
+// gate's choice (rerouted without the capacity when the forward dropped).
+moe_status hier_gate_backward(const moe_config* c, const BwLayout& L, const void* x,
+                              const moe_params* p, const moe_noise* n, const moe_saved* sv,
+                              const void* dy, const float* dimp, moe_grads* g, void* ws,
+                              hipStream_t s) {
+  const int64_t T = c->tokens;
+  const int E = c->n_experts, d = c->d_model, k = c->top_k, G = c->n_groups;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool noisy = c->noisy != 0;
+  float* cs = at<float>(ws, L.cs);
+  float* ns = noisy ? at<float>(ws, L.ns) : nullptr;
+  float* dcp = at<float>(ws, L.dcp);
+  float* drp = noisy ? at<float>(ws, L.drp) : nullptr;
+  if (T > 0) {
+    BwHierGateArgs a;
+    a.y_sorted = sv->y_sorted;
+    a.inv = sv->inv;
+    a.idx = sv->topk_idx;
+    a.gate = sv->topk_gate;
+    a.dy = dy;
+    a.dimp = dimp;
+    a.x = x;
+    a.w_gate = p->w_gate;
+    a.w_noise = noisy ? p->w_noise : nullptr;
+    a.w_gate_p = p->w_gate_p;
+    a.w_noise_p = noisy ? p->w_noise_p : nullptr;
+    a.noise = noisy ? noise_src(n, n->eps, 0) : NoiseSrc();
+    a.noise_p = noisy ? noise_src(n, n->eps_p, 1) : NoiseSrc();
+    a.T = T;
+    a.k = k;
+    a.d = d;
+    a.G = G;
+    a.Eg = E / G;
+    a.kpg = c->k_per_group;
+    a.dxg = at<float>(ws, L.dxg);
+    a.cs = cs;
+    a.ns = ns;
+    a.dcp = dcp;
+    a.drp = drp;
+    MOE_TRY(hip_status(launch_bw_hier_gate(a, bf16, s), "backward hierarchy gate"));
+  }
+  MOE_TRY(gate_table_grad(c, L, x, dcp, G, g->dw_gate_p, at<float>(ws, L.part_g), s));
+  if (noisy)
+    MOE_TRY(gate_table_grad(c, L, x, drp, G, g->dw_noise_p, at<float>(ws, L.part_n), s));
+  if (!g->dw_gate && !g->dw_noise) return MOE_OK;
+  const int32_t* offsets = sv->offsets;
+  const int32_t* perm = sv->perm;
+  if (c->capacity > 0 && T > 0) {
+    Layout R{};
+    R.nb = L.nb;
+    R.bits = L.r_bits;
+    R.base = L.r_base;
+    R.tiles = L.r_counts;  // no tile map is built (with_tiles false)
+    R.desc = L.r_counts;
+    int32_t* offs = at<int32_t>(ws, L.r_offsets);
+    int32_t* pm = at<int32_t>(ws, L.r_perm);
+    MOE_TRY(do_route(c, R, sv->topk_idx, at<int32_t>(ws, L.r_counts), offs, pm,
+                     at<int32_t>(ws, L.r_inv), false, false, ws, s, RouteStats(), false));
+    offsets = offs;
+    perm = pm;
+  }
+  BwRowSumArgs r;
+  r.x = x;
+  r.perm = perm;
+  r.offsets = offsets;
+  r.k = k;
+  r.E = E;
+  r.d = d;
+  const bool both = g->dw_gate && g->dw_noise;
+  r.c0 = g->dw_gate ? cs : ns;
+  r.out0 = g->dw_gate ? g->dw_gate : g->dw_noise;
+  r.c1 = both ? ns : nullptr;
+  r.out1 = both ? g->dw_noise : nullptr;
+  return hip_status(launch_bw_expert_rowsum(r, bf16, s), "backward hierarchy tables");
+}
+
 moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, const moe_params* p,
                        const moe_noise* n, const moe_saved* sv, const void* dy, float wi,
                        float wl, moe_grads* g, void* ws, hipStream_t s) {
@@ -562,6 +687,10 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   MOE_TRY(hip_status(launch_bw_cv2_grad(use_imp ? sv->importance : nullptr,
                                         smooth ? sv->load : nullptr, E, wi, wl, dimp, dload, s),
                      "backward cv2"));
+  float* dxg = at<float>(ws, L.dxg);
+  if (c->n_groups > 0) {
+    MOE_TRY(hier_gate_backward(c, L, x, p, n, sv, dy, use_imp ? dimp : nullptr, g, ws, s));
+  } else {
   // 2. kept-gate gradients through the combine and the importance loss
   float* dhk = at<float>(ws, L.dhk);
   if (T > 0) {
@@ -606,7 +735,6 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   if (g->dbias)
     MOE_TRY(hip_status(launch_bw_sum_rows(dbias_part, L.nblk, E, g->dbias, s), "backward dbias"));
   // 4. gate-table products
-  float* dxg = at<float>(ws, L.dxg);
   if (T > 0) {
     BwGemm q = product(op_rows(dclean, E, true), op_cols(p->w_gate, d, f32));
     q.mode = BW_PLAIN;
@@ -626,25 +754,9 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     const int64_t grid = ((T + 127) / 128) * ((d + 127) / 128);
     MOE_TRY(hip_status(launch_bw_gemm(q, bf16, grid, s), "backward dx gate"));
   }
-  for (int tab = 0; tab < 2; ++tab) {
-    void* out = tab == 0 ? g->dw_gate : g->dw_noise;
-    if (!out) continue;
-    float* part = at<float>(ws, tab == 0 ? L.part_g : L.part_n);
-    BwGemm q = product(op_cols(tab == 0 ? dclean : draw, E, true), op_cols(x, d, f32));
-    q.mode = BW_PLAIN;
-    if (bf16) add_pair(q, low_half(q.a[0]), q.b[0]);
-    q.M = E;
-    q.N = d;
-    q.K = T;
-    q.kchunk = L.kchunk;
-    q.C = part;
-    q.c_f32 = 1;
-    q.ldc = d;
-    q.c_chunk = (int64_t)E * d;
-    const int64_t grid = (int64_t)L.nchunk * ((E + 127) / 128) * ((d + 127) / 128);
-    MOE_TRY(hip_status(launch_bw_gemm(q, bf16, grid, s), "backward gate tables"));
-    MOE_TRY(hip_status(launch_bw_sum_chunks(part, L.nchunk, (int64_t)E * d, bf16, out, s),
-                       "backward gate table sum"));
+  MOE_TRY(gate_table_grad(c, L, x, dclean, E, g->dw_gate, at<float>(ws, L.part_g), s));
+  if (noisy)
+    MOE_TRY(gate_table_grad(c, L, x, draw, E, g->dw_noise, at<float>(ws, L.part_n), s));
   }
   // 5. experts
   void* hid = at<void>(ws, L.hid);
@@ -949,7 +1061,7 @@ moe_status moe_draw_noise(const moe_config* cfg, uint64_t seed, float* eps, floa
 // ---- backward ---------------------------------------------------------------
 
 size_t moe_backward_workspace_size(const moe_config* cfg) {
-  if (check_config(cfg) != MOE_OK || cfg->n_groups > 0) return 0;
+  if (check_config(cfg) != MOE_OK) return 0;
   return bw_layout(cfg).total;
 }
 
@@ -958,15 +1070,26 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* 
                         float w_importance, float w_load, moe_grads* g, void* ws,
                         size_t ws_bytes, void* stream) {
   MOE_TRY(check_config(cfg));
-  if (cfg->n_groups > 0)
-    return fail(MOE_ERR_UNSUPPORTED, "the backward pass covers the flat gate only");
   if (!p || !sv || !g) return fail(MOE_ERR_INVALID_ARG, "params / saved / grads is NULL");
   const int64_t T = cfg->tokens;
   const bool rows = T > 0;
   const bool noisy = cfg->noisy != 0;
   const bool sw = cfg->ffn == MOE_FFN_SWIGLU;
+  const bool hier = cfg->n_groups > 0;
   if (!p->w_gate || (noisy && !p->w_noise))
     return fail(MOE_ERR_INVALID_ARG, "w_gate / w_noise is NULL");
+  if (hier) {
+    if (!p->w_gate_p || (noisy && !p->w_noise_p))
+      return fail(MOE_ERR_INVALID_ARG, "the hierarchy needs w_gate_p (and w_noise_p when noisy)");
+    if (p->bias || g->dbias)
+      return fail(MOE_ERR_INVALID_ARG, "the hierarchy has no bias (bias / dbias must be NULL)");
+    if (g->dw_noise_p && !noisy)
+      return fail(MOE_ERR_INVALID_ARG, "dw_noise_p needs a noisy gate");
+    if (rows && noisy && !has_noise(noise, noise ? noise->eps_p : nullptr))
+      return fail(MOE_ERR_INVALID_ARG, "noisy hierarchy needs eps_p (or noise drawn in the kernels)");
+  } else if (g->dw_gate_p || g->dw_noise_p) {
+    return fail(MOE_ERR_INVALID_ARG, "dw_gate_p / dw_noise_p are for the hierarchy");
+  }
   if (!p->w1 || !p->w2 || (sw && !p->w3))
     return fail(MOE_ERR_INVALID_ARG, "the backward pass needs the unpacked w1 / w2 (/ w3)");
   if (p->w_gate_packed) {
@@ -987,7 +1110,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* 
       return fail(MOE_ERR_INVALID_ARG, "saved topk_idx / topk_gate / perm / inv / y_sorted is NULL");
     if (w_importance != 0.f && !sv->importance)
       return fail(MOE_ERR_INVALID_ARG, "w_importance != 0 needs saved importance");
-    if (noisy && w_load != 0.f && (!sv->load || !sv->thr))
+    if (!hier && noisy && w_load != 0.f && (!sv->load || !sv->thr))
       return fail(MOE_ERR_INVALID_ARG, "w_load != 0 with noise needs saved load and thr");
   }
   const BwLayout L = bw_layout(cfg);
@@ -1000,7 +1123,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* 
   }
   if (cfg->dtype == MOE_F32 && (cfg->d_model % 4 != 0 || cfg->d_hidden % 4 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "the fp32 backward pass needs d_model and d_hidden multiples of 4");
-  if (bw_gate_lds_bytes(cfg->dtype == MOE_BF16, cfg->d_model, cfg->n_experts) > 150 * 1024)
+  if (!hier && bw_gate_lds_bytes(cfg->dtype == MOE_BF16, cfg->d_model, cfg->n_experts) > 150 * 1024)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts / d_model too large for the backward gate tile");
   MOE_TRY(do_backward(cfg, L, x, p, noise, sv, dy, w_importance, w_load, g, ws,
                       (hipStream_t)stream));

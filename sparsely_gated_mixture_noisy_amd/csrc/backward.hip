@@ -78,53 +78,68 @@ __global__ __launch_bounds__(256) void bw_cv2_grad_kernel(const float* imp, cons
 // (lanes over d, then a fixed butterfly) + dImp[idx[t,s]]; then
 // dHk[t,s] = g_s (dg_s - sum_j g_j dg_j).
 // ---------------------------------------------------------------------------
+// This lane's share of the dot product of two d-element rows (lanes over d;
+// the caller reduces over the wave).
+template <typename T>
+__device__ __forceinline__ float row_dot(const T* u, const T* v, int d, int lane) {
+  float acc = 0.f;
+  if ((d & 3) == 0) {
+    // four elements per lane and step: 8-byte (bf16) or 16-byte (fp32) loads
+    for (int c = lane * 4; c < d; c += 256) {
+      float a[4], b[4];
+      if constexpr (sizeof(T) == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(u + c);
+        const uint2 y = *reinterpret_cast<const uint2*>(v + c);
+        a[0] = __uint_as_float(x.x << 16); a[1] = __uint_as_float(x.x & 0xffff0000u);
+        a[2] = __uint_as_float(x.y << 16); a[3] = __uint_as_float(x.y & 0xffff0000u);
+        b[0] = __uint_as_float(y.x << 16); b[1] = __uint_as_float(y.x & 0xffff0000u);
+        b[2] = __uint_as_float(y.y << 16); b[3] = __uint_as_float(y.y & 0xffff0000u);
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(u + c);
+        const float4 y = *reinterpret_cast<const float4*>(v + c);
+        a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+        b[0] = y.x; b[1] = y.y; b[2] = y.z; b[3] = y.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = fmaf(a[j], b[j], acc);
+    }
+  } else {
+    for (int c = lane; c < d; c += 64) acc = fmaf(Elem<T>::load(u, c), Elem<T>::load(v, c), acc);
+  }
+  return acc;
+}
+
+// dg[s] = dy_t . y_sorted[inv[t*k+s]] (+ dImp of the slot's expert) and the
+// slot's gate, for the k slots of token t (k <= 8).
+template <typename T>
+__device__ __forceinline__ void slot_grads(const void* dyp, const void* ysp, const int32_t* inv,
+                                           const int32_t* idx, const float* gate,
+                                           const float* dimp, int64_t t, int k, int d, int lane,
+                                           float (&dg)[8], float (&g)[8]) {
+  const T* dy = (const T*)dyp + t * d;
+  const T* ys = (const T*)ysp;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    dg[s] = 0.f;
+    g[s] = 0.f;
+    if (s < k) {
+      const int64_t p = inv[t * k + s];
+      // a slot dropped by a capacity (inv = -1) contributes nothing to y
+      const float acc = p >= 0 ? row_dot(dy, ys + p * d, d, lane) : 0.f;
+      dg[s] = wave_sum(acc);
+      if (dimp) dg[s] += dimp[idx[t * k + s]];
+      g[s] = gate[t * k + s];
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void bw_gate_out_kernel(BwGateOutArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  const T* dy = (const T*)a.dy + t * a.d;
-  const T* ys = (const T*)a.y_sorted;
   float dg[8], g[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    dg[s] = 0.f;
-    g[s] = 0.f;
-    if (s < a.k) {
-      const int64_t p = a.inv[t * a.k + s];
-      const T* yr = ys + (p < 0 ? 0 : p) * a.d;
-      float acc = 0.f;
-      // a slot dropped by a capacity (inv = -1) contributes nothing to y
-      if (p >= 0) {
-      if ((a.d & 3) == 0) {
-        // four elements per lane and step: 8-byte (bf16) or 16-byte (fp32) loads
-        for (int c = lane * 4; c < a.d; c += 256) {
-          float u[4], v[4];
-          if constexpr (sizeof(T) == 2) {
-            const uint2 x = *reinterpret_cast<const uint2*>(dy + c);
-            const uint2 y = *reinterpret_cast<const uint2*>(yr + c);
-            u[0] = __uint_as_float(x.x << 16); u[1] = __uint_as_float(x.x & 0xffff0000u);
-            u[2] = __uint_as_float(x.y << 16); u[3] = __uint_as_float(x.y & 0xffff0000u);
-            v[0] = __uint_as_float(y.x << 16); v[1] = __uint_as_float(y.x & 0xffff0000u);
-            v[2] = __uint_as_float(y.y << 16); v[3] = __uint_as_float(y.y & 0xffff0000u);
-          } else {
-            const float4 x = *reinterpret_cast<const float4*>(dy + c);
-            const float4 y = *reinterpret_cast<const float4*>(yr + c);
-            u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
-            v[0] = y.x; v[1] = y.y; v[2] = y.z; v[3] = y.w;
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc = fmaf(u[j], v[j], acc);
-        }
-      } else {
-        for (int c = lane; c < a.d; c += 64) acc = fmaf(Elem<T>::load(dy, c), Elem<T>::load(yr, c), acc);
-      }
-      }
-      dg[s] = wave_sum(acc);
-      if (a.dimp) dg[s] += a.dimp[a.idx[t * a.k + s]];
-      g[s] = a.gate[t * a.k + s];
-    }
-  }
+  slot_grads<T>(a.dy, a.y_sorted, a.inv, a.idx, a.gate, a.dimp, t, a.k, a.d, lane, dg, g);
   float sdot = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) sdot = fmaf(g[s], dg[s], sdot);
@@ -135,6 +150,160 @@ __global__ __launch_bounds__(256) void bw_gate_out_kernel(BwGateOutArgs a) {
       if (s == lane) v = g[s] * (dg[s] - sdot);
     a.dhk[t * a.k + lane] = v;
   }
+}
+
+// ---------------------------------------------------------------------------
+// The hierarchy's gate, one wave per token.  The k slots are group-major: the
+// kpg slots of kept group a are a*kpg .. a*kpg+kpg-1.  A kept gate is
+// gp_a gs_s (primary weight of the group times secondary weight of the
+// expert); gp_a is the sum of the group's gates and gs_s = gate_s / gp_a.
+// With V_a = sum of gs dg over the group (the gradient of gp_a), the
+// secondary score gradient is dHs_s = gate_s (dg_s - V_a) and the primary
+// one dHp_a = gp_a (V_a - sum over kept groups of gp V).  Noisy scores H = clean + eps *
+// softplus(raw) add d raw = dH * eps * sigmoid(raw).  dx's share is
+// sum over slots of (dHs W_gate[e] + d raw W_noise[e]) plus the same over the
+// kept groups with the primary tables, in that fixed order.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bw_hier_gate_kernel(BwHierGateArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int k = a.k, kpg = a.kpg, d = a.d, Eg = a.Eg, G = a.G;
+  const bool noisy = a.w_noise != nullptr;
+  const bool noisy_p = a.w_noise_p != nullptr;
+  float dg[8], g[8];
+  slot_grads<T>(a.dy, a.y_sorted, a.inv, a.idx, a.gate, a.dimp, t, k, d, lane, dg, g);
+  int e[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) e[s] = s < k ? a.idx[t * k + s] : 0;
+  // per slot, of its group (groups are runs of kpg slots): gp = the group's
+  // primary weight (sum of its product gates), gs = gate / gp its secondary
+  // weight, V = sum of gs * dg over the group (the primary weight's gradient)
+  float gpg[8], gs[8], V[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    float gp = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < k && u / kpg == s / kpg) gp += g[u];
+    gpg[s] = gp;
+    gs[s] = gp > 0.f ? g[s] / gp : 0.f;
+  }
+  float tot = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    float v = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < k && u / kpg == s / kpg) v = fmaf(gs[u], dg[u], v);
+    V[s] = v;
+    if (s < k && s % kpg == 0) tot += gpg[s];
+  }
+  // primary softmax weights renormalised (their sum is 1 up to rounding, so
+  // a single kept group gets exactly 1 and no gradient)
+  float PV = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    if (s < k && s % kpg == 0) PV = fmaf(gpg[s] / tot, V[s], PV);
+  const T* xr = (const T*)a.x + t * d;
+  float cs[8], ns[8], cp[8], np_[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    cs[s] = ns[s] = cp[s] = np_[s] = 0.f;
+    if (s >= k) continue;
+    cs[s] = g[s] * (dg[s] - V[s]);
+    const int grp = e[s] / Eg, j = e[s] % Eg;
+    if (noisy) {
+      const float raw = wave_sum(row_dot(xr, (const T*)a.w_noise + (int64_t)e[s] * d, d, lane));
+      ns[s] = cs[s] * a.noise.at(t, grp, G, j, Eg) / (1.0f + __expf(-raw));
+    }
+    if (s % kpg == 0) {  // the group's first slot carries its primary gradients
+      cp[s] = gpg[s] / tot * (V[s] - PV);
+      if (noisy_p) {
+        const float raw = wave_sum(row_dot(xr, (const T*)a.w_noise_p + (int64_t)grp * d, d, lane));
+        np_[s] = cp[s] * a.noise_p.at(t, 0, 1, grp, G) / (1.0f + __expf(-raw));
+      }
+    }
+  }
+  if (lane < k) {
+    float c = 0.f, n = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s == lane) {
+        c = cs[s];
+        n = ns[s];
+      }
+    a.cs[t * k + lane] = c;
+    if (a.ns) a.ns[t * k + lane] = n;
+  }
+  for (int gg = lane; gg < G; gg += 64) {
+    float c = 0.f, n = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < k && s % kpg == 0 && e[s] / Eg == gg) {
+        c = cp[s];
+        n = np_[s];
+      }
+    a.dcp[t * G + gg] = c;
+    if (a.drp) a.drp[t * G + gg] = n;
+  }
+  const T* wg = (const T*)a.w_gate;
+  const T* wn = (const T*)a.w_noise;
+  const T* wgp = (const T*)a.w_gate_p;
+  const T* wnp = (const T*)a.w_noise_p;
+  for (int c = lane; c < d; c += 64) {
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s >= k) continue;
+      acc = fmaf(cs[s], Elem<T>::load(wg, (int64_t)e[s] * d + c), acc);
+      if (noisy) acc = fmaf(ns[s], Elem<T>::load(wn, (int64_t)e[s] * d + c), acc);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s >= k || s % kpg != 0) continue;
+      const int64_t grp = e[s] / Eg;
+      acc = fmaf(cp[s], Elem<T>::load(wgp, grp * d + c), acc);
+      if (noisy_p) acc = fmaf(np_[s], Elem<T>::load(wnp, grp * d + c), acc);
+    }
+    a.dxg[t * d + c] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-expert weighted row sums: out[e] = sum over the expert's rows, in
+// routed order, of coefficient * x row.  One workgroup per (expert, 256
+// columns); rows in batches of 8 so that their loads are in flight together.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bw_expert_rowsum_kernel(BwRowSumArgs a) {
+  const int e = blockIdx.x;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= a.d) return;
+  const int lo = a.offsets[e], hi = a.offsets[e + 1];
+  const T* x = (const T*)a.x;
+  float s0 = 0.f, s1 = 0.f;
+  for (int p = lo; p < hi; p += 8) {
+    int r[8];
+    float v[8], c0[8], c1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r[u] = p + u < hi ? a.perm[p + u] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = r[u] >= 0 ? Elem<T>::load(x, (int64_t)(r[u] / a.k) * a.d + c) : 0.f;
+      c0[u] = r[u] >= 0 ? a.c0[r[u]] : 0.f;
+      c1[u] = r[u] >= 0 && a.c1 ? a.c1[r[u]] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (r[u] < 0) continue;
+      s0 = fmaf(c0[u], v[u], s0);
+      s1 = fmaf(c1[u], v[u], s1);
+    }
+  }
+  Elem<T>::store((T*)a.out0, (int64_t)e * a.d + c, s0);
+  if (a.out1) Elem<T>::store((T*)a.out1, (int64_t)e * a.d + c, s1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1006,6 +1175,23 @@ hipError_t launch_bw_gate_out(const BwGateOutArgs& a, bool bf16, hipStream_t s) 
   const dim3 grid((unsigned)((a.T + 3) / 4));
   if (bf16) hipLaunchKernelGGL(bw_gate_out_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(bw_gate_out_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_hier_gate(const BwHierGateArgs& a, bool bf16, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (a.k > 8 || a.kpg <= 0 || a.k % a.kpg != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.T + 3) / 4));
+  if (bf16) hipLaunchKernelGGL(bw_hier_gate_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(bw_hier_gate_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_expert_rowsum(const BwRowSumArgs& a, bool bf16, hipStream_t s) {
+  if (a.E == 0 || a.d == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.E, (unsigned)((a.d + 255) / 256));
+  if (bf16) hipLaunchKernelGGL(bw_expert_rowsum_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(bw_expert_rowsum_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

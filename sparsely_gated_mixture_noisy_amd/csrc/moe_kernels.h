@@ -192,6 +192,53 @@ struct BwGateArgs {
   float* draw;           // [T][E] (noisy)
   float* dbias_part;     // [ceil(T/32)][E]
 };
+// The hierarchy's gate gradients, one wave per token.  A kept gate is the
+// product gp[a] * gs[a, b] of the two levels' softmax weights; with V_a the
+// sum over group a's slots of gs * dgate, the secondary score gradient of
+// slot s is gate_s (dgate_s - V_a) and the primary score gradient of kept
+// group a is gp_a (V_a - sum over kept groups of gp V).  Each then passes
+// through its noisy score
+// (d raw = dH * eps * sigmoid(raw)) to dx and to per-slot / per-group
+// coefficients for the table gradients.
+struct BwHierGateArgs {
+  const void* y_sorted;  // [A][d]
+  const int32_t* inv;    // [A]
+  const int32_t* idx;    // [T][k], group-major (ascending expert index)
+  const float* gate;     // [T][k]
+  const void* dy;        // [T][d]
+  const float* dimp;     // [E] or null
+  const void* x;         // [T][d]
+  const void* w_gate;    // [E][d]
+  const void* w_noise;   // [E][d], null when noise-free
+  const void* w_gate_p;  // [G][d]
+  const void* w_noise_p; // [G][d], null when noise-free
+  NoiseSrc noise;        // secondary: element j of group g of token t
+  NoiseSrc noise_p;      // primary: element g of token t
+  int64_t T;
+  int k, d, G, Eg, kpg;
+  float* dxg;            // [T][d] the gate's share of dx
+  float* cs;             // [T*k] secondary clean-score gradient per slot
+  float* ns;             // [T*k] secondary raw-score gradient per slot (null: noise-free)
+  float* dcp;            // [T][G] primary clean-score gradient (0 outside kept groups)
+  float* drp;            // [T][G] primary raw-score gradient (null: noise-free)
+};
+hipError_t launch_bw_hier_gate(const BwHierGateArgs& a, bool bf16, hipStream_t s);
+
+// out0[e] = sum over the rows p of expert e (offsets / perm, in order) of
+// c0[perm[p]] * x[perm[p] / k], likewise out1 with c1 (nullable); experts
+// with no rows get zeros.
+struct BwRowSumArgs {
+  const void* x;           // [T][d]
+  const int32_t* perm;     // [A]
+  const int32_t* offsets;  // [E+1]
+  const float* c0;         // [T*k]
+  const float* c1;         // [T*k] or null
+  int k, E, d;
+  void* out0;              // [E][d]
+  void* out1;              // [E][d] or null
+};
+hipError_t launch_bw_expert_rowsum(const BwRowSumArgs& a, bool bf16, hipStream_t s);
+
 size_t bw_gate_lds_bytes(bool bf16, int d, int E);
 hipError_t launch_bw_gate(const BwGateArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bw_sum_rows(const float* part, int64_t nrow, int64_t ncol, float* out,

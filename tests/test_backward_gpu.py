@@ -44,7 +44,11 @@ def _say(msg):
 
 
 def _separated(ref, k):
-    """Consecutive sorted noisy scores around ranks k-1 .. k+2 differ by GAP."""
+    """Consecutive sorted noisy scores around ranks k-1 .. k+2 differ by GAP
+    (the hierarchy, which has no smooth load: the k-th and (k+1)-th scores
+    of both levels)."""
+    if "H" not in ref["gate_info"]:
+        return bool((ref["margin"] >= GAP).all())
     H = ref["gate_info"]["H"]
     srt = -np.sort(-H, axis=1)
     E = H.shape[1]
@@ -104,7 +108,18 @@ CASES = {
     "bf16_capacity6": (CONFIGS["flat256"].replace(tokens=300, n_experts=24, d_model=128,
                                                   d_hidden=256, capacity=6), 0.7, 1.2),
     "tiny_capacity40": (CONFIGS["tiny"].replace(capacity=40), 0.5, 0.5),
+    # the hierarchy: both levels' tables, noisy and noise-free, a capacity
+    "tiny_hier": (CONFIGS["tiny"].replace(tokens=150, n_experts=12, n_groups=4, k_groups=2,
+                                          k_per_group=1, top_k=2), 0.9, 1.0),
+    "tiny_hier_swiglu_noise_free": (CONFIGS["tiny"].replace(tokens=97, n_experts=12, n_groups=3,
+                                                            k_groups=1, k_per_group=2, top_k=2,
+                                                            ffn="swiglu", noisy=False), 1.0, 0.0),
+    "bf16_hier": (CONFIGS["hier4096"].replace(tokens=300, n_experts=64, d_model=128,
+                                              d_hidden=256), 0.8, 1.0),
+    "bf16_hier_capacity10": (CONFIGS["hier4096"].replace(tokens=400, n_experts=64, d_model=128,
+                                                         d_hidden=256, capacity=10), 0.8, 0.0),
 }
+KEYS = ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw3", "dw2", "dw_gate_p", "dw_noise_p")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -120,46 +135,63 @@ def test_backward_matches_oracle(name):
     ref = oracle.backward(cpu, cfg, dy.to("cpu"), wi, wl)
     assert (np_(fwd.topk_idx) == ref["forward"]["idx"]).all()
     rtol = RTOL[cfg.dtype]
-    for key in ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw3", "dw2"):
+    for key in KEYS:
         got = getattr(g1, key)
         if got is None:
-            assert key in ("dw_noise", "dw3") and ref[key] is None, key
+            assert ref.get(key) is None, key
             continue
         _check(key, got, ref[key], rtol, FRO[cfg.dtype])
     # deterministic: a second call gives the same bits
     g2 = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
     torch.cuda.synchronize()
-    for key in ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw3", "dw2"):
+    for key in KEYS:
         a, b = getattr(g1, key), getattr(g2, key)
         if a is not None:
             assert torch.equal(a, b), f"{key} differs between two calls"
 
 
-def test_backward_empty_batch_and_idle_experts():
+@pytest.mark.parametrize("base", ["flat256", "hier4096"])
+def test_backward_empty_batch_and_idle_experts(base):
     """T = 0: dx is empty and every table gradient is zero."""
-    cfg = CONFIGS["flat256"].replace(tokens=0, n_experts=8, d_model=64, d_hidden=128)
+    cfg = CONFIGS[base].replace(tokens=0, n_experts=32, d_model=64, d_hidden=128)
     inp = make_inputs(cfg, seed=0, device="cuda")
     dy = make_upstream(cfg, seed=0, device="cuda")
     fwd = L.forward(cfg, inp["x"], inp, inp, 1.0, 1.0, balance=True, save=True)
     g = L.Grads(cfg, 0, "cuda")
-    for key in ("dw_gate", "dw_noise", "dw1", "dw2"):
+    keys = [key for key in KEYS if key != "dx" and getattr(g, key) is not None]
+    for key in keys:
         getattr(g, key).fill_(7.0)
-    g.dbias.fill_(7.0)
     L.Backward(cfg, inp["x"], inp, inp, fwd, dy, 1.0, 1.0, grads=g)()
     torch.cuda.synchronize()
-    for key in ("dw_gate", "dw_noise", "dbias", "dw1", "dw2"):
+    for key in keys:
         assert (getattr(g, key) == 0).all(), key
 
 
-def test_backward_rejects_hierarchy_and_missing_inputs():
-    cfg = CONFIGS["hier4096"].replace(tokens=64, n_experts=64, d_model=64, d_hidden=128)
-    assert L.backward_workspace_size(cfg) == 0
+def test_backward_rejects_missing_and_misplaced_inputs():
+    hier = CONFIGS["hier4096"].replace(tokens=64, n_experts=64, d_model=64, d_hidden=128)
+    assert L.backward_workspace_size(hier) > 0
+    hinp = make_inputs(hier, seed=0, device="cuda")
+    hdy = make_upstream(hier, seed=0, device="cuda")
+    hfwd = L.forward(hier, hinp["x"], hinp, hinp, 1.0, 1.0, balance=True, save=True)
+    # the hierarchy has no bias, so no bias gradient
+    g = L.Grads(hier, 64, "cuda")
+    g.dbias = torch.empty(hier.n_experts, dtype=torch.float32, device="cuda")
+    with pytest.raises(L.MoEError) as e:
+        L.Backward(hier, hinp["x"], hinp, hinp, hfwd, hdy, grads=g)()
+    assert e.value.status == L.MOE_ERR_INVALID_ARG
     flat = CONFIGS["flat256"].replace(tokens=64, n_experts=8, d_model=64, d_hidden=128)
     inp = make_inputs(flat, seed=0, device="cuda")
     dy = make_upstream(flat, seed=0, device="cuda")
     fwd = L.forward(flat, inp["x"], inp, inp, 1.0, 1.0, balance=True, save=False)
     with pytest.raises(L.MoEError) as e:
         L.backward(flat, inp["x"], inp, inp, fwd, dy)
+    assert e.value.status == L.MOE_ERR_INVALID_ARG
+    # the primary tables' gradients belong to the hierarchy
+    sfwd = L.forward(flat, inp["x"], inp, inp, 1.0, 1.0, balance=True, save=True)
+    g = L.Grads(flat, 64, "cuda")
+    g.dw_gate_p = torch.empty((4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(L.MoEError) as e:
+        L.Backward(flat, inp["x"], inp, inp, sfwd, dy, grads=g)()
     assert e.value.status == L.MOE_ERR_INVALID_ARG
 
 
@@ -246,3 +278,88 @@ def test_backward_flat256_full_size_sampled():
         dx_ref[n] = dxe + dclean @ wg + draw @ wn
     got = np_(g.dx)[toks]
     _check("dx[sampled]", got, dx_ref, RTOL["bf16"], FRO["bf16"])
+
+
+def test_backward_hier4096_full_size_sampled():
+    """The full 4096-expert hierarchy (16384 tokens, 16 groups x 256,
+    512 -> 1024 -> 512, two groups then two experts, noisy at both levels)
+    in the launch configuration the timings use.  The oracle computes, one
+    by one: the tables of sampled experts (expert tables from their rows; the
+    secondary gate and noise rows from the tokens that keep them, through
+    the oracle's own hierarchical gate backward on that sub-batch) and the
+    input gradients of sampled tokens.  A token's gate gradients need the
+    outputs of its k experts and the importance gradient, which the oracle
+    computes over all tokens.  The primary tables' gradients sum over every
+    token and so need every expert's outputs; they are checked at the
+    smaller hierarchical sizes above, with the same kernels.  Tokens whose
+    margin at either level is below 1e-5 are not sampled, nor experts that
+    hold such a token."""
+    cfg = CONFIGS["hier4096"]
+    wi, wl = 1.0, 1.0
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    cpu = {key: (v.to("cpu") if v is not None else None) for key, v in inp.items()}
+    dy = make_upstream(cfg, seed=0, device="cuda")
+    _say("[backward] hier4096 full size: forward + backward on the GPU")
+    fwd = L.forward(cfg, inp["x"], inp, inp, wi, wl, balance=True, save=True)
+    g = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
+    torch.cuda.synchronize()
+    _say("[backward] oracle hierarchical gate and statistics")
+    x = cpu["x"].double().numpy()
+    dyn = dy.to("cpu").double().numpy()
+    gi = oracle.gate(cpu, cfg)
+    T, k, E = cfg.tokens, cfg.top_k, cfg.n_experts
+    idx, gates = gi["idx"], gi["gates"]
+    risky = gi["margin"] < GAP
+    assert (np_(fwd.topk_idx)[~risky] == idx[~risky]).all()
+    counts, offsets, perm, inv = oracle.route(idx, E)
+    dimp = wi * oracle.cv_squared_grad(oracle.importance(idx, gates, E))
+    tabs = {key: cpu[key].double().numpy() for key in ("w_gate", "w_noise", "w_gate_p",
+                                                      "w_noise_p")}
+    eps, eps_p = cpu["eps"].double().numpy(), cpu["eps_p"].double().numpy()
+    experts = {}
+
+    def expert(e):
+        if e not in experts:
+            experts[e] = (cpu["w1"][e].double().numpy(), cpu["w2"][e].double().numpy())
+        return experts[e]
+
+    def gate_side(toks):
+        """The oracle's hierarchical gate backward on a sub-batch of tokens."""
+        dgate = np.zeros((toks.size, k))
+        for n, t in enumerate(toks):
+            for s in range(k):
+                e = int(idx[t, s])
+                w1e, w2e = expert(e)
+                dgate[n, s] = oracle.expert_relu(x[t:t + 1], w1e, w2e)[0] @ dyn[t] + dimp[e]
+        sub = dict(idx=idx[toks], primary=dict(gates=gi["primary"]["gates"][toks],
+                                               idx=gi["primary"]["idx"][toks]))
+        sinp = dict(tabs, eps=eps[toks], eps_p=eps_p[toks])
+        return oracle.moe_oracle._hier_gate_backward(sinp, cfg.replace(tokens=toks.size),
+                                                    x[toks], sub, dgate)
+
+    rng = np.random.default_rng(2)
+    risky_e = set(idx[risky].reshape(-1).tolist())
+    cand = [e for e in range(E) if e not in risky_e and counts[e] > 0]
+    _say("[backward] oracle: sampled experts")
+    for e in rng.choice(cand, size=6, replace=False):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        toks = rows // k
+        w1e, w2e = expert(e)
+        dY = gates.reshape(-1)[rows][:, None] * dyn[toks]
+        _, dw1, dw2 = oracle.expert_relu_backward(x[toks], w1e, w2e, dY)
+        _check(f"dw1[{e}]", g.dw1[e], dw1, RTOL["bf16"], FRO["bf16"])
+        _check(f"dw2[{e}]", g.dw2[e], dw2, RTOL["bf16"], FRO["bf16"])
+        res = gate_side(toks)
+        _check(f"dw_gate[{e}]", g.dw_gate[e], res["dw_gate"][e], RTOL["bf16"], FRO["bf16"])
+        _check(f"dw_noise[{e}]", g.dw_noise[e], res["dw_noise"][e], RTOL["bf16"], FRO["bf16"])
+
+    _say("[backward] oracle: sampled tokens")
+    toks = rng.choice(np.nonzero(~risky)[0], size=24, replace=False)
+    dx_ref = gate_side(toks)["dx"]
+    for n, t in enumerate(toks):
+        for s in range(k):
+            w1e, w2e = expert(int(idx[t, s]))
+            dX, _, _ = oracle.expert_relu_backward(x[t:t + 1], w1e, w2e,
+                                                   gates[t, s] * dyn[t:t + 1])
+            dx_ref[n] += dX[0]
+    _check("dx[sampled]", np_(g.dx)[toks], dx_ref, RTOL["bf16"], FRO["bf16"])

@@ -88,18 +88,25 @@ def test_layer_with_in_kernel_noise(name):
     _say(f"[noise] {name}: ok excluded={int(excl.sum())} worst_y={worst:.2e}")
 
 
-def test_backward_with_in_kernel_noise():
-    """The backward recomputes the noisy scores with the same in-kernel draws."""
-    cfg = CONFIGS["flat256"].replace(tokens=300, n_experts=24, d_model=128, d_hidden=256)
+@pytest.mark.parametrize("base", ["flat256", "hier4096"])
+def test_backward_with_in_kernel_noise(base):
+    """The backward recomputes the noisy scores (the flat gate) or reads the
+    kept experts' and groups' draws (the hierarchy) with the same in-kernel
+    draws: bitwise equal to the backward that reads the drawn tensors."""
+    cfg = CONFIGS[base].replace(tokens=300, n_experts=64 if base == "hier4096" else 24,
+                                d_model=128, d_hidden=256)
     inp = make_inputs(cfg, seed=0, device="cuda")
-    gen = dict(inp, eps=None, noise_seed=SEED)
+    gen = dict(inp, eps=None, eps_p=None, noise_seed=SEED)
     dy = make_upstream(cfg, seed=0, device="cuda")
     fwd = L.forward(cfg, inp["x"], gen, gen, save=True)
     g_gen = L.backward(cfg, inp["x"], gen, gen, fwd, dy)
-    eps, _ = L.draw_noise(cfg, SEED)
-    tens = dict(inp, eps=eps)
+    eps, eps_p = L.draw_noise(cfg, SEED)
+    tens = dict(inp, eps=eps, eps_p=eps_p)
     fwd2 = L.forward(cfg, inp["x"], tens, tens, save=True)
     g_ten = L.backward(cfg, inp["x"], tens, tens, fwd2, dy)
     torch.cuda.synchronize()
-    for key in ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw2"):
-        assert torch.equal(getattr(g_gen, key), getattr(g_ten, key)), key
+    for key in ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw2", "dw_gate_p", "dw_noise_p"):
+        a, b = getattr(g_gen, key), getattr(g_ten, key)
+        assert (a is None) == (b is None), key
+        if a is not None:
+            assert torch.equal(a, b), key
