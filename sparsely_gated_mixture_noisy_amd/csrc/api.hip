@@ -480,7 +480,10 @@ BwLayout bw_layout(const moe_config* c) {
   // gate-table products: K = tokens split into chunks, enough workgroups
   const int64_t tiles_mn = ((Etab + 127) / 128) * (int64_t)((d + 127) / 128);
   int64_t nch = (1024 + tiles_mn - 1) / tiles_mn;
-  nch = std::min<int64_t>(nch, std::max<int64_t>(1, (T + 255) / 256));
+  // chunks of at least 256 tokens (bf16, 64-wide K slices) or 64 (fp32,
+  // 16-wide slices)
+  const int64_t min_chunk = es == 2 ? 256 : 64;
+  nch = std::min<int64_t>(nch, std::max<int64_t>(1, (T + min_chunk - 1) / min_chunk));
   nch = std::max<int64_t>(nch, 1);
   int64_t kc = (T + nch - 1) / nch;
   kc = std::max<int64_t>(32, (kc + 31) / 32 * 32);

@@ -1119,45 +1119,131 @@ static size_t bw_gemm_lds() {
   return ops > outs ? ops : outs;
 }
 
-// fp32 products: one thread per output element, plain FMA over k in order.
-__global__ __launch_bounds__(256) void bw_gemm_scalar_kernel(BwGemm g) {
-  // the tile geometry of the MFMA kernel, 256 threads over a 128 x 128 tile
+// fp32 products: the 128 x 128 tile of the bf16 kernel over 512 threads, K
+// in slices of 16 staged through LDS (k-major, padded rows), each thread a
+// 4 x 8 block of outputs (rows ty + 32 i, columns tx + 16 j) accumulated with
+// fp32 FMA in k order.  The next slice's elements are loaded into registers
+// while the current one is multiplied.  NP products share the tile: 1
+// (plain: the operand pairs summed in turn), 2 (the ReLU hidden epilogue:
+// X W1^T and dY W2) or 3 (SwiGLU: also X W3^T).
+constexpr int BF_THREADS = 512, BF_BK = 16, BF_LD = BG_BM + 4;
+constexpr int BF_PER = BG_BM * BF_BK / BF_THREADS;  // staged elements per thread and operand
+
+template <int NP>
+__global__ __launch_bounds__(BF_THREADS) void bw_gemm_f32_kernel(BwGemm g) {
+  constexpr int NOP = NP == 1 ? 2 : NP == 2 ? 4 : 5;  // operands staged per slice
+  __shared__ float S[NOP][BF_BK][BF_LD];
   BwTile t;
   if (!bw_tile_of(g, &t)) return;
-  const bool hidden = g.epi != BW_EPI_NONE;
-  const bool sw = g.epi == BW_EPI_SWIGLU;
-  for (int idx = threadIdx.x; idx < BG_BM * BG_BN; idx += 256) {
-    const int64_t m = t.m0 + idx / BG_BN, n = t.n0 + idx % BG_BN;
-    if (m >= t.M || n >= t.N) continue;
-    const int nseg = hidden ? 1 : g.npair;
-    float s0 = 0.f, s1 = 0.f, s3 = 0.f;
-    for (int seg = 0; seg < nseg; ++seg) {
-      const BwOp& A = g.a[seg];
-      const BwOp& B = g.b[seg];
-      if (A.lo) continue;  // fp32 products take fp32 operands whole
-      for (int64_t k = t.k0; k < t.K; ++k) {
-        s0 = fmaf(bw_elem(A, t.e, m, k), bw_elem(B, t.e, n, k), s0);
-        if (hidden) s1 = fmaf(bw_elem(g.a[1], t.e, m, k), bw_elem(g.b[1], t.e, n, k), s1);
-        if (sw) s3 = fmaf(bw_elem(g.a[0], t.e, m, k), bw_elem(g.b[2], t.e, n, k), s3);
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  float acc[NP][4][8];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[p][i][j] = 0.f;
+  const int64_t nsl = t.K > t.k0 ? (t.K - t.k0 + BF_BK - 1) / BF_BK : 0;
+  const int nseg = NP == 1 ? g.npair : 1;
+  const int64_t steps = nsl * nseg;
+  // operand q of step st: its BwOp and row range (A operands: rows m, B: n)
+  auto opq = [&](int64_t st, int q, const BwOp** o, int64_t* rb, int64_t* R) {
+    const int seg = NP == 1 ? (int)(st / nsl) : 0;
+    const bool isa = NP == 1 ? q == 0 : q < 2;
+    *o = NP == 1 ? (q == 0 ? &g.a[seg] : &g.b[seg]) : (q < 2 ? &g.a[q] : &g.b[q - 2]);
+    *rb = isa ? t.m0 : t.n0;
+    *R = isa ? t.M : t.N;
+  };
+  float pf[NOP][BF_PER];
+  auto fetch = [&](int64_t st) {
+    const int64_t k0 = t.k0 + (st % nsl) * BF_BK;
+#pragma unroll
+    for (int q = 0; q < NOP; ++q) {
+      const BwOp* o;
+      int64_t rb, R;
+      opq(st, q, &o, &rb, &R);
+      const bool km = bw_kmajor(*o);
+#pragma unroll
+      for (int u = 0; u < BF_PER; ++u) {
+        const int idx = tid + BF_THREADS * u;
+        const int r = km ? idx / BF_BK : idx % BG_BM;
+        const int kk = km ? idx % BF_BK : idx / BG_BM;
+        const int64_t row = rb + r, k = k0 + kk;
+        pf[q][u] = (row < R && k < t.K) ? bw_elem(*o, t.e, row, k) : 0.f;
       }
     }
-    if (!hidden) {
-      bw_store(g, t, m, n, s0);
-    } else {
-      const int64_t i = m * g.N + n;
+  };
+  auto put = [&](int64_t st) {
+#pragma unroll
+    for (int q = 0; q < NOP; ++q) {
+      const BwOp* o;
+      int64_t rb, R;
+      opq(st, q, &o, &rb, &R);
+      const bool km = bw_kmajor(*o);
+#pragma unroll
+      for (int u = 0; u < BF_PER; ++u) {
+        const int idx = tid + BF_THREADS * u;
+        const int r = km ? idx / BF_BK : idx % BG_BM;
+        const int kk = km ? idx % BF_BK : idx / BG_BM;
+        S[q][kk][r] = pf[q][u];
+      }
+    }
+  };
+  if (steps > 0) fetch(0);
+  for (int64_t st = 0; st < steps; ++st) {
+    put(st);
+    __syncthreads();
+    if (st + 1 < steps) fetch(st + 1);
+#pragma unroll 4
+    for (int kk = 0; kk < BF_BK; ++kk) {
+      float a0[4], a1[4], b0[8], b1[8], b2[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a0[i] = S[0][kk][ty + 32 * i];
+        if (NP > 1) a1[i] = S[1][kk][ty + 32 * i];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        b0[j] = S[NP == 1 ? 1 : 2][kk][tx + 16 * j];
+        if (NP > 1) b1[j] = S[3][kk][tx + 16 * j];
+        if (NP == 3) b2[j] = S[NOP - 1][kk][tx + 16 * j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[0][i][j] = fmaf(a0[i], b0[j], acc[0][i][j]);
+          if (NP > 1) acc[1][i][j] = fmaf(a1[i], b1[j], acc[1][i][j]);
+          if (NP == 3) acc[NP - 1][i][j] = fmaf(a0[i], b2[j], acc[NP - 1][i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t m = t.m0 + ty + 32 * i, n = t.n0 + tx + 16 * j;
+      if (m >= t.M || n >= t.N) continue;
+      if (NP == 1) {
+        bw_store(g, t, m, n, acc[0][i][j]);
+        continue;
+      }
+      const float a = acc[0][i][j], dh = acc[1][i][j];
+      const int64_t o = m * g.N + n;
       float* hid = (float*)g.C;
       float* d1 = (float*)g.C2;
-      if (!sw) {
-        hid[i] = fmaxf(s0, 0.f);
-        d1[i] = s0 > 0.f ? s1 : 0.f;
+      if (NP == 2) {
+        hid[o] = fmaxf(a, 0.f);
+        d1[o] = a > 0.f ? dh : 0.f;
       } else {
-        const float sg = 1.0f / (1.0f + expf(-s0));
-        hid[i] = s0 * sg * s3;
-        d1[i] = s1 * s3 * sg * (1.0f + s0 * (1.0f - sg));
-        ((float*)g.C3)[i] = s1 * s0 * sg;
+        const float b = acc[NP - 1][i][j];
+        const float sg = 1.0f / (1.0f + expf(-a));
+        hid[o] = a * sg * b;
+        d1[o] = dh * b * sg * (1.0f + a * (1.0f - sg));
+        ((float*)g.C3)[o] = dh * a * sg;
       }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1298,7 +1384,16 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
   g.nrow = (int)((g.M + BG_BM - 1) / BG_BM);
   if (grid <= 0 || g.ncol == 0) return hipSuccess;
   if (!bf16) {
-    hipLaunchKernelGGL(bw_gemm_scalar_kernel, dim3((unsigned)grid), dim3(256), 0, s, g);
+    // fp32 products take fp32 operands whole: no hi / lo halves
+    for (int i = 0; i < g.npair; ++i)
+      if (g.a[i].lo || g.b[i].lo) return hipErrorInvalidValue;
+    const dim3 blk(BF_THREADS);
+    if (g.epi == BW_EPI_RELU)
+      hipLaunchKernelGGL(bw_gemm_f32_kernel<2>, dim3((unsigned)grid), blk, 0, s, g);
+    else if (g.epi == BW_EPI_SWIGLU)
+      hipLaunchKernelGGL(bw_gemm_f32_kernel<3>, dim3((unsigned)grid), blk, 0, s, g);
+    else
+      hipLaunchKernelGGL(bw_gemm_f32_kernel<1>, dim3((unsigned)grid), blk, 0, s, g);
     return hipGetLastError();
   }
   if (g.epi == BW_EPI_RELU) return launch_bw_mfma<2, BW_KB, BW_KB, BW_TB, 64>(g, grid, s);
