@@ -39,8 +39,8 @@ EXPERT_TRAFFIC = {
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
     "sources_sha256": "6735a7185c71e1065cd63277267c93032bf595aac16ea1229ff14c2ca7598253",
-    "fetch_kib": 288812.2, "fetch_scale": 524288.0 / 262156.0,
-    "write_kib": 32768.0, "write_scale": 524288.0 / 524288.0,
+    "fetch_kib": 288889.8, "fetch_scale": 524288.0 / 262156.0,
+    "write_kib": 32768.1, "write_scale": 524288.0 / 524288.0,
 }
 
 

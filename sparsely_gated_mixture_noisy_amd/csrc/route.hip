@@ -59,10 +59,21 @@ __device__ int block_scan4(const int v[4], int* total) {
   return wbase + incl - s;
 }
 
+// Rows of tile i of the nt tiles that hold an expert's m rows: the
+// ceil(m / 32) blocks of 32 rows go to the tiles as evenly as possible, whole
+// blocks first, so the tiles run no more MFMA row blocks than the rows need
+// (near-equal row counts would give 130 rows two tiles of three blocks).
+__device__ __forceinline__ void tile_rows(int m, int nt, int i, int* first, int* rows) {
+  const int nblk = (m + 31) / 32, base = nblk / nt, rem = nblk % nt;
+  const int b0 = i * base + min(i, rem), nb = base + (i < rem ? 1 : 0);
+  *first = 32 * b0;
+  *rows = min(m, 32 * (b0 + nb)) - 32 * b0;
+}
+
 // Tile map of the expert stage from per-expert row counts: tiles[e] = first
 // tile of expert e (exclusive scan of ceil(count / rows)), tiles[E] = total;
 // with desc, desc[q] = {expert, first position, rows}, an expert's rows split
-// into near-equal tiles.  counts_of(e) and offsets_of(e) give the routing.
+// by tile_rows.  counts_of(e) and offsets_of(e) give the routing.
 // Called by all SCAN_THREADS threads of one workgroup.
 template <typename CountF, typename OffF>
 __device__ void build_tile_map(int E, int rows, CountF counts_of, OffF offsets_of, int32_t* tiles,
@@ -85,12 +96,14 @@ __device__ void build_tile_map(int E, int rows, CountF counts_of, OffF offsets_o
       if (e < E) {
         tiles[e] = run;
         if (desc && v[j] > 0) {
-          const int m = cnt[j], base = m / v[j], rem = m % v[j], o = offsets_of(e);
+          const int m = cnt[j], o = offsets_of(e);
           for (int i = 0; i < v[j]; ++i) {
             int32_t* d = desc + 3 * (int64_t)(run + i);
+            int first, nr;
+            tile_rows(m, v[j], i, &first, &nr);
             d[0] = e;
-            d[1] = o + i * base + min(i, rem);
-            d[2] = base + (i < rem ? 1 : 0);
+            d[1] = o + first;
+            d[2] = nr;
           }
         }
       }
@@ -202,8 +215,8 @@ __device__ void scan_counts(const int32_t* counts, int E, int* off) {
 // The expert stage's tile map from the offsets in LDS, by one workgroup of
 // SCATTER_THREADS threads: tiles[e] = first tile of expert e (exclusive scan
 // of ceil(count / rows)), tiles[E] = total; with desc (may be null),
-// desc[q] = {expert, first position, rows}, an expert's rows split into
-// near-equal tiles.
+// desc[q] = {expert, first position, rows}, an expert's rows split by
+// tile_rows.
 __device__ void scatter_tile_map(const int* off, int E, int rows, int32_t* tiles, int32_t* desc) {
   const int tid = threadIdx.x;
   const int per = (E + SCATTER_THREADS - 1) / SCATTER_THREADS;
@@ -216,12 +229,13 @@ __device__ void scatter_tile_map(const int* off, int E, int rows, int32_t* tiles
     const int m = off[e + 1] - off[e], nt = (m + rows - 1) / rows;
     tiles[e] = run;
     if (desc && nt > 0) {
-      const int base = m / nt, rem = m % nt;
       for (int i = 0; i < nt; ++i) {
         int32_t* d = desc + 3 * (int64_t)(run + i);
+        int first, nr;
+        tile_rows(m, nt, i, &first, &nr);
         d[0] = e;
-        d[1] = off[e] + i * base + min(i, rem);
-        d[2] = base + (i < rem ? 1 : 0);
+        d[1] = off[e] + first;
+        d[2] = nr;
       }
     }
     run += nt;
