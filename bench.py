@@ -38,7 +38,7 @@ EXPERT_TRAFFIC = {
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "6735a7185c71e1065cd63277267c93032bf595aac16ea1229ff14c2ca7598253",
+    "sources_sha256": "aec4e0752f41dcf5e8330dcd6d528e0c601fba582cf0002494ddc05af24ccfb0",
     "fetch_kib": 288889.8, "fetch_scale": 524288.0 / 262156.0,
     "write_kib": 32768.1, "write_scale": 524288.0 / 524288.0,
 }

@@ -8,7 +8,8 @@
 // not by MFMA, so the kernel is organised to read each table byte once:
 //
 //   * one workgroup = one tile of at most 96 rows of one expert (an expert
-//     with m rows gets ceil(m/96) tiles of near-equal size); the tiles of an
+//     with m rows gets ceil(m/96) tiles, its 32-row blocks spread evenly
+//     over them, whole blocks first); the tiles of an
 //     expert have consecutive ids that land on one XCD and are dispatched
 //     together, so they share the weight stream through that XCD's L2;
 //   * the tile's gathered input rows sit in LDS (96 x 512 bf16);

@@ -106,7 +106,7 @@ hipError_t launch_gather_rows(const void* x, const int32_t* perm, int k, int64_t
 
 // tiles[e] = sum_{e' < e} ceil(count_{e'} / rows), tiles[E] = total; with
 // desc != null also desc[q] = {expert, first position, rows} for every tile,
-// an expert's rows split into near-equal tiles
+// an expert's 32-row blocks spread evenly over its tiles
 hipError_t launch_tile_map(const int32_t* offsets, int E, int rows, int32_t* tiles,
                            int32_t* desc, hipStream_t s);
 
