@@ -48,6 +48,19 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_resolved(lib: str) -> None:
+    """Fail when the library leaves a symbol of its own namespace undefined
+    (for instance a kernel whose host-side launch stub the compiler dropped):
+    such a library links, but fails at load time."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    r = subprocess.run([nm, "-D", "-C", "--undefined-only", lib], capture_output=True, text=True)
+    missing = [ln.strip() for ln in r.stdout.splitlines() if "moe::" in ln]
+    if missing:
+        raise RuntimeError("libmoe.so leaves symbols undefined:\n  " + "\n  ".join(missing))
+
+
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -58,6 +71,7 @@ def build_library(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    _check_resolved(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -194,7 +194,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 //     tile, then the next column tile, so each XCD keeps one activation tile
 //     in its L2 while the weight column tiles stream past.
 // ---------------------------------------------------------------------------
-constexpr int GB_BM = 256, GB_BN = 128, GB_BK = 64, GB_WIN = 8;
+constexpr int GB_BM = 256, GB_BK = 64, GB_WIN = 8;
+// column tile: 128 with the SwiGLU epilogue (two accumulator sets), 256
+// otherwise (each wave 128 x 128: four activation and four weight fragments
+// per 16 MFMAs, a third less LDS traffic per MFMA than 128 x 64)
+template <int EPI> constexpr int gb_bn() { return EPI == EPI_SWIGLU ? 128 : 256; }
 
 // element offset of chunk c (8 elements) of row r in a swizzled operand tile
 __device__ __forceinline__ int gb_slot(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
@@ -202,7 +206,11 @@ __device__ __forceinline__ int gb_slot(int r, int c) { return (r * 8 + (c ^ ((r 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   constexpr bool SW = (EPI == EPI_SWIGLU);
-  constexpr int AT = GB_BM * GB_BK, BT = GB_BN * GB_BK;  // tile elements
+  constexpr int BN = gb_bn<EPI>();
+  constexpr int NBJ = BN / 32;   // 1 KB weight blocks each wave loads per slice
+  constexpr int WN = BN / 2;     // columns per wave
+  constexpr int NJ = WN / 32;    // 32-column MFMA blocks per wave
+  constexpr int AT = GB_BM * GB_BK, BT = BN * GB_BK;  // tile elements
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   bf16_t* As = smem;               // [2][AT]
   bf16_t* Bs = As + 2 * AT;        // [2][BT]
@@ -231,14 +239,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   if (e < 0) return;
   const int row0 = __builtin_amdgcn_readfirstlane(s_row0);
   const int m = __builtin_amdgcn_readfirstlane(s_m);
-  const int n0 = __builtin_amdgcn_readfirstlane(s_ct) * GB_BN;
+  const int n0 = __builtin_amdgcn_readfirstlane(s_ct) * BN;
 
-  // Direct loads: wave w fills 1 KB blocks w*8 + j (A, j < 8) and w*4 + j
-  // (B, B3, j < 4); lane l of block b fills slot 64b + l: row (64b + l) / 8,
-  // chunk position l % 8, i.e. source chunk (l % 8) ^ ((row >> 1) & 7).
+  // Direct loads: wave w fills 1 KB blocks w*8 + j (A, j < 8) and
+  // w*NBJ + j (B, B3, j < NBJ); lane l of block b fills slot 64b + l: row
+  // (64b + l) / 8, chunk position l % 8, i.e. source chunk
+  // (l % 8) ^ ((row >> 1) & 7).
+  // (arrays sized for the widest tile: the lambdas below capture them, and
+  // the host pass of the compiler drops the kernel when a captured array's
+  // bound depends on the template argument; unused entries are optimised out)
   const bf16_t* ap[8];
-  const bf16_t* bp[4];
-  const bf16_t* b3p[4];
+  const bf16_t* bp[8];
+  const bf16_t* b3p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (w * 8 + j) * 8 + (lane >> 3);
@@ -248,8 +260,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     ap[j] = g.A + src * g.lda + c * 8;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (w * 4 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < NBJ; ++j) {
+    const int r = (w * NBJ + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int n = min(n0 + r, g.N - 1);
     bp[j] = g.B + ((int64_t)e * g.N + n) * g.K + c * 8;
@@ -260,21 +272,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     for (int j = 0; j < 8; ++j)
       __builtin_amdgcn_global_load_lds(ap[j] + k0, As + buf * AT + (w * 8 + j) * 512, 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_global_load_lds(bp[j] + k0, Bs + buf * BT + (w * 4 + j) * 512, 16, 0, 0);
+    for (int j = 0; j < NBJ; ++j) {
+      __builtin_amdgcn_global_load_lds(bp[j] + k0, Bs + buf * BT + (w * NBJ + j) * 512, 16, 0, 0);
       if constexpr (SW)
-        __builtin_amdgcn_global_load_lds(b3p[j] + k0, B3s + buf * BT + (w * 4 + j) * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b3p[j] + k0, B3s + buf * BT + (w * NBJ + j) * 512, 16, 0,
+                                         0);
     }
   };
 
-  const int wm = w >> 1, wn = w & 1;  // wave tile: rows wm*128 .. +128, cols wn*64 .. +64
+  const int wm = w >> 1, wn = w & 1;  // wave tile: rows wm*128 .. +128, cols wn*WN .. +WN
   const bool active = wm * 128 < m;
   const int fr = lane & 31, fh = lane >> 5;
-  f32x16 acc[4][2], acc3[SW ? 4 : 1][SW ? 2 : 1];
+  f32x16 acc[4][4], acc3[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
   if constexpr (SW) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -297,17 +310,17 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
       const bf16_t* Bb = Bs + buf * BT;
       const bf16_t* B3b = B3s + buf * BT;
       // operand fragments one 16-deep k-step ahead of the MFMAs, no further
-      bf16x8 af[2][4], bf[2][2], b3f[2][SW ? 2 : 1];
+      bf16x8 af[2][4], bf[2][4], b3f[2][2];
       auto frags = [&](int st, int sl) {
         const int c = 2 * st + fh;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           af[sl][i] = *reinterpret_cast<const bf16x8*>(Ab + gb_slot(wm * 128 + i * 32 + fr, c));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          bf[sl][j] = *reinterpret_cast<const bf16x8*>(Bb + gb_slot(wn * 64 + j * 32 + fr, c));
+        for (int j = 0; j < NJ; ++j) {
+          bf[sl][j] = *reinterpret_cast<const bf16x8*>(Bb + gb_slot(wn * WN + j * 32 + fr, c));
           if constexpr (SW)
-            b3f[sl][j] = *reinterpret_cast<const bf16x8*>(B3b + gb_slot(wn * 64 + j * 32 + fr, c));
+            b3f[sl][j] = *reinterpret_cast<const bf16x8*>(B3b + gb_slot(wn * WN + j * 32 + fr, c));
         }
       };
       frags(0, 0);
@@ -318,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < NJ; ++j) {
             acc[i][j] = mfma32(bf[sl][j], af[sl][i], acc[i][j]);
             if constexpr (SW) acc3[i][j] = mfma32(b3f[sl][j], af[sl][i], acc3[i][j]);
           }
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   }
 
   if (!active) return;
-  // register group q of acc[i][j] holds columns wn*64 + 32j + 8q + 4(lane/32) .. +3
+  // register group q of acc[i][j] holds columns wn*WN + 32j + 8q + 4(lane/32) .. +3
   // of row wm*128 + 32i + lane%32
   const int q4 = fh * 4;
 #pragma unroll
@@ -340,10 +353,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     if (row >= m) continue;
     bf16_t* crow = g.C + (int64_t)(row0 + row) * g.ldc;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn * 64 + 32 * j + 8 * q + q4;
+        const int col = n0 + wn * WN + 32 * j + 8 * q + q4;
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -436,7 +449,7 @@ int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E) {
 template <int EPI>
 static hipError_t launch_big(const GemmArgs& g, int64_t qmax, hipStream_t s) {
   constexpr size_t lds =
-      sizeof(bf16_t) * (size_t)GB_BK * 2 * (GB_BM + GB_BN * (EPI == EPI_SWIGLU ? 2 : 1));
+      sizeof(bf16_t) * (size_t)GB_BK * 2 * (GB_BM + gb_bn<EPI>() * (EPI == EPI_SWIGLU ? 2 : 1));
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI>,
@@ -461,7 +474,9 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
   }
   if (fused_ffn_supported(a.d, a.h, swiglu)) return launch_fused_ffn(a, s);
   const bool big = big_tiles(a.A, a.E);
-  const int bm = big ? GB_BM : GM_BM, bn = big ? GB_BN : GM_BN;
+  const int bm = big ? GB_BM : GM_BM;
+  const int bn1 = big ? (swiglu ? gb_bn<EPI_SWIGLU>() : gb_bn<EPI_RELU>()) : GM_BN;
+  const int bn2 = big ? gb_bn<EPI_NONE>() : GM_BN;
   // upper bound of tiles: each non-empty expert adds at most one partial tile
   const int64_t qmax = (a.A + bm - 1) / bm + a.E;
   GemmArgs g1;
@@ -478,7 +493,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
   g1.E = a.E;
   g1.C = (bf16_t*)a.hid;
   g1.ldc = a.h;
-  g1.ncol = (a.h + bn - 1) / bn;
+  g1.ncol = (a.h + bn1 - 1) / bn1;
   GemmArgs g2 = g1;
   g2.A = (const bf16_t*)a.hid;
   g2.lda = a.h;
@@ -489,7 +504,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
   g2.K = a.h;
   g2.C = (bf16_t*)a.y_sorted;
   g2.ldc = a.d;
-  g2.ncol = (a.d + bn - 1) / bn;
+  g2.ncol = (a.d + bn2 - 1) / bn2;
   if (big) {
     hipError_t err = swiglu ? launch_big<EPI_SWIGLU>(g1, qmax, s) : launch_big<EPI_RELU>(g1, qmax, s);
     if (err != hipSuccess) return err;
