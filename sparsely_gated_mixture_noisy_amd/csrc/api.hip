@@ -519,7 +519,7 @@ BwLayout bw_layout(const moe_config* c) {
   L.hid = take(es * (size_t)A * h);
   L.dp = take(es * (size_t)A * h);
   L.db = take(sw ? es * (size_t)A * h : 0);
-  L.dxs = take(4 * (size_t)A * d);
+  L.dxs = take(es * (size_t)A * d);
   L.part_g = take(4 * (size_t)L.nchunk * Etab * d);
   L.part_n = take(c->noisy ? 4 * (size_t)L.nchunk * Etab * d : 0);
   L.xs = take(es * (size_t)A * d);
@@ -765,7 +765,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   void* hid = at<void>(ws, L.hid);
   void* dp = at<void>(ws, L.dp);
   void* db = sw ? at<void>(ws, L.db) : nullptr;
-  float* dxs = at<float>(ws, L.dxs);
+  void* dxs = at<void>(ws, L.dxs);
   const int64_t hd = (int64_t)h * d;
   // the routed rows of x and the gate-scaled output gradients, in expert order
   void* xs = at<void>(ws, L.xs);
@@ -810,7 +810,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     r.tiles = tiles;
     r.E = E;
     r.C = dxs;
-    r.c_f32 = 1;
+    r.c_f32 = f32 ? 1 : 0;  // in the layer dtype, like the expert outputs
     r.ldc = d;
     MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((d + 127) / 128), s),
                        "backward expert dx"));

@@ -627,7 +627,7 @@ __global__ __launch_bounds__(256) void bw_gather_rows_kernel(const T* src, const
 // dx[t][c] = dx_gate[t][c] + sum_s dxs[inv[t*k+s]][c], slots in order; four
 // columns per thread (d % 4 == 0)
 template <typename TO>
-__global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, const float* dxs,
+__global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, const TO* dxs,
                                                              const int32_t* inv, int64_t T, int k,
                                                              int d, TO* dx) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -638,11 +638,11 @@ __global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, c
   for (int s = 0; s < k; ++s) {
     const int p = inv[t * k + s];
     if (p < 0) continue;  // dropped by a capacity
-    const float4 u = *reinterpret_cast<const float4*>(dxs + (int64_t)p * d + c);
-    v.x += u.x;
-    v.y += u.y;
-    v.z += u.z;
-    v.w += u.w;
+    const TO* r = dxs + (int64_t)p * d + c;
+    v.x += Elem<TO>::load(r, 0);
+    v.y += Elem<TO>::load(r, 1);
+    v.z += Elem<TO>::load(r, 2);
+    v.w += Elem<TO>::load(r, 3);
   }
   Elem<TO>::store(dx, i, v.x);
   Elem<TO>::store(dx, i + 1, v.y);
@@ -1342,15 +1342,17 @@ hipError_t launch_bw_sum_chunks(const float* part, int nchunk, int64_t n, bool b
   return hipGetLastError();
 }
 
-hipError_t launch_bw_assemble_dx(const float* dxg, const float* dxs, const int32_t* inv, int64_t T,
+hipError_t launch_bw_assemble_dx(const float* dxg, const void* dxs, const int32_t* inv, int64_t T,
                                  int k, int d, bool bf16, void* dx, hipStream_t s) {
   const int64_t n = T * d / 4;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (bf16)
-    hipLaunchKernelGGL(bw_assemble_dx_kernel<bf16_t>, grid, dim3(256), 0, s, dxg, dxs, inv, T, k, d, (bf16_t*)dx);
+    hipLaunchKernelGGL(bw_assemble_dx_kernel<bf16_t>, grid, dim3(256), 0, s, dxg,
+                       (const bf16_t*)dxs, inv, T, k, d, (bf16_t*)dx);
   else
-    hipLaunchKernelGGL(bw_assemble_dx_kernel<float>, grid, dim3(256), 0, s, dxg, dxs, inv, T, k, d, (float*)dx);
+    hipLaunchKernelGGL(bw_assemble_dx_kernel<float>, grid, dim3(256), 0, s, dxg,
+                       (const float*)dxs, inv, T, k, d, (float*)dx);
   return hipGetLastError();
 }
 

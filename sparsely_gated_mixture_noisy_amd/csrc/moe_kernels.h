@@ -245,7 +245,8 @@ hipError_t launch_bw_sum_rows(const float* part, int64_t nrow, int64_t ncol, flo
                               hipStream_t s);
 hipError_t launch_bw_sum_chunks(const float* part, int nchunk, int64_t n, bool bf16, void* out,
                                 hipStream_t s);
-hipError_t launch_bw_assemble_dx(const float* dxg, const float* dxs, const int32_t* inv, int64_t T,
+// dx = dxg + the routed rows' dxs (in the layer dtype), skipping dropped slots
+hipError_t launch_bw_assemble_dx(const float* dxg, const void* dxs, const int32_t* inv, int64_t T,
                                  int k, int d, bool bf16, void* dx, hipStream_t s);
 
 // Operand of a backward product: element (r, k) of an R x K matrix, for
