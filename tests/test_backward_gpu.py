@@ -118,6 +118,10 @@ CASES = {
                                               d_hidden=256), 0.8, 1.0),
     "bf16_hier_capacity10": (CONFIGS["hier4096"].replace(tokens=400, n_experts=64, d_model=128,
                                                          d_hidden=256, capacity=10), 0.8, 0.0),
+    # one group, then one expert: both softmax levels are a single weight of 1
+    "bf16_hier_k1": (CONFIGS["hier4096"].replace(tokens=200, n_experts=64, d_model=128,
+                                                 d_hidden=256, k_groups=1, k_per_group=1,
+                                                 top_k=1), 0.7, 0.0),
 }
 KEYS = ("dx", "dw_gate", "dw_noise", "dbias", "dw1", "dw3", "dw2", "dw_gate_p", "dw_noise_p")
 

@@ -82,6 +82,14 @@ SMALL = {
     "big_swiglu": CONFIGS["mixtral"].replace(tokens=1200, d_model=512, d_hidden=1536, n_experts=4),
     "big_relu_d256": CONFIGS["flat256"].replace(tokens=1500, d_model=256, d_hidden=512,
                                                 n_experts=8, top_k=2),
+    # the 256-wide column tiles of the big GEMMs with a ragged last column tile
+    "big_relu_d320": CONFIGS["flat256"].replace(tokens=1300, d_model=320, d_hidden=640,
+                                                n_experts=4, top_k=1),
+    # one group, then one expert: the hierarchy at k = 1
+    "hier_k1": CONFIGS["hier4096"].replace(tokens=257, n_experts=160, k_groups=1,
+                                           k_per_group=1, top_k=1),
+    # experts in four gate blocks, the last one partial
+    "flat_e1000": CONFIGS["zipf2048"].replace(tokens=400, n_experts=1000, bias="none"),
 }
 
 
