@@ -109,3 +109,30 @@ def test_packed_table_sizes_and_rejections(lib):
     assert _gate_call(L.load(), CONFIGS["flat256"], params=bad) == L.MOE_ERR_INVALID_ARG
     bad = L.moe_params(w_gate=FAKE, w_noise=FAKE, w_gate_packed=FAKE)
     assert _gate_call(L.load(), CONFIGS["tiny"], params=bad) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No fallback: with the HIP library missing, the binding raises before
+    any computation instead of computing the layer some other way."""
+    from sparsely_gated_mixture_noisy_amd import _lib as L
+    from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libmoe.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    cfg = CONFIGS["tiny"]
+    inp = make_inputs(cfg, seed=0)
+    with pytest.raises(RuntimeError, match="missing"):
+        L.forward(cfg, inp["x"], inp, inp)
+
+
+def test_package_does_not_use_the_oracle():
+    """The oracle is test infrastructure: nothing in the package imports it."""
+    import os
+    import re
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "sparsely_gated_mixture_noisy_amd")
+    pat = re.compile(r"^\s*(import|from)\s+oracle\b", re.M)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                with open(os.path.join(root, f)) as fh:
+                    assert not pat.search(fh.read()), f
