@@ -174,11 +174,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Large layers (on average >= GB_BM rows per expert): 256 x 128 output tiles,
-// K staged through LDS 64 at a time, four waves (one per SIMD) of 128 x 64
-// each.  Per 16-deep k-step a wave reads four activation and two (SwiGLU:
-// four) weight fragments for eight (sixteen) MFMAs, half the LDS traffic per
-// MFMA of the 128 x 128 kernel.
+// Large layers (on average >= GB_BM rows per expert): 256 x 256 output tiles
+// (256 x 128 with the SwiGLU epilogue), K staged through LDS 64 at a time,
+// eight waves (two per SIMD, so one wave's MFMAs cover the other's LDS waits
+// and barriers) of 128 x 64 (SwiGLU: 128 x 32) each.  Per 16-deep k-step a
+// wave reads four activation and two (SwiGLU: one and one) weight fragments
+// for eight MFMAs.
 //   * Operand tiles go from global memory straight into LDS
 //     (global_load_lds_dwordx4: each wave-wide load fills 1 KB of LDS in lane
 //     order), with no staging registers and no LDS store pass.  A tile row is
@@ -196,19 +197,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 constexpr int GB_BM = 256, GB_BK = 64, GB_WIN = 8;
 // column tile: 128 with the SwiGLU epilogue (two accumulator sets), 256
-// otherwise (each wave 128 x 128: four activation and four weight fragments
-// per 16 MFMAs, a third less LDS traffic per MFMA than 128 x 64)
+// otherwise
 template <int EPI> constexpr int gb_bn() { return EPI == EPI_SWIGLU ? 128 : 256; }
 
 // element offset of chunk c (8 elements) of row r in a swizzled operand tile
 __device__ __forceinline__ int gb_slot(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
+__global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   constexpr bool SW = (EPI == EPI_SWIGLU);
   constexpr int BN = gb_bn<EPI>();
-  constexpr int NBJ = BN / 32;   // 1 KB weight blocks each wave loads per slice
-  constexpr int WN = BN / 2;     // columns per wave
+  constexpr int NBJ = BN / 64;   // 1 KB weight blocks each wave loads per slice
+  constexpr int WN = BN / 4;     // columns per wave
   constexpr int NJ = WN / 32;    // 32-column MFMA blocks per wave
   constexpr int AT = GB_BM * GB_BK, BT = BN * GB_BK;  // tile elements
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   const int m = __builtin_amdgcn_readfirstlane(s_m);
   const int n0 = __builtin_amdgcn_readfirstlane(s_ct) * BN;
 
-  // Direct loads: wave w fills 1 KB blocks w*8 + j (A, j < 8) and
+  // Direct loads: wave w fills 1 KB blocks w*4 + j (A, j < 4) and
   // w*NBJ + j (B, B3, j < NBJ); lane l of block b fills slot 64b + l: row
   // (64b + l) / 8, chunk position l % 8, i.e. source chunk
   // (l % 8) ^ ((row >> 1) & 7).
@@ -252,8 +252,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   const bf16_t* bp[8];
   const bf16_t* b3p[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (w * 8 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < 4; ++j) {
+    const int r = (w * 4 + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int p = row0 + min(r, m - 1);
     const int64_t src = g.perm ? (int64_t)(g.perm[p] / g.k) : (int64_t)p;
@@ -269,8 +269,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   }
   auto dma = [&](int k0, int buf) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(ap[j] + k0, As + buf * AT + (w * 8 + j) * 512, 16, 0, 0);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(ap[j] + k0, As + buf * AT + (w * 4 + j) * 512, 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
       __builtin_amdgcn_global_load_lds(bp[j] + k0, Bs + buf * BT + (w * NBJ + j) * 512, 16, 0, 0);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     }
   };
 
-  const int wm = w >> 1, wn = w & 1;  // wave tile: rows wm*128 .. +128, cols wn*WN .. +WN
+  const int wm = w >> 2, wn = w & 3;  // wave tile: rows wm*128 .. +128, cols wn*WN .. +WN
   const bool active = wm * 128 < m;
   const int fr = lane & 31, fh = lane >> 5;
   f32x16 acc[4][4], acc3[4][2];
@@ -459,7 +459,7 @@ static hipError_t launch_big(const GemmArgs& g, int64_t qmax, hipStream_t s) {
   }
   const int64_t wins = (qmax + GB_WIN - 1) / GB_WIN;
   hipLaunchKernelGGL(grouped_gemm_big_kernel<EPI>, dim3((unsigned)(wins * GB_WIN * g.ncol)),
-                     dim3(256), lds, s, g);
+                     dim3(512), lds, s, g);
   return hipGetLastError();
 }
 
