@@ -401,7 +401,10 @@ __device__ __forceinline__ float normal_pdf_f(float z) {
   return 0.3989422804014327f * exp2_hw(-0.5f * z * z * 1.4426950408889634f);
 }
 
-template <typename T, bool NOISY, bool XLDS>
+// ONE: the experts fit one block (E <= GATE_BLOCK_E), so the per-row
+// candidates start after the projection instead of living through it (with
+// them alive across the projection the kernel spilled 300 bytes per lane).
+template <typename T, bool NOISY, bool XLDS, bool ONE>
 __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a) {
   __shared__ BwTileShared sh;
   __shared__ RankBest wk[GATE_WAVES][GATE_ROWS], bn[GATE_WAVES][GATE_ROWS];
@@ -415,16 +418,20 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a
   const bool smooth = NOISY && a.dload != nullptr;
   RankBest worst_kept[16], best_drop[16];
   float s_kept[16], s_drop[16];
+  auto init = [&]() {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    worst_kept[r] = RankBest{INFINITY, -1};
-    best_drop[r] = RankBest{-INFINITY, 0x7fffffff};
-    s_kept[r] = 0.f;
-    s_drop[r] = 0.f;
-  }
-  for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
+    for (int r = 0; r < 16; ++r) {
+      worst_kept[r] = RankBest{INFINITY, -1};
+      best_drop[r] = RankBest{-INFINITY, 0x7fffffff};
+      s_kept[r] = 0.f;
+      s_drop[r] = 0.f;
+    }
+  };
+  if (!ONE) init();
+  for (int blk = 0; blk < (ONE ? GATE_BLOCK_E : a.E); blk += GATE_BLOCK_E) {
     f32x16 cs, ss, hs, rs, es;
     bw_block_scores<T, NOISY, XLDS>(a, sh, Xs, xld, blk, cs, ss, hs, rs, es);
+    if (ONE) init();
     const int e = blk + w * 32 + (lane & 31);
     if (e < a.E) {
       const uint32_t km = sb[e];
@@ -1295,12 +1302,19 @@ static hipError_t bw_set_lds(K kernel, size_t bytes) {
 template <typename T, bool NOISY, bool XLDS>
 static hipError_t launch_bw_gate_v(const BwGateArgs& a, hipStream_t s) {
   const size_t lds = bw_gate_lds(XLDS, a.d, a.E);
-  hipError_t err = bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS>, lds);
+  const bool one = a.E <= GATE_BLOCK_E;
+  hipError_t err = one ? bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS, true>, lds)
+                       : bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS, false>, lds);
   if (err != hipSuccess) return err;
   err = bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS>, lds);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
-  hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS>), grid, dim3(GATE_THREADS), lds, s, a);
+  if (one)
+    hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS, true>), grid, dim3(GATE_THREADS), lds,
+                       s, a);
+  else
+    hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS, false>), grid, dim3(GATE_THREADS),
+                       lds, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((bw_gate_grad_kernel<T, NOISY, XLDS>), grid, dim3(GATE_THREADS), lds, s, a);
