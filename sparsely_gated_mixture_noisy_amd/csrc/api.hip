@@ -460,6 +460,9 @@ struct BwLayout {
   // hierarchy: per-slot and per-group score gradients, and the routing
   // without capacity (when the forward capped it) for the secondary tables
   size_t cs, ns, dcp, drp, r_bits, r_base, r_counts, r_offsets, r_perm, r_inv;
+  // flat bf16 gate with E <= 256: the gate tables transposed for the fused dx product
+  size_t wgt, wnt;
+  int e16;
   size_t total;
   int nblk, nchunk, nb;
   int64_t kchunk;
@@ -514,6 +517,10 @@ BwLayout bw_layout(const moe_config* c) {
   L.r_offsets = take(reroute ? 4 * (size_t)(E + 1) : 0);
   L.r_perm = take(reroute ? 4 * (size_t)A : 0);
   L.r_inv = take(reroute ? 4 * (size_t)A : 0);
+  const bool fused_dxg = flat && es == 2 && E <= bw_fused_dxg_max_experts();
+  L.e16 = fused_dxg ? (E + 15) / 16 * 16 : 0;
+  L.wgt = take(fused_dxg ? 2 * (size_t)d * L.e16 : 0);
+  L.wnt = take(fused_dxg && c->noisy ? 2 * (size_t)d * L.e16 : 0);
   L.dxg = take(4 * (size_t)T * d);
   L.tiles = take(4 * (size_t)(E + 1));
   L.hid = take(es * (size_t)A * h);
@@ -734,11 +741,26 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   ga.dclean = dclean;
   ga.draw = draw;
   ga.dbias_part = dbias_part;
+  const bool fused_dxg = L.e16 > 0 && T > 0;
+  if (fused_dxg) {
+    // the gate's share of dx is formed inside the gate-gradient kernel
+    bf16_t* wgt = at<bf16_t>(ws, L.wgt);
+    bf16_t* wnt = noisy ? at<bf16_t>(ws, L.wnt) : nullptr;
+    MOE_TRY(hip_status(launch_bw_transpose_table(p->w_gate, E, d, L.e16, wgt, s),
+                       "backward transpose w_gate"));
+    if (noisy)
+      MOE_TRY(hip_status(launch_bw_transpose_table(p->w_noise, E, d, L.e16, wnt, s),
+                         "backward transpose w_noise"));
+    ga.wgt = wgt;
+    ga.wnt = wnt;
+    ga.e16 = L.e16;
+    ga.dxg = dxg;
+  }
   MOE_TRY(hip_status(launch_bw_gate(ga, bf16, s), "backward gate"));
   if (g->dbias)
     MOE_TRY(hip_status(launch_bw_sum_rows(dbias_part, L.nblk, E, g->dbias, s), "backward dbias"));
   // 4. gate-table products
-  if (T > 0) {
+  if (T > 0 && !fused_dxg) {
     BwGemm q = product(op_rows(dclean, E, true), op_cols(p->w_gate, d, f32));
     q.mode = BW_PLAIN;
     // bf16 products carry the fp32 score gradients as hi + lo halves

@@ -503,7 +503,16 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a
   }
 }
 
-template <typename T, bool NOISY, bool XLDS>
+// LDS row stride (bf16 elements) of the fused dx product's score-gradient tiles
+constexpr int BWD_LD = GATE_BLOCK_E + 8;
+constexpr size_t BWD_LDS = sizeof(bf16_t) * 4 * GATE_ROWS * BWD_LD;
+
+// DXG (bf16, E <= GATE_BLOCK_E): also form the tile's dx_gate = dclean W_gate
+// + draw W_noise on MFMA, from the score gradients staged in LDS as bf16
+// hi + lo halves (the split the separate product uses) and the transposed
+// tables: wave w takes the 32-column blocks w, w + 8, ...; an accumulator lane
+// holds four consecutive columns of one row.
+template <typename T, bool NOISY, bool XLDS, bool DXG>
 __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a) {
   __shared__ BwTileShared sh;
   __shared__ int4 ri[GATE_ROWS];
@@ -512,6 +521,16 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
   const int xld = a.d + 8;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
   uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
+  // [4][GATE_ROWS][BWD_LD]: dclean hi, dclean lo, draw hi, draw lo
+  bf16_t* Ds = reinterpret_cast<bf16_t*>(
+      dyn + (((XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0) + sizeof(uint32_t) * (size_t)a.E + 15) &
+             ~(size_t)15));
+  auto dput = [&](int q, int row, int e, float v) {
+    const uint32_t hi = cvt_pk_bf16(v, 0.f) << 16;
+    const float lo = v - __uint_as_float(hi);
+    Ds[((2 * q) * GATE_ROWS + row) * BWD_LD + e] = (bf16_t)(hi >> 16);
+    Ds[((2 * q + 1) * GATE_ROWS + row) * BWD_LD + e] = (bf16_t)(cvt_pk_bf16(lo, 0.f) & 0xffffu);
+  };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
   if (tid < GATE_ROWS) {
@@ -560,14 +579,75 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
           // d softplus(raw) / d raw = sigmoid(raw)
           const float sg = rcp_hw(1.0f + exp2_hw(-rs[r] * 1.4426950408889634f));
           if (row < valid) a.draw[(t0 + row) * a.E + e] = dsp * sg;
+          if (DXG) dput(1, row, e, row < valid ? dsp * sg : 0.f);
         }
         if (row < valid) a.dclean[(t0 + row) * a.E + e] = dc;
+        if (DXG) dput(0, row, e, row < valid ? dc : 0.f);
         bsum += row < valid ? dc : 0.f;
+      }
+    } else if (DXG) {
+      // experts past E: zero k columns of the product
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, lane);
+        dput(0, row, e, 0.f);
+        if (NOISY) dput(1, row, e, 0.f);
       }
     }
     bsum += __shfl_xor(bsum, 32, 64);
     if (lane < 32 && e < a.E) a.dbias_part[(int64_t)blockIdx.x * a.E + e] = bsum;
   }
+  if constexpr (DXG) {
+    __syncthreads();
+    const int w = threadIdx.x >> 6, fr = lane & 31, fh = lane >> 5, q4 = fh * 4;
+    const int nks = a.e16 / 16;
+    const bf16_t* Dch = Ds;
+    const bf16_t* Dcl = Ds + GATE_ROWS * BWD_LD;
+    const bf16_t* Drh = Ds + 2 * GATE_ROWS * BWD_LD;
+    const bf16_t* Drl = Ds + 3 * GATE_ROWS * BWD_LD;
+    for (int cb = w; cb * 32 < a.d; cb += GATE_WAVES) {
+      const int col = cb * 32 + fr;
+      const bool cok = col < a.d;
+      const bf16_t* wg = a.wgt + (int64_t)(cok ? col : 0) * a.e16 + 8 * fh;
+      const bf16_t* wn = NOISY ? a.wnt + (int64_t)(cok ? col : 0) * a.e16 + 8 * fh : nullptr;
+      f32x16 acc = f32x16{};
+      for (int ks = 0; ks < nks; ++ks) {
+        const int k = ks * 16 + 8 * fh;
+        const bf16x8 zg = cok ? load_bf16x8(wg + ks * 16) : zero_bf16x8();
+        acc = mfma32(zg, load_bf16x8(Dch + fr * BWD_LD + k), acc);
+        acc = mfma32(zg, load_bf16x8(Dcl + fr * BWD_LD + k), acc);
+        if (NOISY) {
+          const bf16x8 zn = cok ? load_bf16x8(wn + ks * 16) : zero_bf16x8();
+          acc = mfma32(zn, load_bf16x8(Drh + fr * BWD_LD + k), acc);
+          acc = mfma32(zn, load_bf16x8(Drl + fr * BWD_LD + k), acc);
+        }
+      }
+      // register group g: columns cb*32 + 8g + q4 .. +3 of row fr
+      if (fr < valid) {
+        float* orow = a.dxg + (t0 + fr) * a.d;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = cb * 32 + 8 * g + q4;
+          if (c + 3 < a.d) {
+            *reinterpret_cast<float4*>(orow + c) =
+                float4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (c + r < a.d) orow[c + r] = acc[4 * g + r];
+          }
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void bw_transpose_table_kernel(const bf16_t* in, int E, int d,
+                                                                 int e16, bf16_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // out index: c * e16 + e
+  if (i >= (int64_t)d * e16) return;
+  const int c = (int)(i / e16), e = (int)(i % e16);
+  out[i] = e < E ? in[(int64_t)e * d + c] : (bf16_t)0;
 }
 
 // out[c] = sum over rows r of part[r][c]: 64 columns per workgroup, wave w
@@ -1288,8 +1368,20 @@ hipError_t launch_bw_expert_rowsum(const BwRowSumArgs& a, bool bf16, hipStream_t
   return hipGetLastError();
 }
 
-static size_t bw_gate_lds(bool xlds, int d, int E) {
-  return (xlds ? sizeof(bf16_t) * GATE_ROWS * (d + 8) : 0) + sizeof(uint32_t) * (size_t)E;
+static size_t bw_gate_lds(bool xlds, int d, int E, bool dxg = false) {
+  const size_t base = (xlds ? sizeof(bf16_t) * GATE_ROWS * (d + 8) : 0) + sizeof(uint32_t) * (size_t)E;
+  return dxg ? ((base + 15) & ~(size_t)15) + BWD_LDS : base;
+}
+
+int bw_fused_dxg_max_experts() { return GATE_BLOCK_E; }
+
+hipError_t launch_bw_transpose_table(const void* in, int E, int d, int e16, void* out,
+                                     hipStream_t s) {
+  const int64_t n = (int64_t)d * e16;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bw_transpose_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const bf16_t*)in, E, d, e16, (bf16_t*)out);
+  return hipGetLastError();
 }
 
 template <typename K>
@@ -1306,7 +1398,11 @@ static hipError_t launch_bw_gate_v(const BwGateArgs& a, hipStream_t s) {
   hipError_t err = one ? bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS, true>, lds)
                        : bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS, false>, lds);
   if (err != hipSuccess) return err;
-  err = bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS>, lds);
+  constexpr bool can_dxg = sizeof(T) == 2;
+  const bool dxg = can_dxg && one && a.dxg != nullptr;
+  const size_t lds_g = bw_gate_lds(XLDS, a.d, a.E, dxg);
+  err = dxg ? bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS, can_dxg>, lds_g)
+            : bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS, false>, lds_g);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
   if (one)
@@ -1317,7 +1413,12 @@ static hipError_t launch_bw_gate_v(const BwGateArgs& a, hipStream_t s) {
                        lds, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((bw_gate_grad_kernel<T, NOISY, XLDS>), grid, dim3(GATE_THREADS), lds, s, a);
+  if (dxg)
+    hipLaunchKernelGGL((bw_gate_grad_kernel<T, NOISY, XLDS, can_dxg>), grid, dim3(GATE_THREADS),
+                       lds_g, s, a);
+  else
+    hipLaunchKernelGGL((bw_gate_grad_kernel<T, NOISY, XLDS, false>), grid, dim3(GATE_THREADS),
+                       lds_g, s, a);
   return hipGetLastError();
 }
 

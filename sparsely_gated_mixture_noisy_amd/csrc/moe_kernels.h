@@ -191,7 +191,20 @@ struct BwGateArgs {
   float* dclean;         // [T][E]
   float* draw;           // [T][E] (noisy)
   float* dbias_part;     // [ceil(T/32)][E]
+  // bf16 layers with E <= 256: the gate's share of dx, dclean W_gate +
+  // draw W_noise, is formed in the same kernel from the tile's score
+  // gradients (bf16 hi + lo halves) and the tables transposed to
+  // [d][ceil(E/16)*16] (zero past E); null: a separate product forms it
+  const bf16_t* wgt = nullptr;
+  const bf16_t* wnt = nullptr;
+  int e16 = 0;
+  float* dxg = nullptr;  // [T][d]
 };
+// the largest expert count for which the gate-gradient kernel forms dx_gate
+int bw_fused_dxg_max_experts();
+// out[c][e] = in[e][c] for e < E, 0 for E <= e < e16 (in [E][d], out [d][e16])
+hipError_t launch_bw_transpose_table(const void* in, int E, int d, int e16, void* out,
+                                     hipStream_t s);
 // The hierarchy's gate gradients, one wave per token.  A kept gate is the
 // product gp[a] * gs[a, b] of the two levels' softmax weights; with V_a the
 // sum over group a's slots of gs * dgate, the secondary score gradient of
