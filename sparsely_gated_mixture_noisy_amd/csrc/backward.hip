@@ -110,7 +110,10 @@ __device__ __forceinline__ float row_dot(const T* u, const T* v, int d, int lane
 }
 
 // dg[s] = dy_t . y_sorted[inv[t*k+s]] (+ dImp of the slot's expert) and the
-// slot's gate, for the k slots of token t (k <= 8).
+// slot's gate, for the k slots of token t (k <= 8).  Each column chunk of dy
+// is loaded once and the k slots' rows are loaded together, so their loads
+// are in flight at the same time; every slot sums its products in column
+// order, then reduces over the wave.
 template <typename T>
 __device__ __forceinline__ void slot_grads(const void* dyp, const void* ysp, const int32_t* inv,
                                            const int32_t* idx, const float* gate,
@@ -118,17 +121,59 @@ __device__ __forceinline__ void slot_grads(const void* dyp, const void* ysp, con
                                            float (&dg)[8], float (&g)[8]) {
   const T* dy = (const T*)dyp + t * d;
   const T* ys = (const T*)ysp;
+  int64_t p[8];
+  float acc[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    // a slot dropped by a capacity (inv = -1) contributes nothing to y
+    p[s] = s < k ? inv[t * k + s] : -1;
+    g[s] = s < k ? gate[t * k + s] : 0.f;
+    acc[s] = 0.f;
+  }
+  if ((d & 3) == 0) {
+    // four elements per lane and step: 8-byte (bf16) or 16-byte (fp32) loads
+    for (int c = lane * 4; c < d; c += 256) {
+      float u[4], v[8][4];
+      if constexpr (sizeof(T) == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(dy + c);
+        u[0] = __uint_as_float(x.x << 16); u[1] = __uint_as_float(x.x & 0xffff0000u);
+        u[2] = __uint_as_float(x.y << 16); u[3] = __uint_as_float(x.y & 0xffff0000u);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint2 y = p[s] >= 0 ? *reinterpret_cast<const uint2*>(ys + p[s] * d + c)
+                                    : uint2{0u, 0u};
+          v[s][0] = __uint_as_float(y.x << 16); v[s][1] = __uint_as_float(y.x & 0xffff0000u);
+          v[s][2] = __uint_as_float(y.y << 16); v[s][3] = __uint_as_float(y.y & 0xffff0000u);
+        }
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(dy + c);
+        u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const float4 y = p[s] >= 0 ? *reinterpret_cast<const float4*>(ys + p[s] * d + c)
+                                     : float4{0.f, 0.f, 0.f, 0.f};
+          v[s][0] = y.x; v[s][1] = y.y; v[s][2] = y.z; v[s][3] = y.w;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[s] = fmaf(u[j], v[s][j], acc[s]);
+    }
+  } else {
+    for (int c = lane; c < d; c += 64) {
+      const float u = Elem<T>::load(dy, c);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (p[s] >= 0) acc[s] = fmaf(u, Elem<T>::load(ys, p[s] * d + c), acc[s]);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     dg[s] = 0.f;
-    g[s] = 0.f;
     if (s < k) {
-      const int64_t p = inv[t * k + s];
-      // a slot dropped by a capacity (inv = -1) contributes nothing to y
-      const float acc = p >= 0 ? row_dot(dy, ys + p * d, d, lane) : 0.f;
-      dg[s] = wave_sum(acc);
+      dg[s] = wave_sum(acc[s]);
       if (dimp) dg[s] += dimp[idx[t * k + s]];
-      g[s] = gate[t * k + s];
     }
   }
 }
