@@ -601,6 +601,29 @@ moe_status gate_table_grad(const moe_config* c, const BwLayout& L, const void* x
                     "backward gate table sum");
 }
 
+// The same for bf16 coefficients already split into hi and lo halves [T][rows].
+moe_status gate_table_grad_halves(const moe_config* c, const BwLayout& L, const void* x,
+                                  const bf16_t* hi, const bf16_t* lo, int rows, void* out,
+                                  float* part, hipStream_t s) {
+  if (!out) return MOE_OK;
+  const int d = c->d_model;
+  BwGemm q = product(op_cols(hi, rows, false), op_cols(x, d, false));
+  q.mode = BW_PLAIN;
+  add_pair(q, op_cols(lo, rows, false), q.b[0]);
+  q.M = rows;
+  q.N = d;
+  q.K = c->tokens;
+  q.kchunk = L.kchunk;
+  q.C = part;
+  q.c_f32 = 1;
+  q.ldc = d;
+  q.c_chunk = (int64_t)rows * d;
+  const int64_t grid = (int64_t)L.nchunk * ((rows + 127) / 128) * ((d + 127) / 128);
+  MOE_TRY(hip_status(launch_bw_gemm(q, true, grid, s), "backward gate tables"));
+  return hip_status(launch_bw_sum_chunks(part, L.nchunk, (int64_t)rows * d, true, out, s),
+                    "backward gate table sum");
+}
+
 // The hierarchy's gate side: score gradients of both levels and dx's share
 // (one wave per token), the primary tables as dense products over tokens,
 // the secondary tables as per-expert sums over the routed rows of the
@@ -740,6 +763,18 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   ga.rinfo = at<int32_t>(ws, L.rinfo);
   ga.dclean = dclean;
   ga.draw = draw;
+  // bf16 layers: the score gradients leave as the bf16 hi / lo halves the
+  // products take (same bytes as fp32, no conversion in the product loaders)
+  bf16_t* ch = bf16 ? reinterpret_cast<bf16_t*>(dclean) : nullptr;
+  bf16_t* cl = bf16 ? ch + T * E : nullptr;
+  bf16_t* rh = bf16 && noisy ? reinterpret_cast<bf16_t*>(draw) : nullptr;
+  bf16_t* rl = bf16 && noisy ? rh + T * E : nullptr;
+  if (bf16) {
+    ga.dclean_hi = ch;
+    ga.dclean_lo = cl;
+    ga.draw_hi = rh;
+    ga.draw_lo = rl;
+  }
   ga.dbias_part = dbias_part;
   const bool fused_dxg = L.e16 > 0 && T > 0;
   if (fused_dxg) {
@@ -761,13 +796,18 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     MOE_TRY(hip_status(launch_bw_sum_rows(dbias_part, L.nblk, E, g->dbias, s), "backward dbias"));
   // 4. gate-table products
   if (T > 0 && !fused_dxg) {
-    BwGemm q = product(op_rows(dclean, E, true), op_cols(p->w_gate, d, f32));
+    // bf16 products carry the score gradients as hi + lo halves
+    BwGemm q = bf16 ? product(op_rows(ch, E, false), op_cols(p->w_gate, d, false))
+                    : product(op_rows(dclean, E, true), op_cols(p->w_gate, d, true));
     q.mode = BW_PLAIN;
-    // bf16 products carry the fp32 score gradients as hi + lo halves
-    if (bf16) add_pair(q, low_half(q.a[0]), q.b[0]);
+    if (bf16) add_pair(q, op_rows(cl, E, false), q.b[0]);
     if (noisy) {
-      add_pair(q, op_rows(draw, E, true), op_cols(p->w_noise, d, f32));
-      if (bf16) add_pair(q, low_half(op_rows(draw, E, true)), op_cols(p->w_noise, d, f32));
+      if (bf16) {
+        add_pair(q, op_rows(rh, E, false), op_cols(p->w_noise, d, false));
+        add_pair(q, op_rows(rl, E, false), op_cols(p->w_noise, d, false));
+      } else {
+        add_pair(q, op_rows(draw, E, true), op_cols(p->w_noise, d, true));
+      }
     }
     q.M = T;
     q.N = d;
@@ -779,9 +819,16 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     const int64_t grid = ((T + 127) / 128) * ((d + 127) / 128);
     MOE_TRY(hip_status(launch_bw_gemm(q, bf16, grid, s), "backward dx gate"));
   }
-  MOE_TRY(gate_table_grad(c, L, x, dclean, E, g->dw_gate, at<float>(ws, L.part_g), s));
-  if (noisy)
-    MOE_TRY(gate_table_grad(c, L, x, draw, E, g->dw_noise, at<float>(ws, L.part_n), s));
+  if (bf16) {
+    MOE_TRY(gate_table_grad_halves(c, L, x, ch, cl, E, g->dw_gate, at<float>(ws, L.part_g), s));
+    if (noisy)
+      MOE_TRY(gate_table_grad_halves(c, L, x, rh, rl, E, g->dw_noise, at<float>(ws, L.part_n),
+                                     s));
+  } else {
+    MOE_TRY(gate_table_grad(c, L, x, dclean, E, g->dw_gate, at<float>(ws, L.part_g), s));
+    if (noisy)
+      MOE_TRY(gate_table_grad(c, L, x, draw, E, g->dw_noise, at<float>(ws, L.part_n), s));
+  }
   }
   // 5. experts
   void* hid = at<void>(ws, L.hid);

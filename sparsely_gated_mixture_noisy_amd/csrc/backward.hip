@@ -548,6 +548,13 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a
   }
 }
 
+// v as bf16 hi = rne(v) and lo = rne(v - hi), the halves the products take
+__device__ __forceinline__ void split_store(bf16_t* hi, bf16_t* lo, int64_t i, float v) {
+  const uint32_t h = cvt_pk_bf16(v, 0.f) << 16;
+  hi[i] = (bf16_t)(h >> 16);
+  lo[i] = (bf16_t)(cvt_pk_bf16(v - __uint_as_float(h), 0.f) & 0xffffu);
+}
+
 // LDS row stride (bf16 elements) of the fused dx product's score-gradient tiles
 constexpr int BWD_LD = GATE_BLOCK_E + 8;
 constexpr size_t BWD_LDS = sizeof(bf16_t) * 4 * GATE_ROWS * BWD_LD;
@@ -623,10 +630,16 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
           }
           // d softplus(raw) / d raw = sigmoid(raw)
           const float sg = rcp_hw(1.0f + exp2_hw(-rs[r] * 1.4426950408889634f));
-          if (row < valid) a.draw[(t0 + row) * a.E + e] = dsp * sg;
+          if (row < valid) {
+            if (a.draw_hi) split_store(a.draw_hi, a.draw_lo, (t0 + row) * a.E + e, dsp * sg);
+            else a.draw[(t0 + row) * a.E + e] = dsp * sg;
+          }
           if (DXG) dput(1, row, e, row < valid ? dsp * sg : 0.f);
         }
-        if (row < valid) a.dclean[(t0 + row) * a.E + e] = dc;
+        if (row < valid) {
+          if (a.dclean_hi) split_store(a.dclean_hi, a.dclean_lo, (t0 + row) * a.E + e, dc);
+          else a.dclean[(t0 + row) * a.E + e] = dc;
+        }
         if (DXG) dput(0, row, e, row < valid ? dc : 0.f);
         bsum += row < valid ? dc : 0.f;
       }

@@ -188,8 +188,15 @@ struct BwGateArgs {
   int64_t T;
   int d, E, k;
   int32_t* rinfo;        // [T][4]: expert ranked k, k+1 (-1: none), their score gradients
-  float* dclean;         // [T][E]
+  float* dclean;         // [T][E] fp32, or null when written as bf16 halves below
   float* draw;           // [T][E] (noisy)
+  // bf16 layers: the score gradients as bf16 hi and lo halves (hi = the
+  // rounded value, lo = the rounded remainder), [T][E] each, the operands the
+  // products take; null: fp32 dclean / draw above
+  bf16_t* dclean_hi = nullptr;
+  bf16_t* dclean_lo = nullptr;
+  bf16_t* draw_hi = nullptr;
+  bf16_t* draw_lo = nullptr;
   float* dbias_part;     // [ceil(T/32)][E]
   // bf16 layers with E <= 256: the gate's share of dx, dclean W_gate +
   // draw W_noise, is formed in the same kernel from the tile's score
