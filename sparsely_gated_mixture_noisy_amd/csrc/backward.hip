@@ -446,10 +446,11 @@ __device__ __forceinline__ float normal_pdf_f(float z) {
   return 0.3989422804014327f * exp2_hw(-0.5f * z * z * 1.4426950408889634f);
 }
 
-// ONE: the experts fit one block (E <= GATE_BLOCK_E), so the per-row
-// candidates start after the projection instead of living through it (with
-// them alive across the projection the kernel spilled 300 bytes per lane).
-template <typename T, bool NOISY, bool XLDS, bool ONE>
+// Each expert block's candidates are reduced over the half-wave right away
+// and merged into the wave's LDS slots, so no per-row state lives through the
+// projections (carried through them, it made the kernel spill 300 bytes per
+// lane).
+template <typename T, bool NOISY, bool XLDS>
 __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a) {
   __shared__ BwTileShared sh;
   __shared__ RankBest wk[GATE_WAVES][GATE_ROWS], bn[GATE_WAVES][GATE_ROWS];
@@ -458,12 +459,22 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a
   const int xld = a.d + 8;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
   uint32_t* sb = reinterpret_cast<uint32_t*>(dyn + (XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0));
-  bw_tile_setup<T, XLDS>(a, sh, sb, Xs, xld);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < GATE_WAVES * GATE_ROWS) {
+    const int ww = tid / GATE_ROWS, row = tid % GATE_ROWS;
+    wk[ww][row] = RankBest{INFINITY, -1};
+    bn[ww][row] = RankBest{-INFINITY, 0x7fffffff};
+    wsk[ww][row] = 0.f;
+    wsn[ww][row] = 0.f;
+  }
+  bw_tile_setup<T, XLDS>(a, sh, sb, Xs, xld);
+  __syncthreads();
   const bool smooth = NOISY && a.dload != nullptr;
-  RankBest worst_kept[16], best_drop[16];
-  float s_kept[16], s_drop[16];
-  auto init = [&]() {
+  for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
+    f32x16 cs, ss, hs, rs, es;
+    bw_block_scores<T, NOISY, XLDS>(a, sh, Xs, xld, blk, cs, ss, hs, rs, es);
+    RankBest worst_kept[16], best_drop[16];
+    float s_kept[16], s_drop[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       worst_kept[r] = RankBest{INFINITY, -1};
@@ -471,12 +482,6 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a
       s_kept[r] = 0.f;
       s_drop[r] = 0.f;
     }
-  };
-  if (!ONE) init();
-  for (int blk = 0; blk < (ONE ? GATE_BLOCK_E : a.E); blk += GATE_BLOCK_E) {
-    f32x16 cs, ss, hs, rs, es;
-    bw_block_scores<T, NOISY, XLDS>(a, sh, Xs, xld, blk, cs, ss, hs, rs, es);
-    if (ONE) init();
     const int e = blk + w * 32 + (lane & 31);
     if (e < a.E) {
       const uint32_t km = sb[e];
@@ -501,28 +506,29 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a
         }
       }
     }
-  }
-  // across the 32 lanes of a half-wave (the experts of one row)
+    // across the 32 lanes of a half-wave (the experts of one row in this block)
 #pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
+    for (int off = 1; off < 32; off <<= 1) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const RankBest ok = rb_xor(worst_kept[r], off);
-      if (rb_before(worst_kept[r], ok)) worst_kept[r] = ok;
-      const RankBest od = rb_xor(best_drop[r], off);
-      if (rb_before(od, best_drop[r])) best_drop[r] = od;
-      s_kept[r] += __shfl_xor(s_kept[r], off, 64);
-      s_drop[r] += __shfl_xor(s_drop[r], off, 64);
+      for (int r = 0; r < 16; ++r) {
+        const RankBest ok = rb_xor(worst_kept[r], off);
+        if (rb_before(worst_kept[r], ok)) worst_kept[r] = ok;
+        const RankBest od = rb_xor(best_drop[r], off);
+        if (rb_before(od, best_drop[r])) best_drop[r] = od;
+        s_kept[r] += __shfl_xor(s_kept[r], off, 64);
+        s_drop[r] += __shfl_xor(s_drop[r], off, 64);
+      }
     }
-  }
-  if ((lane & 31) == 0) {
+    // into the wave's slots, block after block (each row's slot has one writer)
+    if ((lane & 31) == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = acc_row(r, lane);
-      wk[w][row] = worst_kept[r];
-      bn[w][row] = best_drop[r];
-      wsk[w][row] = s_kept[r];
-      wsn[w][row] = s_drop[r];
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, lane);
+        if (rb_before(wk[w][row], worst_kept[r])) wk[w][row] = worst_kept[r];
+        if (rb_before(best_drop[r], bn[w][row])) bn[w][row] = best_drop[r];
+        wsk[w][row] += s_kept[r];
+        wsn[w][row] += s_drop[r];
+      }
     }
   }
   __syncthreads();
@@ -1453,8 +1459,7 @@ template <typename T, bool NOISY, bool XLDS>
 static hipError_t launch_bw_gate_v(const BwGateArgs& a, hipStream_t s) {
   const size_t lds = bw_gate_lds(XLDS, a.d, a.E);
   const bool one = a.E <= GATE_BLOCK_E;
-  hipError_t err = one ? bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS, true>, lds)
-                       : bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS, false>, lds);
+  hipError_t err = bw_set_lds(bw_gate_rank_kernel<T, NOISY, XLDS>, lds);
   if (err != hipSuccess) return err;
   constexpr bool can_dxg = sizeof(T) == 2;
   const bool dxg = can_dxg && one && a.dxg != nullptr;
@@ -1463,12 +1468,7 @@ static hipError_t launch_bw_gate_v(const BwGateArgs& a, hipStream_t s) {
             : bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS, false>, lds_g);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
-  if (one)
-    hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS, true>), grid, dim3(GATE_THREADS), lds,
-                       s, a);
-  else
-    hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS, false>), grid, dim3(GATE_THREADS),
-                       lds, s, a);
+  hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS>), grid, dim3(GATE_THREADS), lds, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (dxg)
