@@ -78,6 +78,19 @@ __global__ __launch_bounds__(256) void bw_cv2_grad_kernel(const float* imp, cons
 // (lanes over d, then a fixed butterfly) + dImp[idx[t,s]]; then
 // dHk[t,s] = g_s (dg_s - sum_j g_j dg_j).
 // ---------------------------------------------------------------------------
+// Four consecutive elements as floats (8-byte bf16 or 16-byte fp32 load).
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
+    v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+  } else {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+}
+
 // This lane's share of the dot product of two d-element rows (lanes over d;
 // the caller reduces over the wave).
 template <typename T>
@@ -252,6 +265,48 @@ __global__ __launch_bounds__(256) void bw_hier_gate_kernel(BwHierGateArgs a) {
   for (int s = 0; s < 8; ++s)
     if (s < k && s % kpg == 0) PV = fmaf(gpg[s] / tot, V[s], PV);
   const T* xr = (const T*)a.x + t * d;
+  // the raw noise scores of the kept experts and groups: all rows' loads in
+  // flight together, then one wave reduction each
+  float rw[8], rp[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) rw[s] = rp[s] = 0.f;
+  const T* wn = (const T*)a.w_noise;
+  const T* wnp = (const T*)a.w_noise_p;
+  if (noisy || noisy_p) {
+    if ((d & 3) == 0) {
+      for (int c = lane * 4; c < d; c += 256) {
+        float xv[4];
+        load4<T>(xr + c, xv);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          if (s >= k) continue;
+          if (noisy) {
+            float v[4];
+            load4<T>(wn + (int64_t)e[s] * d + c, v);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rw[s] = fmaf(xv[j], v[j], rw[s]);
+          }
+          if (noisy_p && s % kpg == 0) {
+            float v[4];
+            load4<T>(wnp + (int64_t)(e[s] / Eg) * d + c, v);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rp[s] = fmaf(xv[j], v[j], rp[s]);
+          }
+        }
+      }
+    } else {
+      for (int c = lane; c < d; c += 64) {
+        const float xv = Elem<T>::load(xr, c);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          if (s >= k) continue;
+          if (noisy) rw[s] = fmaf(xv, Elem<T>::load(wn, (int64_t)e[s] * d + c), rw[s]);
+          if (noisy_p && s % kpg == 0)
+            rp[s] = fmaf(xv, Elem<T>::load(wnp, (int64_t)(e[s] / Eg) * d + c), rp[s]);
+        }
+      }
+    }
+  }
   float cs[8], ns[8], cp[8], np_[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -260,13 +315,13 @@ __global__ __launch_bounds__(256) void bw_hier_gate_kernel(BwHierGateArgs a) {
     cs[s] = g[s] * (dg[s] - V[s]);
     const int grp = e[s] / Eg, j = e[s] % Eg;
     if (noisy) {
-      const float raw = wave_sum(row_dot(xr, (const T*)a.w_noise + (int64_t)e[s] * d, d, lane));
+      const float raw = wave_sum(rw[s]);
       ns[s] = cs[s] * a.noise.at(t, grp, G, j, Eg) / (1.0f + __expf(-raw));
     }
     if (s % kpg == 0) {  // the group's first slot carries its primary gradients
       cp[s] = gpg[s] / tot * (V[s] - PV);
       if (noisy_p) {
-        const float raw = wave_sum(row_dot(xr, (const T*)a.w_noise_p + (int64_t)grp * d, d, lane));
+        const float raw = wave_sum(rp[s]);
         np_[s] = cp[s] * a.noise_p.at(t, 0, 1, grp, G) / (1.0f + __expf(-raw));
       }
     }
@@ -294,9 +349,40 @@ __global__ __launch_bounds__(256) void bw_hier_gate_kernel(BwHierGateArgs a) {
     if (a.drp) a.drp[t * G + gg] = n;
   }
   const T* wg = (const T*)a.w_gate;
-  const T* wn = (const T*)a.w_noise;
   const T* wgp = (const T*)a.w_gate_p;
-  const T* wnp = (const T*)a.w_noise_p;
+  if ((d & 3) == 0) {
+    // four columns per lane and step, every table row's chunk loaded together
+    for (int c = lane * 4; c < d; c += 256) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s >= k) continue;
+        float v[4], u[4];
+        load4<T>(wg + (int64_t)e[s] * d + c, v);
+        if (noisy) load4<T>(wn + (int64_t)e[s] * d + c, u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] = fmaf(cs[s], v[j], acc[j]);
+          if (noisy) acc[j] = fmaf(ns[s], u[j], acc[j]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s >= k || s % kpg != 0) continue;
+        const int64_t grp = e[s] / Eg;
+        float v[4], u[4];
+        load4<T>(wgp + grp * d + c, v);
+        if (noisy_p) load4<T>(wnp + grp * d + c, u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] = fmaf(cp[s], v[j], acc[j]);
+          if (noisy_p) acc[j] = fmaf(np_[s], u[j], acc[j]);
+        }
+      }
+      *reinterpret_cast<float4*>(a.dxg + t * d + c) = float4{acc[0], acc[1], acc[2], acc[3]};
+    }
+    return;
+  }
   for (int c = lane; c < d; c += 64) {
     float acc = 0.f;
 #pragma unroll
