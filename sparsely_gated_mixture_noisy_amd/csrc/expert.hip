@@ -190,12 +190,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 //   * The MFMAs run transposed (weights in operand A), so an accumulator lane
 //     holds four consecutive output columns of one row and the epilogue
 //     stores them as 8 bytes.
-//   * Tiles go in windows of GB_WIN = 8 row tiles.  When the column tiles
-//     come in multiples of 8, each XCD runs the window's 8 row tiles against
-//     every 8th column tile, so a weight tile is fetched by one XCD and read
-//     from its L2 by 8 workgroups, and 8 activation tiles are shared by the
-//     XCD's 32 CUs (otherwise consecutive workgroups take the window's row
-//     tiles against one column tile, then the next).
+//   * Tiles go in windows of GB_WIN = 8 row tiles.  When there are at least
+//     32 column tiles, a multiple of 8, each XCD runs the window's 8 row
+//     tiles against every 8th column tile, so a weight tile is fetched by one
+//     XCD and read from its L2 by 8 workgroups, and 8 activation tiles are
+//     shared by the XCD's 32 CUs.  Otherwise consecutive workgroups take the
+//     window's row tiles against one column tile, then the next (with fewer
+//     column tiles an XCD's CUs would hold tiles of several windows).
 // ---------------------------------------------------------------------------
 constexpr int GB_BM = 256, GB_BK = 64, GB_WIN = 8;
 // column tile: 128 with the SwiGLU epilogue (two accumulator sets), 256
@@ -224,13 +225,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     const int Q = g.tiles[g.E];
     const int per_win = GB_WIN * g.ncol;
     const int win = blockIdx.x / per_win, within = blockIdx.x % per_win;
-    // workgroups go to the XCDs round robin: with a column tile count that
-    // is a multiple of 8, XCD x = within % 8 takes the window's row tiles
+    // workgroups go to the XCDs round robin: with at least 32 column tiles,
+    // a multiple of 8, XCD x = within % 8 takes the window's row tiles
     // against column tiles x, x + 8, x + 16, ...  At a time its 32 CUs run 8
     // row tiles against 4 column tiles, so each weight tile is fetched into
     // one XCD's L2 and read there by 8 workgroups
     int qw = within % GB_WIN, ct = within / GB_WIN;
-    if (g.ncol % 8 == 0) {
+    if (g.ncol % 8 == 0 && g.ncol >= 32) {
       const int x = within % 8, j = within / 8;
       qw = j % GB_WIN;
       ct = (j / GB_WIN) * 8 + x;

@@ -85,12 +85,12 @@ SMALL = {
     # the 256-wide column tiles of the big GEMMs with a ragged last column tile
     "big_relu_d320": CONFIGS["flat256"].replace(tokens=1300, d_model=320, d_hidden=640,
                                                 n_experts=4, top_k=1),
-    # column tile counts that are multiples of 8 (8 and 8): the XCD-grouped
-    # tile order of the big GEMMs
-    "big_swiglu_ncol8": CONFIGS["mixtral"].replace(tokens=1100, d_model=2048, d_hidden=1024,
-                                                   n_experts=4),
-    "big_relu_ncol8": CONFIGS["flat256"].replace(tokens=1100, d_model=2048, d_hidden=2048,
-                                                 n_experts=4, top_k=1),
+    # 32 column tiles in the first GEMM: the XCD-grouped tile order of the
+    # big GEMMs (the second GEMM, 2 column tiles, keeps the plain order)
+    "big_swiglu_ncol32": CONFIGS["mixtral"].replace(tokens=1100, d_model=512, d_hidden=4096,
+                                                    n_experts=4),
+    "big_relu_ncol32": CONFIGS["flat256"].replace(tokens=1100, d_model=512, d_hidden=8192,
+                                                  n_experts=4, top_k=1),
     # one group, then one expert: the hierarchy at k = 1
     "hier_k1": CONFIGS["hier4096"].replace(tokens=257, n_experts=160, k_groups=1,
                                            k_per_group=1, top_k=1),
