@@ -455,7 +455,7 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
 // ---- backward layout and launch order ----------------------------------------
 
 struct BwLayout {
-  size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, hid, dp, db, dxs, part_g,
+  size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, tiles_big, hid, dp, db, dxs, part_g,
       part_n, xs, dys;
   // hierarchy: per-slot and per-group score gradients, and the routing
   // without capacity (when the forward capped it) for the secondary tables
@@ -523,6 +523,7 @@ BwLayout bw_layout(const moe_config* c) {
   L.wnt = take(fused_dxg && c->noisy ? 2 * (size_t)d * L.e16 : 0);
   L.dxg = take(4 * (size_t)T * d);
   L.tiles = take(4 * (size_t)(E + 1));
+  L.tiles_big = take(4 * (size_t)(E + 1));
   L.hid = take(es * (size_t)A * h);
   L.dp = take(es * (size_t)A * h);
   L.db = take(sw ? es * (size_t)A * h : 0);
@@ -850,24 +851,61 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, s),
                        "backward tiles"));
     const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
-    // hidden layer recomputed with its gradient
-    BwGemm q = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
-    q.mode = BW_POS;
-    q.epi = sw ? BW_EPI_SWIGLU : BW_EPI_RELU;
-    q.a[1] = op_rows(dys, d, f32);
-    q.b[1] = per_expert(op_cols(p->w2, h, f32), hd);
-    if (sw) q.b[2] = per_expert(op_rows(p->w3, d, f32), hd);
-    q.M = A;
-    q.N = h;
-    q.K = d;
-    q.offsets = sv->offsets;
-    q.tiles = tiles;
-    q.E = E;
-    q.C = hid;
-    q.C2 = dp;
-    q.C3 = db;
-    MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
-                       "backward hidden"));
+    if (bw_hidden_big_tiles(bf16, A, E)) {
+      // large experts: dHid = dY W2 into the dP (dA) buffer, then the
+      // forward's large-tile GEMM recomputes the hidden layer and applies
+      // the activation's derivative in its epilogue
+      BwGemm q = product(op_rows(dys, d, f32), per_expert(op_cols(p->w2, h, f32), hd));
+      q.mode = BW_POS;
+      q.M = A;
+      q.N = h;
+      q.K = d;
+      q.offsets = sv->offsets;
+      q.tiles = tiles;
+      q.E = E;
+      q.C = dp;
+      q.c_f32 = 0;
+      q.ldc = h;
+      MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
+                         "backward dhid"));
+      int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
+      MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_big_rows(), tiles_big,
+                                         nullptr, s),
+                         "backward tiles"));
+      BwHiddenArgs ha;
+      ha.xs = xs;
+      ha.offsets = sv->offsets;
+      ha.tiles = tiles_big;
+      ha.E = E;
+      ha.d = d;
+      ha.h = h;
+      ha.A = A;
+      ha.w1 = p->w1;
+      ha.w3 = sw ? p->w3 : nullptr;
+      ha.hid = hid;
+      ha.d1 = dp;
+      ha.d3 = db;
+      MOE_TRY(hip_status(launch_bw_hidden_big(ha, sw, s), "backward hidden"));
+    } else {
+      // hidden layer recomputed with its gradient
+      BwGemm q = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
+      q.mode = BW_POS;
+      q.epi = sw ? BW_EPI_SWIGLU : BW_EPI_RELU;
+      q.a[1] = op_rows(dys, d, f32);
+      q.b[1] = per_expert(op_cols(p->w2, h, f32), hd);
+      if (sw) q.b[2] = per_expert(op_rows(p->w3, d, f32), hd);
+      q.M = A;
+      q.N = h;
+      q.K = d;
+      q.offsets = sv->offsets;
+      q.tiles = tiles;
+      q.E = E;
+      q.C = hid;
+      q.C2 = dp;
+      q.C3 = db;
+      MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
+                         "backward hidden"));
+    }
     // dX = dP W1 (+ dB W3), per routed row
     BwGemm r = product(op_rows(dp, h, f32), per_expert(op_cols(p->w1, d, f32), hd));
     r.mode = BW_POS;

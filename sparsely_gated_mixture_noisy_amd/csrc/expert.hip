@@ -21,7 +21,10 @@ namespace moe {
 
 constexpr int GM_BM = 128, GM_BN = 128, GM_BK = 32, GM_LD = GM_BK + 8;
 
-enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+// EPI_RELU_BWD, EPI_SWIGLU_BWD: the backward's hidden layer (large tiles
+// only); C2 holds dHid = dY W2_e on entry and gets dP (ReLU) or dA (SwiGLU),
+// C3 gets dB, C gets the recomputed hidden activations
+enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RELU_BWD = 3, EPI_SWIGLU_BWD = 4 };
 
 struct GemmArgs {
   const bf16_t* A;
@@ -37,6 +40,8 @@ struct GemmArgs {
   bf16_t* C;               // [A][ldc]
   int64_t ldc;
   int ncol;                // ceil(N / GM_BN)
+  bf16_t* C2 = nullptr;    // backward epilogues: [A][ldc], dHid in, dP / dA out
+  bf16_t* C3 = nullptr;    // SwiGLU backward: dB [A][ldc]
 };
 
 // Expert owning tile q: the largest e with tiles[e] <= q (tiles non-decreasing).
@@ -201,14 +206,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 constexpr int GB_BM = 256, GB_BK = 64, GB_WIN = 8;
 // column tile: 128 with the SwiGLU epilogue (two accumulator sets), 256
 // otherwise
-template <int EPI> constexpr int gb_bn() { return EPI == EPI_SWIGLU ? 128 : 256; }
+template <int EPI> constexpr int gb_bn() {
+  return EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD ? 128 : 256;
+}
 
 // element offset of chunk c (8 elements) of row r in a swizzled operand tile
 __device__ __forceinline__ int gb_slot(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
-  constexpr bool SW = (EPI == EPI_SWIGLU);
+  constexpr bool SW = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD);
+  constexpr bool BWD = (EPI == EPI_RELU_BWD || EPI == EPI_SWIGLU_BWD);
   constexpr int BN = gb_bn<EPI>();
   constexpr int NBJ = BN / 64;   // 1 KB weight blocks each wave loads per slice
   constexpr int WN = BN / 4;     // columns per wave
@@ -365,26 +373,70 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i) {
     const int row = wm * 128 + 32 * i + fr;
     if (row >= m) continue;
-    bf16_t* crow = g.C + (int64_t)(row0 + row) * g.ldc;
+    const int64_t roff = (int64_t)(row0 + row) * g.ldc;
+    bf16_t* crow = g.C + roff;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = n0 + wn * WN + 32 * j + 8 * q + q4;
-        float v[4];
+        const bool full = col + 3 < g.N;
+        float v[4], v2[4], v3[4];
+        if constexpr (BWD) {
+          // this lane's dHid values; it overwrites them below
+          float dh[4];
+          if (full) {
+            const uint2 u = *reinterpret_cast<const uint2*>(g.C2 + roff + col);
+            dh[0] = __uint_as_float(u.x << 16);
+            dh[1] = __uint_as_float(u.x & 0xffff0000u);
+            dh[2] = __uint_as_float(u.y << 16);
+            dh[3] = __uint_as_float(u.y & 0xffff0000u);
+          } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = acc[i][j][4 * q + r];
-          if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.f);
-          if constexpr (EPI == EPI_SWIGLU) x = silu_f(x) * acc3[i][j][4 * q + r];
-          v[r] = x;
+            for (int r = 0; r < 4; ++r)
+              dh[r] = col + r < g.N ? bf16_to_f32(g.C2[roff + col + r]) : 0.f;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = acc[i][j][4 * q + r];
+            if constexpr (EPI == EPI_RELU_BWD) {
+              v[r] = fmaxf(a, 0.f);
+              v2[r] = a > 0.f ? dh[r] : 0.f;
+              v3[r] = 0.f;
+            } else {
+              const float b = acc3[i][j][4 * q + r];
+              const float sg = 1.0f / (1.0f + expf(-a));
+              const float sl = a * sg;
+              v[r] = sl * b;
+              v2[r] = dh[r] * b * sg * (1.0f + a * (1.0f - sg));
+              v3[r] = dh[r] * sl;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = acc[i][j][4 * q + r];
+            if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+            if constexpr (EPI == EPI_SWIGLU) x = silu_f(x) * acc3[i][j][4 * q + r];
+            v[r] = x;
+          }
         }
-        if (col + 3 < g.N) {
+        if (full) {
           *reinterpret_cast<uint2*>(crow + col) = uint2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
+          if constexpr (BWD)
+            *reinterpret_cast<uint2*>(g.C2 + roff + col) =
+                uint2{cvt_pk_bf16(v2[0], v2[1]), cvt_pk_bf16(v2[2], v2[3])};
+          if constexpr (EPI == EPI_SWIGLU_BWD)
+            *reinterpret_cast<uint2*>(g.C3 + roff + col) =
+                uint2{cvt_pk_bf16(v3[0], v3[1]), cvt_pk_bf16(v3[2], v3[3])};
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (col + r < g.N) crow[col + r] = f32_to_bf16(v[r]);
+            if (col + r < g.N) {
+              crow[col + r] = f32_to_bf16(v[r]);
+              if constexpr (BWD) g.C2[roff + col + r] = f32_to_bf16(v2[r]);
+              if constexpr (EPI == EPI_SWIGLU_BWD) g.C3[roff + col + r] = f32_to_bf16(v3[r]);
+            }
         }
       }
   }
@@ -462,8 +514,8 @@ int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E) {
 
 template <int EPI>
 static hipError_t launch_big(const GemmArgs& g, int64_t qmax, hipStream_t s) {
-  constexpr size_t lds =
-      sizeof(bf16_t) * (size_t)GB_BK * 2 * (GB_BM + gb_bn<EPI>() * (EPI == EPI_SWIGLU ? 2 : 1));
+  constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD;
+  constexpr size_t lds = sizeof(bf16_t) * (size_t)GB_BK * 2 * (GB_BM + gb_bn<EPI>() * (SW ? 2 : 1));
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI>,
@@ -533,6 +585,37 @@ hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_
   hipLaunchKernelGGL(grouped_gemm_kernel<EPI_NONE>, dim3((unsigned)(qmax * g2.ncol)), dim3(256), 0,
                      s, g2);
   return hipGetLastError();
+}
+
+bool bw_hidden_big_tiles(bool bf16, int64_t A, int E) { return bf16 && big_tiles(A, E); }
+int bw_hidden_big_rows() { return GB_BM; }
+
+// The backward's hidden layer on the large-tile kernel: the forward's first
+// GEMM over the routed rows (X W1_e^T, and X W3_e^T with SwiGLU), with an
+// epilogue that takes dHid from d1 and leaves the recomputed activations in
+// hid, dP or dA in d1 and dB in d3.
+hipError_t launch_bw_hidden_big(const BwHiddenArgs& a, bool swiglu, hipStream_t s) {
+  if (a.A == 0) return hipSuccess;
+  const int bn = swiglu ? gb_bn<EPI_SWIGLU_BWD>() : gb_bn<EPI_RELU_BWD>();
+  GemmArgs g;
+  g.A = (const bf16_t*)a.xs;
+  g.lda = a.d;
+  g.perm = nullptr;
+  g.k = 1;
+  g.B = (const bf16_t*)a.w1;
+  g.B3 = (const bf16_t*)a.w3;
+  g.N = a.h;
+  g.K = a.d;
+  g.offsets = a.offsets;
+  g.tiles = a.tiles;
+  g.E = a.E;
+  g.C = (bf16_t*)a.hid;
+  g.ldc = a.h;
+  g.ncol = (a.h + bn - 1) / bn;
+  g.C2 = (bf16_t*)a.d1;
+  g.C3 = (bf16_t*)a.d3;
+  const int64_t qmax = (a.A + GB_BM - 1) / GB_BM + a.E;
+  return swiglu ? launch_big<EPI_SWIGLU_BWD>(g, qmax, s) : launch_big<EPI_RELU_BWD>(g, qmax, s);
 }
 
 }  // namespace moe

@@ -138,6 +138,25 @@ hipError_t launch_pack_experts(const void* w1, const void* w2, int E, int d, int
                                hipStream_t s);
 hipError_t launch_expert_ffn(const FfnArgs& a, bool bf16, int swiglu, hipStream_t s);
 
+// The backward's hidden layer on the large-tile GEMM (bf16 layers whose
+// experts average at least bw_hidden_big_rows() rows): recomputes the hidden
+// activations and turns dHid into the pre-activation gradients.
+struct BwHiddenArgs {
+  const void* xs;          // [A][d] routed rows of x, in expert order
+  const int32_t* offsets;  // [E+1]
+  const int32_t* tiles;    // [E+1] tile map of bw_hidden_big_rows() rows
+  int E, d, h;
+  int64_t A;
+  const void* w1;          // [E][h][d]
+  const void* w3;          // [E][h][d] (SwiGLU) or null
+  void* hid;               // [A][h] out: relu(a), or silu(a) b
+  void* d1;                // [A][h] in: dHid = dY W2; out: dP (ReLU) or dA (SwiGLU)
+  void* d3;                // [A][h] out: dB (SwiGLU) or null
+};
+bool bw_hidden_big_tiles(bool bf16, int64_t A, int E);
+int bw_hidden_big_rows();
+hipError_t launch_bw_hidden_big(const BwHiddenArgs& a, bool swiglu, hipStream_t s);
+
 // -------------------------------------------------------- combine / stats --
 hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float* gate, int64_t T,
                           int k, int d, bool bf16, void* y, hipStream_t s);

@@ -118,6 +118,15 @@ CASES = {
                                               d_hidden=256), 0.8, 1.0),
     "bf16_hier_capacity10": (CONFIGS["hier4096"].replace(tokens=400, n_experts=64, d_model=128,
                                                          d_hidden=256, capacity=10), 0.8, 0.0),
+    # experts with >= 256 rows on average: dHid on the product kernel, the
+    # hidden layer on the large-tile GEMM (ragged last column tiles; 32
+    # column tiles, the XCD-grouped order, in the last case)
+    "bf16_big_relu": (CONFIGS["flat256"].replace(tokens=700, n_experts=4, d_model=256,
+                                                 d_hidden=640, top_k=2), 0.8, 1.0),
+    "bf16_big_swiglu": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=256,
+                                                   d_hidden=320), 0.8, 0.0),
+    "bf16_big_swiglu_h4096": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=64,
+                                                         d_hidden=4096), 0.8, 0.0),
     # one group, then one expert: both softmax levels are a single weight of 1
     "bf16_hier_k1": (CONFIGS["hier4096"].replace(tokens=200, n_experts=64, d_model=128,
                                                  d_hidden=256, k_groups=1, k_per_group=1,
@@ -282,6 +291,80 @@ def test_backward_flat256_full_size_sampled():
         dx_ref[n] = dxe + dclean @ wg + draw @ wn
     got = np_(g.dx)[toks]
     _check("dx[sampled]", got, dx_ref, RTOL["bf16"], FRO["bf16"])
+
+
+def test_backward_mixtral_full_size_sampled():
+    """The Mixtral-shaped layer (8192 tokens, 8 SwiGLU experts 4096 -> 14336
+    -> 4096, top-2, noise-free) in the launch configuration the timings use,
+    where the hidden layer runs on the large-tile GEMM.  The oracle computes,
+    one by one: for sampled experts and hidden units, the rows of dW1 and dW3
+    and the columns of dW2 of those units (hidden units are independent, so
+    the unit-sliced expert gives them exactly), and the input gradients of
+    sampled tokens (their own slots and the gate part)."""
+    cfg = CONFIGS["mixtral"]
+    wi, wl = 1.0, 0.0
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    dy = make_upstream(cfg, seed=0, device="cuda")
+    _say("[backward] mixtral full size: forward + backward on the GPU")
+    fwd = L.forward(cfg, inp["x"], inp, inp, wi, wl, balance=True, save=True)
+    g = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
+    torch.cuda.synchronize()
+    _say("[backward] oracle gate and statistics")
+    big = ("w1", "w2", "w3")
+    cpu = {key: (v.to("cpu") if v is not None else None) for key, v in inp.items()
+           if key not in big}
+    x = cpu["x"].double().numpy()
+    dyn = dy.to("cpu").double().numpy()
+    gi = oracle.gate(cpu, cfg)
+    T, k, E = cfg.tokens, cfg.top_k, cfg.n_experts
+    idx, gates = gi["idx"], gi["gates"]
+    assert (np_(fwd.topk_idx) == idx).all()
+    counts, offsets, perm, inv = oracle.route(idx, E)
+    dimp = wi * oracle.cv_squared_grad(oracle.importance(idx, gates, E))
+
+    def tables(e):
+        return tuple(inp[key][e].to("cpu").double().numpy() for key in ("w1", "w3", "w2"))
+
+    rng = np.random.default_rng(1)
+    # table gradients of sampled experts and hidden units
+    for e in rng.choice(np.nonzero(counts > 0)[0], size=2, replace=False):
+        w1e, w3e, w2e = tables(e)
+        rows = perm[offsets[e]:offsets[e + 1]]
+        toks = rows // k
+        dY = gates.reshape(-1)[rows][:, None] * dyn[toks]
+        units = np.sort(rng.choice(cfg.d_hidden, size=8, replace=False))
+        _, dw1, dw3, dw2 = oracle.expert_swiglu_backward(x[toks], w1e[units], w3e[units],
+                                                         w2e[:, units], dY)
+        _check(f"dw1[{e}][units]", g.dw1[e][torch.from_numpy(units).cuda()], dw1,
+               RTOL["bf16"], FRO["bf16"])
+        _check(f"dw3[{e}][units]", g.dw3[e][torch.from_numpy(units).cuda()], dw3,
+               RTOL["bf16"], FRO["bf16"])
+        _check(f"dw2[{e}][:, units]", g.dw2[e][:, torch.from_numpy(units).cuda()], dw2,
+               RTOL["bf16"], FRO["bf16"])
+
+    # input gradients of sampled tokens: expert part + gate part
+    srt = -np.sort(-gi["H"], axis=1)
+    risky = ((srt[:, k - 2:k + 1] - srt[:, k - 1:k + 2]) < GAP).any(axis=1)
+    toks = np.sort(rng.choice(np.nonzero(~risky)[0], size=12, replace=False))
+    dxe = np.zeros((toks.size, cfg.d_model))
+    dg = np.zeros((toks.size, k))
+    for e in np.unique(idx[toks]):
+        w1e, w3e, w2e = tables(e)
+        for n, t in enumerate(toks):
+            for sl in np.nonzero(idx[t] == e)[0]:
+                xt = x[t:t + 1]
+                dg[n, sl] = oracle.expert_swiglu(xt, w1e, w3e, w2e)[0] @ dyn[t] + dimp[e]
+                dX, _, _, _ = oracle.expert_swiglu_backward(xt, w1e, w3e, w2e,
+                                                            gates[t, sl] * dyn[t:t + 1])
+                dxe[n] += dX[0]
+    wg = cpu["w_gate"].double().numpy()
+    dx_ref = np.zeros_like(dxe)
+    for n, t in enumerate(toks):
+        dH = np.zeros(E)
+        dH[idx[t]] = gates[t] * (dg[n] - gates[t] @ dg[n])
+        dx_ref[n] = dxe[n] + dH @ wg
+    _check("dx[sampled]", np_(g.dx)[toks], dx_ref, RTOL["bf16"], FRO["bf16"])
+    _say("[backward] mixtral full size: ok")
 
 
 def test_backward_hier4096_full_size_sampled():
