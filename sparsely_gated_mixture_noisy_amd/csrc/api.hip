@@ -851,27 +851,29 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, s),
                        "backward tiles"));
     const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
-    if (bw_hidden_big_tiles(bf16, A, E)) {
-      // large experts: dHid = dY W2 into the dP (dA) buffer, then the
-      // forward's large-tile GEMM recomputes the hidden layer and applies
-      // the activation's derivative in its epilogue
-      BwGemm q = product(op_rows(dys, d, f32), per_expert(op_cols(p->w2, h, f32), hd));
-      q.mode = BW_POS;
-      q.M = A;
-      q.N = h;
-      q.K = d;
-      q.offsets = sv->offsets;
-      q.tiles = tiles;
-      q.E = E;
-      q.C = dp;
-      q.c_f32 = 0;
-      q.ldc = h;
-      MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
-                         "backward dhid"));
-      int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
+    const bool big = bw_hidden_big_tiles(bf16, A, E);
+    int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
+    if (big)
       MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_big_rows(), tiles_big,
                                          nullptr, s),
                          "backward tiles"));
+    if (big) {
+      // large experts, on the forward's large-tile GEMM: dHid = dY W2 into
+      // the dP (dA) buffer, then the hidden layer recomputed with the
+      // activation's derivative applied in the epilogue
+      BwBigProduct q;
+      q.a = dys;
+      q.a2 = nullptr;
+      q.b = p->w2;
+      q.b2 = nullptr;
+      q.A = A;
+      q.E = E;
+      q.N = h;
+      q.K = d;
+      q.offsets = sv->offsets;
+      q.tiles = tiles_big;
+      q.c = dp;
+      MOE_TRY(hip_status(launch_bw_big_product(q, s), "backward dhid"));
       BwHiddenArgs ha;
       ha.xs = xs;
       ha.offsets = sv->offsets;
@@ -907,20 +909,36 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
                          "backward hidden"));
     }
     // dX = dP W1 (+ dB W3), per routed row
-    BwGemm r = product(op_rows(dp, h, f32), per_expert(op_cols(p->w1, d, f32), hd));
-    r.mode = BW_POS;
-    if (sw) add_pair(r, op_rows(db, h, f32), per_expert(op_cols(p->w3, d, f32), hd));
-    r.M = A;
-    r.N = d;
-    r.K = h;
-    r.offsets = sv->offsets;
-    r.tiles = tiles;
-    r.E = E;
-    r.C = dxs;
-    r.c_f32 = f32 ? 1 : 0;  // in the layer dtype, like the expert outputs
-    r.ldc = d;
-    MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((d + 127) / 128), s),
-                       "backward expert dx"));
+    if (big) {
+      BwBigProduct q;
+      q.a = dp;
+      q.a2 = sw ? db : nullptr;
+      q.b = p->w1;
+      q.b2 = sw ? p->w3 : nullptr;
+      q.A = A;
+      q.E = E;
+      q.N = d;
+      q.K = h;
+      q.offsets = sv->offsets;
+      q.tiles = tiles_big;
+      q.c = dxs;
+      MOE_TRY(hip_status(launch_bw_big_product(q, s), "backward expert dx"));
+    } else {
+      BwGemm r = product(op_rows(dp, h, f32), per_expert(op_cols(p->w1, d, f32), hd));
+      r.mode = BW_POS;
+      if (sw) add_pair(r, op_rows(db, h, f32), per_expert(op_cols(p->w3, d, f32), hd));
+      r.M = A;
+      r.N = d;
+      r.K = h;
+      r.offsets = sv->offsets;
+      r.tiles = tiles;
+      r.E = E;
+      r.C = dxs;
+      r.c_f32 = f32 ? 1 : 0;  // in the layer dtype, like the expert outputs
+      r.ldc = d;
+      MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((d + 127) / 128), s),
+                         "backward expert dx"));
+    }
   }
   // table gradients, one problem per expert over its rows (zero without rows)
   auto wgrad = [&](void* out, BwOp a, BwOp b, int64_t M, int64_t N, const char* what) {

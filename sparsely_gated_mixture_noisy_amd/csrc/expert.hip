@@ -21,6 +21,8 @@ namespace moe {
 
 constexpr int GM_BM = 128, GM_BN = 128, GM_BK = 32, GM_LD = GM_BK + 8;
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
 // EPI_RELU_BWD, EPI_SWIGLU_BWD: the backward's hidden layer (large tiles
 // only); C2 holds dHid = dY W2_e on entry and gets dP (ReLU) or dA (SwiGLU),
 // C3 gets dB, C gets the recomputed hidden activations
@@ -42,6 +44,10 @@ struct GemmArgs {
   int ncol;                // ceil(N / GM_BN)
   bf16_t* C2 = nullptr;    // backward epilogues: [A][ldc], dHid in, dP / dA out
   bf16_t* C3 = nullptr;    // SwiGLU backward: dB [A][ldc]
+  // large tiles only: a second operand pair (same layouts) whose product is
+  // added, K running over A, B first and then A2, B2
+  const bf16_t* A2 = nullptr;
+  const bf16_t* B2 = nullptr;
 };
 
 // Expert owning tile q: the largest e with tiles[e] <= q (tiles non-decreasing).
@@ -213,10 +219,24 @@ template <int EPI> constexpr int gb_bn() {
 // element offset of chunk c (8 elements) of row r in a swizzled operand tile
 __device__ __forceinline__ int gb_slot(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
 
-template <int EPI>
+// Transposed read of four k values of one weight column from a [k][n] LDS
+// tile (BN columns, 16-byte chunks swizzled as chunk ^ 2 (row & 3)).  Within
+// each group of 16 lanes, lane j points at row kb + j / 4, columns
+// nb + 4 (j % 4) .. +3, and ds_read_b64_tr_b16 hands lane i the values at
+// rows kb .. kb + 3 of column nb + i: lane i of group G receives column
+// nb(G) + i, rows kb(G) .. kb(G) + 3.
+template <int BN>
+__device__ __forceinline__ v4i16_t gb_read_tr(const bf16_t* T, int row, int n) {
+  const int slot = row * (BN / 8) + ((n >> 3) ^ (2 * (row & 3)));
+  typedef v4i16_t __attribute__((address_space(3))) * lds_v4p;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(T + slot * 8 + (n & 7)));
+}
+
+template <int EPI, bool TBB>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   constexpr bool SW = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD);
   constexpr bool BWD = (EPI == EPI_RELU_BWD || EPI == EPI_SWIGLU_BWD);
+  static_assert(!TBB || EPI == EPI_NONE, "weights stored [K][N] only for plain products");
   constexpr int BN = gb_bn<EPI>();
   constexpr int NBJ = BN / 64;   // 1 KB weight blocks each wave loads per slice
   constexpr int WN = BN / 4;     // columns per wave
@@ -264,41 +284,58 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   const int n0 = __builtin_amdgcn_readfirstlane(s_ct) * BN;
 
   // Direct loads: wave w fills 1 KB blocks w*4 + j (A, j < 4) and
-  // w*NBJ + j (B, B3, j < NBJ); lane l of block b fills slot 64b + l: row
-  // (64b + l) / 8, chunk position l % 8, i.e. source chunk
-  // (l % 8) ^ ((row >> 1) & 7).
-  // (arrays sized for the widest tile: the lambdas below capture them, and
-  // the host pass of the compiler drops the kernel when a captured array's
-  // bound depends on the template argument; unused entries are optimised out)
-  const bf16_t* ap[8];
-  const bf16_t* bp[8];
-  const bf16_t* b3p[8];
+  // w*NBJ + j (B, B3, j < NBJ); lane l of block b fills slot 64b + l.
+  //   K-major tiles (activations; weights stored [N][K]): row (64b + l) / 8,
+  //   chunk position l % 8, i.e. source chunk (l % 8) ^ ((row >> 1) & 7).
+  //   Weights stored [K][N] (TBB): the tile is [k][n], 32 chunks per k row:
+  //   row 2b + l / 32, chunk position l % 32, i.e. source chunk
+  //   (l % 32) ^ (2 (row & 3)).
+  // Offsets are kept per lane so that a second operand pair can use them.
+  // (arrays of a fixed size: the lambdas below capture them, and the host
+  // pass of the compiler drops the kernel when a captured array's bound
+  // depends on the template argument; unused entries are optimised out)
+  int64_t aoff[4], boff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = (w * 4 + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int p = row0 + min(r, m - 1);
     const int64_t src = g.perm ? (int64_t)(g.perm[p] / g.k) : (int64_t)p;
-    ap[j] = g.A + src * g.lda + c * 8;
+    aoff[j] = src * g.lda + c * 8;
   }
 #pragma unroll
-  for (int j = 0; j < NBJ; ++j) {
-    const int r = (w * NBJ + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int n = min(n0 + r, g.N - 1);
-    bp[j] = g.B + ((int64_t)e * g.N + n) * g.K + c * 8;
-    b3p[j] = SW ? g.B3 + ((int64_t)e * g.N + n) * g.K + c * 8 : g.B;
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (TBB) {
+      const int r = 2 * (w * NBJ + (j < NBJ ? j : 0)) + (lane >> 5);
+      const int c = (lane & 31) ^ (2 * (r & 3));
+      const int n = min(n0 + 8 * c, g.N - 8);
+      boff[j] = (int64_t)e * g.N * g.K + (int64_t)r * g.N + n;
+    } else {
+      const int r = (w * NBJ + (j < NBJ ? j : 0)) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int n = min(n0 + r, g.N - 1);
+      boff[j] = ((int64_t)e * g.N + n) * g.K + c * 8;
+    }
   }
-  auto dma = [&](int k0, int buf) {
+  const int nk = g.K / GB_BK;
+  // slice kt of the K loop: the first pair's slices, then the second's
+  auto dma = [&](int kt, int buf) {
+    const bool second = kt >= nk;
+    const int k0 = (second ? kt - nk : kt) * GB_BK;
+    const bf16_t* Ab = second ? g.A2 : g.A;
+    const bf16_t* Bb = second ? g.B2 : g.B;
+    const int64_t bk = TBB ? (int64_t)k0 * g.N : (int64_t)k0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds(ap[j] + k0, As + buf * AT + (w * 4 + j) * 512, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Ab + aoff[j] + k0, As + buf * AT + (w * 4 + j) * 512, 16, 0,
+                                       0);
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-      __builtin_amdgcn_global_load_lds(bp[j] + k0, Bs + buf * BT + (w * NBJ + j) * 512, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Bb + boff[j] + bk, Bs + buf * BT + (w * NBJ + j) * 512, 16,
+                                       0, 0);
       if constexpr (SW)
-        __builtin_amdgcn_global_load_lds(b3p[j] + k0, B3s + buf * BT + (w * NBJ + j) * 512, 16, 0,
-                                         0);
+        __builtin_amdgcn_global_load_lds(g.B3 + boff[j] + bk, B3s + buf * BT + (w * NBJ + j) * 512,
+                                         16, 0, 0);
     }
   };
 
@@ -317,13 +354,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
       for (int j = 0; j < 2; ++j) acc3[i][j] = f32x16{};
   }
 
-  const int nk = g.K / GB_BK;
+  const int nkt = (g.A2 ? 2 : 1) * nk;
   dma(0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
     // the next K slice streams into the other buffer while this one is used
-    if (kt + 1 < nk) dma((kt + 1) * GB_BK, buf ^ 1);
+    if (kt + 1 < nkt) dma(kt + 1, buf ^ 1);
     // every wave runs the MFMAs (rows past m hold copies of a valid row and are
     // dropped at the store): a branch here would make the compiler keep a
     // second copy of the accumulators
@@ -340,7 +377,18 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
           af[sl][i] = *reinterpret_cast<const bf16x8*>(Ab + gb_slot(wm * 128 + i * 32 + fr, c));
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          bf[sl][j] = *reinterpret_cast<const bf16x8*>(Bb + gb_slot(wn * WN + j * 32 + fr, c));
+          if constexpr (TBB) {
+            // column wn*WN + 32j + lane % 32, k = 16 st + 8 (lane / 32) + 0..7
+            const int G = lane >> 4, jj = lane & 15;
+            const int nb = wn * WN + j * 32 + 16 * (G & 1) + 4 * (jj & 3);
+            const int kb = st * 16 + 8 * (G >> 1) + (jj >> 2);
+            const v4i16_t lo = gb_read_tr<BN>(Bb, kb, nb);
+            const v4i16_t hi = gb_read_tr<BN>(Bb, kb + 4, nb);
+            bf[sl][j] = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+            bf[sl][j] = *reinterpret_cast<const bf16x8*>(Bb + gb_slot(wn * WN + j * 32 + fr, c));
+          }
           if constexpr (SW)
             b3f[sl][j] = *reinterpret_cast<const bf16x8*>(B3b + gb_slot(wn * WN + j * 32 + fr, c));
         }
@@ -512,20 +560,20 @@ int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E) {
   return big_tiles(A, E) ? GB_BM : GM_BM;
 }
 
-template <int EPI>
+template <int EPI, bool TBB = false>
 static hipError_t launch_big(const GemmArgs& g, int64_t qmax, hipStream_t s) {
   constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD;
   constexpr size_t lds = sizeof(bf16_t) * (size_t)GB_BK * 2 * (GB_BM + gb_bn<EPI>() * (SW ? 2 : 1));
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI>,
+    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI, TBB>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     attr_done = true;
   }
   const int64_t wins = (qmax + GB_WIN - 1) / GB_WIN;
-  hipLaunchKernelGGL(grouped_gemm_big_kernel<EPI>, dim3((unsigned)(wins * GB_WIN * g.ncol)),
-                     dim3(512), lds, s, g);
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<EPI, TBB>),
+                     dim3((unsigned)(wins * GB_WIN * g.ncol)), dim3(512), lds, s, g);
   return hipGetLastError();
 }
 
@@ -616,6 +664,33 @@ hipError_t launch_bw_hidden_big(const BwHiddenArgs& a, bool swiglu, hipStream_t 
   g.C3 = (bf16_t*)a.d3;
   const int64_t qmax = (a.A + GB_BM - 1) / GB_BM + a.E;
   return swiglu ? launch_big<EPI_SWIGLU_BWD>(g, qmax, s) : launch_big<EPI_RELU_BWD>(g, qmax, s);
+}
+
+// A plain product of the backward on the large tiles: c = a b_e (+ a2 b2_e)
+// per routed row, with the tables stored [E][K][N] (read across their rows
+// through the transposed LDS reads).
+hipError_t launch_bw_big_product(const BwBigProduct& p, hipStream_t s) {
+  if (p.A == 0) return hipSuccess;
+  if (p.N % 8 != 0 || p.K % GB_BK != 0) return hipErrorInvalidValue;
+  GemmArgs g;
+  g.A = (const bf16_t*)p.a;
+  g.lda = p.K;
+  g.perm = nullptr;
+  g.k = 1;
+  g.B = (const bf16_t*)p.b;
+  g.B3 = nullptr;
+  g.N = p.N;
+  g.K = p.K;
+  g.offsets = p.offsets;
+  g.tiles = p.tiles;
+  g.E = p.E;
+  g.C = (bf16_t*)p.c;
+  g.ldc = p.N;
+  g.ncol = (p.N + gb_bn<EPI_NONE>() - 1) / gb_bn<EPI_NONE>();
+  g.A2 = (const bf16_t*)p.a2;
+  g.B2 = (const bf16_t*)p.b2;
+  const int64_t qmax = (p.A + GB_BM - 1) / GB_BM + p.E;
+  return launch_big<EPI_NONE, true>(g, qmax, s);
 }
 
 }  // namespace moe

@@ -156,6 +156,21 @@ struct BwHiddenArgs {
 bool bw_hidden_big_tiles(bool bf16, int64_t A, int E);
 int bw_hidden_big_rows();
 hipError_t launch_bw_hidden_big(const BwHiddenArgs& a, bool swiglu, hipStream_t s);
+// c[p] = a[p] b_e (+ a2[p] b2_e) for the routed rows p of expert e, on the
+// same large tiles; a, a2 [A][K] bf16 in expert order, b, b2 [E][K][N] bf16,
+// c [A][N] bf16; N % 8 == 0, K % 64 == 0
+struct BwBigProduct {
+  const void* a;
+  const void* a2;          // or null
+  const void* b;
+  const void* b2;          // or null
+  int64_t A;
+  int E, N, K;
+  const int32_t* offsets;  // [E+1]
+  const int32_t* tiles;    // [E+1] tile map of bw_hidden_big_rows() rows
+  void* c;
+};
+hipError_t launch_bw_big_product(const BwBigProduct& p, hipStream_t s);
 
 // -------------------------------------------------------- combine / stats --
 hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float* gate, int64_t T,
