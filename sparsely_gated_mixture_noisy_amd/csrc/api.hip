@@ -455,7 +455,7 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
 // ---- backward layout and launch order ----------------------------------------
 
 struct BwLayout {
-  size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, tiles_big, hid, dp, db, dxs, part_g,
+  size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, tiles_big, zero, hid, dp, db, dxs, part_g,
       part_n, xs, dys;
   // hierarchy: per-slot and per-group score gradients, and the routing
   // without capacity (when the forward capped it) for the secondary tables
@@ -524,6 +524,7 @@ BwLayout bw_layout(const moe_config* c) {
   L.dxg = take(4 * (size_t)T * d);
   L.tiles = take(4 * (size_t)(E + 1));
   L.tiles_big = take(4 * (size_t)(E + 1));
+  L.zero = take(2 * (size_t)std::max(h, d));
   L.hid = take(es * (size_t)A * h);
   L.dp = take(es * (size_t)A * h);
   L.db = take(sw ? es * (size_t)A * h : 0);
@@ -846,12 +847,13 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     MOE_TRY(hip_status(launch_bw_gather_rows(dy, sv->perm, k, sv->topk_gate, A, d, bf16, dys, s),
                        "backward gather dy"));
   }
+  // experts averaging >= 256 rows (bf16): the large-tile products
+  const bool big = bw_hidden_big_tiles(bf16, A, E);
   if (A > 0) {
     int32_t* tiles = at<int32_t>(ws, L.tiles);
     MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, s),
                        "backward tiles"));
     const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
-    const bool big = bw_hidden_big_tiles(bf16, A, E);
     int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
     if (big)
       MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_big_rows(), tiles_big,
@@ -956,9 +958,34 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     const int64_t grid = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
     return hip_status(launch_bw_gemm(q, bf16, grid, s), what);
   };
-  MOE_TRY(wgrad(g->dw1, op_cols(dp, h, f32), op_cols(xs, d, f32), h, d, "backward dw1"));
-  if (sw) MOE_TRY(wgrad(g->dw3, op_cols(db, h, f32), op_cols(xs, d, f32), h, d, "backward dw3"));
-  MOE_TRY(wgrad(g->dw2, op_cols(dys, d, f32), op_cols(hid, h, f32), d, h, "backward dw2"));
+  if (big) {
+    // positions past an expert's rows are read from a row of zeros
+    void* zero = at<void>(ws, L.zero);
+    MOE_TRY(hip_status(launch_fill_i32((int32_t*)zero, std::max(h, d) / 2, 0, s),
+                       "backward zero row"));
+    auto wgrad_big = [&](void* out, const void* a, int M, const void* b, int N,
+                         const char* what) {
+      if (!out) return MOE_OK;
+      BwBigWgrad q;
+      q.a = a;
+      q.b = b;
+      q.E = E;
+      q.M = M;
+      q.N = N;
+      q.offsets = sv->offsets;
+      q.zero = zero;
+      q.c = out;
+      return hip_status(launch_bw_big_wgrad(q, s), what);
+    };
+    MOE_TRY(wgrad_big(g->dw1, dp, h, xs, d, "backward dw1"));
+    if (sw) MOE_TRY(wgrad_big(g->dw3, db, h, xs, d, "backward dw3"));
+    MOE_TRY(wgrad_big(g->dw2, dys, d, hid, h, "backward dw2"));
+  } else {
+    MOE_TRY(wgrad(g->dw1, op_cols(dp, h, f32), op_cols(xs, d, f32), h, d, "backward dw1"));
+    if (sw)
+      MOE_TRY(wgrad(g->dw3, op_cols(db, h, f32), op_cols(xs, d, f32), h, d, "backward dw3"));
+    MOE_TRY(wgrad(g->dw2, op_cols(dys, d, f32), op_cols(hid, h, f32), d, h, "backward dw2"));
+  }
   // 6. dx
   if (T > 0)
     MOE_TRY(hip_status(launch_bw_assemble_dx(dxg, dxs, sv->inv, T, k, d, bf16, g->dx, s),

@@ -48,6 +48,11 @@ struct GemmArgs {
   // added, K running over A, B first and then A2, B2
   const bf16_t* A2 = nullptr;
   const bf16_t* B2 = nullptr;
+  // per-expert table gradients (large tiles, WGT): C_e [M][N] = sum over
+  // the positions p of expert e of A[p][m] B[p][n]; positions past an
+  // expert's rows read the zero row (at least max(M, N) zeros)
+  int M = 0, mtiles = 0;
+  const bf16_t* zero = nullptr;
 };
 
 // Expert owning tile q: the largest e with tiles[e] <= q (tiles non-decreasing).
@@ -232,11 +237,12 @@ __device__ __forceinline__ v4i16_t gb_read_tr(const bf16_t* T, int row, int n) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(T + slot * 8 + (n & 7)));
 }
 
-template <int EPI, bool TBB>
+template <int EPI, bool TBB, bool WGT>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   constexpr bool SW = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD);
   constexpr bool BWD = (EPI == EPI_RELU_BWD || EPI == EPI_SWIGLU_BWD);
   static_assert(!TBB || EPI == EPI_NONE, "weights stored [K][N] only for plain products");
+  static_assert(!WGT || TBB, "table gradients read both operands as [K][rows]");
   constexpr int BN = gb_bn<EPI>();
   constexpr int NBJ = BN / 64;   // 1 KB weight blocks each wave loads per slice
   constexpr int WN = BN / 4;     // columns per wave
@@ -246,11 +252,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   bf16_t* As = smem;               // [2][AT]
   bf16_t* Bs = As + 2 * AT;        // [2][BT]
   bf16_t* B3s = Bs + 2 * BT;       // [2][BT], SwiGLU only
-  __shared__ int s_e, s_row0, s_m, s_ct;
+  __shared__ int s_e, s_row0, s_m, s_ct, s_k0, s_kn;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) {
-    const int Q = g.tiles[g.E];
+    // row tiles: of the routed rows (tile map), or WGT: mtiles output row
+    // tiles per expert
+    const int Q = WGT ? g.E * g.mtiles : g.tiles[g.E];
     const int per_win = GB_WIN * g.ncol;
     const int win = blockIdx.x / per_win, within = blockIdx.x % per_win;
     // workgroups go to the XCDs round robin: with at least 32 column tiles,
@@ -266,11 +274,22 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     }
     const int q = win * GB_WIN + qw;
     if (q < Q) {
-      const int e = expert_of_tile(g.tiles, g.E, q);
-      const int row0 = g.offsets[e] + (q - g.tiles[e]) * GB_BM;
-      s_e = e;
-      s_row0 = row0;
-      s_m = min(GB_BM, g.offsets[e + 1] - row0);
+      if constexpr (WGT) {
+        const int e = q / g.mtiles, mt = q % g.mtiles;
+        s_e = e;
+        s_row0 = mt * GB_BM;
+        s_m = min(GB_BM, g.M - mt * GB_BM);
+        s_k0 = g.offsets[e];
+        s_kn = g.offsets[e + 1] - g.offsets[e];
+      } else {
+        const int e = expert_of_tile(g.tiles, g.E, q);
+        const int row0 = g.offsets[e] + (q - g.tiles[e]) * GB_BM;
+        s_e = e;
+        s_row0 = row0;
+        s_m = min(GB_BM, g.offsets[e + 1] - row0);
+        s_k0 = 0;
+        s_kn = g.K;
+      }
       s_ct = ct;
     } else {
       s_e = -1;
@@ -282,6 +301,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   const int row0 = __builtin_amdgcn_readfirstlane(s_row0);
   const int m = __builtin_amdgcn_readfirstlane(s_m);
   const int n0 = __builtin_amdgcn_readfirstlane(s_ct) * BN;
+  const int kstart = __builtin_amdgcn_readfirstlane(s_k0);
+  const int kn = __builtin_amdgcn_readfirstlane(s_kn);
 
   // Direct loads: wave w fills 1 KB blocks w*4 + j (A, j < 4) and
   // w*NBJ + j (B, B3, j < NBJ); lane l of block b fills slot 64b + l.
@@ -294,14 +315,25 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   // (arrays of a fixed size: the lambdas below capture them, and the host
   // pass of the compiler drops the kernel when a captured array's bound
   // depends on the template argument; unused entries are optimised out)
+  //   WGT: both tiles are [k][rows] like the TBB weight tile; the k row of
+  //   each load (ar, br) decides between the position's row and the zero row.
   int64_t aoff[4], boff[4];
+  int ar[4], br[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = (w * 4 + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int p = row0 + min(r, m - 1);
-    const int64_t src = g.perm ? (int64_t)(g.perm[p] / g.k) : (int64_t)p;
-    aoff[j] = src * g.lda + c * 8;
+    if constexpr (WGT) {
+      const int r = 2 * (w * 4 + j) + (lane >> 5);
+      const int c = (lane & 31) ^ (2 * (r & 3));
+      ar[j] = r;
+      aoff[j] = min(row0 + 8 * c, g.M - 8);
+    } else {
+      const int r = (w * 4 + j) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int p = row0 + min(r, m - 1);
+      const int64_t src = g.perm ? (int64_t)(g.perm[p] / g.k) : (int64_t)p;
+      ar[j] = 0;
+      aoff[j] = src * g.lda + c * 8;
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -309,17 +341,37 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
       const int r = 2 * (w * NBJ + (j < NBJ ? j : 0)) + (lane >> 5);
       const int c = (lane & 31) ^ (2 * (r & 3));
       const int n = min(n0 + 8 * c, g.N - 8);
-      boff[j] = (int64_t)e * g.N * g.K + (int64_t)r * g.N + n;
+      br[j] = r;
+      boff[j] = WGT ? (int64_t)n : (int64_t)e * g.N * g.K + (int64_t)r * g.N + n;
     } else {
+      br[j] = 0;
       const int r = (w * NBJ + (j < NBJ ? j : 0)) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int n = min(n0 + r, g.N - 1);
       boff[j] = ((int64_t)e * g.N + n) * g.K + c * 8;
     }
   }
-  const int nk = g.K / GB_BK;
+  const int nk = WGT ? (kn + GB_BK - 1) / GB_BK : g.K / GB_BK;
   // slice kt of the K loop: the first pair's slices, then the second's
   auto dma = [&](int kt, int buf) {
+    if constexpr (WGT) {
+      const int k0 = kt * GB_BK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = k0 + ar[j];
+        const bf16_t* src =
+            kk < kn ? g.A + (int64_t)(kstart + kk) * g.lda + aoff[j] : g.zero + aoff[j];
+        __builtin_amdgcn_global_load_lds(src, As + buf * AT + (w * 4 + j) * 512, 16, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < NBJ; ++j) {
+        const int kk = k0 + br[j];
+        const bf16_t* src =
+            kk < kn ? g.B + (int64_t)(kstart + kk) * g.N + boff[j] : g.zero + boff[j];
+        __builtin_amdgcn_global_load_lds(src, Bs + buf * BT + (w * NBJ + j) * 512, 16, 0, 0);
+      }
+      return;
+    }
     const bool second = kt >= nk;
     const int k0 = (second ? kt - nk : kt) * GB_BK;
     const bf16_t* Ab = second ? g.A2 : g.A;
@@ -355,7 +407,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   }
 
   const int nkt = (g.A2 ? 2 : 1) * nk;
-  dma(0, 0);
+  if (nkt > 0) dma(0, 0);  // (an expert without rows: zero gradients)
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
@@ -373,8 +425,20 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
       auto frags = [&](int st, int sl) {
         const int c = 2 * st + fh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[sl][i] = *reinterpret_cast<const bf16x8*>(Ab + gb_slot(wm * 128 + i * 32 + fr, c));
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (WGT) {
+            // row wm*128 + 32i + lane % 32, k = 16 st + 8 (lane / 32) + 0..7
+            const int G = lane >> 4, jj = lane & 15;
+            const int mb = wm * 128 + i * 32 + 16 * (G & 1) + 4 * (jj & 3);
+            const int kb = st * 16 + 8 * (G >> 1) + (jj >> 2);
+            const v4i16_t lo = gb_read_tr<GB_BM>(Ab, kb, mb);
+            const v4i16_t hi = gb_read_tr<GB_BM>(Ab, kb + 4, mb);
+            af[sl][i] = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+            af[sl][i] = *reinterpret_cast<const bf16x8*>(Ab + gb_slot(wm * 128 + i * 32 + fr, c));
+          }
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           if constexpr (TBB) {
@@ -421,7 +485,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i) {
     const int row = wm * 128 + 32 * i + fr;
     if (row >= m) continue;
-    const int64_t roff = (int64_t)(row0 + row) * g.ldc;
+    const int64_t roff = (WGT ? (int64_t)e * g.M * g.N : 0) + (int64_t)(row0 + row) * g.ldc;
     bf16_t* crow = g.C + roff;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -560,19 +624,19 @@ int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E) {
   return big_tiles(A, E) ? GB_BM : GM_BM;
 }
 
-template <int EPI, bool TBB = false>
+template <int EPI, bool TBB = false, bool WGT = false>
 static hipError_t launch_big(const GemmArgs& g, int64_t qmax, hipStream_t s) {
   constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD;
   constexpr size_t lds = sizeof(bf16_t) * (size_t)GB_BK * 2 * (GB_BM + gb_bn<EPI>() * (SW ? 2 : 1));
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI, TBB>,
+    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_big_kernel<EPI, TBB, WGT>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     attr_done = true;
   }
   const int64_t wins = (qmax + GB_WIN - 1) / GB_WIN;
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<EPI, TBB>),
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<EPI, TBB, WGT>),
                      dim3((unsigned)(wins * GB_WIN * g.ncol)), dim3(512), lds, s, g);
   return hipGetLastError();
 }
@@ -691,6 +755,33 @@ hipError_t launch_bw_big_product(const BwBigProduct& p, hipStream_t s) {
   g.B2 = (const bf16_t*)p.b2;
   const int64_t qmax = (p.A + GB_BM - 1) / GB_BM + p.E;
   return launch_big<EPI_NONE, true>(g, qmax, s);
+}
+
+// Per-expert table gradients on the large tiles: c_e [M][N] = a_e^T b_e
+// over the positions of expert e (a [A][M], b [A][N] bf16 in expert order,
+// c [E][M][N] bf16); zero: max(M, N) bf16 zeros.
+hipError_t launch_bw_big_wgrad(const BwBigWgrad& p, hipStream_t s) {
+  if (p.E == 0) return hipSuccess;
+  if (p.M % 8 != 0 || p.N % 8 != 0) return hipErrorInvalidValue;
+  GemmArgs g;
+  g.A = (const bf16_t*)p.a;
+  g.lda = p.M;
+  g.perm = nullptr;
+  g.k = 1;
+  g.B = (const bf16_t*)p.b;
+  g.B3 = nullptr;
+  g.N = p.N;
+  g.K = 0;
+  g.offsets = p.offsets;
+  g.tiles = nullptr;
+  g.E = p.E;
+  g.C = (bf16_t*)p.c;
+  g.ldc = p.N;
+  g.ncol = (p.N + gb_bn<EPI_NONE>() - 1) / gb_bn<EPI_NONE>();
+  g.M = p.M;
+  g.mtiles = (p.M + GB_BM - 1) / GB_BM;
+  g.zero = (const bf16_t*)p.zero;
+  return launch_big<EPI_NONE, true, true>(g, (int64_t)p.E * g.mtiles, s);
 }
 
 }  // namespace moe

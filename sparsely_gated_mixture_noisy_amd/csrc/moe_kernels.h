@@ -171,6 +171,19 @@ struct BwBigProduct {
   void* c;
 };
 hipError_t launch_bw_big_product(const BwBigProduct& p, hipStream_t s);
+// c_e [M][N] = sum over the positions p of expert e of a[p][m] b[p][n], on
+// the same large tiles; a [A][M], b [A][N] bf16 in expert order, c [E][M][N]
+// bf16 (zero for an expert without rows); zero: max(M, N) bf16 zeros;
+// M, N % 8 == 0
+struct BwBigWgrad {
+  const void* a;
+  const void* b;
+  int E, M, N;
+  const int32_t* offsets;  // [E+1]
+  const void* zero;
+  void* c;
+};
+hipError_t launch_bw_big_wgrad(const BwBigWgrad& p, hipStream_t s);
 
 // -------------------------------------------------------- combine / stats --
 hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float* gate, int64_t T,

@@ -127,6 +127,10 @@ CASES = {
                                                    d_hidden=320), 0.8, 0.0),
     "bf16_big_swiglu_h4096": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=64,
                                                          d_hidden=4096), 0.8, 0.0),
+    # large-tile path with a Zipf bias: an idle expert (zero table gradients),
+    # experts with 1 to 4 rows (mostly zero-row positions) and one of 2342 rows
+    "bf16_big_zipf_idle": (CONFIGS["zipf2048"].replace(tokens=3100, n_experts=12, d_model=64,
+                                                       d_hidden=128, top_k=1), 0.5, 0.5),
     # one group, then one expert: both softmax levels are a single weight of 1
     "bf16_hier_k1": (CONFIGS["hier4096"].replace(tokens=200, n_experts=64, d_model=128,
                                                  d_hidden=256, k_groups=1, k_per_group=1,
