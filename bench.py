@@ -38,7 +38,7 @@ EXPERT_TRAFFIC = {
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "9ca5962de6cbb84e10e03da2cc1f22b88d293cc833697d1eda0191c8ec21318e",
+    "sources_sha256": "38da87ab8136fd85fe4fb4013550a2c17b2ea3708ae913ea3753e4a59ae58eb7",
     "fetch_kib": 288889.8, "fetch_scale": 524288.0 / 262156.0,
     "write_kib": 32768.1, "write_scale": 524288.0 / 524288.0,
 }
