@@ -51,7 +51,10 @@ struct GemmArgs {
   // per-expert table gradients (large tiles, WGT): C_e [M][N] = sum over
   // the positions p of expert e of A[p][m] B[p][n]; positions past an
   // expert's rows read the zero row (at least max(M, N) zeros)
-  int M = 0, mtiles = 0;
+  // The tile enumeration runs over wrows row tiles per expert against ncol
+  // column tiles; with wswap its rows are the output's column tiles and its
+  // columns the output's row tiles
+  int M = 0, wrows = 0, wswap = 0;
   const bf16_t* zero = nullptr;
 };
 
@@ -256,9 +259,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) {
-    // row tiles: of the routed rows (tile map), or WGT: mtiles output row
-    // tiles per expert
-    const int Q = WGT ? g.E * g.mtiles : g.tiles[g.E];
+    // row tiles: of the routed rows (tile map), or WGT: wrows per expert
+    const int Q = WGT ? g.E * g.wrows : g.tiles[g.E];
     const int per_win = GB_WIN * g.ncol;
     const int win = blockIdx.x / per_win, within = blockIdx.x % per_win;
     // workgroups go to the XCDs round robin: with at least 32 column tiles,
@@ -275,12 +277,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
     const int q = win * GB_WIN + qw;
     if (q < Q) {
       if constexpr (WGT) {
-        const int e = q / g.mtiles, mt = q % g.mtiles;
+        const int e = q / g.wrows, r = q % g.wrows;
+        const int mt = g.wswap ? ct : r;
         s_e = e;
         s_row0 = mt * GB_BM;
         s_m = min(GB_BM, g.M - mt * GB_BM);
         s_k0 = g.offsets[e];
         s_kn = g.offsets[e + 1] - g.offsets[e];
+        s_ct = g.wswap ? r : ct;
       } else {
         const int e = expert_of_tile(g.tiles, g.E, q);
         const int row0 = g.offsets[e] + (q - g.tiles[e]) * GB_BM;
@@ -289,8 +293,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmArgs g) {
         s_m = min(GB_BM, g.offsets[e + 1] - row0);
         s_k0 = 0;
         s_kn = g.K;
+        s_ct = ct;
       }
-      s_ct = ct;
     } else {
       s_e = -1;
     }
@@ -777,11 +781,17 @@ hipError_t launch_bw_big_wgrad(const BwBigWgrad& p, hipStream_t s) {
   g.E = p.E;
   g.C = (bf16_t*)p.c;
   g.ldc = p.N;
-  g.ncol = (p.N + gb_bn<EPI_NONE>() - 1) / gb_bn<EPI_NONE>();
+  // an expert's output tiles in the enumeration: its row tiles against its
+  // column tiles, or the other way round when only the row tiles are enough
+  // for the XCD-grouped order
+  const int mt = (p.M + GB_BM - 1) / GB_BM;
+  const int nt = (p.N + gb_bn<EPI_NONE>() - 1) / gb_bn<EPI_NONE>();
+  g.wswap = nt < 32 && mt >= 32 && mt % 8 == 0;
+  g.wrows = g.wswap ? nt : mt;
+  g.ncol = g.wswap ? mt : nt;
   g.M = p.M;
-  g.mtiles = (p.M + GB_BM - 1) / GB_BM;
   g.zero = (const bf16_t*)p.zero;
-  return launch_big<EPI_NONE, true, true>(g, (int64_t)p.E * g.mtiles, s);
+  return launch_big<EPI_NONE, true, true>(g, (int64_t)p.E * g.wrows, s);
 }
 
 }  // namespace moe

@@ -118,15 +118,15 @@ CASES = {
                                               d_hidden=256), 0.8, 1.0),
     "bf16_hier_capacity10": (CONFIGS["hier4096"].replace(tokens=400, n_experts=64, d_model=128,
                                                          d_hidden=256, capacity=10), 0.8, 0.0),
-    # experts with >= 256 rows on average: dHid on the product kernel, the
-    # hidden layer on the large-tile GEMM (ragged last column tiles; 32
-    # column tiles, the XCD-grouped order, in the last case)
+    # experts with >= 256 rows on average: the large-tile products (ragged
+    # last column tiles; at h = 8192 the XCD-grouped order for the hidden
+    # layer, dHid and dW2, and the swapped enumeration for dW1 and dW3)
     "bf16_big_relu": (CONFIGS["flat256"].replace(tokens=700, n_experts=4, d_model=256,
                                                  d_hidden=640, top_k=2), 0.8, 1.0),
     "bf16_big_swiglu": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=256,
                                                    d_hidden=320), 0.8, 0.0),
-    "bf16_big_swiglu_h4096": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=64,
-                                                         d_hidden=4096), 0.8, 0.0),
+    "bf16_big_swiglu_h8192": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=64,
+                                                         d_hidden=8192), 0.8, 0.0),
     # large-tile path with a Zipf bias: an idle expert (zero table gradients),
     # experts with 1 to 4 rows (mostly zero-row positions) and one of 2342 rows
     "bf16_big_zipf_idle": (CONFIGS["zipf2048"].replace(tokens=3100, n_experts=12, d_model=64,
