@@ -38,7 +38,7 @@ EXPERT_TRAFFIC = {
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "38da87ab8136fd85fe4fb4013550a2c17b2ea3708ae913ea3753e4a59ae58eb7",
+    "sources_sha256": "1ee1d350a9722fe32f56ac838d7393f4ade3de915d6ca2e4a027bb0de3b341e5",
     "fetch_kib": 288889.8, "fetch_scale": 524288.0 / 262156.0,
     "write_kib": 32768.1, "write_scale": 524288.0 / 524288.0,
 }

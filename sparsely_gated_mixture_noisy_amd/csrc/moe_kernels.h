@@ -329,7 +329,9 @@ struct BwOp {
   int lo = 0;                   // bf16 products: the residual v - bf16(v) of each value
 };
 enum { BW_POS = 0, BW_WGT = 1, BW_PLAIN = 2 };
-enum { BW_EPI_NONE = 0, BW_EPI_RELU = 1, BW_EPI_SWIGLU = 2 };
+// BW_EPI_RELU_IN (one product, X W1^T): C2 holds dHid on entry and gets
+// dP = dHid * (a > 0), C gets relu(a)
+enum { BW_EPI_NONE = 0, BW_EPI_RELU = 1, BW_EPI_SWIGLU = 2, BW_EPI_RELU_IN = 3 };
 struct BwGemm {
   int mode = BW_PLAIN;
   int epi = BW_EPI_NONE;
