@@ -216,6 +216,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 //     shared by the XCD's 32 CUs.  Otherwise consecutive workgroups take the
 //     window's row tiles against one column tile, then the next (with fewer
 //     column tiles an XCD's CUs would hold tiles of several windows).
+// The same kernel serves the backward of such layers (template arguments):
+//   * EPI_RELU_BWD / EPI_SWIGLU_BWD: the first GEMM's products with an
+//     epilogue that reads dHid and writes the recomputed hidden activations
+//     and the pre-activation gradients.
+//   * TBB: weights stored [K][N] (W2 for dHid = dY W2, W1 and W3 for dX),
+//     brought into LDS as stored and read into MFMA fragments by the
+//     transposing LDS read; A2, B2 add a second operand pair along K.
+//   * WGT: per-expert table gradients, both operands [positions][columns]
+//     through the transposing read, K over the expert's positions, rows past
+//     them read from a zero row.
 // ---------------------------------------------------------------------------
 constexpr int GB_BM = 256, GB_BK = 64, GB_WIN = 8;
 // column tile: 128 with the SwiGLU epilogue (two accumulator sets), 256
