@@ -127,6 +127,9 @@ CASES = {
                                                    d_hidden=320), 0.8, 0.0),
     "bf16_big_swiglu_h8192": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=64,
                                                          d_hidden=8192), 0.8, 0.0),
+    # the large-tile backward on capped experts (about 300 rows each, 200 kept)
+    "bf16_big_swiglu_cap200": (CONFIGS["mixtral"].replace(tokens=600, n_experts=4, d_model=256,
+                                                          d_hidden=320, capacity=200), 0.8, 0.0),
     # large-tile path with a Zipf bias: an idle expert (zero table gradients),
     # experts with 1 to 4 rows (mostly zero-row positions) and one of 2342 rows
     "bf16_big_zipf_idle": (CONFIGS["zipf2048"].replace(tokens=3100, n_experts=12, d_model=64,

@@ -37,6 +37,9 @@ CASES = {
     "zipf_t500_cap3": CONFIGS["zipf2048"].replace(tokens=500, capacity=3),
     "hier_t300_cap1": CONFIGS["hier4096"].replace(tokens=300, capacity=1),
     "swiglu_cap30": CONFIGS["mixtral"].replace(tokens=200, d_model=512, d_hidden=1536, capacity=30),
+    # the large-tile GEMMs on capped experts (about 600 routed rows each, 400 kept)
+    "big_swiglu_cap400": CONFIGS["mixtral"].replace(tokens=1200, d_model=512, d_hidden=1536,
+                                                    n_experts=4, capacity=400),
     "cap_above_every_count": CONFIGS["flat256"].replace(tokens=300, capacity=10 ** 6),
 }
 
