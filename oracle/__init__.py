@@ -9,7 +9,7 @@ from .moe_oracle import (cv_squared, combine, dense_forward, dense_gates,  # noq
                          expert_relu, expert_swiglu, flat_gate, forward, gate,
                          hier_gate, importance, keep_top_k, kept_softmax,
                          load_estimate, noisy_logits, normal_cdf, route,
-                         run_experts, silu, softplus, token_outputs,
+                         run_experts, silu, softplus,
                          balance_stats, backward, cv_squared_grad, rank_experts,
                          expert_relu_backward, expert_swiglu_backward, normal_pdf,
                          sigmoid, philox4x32_10, uniform23, philox_normals, draw_noise)

@@ -409,27 +409,6 @@ def forward(inp: Dict, cfg, w_importance=1.0, w_load=1.0,
     return out
 
 
-def token_outputs(inp: Dict, cfg, tokens, idx, gates) -> np.ndarray:
-    """y for a subset of tokens, given that token's selection and gates:
-    y_t = sum_s gates[t,s] * E_{idx[t,s]}(x_t).  Used to check sampled rows of
-    large layers one by one."""
-    x = _f64(inp["x"])
-    out = []
-    for t in tokens:
-        acc = 0.0
-        for s in range(idx.shape[1]):
-            e = int(idx[t, s])
-            w1 = _f64(inp["w1"][e])
-            w2 = _f64(inp["w2"][e])
-            if inp.get("w3") is not None:
-                ye = expert_swiglu(x[t:t + 1], w1, _f64(inp["w3"][e]), w2)
-            else:
-                ye = expert_relu(x[t:t + 1], w1, w2)
-            acc = acc + gates[t, s] * ye[0]
-        out.append(acc)
-    return np.array(out)
-
-
 def dense_forward(inp: Dict, cfg) -> np.ndarray:
     """Brute force: evaluate every expert on every token and sum with the dense
     gate vector, y_t = sum over all e of G(x_t)_e E_e(x_t).  Tiny inputs only.

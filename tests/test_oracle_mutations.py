@@ -351,6 +351,33 @@ def hier_backward_primary_level_dropped(inp, cfg, x, g, dgate):
     return res
 
 
+def noise_primary_on_stream_zero(cfg, seed):
+    """The primary noise drawn on the secondary stream (counter word 3 = 0)."""
+    d = _orig["draw_noise"](cfg, seed)
+    if cfg.n_groups:
+        d["eps_p"] = om.philox_normals(np.arange(cfg.tokens), cfg.n_groups, seed, 0, 0)
+    return d
+
+
+def noise_flat_rows_from_one(cfg, seed):
+    """Token t's flat noise row read at counter row t + 1."""
+    d = _orig["draw_noise"](cfg, seed)
+    if not cfg.n_groups:
+        d["eps"] = om.philox_normals(np.arange(1, cfg.tokens + 1), cfg.n_experts, seed, 0, 0)
+    return d
+
+
+def noise_group_in_stream_word(cfg, seed):
+    """The secondary noise of group g with g in the stream word, not the group word."""
+    d = _orig["draw_noise"](cfg, seed)
+    if cfg.n_groups:
+        Eg = cfg.n_experts // cfg.n_groups
+        rows = np.arange(cfg.tokens)
+        d["eps"] = np.stack([om.philox_normals(rows, Eg, seed, 0, g) for g in
+                             range(cfg.n_groups)], axis=1)
+    return d
+
+
 # (function patched, mistake, pins that must reject it)
 MUTATIONS = [
     ("noisy_logits", noise_term_dropped, ["test_noisy_logits_hand_example"]),
@@ -403,6 +430,9 @@ MUTATIONS = [
     ("philox4x32_10", philox_words_of_product_swapped, ["test_philox_known_answers"]),
     ("uniform23", uniform_from_24_bits, ["test_uniform23_range_and_exactness"]),
     ("philox_normals", normals_sin_and_cos_swapped, ["test_normals_follow_the_counter_layout"]),
+    ("draw_noise", noise_primary_on_stream_zero, ["test_draw_noise_counter_layout"]),
+    ("draw_noise", noise_flat_rows_from_one, ["test_draw_noise_counter_layout"]),
+    ("draw_noise", noise_group_in_stream_word, ["test_draw_noise_counter_layout"]),
     # backward
     ("cv_squared_grad", cv2_grad_without_mean_term, ["test_cv_squared_gradient_closed_forms",
                                                      "test_gradients_match_central_differences"]),

@@ -65,10 +65,42 @@ def test_normals_follow_the_counter_layout():
         assert not np.allclose(other, base)
 
 
-def test_draw_noise_shapes():
-    flat = oracle.draw_noise(CONFIGS["tiny"].replace(tokens=10), seed=3)
-    assert flat["eps"].shape == (10, 8) and flat["eps_p"] is None
-    hc = CONFIGS["hier4096"].replace(tokens=6, n_experts=32, n_groups=4)
-    h = oracle.draw_noise(hc, seed=3)
-    assert h["eps"].shape == (6, 4, 8) and h["eps_p"].shape == (6, 4)
-    assert np.allclose(h["eps"][:, 2, :], oracle.philox_normals(np.arange(6), 8, 3, sub=2))
+def _element(seed, ctr):
+    """The four normals of one Philox counter, written out from the
+    documented mapping: words (0, 1) give elements 0 and 1 (cos and sin of
+    one Box-Muller pair), words (2, 3) give elements 2 and 3, each word
+    mapped to (top 23 bits + 1/2) / 2^23."""
+    w = oracle.philox4x32_10(np.array(ctr, dtype=np.uint64),
+                             np.array([seed & 0xFFFFFFFF, seed >> 32], dtype=np.uint64))
+    u = [((int(v) >> 9) + 0.5) / 8388608.0 for v in w]
+    out = []
+    for a, b in ((u[0], u[1]), (u[2], u[3])):
+        r = math.sqrt(-2.0 * math.log(a))
+        out += [r * math.cos(2.0 * math.pi * b), r * math.sin(2.0 * math.pi * b)]
+    return out
+
+
+def test_draw_noise_counter_layout():
+    """Every element of a layer's noise against Philox computed at the
+    documented counter: flat element j of token t at (j // 4, t, 0, 0); the
+    hierarchy's secondary element j of group g at (j // 4, t, g, 0) and its
+    primary element g at (g // 4, t, 0, 1).  The rows are ragged (6 and 10
+    elements, not multiples of 4), the seed uses both key words."""
+    seed = (0x1234 << 32) | 0xABCDEF
+    flat = oracle.draw_noise(CONFIGS["tiny"].replace(tokens=3, n_experts=10, top_k=2), seed)
+    assert flat["eps"].shape == (3, 10) and flat["eps_p"] is None
+    for t in range(3):
+        for j in range(10):
+            want = _element(seed, [j // 4, t, 0, 0])[j % 4]
+            assert abs(flat["eps"][t, j] - want) < 1e-12, (t, j)
+    hc = CONFIGS["hier4096"].replace(tokens=3, n_experts=18, n_groups=3, k_groups=2,
+                                     k_per_group=2, top_k=4)
+    h = oracle.draw_noise(hc, seed)
+    assert h["eps"].shape == (3, 3, 6) and h["eps_p"].shape == (3, 3)
+    for t in range(3):
+        for g in range(3):
+            want = _element(seed, [g // 4, t, 0, 1])[g % 4]
+            assert abs(h["eps_p"][t, g] - want) < 1e-12, (t, g)
+            for j in range(6):
+                want = _element(seed, [j // 4, t, g, 0])[j % 4]
+                assert abs(h["eps"][t, g, j] - want) < 1e-12, (t, g, j)
