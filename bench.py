@@ -350,15 +350,11 @@ def main():
     cfg = CONFIGS[args.config]
     print(f"[bench] {describe(cfg)}", file=sys.stderr, flush=True)
     inp = make_inputs(cfg, seed=0, device="cuda")
-    # expert tables repacked once into the expert kernel's stream order (a
-    # parameter transform, outside the timed region), when the layer has one
-    packed = L.pack_experts(cfg, inp)
-    if packed is not None:
-        inp = dict(inp, w_packed=packed)
-    # likewise the gate tables into the gate kernels' stream order
-    gpacked = L.pack_gate(cfg, inp)
-    if gpacked is not None:
-        inp = dict(inp, w_gate_packed=gpacked)
+    # expert and gate tables repacked once into the kernels' stream order (a
+    # parameter transform, outside the timed region), when the layer has them
+    inp = L.packed_params(cfg, inp)
+    packed = inp.get("w_packed")
+    gpacked = inp.get("w_gate_packed")
     torch.cuda.synchronize()
     fwd = L.Forward(cfg, inp["x"], inp, inp, balance=True)
     for _ in range(args.warmup):

@@ -163,7 +163,10 @@ size_t moe_workspace_size(const moe_config* cfg);
  * Ties between equal scores go to the lower expert index.  The hierarchy
  * keeps k_groups groups by the primary scores, then k_per_group experts in
  * each kept group; a gate is the product of the primary and secondary
- * softmax weights. */
+ * softmax weights.  A NaN score (from a NaN in x or the tables) ranks as
+ * -inf, so every row keeps k experts in [0, E); its gates are then NaN.
+ * noise must be non-NULL when cfg->noisy (MOE_ERR_INVALID_ARG otherwise,
+ * whatever the token count). */
 moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
                     const moe_noise* noise, int32_t* topk_idx, float* topk_gate,
                     float* thr, void* ws, size_t ws_bytes, void* stream);
@@ -180,8 +183,9 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const moe_params* p,
  *   x, x_sorted  nullable pair: when both are given, x_sorted[p] = x[perm[p]/k]
  * With cfg->capacity > 0: counts and offsets count the kept rows only,
  * inv[a] = -1 for a dropped assignment, and perm[p] = 0 for the positions
- * p >= offsets[E] that no kept assignment takes.
- * Out-of-range expert ids in topk_idx are undefined behaviour. */
+ * p >= offsets[E] that no kept assignment takes.  An expert id outside
+ * [0, E) in topk_idx is dropped the same way: it takes no row, its inv is -1
+ * and it adds nothing downstream. */
 moe_status moe_route(const moe_config* cfg, const int32_t* topk_idx,
                      int32_t* counts, int32_t* offsets, int32_t* perm,
                      int32_t* inv, const void* x, void* x_sorted, void* ws,

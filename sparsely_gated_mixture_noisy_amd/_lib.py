@@ -228,6 +228,21 @@ def pack_gate(cfg: MoEConfig, params) -> Optional[torch.Tensor]:
     return out
 
 
+def packed_params(cfg: MoEConfig, params):
+    """params plus the packed expert and gate tables when the layer has them
+    (w_packed, w_gate_packed): the form moe_forward reads them in at full
+    speed.  The plain tables stay in the dict for the entry points that read
+    them (the backward pass)."""
+    out = dict(params)
+    packed = pack_experts(cfg, params)
+    if packed is not None:
+        out["w_packed"] = packed
+    gpacked = pack_gate(cfg, params)
+    if gpacked is not None:
+        out["w_gate_packed"] = gpacked
+    return out
+
+
 def workspace_size(cfg: MoEConfig, tokens: Optional[int] = None) -> int:
     c = make_config(cfg, tokens)
     return int(load().moe_workspace_size(ctypes.byref(c)))

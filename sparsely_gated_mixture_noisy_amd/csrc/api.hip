@@ -183,6 +183,7 @@ moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_param
   // an empty batch reads no activations and no noise
   const bool rows = c->tokens > 0;
   if (c->noisy) {
+    if (!n) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs a moe_noise (noise is NULL)");
     if (rows && !has_noise(n, n ? n->eps : nullptr))
       return fail(MOE_ERR_INVALID_ARG, "noisy gate needs eps (or noise drawn in the kernels)");
     if (!p->w_noise) return fail(MOE_ERR_INVALID_ARG, "noisy gate needs w_noise");
@@ -196,7 +197,7 @@ moe_status check_gate_inputs(const moe_config* c, const void* x, const moe_param
   if (c->n_groups > 0) {
     if (!p->w_gate_p) return fail(MOE_ERR_INVALID_ARG, "hierarchy needs w_gate_p");
     if (p->bias) return fail(MOE_ERR_UNSUPPORTED, "bias is supported by the flat gate only");
-    if (c->noisy && ((rows && !has_noise(n, n->eps_p)) || !p->w_noise_p))
+    if (c->noisy && ((rows && !has_noise(n, n ? n->eps_p : nullptr)) || !p->w_noise_p))
       return fail(MOE_ERR_INVALID_ARG, "noisy hierarchy needs eps_p and w_noise_p");
   }
   return MOE_OK;
@@ -246,7 +247,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
     a.w_gate = p->w_gate;
     a.w_noise = noisy ? p->w_noise : nullptr;
     a.bias = p->bias;
-    a.noise = noisy ? noise_src(n, n->eps, 0) : NoiseSrc();
+    a.noise = noisy ? noise_src(n, n ? n->eps : nullptr, 0) : NoiseSrc();
     a.T = c->tokens;
     a.d = c->d_model;
     a.E = c->n_experts;
@@ -269,7 +270,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   a.w_gate = p->w_gate_p;
   a.w_noise = noisy ? p->w_noise_p : nullptr;
   a.bias = nullptr;
-  a.noise = noisy ? noise_src(n, n->eps_p, 1) : NoiseSrc();
+  a.noise = noisy ? noise_src(n, n ? n->eps_p : nullptr, 1) : NoiseSrc();
   a.T = c->tokens;
   a.d = c->d_model;
   a.E = G;
@@ -303,7 +304,7 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   ga.x = x;
   ga.w_gate = p->w_gate;
   ga.w_noise = noisy ? p->w_noise : nullptr;
-  ga.noise = noisy ? noise_src(n, n->eps, 0) : NoiseSrc();
+  ga.noise = noisy ? noise_src(n, n ? n->eps : nullptr, 0) : NoiseSrc();
   ga.d = c->d_model;
   ga.G = G;
   ga.Eg = c->n_experts / G;
@@ -662,8 +663,8 @@ moe_status hier_gate_backward(const moe_config* c, const BwLayout& L, const void
     a.w_noise = noisy ? p->w_noise : nullptr;
     a.w_gate_p = p->w_gate_p;
     a.w_noise_p = noisy ? p->w_noise_p : nullptr;
-    a.noise = noisy ? noise_src(n, n->eps, 0) : NoiseSrc();
-    a.noise_p = noisy ? noise_src(n, n->eps_p, 1) : NoiseSrc();
+    a.noise = noisy ? noise_src(n, n ? n->eps : nullptr, 0) : NoiseSrc();
+    a.noise_p = noisy ? noise_src(n, n ? n->eps_p : nullptr, 1) : NoiseSrc();
     a.T = T;
     a.k = k;
     a.d = d;
@@ -758,7 +759,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   ga.w_gate = p->w_gate;
   ga.w_noise = noisy ? p->w_noise : nullptr;
   ga.bias = p->bias;
-  ga.noise = noisy && n ? noise_src(n, n->eps, 0) : NoiseSrc();
+  ga.noise = noisy && n ? noise_src(n, n ? n->eps : nullptr, 0) : NoiseSrc();
   ga.w_pack = p->w_gate_packed;
   ga.pack_nt = gate_pack_tables(c);
   ga.idx = sv->topk_idx;
@@ -1171,14 +1172,23 @@ moe_status moe_balance_loss(const moe_config* cfg, const void* x, const moe_para
   return ok();
 }
 
-moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p,
-                       const moe_noise* noise, float w_importance, float w_load, moe_outputs* out,
-                       void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status check_forward_args(const moe_config* cfg, const void* x, const moe_params* p,
+                              const moe_noise* noise, const moe_outputs* out) {
   MOE_TRY(check_config(cfg));
   MOE_TRY(check_gate_inputs(cfg, x, p, noise));
   MOE_TRY(check_expert_inputs(cfg, p));
   if (!out || (!out->y && cfg->tokens > 0)) return fail(MOE_ERR_INVALID_ARG, "out / out->y is NULL");
-  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  return MOE_OK;
+}
+
+// The layer on a validated call, with its scratch at ws (layout(cfg) bytes).
+moe_status forward_on(const moe_config* cfg, const void* x, const moe_params* p,
+                      const moe_noise* noise, float w_importance, float w_load,
+                      moe_outputs* out, void* ws, void* stream) {
   const Layout L = layout(cfg);
   hipStream_t s = (hipStream_t)stream;
   int32_t* idx = out->topk_idx ? out->topk_idx : at<int32_t>(ws, L.idx);
@@ -1239,6 +1249,18 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
                        out->balance, false, ws, s));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p,
+                       const moe_noise* noise, float w_importance, float w_load, moe_outputs* out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_forward_args(cfg, x, p, noise, out));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  return forward_on(cfg, x, p, noise, w_importance, w_load, out, ws, stream);
 }
 
 moe_status moe_draw_noise(const moe_config* cfg, uint64_t seed, float* eps, float* eps_p,

@@ -517,11 +517,11 @@ __device__ __forceinline__ void bw_block_scores(const BwGateArgs& a, const BwTil
     if (NOISY) {
       const float sp = softplus_f(ar[0][r]);
       ss[r] = sp;
-      hs[r] = noisy_score(c, es[r], sp);
+      hs[r] = select_score(noisy_score(c, es[r], sp));
       rs[r] = ar[0][r];
     } else {
       ss[r] = 0.f;
-      hs[r] = c;
+      hs[r] = select_score(c);
       rs[r] = 0.f;
     }
   }

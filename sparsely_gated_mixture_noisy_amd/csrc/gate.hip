@@ -187,7 +187,7 @@ __device__ void score_tile(const TileX<T>& tx, int d, const GateTabs& tb,
           ss[i][r] = 0.f;
         }
         cs[i][r] = c;
-        Hs[(32 * i + acc_row(r, lane)) * HLD + w * 32 + (lane & 31)] = h;
+        Hs[(32 * i + acc_row(r, lane)) * HLD + w * 32 + (lane & 31)] = select_score(h);
       }
     __syncthreads();
     // lane `sub` of the row holds columns sub + TPR*q.  Only scores at or above

@@ -277,4 +277,11 @@ __device__ __forceinline__ float noisy_score(float clean, float eps, float sp) {
   return __builtin_fmaf(eps, sp, clean);
 }
 
+// The score a selection ranks: a NaN score (from a NaN input) ranks as -inf,
+// so that every row still keeps k real experts (lowest index first among
+// equals) and no sentinel index leaves the gate.
+__device__ __forceinline__ float select_score(float h) {
+  return __builtin_isnan(h) ? -INFINITY : h;
+}
+
 }  // namespace moe

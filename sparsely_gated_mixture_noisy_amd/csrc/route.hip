@@ -126,7 +126,11 @@ __global__ __launch_bounds__(256) void route_hist_kernel(RouteArgs a) {
   __syncthreads();
   const int64_t t0 = (int64_t)b * ROUTE_BLOCK_TOKENS;
   const int nt = (int)min<int64_t>(ROUTE_BLOCK_TOKENS, a.T - t0);
-  for (int i = tid; i < nt * a.k; i += 256) atomicOr(&sb[a.idx[t0 * a.k + i]], 1u << (i / a.k));
+  // an index outside [0, E) (caller-supplied) takes no row
+  for (int i = tid; i < nt * a.k; i += 256) {
+    const int e = a.idx[t0 * a.k + i];
+    if ((unsigned)e < (unsigned)a.E) atomicOr(&sb[e], 1u << (i / a.k));
+  }
   __syncthreads();
   for (int e = tid; e < a.E; e += 256) a.bits[(int64_t)b * a.E + e] = sb[e];
 }
@@ -267,6 +271,10 @@ __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArg
     const int tl = i / a.k;
     const int64_t as = t0 * a.k + i;
     const int e = a.idx[as];
+    if ((unsigned)e >= (unsigned)a.E) {
+      a.inv[as] = -1;  // no such expert: the assignment takes no row
+      continue;
+    }
     const int64_t o = (int64_t)b * a.E + e;
     const int rank = a.base[o] + __popc(a.bits[o] & ((1u << tl) - 1u));
     if (a.capacity > 0 && rank >= a.capacity) {
@@ -277,9 +285,10 @@ __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArg
     a.perm[pos] = (int32_t)as;
     a.inv[as] = pos;
   }
-  if (a.capacity > 0) {
-    // positions no kept assignment took: a valid index, so that row gathers
-    // over all T*k positions stay in bounds
+  {
+    // positions no kept assignment took (a capacity, an index outside
+    // [0, E)): a valid index, so that row gathers over all T*k positions stay
+    // in bounds; none when every assignment has a row
     const int64_t A = a.T * a.k;
     for (int64_t p = off[a.E] + (int64_t)b * SCATTER_THREADS + tid; p < A;
          p += (int64_t)gridDim.x * SCATTER_THREADS)

@@ -125,3 +125,37 @@ def check_balance(imp, load, out, ref, excl, idx_ref, k1_sets=None, smooth=True,
         assert abs(out[1] - ref["cv2_load"]) <= 1e-4 * abs(ref["cv2_load"]) + 1e-7
         assert abs(out[2] - (w[0] * ref["cv2_importance"] + w[1] * ref["cv2_load"])) <= \
             1e-4 * abs(out[2]) + 1e-7
+
+
+def sampled_outputs(cfg, inp, x_cpu, ref, sample):
+    """y of the sampled tokens from the oracle's experts, one expert at a
+    time over the tokens of the sample that keep it (dropped slots of a
+    capacity add nothing): for layers too large for the whole oracle."""
+    import oracle
+    y_ref = np.zeros((sample.size, cfg.d_model))
+    ridx, rg = ref["idx"][sample], ref["gates"][sample]
+    kept = np.asarray(ref["inv"]).reshape(-1, cfg.top_k)[sample] >= 0
+    for e in np.unique(ridx):
+        rows, slots = np.nonzero((ridx == e) & kept)
+        if rows.size == 0:
+            continue
+        w1 = inp["w1"][e].cpu()
+        w2 = inp["w2"][e].cpu()
+        w3 = inp["w3"][e].cpu() if inp.get("w3") is not None else None
+        xe = x_cpu[sample[rows]]
+        ye = oracle.expert_swiglu(xe, w1, w3, w2) if w3 is not None else oracle.expert_relu(xe, w1, w2)
+        y_ref[rows] += rg[rows, slots][:, None] * ye
+    return y_ref
+
+
+def top_k1_sets(ref, cfg):
+    """Per token, the experts an excluded (near-tied) token could swap in:
+    its top-(k+1) experts, or every expert of its top-(k_groups+1) groups."""
+    g = ref["gate_info"]
+    if cfg.hierarchical:
+        prim = g["primary"]
+        order = np.argsort(-prim["H"], axis=1, kind="stable")[:, :cfg.k_groups + 1]
+        Eg = cfg.experts_per_group
+        return [np.concatenate([np.arange(q * Eg, (q + 1) * Eg) for q in row]) for row in order]
+    order = np.argsort(-g["H"], axis=1, kind="stable")[:, :cfg.top_k + 1]
+    return [row for row in order]

@@ -75,6 +75,22 @@ def test_missing_tensors_rejected(lib):
     assert b"w3" in lib.moe_last_error()
 
 
+def test_noisy_gate_without_noise_struct_rejected(lib):
+    """A noisy layer called with noise == NULL is refused with a status, also
+    for an empty batch (which reads no noise), instead of reading through
+    the null pointer on the host."""
+    for cfg in (CONFIGS["flat256"], CONFIGS["flat256"].replace(tokens=0),
+                CONFIGS["hier4096"].replace(tokens=0)):
+        c = L.make_config(cfg)
+        p = L.moe_params(w_gate=FAKE, w_noise=FAKE, w_gate_p=FAKE, w_noise_p=FAKE)
+        assert lib.moe_gate(ctypes.byref(c), FAKE, ctypes.byref(p), None, FAKE, FAKE, None,
+                            FAKE, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+        assert b"noise" in lib.moe_last_error()
+        o = L.moe_outputs(y=FAKE, topk_idx=FAKE, topk_gate=FAKE, counts=FAKE)
+        assert lib.moe_forward(ctypes.byref(c), FAKE, ctypes.byref(p), None, 1.0, 1.0,
+                               ctypes.byref(o), FAKE, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_workspace_checks(lib):
     cfg = CONFIGS["flat256"]
     need = L.workspace_size(cfg)

@@ -230,8 +230,9 @@ def test_backward_flat256_full_size_sampled():
     cpu = {key: (v.to("cpu") if v is not None else None) for key, v in inp.items()}
     dy = make_upstream(cfg, seed=0, device="cuda")
     _say("[backward] flat256 full size: forward + backward on the GPU")
-    fwd = L.forward(cfg, inp["x"], inp, inp, wi, wl, balance=True, save=True)
-    g = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
+    binp = L.packed_params(cfg, inp)
+    fwd = L.forward(cfg, inp["x"], binp, binp, wi, wl, balance=True, save=True)
+    g = L.backward(cfg, inp["x"], binp, binp, fwd, dy, wi, wl)
     torch.cuda.synchronize()
     _say("[backward] oracle gate and statistics")
     x = cpu["x"].double().numpy()
@@ -244,7 +245,6 @@ def test_backward_flat256_full_size_sampled():
     imp = oracle.importance(idx, gates, E)
     load = oracle.load_estimate(gi["clean"], gi["sp"], gi["H"], idx, gi["kth"], gi["k1th"])
     dimp = wi * oracle.cv_squared_grad(imp)
-    dload = wl * oracle.cv_squared_grad(load)
     srt = -np.sort(-gi["H"], axis=1)
     risky = ((srt[:, k - 2:k + 1] - srt[:, k - 1:k + 2]) < GAP).any(axis=1)
     w1 = cpu["w1"].double().numpy()
@@ -262,40 +262,26 @@ def test_backward_flat256_full_size_sampled():
         _check(f"dw1[{e}]", g.dw1[e], dw1, RTOL["bf16"], FRO["bf16"])
         _check(f"dw2[{e}]", g.dw2[e], dw2, RTOL["bf16"], FRO["bf16"])
 
-    # input gradients of sampled tokens: expert part + gate part
-    jk, jk1 = oracle.rank_experts(gi["H"], k)
-    wg = cpu["w_gate"].double().numpy()
-    wn = cpu["w_noise"].double().numpy()
-    eps = cpu["eps"].double().numpy()
-    toks = rng.choice(np.nonzero(~risky)[0], size=24, replace=False)
-    dx_ref = np.zeros((toks.size, cfg.d_model))
+    # input gradients of sampled tokens: the expert part from each kept
+    # expert's own backward, the gate part from the oracle's flat-gate
+    # backward on the sampled tokens, given their gate gradients and the
+    # whole layer's load (whose CV^2 gradient spans every token)
+    toks = np.sort(rng.choice(np.nonzero(~risky)[0], size=24, replace=False))
+    dgate = np.zeros((toks.size, k))
+    dxe = np.zeros((toks.size, cfg.d_model))
     for n, t in enumerate(toks):
         xt = x[t:t + 1]
-        dg = np.zeros(k)
-        dxe = np.zeros(cfg.d_model)
         for s in range(k):
             e = idx[t, s]
-            y_e = oracle.expert_relu(xt, w1[e], w2[e])[0]
-            dg[s] = y_e @ dyn[t] + dimp[e]
+            dgate[n, s] = oracle.expert_relu(xt, w1[e], w2[e])[0] @ dyn[t] + dimp[e]
             dX, _, _ = oracle.expert_relu_backward(xt, w1[e], w2[e], gates[t, s] * dyn[t:t + 1])
-            dxe += dX[0]
-        dH = np.zeros(E)
-        dH[idx[t]] = gates[t] * (dg - gates[t] @ dg)
-        kept = np.zeros(E, dtype=bool)
-        kept[idx[t]] = True
-        theta = np.where(kept, gi["k1th"][t], gi["kth"][t])
-        sp = gi["sp"][t]
-        z = (gi["clean"][t] - theta) / sp
-        dz = dload * oracle.normal_pdf(z)
-        dclean = dz / sp
-        dsp = -dz * z / sp
-        dtheta = -dz / sp
-        dH[jk[t]] += dtheta[~kept].sum()
-        dH[jk1[t]] += dtheta[kept].sum()
-        dclean = dclean + dH
-        dsp = dsp + dH * eps[t]
-        draw = dsp * oracle.sigmoid(xt[0] @ wn.T)
-        dx_ref[n] = dxe + dclean @ wg + draw @ wn
+            dxe[n] += dX[0]
+    sub_gate = {key: gi[key][toks] for key in ("clean", "sp", "H", "kth", "k1th")}
+    sub_fw = dict(gate_info=sub_gate, idx=idx[toks], gates=gates[toks], load=load)
+    sub_inp = dict(eps=cpu["eps"][toks], w_gate=cpu["w_gate"], w_noise=cpu["w_noise"])
+    res = oracle.moe_oracle._flat_gate_backward(sub_inp, cfg.replace(tokens=toks.size), x[toks],
+                                                sub_fw, dgate, wl)
+    dx_ref = dxe + res["dx"]
     got = np_(g.dx)[toks]
     _check("dx[sampled]", got, dx_ref, RTOL["bf16"], FRO["bf16"])
 
@@ -313,8 +299,9 @@ def test_backward_mixtral_full_size_sampled():
     inp = make_inputs(cfg, seed=0, device="cuda")
     dy = make_upstream(cfg, seed=0, device="cuda")
     _say("[backward] mixtral full size: forward + backward on the GPU")
-    fwd = L.forward(cfg, inp["x"], inp, inp, wi, wl, balance=True, save=True)
-    g = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
+    binp = L.packed_params(cfg, inp)
+    fwd = L.forward(cfg, inp["x"], binp, binp, wi, wl, balance=True, save=True)
+    g = L.backward(cfg, inp["x"], binp, binp, fwd, dy, wi, wl)
     torch.cuda.synchronize()
     _say("[backward] oracle gate and statistics")
     big = ("w1", "w2", "w3")
@@ -394,8 +381,9 @@ def test_backward_hier4096_full_size_sampled():
     cpu = {key: (v.to("cpu") if v is not None else None) for key, v in inp.items()}
     dy = make_upstream(cfg, seed=0, device="cuda")
     _say("[backward] hier4096 full size: forward + backward on the GPU")
-    fwd = L.forward(cfg, inp["x"], inp, inp, wi, wl, balance=True, save=True)
-    g = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
+    binp = L.packed_params(cfg, inp)
+    fwd = L.forward(cfg, inp["x"], binp, binp, wi, wl, balance=True, save=True)
+    g = L.backward(cfg, inp["x"], binp, binp, fwd, dy, wi, wl)
     torch.cuda.synchronize()
     _say("[backward] oracle hierarchical gate and statistics")
     x = cpu["x"].double().numpy()

@@ -15,7 +15,8 @@ import pytest
 import torch
 
 import oracle
-from moe_check import (check_balance, check_close, check_gate, check_routing, excluded, np_)
+from moe_check import (check_balance, check_close, check_gate, check_routing, excluded, np_,
+                       sampled_outputs, top_k1_sets)
 from sparsely_gated_mixture_noisy_amd import _lib as L
 from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs, make_upstream
 
@@ -110,3 +111,33 @@ def test_backward_with_in_kernel_noise(base):
         assert (a is None) == (b is None), key
         if a is not None:
             assert torch.equal(a, b), key
+
+
+def test_zipf2048_full_size_in_kernel_noise():
+    """The load-skewed workload at full size (32768 tokens, 2048 experts,
+    top-2, Zipf bias) gated by noise drawn inside the kernels, on the packed
+    tables: kept experts, gates, thresholds and routing over every token,
+    the smooth load and importance, and y on sampled tokens, against the
+    oracle fed its own draws of the same generator."""
+    cfg = CONFIGS["zipf2048"]
+    _say(f"[noise-full] zipf2048: {cfg}")
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    inp["eps"] = None   # never read: the kernels draw the noise
+    gen = dict(L.packed_params(cfg, inp), noise_seed=SEED)
+    out = L.forward(cfg, inp["x"], gen, gen, save=True)
+    torch.cuda.synchronize()
+    _say("[noise-full] zipf2048: oracle draws and gate")
+    cin = {k: (v.to("cpu") if isinstance(v, torch.Tensor) else v) for k, v in inp.items()
+           if k not in ("w1", "w2", "w3")}
+    cin["eps"] = oracle.draw_noise(cfg, SEED)["eps"]
+    ref = oracle.forward(cin, cfg, with_experts=False)
+    excl = excluded(ref)
+    check_gate(out.topk_idx, out.topk_gate, ref, excl, thr=out.thr)
+    check_routing(out.counts, out.offsets, out.perm, out.inv, out.topk_idx, ref, excl, cfg.top_k)
+    check_balance(out.importance, out.load, out.balance, ref, excl, ref["idx"],
+                  k1_sets=top_k1_sets(ref, cfg), smooth=True)
+    rng = np.random.default_rng(4)
+    sample = np.sort(rng.choice(np.nonzero(~excl)[0], size=64, replace=False))
+    worst = check_close(out.y[torch.from_numpy(sample).cuda()],
+                        sampled_outputs(cfg, inp, cin["x"], ref, sample), RTOL[cfg.dtype])
+    _say(f"[noise-full] zipf2048: ok excluded={int(excl.sum())} worst_y={worst:.2e}")

@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import oracle
-from moe_check import (check_balance, check_close, check_gate, check_routing, excluded, np_)
+from moe_check import (check_balance, check_close, check_gate, check_routing, excluded, np_,
+                       sampled_outputs, top_k1_sets)
 from sparsely_gated_mixture_noisy_amd import _lib as L
 from sparsely_gated_mixture_noisy_amd.inputs import CONFIGS, make_inputs
 
@@ -27,17 +28,6 @@ def _say(msg):
 
 def cpu_inputs(inp):
     return {k: (v.detach().to("cpu") if v is not None else None) for k, v in inp.items()}
-
-
-def top_k1_sets(ref, cfg):
-    g = ref["gate_info"]
-    if cfg.hierarchical:
-        prim = g["primary"]
-        order = np.argsort(-prim["H"], axis=1, kind="stable")[:, :cfg.k_groups + 1]
-        Eg = cfg.experts_per_group
-        return [np.concatenate([np.arange(q * Eg, (q + 1) * Eg) for q in row]) for row in order]
-    order = np.argsort(-g["H"], axis=1, kind="stable")[:, :cfg.top_k + 1]
-    return [row for row in order]
 
 
 def run_staged(cfg, inp):
@@ -127,41 +117,45 @@ def test_small_full_layer(name):
 
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_full_size(name):
+    """Each workload at its full size, twice: through the staged entry points
+    on the plain tables, and through moe_forward on the packed expert and
+    gate tables, the launch configuration the benchmark times.  Both are
+    compared with the oracle: gates and routing over every token, the
+    balance statistics, and y on sampled included tokens."""
     cfg = CONFIGS[name]
     _say(f"[parity-full] {name}: {cfg}")
     inp = make_inputs(cfg, seed=0, device="cuda")
     got = run_staged(cfg, inp)
+    binp = L.packed_params(cfg, inp)
+    fo = L.forward(cfg, inp["x"], binp, binp, save=True)
+    torch.cuda.synchronize()
+    bench = dict(idx=fo.topk_idx, gate=fo.topk_gate, thr=fo.thr, counts=fo.counts,
+                 offsets=fo.offsets, perm=fo.perm, inv=fo.inv, y=fo.y, importance=fo.importance,
+                 load=fo.load, balance=fo.balance)
     cin = cpu_inputs({k: v for k, v in inp.items() if k not in ("w1", "w2", "w3")})
     ref = oracle.forward(cin, cfg, with_experts=False)
     excl = excluded(ref)
-    rep = {}
-    check_gate(got["idx"], got["gate"], ref, excl, thr=got["thr"], report=rep)
-    check_routing(got["counts"], got["offsets"], got["perm"], got["inv"], got["idx"], ref, excl,
-                  cfg.top_k)
-    check_balance(got["importance"], got["load"], got["balance"], ref, excl, ref["idx"],
-                  k1_sets=top_k1_sets(ref, cfg), smooth=(cfg.noisy and not cfg.hierarchical))
-    # layer outputs on sampled included tokens, computed expert by expert
     rng = np.random.default_rng(1)
     inc = np.nonzero(~excl)[0]
     sample = np.sort(rng.choice(inc, size=min(96, inc.size), replace=False))
-    x = cin["x"]
-    y_ref = np.zeros((sample.size, cfg.d_model))
-    ridx, rg = ref["idx"][sample], ref["gates"][sample]
-    for e in np.unique(ridx):
-        rows, slots = np.nonzero(ridx == e)
-        w1 = inp["w1"][e].cpu()
-        w2 = inp["w2"][e].cpu()
-        w3 = inp["w3"][e].cpu() if inp["w3"] is not None else None
-        xe = x[sample[rows]]
-        ye = oracle.expert_swiglu(xe, w1, w3, w2) if w3 is not None else oracle.expert_relu(xe, w1, w2)
-        y_ref[rows] += rg[rows, slots][:, None] * ye
-    worst = check_close(got["y"][torch.from_numpy(sample).cuda()], y_ref, RTOL[cfg.dtype])
-    fo = L.forward(cfg, inp["x"], inp, inp)
-    torch.cuda.synchronize()
+    y_ref = sampled_outputs(cfg, inp, cin["x"], ref, sample)
+    for label, res in (("staged, plain tables", got), ("moe_forward, packed tables", bench)):
+        _say(f"[parity-full] {name}: {label}")
+        rep = {}
+        check_gate(res["idx"], res["gate"], ref, excl, thr=res["thr"], report=rep)
+        check_routing(res["counts"], res["offsets"], res["perm"], res["inv"], res["idx"], ref,
+                      excl, cfg.top_k)
+        check_balance(res["importance"], res["load"], res["balance"], ref, excl, ref["idx"],
+                      k1_sets=top_k1_sets(ref, cfg),
+                      smooth=(cfg.noisy and not cfg.hierarchical))
+        worst = check_close(res["y"][torch.from_numpy(sample).cuda()], y_ref, RTOL[cfg.dtype])
+        _say(f"[parity-full] {name}: {label} ok excluded={rep['excluded']} worst_y={worst:.2e}")
+    # the packed tables hold the same values in another order: same bits
     assert torch.equal(fo.y, got["y"]) and torch.equal(fo.topk_idx, got["idx"])
+    assert torch.equal(fo.topk_gate, got["gate"]) and torch.equal(fo.balance, got["balance"])
     c = np_(got["counts"])
-    _say(f"[parity-full] {name}: ok excluded={rep['excluded']} worst_y={worst:.2e} "
-         f"counts max/mean={c.max() / max(c.mean(), 1e-9):.1f} zero={int((c == 0).sum())}")
+    _say(f"[parity-full] {name}: counts max/mean={c.max() / max(c.mean(), 1e-9):.1f} "
+         f"zero={int((c == 0).sum())}")
 
 
 def test_determinism_bitwise():
@@ -309,3 +303,57 @@ def test_packed_gate_matches_unpacked_bitwise(name):
     torch.cuda.synchronize()
     for key in ("y", "topk_idx", "topk_gate", "counts", "importance", "load", "balance"):
         assert torch.equal(getattr(fa, key), getattr(fb, key)), key
+
+
+@pytest.mark.parametrize("base", ["flat256", "hier4096", "zipf2048"])
+def test_nan_row_keeps_real_experts(base):
+    """A token whose input row is NaN scores NaN everywhere; its selection
+    ranks NaN as -inf, so it still keeps k experts inside [0, E) (the lowest
+    indices, as among equal scores) and the routing, the experts and the
+    combine stay in bounds; every other token matches the oracle."""
+    cfg = CONFIGS[base].replace(tokens=300)
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    bad = 77
+    inp["x"][bad] = float("nan")
+    fo = L.forward(cfg, inp["x"], inp, inp, save=True)
+    torch.cuda.synchronize()
+    idx = np_(fo.topk_idx)
+    assert ((idx >= 0) & (idx < cfg.n_experts)).all()
+    c = np_(fo.counts)
+    assert int(c.sum()) == cfg.tokens * cfg.top_k
+    perm, inv = np_(fo.perm), np_(fo.inv)
+    assert (np.sort(perm) == np.arange(perm.size)).all() and (perm[inv] == np.arange(perm.size)).all()
+    if not cfg.hierarchical:
+        assert (idx[bad] == np.arange(cfg.top_k)).all()
+    ref = oracle.forward(cpu_inputs(inp), cfg)
+    excl = excluded(ref)
+    excl[bad] = True
+    check_gate(fo.topk_idx, fo.topk_gate, ref, excl)
+    check_close(fo.y, ref["y"], RTOL[cfg.dtype], rows=np.nonzero(~excl)[0])
+
+
+def test_route_drops_expert_ids_outside_the_layer():
+    """moe_route on caller-supplied indices, some of them outside [0, E)
+    (-1, E, the largest int32): those assignments take no row (inv = -1),
+    and the others are grouped exactly as the stable routing of the valid
+    assignments alone."""
+    cfg = CONFIGS["flat256"].replace(tokens=500, n_experts=40, top_k=3)
+    rng = np.random.default_rng(5)
+    idx = np.stack([np.sort(rng.choice(cfg.n_experts, size=3, replace=False))
+                    for _ in range(cfg.tokens)]).astype(np.int32)
+    bad = rng.choice(idx.size, size=37, replace=False)
+    idx.reshape(-1)[bad] = rng.choice([-1, cfg.n_experts, 2 ** 31 - 1], size=bad.size)
+    counts, offsets, perm, inv, _ = L.route(cfg, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < cfg.n_experts)
+    want_counts = np.bincount(flat[valid], minlength=cfg.n_experts)
+    assert (np_(counts) == want_counts).all()
+    assert (np_(offsets) == np.concatenate([[0], np.cumsum(want_counts)])).all()
+    a = np.nonzero(valid)[0]
+    order = a[np.argsort(flat[a], kind="stable")]   # by expert, assignments ascending
+    n = order.size
+    assert (np_(perm)[:n] == order).all() and (np_(perm)[n:] == 0).all()
+    want_inv = np.full(flat.size, -1)
+    want_inv[order] = np.arange(n)
+    assert (np_(inv) == want_inv).all()
