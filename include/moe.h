@@ -287,6 +287,32 @@ moe_status moe_forward(const moe_config* cfg, const void* x,
                        float w_importance, float w_load, moe_outputs* out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Forward pass that allocates nothing --------------------------------
+ * For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  moe_forward_static is
+ * moe_forward (same arguments without ws / ws_bytes, same kernels, bitwise
+ * the same results) with its scratch in a static device array of
+ * MOE_FORWARD_STATIC_SCRATCH_BYTES inside the library: each GPU the library
+ * runs on holds one such array until the process ends.  It calls no
+ * allocating routine.  The array of the current device is used, so `stream`
+ * must belong to the current device.
+ *   - Returns MOE_ERR_WORKSPACE, enqueueing nothing, when the layer needs more
+ *     scratch than that (moe_workspace_size(cfg) > the limit; for example the
+ *     8192-token, 256-expert, d_model 512 layer needs about 34 MiB).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (on different streams, or from several threads without
+ *     ordering) race and give wrong results.  Calls ordered on one stream are
+ *     safe.  The array needs no initialization; each call overwrites what it
+ *     uses.
+ *   - The first call on a device looks the array's address up (thread-safe)
+ *     and keeps it; a failure there returns MOE_ERR_HIP. */
+#define MOE_FORWARD_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+moe_status moe_forward_static(const moe_config* cfg, const void* x,
+                              const moe_params* p, const moe_noise* noise,
+                              float w_importance, float w_load, moe_outputs* out,
+                              void* stream);
+
 /* ---- Backward pass -------------------------------------------------------
  * Gradients of L = sum(dy * y) + w_importance * CV^2(importance) +
  * w_load * CV^2(load) for the flat gate or the hierarchy, ReLU or SwiGLU

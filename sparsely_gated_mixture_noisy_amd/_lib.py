@@ -90,6 +90,10 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(moe_config), _P, ctypes.POINTER(moe_params),
                                    ctypes.POINTER(moe_noise), ctypes.c_float, ctypes.c_float,
                                    ctypes.POINTER(moe_outputs), _P, ctypes.c_size_t, _P]),
+    "moe_forward_static": (ctypes.c_int, [ctypes.POINTER(moe_config), _P,
+                                          ctypes.POINTER(moe_params), ctypes.POINTER(moe_noise),
+                                          ctypes.c_float, ctypes.c_float,
+                                          ctypes.POINTER(moe_outputs), _P]),
     "moe_packed_experts_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config)]),
     "moe_pack_experts": (ctypes.c_int, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_params),
                                         _P, _P]),
@@ -407,6 +411,20 @@ class Forward:
 def forward(cfg: MoEConfig, x, params, noise, w_importance=1.0, w_load=1.0, balance=True,
             ws: Optional[Workspace] = None, save: bool = False) -> ForwardOut:
     return Forward(cfg, x, params, noise, w_importance, w_load, balance, ws, save=save)()
+
+
+def forward_static(cfg: MoEConfig, x, params, noise, w_importance=1.0, w_load=1.0,
+                   balance=True, save: bool = False) -> ForwardOut:
+    """moe_forward_static: the layer with the library's static scratch
+    instead of a workspace (no allocation inside the call; the outputs are
+    allocated here, by the caller)."""
+    T = x.shape[0]
+    out = ForwardOut(cfg, T, x.device, balance, save)
+    c, p, n, o = make_config(cfg, T), make_params(params), make_noise(noise), out.struct()
+    _check(load().moe_forward_static(ctypes.byref(c), _ptr(x), ctypes.byref(p), ctypes.byref(n),
+                                     float(w_importance), float(w_load), ctypes.byref(o),
+                                     _stream()), "moe_forward_static")
+    return out
 
 
 def backward_workspace_size(cfg: MoEConfig, tokens: Optional[int] = None) -> int:

@@ -6,12 +6,20 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
 #include "moe_kernels.h"
 
 using namespace moe;
+
+// Scratch of moe_forward_static: one array per GPU, in the library's code
+// object, held until the process ends.  Host code reaches it only through
+// the device address hipGetSymbolAddress returns for the current device
+// (scratch_ptr below); in host code the array's name is a stand-in, not a
+// device address.
+static __device__ __align__(256) unsigned char scratch[MOE_FORWARD_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -74,7 +82,10 @@ Layout layout(const moe_config* c) {
   L.tiles = take(4 * (size_t)(E + 1));
   // tile descriptors of the fused expert kernel (64-row tiles)
   L.desc = take(12 * (size_t)((A + 63) / 64 + E));
-  L.hid = take(elem_size(c) * (size_t)A * c->d_hidden);
+  // the hidden layer in memory: only the unfused expert paths keep it there
+  const bool fused_ffn = c->dtype == MOE_BF16 &&
+                         fused_ffn_supported(c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
+  L.hid = take(fused_ffn ? 0 : elem_size(c) * (size_t)A * c->d_hidden);
   L.ysorted = take(elem_size(c) * (size_t)A * c->d_model);
   L.part = take(4 * (size_t)L.load_blocks * E);
   L.imp_part = take(gate_fuses_load(E) ? 4 * (size_t)L.nb * E : 0);
@@ -1251,6 +1262,29 @@ moe_status forward_on(const moe_config* cfg, const void* x, const moe_params* p,
   return ok();
 }
 
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES];  // per device, set on its first call
+
+moe_status scratch_ptr(void** ptr) {
+  int dev = -1;
+  MOE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is past the %d devices the library tracks", dev,
+                MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    MOE_TRY(hip_status(hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)),
+                       "hipGetSymbolAddress(scratch)"));
+    if (!a || (reinterpret_cast<uintptr_t>(a) & 255))
+      return fail(MOE_ERR_HIP, "static scratch of device %d has no usable address", dev);
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1260,6 +1294,21 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const moe_params* p
                        void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_forward_args(cfg, x, p, noise, out));
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  return forward_on(cfg, x, p, noise, w_importance, w_load, out, ws, stream);
+}
+
+moe_status moe_forward_static(const moe_config* cfg, const void* x, const moe_params* p,
+                              const moe_noise* noise, float w_importance, float w_load,
+                              moe_outputs* out, void* stream) {
+  MOE_TRY(check_forward_args(cfg, x, p, noise, out));
+  const size_t need = layout(cfg).total;
+  if (need > MOE_FORWARD_STATIC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this layer needs %zu bytes of scratch, more than the %zu of the static array "
+                "(use moe_forward with a workspace)",
+                need, (size_t)MOE_FORWARD_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  MOE_TRY(scratch_ptr(&ws));
   return forward_on(cfg, x, p, noise, w_importance, w_load, out, ws, stream);
 }
 

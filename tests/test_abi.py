@@ -91,6 +91,23 @@ def test_noisy_gate_without_noise_struct_rejected(lib):
                                ctypes.byref(o), FAKE, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
 
 
+def test_static_scratch_forward_refuses_layers_too_large(lib):
+    """moe_forward_static takes layers whose workspace fits its 64 MiB static
+    array (the 8192-token, 256-expert layer needs about 34 MiB) and refuses
+    larger ones with MOE_ERR_WORKSPACE before touching a GPU."""
+    assert L.workspace_size(CONFIGS["flat256"]) <= 64 << 20
+    for cfg in (CONFIGS["mixtral"], CONFIGS["hier4096"], CONFIGS["flat256"].replace(tokens=20000)):
+        assert L.workspace_size(cfg) > 64 << 20
+        c = L.make_config(cfg)
+        p = L.moe_params(w_gate=FAKE, w_noise=FAKE, w_gate_p=FAKE, w_noise_p=FAKE, w1=FAKE,
+                         w2=FAKE, w3=FAKE)
+        n = L.moe_noise(eps=FAKE, eps_p=FAKE)
+        o = L.moe_outputs(y=FAKE)
+        assert lib.moe_forward_static(ctypes.byref(c), FAKE, ctypes.byref(p), ctypes.byref(n),
+                                      1.0, 1.0, ctypes.byref(o), None) == L.MOE_ERR_WORKSPACE
+        assert b"static" in lib.moe_last_error()
+
+
 def test_workspace_checks(lib):
     cfg = CONFIGS["flat256"]
     need = L.workspace_size(cfg)
