@@ -12,4 +12,6 @@ from .moe_oracle import (cv_squared, combine, dense_forward, dense_gates,  # noq
                          run_experts, silu, softplus,
                          balance_stats, backward, cv_squared_grad, rank_experts,
                          expert_relu_backward, expert_swiglu_backward, normal_pdf,
-                         sigmoid, philox4x32_10, uniform23, philox_normals, draw_noise)
+                         sigmoid, philox4x32_10, uniform23, philox_normals, draw_noise,
+                         batch_mask, threshold_mask, masked_gates, masked_route,
+                         masked_forward)

@@ -409,6 +409,120 @@ def forward(inp: Dict, cfg, w_importance=1.0, w_load=1.0,
     return out
 
 
+# ---------------------------------------------------------------------------
+# Per-batch equal-size expert mask and its inference thresholds  [Paper card,
+# section 方法适配: in some translation runs a per-batch mask gives every
+# expert the same batch size during training, and per-expert thresholds
+# approximate that mask at inference]
+#
+# Readings of what the page leaves open (each also in the design notes):
+#   * batch mask: expert e keeps the m tokens of the batch with the largest
+#     scores H[:, e] (ties: the lower token index), m given by the caller
+#     (m = k T / E gives every token k experts on average);
+#   * threshold mask: token t is kept by expert e iff H[t, e] >= theta[e]
+#     (theta set to each expert's m-th largest score over a batch reproduces
+#     that batch's mask when the scores have no ties);
+#   * a token's gates are the softmax over the scores of the experts that
+#     kept it (the lesson page's softmax over the kept scores), zero
+#     elsewhere; a token kept by no expert has no gates and y = 0;
+#   * rows: expert e takes its kept tokens in ascending token order, at most
+#     `capacity` of them (0: no limit); later ones are dropped and add
+#     nothing to y, the gates are not renormalised (as with the capacity of
+#     the top-k layer);
+#   * balance statistics: importance as in the top-k layer (sum of each
+#     expert's gates over the batch, before any drop), load = the hard count
+#     of kept tokens per expert before any drop.
+# ---------------------------------------------------------------------------
+
+def batch_mask(H: np.ndarray, m: int) -> np.ndarray:
+    """[T][E] bool: expert e keeps the m best tokens of its column of H."""
+    H = np.asarray(H, dtype=np.float64)
+    T, E = H.shape
+    keep = np.zeros((T, E), dtype=bool)
+    for e in range(E):
+        order = np.argsort(-H[:, e], kind="stable")   # ties: lower token first
+        keep[order[:min(m, T)], e] = True
+    return keep
+
+
+def threshold_mask(H: np.ndarray, theta: np.ndarray) -> np.ndarray:
+    """[T][E] bool: H[t, e] >= theta[e]."""
+    return np.asarray(H, dtype=np.float64) >= np.asarray(theta, dtype=np.float64)[None, :]
+
+
+def masked_gates(H: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """[T][E] gates: per token, the softmax over its kept scores."""
+    H = np.asarray(H, dtype=np.float64)
+    G = np.zeros_like(H)
+    for t in range(H.shape[0]):
+        kept = np.nonzero(keep[t])[0]
+        if kept.size == 0:
+            continue
+        h = H[t, kept]
+        w = np.exp(h - h.max())
+        G[t, kept] = w / w.sum()
+    return G
+
+
+def masked_route(keep: np.ndarray, capacity: int = 0):
+    """Rows of each expert from a keep mask: counts[E], offsets[E+1],
+    perm[p] = the token at position p (expert-contiguous, tokens ascending),
+    and pos[T][E] = the position of (t, e), or -1 when e did not keep t or
+    its capacity dropped it."""
+    T, E = keep.shape
+    counts = np.zeros(E, dtype=np.int64)
+    pos = np.full((T, E), -1, dtype=np.int64)
+    cols = []
+    for e in range(E):
+        toks = np.nonzero(keep[:, e])[0]           # ascending
+        if capacity > 0:
+            toks = toks[:capacity]
+        counts[e] = toks.size
+        cols.append(toks)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.zeros(int(offsets[-1]), dtype=np.int64)
+    for e in range(E):
+        p = offsets[e] + np.arange(cols[e].size)
+        perm[p] = cols[e]
+        pos[cols[e], e] = p
+    return counts.astype(np.int32), offsets.astype(np.int32), perm.astype(np.int32), pos
+
+
+def masked_forward(inp: Dict, cfg, rows_per_expert: int = 0, thresholds=None,
+                   w_importance=1.0, w_load=1.0) -> Dict:
+    """The flat layer with the batch mask (rows_per_expert = m > 0) or the
+    threshold mask (thresholds [E]) in place of KeepTopK; cfg.capacity caps
+    the rows of an expert.  Returns the mask, gates [T][E], routing, y and
+    the balance statistics."""
+    clean, sp, H = noisy_logits(inp["x"], inp["w_gate"], inp.get("w_noise"), inp.get("bias"),
+                                inp.get("eps"))
+    if thresholds is None:
+        keep = batch_mask(H, rows_per_expert)
+    else:
+        keep = threshold_mask(H, thresholds)
+    G = masked_gates(H, keep)
+    counts, offsets, perm, pos = masked_route(keep, getattr(cfg, "capacity", 0))
+    x = _f64(inp["x"])
+    w1, w2, w3 = _f64(inp["w1"]), _f64(inp["w2"]), _f64(inp.get("w3"))
+    E = cfg.n_experts
+    y_sorted = np.zeros((int(offsets[-1]), x.shape[1]))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y_sorted[lo:hi] = expert_apply(x[perm[lo:hi]], e, w1, w2, w3)
+    y = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        for e in np.nonzero(pos[t] >= 0)[0]:         # experts ascending
+            y[t] += G[t, e] * y_sorted[pos[t, e]]
+    imp = G.sum(axis=0)
+    load = keep.sum(axis=0).astype(np.float64)
+    ci, cl = cv_squared(imp), cv_squared(load)
+    return dict(H=H, keep=keep, gates=G, counts=counts, offsets=offsets, perm=perm, pos=pos,
+                y_sorted=y_sorted, y=y, importance=imp, load=load, cv2_importance=ci,
+                cv2_load=cl, loss=w_importance * ci + w_load * cl)
+
+
 def dense_forward(inp: Dict, cfg) -> np.ndarray:
     """Brute force: evaluate every expert on every token and sum with the dense
     gate vector, y_t = sum over all e of G(x_t)_e E_e(x_t).  Tiny inputs only.

@@ -29,6 +29,7 @@ pins = _load("test_oracle_pins")
 bpins = _load("test_oracle_backward_pins")
 cpins = _load("test_oracle_capacity_pins")
 npins = _load("test_oracle_noise_pins")
+mpins = _load("test_oracle_mask_pins")
 
 _orig = {name: getattr(om, name) for name in dir(om) if not name.startswith("__")}
 
@@ -43,7 +44,7 @@ def _cases(fn):
 
 def _pin_fails(name):
     fn = (getattr(pins, name, None) or getattr(bpins, name, None) or getattr(cpins, name, None)
-          or getattr(npins, name))
+          or getattr(npins, name, None) or getattr(mpins, name))
     for args in _cases(fn):
         try:
             fn(*args)
@@ -378,6 +379,47 @@ def noise_group_in_stream_word(cfg, seed):
     return d
 
 
+def batch_mask_ties_to_higher_token(H, m):
+    H = np.asarray(H, dtype=np.float64)
+    T, E = H.shape
+    keep = np.zeros((T, E), dtype=bool)
+    for e in range(E):
+        order = (T - 1 - np.argsort(-H[::-1, e], kind="stable"))
+        keep[order[:min(m, T)], e] = True
+    return keep
+
+
+def batch_mask_keeps_one_more(H, m):
+    return _orig["batch_mask"](H, m + 1)
+
+
+def threshold_strictly_above(H, theta):
+    return np.asarray(H, dtype=np.float64) > np.asarray(theta, dtype=np.float64)[None, :]
+
+
+def masked_softmax_over_all_experts(H, keep):
+    H = np.asarray(H, dtype=np.float64)
+    w = np.exp(H - H.max(axis=1, keepdims=True))
+    return np.where(keep, w / w.sum(axis=1, keepdims=True), 0.0)
+
+
+def masked_route_tokens_descending(keep, capacity=0):
+    T = keep.shape[0]
+    counts, offsets, perm, pos = _orig["masked_route"](keep[::-1], capacity)
+    perm = (T - 1 - perm).astype(np.int32)
+    return counts, offsets, perm, pos[::-1]
+
+
+def masked_route_capacity_keeps_latest(keep, capacity=0):
+    if capacity <= 0:
+        return _orig["masked_route"](keep, capacity)
+    keep = keep.copy()
+    for e in range(keep.shape[1]):
+        toks = np.nonzero(keep[:, e])[0]
+        keep[toks[:max(0, toks.size - capacity)], e] = False
+    return _orig["masked_route"](keep, 0)
+
+
 # (function patched, mistake, pins that must reject it)
 MUTATIONS = [
     ("noisy_logits", noise_term_dropped, ["test_noisy_logits_hand_example"]),
@@ -433,6 +475,18 @@ MUTATIONS = [
     ("draw_noise", noise_primary_on_stream_zero, ["test_draw_noise_counter_layout"]),
     ("draw_noise", noise_flat_rows_from_one, ["test_draw_noise_counter_layout"]),
     ("draw_noise", noise_group_in_stream_word, ["test_draw_noise_counter_layout"]),
+    ("batch_mask", batch_mask_ties_to_higher_token, ["test_batch_mask_hand_example",
+                                                     "test_every_expert_keeps_exactly_m_of_its_best"]),
+    ("batch_mask", batch_mask_keeps_one_more, ["test_batch_mask_hand_example",
+                                               "test_every_expert_keeps_exactly_m_of_its_best",
+                                               "test_calibrated_thresholds_reproduce_the_batch_mask"]),
+    ("threshold_mask", threshold_strictly_above, ["test_threshold_mask_hand_example",
+                                                  "test_calibrated_thresholds_reproduce_the_batch_mask"]),
+    ("masked_gates", masked_softmax_over_all_experts, ["test_batch_mask_hand_example",
+                                                       "test_masked_gates_invariants"]),
+    ("masked_route", masked_route_tokens_descending, ["test_batch_mask_hand_example"]),
+    ("masked_route", masked_route_capacity_keeps_latest, ["test_batch_mask_hand_example",
+                                                          "test_masked_layer_equals_dense_mixture_over_kept_pairs"]),
     # backward
     ("cv_squared_grad", cv2_grad_without_mean_term, ["test_cv_squared_gradient_closed_forms",
                                                      "test_gradients_match_central_differences"]),
