@@ -6,10 +6,17 @@ balance statistics) over one batch of synthetic inputs already resident in
 HBM.  Default workload: 8192 tokens, d_model 512, 256 ReLU experts
 512 -> 1024 -> 512, noisy top-4 gating (bf16, fp32 accumulation).
 
-Besides the timed steps, the same stages are replayed through their own entry
-points with HIP events between them (same stream, same kernels) to give the
-per-stage times and the roofline of the dominant stage.  The CPU oracle is
-timed on a bounded token sample of the same workload.
+Every timed step is preceded by an untimed write and read-back of a 1 GiB
+scratch buffer, which evicts the 256 MB last-level cache (the expert tables
+are 537 MB) and leaves it clean, and HIP events on the library's stream
+bracket the forward alone; the same steps run back to back are reported
+beside it.  The stages are
+replayed through their own entry points, with the same write before each
+replay and events between the stages, for the per-stage times and the
+roofline of each stage.  The other four workloads are measured the same way
+(forward and stages, no backward and no CPU leg) and reported in the same
+line.  The CPU oracle is timed on a bounded token sample of the headline
+workload.
 """
 import argparse
 import ctypes
@@ -123,7 +130,39 @@ class Stages:
             raise RuntimeError(f"{name}: {self.lib.moe_last_error().decode()}")
 
 
-def stage_times(st, steps):
+FLUSH_BYTES = 1 << 30  # > 4x the 256 MB last-level cache
+
+
+class Flush:
+    """Untimed work on the current stream, enqueued before each timed step so
+    that the step's reads come from HBM rather than the 256 MB last-level
+    cache.  "write_read" (the default) writes a 1 GiB scratch buffer and then
+    reads it back: the cache ends up holding clean lines of the scratch
+    buffer only.  "write" leaves the cache full of dirty scratch lines, whose
+    write-back then competes with the step's own traffic (an artifact of the
+    method, not a property of the layer); "read" evicts with clean lines
+    only; "none" runs the steps back to back."""
+
+    MODES = ("write_read", "write", "read", "none")
+
+    def __init__(self, mode="write_read", device="cuda"):
+        import torch
+        self.mode = mode
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device).fill_(1)
+        self.words = self.buf.view(torch.int64)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        if self.mode in ("write_read", "write"):
+            self.buf.fill_(self.n & 0xFF)
+        if self.mode in ("write_read", "read"):
+            self.sink = self.words.sum()
+
+
+def stage_times(st, steps, flush=None):
+    """Mean event time of each stage over `steps` replays of the stages in
+    order, each replay preceded by the flush when one is given."""
     import torch
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
@@ -133,6 +172,8 @@ def stage_times(st, steps):
         st.call(name, s)
     torch.cuda.synchronize()
     for i in range(steps):
+        if flush is not None:
+            flush()
         evs[i][0].record(stream)
         for j, name in enumerate(st.names):
             st.call(name, s)
@@ -140,6 +181,37 @@ def stage_times(st, steps):
     torch.cuda.synchronize()
     return {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
             for j, name in enumerate(st.names)}
+
+
+def time_forward(fwd, steps, warmup, flush):
+    """Flushed: each of `steps` forwards after the flush, events around the
+    forward alone.  Unflushed: `steps` forwards back to back between two
+    events.  Returns (per-step flushed ms list, unflushed ms per step, wall
+    seconds of the flushed timed region)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        flush()
+        fwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flushed = [a.elapsed_time(b) for a, b in ev]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return flushed, e0.elapsed_time(e1) / steps, wall
 
 
 def expert_work(cfg, counts):
@@ -183,6 +255,73 @@ def stage_bytes(cfg):
     return {"gate": gate, "route": route, "combine": combine}
 
 
+def stage_flops(cfg):
+    """Algorithmic flops of the gate's projections (the route and the
+    combine are bound by memory: integer work, one multiply-add per element
+    read)."""
+    T, d, k = cfg.tokens, cfg.d_model, cfg.top_k
+    tabs = 2 if cfg.noisy else 1
+    if cfg.hierarchical:
+        cols = cfg.n_groups + cfg.k_groups * cfg.experts_per_group
+    else:
+        cols = cfg.n_experts
+    return {"gate": 2.0 * T * d * cols * tabs, "route": 0.0, "combine": 2.0 * T * k * d}
+
+
+def roofline(nbytes, flops, ms, dtype):
+    """The stage's bound (whichever of its HBM bytes at 8 TB/s and its flops
+    at the MFMA peak of its dtype takes longer) and the fraction of that
+    peak it reaches."""
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (peak_tf * 1e12)
+    sec = ms * 1e-3
+    if t_mfma > t_hbm:
+        ach = flops / sec / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": ach / peak_tf}
+    ach = nbytes / sec / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBS}
+
+
+def stage_rooflines(cfg, stages, counts):
+    flops, ebytes, hit = expert_work(cfg, counts)
+    sb, sf = stage_bytes(cfg), stage_flops(cfg)
+    out = {name: dict(roofline(sb[name], sf[name], stages[name], cfg.dtype), bytes=sb[name],
+                      flops=sf[name], ms=stages[name])
+           for name in ("gate", "route", "combine")}
+    out["experts"] = dict(roofline(ebytes, flops, stages["experts"], cfg.dtype), bytes=ebytes,
+                          flops=flops, ms=stages["experts"], experts_hit=hit)
+    return out
+
+
+def workload_line(L, cfg, steps, warmup, flush):
+    """Forward (flushed and back to back) and flushed stage times with each
+    stage's roofline, for one workload on its packed tables."""
+    import numpy as np
+    import torch
+    from sparsely_gated_mixture_noisy_amd.inputs import make_inputs
+    inp = L.packed_params(cfg, make_inputs(cfg, seed=0, device="cuda"))
+    torch.cuda.synchronize()
+    fwd = L.Forward(cfg, inp["x"], inp, inp, balance=True)
+    flushed, unflushed, _ = time_forward(fwd, steps, warmup, flush)
+    ms = float(np.mean(flushed))
+    counts = fwd.out.counts.cpu().numpy()
+    stages = stage_times(Stages(L, cfg, inp), steps, flush)
+    line = {"workload": describe(cfg), "forward_ms": ms,
+            "tokens_per_s": cfg.tokens / (ms * 1e-3), "forward_ms_unflushed": unflushed,
+            "stages_ms": stages, "stages": stage_rooflines(cfg, stages, counts),
+            "counts_max_over_mean": float(counts.max() / max(counts.mean(), 1e-9)),
+            "experts_without_rows": int((counts == 0).sum())}
+    print(f"[bench] {cfg.name}: forward {ms:.4f} ms flushed, {unflushed:.4f} ms back to back; "
+          f"stages {json.dumps({k: round(v, 4) for k, v in stages.items()})}",
+          file=sys.stderr, flush=True)
+    del fwd, inp
+    torch.cuda.empty_cache()
+    return line
+
+
 def backward_work(cfg, hit):
     """Algorithmic flops and HBM bytes of one backward pass: the hidden layer
     recomputed and four more products per routed row (dHid, dX and the two
@@ -205,30 +344,23 @@ def backward_work(cfg, hit):
     return flops, tables + acts + noise
 
 
-def backward_line(L, cfg, inp, fwd_ms, steps, warmup, hit, cpu_budget=0.0):
+def backward_line(L, cfg, inp, fwd_ms, steps, warmup, hit, flush, cpu_budget=0.0):
     """moe_backward timed on the forward's saved tensors (HIP events around
-    `steps` calls after `warmup`), with the gradients of sum(dy * y) + CV^2
-    losses of weight 1 for a seeded dy."""
+    each of `steps` calls after `warmup`, each after the flush), with the
+    gradients of sum(dy * y) + CV^2 losses of weight 1 for a seeded dy."""
+    import numpy as np
     import torch
     from sparsely_gated_mixture_noisy_amd.inputs import make_upstream
     dy = make_upstream(cfg, seed=0, device="cuda")
     saved = L.Forward(cfg, inp["x"], inp, inp, balance=True, save=True)()
     bwd = L.Backward(cfg, inp["x"], inp, inp, saved, dy)
-    for _ in range(max(1, warmup)):
-        bwd()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        bwd()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    bms = e0.elapsed_time(e1) / steps
+    flushed, _, _ = time_forward(bwd, steps, max(1, warmup), flush)
+    bms = float(np.mean(flushed))
     print(f"[bench] moe_backward {bms:.4f} ms/step", file=sys.stderr, flush=True)
     flops, nbytes = backward_work(cfg, hit)
     peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-    line = {"ms_per_step": bms, "tokens_per_s": cfg.tokens / (bms * 1e-3),
+    line = {"ms_per_step": bms, "ms_per_step_note": "each call after the flush work",
+            "tokens_per_s": cfg.tokens / (bms * 1e-3),
             "train_step_tokens_per_s": cfg.tokens / ((bms + fwd_ms) * 1e-3),
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "flops": flops, "mfma_frac": flops / (bms * 1e-3) / 1e12 / peak_tf,
@@ -314,17 +446,21 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; about 40 ms of work lets the clocks settle")
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (each after the flush, like the timed ones)")
     ap.add_argument("--config", default="flat256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement (reported beside the forward)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other four workloads (reported beside the headline)")
+    ap.add_argument("--flush", choices=Flush.MODES, default="write_read",
+                    help="untimed work before each timed step (see Flush)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer (device to device) a few times and exit: "
-                         "the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
+                         "the reference kernel for the read and write request counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: every expert of this layer sits on one MI355X and "
@@ -349,6 +485,7 @@ def main():
         return
     cfg = CONFIGS[args.config]
     print(f"[bench] {describe(cfg)}", file=sys.stderr, flush=True)
+    flush = Flush(args.flush)
     inp = make_inputs(cfg, seed=0, device="cuda")
     # expert and gate tables repacked once into the kernels' stream order (a
     # parameter transform, outside the timed region), when the layer has them
@@ -357,21 +494,11 @@ def main():
     gpacked = inp.get("w_gate_packed")
     torch.cuda.synchronize()
     fwd = L.Forward(cfg, inp["x"], inp, inp, balance=True)
-    for _ in range(args.warmup):
-        fwd()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        fwd()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] moe_forward {ms:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})",
+    flushed, unflushed, wall = time_forward(fwd, args.steps, args.warmup, flush)
+    ms = float(np.mean(flushed))
+    print(f"[bench] moe_forward {ms:.4f} ms/step after the flush (p10 "
+          f"{np.percentile(flushed, 10):.4f}, p90 {np.percentile(flushed, 90):.4f}); "
+          f"{unflushed:.4f} back to back; timed region wall {wall:.3f} s",
           file=sys.stderr, flush=True)
     counts = fwd.out.counts.cpu().numpy()
 
@@ -394,38 +521,46 @@ def main():
                    "ffn": cfg.ffn, "noisy": cfg.noisy,
                    "expert_tables": "packed" if packed is not None else "plain",
                    "gate_tables": "packed" if gpacked is not None else "plain"},
+        "timing": f"each timed step follows untimed flush work '{args.flush}' on a 1 GiB "
+                  "scratch buffer (write_read: written, then read back, so the expert tables "
+                  "come from HBM and the 256 MB last-level cache holds no dirty lines); events "
+                  "bracket the forward alone",
+        "ms_per_step_p10_p90": [float(np.percentile(flushed, 10)),
+                                float(np.percentile(flushed, 90))],
+        "unflushed": {"ms_per_step": unflushed, "value": cfg.tokens / (unflushed * 1e-3),
+                      "note": "the same steps back to back, no scratch write between them"},
     }
-    flops, ebytes, hit = expert_work(cfg, counts)
+    hit = int((counts > 0).sum())
     if not args.no_stages:
-        st = Stages(L, cfg, inp)
-        stages = stage_times(st, args.steps)
-        print(f"[bench] stages ms: {json.dumps({k: round(v, 4) for k, v in stages.items()})}",
+        stages = stage_times(Stages(L, cfg, inp), args.steps, flush)
+        print(f"[bench] stages ms after the flush: "
+              f"{json.dumps({k: round(v, 4) for k, v in stages.items()})}",
               file=sys.stderr, flush=True)
-        t_exp = stages["experts"] * 1e-3
-        achieved = ebytes / t_exp / 1e9
-        peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-        tflops = flops / t_exp / 1e12
-        res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+        sr = stage_rooflines(cfg, stages, counts)
+        ex = sr["experts"]
+        res["roofline"] = {"bound": ex["bound"], "achieved": ex["achieved"], "peak": ex["peak"],
+                           "unit": ex["unit"], "frac": ex["frac"],
                            "traffic": expert_traffic_bytes(args.config, packed is not None),
-                           "kernel": "expert FFN stage (moe_expert_ffn)",
-                           "bytes_per_launch": ebytes}
+                           "kernel": "expert FFN stage (moe_expert_ffn, one kernel launch)",
+                           "bytes_per_launch": ex["bytes"], "flops_per_launch": ex["flops"]}
         res["stages_ms"] = stages
-        sb = stage_bytes(cfg)
-        res["stages_hbm"] = {
-            name: {"bytes": b, "gbs": b / (stages[name] * 1e-3) / 1e9,
-                   "frac": b / (stages[name] * 1e-3) / 1e9 / HBM_PEAK_GBS}
-            for name, b in sb.items()}
-        res["expert_tflops"] = tflops
-        res["expert_mfma_frac"] = tflops / peak_tf
+        res["stages"] = sr
+        peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+        res["expert_tflops"] = ex["flops"] / (stages["experts"] * 1e-3) / 1e12
+        res["expert_mfma_frac"] = res["expert_tflops"] / peak_tf
         res["experts_hit"] = hit
     res["counts_max_over_mean"] = float(counts.max() / max(counts.mean(), 1e-9))
     if not args.no_backward:
         res["backward"] = backward_line(
-            L, cfg, inp, fwd_ms=ms, steps=args.steps, warmup=args.warmup, hit=hit,
+            L, cfg, inp, fwd_ms=ms, steps=args.steps, warmup=args.warmup, hit=hit, flush=flush,
             cpu_budget=0.0 if args.no_cpu_baseline else args.cpu_budget / 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    if not args.no_workloads:
+        del fwd, inp
+        torch.cuda.empty_cache()
+        res["workloads"] = {name: workload_line(L, c, args.steps, min(args.warmup, 5), flush)
+                            for name, c in CONFIGS.items() if name != args.config}
     print(json.dumps(res), flush=True)
 
 

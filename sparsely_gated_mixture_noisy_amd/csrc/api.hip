@@ -49,7 +49,7 @@ size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
 // Every workspace region, at fixed offsets for a given configuration.
 struct Layout {
-  size_t idx, gate, thr, counts, offsets, perm, inv, bits, base, tiles, desc, hid, ysorted, part,
+  size_t idx, gate, thr, counts, offsets, perm, inv, bits, base, tiles, hid, ysorted, part,
       imp_part, imp, load;
   size_t idx_p, gate_p, counts_g, offsets_g, perm_g, inv_g, bits_g, base_g, tiles_g;
   size_t counts_u, offsets_u, perm_u, inv_u;
@@ -80,8 +80,6 @@ Layout layout(const moe_config* c) {
   L.base = take(4 * (size_t)L.nb * E);
 
   L.tiles = take(4 * (size_t)(E + 1));
-  // tile descriptors of the fused expert kernel (64-row tiles)
-  L.desc = take(12 * (size_t)((A + 63) / 64 + E));
   // the hidden layer in memory: only the unfused expert paths keep it there
   const bool fused_ffn = c->dtype == MOE_BF16 &&
                          fused_ffn_supported(c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
@@ -371,9 +369,7 @@ moe_status do_route(const moe_config* c, const Layout& L, const int32_t* idx, in
   r.inv = inv;
   r.tile_rows = with_tiles ? expert_tile_rows(c) : 0;
   r.tiles = at<int32_t>(ws, L.tiles);
-  const bool fused = c->dtype == MOE_BF16 &&
-                     fused_ffn_supported(c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
-  r.desc = fused ? at<int32_t>(ws, L.desc) : nullptr;
+  r.desc = nullptr;
   if (st.imp_part) {
     r.imp_part = st.imp_part;
     r.load_part = st.load_part;
@@ -409,15 +405,10 @@ moe_status do_ffn(const moe_config* c, const Layout& L, const void* x, const int
   f.y_sorted = y_sorted;
   f.A = c->tokens * c->top_k;
   f.wpacked = p->w_packed;
-  const bool fused = bf16 && fused_ffn_supported(c->d_model, c->d_hidden, sw);
-  int32_t* desc = fused ? at<int32_t>(ws, L.desc) : nullptr;
-  f.desc = desc;
   if (f.A == 0) return MOE_OK;
-  if (bf16 && !tiles_ready)
-    MOE_TRY(hip_status(launch_tile_map(offsets, c->n_experts,
-                                       ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw, f.A,
-                                                     c->n_experts),
-                                       tiles, desc, s),
+  const int rows = bf16 ? ffn_tile_rows(bf16, c->d_model, c->d_hidden, sw, f.A, c->n_experts) : 0;
+  if (rows > 0 && !tiles_ready)
+    MOE_TRY(hip_status(launch_tile_map(offsets, c->n_experts, rows, tiles, nullptr, s),
                        "expert tiles"));
   return hip_status(launch_expert_ffn(f, bf16, sw, s), "experts");
 }
@@ -701,7 +692,6 @@ moe_status hier_gate_backward(const moe_config* c, const BwLayout& L, const void
     R.bits = L.r_bits;
     R.base = L.r_base;
     R.tiles = L.r_counts;  // no tile map is built (with_tiles false)
-    R.desc = L.r_counts;
     int32_t* offs = at<int32_t>(ws, L.r_offsets);
     int32_t* pm = at<int32_t>(ws, L.r_perm);
     MOE_TRY(do_route(c, R, sv->topk_idx, at<int32_t>(ws, L.r_counts), offs, pm,

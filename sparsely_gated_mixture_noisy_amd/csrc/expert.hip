@@ -634,7 +634,7 @@ static bool big_tiles(int64_t A, int E) { return A >= (int64_t)GB_BM * E; }
 
 int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E) {
   if (!bf16) return 1;
-  if (fused_ffn_supported(d, h, swiglu)) return fused_ffn_tile_rows();
+  if (fused_ffn_supported(d, h, swiglu)) return 0;  // finds its tiles from the offsets
   return big_tiles(A, E) ? GB_BM : GM_BM;
 }
 

@@ -44,8 +44,8 @@ struct FusedArgs {
   const bf16_t* x;
   const int32_t* perm;  // null: row p is x[p]
   int k;
-  const int32_t* tiles;  // [E+1], tiles of FZ_M rows
-  const int32_t* desc;   // [tiles][3]: expert, first position, rows
+  const int32_t* offsets;  // [E+1] routing offsets: expert e holds positions
+                           // offsets[e] .. offsets[e+1]-1
   int E, h;
   const bf16_t* w1;      // [E][h][D]   (unpacked)
   const bf16_t* w2;      // [E][D][h]   (unpacked)
@@ -253,20 +253,37 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
   __shared__ int s_src[M];
 
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    const int Q = a.tiles[a.E];
-    const int per = (Q + 7) / 8;
+  // This workgroup's tile, found from the offsets: expert e holds
+  // ceil(m_e / M) tiles (m_e its rows), numbered in expert order, its 32-row
+  // blocks split over them by tile_rows.  Workgroup b takes tile
+  // (b % 8) * ceil(Q / 8) + b / 8 of the Q tiles, so that the tiles of an
+  // expert run on one XCD (workgroups go to the XCDs round-robin).
+  {
+    const int per = (a.E + FZ_THREADS - 1) / FZ_THREADS;  // experts per thread
+    const int e0 = min(a.E, tid * per), e1 = min(a.E, e0 + per);
+    int nt = 0;
+    for (int e = e0; e < e1; ++e) nt += (a.offsets[e + 1] - a.offsets[e] + M - 1) / M;
+    int Q;
+    int run = block_excl_scan<FZ_THREADS>(nt, &Q);
+    const int perx = (Q + 7) / 8;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int q = xcd * per + slot;
-    int e = -1, p0 = 0, m = 0;
-    if (slot < per && q < Q) {
-      e = a.desc[3 * q];
-      p0 = a.desc[3 * q + 1];
-      m = a.desc[3 * q + 2];
+    const int q = xcd * perx + slot;
+    if (tid == 0) s_info[0] = -1;
+    __syncthreads();
+    if (slot < perx && q < Q && q >= run && q < run + nt) {
+      for (int e = e0; e < e1; ++e) {
+        const int o = a.offsets[e], m = a.offsets[e + 1] - o, n = (m + M - 1) / M;
+        if (q < run + n) {
+          int first, rows;
+          tile_rows(m, n, q - run, &first, &rows);
+          s_info[0] = e;
+          s_info[1] = o + first;
+          s_info[2] = rows;
+          break;
+        }
+        run += n;
+      }
     }
-    s_info[0] = e;
-    s_info[1] = p0;
-    s_info[2] = m;
   }
   __syncthreads();
   const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
@@ -298,8 +315,6 @@ __global__ __launch_bounds__(FZ_THREADS, 1) void ffn_relu_fused_kernel(FusedArgs
 bool fused_ffn_supported(int d, int h, int swiglu) {
   return !swiglu && d == FZ_D && h % FZ_H == 0;
 }
-
-int fused_ffn_tile_rows() { return FZ_M; }
 
 size_t fused_packed_bytes(int E, int d, int h) {
   return sizeof(bf16_t) * 2 * (size_t)E * d * h;
@@ -361,8 +376,7 @@ hipError_t launch_fused_ffn(const FfnArgs& f, hipStream_t s) {
   a.x = (const bf16_t*)f.x;
   a.perm = f.perm;
   a.k = f.k;
-  a.tiles = f.tiles;
-  a.desc = f.desc;
+  a.offsets = f.offsets;
   a.E = f.E;
   a.h = f.h;
   a.w1 = (const bf16_t*)f.w1;

@@ -140,6 +140,17 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Rows of tile i of the nt tiles that hold an expert's m rows: the
+// ceil(m / 32) blocks of 32 rows go to the tiles as evenly as possible, whole
+// blocks first, so the tiles run no more MFMA row blocks than the rows need
+// (near-equal row counts would give 130 rows two tiles of three blocks).
+__device__ __forceinline__ void tile_rows(int m, int nt, int i, int* first, int* rows) {
+  const int nblk = (m + 31) / 32, base = nblk / nt, rem = nblk % nt;
+  const int b0 = i * base + min(i, rem), nb = base + (i < rem ? 1 : 0);
+  *first = 32 * b0;
+  *rows = min(m, 32 * (b0 + nb)) - 32 * b0;
+}
+
 // Exclusive prefix sum of one int per thread over a workgroup of NT threads
 // (NT a multiple of 64); *total gets the sum.  One barrier pair.
 template <int NT>

@@ -116,8 +116,8 @@ struct FfnArgs {
   const int32_t* perm;    // null: row p is x[p]; else x[perm[p] / k]
   int k;
   const int32_t* offsets; // [E+1]
-  const int32_t* tiles;   // [E+1] tile map for the kernel's row tile
-  const int32_t* desc;    // [tiles][3] tile descriptors (fused path)
+  const int32_t* tiles;   // [E+1] tile map for the kernel's row tile (grouped
+                          // GEMM paths; the fused path finds its tiles itself)
   int E, d, h;
   const void* w1;         // [E][h][d]
   const void* w3;         // [E][h][d] or null
@@ -127,11 +127,11 @@ struct FfnArgs {
   int64_t A;
   const void* wpacked;    // packed expert tables (fused path) or null
 };
-// rows per tile of the expert stage for A routed rows over E experts
+// rows per tile of the expert stage's tile map for A routed rows over E
+// experts; 0 when the path needs no tile map (the fused path)
 int ffn_tile_rows(bool bf16, int d, int h, int swiglu, int64_t A, int E);
 // fused ReLU path (hidden layer kept on chip), d_model 512
 bool fused_ffn_supported(int d, int h, int swiglu);
-int fused_ffn_tile_rows();
 hipError_t launch_fused_ffn(const FfnArgs& a, hipStream_t s);
 size_t fused_packed_bytes(int E, int d, int h);
 hipError_t launch_pack_experts(const void* w1, const void* w2, int E, int d, int h, void* out,

@@ -59,17 +59,6 @@ __device__ int block_scan4(const int v[4], int* total) {
   return wbase + incl - s;
 }
 
-// Rows of tile i of the nt tiles that hold an expert's m rows: the
-// ceil(m / 32) blocks of 32 rows go to the tiles as evenly as possible, whole
-// blocks first, so the tiles run no more MFMA row blocks than the rows need
-// (near-equal row counts would give 130 rows two tiles of three blocks).
-__device__ __forceinline__ void tile_rows(int m, int nt, int i, int* first, int* rows) {
-  const int nblk = (m + 31) / 32, base = nblk / nt, rem = nblk % nt;
-  const int b0 = i * base + min(i, rem), nb = base + (i < rem ? 1 : 0);
-  *first = 32 * b0;
-  *rows = min(m, 32 * (b0 + nb)) - 32 * b0;
-}
-
 // Tile map of the expert stage from per-expert row counts: tiles[e] = first
 // tile of expert e (exclusive scan of ceil(count / rows)), tiles[E] = total;
 // with desc, desc[q] = {expert, first position, rows}, an expert's rows split
