@@ -34,20 +34,20 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_FP32_PEAK_TFLOPS = 157.3
 
 # HBM traffic of one launch of the fused expert kernel on the default workload,
-# from two rocprofv3 --pmc passes over this script (FETCH_SIZE, then
-# WRITE_SIZE; KiB per dispatch, averaged over the dispatches).  Each counter is
-# scaled by what it reads for a plain 512 MiB device-to-device copy
-# (--copy-calibration 512): FETCH_SIZE 262156 KiB for 524288 KiB read,
-# WRITE_SIZE 524288 KiB for 524288 KiB written.  Valid only while the kernel's
-# sources hash to `sources_sha256`; otherwise the traffic is reported as null.
+# from rocprofv3 --pmc passes over this script: read requests by size
+# (TCC_EA0_RDREQ_32B / _64B / _128B, summed over the L2 channels) and write
+# requests (TCC_EA0_WRREQ, all 64 B), per dispatch, averaged over the
+# dispatches.  Bytes are the request counts times their sizes; a plain 512 MiB
+# device-to-device copy reads 4194304 x 128 B = 512 MiB by the same count.
+# Valid only while the kernel's sources hash to `sources_sha256`; otherwise
+# the traffic is reported as null.
 EXPERT_TRAFFIC = {
     "config": "flat256",
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
-                "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h",
-                "sparsely_gated_mixture_noisy_amd/csrc/moe_kernels.h"],
-    "sources_sha256": "1ee1d350a9722fe32f56ac838d7393f4ade3de915d6ca2e4a027bb0de3b341e5",
-    "fetch_kib": 288889.8, "fetch_scale": 524288.0 / 262156.0,
-    "write_kib": 32768.1, "write_scale": 524288.0 / 524288.0,
+                "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h"],
+    "sources_sha256": "75d2575f862b4bfe9469aa93e5e9638e43490abd5c7267358caeeb07dcd45cf4",
+    "rdreq_128b": 4615856.857, "rdreq_64b": 3804.571, "rdreq_32b": 0.0,
+    "wrreq_64b": 524288.571,
 }
 
 
@@ -64,7 +64,8 @@ def expert_traffic_bytes(config_name, packed):
             h.update(fh.read())
     if h.hexdigest() != t["sources_sha256"]:
         return None
-    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
+    return 128.0 * t["rdreq_128b"] + 64.0 * t["rdreq_64b"] + 32.0 * t["rdreq_32b"] + \
+        64.0 * t["wrreq_64b"]
 
 
 def describe(cfg):
