@@ -313,6 +313,52 @@ moe_status moe_forward_static(const moe_config* cfg, const void* x,
                               float w_importance, float w_load, moe_outputs* out,
                               void* stream);
 
+/* ---- Per-batch equal-size expert mask ------------------------------------
+ * In place of KeepTopK, the flat layer's experts choose their tokens
+ * ("Outrageously Large Neural Networks: The Sparsely-Gated Mixture-of-Experts
+ * Layer - 中文验证版", ai-papers.xuzou.cn, section 方法适配: in some
+ * translation runs a per-batch mask gives every expert the same batch size in
+ * training, and per-expert thresholds approximate that mask at inference):
+ *   batch mask (thresholds == NULL): expert e keeps the rows_per_expert = m
+ *     tokens of the batch with the largest noisy scores H[:, e] (ties: the
+ *     lower token), so every expert receives exactly m rows;
+ *   threshold mask (thresholds [E] f32 given): expert e keeps every token
+ *     with H[t, e] >= thresholds[e]; the first m of them in token order take
+ *     rows, later ones are dropped and add nothing to y.
+ * A token's gates are the softmax over the scores of the experts that kept
+ * it; a token kept by no expert gets y = 0.  The balance statistics are
+ * importance[e] = sum of e's gates over the batch and load[e] = the number of
+ * tokens e kept (before the cap), CV^2 and the weighted loss as in
+ * moe_balance_loss.  H, the projections and the noise are those of moe_gate
+ * (same tables, bias, noise and packed tables).  Flat gate only
+ * (cfg->n_groups == 0); cfg->capacity must be 0 (m sets the rows);
+ * cfg->top_k is not used.  1 <= m <= tokens (any m >= 1 for an empty batch).
+ * A NaN score ranks as -inf.  Rows: at most R = E * m. */
+typedef struct moe_mask_outputs {
+  void* y;                 /* [T][d], required when T > 0 */
+  int32_t* counts;         /* [E] rows of each expert (nullable, as all below) */
+  int32_t* offsets;        /* [E+1] exclusive prefix sum of counts */
+  int32_t* perm;           /* [R] token of each row: expert-contiguous, tokens
+                              ascending inside an expert; rows past offsets[E]
+                              hold 0 */
+  int32_t* tok_offsets;    /* [T+1] token t's slots are [tok_offsets[t],
+                              tok_offsets[t+1]) */
+  int32_t* slot_expert;    /* [R] expert of each slot, ascending in a token */
+  float* slot_gate;        /* [R] its gate */
+  int32_t* slot_row;       /* [R] its row (position in expert order) */
+  float* importance;       /* [E]; the statistics are computed only when */
+  float* load;             /* [E]; `balance` is non-NULL */
+  float* balance;          /* [3]: cv2 importance, cv2 load, weighted loss */
+} moe_mask_outputs;
+
+/* Bytes of workspace moe_forward_mask needs (0 for an invalid request). */
+size_t moe_mask_workspace_size(const moe_config* cfg, int32_t rows_per_expert);
+
+moe_status moe_forward_mask(const moe_config* cfg, const void* x, const moe_params* p,
+                            const moe_noise* noise, int32_t rows_per_expert,
+                            const float* thresholds, float w_importance, float w_load,
+                            moe_mask_outputs* out, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Backward pass -------------------------------------------------------
  * Gradients of L = sum(dy * y) + w_importance * CV^2(importance) +
  * w_load * CV^2(load) for the flat gate or the hierarchy, ReLU or SwiGLU

@@ -62,6 +62,12 @@ class moe_outputs(ctypes.Structure):
                  "thr", "offsets", "perm", "inv", "y_sorted")]
 
 
+class moe_mask_outputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("y", "counts", "offsets", "perm", "tok_offsets", "slot_expert", "slot_gate",
+                 "slot_row", "importance", "load", "balance")]
+
+
 class moe_saved(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_gate", "thr", "offsets", "perm", "inv", "y_sorted",
@@ -94,6 +100,11 @@ _SIGS = {
                                           ctypes.POINTER(moe_params), ctypes.POINTER(moe_noise),
                                           ctypes.c_float, ctypes.c_float,
                                           ctypes.POINTER(moe_outputs), _P]),
+    "moe_mask_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config), ctypes.c_int32]),
+    "moe_forward_mask": (ctypes.c_int, [ctypes.POINTER(moe_config), _P, ctypes.POINTER(moe_params),
+                                        ctypes.POINTER(moe_noise), ctypes.c_int32, _P,
+                                        ctypes.c_float, ctypes.c_float,
+                                        ctypes.POINTER(moe_mask_outputs), _P, ctypes.c_size_t, _P]),
     "moe_packed_experts_size": (ctypes.c_size_t, [ctypes.POINTER(moe_config)]),
     "moe_pack_experts": (ctypes.c_int, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_params),
                                         _P, _P]),
@@ -424,6 +435,52 @@ def forward_static(cfg: MoEConfig, x, params, noise, w_importance=1.0, w_load=1.
     _check(load().moe_forward_static(ctypes.byref(c), _ptr(x), ctypes.byref(p), ctypes.byref(n),
                                      float(w_importance), float(w_load), ctypes.byref(o),
                                      _stream()), "moe_forward_static")
+    return out
+
+
+def mask_workspace_size(cfg: MoEConfig, rows_per_expert: int,
+                        tokens: Optional[int] = None) -> int:
+    c = make_config(cfg, tokens)
+    return int(load().moe_mask_workspace_size(ctypes.byref(c), int(rows_per_expert)))
+
+
+class MaskOut:
+    """Output tensors of one moe_forward_mask call (see include/moe.h)."""
+
+    def __init__(self, cfg: MoEConfig, T: int, m: int, device, balance: bool):
+        E, R = cfg.n_experts, cfg.n_experts * m
+        i32 = dict(dtype=torch.int32, device=device)
+        self.y = torch.empty((T, cfg.d_model), dtype=_act_dtype(cfg), device=device)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.perm = torch.empty(R, **i32)
+        self.tok_offsets = torch.empty(T + 1, **i32)
+        self.slot_expert = torch.empty(R, **i32)
+        self.slot_gate = torch.empty(R, dtype=torch.float32, device=device)
+        self.slot_row = torch.empty(R, **i32)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.importance = torch.empty(E, **f32) if balance else None
+        self.load = torch.empty(E, **f32) if balance else None
+        self.balance = torch.empty(3, **f32) if balance else None
+
+    def struct(self) -> moe_mask_outputs:
+        return moe_mask_outputs(**{n: _ptr(getattr(self, n)) for n, _ in moe_mask_outputs._fields_})
+
+
+def forward_mask(cfg: MoEConfig, x, params, noise, rows_per_expert: int, thresholds=None,
+                 w_importance=1.0, w_load=1.0, balance=True,
+                 ws: Optional[Workspace] = None) -> MaskOut:
+    """moe_forward_mask: the batch mask (thresholds None) or the threshold
+    mask (thresholds [E] float32) in place of KeepTopK."""
+    T = x.shape[0]
+    m = int(rows_per_expert)
+    ws = ws or Workspace(mask_workspace_size(cfg, m, T), x.device)
+    out = MaskOut(cfg, T, m, x.device, balance)
+    c, p, n, o = make_config(cfg, T), make_params(params), make_noise(noise), out.struct()
+    _check(load().moe_forward_mask(ctypes.byref(c), _ptr(x), ctypes.byref(p), ctypes.byref(n), m,
+                                   _ptr(thresholds), float(w_importance), float(w_load),
+                                   ctypes.byref(o), ws.ptr, ws.nbytes, _stream()),
+           "moe_forward_mask")
     return out
 
 

@@ -1302,6 +1302,168 @@ moe_status moe_forward_static(const moe_config* cfg, const void* x, const moe_pa
   return forward_on(cfg, x, p, noise, w_importance, w_load, out, ws, stream);
 }
 
+// ---- per-batch equal-size mask ---------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+struct MaskLayout {
+  size_t Ht, bits, base, counts, offsets, perm, tokstat, nslot, tok_off, slot_e, slot_g, slot_pos,
+      ysorted, hid, tiles, imp, load, bal;
+  size_t total;
+  int nb;
+  int64_t tp, rows;
+};
+
+MaskLayout mask_layout(const moe_config* c, int m) {
+  MaskLayout L;
+  const int64_t T = c->tokens;
+  const int E = c->n_experts;
+  L.nb = (int)((T + 31) / 32);
+  L.tp = 32 * (int64_t)L.nb;
+  L.rows = (int64_t)E * m;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.Ht = take(4 * (size_t)E * L.tp);
+  L.bits = take(4 * (size_t)L.nb * E);
+  L.base = take(4 * (size_t)L.nb * E);
+  L.counts = take(4 * (size_t)E);
+  L.offsets = take(4 * (size_t)(E + 1));
+  L.perm = take(4 * (size_t)L.rows);
+  L.tokstat = take(8 * (size_t)T);
+  L.nslot = take(4 * (size_t)T);
+  L.tok_off = take(4 * (size_t)(T + 1));
+  L.slot_e = take(4 * (size_t)L.rows);
+  L.slot_g = take(4 * (size_t)L.rows);
+  L.slot_pos = take(4 * (size_t)L.rows);
+  L.ysorted = take(elem_size(c) * (size_t)L.rows * c->d_model);
+  const bool fused_ffn = c->dtype == MOE_BF16 &&
+                         fused_ffn_supported(c->d_model, c->d_hidden, c->ffn == MOE_FFN_SWIGLU);
+  L.hid = take(fused_ffn ? 0 : elem_size(c) * (size_t)L.rows * c->d_hidden);
+  L.tiles = take(4 * (size_t)(E + 1));
+  L.imp = take(4 * (size_t)E);
+  L.load = take(4 * (size_t)E);
+  L.bal = take(4 * 4);
+  L.total = o;
+  return L;
+}
+
+moe_status check_mask_request(const moe_config* c, int32_t m) {
+  MOE_TRY(check_config(c));
+  if (c->n_groups > 0)
+    return fail(MOE_ERR_UNSUPPORTED, "the per-batch expert mask is for the flat gate");
+  if (c->capacity != 0)
+    return fail(MOE_ERR_INVALID_ARG, "capacity must be 0: rows_per_expert sets the rows");
+  if (m < 1 || (c->tokens > 0 && m > c->tokens))
+    return fail(MOE_ERR_INVALID_ARG, "rows_per_expert must be in [1, tokens]");
+  if ((int64_t)c->n_experts * m > (int64_t)INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts * rows_per_expert exceeds int32 rows");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_mask_workspace_size(const moe_config* cfg, int32_t rows_per_expert) {
+  if (check_mask_request(cfg, rows_per_expert) != MOE_OK) return 0;
+  return mask_layout(cfg, rows_per_expert).total;
+}
+
+moe_status moe_forward_mask(const moe_config* cfg, const void* x, const moe_params* p,
+                            const moe_noise* noise, int32_t rows_per_expert,
+                            const float* thresholds, float w_importance, float w_load,
+                            moe_mask_outputs* out, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_mask_request(cfg, rows_per_expert));
+  MOE_TRY(check_gate_inputs(cfg, x, p, noise));
+  MOE_TRY(check_expert_inputs(cfg, p));
+  if (!out || (!out->y && cfg->tokens > 0)) return fail(MOE_ERR_INVALID_ARG, "out / out->y is NULL");
+  const MaskLayout L = mask_layout(cfg, rows_per_expert);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  const bool noisy = cfg->noisy != 0;
+  const int E = cfg->n_experts, m = rows_per_expert;
+  int32_t* counts = out->counts ? out->counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = out->offsets ? out->offsets : at<int32_t>(ws, L.offsets);
+  int32_t* perm = out->perm ? out->perm : at<int32_t>(ws, L.perm);
+  MaskArgs a;
+  a.x = x;
+  a.w_gate = p->w_gate;
+  a.w_noise = noisy ? p->w_noise : nullptr;
+  a.bias = p->bias;
+  a.noise = noisy ? noise_src(noise, noise ? noise->eps : nullptr, 0) : NoiseSrc();
+  a.w_pack = p->w_gate_packed;
+  a.pack_nt = gate_pack_tables(cfg);
+  a.T = cfg->tokens;
+  a.d = cfg->d_model;
+  a.E = E;
+  a.NB = L.nb;
+  a.Tp = L.tp;
+  a.m = m;
+  a.theta = thresholds;
+  a.Ht = at<float>(ws, L.Ht);
+  a.bits = at<uint32_t>(ws, L.bits);
+  a.base = at<int32_t>(ws, L.base);
+  a.offsets = offsets;
+  a.tokstat = at<float2>(ws, L.tokstat);
+  a.nslot = at<int32_t>(ws, L.nslot);
+  a.tok_off = out->tok_offsets ? out->tok_offsets : at<int32_t>(ws, L.tok_off);
+  a.slot_e = out->slot_expert ? out->slot_expert : at<int32_t>(ws, L.slot_e);
+  a.slot_g = out->slot_gate ? out->slot_gate : at<float>(ws, L.slot_g);
+  a.slot_pos = out->slot_row ? out->slot_row : at<int32_t>(ws, L.slot_pos);
+  a.importance = out->importance ? out->importance : at<float>(ws, L.imp);
+  a.load = out->load ? out->load : at<float>(ws, L.load);
+  MOE_TRY(hip_status(launch_mask_scores(a, bf16, noisy, s), "mask scores"));
+  if (!thresholds) MOE_TRY(hip_status(launch_mask_select(a, s), "batch mask"));
+  RouteArgs r;
+  r.idx = nullptr;
+  r.T = cfg->tokens;
+  r.k = 1;
+  r.E = E;
+  r.NB = L.nb;
+  r.bits = a.bits;
+  r.base = at<int32_t>(ws, L.base);
+  r.have_bits = 1;
+  r.counts = counts;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.inv = nullptr;
+  r.tile_rows = 0;
+  r.tiles = nullptr;
+  r.desc = nullptr;
+  r.capacity = m;
+  MOE_TRY(hip_status(launch_mask_route(r, L.rows, s), "mask rows"));
+  MOE_TRY(hip_status(launch_mask_tokens(a, s), "mask slots"));
+  // the experts over the rows: row p is token perm[p]
+  moe_config rc = *cfg;
+  rc.tokens = L.rows;
+  rc.top_k = 1;
+  Layout RL{};
+  RL.tiles = L.tiles;
+  RL.hid = L.hid;
+  void* y_sorted = at<void>(ws, L.ysorted);
+  MOE_TRY(do_ffn(&rc, RL, x, perm, offsets, p, y_sorted, false, ws, s));
+  MOE_TRY(hip_status(launch_combine_csr(y_sorted, a.tok_off, a.slot_pos, a.slot_g, cfg->tokens,
+                                        cfg->d_model, bf16, out->y, s),
+                     "mask combine"));
+  if (out->balance) {
+    MOE_TRY(hip_status(launch_mask_balance(a, s), "mask balance"));
+    MOE_TRY(hip_status(launch_cv2(a.importance, a.load, E, w_importance, w_load, out->balance, s),
+                       "mask cv2"));
+  }
+  return ok();
+}
+
 moe_status moe_draw_noise(const moe_config* cfg, uint64_t seed, float* eps, float* eps_p,
                           void* stream) {
   MOE_TRY(check_config(cfg));

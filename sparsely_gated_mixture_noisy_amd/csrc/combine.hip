@@ -161,6 +161,19 @@ __global__ __launch_bounds__(BAL_THREADS) void cv2_kernel(BalanceArgs a) {
   }
 }
 
+hipError_t launch_cv2(const float* importance, const float* load, int E, float w_imp,
+                      float w_load, float* out, hipStream_t s) {
+  BalanceArgs a{};
+  a.importance = const_cast<float*>(importance);
+  a.load = const_cast<float*>(load);
+  a.E = E;
+  a.w_imp = w_imp;
+  a.w_load = w_load;
+  a.out = out;
+  hipLaunchKernelGGL(cv2_kernel, dim3(1), dim3(BAL_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(balance_kernel, dim3((a.E + BAL_EXPERTS - 1) / BAL_EXPERTS),
                      dim3(BAL_THREADS), 0, s, a);

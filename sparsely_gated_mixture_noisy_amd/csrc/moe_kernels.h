@@ -98,6 +98,10 @@ struct RouteArgs {
   int capacity = 0;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Rows of a keep mask (bits [NB][E], one bit per token): counts per expert
+// (capped at a.capacity when > 0), offsets, and perm[p] = the token at row
+// p, tokens ascending inside each expert; perm[offsets[E] .. perm_len) = 0.
+hipError_t launch_mask_route(const RouteArgs& a, int64_t perm_len, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
 
 // x_sorted[p] = x[perm[p] / k] for p < A (elem_bytes per element, d per row)
@@ -202,6 +206,53 @@ struct BalanceArgs {
   float* out;         // [3]
 };
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t s);
+// CV^2 of importance and load (fp64, fixed order) and their weighted sum
+hipError_t launch_cv2(const float* importance, const float* load, int E, float w_imp,
+                      float w_load, float* out, hipStream_t s);
+
+// ------------------------------------------- per-batch equal-size mask ---
+// In place of KeepTopK: expert e keeps the m tokens of the batch with the
+// largest noisy scores (batch mask), or every token whose score reaches
+// theta[e], at most m of them in token order (threshold mask).
+struct MaskArgs {
+  const void* x;
+  const void* w_gate;   // [E][d]
+  const void* w_noise;  // [E][d] or null
+  const float* bias;    // [E] or null
+  NoiseSrc noise;
+  const void* w_pack = nullptr;  // packed gate tables or null
+  int pack_nt = 1;
+  int64_t T;
+  int d, E;
+  int NB;               // ceil(T / 32)
+  int64_t Tp;           // row stride of Ht: 32 * NB
+  int m;                // batch mask: rows per expert; threshold mask: the cap
+  const float* theta;   // [E] threshold mask, or null (batch mask)
+  float* Ht;            // [E][Tp] scores, expert-major
+  uint32_t* bits;       // [NB][E] keep masks: bit i = token 32b+i kept by e
+  const int32_t* base;  // [NB][E] kept tokens of e in blocks before b (colscan)
+  const int32_t* offsets;  // [E+1] rows of each expert
+  float2* tokstat;      // [T] max kept score, 1 / sum of exp over the kept experts
+  int32_t* nslot;       // [T] kept pairs of the token that have a row
+  int32_t* tok_off;     // [T+1]
+  int32_t* slot_e;      // [rows] expert of each slot, ascending within a token
+  float* slot_g;        // [rows] its gate
+  int32_t* slot_pos;    // [rows] its row
+  float* importance;    // [E] or null
+  float* load;          // [E]
+};
+// scores (and, threshold mask, the keep masks)
+hipError_t launch_mask_scores(const MaskArgs& a, bool bf16, bool noisy, hipStream_t s);
+// batch mask: each expert's m best tokens -> keep masks
+hipError_t launch_mask_select(const MaskArgs& a, hipStream_t s);
+// per token: softmax statistics and slot counts; the slot offsets; the slots
+hipError_t launch_mask_tokens(const MaskArgs& a, hipStream_t s);
+// importance (gates recomputed from the token statistics) and hard load
+hipError_t launch_mask_balance(const MaskArgs& a, hipStream_t s);
+// y[t] = sum over the token's slots (ascending) of gate * y_sorted[row]
+hipError_t launch_combine_csr(const void* y_sorted, const int32_t* tok_off,
+                              const int32_t* slot_pos, const float* slot_g, int64_t T, int d,
+                              bool bf16, void* y, hipStream_t s);
 
 // -------------------------------------------------------------- backward ---
 hipError_t launch_bw_cv2_grad(const float* imp, const float* load, int E, float wi, float wl,

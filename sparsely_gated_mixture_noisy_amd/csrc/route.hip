@@ -285,6 +285,48 @@ __global__ __launch_bounds__(SCATTER_THREADS) void route_scatter_kernel(RouteArg
   }
 }
 
+// Rows of a keep mask: workgroup b places the tokens of 32-token block b.
+// Expert e's kept tokens of the block take ranks base[b][e], +1, ... in
+// token order; ranks at or past the cap take no row.
+__global__ __launch_bounds__(SCATTER_THREADS) void mask_scatter_kernel(RouteArgs a,
+                                                                       int64_t perm_len) {
+  extern __shared__ int off[];  // [E+1]
+  const int b = blockIdx.x, tid = threadIdx.x;
+  scan_counts(a.counts, a.E, off);
+  if (b == 0)
+    for (int e = tid; e <= a.E; e += SCATTER_THREADS) a.offsets[e] = off[e];
+  for (int e = tid; e < a.E; e += SCATTER_THREADS) {
+    const int64_t o = (int64_t)b * a.E + e;
+    uint32_t rest = a.bits[o];
+    int rank = a.base[o];
+    while (rest) {
+      if (a.capacity > 0 && rank >= a.capacity) break;
+      const int i = __ffs(rest) - 1;
+      rest &= rest - 1u;
+      a.perm[off[e] + rank] = b * ROUTE_BLOCK_TOKENS + i;
+      ++rank;
+    }
+  }
+  // rows no kept token took: a valid token, so row gathers stay in bounds
+  for (int64_t p = off[a.E] + (int64_t)b * SCATTER_THREADS + tid; p < perm_len;
+       p += (int64_t)gridDim.x * SCATTER_THREADS)
+    a.perm[p] = 0;
+}
+
+hipError_t launch_mask_route(const RouteArgs& a, int64_t perm_len, hipStream_t s) {
+  if (a.T == 0) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((a.E + 256) / 256), dim3(256), 0, s, a.counts, a.E, 0);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((a.E + 256) / 256), dim3(256), 0, s, a.offsets,
+                       a.E + 1, 0);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_colscan_kernel, dim3((a.E + SCAN_EXPERTS - 1) / SCAN_EXPERTS),
+                     dim3(SCAN_THREADS), 0, s, a);
+  hipLaunchKernelGGL(mask_scatter_kernel, dim3(a.NB), dim3(SCATTER_THREADS),
+                     sizeof(int) * (size_t)(a.E + 1), s, a, perm_len);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) {
     // empty batch: counts = 0, offsets = 0, no tiles

@@ -108,6 +108,32 @@ def test_static_scratch_forward_refuses_layers_too_large(lib):
         assert b"static" in lib.moe_last_error()
 
 
+def test_mask_requests_rejected_before_launch(lib):
+    """moe_forward_mask refuses the hierarchy, a capacity (rows_per_expert sets
+    the rows), rows_per_expert outside [1, tokens] and a missing workspace,
+    before touching a GPU; its workspace size is 0 for such requests."""
+    flat = CONFIGS["flat256"]
+    assert L.mask_workspace_size(flat, 128) > 0
+    p = L.moe_params(w_gate=FAKE, w_noise=FAKE, w_gate_p=FAKE, w_noise_p=FAKE, w1=FAKE, w2=FAKE)
+    n = L.moe_noise(eps=FAKE, eps_p=FAKE)
+    o = L.moe_mask_outputs(y=FAKE)
+    for cfg, m, status in ((CONFIGS["hier4096"], 4, L.MOE_ERR_UNSUPPORTED),
+                           (flat.replace(capacity=8), 8, L.MOE_ERR_INVALID_ARG),
+                           (flat, 0, L.MOE_ERR_INVALID_ARG),
+                           (flat, flat.tokens + 1, L.MOE_ERR_INVALID_ARG)):
+        assert L.mask_workspace_size(cfg, m) == 0
+        c = L.make_config(cfg)
+        assert lib.moe_forward_mask(ctypes.byref(c), FAKE, ctypes.byref(p), ctypes.byref(n), m,
+                                    None, 1.0, 1.0, ctypes.byref(o), FAKE, 1 << 40,
+                                    None) == status
+    c = L.make_config(flat)
+    assert lib.moe_forward_mask(ctypes.byref(c), FAKE, ctypes.byref(p), ctypes.byref(n), 128, None,
+                                1.0, 1.0, ctypes.byref(o), None, 0, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_mask(ctypes.byref(c), FAKE, ctypes.byref(p), ctypes.byref(n), 128, None,
+                                1.0, 1.0, ctypes.byref(o), FAKE,
+                                L.mask_workspace_size(flat, 128) - 1, None) == L.MOE_ERR_WORKSPACE
+
+
 def test_workspace_checks(lib):
     cfg = CONFIGS["flat256"]
     need = L.workspace_size(cfg)
