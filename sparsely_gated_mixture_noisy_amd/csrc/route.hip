@@ -143,7 +143,28 @@ __global__ __launch_bounds__(SCAN_THREADS) void route_colscan_kernel(RouteArgs a
   int s = 0;
   float si = 0.f, sl = 0.f;
   if (e < a.E) {
-    for (int b = b0; b < b1; ++b) {
+    // four blocks' loads in flight together; the sums still run in block order
+    int b = b0;
+    for (; b + 4 <= b1; b += 4) {
+      uint32_t wd[4];
+      float ip[4], lp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t o = (int64_t)(b + j) * a.E + e;
+        wd[j] = a.bits[o];
+        ip[j] = stats ? a.imp_part[o] : 0.f;
+        lp[j] = (stats && a.load_part) ? a.load_part[o] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s += __popc(wd[j]);
+        if (stats) {
+          si += ip[j];
+          if (a.load_part) sl += lp[j];
+        }
+      }
+    }
+    for (; b < b1; ++b) {
       const int64_t o = (int64_t)b * a.E + e;
       s += __popc(a.bits[o]);
       if (stats) {
