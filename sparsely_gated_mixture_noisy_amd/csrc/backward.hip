@@ -656,11 +656,87 @@ constexpr size_t BWD_LDS = sizeof(bf16_t) * 4 * GATE_ROWS * BWD_LD;
 // hi + lo halves (the split the separate product uses) and the transposed
 // tables: wave w takes the 32-column blocks w, w + 8, ...; an accumulator lane
 // holds four consecutive columns of one row.
-template <typename T, bool NOISY, bool XLDS, bool DXG>
+// RANK (E <= GATE_BLOCK_E, one expert block): the rank step runs here, on the
+// scores this kernel holds anyway, with the rank kernel's operations in its
+// order (one block: each wave's slot takes its half-wave's result as is), so
+// the projections are computed once instead of twice.
+__device__ __forceinline__ void rank_in_registers(const f32x16& cs, const f32x16& ss,
+                                                  const f32x16& hs, int e, int E,
+                                                  const uint32_t* sb, const BwTileShared& sh,
+                                                  const float* dload, bool smooth,
+                                                  RankBest (&wk)[GATE_WAVES][GATE_ROWS],
+                                                  RankBest (&bn)[GATE_WAVES][GATE_ROWS],
+                                                  float (&wsk)[GATE_WAVES][GATE_ROWS],
+                                                  float (&wsn)[GATE_WAVES][GATE_ROWS],
+                                                  int4* ri, int64_t t0, int64_t T) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool live = e < E;
+  const uint32_t km = live ? sb[e] : 0u;
+  const float dl = (smooth && live) ? dload[e] : 0.f;
+  // one accumulator row at a time, reduced over the half-wave and parked in
+  // LDS at once, so that nothing of it stays live across rows
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = acc_row(r, lane);
+    RankBest worst_kept{INFINITY, -1}, best_drop{-INFINITY, 0x7fffffff};
+    float s_kept = 0.f, s_drop = 0.f;
+    if (live) {
+      const bool kept = (km >> row) & 1u;
+      const RankBest cur{hs[r], e};
+      if (kept) worst_kept = cur;
+      else best_drop = cur;
+      if (smooth) {
+        const float th = kept ? sh.k1th[row] : sh.kth[row];
+        const float isp = rcp_hw(ss[r]);
+        const float z = (cs[r] - th) * isp;
+        const float dt = (z == INFINITY || z == -INFINITY) ? 0.f : -dl * normal_pdf_f(z) * isp;
+        if (kept) s_kept += dt;
+        else s_drop += dt;
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      const RankBest ok = rb_xor(worst_kept, off);
+      if (rb_before(worst_kept, ok)) worst_kept = ok;
+      const RankBest od = rb_xor(best_drop, off);
+      if (rb_before(od, best_drop)) best_drop = od;
+      s_kept += __shfl_xor(s_kept, off, 64);
+      s_drop += __shfl_xor(s_drop, off, 64);
+    }
+    if ((lane & 31) == 0) {
+      wk[w][row] = worst_kept;
+      bn[w][row] = best_drop;
+      wsk[w][row] = 0.f + s_kept;
+      wsn[w][row] = 0.f + s_drop;
+    }
+  }
+  __syncthreads();
+  if (tid < GATE_ROWS) {
+    RankBest k0 = wk[0][tid], d0 = bn[0][tid];
+    float sk = wsk[0][tid], sd = wsn[0][tid];
+    for (int i = 1; i < GATE_WAVES; ++i) {
+      if (rb_before(k0, wk[i][tid])) k0 = wk[i][tid];
+      if (rb_before(bn[i][tid], d0)) d0 = bn[i][tid];
+      sk += wsk[i][tid];
+      sd += wsn[i][tid];
+    }
+    int4 out;
+    out.x = k0.e;
+    out.y = d0.e == 0x7fffffff ? -1 : d0.e;
+    out.z = __float_as_int(sd);
+    out.w = __float_as_int(sk);
+    ri[tid] = out;
+  }
+  __syncthreads();
+}
+
+template <typename T, bool NOISY, bool XLDS, bool DXG, bool RANK = false>
 __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a) {
   __shared__ BwTileShared sh;
   __shared__ int4 ri[GATE_ROWS];
   __shared__ float dhk[GATE_ROWS][8];
+  __shared__ RankBest rk_wk[RANK ? GATE_WAVES : 1][GATE_ROWS], rk_bn[RANK ? GATE_WAVES : 1][GATE_ROWS];
+  __shared__ float rk_wsk[RANK ? GATE_WAVES : 1][GATE_ROWS], rk_wsn[RANK ? GATE_WAVES : 1][GATE_ROWS];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int xld = a.d + 8;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
@@ -679,7 +755,7 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
   if (tid < GATE_ROWS) {
     const int64_t t = min<int64_t>(t0 + tid, a.T - 1);
-    ri[tid] = reinterpret_cast<const int4*>(a.rinfo)[t];
+    if (!RANK) ri[tid] = reinterpret_cast<const int4*>(a.rinfo)[t];
 #pragma unroll
     for (int s = 0; s < 8; ++s) dhk[tid][s] = s < a.k ? a.dhk[t * a.k + s] : 0.f;
   }
@@ -690,6 +766,9 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
     f32x16 cs, ss, hs, rs, es;
     bw_block_scores<T, NOISY, XLDS>(a, sh, Xs, xld, blk, cs, ss, hs, rs, es);
     const int e = blk + w * 32 + (lane & 31);
+    if constexpr (RANK)
+      rank_in_registers(cs, ss, hs, e, a.E, sb, sh, a.dload, smooth, rk_wk, rk_bn, rk_wsk, rk_wsn, ri,
+                        t0, a.T);
     float bsum = 0.f;
     if (e < a.E) {
       const uint32_t km = sb[e];
@@ -1587,6 +1666,19 @@ static hipError_t launch_bw_gate_v(const BwGateArgs& a, hipStream_t s) {
             : bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS, false>, lds_g);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)((a.T + GATE_ROWS - 1) / GATE_ROWS));
+  if (one) {
+    // one expert block: the rank step runs inside the gradient kernel
+    err = dxg ? bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS, can_dxg, true>, lds_g)
+              : bw_set_lds(bw_gate_grad_kernel<T, NOISY, XLDS, false, true>, lds_g);
+    if (err != hipSuccess) return err;
+    if (dxg)
+      hipLaunchKernelGGL((bw_gate_grad_kernel<T, NOISY, XLDS, can_dxg, true>), grid,
+                         dim3(GATE_THREADS), lds_g, s, a);
+    else
+      hipLaunchKernelGGL((bw_gate_grad_kernel<T, NOISY, XLDS, false, true>), grid,
+                         dim3(GATE_THREADS), lds_g, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((bw_gate_rank_kernel<T, NOISY, XLDS>), grid, dim3(GATE_THREADS), lds, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

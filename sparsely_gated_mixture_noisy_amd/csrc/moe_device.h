@@ -194,19 +194,42 @@ __device__ double sum256_f64(double v) {
 // Squared coefficient of variation of v[0..E): population variance / mean^2
 // in fp64 (0 when the mean is 0).  Slot i < 256 sums v[i], v[i+256], ... in
 // order; the slots are added by sum256_f64.  Called by all NT threads.
+// A slot's values are loaded eight at a time, so that their loads are in
+// flight together; the sums keep the order above.
 template <int NT>
 __device__ double cv2_of(const float* v, int E) {
   const int tid = threadIdx.x;
   double s = 0.0;
-  if (tid < 256)
-    for (int i = tid; i < E; i += 256) s += (double)v[i];
+  if (tid < 256) {
+    int i = tid;
+    for (; i + 7 * 256 < E; i += 8 * 256) {
+      float u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = v[i + j * 256];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += (double)u[j];
+    }
+    for (; i < E; i += 256) s += (double)v[i];
+  }
   const double mean = sum256_f64<NT>(s) / E;
   double q = 0.0;
-  if (tid < 256)
-    for (int i = tid; i < E; i += 256) {
+  if (tid < 256) {
+    int i = tid;
+    for (; i + 7 * 256 < E; i += 8 * 256) {
+      float u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = v[i + j * 256];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double dv = (double)u[j] - mean;
+        q += dv * dv;
+      }
+    }
+    for (; i < E; i += 256) {
       const double dv = (double)v[i] - mean;
       q += dv * dv;
     }
+  }
   const double var = sum256_f64<NT>(q) / E;
   return mean == 0.0 ? 0.0 : var / (mean * mean);
 }
