@@ -38,7 +38,7 @@ constexpr int FZ_H = 256;     // hidden units per chunk
 constexpr int FZ_WAVES = 8;
 constexpr int FZ_THREADS = 64 * FZ_WAVES;
 constexpr int FZ_D = 512;     // d_model handled by this kernel
-constexpr int FZ_RING = 16;   // weight fragments in flight per wave
+constexpr int FZ_RING = 8;    // weight fragments in flight per wave
 
 struct FusedArgs {
   const bf16_t* x;
@@ -152,12 +152,16 @@ __device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, in
   __syncthreads();
   for (int hc = 0; hc < nchunks; ++hc) {
     const bool more = hc + 1 < nchunks;
-    // consume entry n of this chunk's stream and refill its ring slot
+    // consume entry n of this chunk's stream and refill its ring slot.  Every
+    // take issues a load: after the last chunk the refills all read this
+    // chunk's first fragment again (a cache hit), so that no load hangs on a
+    // branch and the compiler's wait counts stay at the ring's depth instead
+    // of draining it at each chunk's end.
     auto take = [&](int n) -> bf16x8 {
       const bf16x8 v = __builtin_bit_cast(bf16x8, ring[n % RING]);
       const int nn = n + RING;
       if (nn < NE) ring[n % RING] = frag(hc, nn);
-      else if (more) ring[n % RING] = frag(hc + 1, nn - NE);
+      else ring[n % RING] = frag(more ? hc + 1 : hc, more ? nn - NE : 0);
       return v;
     };
     // ---- first layer: S^T[32w .. +32 units][rows] = W1[units] X^T ----
@@ -181,6 +185,10 @@ __device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, in
       }
 #pragma unroll
       for (int i = 0; i < MB; ++i) sa[i] = mfma32(b, av[i], sa[i]);
+      // keep each k-step's refill where it is issued: left free, the
+      // scheduler sinks the refills next to their uses and the ring drains
+      // (three row blocks have no registers to spare for it and stay free)
+      __builtin_amdgcn_sched_barrier(0);
     }
     // relu -> bf16 -> S[row][unit]: register group g holds units
     // 8g + q4 .. +3 of row 32i + fr
@@ -215,6 +223,7 @@ __device__ __forceinline__ void fused_tile(const FusedArgs& a, int e, int p0, in
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NT2; ++j) acc[i][j] = mfma32(b[j], av[i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
