@@ -1248,8 +1248,9 @@ constexpr int BG_CLD_F = BG_BN + 4;   // fp32 row stride
 // (ReLU) or 3 (SwiGLU) products.  Operand kinds are template arguments: KA
 // for every A operand, KB0 for the B operands except that of product 1 (KB1).
 // The results go through LDS and leave as 16-byte row pieces.
+// (two products in slices of 32: two workgroups per compute unit)
 template <int NPROD, int KA, int KB0, int KB1, int BK>
-__global__ __launch_bounds__(256, 1) void bw_gemm_mfma_kernel(BwGemm g) {
+__global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm_mfma_kernel(BwGemm g) {
   extern __shared__ __attribute__((aligned(16))) bf16_t bw_lds[];
   using Tile = BwTileT<BK>;
   Tile* tiles = reinterpret_cast<Tile*>(bw_lds);  // [2 buffers][2 * NPROD operands]
@@ -1782,7 +1783,11 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
       hipLaunchKernelGGL(bw_gemm_f32_kernel<1>, dim3((unsigned)grid), blk, 0, s, g);
     return hipGetLastError();
   }
-  if (g.epi == BW_EPI_RELU) return launch_bw_mfma<2, BW_KB, BW_KB, BW_TB, 64>(g, grid, s);
+  // slices of 32: the two products' operand tiles take 80 KB of LDS and at
+  // most 256 registers, so that two workgroups share a compute unit (the
+  // table gradients, with K over an expert's few rows, keep slices of 64:
+  // twice the slices per tile made them slower)
+  if (g.epi == BW_EPI_RELU) return launch_bw_mfma<2, BW_KB, BW_KB, BW_TB, 32>(g, grid, s);
   if (g.epi == BW_EPI_RELU_IN) {
     if (g.a[0].kind != BW_KB || g.b[0].kind != BW_KB || g.npair != 1) return hipErrorInvalidValue;
     return launch_bw_mfma<1, BW_KB, BW_KB, BW_KB, 64>(g, grid, s);
