@@ -45,9 +45,9 @@ EXPERT_TRAFFIC = {
     "config": "flat256",
     "sources": ["sparsely_gated_mixture_noisy_amd/csrc/expert_fused.hip",
                 "sparsely_gated_mixture_noisy_amd/csrc/moe_device.h"],
-    "sources_sha256": "75d2575f862b4bfe9469aa93e5e9638e43490abd5c7267358caeeb07dcd45cf4",
-    "rdreq_128b": 4615856.857, "rdreq_64b": 3804.571, "rdreq_32b": 0.0,
-    "wrreq_64b": 524288.571,
+    "sources_sha256": "172fa33260bce3f1337df8ccca5a6b66cccaa4de8b5668aeda8cdda690b377a6",
+    "rdreq_128b": 4633014.143, "rdreq_64b": 3824.429, "rdreq_32b": 0.0,
+    "wrreq_64b": 524288.0,
 }
 
 

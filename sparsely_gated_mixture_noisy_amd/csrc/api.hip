@@ -864,7 +864,11 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
                        "backward tiles"));
     const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
     int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
-    if (big)
+    // dX on the large tiles from 128 rows per expert on average: one 256-row
+    // tile then holds most experts whole, so each of an expert's two column
+    // tiles reads its dP rows once (flat256 backward 0.849 -> 0.833 ms)
+    const bool big_dx = bf16 && A >= 128 * (int64_t)E;
+    if (big || big_dx)
       MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_big_rows(), tiles_big,
                                          nullptr, s),
                          "backward tiles"));
@@ -951,7 +955,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
                          "backward hidden"));
     }
     // dX = dP W1 (+ dB W3), per routed row
-    if (big) {
+    if (big || big_dx) {
       BwBigProduct q;
       q.a = dp;
       q.a2 = sw ? db : nullptr;
