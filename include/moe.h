@@ -422,7 +422,13 @@ size_t moe_backward_workspace_size(const moe_config* cfg);
  * gate side runs in fp32 arithmetic for both dtypes.  bf16: products on MFMA
  * with fp32 accumulation; fp32 operands (score gradients) and gate-scaled
  * output gradients are rounded to bf16 as they enter a product, the hidden
- * activation and its gradients are rounded to bf16 between products. */
+ * activation and its gradients are rounded to bf16 between products.
+ * Streams: the work is ordered on `stream`.  The expert-side products run on
+ * a second stream of the current device (created by the device's first call,
+ * non-blocking, default priority, kept until the process ends), forked from
+ * `stream` and joined back to it with events before the call's last kernel,
+ * on error paths too; calls on one device share that stream, so their
+ * expert sides run one after another. */
 moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* p,
                         const moe_noise* noise, const moe_saved* saved, const void* dy,
                         float w_importance, float w_load, moe_grads* grads, void* ws,

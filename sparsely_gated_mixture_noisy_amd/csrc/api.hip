@@ -714,6 +714,71 @@ moe_status hier_gate_backward(const moe_config* c, const BwLayout& L, const void
   return hip_status(launch_bw_expert_rowsum(r, bf16, s), "backward hierarchy tables");
 }
 
+// A second stream per device for the backward's expert side: created on the
+// device's first backward call and kept until the process ends, at the
+// default priority.  Backward calls on one device share it, so their expert
+// sides run one after another.
+constexpr int SIDE_MAX_DEVICES = 64;
+std::mutex g_side_mutex;
+hipStream_t g_side_stream[SIDE_MAX_DEVICES];
+
+moe_status side_stream(hipStream_t* out) {
+  *out = nullptr;
+  int dev = -1;
+  MOE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= SIDE_MAX_DEVICES) return MOE_OK;  // one stream, then
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  if (!g_side_stream[dev])
+    MOE_TRY(hip_status(hipStreamCreateWithFlags(&g_side_stream[dev], hipStreamNonBlocking),
+                       "hipStreamCreateWithFlags"));
+  *out = g_side_stream[dev];
+  return MOE_OK;
+}
+
+// The fork of the caller's stream onto the side stream, and the join back.
+// The caller's stream waits for the join on every return path, so that work
+// queued on it after a failed call still follows everything the call launched.
+struct SideJoin {
+  hipStream_t main, side;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  bool forked = false, recorded = false, waited = false;
+  explicit SideJoin(hipStream_t s) : main(s), side(s) {}
+  SideJoin(const SideJoin&) = delete;
+  SideJoin& operator=(const SideJoin&) = delete;
+  moe_status fork() {
+    hipStream_t t = nullptr;
+    MOE_TRY(side_stream(&t));
+    if (!t || t == main) return MOE_OK;
+    MOE_TRY(hip_status(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming), "hipEventCreate"));
+    MOE_TRY(hip_status(hipEventCreateWithFlags(&ev_join, hipEventDisableTiming), "hipEventCreate"));
+    MOE_TRY(hip_status(hipEventRecord(ev_fork, main), "hipEventRecord"));
+    MOE_TRY(hip_status(hipStreamWaitEvent(t, ev_fork, 0), "hipStreamWaitEvent"));
+    side = t;
+    forked = true;
+    return MOE_OK;
+  }
+  moe_status record() {
+    if (!forked || recorded) return MOE_OK;
+    MOE_TRY(hip_status(hipEventRecord(ev_join, side), "hipEventRecord"));
+    recorded = true;
+    return MOE_OK;
+  }
+  moe_status wait() {
+    if (!forked || waited) return MOE_OK;
+    MOE_TRY(record());
+    waited = true;
+    return hip_status(hipStreamWaitEvent(main, ev_join, 0), "hipStreamWaitEvent");
+  }
+  ~SideJoin() {
+    if (forked && !waited) {
+      if (!recorded) (void)hipEventRecord(ev_join, side);
+      (void)hipStreamWaitEvent(main, ev_join, 0);
+    }
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    if (ev_join) (void)hipEventDestroy(ev_join);
+  }
+};
+
 moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, const moe_params* p,
                        const moe_noise* n, const moe_saved* sv, const void* dy, float wi,
                        float wl, moe_grads* g, void* ws, hipStream_t s) {
@@ -731,6 +796,205 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   MOE_TRY(hip_status(launch_bw_cv2_grad(use_imp ? sv->importance : nullptr,
                                         smooth ? sv->load : nullptr, E, wi, wl, dimp, dload, s),
                      "backward cv2"));
+  // 5. experts
+  void* hid = at<void>(ws, L.hid);
+  void* dp = at<void>(ws, L.dp);
+  void* db = sw ? at<void>(ws, L.db) : nullptr;
+  void* dxs = at<void>(ws, L.dxs);
+  const int64_t hd = (int64_t)h * d;
+  // The expert side shares no buffer with the gate side (1-4) up to the dx
+  // assembly, so it runs on a second stream of the device (see side_stream)
+  // while the gate side runs on the caller's.
+  auto expert_side = [&](hipStream_t se) -> moe_status {
+    // the routed rows of x and the gate-scaled output gradients, in expert order
+    void* xs = at<void>(ws, L.xs);
+    void* dys = at<void>(ws, L.dys);
+    if (A > 0) {
+      MOE_TRY(hip_status(launch_bw_gather_rows(x, sv->perm, k, nullptr, A, d, bf16, xs, se),
+                         "backward gather x"));
+      MOE_TRY(hip_status(launch_bw_gather_rows(dy, sv->perm, k, sv->topk_gate, A, d, bf16, dys, se),
+                         "backward gather dy"));
+    }
+    // experts averaging >= 256 rows (bf16): the large-tile products
+    const bool big = bw_hidden_big_tiles(bf16, A, E);
+    if (A > 0) {
+      int32_t* tiles = at<int32_t>(ws, L.tiles);
+      MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, se),
+                         "backward tiles"));
+      const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
+      int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
+      // dX on the large tiles from 128 rows per expert on average: one 256-row
+      // tile then holds most experts whole, so each of an expert's two column
+      // tiles reads its dP rows once (flat256 backward 0.849 -> 0.833 ms)
+      const bool big_dx = bf16 && A >= 128 * (int64_t)E;
+      if (big || big_dx)
+        MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_big_rows(), tiles_big,
+                                           nullptr, se),
+                           "backward tiles"));
+      if (big) {
+        // large experts, on the forward's large-tile GEMM: dHid = dY W2 into
+        // the dP (dA) buffer, then the hidden layer recomputed with the
+        // activation's derivative applied in the epilogue
+        BwBigProduct q;
+        q.a = dys;
+        q.a2 = nullptr;
+        q.b = p->w2;
+        q.b2 = nullptr;
+        q.A = A;
+        q.E = E;
+        q.N = h;
+        q.K = d;
+        q.offsets = sv->offsets;
+        q.tiles = tiles_big;
+        q.c = dp;
+        MOE_TRY(hip_status(launch_bw_big_product(q, se), "backward dhid"));
+        BwHiddenArgs ha;
+        ha.xs = xs;
+        ha.offsets = sv->offsets;
+        ha.tiles = tiles_big;
+        ha.E = E;
+        ha.d = d;
+        ha.h = h;
+        ha.A = A;
+        ha.w1 = p->w1;
+        ha.w3 = sw ? p->w3 : nullptr;
+        ha.hid = hid;
+        ha.d1 = dp;
+        ha.d3 = db;
+        MOE_TRY(hip_status(launch_bw_hidden_big(ha, sw, se), "backward hidden"));
+      } else if (bf16 && !sw && bw_relu_split(A, E)) {
+        // dHid = dY W2 on the one-product kernel, written into dP; then X W1^T,
+        // whose epilogue applies the ReLU derivative to dHid (two launches that
+        // each fit two workgroups per compute unit)
+        BwGemm q = product(op_rows(dys, d, f32), per_expert(op_cols(p->w2, h, f32), hd));
+        q.mode = BW_POS;
+        q.M = A;
+        q.N = h;
+        q.K = d;
+        q.offsets = sv->offsets;
+        q.tiles = tiles;
+        q.E = E;
+        q.C = dp;
+        q.c_f32 = 0;
+        q.ldc = h;
+        MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), se),
+                           "backward dhid"));
+        BwGemm r = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
+        r.mode = BW_POS;
+        r.epi = BW_EPI_RELU_IN;
+        r.M = A;
+        r.N = h;
+        r.K = d;
+        r.offsets = sv->offsets;
+        r.tiles = tiles;
+        r.E = E;
+        r.C = hid;
+        r.C2 = dp;
+        r.ldc = h;
+        MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((h + 127) / 128), se),
+                           "backward hidden"));
+      } else {
+        // hidden layer recomputed with its gradient
+        BwGemm q = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
+        q.mode = BW_POS;
+        q.epi = sw ? BW_EPI_SWIGLU : BW_EPI_RELU;
+        q.a[1] = op_rows(dys, d, f32);
+        q.b[1] = per_expert(op_cols(p->w2, h, f32), hd);
+        if (sw) q.b[2] = per_expert(op_rows(p->w3, d, f32), hd);
+        q.M = A;
+        q.N = h;
+        q.K = d;
+        q.offsets = sv->offsets;
+        q.tiles = tiles;
+        q.E = E;
+        q.C = hid;
+        q.C2 = dp;
+        q.C3 = db;
+        MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), se),
+                           "backward hidden"));
+      }
+      // dX = dP W1 (+ dB W3), per routed row
+      if (big || big_dx) {
+        BwBigProduct q;
+        q.a = dp;
+        q.a2 = sw ? db : nullptr;
+        q.b = p->w1;
+        q.b2 = sw ? p->w3 : nullptr;
+        q.A = A;
+        q.E = E;
+        q.N = d;
+        q.K = h;
+        q.offsets = sv->offsets;
+        q.tiles = tiles_big;
+        q.c = dxs;
+        MOE_TRY(hip_status(launch_bw_big_product(q, se), "backward expert dx"));
+      } else {
+        BwGemm r = product(op_rows(dp, h, f32), per_expert(op_cols(p->w1, d, f32), hd));
+        r.mode = BW_POS;
+        if (sw) add_pair(r, op_rows(db, h, f32), per_expert(op_cols(p->w3, d, f32), hd));
+        r.M = A;
+        r.N = d;
+        r.K = h;
+        r.offsets = sv->offsets;
+        r.tiles = tiles;
+        r.E = E;
+        r.C = dxs;
+        r.c_f32 = f32 ? 1 : 0;  // in the layer dtype, like the expert outputs
+        r.ldc = d;
+        MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((d + 127) / 128), se),
+                           "backward expert dx"));
+      }
+    }
+    // table gradients, one problem per expert over its rows (zero without rows)
+    auto wgrad = [&](void* out, BwOp a, BwOp b, int64_t M, int64_t N, const char* what) {
+      if (!out) return MOE_OK;
+      BwGemm q = product(a, b);
+      q.mode = BW_WGT;
+      q.M = M;
+      q.N = N;
+      q.offsets = sv->offsets;
+      q.E = E;
+      q.C = out;
+      q.c_f32 = f32 ? 1 : 0;
+      q.ldc = N;
+      q.c_estride = M * N;
+      const int64_t grid = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
+      return hip_status(launch_bw_gemm(q, bf16, grid, se), what);
+    };
+    if (big) {
+      // positions past an expert's rows are read from a row of zeros
+      void* zero = at<void>(ws, L.zero);
+      MOE_TRY(hip_status(launch_fill_i32((int32_t*)zero, std::max(h, d) / 2, 0, se),
+                         "backward zero row"));
+      auto wgrad_big = [&](void* out, const void* a, int M, const void* b, int N,
+                           const char* what) {
+        if (!out) return MOE_OK;
+        BwBigWgrad q;
+        q.a = a;
+        q.b = b;
+        q.E = E;
+        q.M = M;
+        q.N = N;
+        q.offsets = sv->offsets;
+        q.zero = zero;
+        q.c = out;
+        return hip_status(launch_bw_big_wgrad(q, se), what);
+      };
+      MOE_TRY(wgrad_big(g->dw1, dp, h, xs, d, "backward dw1"));
+      if (sw) MOE_TRY(wgrad_big(g->dw3, db, h, xs, d, "backward dw3"));
+      MOE_TRY(wgrad_big(g->dw2, dys, d, hid, h, "backward dw2"));
+    } else {
+      MOE_TRY(wgrad(g->dw1, op_cols(dp, h, f32), op_cols(xs, d, f32), h, d, "backward dw1"));
+      if (sw)
+        MOE_TRY(wgrad(g->dw3, op_cols(db, h, f32), op_cols(xs, d, f32), h, d, "backward dw3"));
+      MOE_TRY(wgrad(g->dw2, op_cols(dys, d, f32), op_cols(hid, h, f32), d, h, "backward dw2"));
+    }
+    return MOE_OK;
+  };
+  SideJoin join(s);
+  MOE_TRY(join.fork());
+  MOE_TRY(expert_side(join.side));
+  MOE_TRY(join.record());
   float* dxg = at<float>(ws, L.dxg);
   if (c->n_groups > 0) {
     MOE_TRY(hier_gate_backward(c, L, x, p, n, sv, dy, use_imp ? dimp : nullptr, g, ws, s));
@@ -841,196 +1105,8 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
       MOE_TRY(gate_table_grad(c, L, x, draw, E, g->dw_noise, at<float>(ws, L.part_n), s));
   }
   }
-  // 5. experts
-  void* hid = at<void>(ws, L.hid);
-  void* dp = at<void>(ws, L.dp);
-  void* db = sw ? at<void>(ws, L.db) : nullptr;
-  void* dxs = at<void>(ws, L.dxs);
-  const int64_t hd = (int64_t)h * d;
-  // the routed rows of x and the gate-scaled output gradients, in expert order
-  void* xs = at<void>(ws, L.xs);
-  void* dys = at<void>(ws, L.dys);
-  if (A > 0) {
-    MOE_TRY(hip_status(launch_bw_gather_rows(x, sv->perm, k, nullptr, A, d, bf16, xs, s),
-                       "backward gather x"));
-    MOE_TRY(hip_status(launch_bw_gather_rows(dy, sv->perm, k, sv->topk_gate, A, d, bf16, dys, s),
-                       "backward gather dy"));
-  }
-  // experts averaging >= 256 rows (bf16): the large-tile products
-  const bool big = bw_hidden_big_tiles(bf16, A, E);
-  if (A > 0) {
-    int32_t* tiles = at<int32_t>(ws, L.tiles);
-    MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, s),
-                       "backward tiles"));
-    const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
-    int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
-    // dX on the large tiles from 128 rows per expert on average: one 256-row
-    // tile then holds most experts whole, so each of an expert's two column
-    // tiles reads its dP rows once (flat256 backward 0.849 -> 0.833 ms)
-    const bool big_dx = bf16 && A >= 128 * (int64_t)E;
-    if (big || big_dx)
-      MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_big_rows(), tiles_big,
-                                         nullptr, s),
-                         "backward tiles"));
-    if (big) {
-      // large experts, on the forward's large-tile GEMM: dHid = dY W2 into
-      // the dP (dA) buffer, then the hidden layer recomputed with the
-      // activation's derivative applied in the epilogue
-      BwBigProduct q;
-      q.a = dys;
-      q.a2 = nullptr;
-      q.b = p->w2;
-      q.b2 = nullptr;
-      q.A = A;
-      q.E = E;
-      q.N = h;
-      q.K = d;
-      q.offsets = sv->offsets;
-      q.tiles = tiles_big;
-      q.c = dp;
-      MOE_TRY(hip_status(launch_bw_big_product(q, s), "backward dhid"));
-      BwHiddenArgs ha;
-      ha.xs = xs;
-      ha.offsets = sv->offsets;
-      ha.tiles = tiles_big;
-      ha.E = E;
-      ha.d = d;
-      ha.h = h;
-      ha.A = A;
-      ha.w1 = p->w1;
-      ha.w3 = sw ? p->w3 : nullptr;
-      ha.hid = hid;
-      ha.d1 = dp;
-      ha.d3 = db;
-      MOE_TRY(hip_status(launch_bw_hidden_big(ha, sw, s), "backward hidden"));
-    } else if (bf16 && !sw && bw_relu_split(A, E)) {
-      // dHid = dY W2 on the one-product kernel, written into dP; then X W1^T,
-      // whose epilogue applies the ReLU derivative to dHid (two launches that
-      // each fit two workgroups per compute unit)
-      BwGemm q = product(op_rows(dys, d, f32), per_expert(op_cols(p->w2, h, f32), hd));
-      q.mode = BW_POS;
-      q.M = A;
-      q.N = h;
-      q.K = d;
-      q.offsets = sv->offsets;
-      q.tiles = tiles;
-      q.E = E;
-      q.C = dp;
-      q.c_f32 = 0;
-      q.ldc = h;
-      MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
-                         "backward dhid"));
-      BwGemm r = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
-      r.mode = BW_POS;
-      r.epi = BW_EPI_RELU_IN;
-      r.M = A;
-      r.N = h;
-      r.K = d;
-      r.offsets = sv->offsets;
-      r.tiles = tiles;
-      r.E = E;
-      r.C = hid;
-      r.C2 = dp;
-      r.ldc = h;
-      MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((h + 127) / 128), s),
-                         "backward hidden"));
-    } else {
-      // hidden layer recomputed with its gradient
-      BwGemm q = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
-      q.mode = BW_POS;
-      q.epi = sw ? BW_EPI_SWIGLU : BW_EPI_RELU;
-      q.a[1] = op_rows(dys, d, f32);
-      q.b[1] = per_expert(op_cols(p->w2, h, f32), hd);
-      if (sw) q.b[2] = per_expert(op_rows(p->w3, d, f32), hd);
-      q.M = A;
-      q.N = h;
-      q.K = d;
-      q.offsets = sv->offsets;
-      q.tiles = tiles;
-      q.E = E;
-      q.C = hid;
-      q.C2 = dp;
-      q.C3 = db;
-      MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), s),
-                         "backward hidden"));
-    }
-    // dX = dP W1 (+ dB W3), per routed row
-    if (big || big_dx) {
-      BwBigProduct q;
-      q.a = dp;
-      q.a2 = sw ? db : nullptr;
-      q.b = p->w1;
-      q.b2 = sw ? p->w3 : nullptr;
-      q.A = A;
-      q.E = E;
-      q.N = d;
-      q.K = h;
-      q.offsets = sv->offsets;
-      q.tiles = tiles_big;
-      q.c = dxs;
-      MOE_TRY(hip_status(launch_bw_big_product(q, s), "backward expert dx"));
-    } else {
-      BwGemm r = product(op_rows(dp, h, f32), per_expert(op_cols(p->w1, d, f32), hd));
-      r.mode = BW_POS;
-      if (sw) add_pair(r, op_rows(db, h, f32), per_expert(op_cols(p->w3, d, f32), hd));
-      r.M = A;
-      r.N = d;
-      r.K = h;
-      r.offsets = sv->offsets;
-      r.tiles = tiles;
-      r.E = E;
-      r.C = dxs;
-      r.c_f32 = f32 ? 1 : 0;  // in the layer dtype, like the expert outputs
-      r.ldc = d;
-      MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((d + 127) / 128), s),
-                         "backward expert dx"));
-    }
-  }
-  // table gradients, one problem per expert over its rows (zero without rows)
-  auto wgrad = [&](void* out, BwOp a, BwOp b, int64_t M, int64_t N, const char* what) {
-    if (!out) return MOE_OK;
-    BwGemm q = product(a, b);
-    q.mode = BW_WGT;
-    q.M = M;
-    q.N = N;
-    q.offsets = sv->offsets;
-    q.E = E;
-    q.C = out;
-    q.c_f32 = f32 ? 1 : 0;
-    q.ldc = N;
-    q.c_estride = M * N;
-    const int64_t grid = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
-    return hip_status(launch_bw_gemm(q, bf16, grid, s), what);
-  };
-  if (big) {
-    // positions past an expert's rows are read from a row of zeros
-    void* zero = at<void>(ws, L.zero);
-    MOE_TRY(hip_status(launch_fill_i32((int32_t*)zero, std::max(h, d) / 2, 0, s),
-                       "backward zero row"));
-    auto wgrad_big = [&](void* out, const void* a, int M, const void* b, int N,
-                         const char* what) {
-      if (!out) return MOE_OK;
-      BwBigWgrad q;
-      q.a = a;
-      q.b = b;
-      q.E = E;
-      q.M = M;
-      q.N = N;
-      q.offsets = sv->offsets;
-      q.zero = zero;
-      q.c = out;
-      return hip_status(launch_bw_big_wgrad(q, s), what);
-    };
-    MOE_TRY(wgrad_big(g->dw1, dp, h, xs, d, "backward dw1"));
-    if (sw) MOE_TRY(wgrad_big(g->dw3, db, h, xs, d, "backward dw3"));
-    MOE_TRY(wgrad_big(g->dw2, dys, d, hid, h, "backward dw2"));
-  } else {
-    MOE_TRY(wgrad(g->dw1, op_cols(dp, h, f32), op_cols(xs, d, f32), h, d, "backward dw1"));
-    if (sw)
-      MOE_TRY(wgrad(g->dw3, op_cols(db, h, f32), op_cols(xs, d, f32), h, d, "backward dw3"));
-    MOE_TRY(wgrad(g->dw2, op_cols(dys, d, f32), op_cols(hid, h, f32), d, h, "backward dw2"));
-  }
-  // 6. dx
+  // 6. dx, once the expert side is done
+  MOE_TRY(join.wait());
   if (T > 0)
     MOE_TRY(hip_status(launch_bw_assemble_dx(dxg, dxs, sv->inv, T, k, d, bf16, g->dx, s),
                        "backward dx"));
