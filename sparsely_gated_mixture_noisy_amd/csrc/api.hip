@@ -305,7 +305,10 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   r.perm = at<int32_t>(ws, L.perm_g);
   r.inv = at<int32_t>(ws, L.inv_g);
   int32_t* tiles_g = at<int32_t>(ws, L.tiles_g);
-  r.tile_rows = 32;  // the secondary gate's row tiles
+  // the secondary gate's row tiles (64 rows once the groups average as many:
+  // each table fragment fetched from L2 then serves twice the rows)
+  const int grows = gate_group_tile_rows(c->dtype == MOE_BF16, c->d_model, c->tokens * kg, G);
+  r.tile_rows = grows;
   r.tiles = tiles_g;
   r.desc = nullptr;
   MOE_TRY(hip_status(launch_route(r, s), "group routing"));
@@ -327,7 +330,8 @@ moe_status do_gate(const moe_config* c, const Layout& L, const void* x, const mo
   ga.gate = gate;
   ga.w_pack = p->w_gate_packed;
   ga.pack_nt = gate_pack_tables(c);
-  const int64_t grid = (c->tokens * kg + 31) / 32 + G;
+  ga.tile_rows = grows;
+  const int64_t grid = (c->tokens * kg + grows - 1) / grows + G;
   return hip_status(launch_gate_group(ga, (int)grid, bf16, s), "secondary gate");
 }
 

@@ -340,11 +340,11 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_flat_kernel(GateFlatArgs a)
 // Writes the final experts g*Eg + j and gates gate_p * gate_s directly.
 // Dynamic LDS: input tile (XLDS), score block Hs[32][HLD].
 // ---------------------------------------------------------------------------
-template <typename T, int K1, bool NOISY, bool XLDS>
+template <typename T, int K1, bool NOISY, bool XLDS, int RB>
 __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs a) {
-  constexpr int TPR = GateTile<1>::TPR;
-  __shared__ int rows[GATE_ROWS];
-  __shared__ int asg[GATE_ROWS];
+  constexpr int TPR = GateTile<RB>::TPR, R = GateTile<RB>::R;
+  __shared__ int rows[R];
+  __shared__ int asg[R];
   __shared__ int s_g, s_p0, s_n;
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int tid = threadIdx.x;
@@ -354,26 +354,26 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
       if (q >= a.tiles_g[i] && q < a.tiles_g[i + 1]) g = i;
     s_g = g;
     if (g >= 0) {
-      int p0 = a.offsets_g[g] + GATE_ROWS * (q - a.tiles_g[g]);
+      int p0 = a.offsets_g[g] + R * (q - a.tiles_g[g]);
       s_p0 = p0;
-      s_n = min(GATE_ROWS, a.offsets_g[g + 1] - p0);
+      s_n = min(R, a.offsets_g[g + 1] - p0);
     }
   }
   __syncthreads();
   const int g = s_g;
   if (g < 0) return;
   const int p0 = s_p0, n = s_n;
-  if (tid < GATE_ROWS) {
+  if (tid < R) {
     int as = a.perm_g[p0 + min(tid, n - 1)];
     asg[tid] = as;
     rows[tid] = as / a.kg;
   }
   __syncthreads();
   const int xld = a.d + 8;
-  const size_t xbytes = XLDS ? sizeof(bf16_t) * GATE_ROWS * xld : 0;
+  const size_t xbytes = XLDS ? sizeof(bf16_t) * R * xld : 0;
   bf16_t* Xs = reinterpret_cast<bf16_t*>(dyn);
   float* Hs = reinterpret_cast<float*>(dyn + xbytes);
-  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, GATE_ROWS, Xs, xld);
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, rows, R, Xs, xld);
   __syncthreads();
   const TileX<T> tx{(const T*)a.x, rows, XLDS ? Xs : nullptr, xld};
   const int Eg = a.Eg, G = a.G;
@@ -383,10 +383,10 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_group_kernel(GateGroupArgs 
   };
   float ov[K1];
   int oe[K1];
-  f32x16 cs[1], ss[1];
+  f32x16 cs[RB], ss[RB];
   const GateTabs tb{a.w_gate, a.w_noise, g * Eg, (const bf16_t*)a.w_pack,
                     g * ((Eg + 31) / 32), a.pack_nt};
-  score_tile<T, K1, NOISY, XLDS, 1>(tx, a.d, tb, nullptr, Eg, eps_row, Hs, ov, oe, cs, ss);
+  score_tile<T, K1, NOISY, XLDS, RB>(tx, a.d, tb, nullptr, Eg, eps_row, Hs, ov, oe, cs, ss);
   const int row = tid / TPR;
   if (tid % TPR == 0 && row < n) {
     int ke[K1];
@@ -555,14 +555,28 @@ hipError_t launch_gate_flat(const GateFlatArgs& a, bool bf16, hipStream_t s) {
   return bf16 ? launch_flat_t<bf16_t>(a, s) : launch_flat_t<float>(a, s);
 }
 
-template <typename T, int K1, bool NOISY, bool XLDS>
-static hipError_t launch_group_v(const GateGroupArgs& a, int grid, size_t sh, hipStream_t s) {
+template <typename T, int K1, bool NOISY, bool XLDS, int RB>
+static hipError_t launch_group_r(const GateGroupArgs& a, int grid, hipStream_t s) {
+  const size_t sh = xtile_bytes(sizeof(T) == 2, a.d, 32 * RB) + sizeof(float) * 32 * RB * HLD;
   static size_t granted = 0;
-  hipError_t err = set_lds(gate_group_kernel<T, K1, NOISY, XLDS>, sh, &granted);
+  hipError_t err = set_lds(gate_group_kernel<T, K1, NOISY, XLDS, RB>, sh, &granted);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gate_group_kernel<T, K1, NOISY, XLDS>), dim3(grid), dim3(GATE_THREADS), sh,
-                     s, a);
+  hipLaunchKernelGGL((gate_group_kernel<T, K1, NOISY, XLDS, RB>), dim3(grid), dim3(GATE_THREADS),
+                     sh, s, a);
   return hipGetLastError();
+}
+
+// 64-row tiles (RB = 2) when the launch asks for them (bf16 with the input
+// tile in LDS, see gate_group_tile_rows): every table fragment fetched then
+// serves twice the rows
+template <typename T, int K1, bool NOISY, bool XLDS>
+static hipError_t launch_group_v(const GateGroupArgs& a, int grid, size_t, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && XLDS) {
+    if (a.tile_rows == 64) return launch_group_r<T, K1, NOISY, XLDS, 2>(a, grid, s);
+  } else {
+    if (a.tile_rows != 32) return hipErrorInvalidValue;
+  }
+  return launch_group_r<T, K1, NOISY, XLDS, 1>(a, grid, s);
 }
 
 template <typename T, int K1>
@@ -585,8 +599,13 @@ static hipError_t launch_group_t(const GateGroupArgs& a, int grid, hipStream_t s
   return launch_group_k<T, 9>(a, grid, sh, s);
 }
 
+int gate_group_tile_rows(bool bf16, int d, int64_t rows, int G) {
+  return bf16 && xtile_in_lds(true, d) && rows >= 64 * (int64_t)G ? 64 : 32;
+}
+
 hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStream_t s) {
   if (grid == 0) return hipSuccess;
+  if (a.tile_rows != 32 && a.tile_rows != 64) return hipErrorInvalidValue;
   return bf16 ? launch_group_t<bf16_t>(a, grid, s) : launch_group_t<float>(a, grid, s);
 }
 

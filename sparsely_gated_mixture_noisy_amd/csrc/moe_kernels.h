@@ -43,7 +43,8 @@ struct GateGroupArgs {
   int d, G, Eg, kg, kpg;
   const int32_t* perm_g;     // group routing of the primary selection
   const int32_t* offsets_g;  // [G+1]
-  const int32_t* tiles_g;    // [G+1], 32-row tiles per group (exclusive scan)
+  const int32_t* tiles_g;    // [G+1], tile_rows-row tiles per group (exclusive scan)
+  int tile_rows = 32;        // 32 or 64
   const float* gate_p;       // [T][kg] primary gates
   int32_t* idx;              // [T][kg*kpg] final experts
   float* gate;               // [T][kg*kpg] final gates
@@ -51,6 +52,10 @@ struct GateGroupArgs {
   int pack_nt = 0;
 };
 hipError_t launch_gate_group(const GateGroupArgs& a, int grid, bool bf16, hipStream_t s);
+// Row tile of the secondary gate for `rows` (token, kept group) pairs over G
+// groups: 64 for bf16 layers whose input tile fits LDS once the groups
+// average 64 rows, else 32.  The group routing's tile map takes the same.
+int gate_group_tile_rows(bool bf16, int d, int64_t rows, int G);
 
 struct LoadArgs {
   const void* x;
