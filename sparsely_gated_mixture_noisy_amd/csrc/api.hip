@@ -794,12 +794,6 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   const bool sw = c->ffn == MOE_FFN_SWIGLU;
   float* dimp = at<float>(ws, L.dimp);
   float* dload = at<float>(ws, L.dload);
-  // 1. CV^2 gradients of the two balance losses
-  const bool use_imp = wi != 0.f && T > 0;
-  const bool smooth = noisy && wl != 0.f && T > 0;
-  MOE_TRY(hip_status(launch_bw_cv2_grad(use_imp ? sv->importance : nullptr,
-                                        smooth ? sv->load : nullptr, E, wi, wl, dimp, dload, s),
-                     "backward cv2"));
   // 5. experts
   void* hid = at<void>(ws, L.hid);
   void* dp = at<void>(ws, L.dp);
@@ -999,6 +993,12 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
   MOE_TRY(join.fork());
   MOE_TRY(expert_side(join.side));
   MOE_TRY(join.record());
+  // 1. CV^2 gradients of the two balance losses
+  const bool use_imp = wi != 0.f && T > 0;
+  const bool smooth = noisy && wl != 0.f && T > 0;
+  MOE_TRY(hip_status(launch_bw_cv2_grad(use_imp ? sv->importance : nullptr,
+                                        smooth ? sv->load : nullptr, E, wi, wl, dimp, dload, s),
+                     "backward cv2"));
   float* dxg = at<float>(ws, L.dxg);
   if (c->n_groups > 0) {
     MOE_TRY(hier_gate_backward(c, L, x, p, n, sv, dy, use_imp ? dimp : nullptr, g, ws, s));

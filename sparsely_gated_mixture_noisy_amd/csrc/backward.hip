@@ -940,30 +940,48 @@ __global__ __launch_bounds__(256) void bw_gather_rows_kernel(const T* src, const
   *reinterpret_cast<u32x4*>(out + p * d + c) = o;
 }
 
-// dx[t][c] = dx_gate[t][c] + sum_s dxs[inv[t*k+s]][c], slots in order; four
-// columns per thread (d % 4 == 0)
+// dx[t][c] = dx_gate[t][c] + sum_s dxs[inv[t*k+s]][c], slots in order; 16
+// bytes of dx per thread (8 bf16 or 4 fp32 columns; d a multiple of that),
+// the token's k <= 8 slot positions loaded before the rows
 template <typename TO>
 __global__ __launch_bounds__(256) void bw_assemble_dx_kernel(const float* dxg, const TO* dxs,
                                                              const int32_t* inv, int64_t T, int k,
-                                                             int d, TO* dx) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+                                                             int d, TO* dx, bool vec_out) {
+  constexpr int V = 16 / sizeof(TO);
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
   if (i >= T * d) return;
   const int64_t t = i / d;
   const int c = (int)(i % d);
-  float4 v = *reinterpret_cast<const float4*>(dxg + i);
-  for (int s = 0; s < k; ++s) {
-    const int p = inv[t * k + s];
-    if (p < 0) continue;  // dropped by a capacity
-    const TO* r = dxs + (int64_t)p * d + c;
-    v.x += Elem<TO>::load(r, 0);
-    v.y += Elem<TO>::load(r, 1);
-    v.z += Elem<TO>::load(r, 2);
-    v.w += Elem<TO>::load(r, 3);
+  int rows[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) rows[s] = s < k ? inv[t * k + s] : -1;
+  float v[V];
+#pragma unroll
+  for (int j = 0; j < V; j += 4) {
+    const float4 q = *reinterpret_cast<const float4*>(dxg + i + j);
+    v[j] = q.x;
+    v[j + 1] = q.y;
+    v[j + 2] = q.z;
+    v[j + 3] = q.w;
   }
-  Elem<TO>::store(dx, i, v.x);
-  Elem<TO>::store(dx, i + 1, v.y);
-  Elem<TO>::store(dx, i + 2, v.z);
-  Elem<TO>::store(dx, i + 3, v.w);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (rows[s] < 0) continue;  // no slot, or dropped by a capacity
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(dxs + (int64_t)rows[s] * d + c);
+    const TO* r = reinterpret_cast<const TO*>(&raw);
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] += Elem<TO>::load(r, j);
+  }
+  if (vec_out) {
+    u32x4 out;
+    TO* o = reinterpret_cast<TO*>(&out);
+#pragma unroll
+    for (int j = 0; j < V; ++j) Elem<TO>::store(o, j, v[j]);
+    *reinterpret_cast<u32x4*>(dx + i) = out;
+  } else {  // dx not 16-byte aligned
+#pragma unroll
+    for (int j = 0; j < V; ++j) Elem<TO>::store(dx, i + j, v[j]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1729,15 +1747,18 @@ hipError_t launch_bw_sum_chunks(const float* part, int nchunk, int64_t n, bool b
 
 hipError_t launch_bw_assemble_dx(const float* dxg, const void* dxs, const int32_t* inv, int64_t T,
                                  int k, int d, bool bf16, void* dx, hipStream_t s) {
-  const int64_t n = T * d / 4;
+  const int V = bf16 ? 8 : 4;  // columns per thread
+  if (d % V != 0 || k > 8) return hipErrorInvalidValue;
+  const int64_t n = T * d / V;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
+  const bool vec_out = (reinterpret_cast<uintptr_t>(dx) & 15) == 0;
   if (bf16)
     hipLaunchKernelGGL(bw_assemble_dx_kernel<bf16_t>, grid, dim3(256), 0, s, dxg,
-                       (const bf16_t*)dxs, inv, T, k, d, (bf16_t*)dx);
+                       (const bf16_t*)dxs, inv, T, k, d, (bf16_t*)dx, vec_out);
   else
     hipLaunchKernelGGL(bw_assemble_dx_kernel<float>, grid, dim3(256), 0, s, dxg,
-                       (const float*)dxs, inv, T, k, d, (float*)dx);
+                       (const float*)dxs, inv, T, k, d, (float*)dx, vec_out);
   return hipGetLastError();
 }
 
