@@ -544,13 +544,6 @@ BwLayout bw_layout(const moe_config* c) {
   return L;
 }
 
-// The ReLU hidden layer of the backward as two one-product launches when the
-// experts average fewer than 64 rows: the one-product kernel fits two
-// workgroups per compute unit where the fused two-product one fits one, which
-// pays where the tiles are mostly short experts' rows (hier4096 6.91 -> 6.52
-// ms, zipf2048 5.93 -> 5.78 ms; the same at flat256's 128 rows)
-static bool bw_relu_split(int64_t A, int E) { return A > 0 && A < 64 * (int64_t)E; }
-
 // Operands: rows (element (r, k) at r*ld + k) or columns (at k*ld + r).
 BwOp op_rows(const void* ptr, int64_t ld, bool f32) {
   BwOp o;
@@ -860,37 +853,6 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
         ha.d1 = dp;
         ha.d3 = db;
         MOE_TRY(hip_status(launch_bw_hidden_big(ha, sw, se), "backward hidden"));
-      } else if (bf16 && !sw && bw_relu_split(A, E)) {
-        // dHid = dY W2 on the one-product kernel, written into dP; then X W1^T,
-        // whose epilogue applies the ReLU derivative to dHid (two launches that
-        // each fit two workgroups per compute unit)
-        BwGemm q = product(op_rows(dys, d, f32), per_expert(op_cols(p->w2, h, f32), hd));
-        q.mode = BW_POS;
-        q.M = A;
-        q.N = h;
-        q.K = d;
-        q.offsets = sv->offsets;
-        q.tiles = tiles;
-        q.E = E;
-        q.C = dp;
-        q.c_f32 = 0;
-        q.ldc = h;
-        MOE_TRY(hip_status(launch_bw_gemm(q, bf16, row_tiles * ((h + 127) / 128), se),
-                           "backward dhid"));
-        BwGemm r = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
-        r.mode = BW_POS;
-        r.epi = BW_EPI_RELU_IN;
-        r.M = A;
-        r.N = h;
-        r.K = d;
-        r.offsets = sv->offsets;
-        r.tiles = tiles;
-        r.E = E;
-        r.C = hid;
-        r.C2 = dp;
-        r.ldc = h;
-        MOE_TRY(hip_status(launch_bw_gemm(r, bf16, row_tiles * ((h + 127) / 128), se),
-                           "backward hidden"));
       } else {
         // hidden layer recomputed with its gradient
         BwGemm q = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));

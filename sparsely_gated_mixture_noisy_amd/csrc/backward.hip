@@ -1356,40 +1356,7 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
   // consecutive columns of one row
   const int erow = lane & 31, ecol = 4 * (lane >> 5);
   if constexpr (NPROD == 1) {
-    if (g.epi == BW_EPI_RELU_IN) {
-      // the pre-activation a meets this tile's dHid: Hid = relu(a), dP =
-      // dHid * (a > 0), both bf16 [A][ldc]; dP overwrites dHid in place
-      float (*Cs)[BG_CLD_F] = reinterpret_cast<float (*)[BG_CLD_F]>(bw_lds);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<float4*>(&Cs[wm * 64 + i * 32 + erow][wn * 64 + j * 32 + 8 * q + ecol]) =
-                float4{acc[0][i][j][4 * q], acc[0][i][j][4 * q + 1], acc[0][i][j][4 * q + 2],
-                       acc[0][i][j][4 * q + 3]};
-      __syncthreads();
-      bf16_t* hid = (bf16_t*)g.C;
-      bf16_t* dp = (bf16_t*)g.C2;
-      for (int c = tid; c < BG_BM * (BG_BN / 4); c += 256) {
-        const int rr = c / (BG_BN / 4), cc = (c % (BG_BN / 4)) * 4;
-        const int64_t m = t.m0 + rr, n = t.n0 + cc;
-        if (m < t.M && n < t.N) {
-          const float4 a = *reinterpret_cast<const float4*>(&Cs[rr][cc]);
-          const int64_t o = m * g.ldc + n;
-          const uint2 u = *reinterpret_cast<const uint2*>(dp + o);
-          const float d0 = __uint_as_float(u.x << 16), d1 = __uint_as_float(u.x & 0xffff0000u);
-          const float d2 = __uint_as_float(u.y << 16), d3 = __uint_as_float(u.y & 0xffff0000u);
-          *reinterpret_cast<uint2*>(hid + o) =
-              uint2{cvt_pk_bf16(fmaxf(a.x, 0.f), fmaxf(a.y, 0.f)),
-                    cvt_pk_bf16(fmaxf(a.z, 0.f), fmaxf(a.w, 0.f))};
-          *reinterpret_cast<uint2*>(dp + o) =
-              uint2{cvt_pk_bf16(a.x > 0.f ? d0 : 0.f, a.y > 0.f ? d1 : 0.f),
-                    cvt_pk_bf16(a.z > 0.f ? d2 : 0.f, a.w > 0.f ? d3 : 0.f)};
-        }
-      }
-    } else if (g.c_f32) {
+    if (g.c_f32) {
       float (*Cs)[BG_CLD_F] = reinterpret_cast<float (*)[BG_CLD_F]>(bw_lds);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -1809,10 +1776,6 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
   // table gradients, with K over an expert's few rows, keep slices of 64:
   // twice the slices per tile made them slower)
   if (g.epi == BW_EPI_RELU) return launch_bw_mfma<2, BW_KB, BW_KB, BW_TB, 32>(g, grid, s);
-  if (g.epi == BW_EPI_RELU_IN) {
-    if (g.a[0].kind != BW_KB || g.b[0].kind != BW_KB || g.npair != 1) return hipErrorInvalidValue;
-    return launch_bw_mfma<1, BW_KB, BW_KB, BW_KB, 64>(g, grid, s);
-  }
   if (g.epi == BW_EPI_SWIGLU) return launch_bw_mfma<3, BW_KB, BW_KB, BW_TB, 32>(g, grid, s);
   const int ka = g.a[0].kind, kb = g.b[0].kind;
   if (kb != BW_TB) return hipErrorInvalidValue;
