@@ -1267,11 +1267,14 @@ constexpr int BG_CLD_F = BG_BN + 4;   // fp32 row stride
 // for every A operand, KB0 for the B operands except that of product 1 (KB1).
 // The results go through LDS and leave as 16-byte row pieces.
 // (two products in slices of 32: two workgroups per compute unit)
-template <int NPROD, int KA, int KB0, int KB1, int BK>
+// NB = 1: one LDS buffer, the next slice written once every wave has read the
+// current one (table gradients of experts with a few rows, mostly one slice:
+// the smaller LDS fits more workgroups per compute unit)
+template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2>
 __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm_mfma_kernel(BwGemm g) {
   extern __shared__ __attribute__((aligned(16))) bf16_t bw_lds[];
   using Tile = BwTileT<BK>;
-  Tile* tiles = reinterpret_cast<Tile*>(bw_lds);  // [2 buffers][2 * NPROD operands]
+  Tile* tiles = reinterpret_cast<Tile*>(bw_lds);  // [NB buffers][2 * NPROD operands]
   BwTile t;
   if (!bw_tile_of(g, &t)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1320,9 +1323,9 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
     put_all(tiles);
     __syncthreads();
     for (int64_t s = 0; s < nk; ++s) {
-      const int cur = (int)(s & 1);
+      const int cur = NB == 2 ? (int)(s & 1) : 0;
       Tile* T0 = tiles + cur * 2 * NPROD;
-      Tile* T1 = tiles + (cur ^ 1) * 2 * NPROD;
+      Tile* T1 = tiles + (NB == 2 ? cur ^ 1 : 0) * 2 * NPROD;
       const bool more = s + 1 < nk;
       if (more) load_all(t.k0 + (s + 1) * BK);
 #pragma unroll
@@ -1346,7 +1349,10 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
             for (int j = 0; j < 2; ++j) acc[p][i][j] = mfma32(bf[j], af[i], acc[p][i][j]);
         }
       }
-      if (more) put_all(T1);
+      if (more) {
+        if constexpr (NB == 1) __syncthreads();  // every wave is done with T0
+        put_all(T1);
+      }
       __syncthreads();
     }
   }
@@ -1446,11 +1452,12 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
   }
 }
 
-template <int NPROD, int BK>
+// NB = 1 serves bf16 outputs only, so its output tile is bf16 too
+template <int NPROD, int BK, int NB = 2>
 static size_t bw_gemm_lds() {
-  const size_t ops = sizeof(bf16_t) * 2 * 2 * NPROD * BG_BM * (BK + 8);
-  const size_t outs = NPROD == 1 ? sizeof(float) * BG_BM * BG_CLD_F
-                                 : sizeof(bf16_t) * NPROD * BG_BM * BG_CLD_B;
+  const size_t ops = sizeof(bf16_t) * NB * 2 * NPROD * BG_BM * (BK + 8);
+  const size_t outs = NPROD == 1 && NB == 2 ? sizeof(float) * BG_BM * BG_CLD_F
+                                            : sizeof(bf16_t) * NPROD * BG_BM * BG_CLD_B;
   return ops > outs ? ops : outs;
 }
 
@@ -1744,10 +1751,10 @@ hipError_t launch_bw_gather_rows(const void* src, const int32_t* perm, int k, co
 
 int bw_tile_rows() { return BG_BM; }
 
-template <int NPROD, int KA, int KB0, int KB1, int BK>
+template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2>
 static hipError_t launch_bw_mfma(const BwGemm& g, int64_t grid, hipStream_t s) {
-  auto kern = bw_gemm_mfma_kernel<NPROD, KA, KB0, KB1, BK>;
-  const size_t lds = bw_gemm_lds<NPROD, BK>();
+  auto kern = bw_gemm_mfma_kernel<NPROD, KA, KB0, KB1, BK, NB>;
+  const size_t lds = bw_gemm_lds<NPROD, BK, NB>();
   hipError_t err = bw_set_lds(kern, lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, g);
@@ -1781,7 +1788,12 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
   if (kb != BW_TB) return hipErrorInvalidValue;
   switch (ka) {
     case BW_KB: return launch_bw_mfma<1, BW_KB, BW_TB, BW_TB, 64>(g, grid, s);
-    case BW_TB: return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64>(g, grid, s);
+    case BW_TB:
+      // bf16 expert table gradients: one LDS buffer.  Experts that reach this
+      // kernel average under 256 rows, so each tile runs a few K slices, and
+      // the smaller LDS lets three workgroups share a compute unit, not two
+      if (g.mode == BW_WGT && !g.c_f32) return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64, 1>(g, grid, s);
+      return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64>(g, grid, s);
     case BW_KF: return launch_bw_mfma<1, BW_KF, BW_TB, BW_TB, 32>(g, grid, s);
     default: return launch_bw_mfma<1, BW_TF, BW_TB, BW_TB, 32>(g, grid, s);
   }

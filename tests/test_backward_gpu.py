@@ -134,6 +134,11 @@ CASES = {
     # experts with 1 to 4 rows (mostly zero-row positions) and one of 2342 rows
     "bf16_big_zipf_idle": (CONFIGS["zipf2048"].replace(tokens=3100, n_experts=12, d_model=64,
                                                        d_hidden=128, top_k=1), 0.5, 0.5),
+    # 15 rows per expert on average (table gradients on one LDS buffer), idle
+    # experts, and nine experts with 65 to 463 rows: tiles of several K slices
+    # with a ragged last slice
+    "bf16_zipf_one_buffer": (CONFIGS["zipf2048"].replace(tokens=1200, n_experts=160, d_model=64,
+                                                         d_hidden=128), 0.5, 0.5),
     # one group, then one expert: both softmax levels are a single weight of 1
     "bf16_hier_k1": (CONFIGS["hier4096"].replace(tokens=200, n_experts=64, d_model=128,
                                                  d_hidden=256, k_groups=1, k_per_group=1,
