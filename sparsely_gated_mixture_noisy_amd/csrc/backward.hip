@@ -1020,14 +1020,14 @@ __device__ __forceinline__ float bw_part(int lo, float v) {
 template <int BK>
 using BwTileT = bf16_t[BG_BM][BK + 8];
 
-// Column of element (row, k) in a tile.  64-wide slices swap their 16-byte
-// chunks by row, chunk ^ ((row >> 4) & 7): the fragment reads of the MFMAs
+// Column of element (row, k) in a tile.  Slices swap their 16-byte chunks by
+// row, chunk ^ ((row >> 4) & (BK / 8 - 1)): the fragment reads of the MFMAs
 // stay free of bank conflicts and the 4-row pieces written by the transposing
-// loader conflict 2-way instead of 8-way.
+// loaders conflict 2-way instead of 8-way.  Every tile write and read goes
+// through this map.
 template <int BK>
 __device__ __forceinline__ int bw_col(int row, int k) {
-  if constexpr (BK == 64) return (((k >> 3) ^ ((row >> 4) & 7)) << 3) | (k & 7);
-  return k;
+  return (((k >> 3) ^ ((row >> 4) & (BK / 8 - 1))) << 3) | (k & 7);
 }
 
 // Loaders of one K slice (BK) of 128 rows of an operand, by kind: load()
@@ -1131,7 +1131,8 @@ template <int BK> struct BwLd<BW_KF, BK> {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         out[j] = cvt_pk_bf16(bw_part(o.lo, raw.v[i][2 * j]), bw_part(o.lo, raw.v[i][2 * j + 1]));
-      *reinterpret_cast<u32x4*>(&S[(tid >> 2) + 64 * i][(tid & 3) * 8]) = out;
+      const int row = (tid >> 2) + 64 * i;
+      *reinterpret_cast<u32x4*>(&S[row][bw_col<BK>(row, (tid & 3) * 8)]) = out;
     }
   }
 };
@@ -1165,7 +1166,7 @@ template <int BK> struct BwLd<BW_TF, BK> {
     for (int c = 0; c < 4; ++c) {
       const uint32_t x = cvt_pk_bf16(bw_part(o.lo, raw.v[0][c]), bw_part(o.lo, raw.v[1][c]));
       const uint32_t y = cvt_pk_bf16(bw_part(o.lo, raw.v[2][c]), bw_part(o.lo, raw.v[3][c]));
-      *reinterpret_cast<uint2*>(&S[rr + c][kq]) = uint2{x, y};
+      *reinterpret_cast<uint2*>(&S[rr + c][bw_col<BK>(rr + c, kq)]) = uint2{x, y};
     }
   }
 };
