@@ -810,9 +810,13 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     const bool big = bw_hidden_big_tiles(bf16, A, E);
     if (A > 0) {
       int32_t* tiles = at<int32_t>(ws, L.tiles);
-      MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_tile_rows(), tiles, nullptr, se),
+      // rows per tile of the row-position products: 32 when the experts
+      // average at most 32 rows (a quarter of the accumulators; three
+      // workgroups per compute unit keep more table loads in flight)
+      const int prow = bw_pos_tile_rows(bf16, A, E);
+      MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, prow, tiles, nullptr, se),
                          "backward tiles"));
-      const int64_t row_tiles = (A + bw_tile_rows() - 1) / bw_tile_rows() + E;
+      const int64_t row_tiles = (A + prow - 1) / prow + E;
       int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
       // dX on the large tiles from 128 rows per expert on average: one 256-row
       // tile then holds most experts whole, so each of an expert's two column
@@ -866,6 +870,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
         q.K = d;
         q.offsets = sv->offsets;
         q.tiles = tiles;
+        q.pos_rows = prow;
         q.E = E;
         q.C = hid;
         q.C2 = dp;
@@ -897,6 +902,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
         r.K = h;
         r.offsets = sv->offsets;
         r.tiles = tiles;
+        r.pos_rows = prow;
         r.E = E;
         r.C = dxs;
         r.c_f32 = f32 ? 1 : 0;  // in the layer dtype, like the expert outputs

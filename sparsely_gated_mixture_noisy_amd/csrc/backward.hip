@@ -1016,9 +1016,10 @@ __device__ __forceinline__ float bw_part(int lo, float v) {
   return v - __uint_as_float(hi);
 }
 
-// An LDS operand tile: 128 rows of BK bf16 k values (+8 of padding).
-template <int BK>
-using BwTileT = bf16_t[BG_BM][BK + 8];
+// An LDS operand tile: ROWS rows (128, or 32 for the row operands of small
+// experts' tiles) of BK bf16 k values (+8 of padding).
+template <int BK, int ROWS = BG_BM>
+using BwTileT = bf16_t[ROWS][BK + 8];
 
 // Column of element (row, k) in a tile.  Slices swap their 16-byte chunks by
 // row, chunk ^ ((row >> 4) & (BK / 8 - 1)): the fragment reads of the MFMAs
@@ -1035,10 +1036,13 @@ __device__ __forceinline__ int bw_col(int row, int k) {
 // to an LDS tile as bf16 [row][k].  Thread t covers
 //   KB, KF: 16-byte k pieces: rows t/(BK/8) + (2048/BK) i, k = (t%(BK/8))*8 .. +7
 //   TB, TF: 4-row pieces: rows (t%32)*4 .. +3, k = (t/32)*4 + 32 j .. +3
-template <int KIND, int BK> struct BwLd;
+template <int KIND, int BK, int ROWS = BG_BM> struct BwLd;
 
-template <int BK> struct BwLd<BW_KB, BK> {
-  static constexpr int CPR = BK / 8, NI = BK / 16;  // pieces per row, per thread
+// (KB: piece tid + 256 i is row (tid + 256 i) / CPR; with 32 rows and
+// 32-wide slices only the first 128 threads hold one)
+template <int BK, int ROWS> struct BwLd<BW_KB, BK, ROWS> {
+  static constexpr int CPR = BK / 8;                      // pieces per row
+  static constexpr int PIECES = ROWS * CPR, NI = (PIECES + 255) / 256;  // per thread
   struct Raw { u32x4 v[NI]; };
   static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
                                               int64_t k0, int64_t K, Raw& raw) {
@@ -1047,22 +1051,27 @@ template <int BK> struct BwLd<BW_KB, BK> {
     const int64_t k = k0 + (tid % CPR) * 8;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int64_t r = r0 + tid / CPR + (256 / CPR) * i;
-      raw.v[i] = (r < R && k < K) ? *reinterpret_cast<const u32x4*>(p + r * o.ld + k)
-                                  : u32x4{0u, 0u, 0u, 0u};
+      const int piece = tid + 256 * i;
+      const int64_t r = r0 + piece / CPR;
+      raw.v[i] = (piece < PIECES && r < R && k < K)
+                     ? *reinterpret_cast<const u32x4*>(p + r * o.ld + k)
+                     : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  static __device__ __forceinline__ void put(const BwOp&, const Raw& raw, BwTileT<BK>& S) {
+  static __device__ __forceinline__ void put(const BwOp&, const Raw& raw, BwTileT<BK, ROWS>& S) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = tid / CPR + (256 / CPR) * i;
+      const int piece = tid + 256 * i;
+      if (piece >= PIECES) continue;
+      const int row = piece / CPR;
       *reinterpret_cast<u32x4*>(&S[row][bw_col<BK>(row, (tid % CPR) * 8)]) = raw.v[i];
     }
   }
 };
 
-template <int BK> struct BwLd<BW_TB, BK> {
+template <int BK, int ROWS> struct BwLd<BW_TB, BK, ROWS> {
+  static_assert(ROWS == BG_BM, "transposed operands fill 128-row tiles");
   static constexpr int NJ = BK / 32;  // 4-k groups per thread
   struct Raw { uint2 v[NJ][4]; };
   static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
@@ -1099,7 +1108,8 @@ template <int BK> struct BwLd<BW_TB, BK> {
   }
 };
 
-template <int BK> struct BwLd<BW_KF, BK> {
+template <int BK, int ROWS> struct BwLd<BW_KF, BK, ROWS> {
+  static_assert(ROWS == BG_BM, "fp32 operands fill 128-row tiles");
   static_assert(BK == 32, "fp32 operands use 32-wide slices");
   struct Raw { float v[2][8]; };
   static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
@@ -1137,7 +1147,8 @@ template <int BK> struct BwLd<BW_KF, BK> {
   }
 };
 
-template <int BK> struct BwLd<BW_TF, BK> {
+template <int BK, int ROWS> struct BwLd<BW_TF, BK, ROWS> {
+  static_assert(ROWS == BG_BM, "fp32 operands fill 128-row tiles");
   static_assert(BK == 32, "fp32 operands use 32-wide slices");
   struct Raw { float v[4][4]; };  // [k][row]
   static __device__ __forceinline__ void load(const BwOp& o, int e, int64_t r0, int64_t R,
@@ -1180,6 +1191,7 @@ struct BwTile {
   int chunk;
 };
 
+template <int BM = BG_BM>
 __device__ __forceinline__ bool bw_tile_of(const BwGemm& g, BwTile* t) {
   const int bid = blockIdx.x;
   if (g.mode == BW_POS) {
@@ -1192,7 +1204,7 @@ __device__ __forceinline__ bool bw_tile_of(const BwGemm& g, BwTile* t) {
       if (g.tiles[mid] <= q) lo = mid; else hi = mid - 1;
     }
     t->e = lo;
-    t->m0 = g.offsets[lo] + (int64_t)(q - g.tiles[lo]) * BG_BM;
+    t->m0 = g.offsets[lo] + (int64_t)(q - g.tiles[lo]) * BM;
     t->M = g.offsets[lo + 1];
     t->n0 = (int64_t)ct * BG_BN;
     t->N = g.N;
@@ -1259,37 +1271,58 @@ __device__ __forceinline__ void bw_hidden_store(const BwGemm& g, int64_t m, int6
 constexpr int BG_CLD_B = BG_BN + 8;   // bf16 row stride
 constexpr int BG_CLD_F = BG_BN + 4;   // fp32 row stride
 
-// bf16 MFMA product: 128 x 128 tile, four waves of 64 x 64, K in slices of BK
-// through two LDS buffers: the global loads of slice s+1 are in flight during
-// the MFMAs of slice s and land in the other buffer afterwards (one barrier
-// per slice).  NPROD products share the tile: plain products (NPROD = 1) sum
-// their npair operand pairs into one accumulator, the hidden epilogue runs 2
-// (ReLU) or 3 (SwiGLU) products.  Operand kinds are template arguments: KA
-// for every A operand, KB0 for the B operands except that of product 1 (KB1).
-// The results go through LDS and leave as 16-byte row pieces.
-// (two products in slices of 32: two workgroups per compute unit)
+// bf16 MFMA product: BM x 128 tile (BM = 128: four waves of 64 x 64; BM =
+// 32, the row-position products of small experts: four waves of 32 x 32), K
+// in slices of BK through two LDS buffers: the global loads of slice s+1 are
+// in flight during the MFMAs of slice s and land in the other buffer
+// afterwards (one barrier per slice).  NPROD products share the tile: plain
+// products (NPROD = 1) sum their npair operand pairs into one accumulator,
+// the hidden epilogue runs 2 (ReLU) or 3 (SwiGLU) products.  Operand kinds
+// are template arguments: KA for every A operand, KB0 for the B operands
+// except that of product 1 (KB1).  The results go through LDS and leave as
+// 16-byte row pieces.
+// (two products in slices of 32: two workgroups per compute unit; 32-row
+// tiles hold a quarter of the accumulators and of the row operands' LDS, and
+// three share a compute unit)
 // NB = 1: one LDS buffer, the next slice written once every wave has read the
 // current one (table gradients of experts with a few rows, mostly one slice:
 // the smaller LDS fits more workgroups per compute unit)
-template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2>
-__global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm_mfma_kernel(BwGemm g) {
+template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2, int BM = BG_BM>
+__global__ __launch_bounds__(256, BM == 32 ? 3 : (NPROD == 2 && BK == 32) ? 2 : 1) void
+bw_gemm_mfma_kernel(BwGemm g) {
+  static_assert(BM == 32 || BM == BG_BM, "tiles of 32 or 128 rows");
   extern __shared__ __attribute__((aligned(16))) bf16_t bw_lds[];
-  using Tile = BwTileT<BK>;
-  Tile* tiles = reinterpret_cast<Tile*>(bw_lds);  // [NB buffers][2 * NPROD operands]
+  using TileA = BwTileT<BK, BM>;
+  using TileB = BwTileT<BK>;
+  // per buffer: the A tiles (A0, and A1 with two or three products: product
+  // 2 shares A0), then the B tiles (one per product)
+  constexpr int NTA = NPROD == 1 ? 1 : 2, NTB = NPROD;
+  constexpr int BUF = NTA * (int)sizeof(TileA) + NTB * (int)sizeof(TileB);
+  char* lds_b = reinterpret_cast<char*>(bw_lds);
+  auto tA = [&](int buf, int i) -> TileA& {
+    return *reinterpret_cast<TileA*>(lds_b + buf * BUF + i * (int)sizeof(TileA));
+  };
+  auto tB = [&](int buf, int i) -> TileB& {
+    return *reinterpret_cast<TileB*>(lds_b + buf * BUF + NTA * (int)sizeof(TileA) +
+                                     i * (int)sizeof(TileB));
+  };
   BwTile t;
-  if (!bw_tile_of(g, &t)) return;
+  if (!bw_tile_of<BM>(g, &t)) return;
+  // wave grid WM x WN, wave tile RW x CW of MI x NJ 32 x 32 blocks
+  constexpr int WM = BM == 32 ? 1 : 2, WN = 4 / WM;
+  constexpr int RW = BM / WM, CW = BG_BN / WN, MI = RW / 32, NJ = CW / 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1, fr = lane & 31, fk = (lane >> 5) * 8;
-  using LA = BwLd<KA, BK>;
+  const int wm = w / WN, wn = w % WN, fr = lane & 31, fk = (lane >> 5) * 8;
+  using LA = BwLd<KA, BK, BM>;
   using LB0 = BwLd<KB0, BK>;
   using LB1 = BwLd<KB1, BK>;
-  f32x16 acc[NPROD][2][2];
+  f32x16 acc[NPROD][MI][NJ];
 #pragma unroll
   for (int p = 0; p < NPROD; ++p)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[p][i][j] = f32x16{};
+      for (int j = 0; j < NJ; ++j) acc[p][i][j] = f32x16{};
   const int64_t nk = (t.K - t.k0 + BK - 1) / BK;
   const int nseg = NPROD == 1 ? g.npair : 1;
   for (int seg = 0; seg < nseg && nk > 0; ++seg) {
@@ -1310,23 +1343,22 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
       }
       if constexpr (NPROD == 3) LB0::load(B2, t.e, t.n0, t.N, k0, t.K, rb2);
     };
-    auto put_all = [&](Tile* T) {
-      LA::put(A0, ra0, T[0]);
-      LB0::put(B0, rb0, T[1]);
+    auto put_all = [&](int buf) {
+      LA::put(A0, ra0, tA(buf, 0));
+      LB0::put(B0, rb0, tB(buf, 0));
       if constexpr (NPROD >= 2) {
-        LA::put(A1, ra1, T[2]);
-        LB1::put(B1, rb1, T[3]);
+        LA::put(A1, ra1, tA(buf, 1));
+        LB1::put(B1, rb1, tB(buf, 1));
       }
-      if constexpr (NPROD == 3) LB0::put(B2, rb2, T[5]);
+      if constexpr (NPROD == 3) LB0::put(B2, rb2, tB(buf, 2));
     };
     __syncthreads();  // the previous segment's last reads are done
     load_all(t.k0);
-    put_all(tiles);
+    put_all(0);
     __syncthreads();
     for (int64_t s = 0; s < nk; ++s) {
       const int cur = NB == 2 ? (int)(s & 1) : 0;
-      Tile* T0 = tiles + cur * 2 * NPROD;
-      Tile* T1 = tiles + (NB == 2 ? cur ^ 1 : 0) * 2 * NPROD;
+      const int nxt = NB == 2 ? cur ^ 1 : 0;
       const bool more = s + 1 < nk;
       if (more) load_all(t.k0 + (s + 1) * BK);
 #pragma unroll
@@ -1334,25 +1366,30 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
 #pragma unroll
         for (int p = 0; p < NPROD; ++p) {
           // product 2 (SwiGLU up) shares product 0's A tile
-          const int ta = p == 2 ? 0 : 2 * p;
-          bf16x8 af[2], bf[2];
+          const TileA& Ta = tA(cur, p == 2 ? 0 : p);
+          const TileB& Tb = tB(cur, p);
+          bf16x8 af[MI], bf[NJ];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int ra = wm * 64 + i * 32 + fr, rb = wn * 64 + i * 32 + fr;
-            af[i] = *reinterpret_cast<const bf16x8*>(&T0[ta][ra][bw_col<BK>(ra, ks + fk)]);
-            bf[i] = *reinterpret_cast<const bf16x8*>(&T0[2 * p + 1][rb][bw_col<BK>(rb, ks + fk)]);
+          for (int i = 0; i < MI; ++i) {
+            const int ra = wm * RW + i * 32 + fr;
+            af[i] = *reinterpret_cast<const bf16x8*>(&Ta[ra][bw_col<BK>(ra, ks + fk)]);
+          }
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int rb = wn * CW + j * 32 + fr;
+            bf[j] = *reinterpret_cast<const bf16x8*>(&Tb[rb][bw_col<BK>(rb, ks + fk)]);
           }
           // B as the first operand: the accumulators hold C^T, so that a lane
           // holds four consecutive columns of one row
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[p][i][j] = mfma32(bf[j], af[i], acc[p][i][j]);
+            for (int j = 0; j < NJ; ++j) acc[p][i][j] = mfma32(bf[j], af[i], acc[p][i][j]);
         }
       }
       if (more) {
-        if constexpr (NB == 1) __syncthreads();  // every wave is done with T0
-        put_all(T1);
+        if constexpr (NB == 1) __syncthreads();  // every wave is done with this buffer
+        put_all(nxt);
       }
       __syncthreads();
     }
@@ -1366,17 +1403,17 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
     if (g.c_f32) {
       float (*Cs)[BG_CLD_F] = reinterpret_cast<float (*)[BG_CLD_F]>(bw_lds);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<float4*>(&Cs[wm * 64 + i * 32 + erow][wn * 64 + j * 32 + 8 * q + ecol]) =
+            *reinterpret_cast<float4*>(&Cs[wm * RW + i * 32 + erow][wn * CW + j * 32 + 8 * q + ecol]) =
                 float4{acc[0][i][j][4 * q], acc[0][i][j][4 * q + 1], acc[0][i][j][4 * q + 2],
                        acc[0][i][j][4 * q + 3]};
       __syncthreads();
       float* C = (float*)g.C + (int64_t)t.e * g.c_estride + (int64_t)t.chunk * g.c_chunk;
-      for (int c = tid; c < BG_BM * (BG_BN / 4); c += 256) {
+      for (int c = tid; c < BM * (BG_BN / 4); c += 256) {
         const int rr = c / (BG_BN / 4), cc = (c % (BG_BN / 4)) * 4;
         const int64_t m = t.m0 + rr, n = t.n0 + cc;
         if (m < t.M && n < t.N)
@@ -1385,17 +1422,17 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
     } else {
       bf16_t (*Cs)[BG_CLD_B] = reinterpret_cast<bf16_t (*)[BG_CLD_B]>(bw_lds);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint2*>(&Cs[wm * 64 + i * 32 + erow][wn * 64 + j * 32 + 8 * q + ecol]) =
+            *reinterpret_cast<uint2*>(&Cs[wm * RW + i * 32 + erow][wn * CW + j * 32 + 8 * q + ecol]) =
                 uint2{cvt_pk_bf16(acc[0][i][j][4 * q], acc[0][i][j][4 * q + 1]),
                       cvt_pk_bf16(acc[0][i][j][4 * q + 2], acc[0][i][j][4 * q + 3])};
       __syncthreads();
       bf16_t* C = (bf16_t*)g.C + (int64_t)t.e * g.c_estride + (int64_t)t.chunk * g.c_chunk;
-      for (int c = tid; c < BG_BM * (BG_BN / 8); c += 256) {
+      for (int c = tid; c < BM * (BG_BN / 8); c += 256) {
         const int rr = c / (BG_BN / 8), cc = (c % (BG_BN / 8)) * 8;
         const int64_t m = t.m0 + rr, n = t.n0 + cc;
         if (m < t.M && n < t.N)
@@ -1405,14 +1442,14 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
   } else {
     // Hid, dP (ReLU) or Hid, dA, dB (SwiGLU), each [A][N] bf16
     constexpr int NOUT = NPROD;
-    bf16_t (*Cs)[BG_BM][BG_CLD_B] = reinterpret_cast<bf16_t (*)[BG_BM][BG_CLD_B]>(bw_lds);
+    bf16_t (*Cs)[BM][BG_CLD_B] = reinterpret_cast<bf16_t (*)[BM][BG_CLD_B]>(bw_lds);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int rr = wm * 64 + i * 32 + erow, cc = wn * 64 + j * 32 + 8 * q + ecol;
+          const int rr = wm * RW + i * 32 + erow, cc = wn * CW + j * 32 + 8 * q + ecol;
           float o0[4], o1[4], o2[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -1439,7 +1476,7 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
                 uint2{cvt_pk_bf16(o2[0], o2[1]), cvt_pk_bf16(o2[2], o2[3])};
         }
     __syncthreads();
-    for (int c = tid; c < BG_BM * (BG_BN / 8); c += 256) {
+    for (int c = tid; c < BM * (BG_BN / 8); c += 256) {
       const int rr = c / (BG_BN / 8), cc = (c % (BG_BN / 8)) * 8;
       const int64_t m = t.m0 + rr, n = t.n0 + cc;
       if (m < t.M && n < t.N) {
@@ -1454,11 +1491,12 @@ __global__ __launch_bounds__(256, (NPROD == 2 && BK == 32) ? 2 : 1) void bw_gemm
 }
 
 // NB = 1 serves bf16 outputs only, so its output tile is bf16 too
-template <int NPROD, int BK, int NB = 2>
+template <int NPROD, int BK, int NB = 2, int BM = BG_BM>
 static size_t bw_gemm_lds() {
-  const size_t ops = sizeof(bf16_t) * NB * 2 * NPROD * BG_BM * (BK + 8);
-  const size_t outs = NPROD == 1 && NB == 2 ? sizeof(float) * BG_BM * BG_CLD_F
-                                            : sizeof(bf16_t) * NPROD * BG_BM * BG_CLD_B;
+  const int nta = NPROD == 1 ? 1 : 2, ntb = NPROD;
+  const size_t ops = sizeof(bf16_t) * NB * (nta * BM + ntb * BG_BM) * (BK + 8);
+  const size_t outs = NPROD == 1 && NB == 2 ? sizeof(float) * BM * BG_CLD_F
+                                            : sizeof(bf16_t) * NPROD * BM * BG_CLD_B;
   return ops > outs ? ops : outs;
 }
 
@@ -1477,7 +1515,7 @@ __global__ __launch_bounds__(BF_THREADS) void bw_gemm_f32_kernel(BwGemm g) {
   constexpr int NOP = NP == 1 ? 2 : NP == 2 ? 4 : 5;  // operands staged per slice
   __shared__ float S[NOP][BF_BK][BF_LD];
   BwTile t;
-  if (!bw_tile_of(g, &t)) return;
+  if (!bw_tile_of<BG_BM>(g, &t)) return;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   float acc[NP][4][8];
 #pragma unroll
@@ -1750,12 +1788,14 @@ hipError_t launch_bw_gather_rows(const void* src, const int32_t* perm, int k, co
   return hipGetLastError();
 }
 
-int bw_tile_rows() { return BG_BM; }
+int bw_pos_tile_rows(bool bf16, int64_t A, int E) {
+  return bf16 && A <= 32 * (int64_t)E ? 32 : BG_BM;
+}
 
-template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2>
+template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2, int BM = BG_BM>
 static hipError_t launch_bw_mfma(const BwGemm& g, int64_t grid, hipStream_t s) {
-  auto kern = bw_gemm_mfma_kernel<NPROD, KA, KB0, KB1, BK, NB>;
-  const size_t lds = bw_gemm_lds<NPROD, BK, NB>();
+  auto kern = bw_gemm_mfma_kernel<NPROD, KA, KB0, KB1, BK, NB, BM>;
+  const size_t lds = bw_gemm_lds<NPROD, BK, NB, BM>();
   hipError_t err = bw_set_lds(kern, lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, g);
@@ -1778,6 +1818,15 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
     else
       hipLaunchKernelGGL(bw_gemm_f32_kernel<1>, dim3((unsigned)grid), blk, 0, s, g);
     return hipGetLastError();
+  }
+  if (g.mode == BW_POS && g.pos_rows != BG_BM) {
+    // 32-row tiles of the row-position products (experts averaging at most
+    // 32 rows): bf16 rows against 128 columns of a table
+    if (g.pos_rows != 32) return hipErrorInvalidValue;
+    if (g.epi == BW_EPI_RELU) return launch_bw_mfma<2, BW_KB, BW_KB, BW_TB, 32, 2, 32>(g, grid, s);
+    if (g.epi == BW_EPI_SWIGLU) return launch_bw_mfma<3, BW_KB, BW_KB, BW_TB, 32, 2, 32>(g, grid, s);
+    if (g.a[0].kind != BW_KB || g.b[0].kind != BW_TB) return hipErrorInvalidValue;
+    return launch_bw_mfma<1, BW_KB, BW_TB, BW_TB, 64, 2, 32>(g, grid, s);
   }
   // slices of 32: the two products' operand tiles take 80 KB of LDS and at
   // most 256 registers, so that two workgroups share a compute unit (the

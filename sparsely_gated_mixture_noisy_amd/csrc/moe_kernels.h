@@ -397,7 +397,8 @@ struct BwGemm {
   int64_t M = 0, N = 0, K = 0;
   int64_t kchunk = 0;           // PLAIN: K per chunk (grid covers the chunks)
   const int32_t* offsets = nullptr;  // [E+1]
-  const int32_t* tiles = nullptr;    // POS: [E+1] row tiles of bw_tile_rows()
+  const int32_t* tiles = nullptr;    // POS: [E+1] row tiles of pos_rows rows
+  int pos_rows = 128;                // POS: rows per tile, bw_pos_tile_rows()
   int E = 0;
   void* C = nullptr;            // plain: output; hidden: Hid [A][N]
   void* C2 = nullptr;           // hidden: dP (ReLU) or dA (SwiGLU)
@@ -409,7 +410,9 @@ struct BwGemm {
 // out[p] = src[perm[p] / k] (times scale[perm[p]]), d % 8 == 0 (bf16) or % 4 (fp32)
 hipError_t launch_bw_gather_rows(const void* src, const int32_t* perm, int k, const float* scale,
                                  int64_t A, int d, bool bf16, void* out, hipStream_t s);
-int bw_tile_rows();
+// Rows per tile of the row-position products (the hidden recompute and dX):
+// 32 when a bf16 layer's experts average at most 32 rows, else 128.
+int bw_pos_tile_rows(bool bf16, int64_t A, int E);
 hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s);
 
 }  // namespace moe

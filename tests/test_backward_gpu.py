@@ -97,6 +97,11 @@ CASES = {
                   0.6, 1.1),
     "bf16_swiglu": (CONFIGS["flat256"].replace(tokens=300, n_experts=12, d_model=128,
                                                d_hidden=192, ffn="swiglu", top_k=2), 0.4, 0.9),
+    # experts averaging about 17 rows: 32-row tiles of the three-product
+    # SwiGLU recompute and of dX, a ragged last column tile (192 hidden units)
+    "bf16_swiglu_small_experts": (CONFIGS["flat256"].replace(tokens=200, n_experts=24, d_model=128,
+                                                             d_hidden=192, ffn="swiglu", top_k=2),
+                                  0.4, 0.9),
     # two expert blocks in the gate tiles, a bias, a ragged last tile, idle experts
     "bf16_e300_bias": (CONFIGS["zipf2048"].replace(tokens=230, n_experts=300, d_model=64,
                                                    d_hidden=128), 0.3, 2.0),
