@@ -93,6 +93,9 @@ CASES = {
     "tiny": (CONFIGS["tiny"], 0.7, 1.3),
     "tiny_ragged_swiglu": (CONFIGS["tiny"].replace(tokens=77, ffn="swiglu"), 0.5, 0.8),
     "tiny_noise_free": (CONFIGS["tiny"].replace(tokens=90, noisy=False), 1.0, 0.0),
+    # fp32, two expert blocks of 256 in the gate tiles: the rank kernel, then
+    # the gradient kernel
+    "tiny_e300": (CONFIGS["tiny"].replace(tokens=120, n_experts=300), 0.6, 1.2),
     "bf16_relu": (CONFIGS["flat256"].replace(tokens=400, n_experts=24, d_model=128, d_hidden=256),
                   0.6, 1.1),
     "bf16_swiglu": (CONFIGS["flat256"].replace(tokens=300, n_experts=12, d_model=128,
