@@ -1285,8 +1285,8 @@ constexpr int BG_CLD_F = BG_BN + 4;   // fp32 row stride
 // tiles hold a quarter of the accumulators and of the row operands' LDS, and
 // three share a compute unit)
 // NB = 1: one LDS buffer, the next slice written once every wave has read the
-// current one (table gradients of experts with a few rows, mostly one slice:
-// the smaller LDS fits more workgroups per compute unit)
+// current one (bf16 expert table gradients, whose tiles run one to a few
+// slices: the smaller LDS fits three workgroups per compute unit)
 template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2, int BM = BG_BM>
 __global__ __launch_bounds__(256, BM == 32 ? 3 : (NPROD == 2 && BK == 32) ? 2 : 1) void
 bw_gemm_mfma_kernel(BwGemm g) {
