@@ -1021,14 +1021,36 @@ __device__ __forceinline__ float bw_part(int lo, float v) {
 template <int BK, int ROWS = BG_BM>
 using BwTileT = bf16_t[ROWS][BK + 8];
 
-// Column of element (row, k) in a tile.  Slices swap their 16-byte chunks by
-// row, chunk ^ ((row >> 4) & (BK / 8 - 1)): the fragment reads of the MFMAs
-// stay free of bank conflicts and the 4-row pieces written by the transposing
-// loaders conflict 2-way instead of 8-way.  Every tile write and read goes
-// through this map.
+// Column of element (row, k) in a tile of a K-major operand (KB, KF).
+// Slices swap their 16-byte chunks by row, chunk ^ ((row >> 4) & (BK / 8 -
+// 1)), so that the fragment reads of the MFMAs stay free of bank conflicts.
+// Every write and read of such a tile goes through this map.
 template <int BK>
 __device__ __forceinline__ int bw_col(int row, int k) {
   return (((k >> 3) ^ ((row >> 4) & (BK / 8 - 1))) << 3) | (k & 7);
+}
+
+// Transposed operands (TB, TF) sit in their tile as stored, [k][128 rows]
+// (256 bytes per k, no padding), 16-byte chunks swizzled as chunk ^ 2 (k & 3);
+// element (row, k) is at bw_tr_at(k, row).  The MFMA fragments come from
+// gfx950's transposing LDS read: within each group of 16 lanes, lane j points
+// at k + j / 4, rows r + 4 (j % 4) .. +3, and ds_read_b64_tr_b16 hands lane i
+// of the group the four k values of row r + i.  A group's 16 reads touch 8
+// distinct chunks, and a wave's 8-byte tile writes fill whole 256-byte k rows,
+// so neither conflicts on banks.
+typedef short bw_v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int bw_tr_at(int k, int row) {
+  return (k * (BG_BM / 8) + ((row >> 3) ^ (2 * (k & 3)))) * 8 + (row & 7);
+}
+// fragment of rows r0 .. r0 + 31 (lane l: row r0 + l % 32), k0 + 8 (l / 32) .. +7
+__device__ __forceinline__ bf16x8 bw_frag_tr(const bf16_t* T, int r0, int k0) {
+  typedef bw_v4i16 __attribute__((address_space(3))) * lds_v4p;
+  const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
+  const int r = r0 + 16 * (G & 1) + 4 * (j & 3);
+  const int k = k0 + 8 * (G >> 1) + (j >> 2);
+  const bw_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(T + bw_tr_at(k, r)));
+  const bw_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(T + bw_tr_at(k + 4, r)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Loaders of one K slice (BK) of 128 rows of an operand, by kind: load()
@@ -1091,19 +1113,13 @@ template <int BK, int ROWS> struct BwLd<BW_TB, BK, ROWS> {
   static __device__ __forceinline__ void put(const BwOp&, const Raw& raw, BwTileT<BK>& S) {
     const int tid = threadIdx.x;
     const int rr = (tid & 31) * 4;
+    bf16_t* T = &S[0][0];
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int kq = (tid >> 5) * 4 + 32 * jj;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // row q of the four 4-row pieces: its bf16 half of each piece
-        const int wd = q >> 1, sh = (q & 1) * 16;
-        uint32_t a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = ((wd ? raw.v[jj][j].y : raw.v[jj][j].x) >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(&S[rr + q][bw_col<BK>(rr + q, kq)]) =
-            uint2{a[0] | (a[1] << 16), a[2] | (a[3] << 16)};
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(T + bw_tr_at(kq + j, rr)) = raw.v[jj][j];
     }
   }
 };
@@ -1173,11 +1189,12 @@ template <int BK, int ROWS> struct BwLd<BW_TF, BK, ROWS> {
   static __device__ __forceinline__ void put(const BwOp& o, const Raw& raw, BwTileT<BK>& S) {
     const int tid = threadIdx.x;
     const int rr = (tid & 31) * 4, kq = (tid >> 5) * 4;
+    bf16_t* T = &S[0][0];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t x = cvt_pk_bf16(bw_part(o.lo, raw.v[0][c]), bw_part(o.lo, raw.v[1][c]));
-      const uint32_t y = cvt_pk_bf16(bw_part(o.lo, raw.v[2][c]), bw_part(o.lo, raw.v[3][c]));
-      *reinterpret_cast<uint2*>(&S[rr + c][bw_col<BK>(rr + c, kq)]) = uint2{x, y};
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = cvt_pk_bf16(bw_part(o.lo, raw.v[j][0]), bw_part(o.lo, raw.v[j][1]));
+      const uint32_t y = cvt_pk_bf16(bw_part(o.lo, raw.v[j][2]), bw_part(o.lo, raw.v[j][3]));
+      *reinterpret_cast<uint2*>(T + bw_tr_at(kq + j, rr)) = uint2{x, y};
     }
   }
 };
@@ -1369,15 +1386,24 @@ bw_gemm_mfma_kernel(BwGemm g) {
           const TileA& Ta = tA(cur, p == 2 ? 0 : p);
           const TileB& Tb = tB(cur, p);
           bf16x8 af[MI], bf[NJ];
+          // transposed kinds (TB, TF) through the transposing read
+          constexpr bool TRA = KA == BW_TB || KA == BW_TF;
+          const bool trb = (p == 1 ? KB1 : KB0) == BW_TB || (p == 1 ? KB1 : KB0) == BW_TF;
 #pragma unroll
           for (int i = 0; i < MI; ++i) {
             const int ra = wm * RW + i * 32 + fr;
-            af[i] = *reinterpret_cast<const bf16x8*>(&Ta[ra][bw_col<BK>(ra, ks + fk)]);
+            if constexpr (TRA)
+              af[i] = bw_frag_tr(&Ta[0][0], wm * RW + i * 32, ks);
+            else
+              af[i] = *reinterpret_cast<const bf16x8*>(&Ta[ra][bw_col<BK>(ra, ks + fk)]);
           }
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int rb = wn * CW + j * 32 + fr;
-            bf[j] = *reinterpret_cast<const bf16x8*>(&Tb[rb][bw_col<BK>(rb, ks + fk)]);
+            if (trb)
+              bf[j] = bw_frag_tr(&Tb[0][0], wn * CW + j * 32, ks);
+            else
+              bf[j] = *reinterpret_cast<const bf16x8*>(&Tb[rb][bw_col<BK>(rb, ks + fk)]);
           }
           // B as the first operand: the accumulators hold C^T, so that a lane
           // holds four consecutive columns of one row
