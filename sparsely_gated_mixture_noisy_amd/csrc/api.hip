@@ -531,7 +531,7 @@ BwLayout bw_layout(const moe_config* c) {
   L.dxg = take(4 * (size_t)T * d);
   L.tiles = take(4 * (size_t)(E + 1));
   L.tiles_big = take(4 * (size_t)(E + 1));
-  L.zero = take(2 * (size_t)std::max(h, d));
+  L.zero = take(2 * (size_t)std::max(std::max(h, d), 128));
   L.hid = take(es * (size_t)A * h);
   L.dp = take(es * (size_t)A * h);
   L.db = take(sw ? es * (size_t)A * h : 0);
@@ -911,6 +911,13 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
                            "backward expert dx"));
       }
     }
+    // positions past an expert's rows (and, in the table-gradient products
+    // that load straight into LDS, rows past a tile) are read from a row of
+    // zeros
+    void* zero = at<void>(ws, L.zero);
+    if (bf16)
+      MOE_TRY(hip_status(launch_fill_i32((int32_t*)zero, std::max(std::max(h, d), 128) / 2, 0, se),
+                         "backward zero row"));
     // table gradients, one problem per expert over its rows (zero without rows)
     auto wgrad = [&](void* out, BwOp a, BwOp b, int64_t M, int64_t N, const char* what) {
       if (!out) return MOE_OK;
@@ -924,14 +931,11 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
       q.c_f32 = f32 ? 1 : 0;
       q.ldc = N;
       q.c_estride = M * N;
+      q.zero = bf16 ? zero : nullptr;
       const int64_t grid = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
       return hip_status(launch_bw_gemm(q, bf16, grid, se), what);
     };
     if (big) {
-      // positions past an expert's rows are read from a row of zeros
-      void* zero = at<void>(ws, L.zero);
-      MOE_TRY(hip_status(launch_fill_i32((int32_t*)zero, std::max(h, d) / 2, 0, se),
-                         "backward zero row"));
       auto wgrad_big = [&](void* out, const void* a, int M, const void* b, int N,
                            const char* what) {
         if (!out) return MOE_OK;

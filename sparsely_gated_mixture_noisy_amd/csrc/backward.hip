@@ -1200,6 +1200,37 @@ template <int BK, int ROWS> struct BwLd<BW_TF, BK, ROWS> {
 };
 
 // Which problem, rows, columns and K range a workgroup covers.
+// TD: a transposed bf16 operand loaded straight into LDS (global_load_lds,
+// 16 bytes a lane, no staging registers) in the TB layout above: wave w's
+// instruction q fills 16-byte slots s = 64 (NQ w + q) + lane, slot s holding
+// rows 8 c .. 8 c + 7 of k = s / 16, c = (s % 16) ^ 2 (k & 3).  Positions past
+// K and rows past R read a row of zeros (the launcher checks that rows come
+// in whole 16-byte pieces).
+template <int BK, int ROWS> struct BwLd<BW_TD, BK, ROWS> {
+  static_assert(ROWS == BG_BM, "transposed operands fill 128-row tiles");
+  struct Raw {};
+  static __device__ __forceinline__ void load(const BwOp&, int, int64_t, int64_t, int64_t,
+                                              int64_t, Raw&) {}
+  static __device__ __forceinline__ void put(const BwOp&, const Raw&, BwTileT<BK>&) {}
+  static __device__ __forceinline__ void direct(const BwOp& o, const bf16_t* zero, int e,
+                                                int64_t r0, int64_t R, int64_t k0, int64_t K,
+                                                BwTileT<BK>& S) {
+    constexpr int NQ = BK * BG_BM * 2 / 1024 / 4;  // 1 KB loads per wave
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const bf16_t* p = (const bf16_t*)o.p + (int64_t)e * o.estride;
+    bf16_t* T = &S[0][0];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int sl = 64 * (NQ * w + q) + lane;
+      const int kl = sl >> 4;
+      const int c = (sl & 15) ^ (2 * (kl & 3));
+      const int64_t k = k0 + kl, r = r0 + 8 * c;
+      const bf16_t* src = (k < K && r < R) ? p + k * o.ld + r : zero + 8 * c;
+      __builtin_amdgcn_global_load_lds(src, T + 512 * (NQ * w + q), 16, 0, 0);
+    }
+  }
+};
+
 struct BwTile {
   int e;
   int64_t m0, M;   // rows m0 .. M-1 (absolute positions in POS mode)
@@ -1305,7 +1336,7 @@ constexpr int BG_CLD_F = BG_BN + 4;   // fp32 row stride
 // current one (bf16 expert table gradients, whose tiles run one to a few
 // slices: the smaller LDS fits three workgroups per compute unit)
 template <int NPROD, int KA, int KB0, int KB1, int BK, int NB = 2, int BM = BG_BM>
-__global__ __launch_bounds__(256, BM == 32 ? 3 : (NPROD == 2 && BK == 32) ? 2 : 1) void
+__global__ __launch_bounds__(256, KA == BW_TD ? 4 : BM == 32 ? 3 : (NPROD == 2 && BK == 32) ? 2 : 1) void
 bw_gemm_mfma_kernel(BwGemm g) {
   static_assert(BM == 32 || BM == BG_BM, "tiles of 32 or 128 rows");
   extern __shared__ __attribute__((aligned(16))) bf16_t bw_lds[];
@@ -1360,7 +1391,15 @@ bw_gemm_mfma_kernel(BwGemm g) {
       }
       if constexpr (NPROD == 3) LB0::load(B2, t.e, t.n0, t.N, k0, t.K, rb2);
     };
-    auto put_all = [&](int buf) {
+    // TD (direct) operands are issued with the puts, into their buffer
+    auto put_all = [&](int buf, int64_t k0) {
+      if constexpr (KA == BW_TD) {
+        static_assert(NPROD == 1 && KB0 == BW_TD && NB == 1, "direct loads: table gradients");
+        const bf16_t* zero = (const bf16_t*)g.zero;
+        LA::direct(A0, zero, t.e, t.m0, t.M, k0, t.K, tA(buf, 0));
+        LB0::direct(B0, zero, t.e, t.n0, t.N, k0, t.K, tB(buf, 0));
+        return;
+      }
       LA::put(A0, ra0, tA(buf, 0));
       LB0::put(B0, rb0, tB(buf, 0));
       if constexpr (NPROD >= 2) {
@@ -1371,7 +1410,7 @@ bw_gemm_mfma_kernel(BwGemm g) {
     };
     __syncthreads();  // the previous segment's last reads are done
     load_all(t.k0);
-    put_all(0);
+    put_all(0, t.k0);
     __syncthreads();
     for (int64_t s = 0; s < nk; ++s) {
       const int cur = NB == 2 ? (int)(s & 1) : 0;
@@ -1387,8 +1426,9 @@ bw_gemm_mfma_kernel(BwGemm g) {
           const TileB& Tb = tB(cur, p);
           bf16x8 af[MI], bf[NJ];
           // transposed kinds (TB, TF) through the transposing read
-          constexpr bool TRA = KA == BW_TB || KA == BW_TF;
-          const bool trb = (p == 1 ? KB1 : KB0) == BW_TB || (p == 1 ? KB1 : KB0) == BW_TF;
+          constexpr bool TRA = KA == BW_TB || KA == BW_TF || KA == BW_TD;
+          const int KBp = p == 1 ? KB1 : KB0;
+          const bool trb = KBp == BW_TB || KBp == BW_TF || KBp == BW_TD;
 #pragma unroll
           for (int i = 0; i < MI; ++i) {
             const int ra = wm * RW + i * 32 + fr;
@@ -1415,7 +1455,7 @@ bw_gemm_mfma_kernel(BwGemm g) {
       }
       if (more) {
         if constexpr (NB == 1) __syncthreads();  // every wave is done with this buffer
-        put_all(nxt);
+        put_all(nxt, t.k0 + (s + 1) * BK);
       }
       __syncthreads();
     }
@@ -1868,7 +1908,16 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
       // bf16 expert table gradients: one LDS buffer.  Experts that reach this
       // kernel average under 256 rows, so each tile runs a few K slices, and
       // the smaller LDS lets three workgroups share a compute unit, not two
-      if (g.mode == BW_WGT && !g.c_f32) return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64, 1>(g, grid, s);
+      if (g.mode == BW_WGT && !g.c_f32) {
+        // operand rows straight into LDS when they come in whole 16-byte
+        // pieces: no staging registers, four workgroups per compute unit
+        const bool direct =
+            g.zero && g.M % 8 == 0 && g.N % 8 == 0 && g.a[0].ld % 8 == 0 && g.b[0].ld % 8 == 0 &&
+            g.a[0].estride % 8 == 0 && g.b[0].estride % 8 == 0 && g.npair == 1 &&
+            (((uintptr_t)g.a[0].p | (uintptr_t)g.b[0].p | (uintptr_t)g.zero) & 15) == 0;
+        if (direct) return launch_bw_mfma<1, BW_TD, BW_TD, BW_TD, 64, 1>(g, grid, s);
+        return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64, 1>(g, grid, s);
+      }
       return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64>(g, grid, s);
     case BW_KF: return launch_bw_mfma<1, BW_KF, BW_TB, BW_TB, 32>(g, grid, s);
     default: return launch_bw_mfma<1, BW_TF, BW_TB, BW_TB, 32>(g, grid, s);

@@ -376,7 +376,8 @@ hipError_t launch_bw_assemble_dx(const float* dxg, const void* dxs, const int32_
 // problem (expert) e at p + e*estride + (kind KB/KF: r*ld + k; TB/TF:
 // k*ld + r); B = bf16, F = fp32.  Kinds KB and TB need K % 8 == 0 (KB) and
 // R % 4 == 0 (TB) and ld % 8 == 0.
-enum { BW_KB = 0, BW_TB = 1, BW_KF = 2, BW_TF = 3 };
+// TD: a TB operand the launcher loads straight into LDS (set by launch_bw_gemm)
+enum { BW_KB = 0, BW_TB = 1, BW_KF = 2, BW_TF = 3, BW_TD = 4 };
 struct BwOp {
   const void* p = nullptr;
   int64_t estride = 0;
@@ -399,6 +400,7 @@ struct BwGemm {
   const int32_t* offsets = nullptr;  // [E+1]
   const int32_t* tiles = nullptr;    // POS: [E+1] row tiles of pos_rows rows
   int pos_rows = 128;                // POS: rows per tile, bw_pos_tile_rows()
+  const void* zero = nullptr;        // WGT, bf16: >= 128 zero elements (or null)
   int E = 0;
   void* C = nullptr;            // plain: output; hidden: Hid [A][N]
   void* C2 = nullptr;           // hidden: dP (ReLU) or dA (SwiGLU)
