@@ -611,9 +611,10 @@ moe_status gate_table_grad(const moe_config* c, const BwLayout& L, const void* x
 }
 
 // The same for bf16 coefficients already split into hi and lo halves [T][rows].
+// zero: a row of at least 128 zeros (bf16), read past the last token
 moe_status gate_table_grad_halves(const moe_config* c, const BwLayout& L, const void* x,
                                   const bf16_t* hi, const bf16_t* lo, int rows, void* out,
-                                  float* part, hipStream_t s) {
+                                  float* part, const void* zero, hipStream_t s) {
   if (!out) return MOE_OK;
   const int d = c->d_model;
   BwGemm q = product(op_cols(hi, rows, false), op_cols(x, d, false));
@@ -627,6 +628,7 @@ moe_status gate_table_grad_halves(const moe_config* c, const BwLayout& L, const 
   q.c_f32 = 1;
   q.ldc = d;
   q.c_chunk = (int64_t)rows * d;
+  q.zero = zero;
   const int64_t grid = (int64_t)L.nchunk * ((rows + 127) / 128) * ((d + 127) / 128);
   MOE_TRY(hip_status(launch_bw_gemm(q, true, grid, s), "backward gate tables"));
   return hip_status(launch_bw_sum_chunks(part, L.nchunk, (int64_t)rows * d, true, out, s),
@@ -911,13 +913,10 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
                            "backward expert dx"));
       }
     }
-    // positions past an expert's rows (and, in the table-gradient products
-    // that load straight into LDS, rows past a tile) are read from a row of
-    // zeros
+    // positions past an expert's rows (and, in the products that load
+    // straight into LDS, rows past a tile) are read from a row of zeros,
+    // filled before the fork
     void* zero = at<void>(ws, L.zero);
-    if (bf16)
-      MOE_TRY(hip_status(launch_fill_i32((int32_t*)zero, std::max(std::max(h, d), 128) / 2, 0, se),
-                         "backward zero row"));
     // table gradients, one problem per expert over its rows (zero without rows)
     auto wgrad = [&](void* out, BwOp a, BwOp b, int64_t M, int64_t N, const char* what) {
       if (!out) return MOE_OK;
@@ -961,6 +960,10 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     }
     return MOE_OK;
   };
+  if (bf16)
+    MOE_TRY(hip_status(launch_fill_i32(at<int32_t>(ws, L.zero),
+                                       std::max(std::max(h, d), 128) / 2, 0, s),
+                       "backward zero row"));
   SideJoin join(s);
   MOE_TRY(join.fork());
   MOE_TRY(expert_side(join.side));
@@ -1071,10 +1074,11 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     MOE_TRY(hip_status(launch_bw_gemm(q, bf16, grid, s), "backward dx gate"));
   }
   if (bf16) {
-    MOE_TRY(gate_table_grad_halves(c, L, x, ch, cl, E, g->dw_gate, at<float>(ws, L.part_g), s));
+    MOE_TRY(gate_table_grad_halves(c, L, x, ch, cl, E, g->dw_gate, at<float>(ws, L.part_g),
+                                   at<void>(ws, L.zero), s));
     if (noisy)
       MOE_TRY(gate_table_grad_halves(c, L, x, rh, rl, E, g->dw_noise, at<float>(ws, L.part_n),
-                                     s));
+                                     at<void>(ws, L.zero), s));
   } else {
     MOE_TRY(gate_table_grad(c, L, x, dclean, E, g->dw_gate, at<float>(ws, L.part_g), s));
     if (noisy)

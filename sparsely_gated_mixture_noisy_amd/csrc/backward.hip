@@ -1394,7 +1394,7 @@ bw_gemm_mfma_kernel(BwGemm g) {
     // TD (direct) operands are issued with the puts, into their buffer
     auto put_all = [&](int buf, int64_t k0) {
       if constexpr (KA == BW_TD) {
-        static_assert(NPROD == 1 && KB0 == BW_TD && NB == 1, "direct loads: table gradients");
+        static_assert(NPROD == 1 && KB0 == BW_TD && NB == 1, "direct loads: one product, one buffer");
         const bf16_t* zero = (const bf16_t*)g.zero;
         LA::direct(A0, zero, t.e, t.m0, t.M, k0, t.K, tA(buf, 0));
         LB0::direct(B0, zero, t.e, t.n0, t.N, k0, t.K, tB(buf, 0));
@@ -1465,6 +1465,33 @@ bw_gemm_mfma_kernel(BwGemm g) {
   // 4*(l/32) + r%4] of the wave's (i, j) block: register group g is four
   // consecutive columns of one row
   const int erow = lane & 31, ecol = 4 * (lane >> 5);
+  if constexpr (KA == BW_TD) {
+    // fp32 partial sums straight from the accumulators, 16 bytes a lane (no
+    // LDS staging, which would hold the kernel to two workgroups per CU)
+    if (g.c_f32) {
+      float* C = (float*)g.C + (int64_t)t.e * g.c_estride + (int64_t)t.chunk * g.c_chunk;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t m = t.m0 + wm * RW + i * 32 + erow;
+            const int64_t n = t.n0 + wn * CW + j * 32 + 8 * q + ecol;
+            if (m >= t.M) continue;
+            if (n + 3 < t.N) {
+              *reinterpret_cast<float4*>(C + m * g.ldc + n) =
+                  float4{acc[0][i][j][4 * q], acc[0][i][j][4 * q + 1], acc[0][i][j][4 * q + 2],
+                         acc[0][i][j][4 * q + 3]};
+            } else {
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (n + u < t.N) C[m * g.ldc + n + u] = acc[0][i][j][4 * q + u];
+            }
+          }
+      return;
+    }
+  }
   if constexpr (NPROD == 1) {
     if (g.c_f32) {
       float (*Cs)[BG_CLD_F] = reinterpret_cast<float (*)[BG_CLD_F]>(bw_lds);
@@ -1908,15 +1935,20 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
       // bf16 expert table gradients: one LDS buffer.  Experts that reach this
       // kernel average under 256 rows, so each tile runs a few K slices, and
       // the smaller LDS lets three workgroups share a compute unit, not two
-      if (g.mode == BW_WGT && !g.c_f32) {
-        // operand rows straight into LDS when they come in whole 16-byte
-        // pieces: no staging registers, four workgroups per compute unit
-        const bool direct =
-            g.zero && g.M % 8 == 0 && g.N % 8 == 0 && g.a[0].ld % 8 == 0 && g.b[0].ld % 8 == 0 &&
-            g.a[0].estride % 8 == 0 && g.b[0].estride % 8 == 0 && g.npair == 1 &&
-            (((uintptr_t)g.a[0].p | (uintptr_t)g.b[0].p | (uintptr_t)g.zero) & 15) == 0;
+      // operand rows straight into LDS when they come in whole 16-byte
+      // pieces (no staging registers: four workgroups per compute unit), for
+      // the bf16 expert table gradients and the fp32 partial sums of the
+      // gate-table products
+      if ((g.mode == BW_WGT && !g.c_f32) || (g.mode == BW_PLAIN && g.c_f32 && g.ldc % 4 == 0 &&
+                                              ((uintptr_t)g.C & 15) == 0)) {
+        bool direct = g.zero && g.M % 8 == 0 && g.N % 8 == 0 && ((uintptr_t)g.zero & 15) == 0;
+        for (int i = 0; i < g.npair && direct; ++i)
+          direct = g.a[i].kind == BW_TB && g.b[i].kind == BW_TB && !g.a[i].lo && !g.b[i].lo &&
+                   g.a[i].ld % 8 == 0 && g.b[i].ld % 8 == 0 && g.a[i].estride % 8 == 0 &&
+                   g.b[i].estride % 8 == 0 &&
+                   (((uintptr_t)g.a[i].p | (uintptr_t)g.b[i].p) & 15) == 0;
         if (direct) return launch_bw_mfma<1, BW_TD, BW_TD, BW_TD, 64, 1>(g, grid, s);
-        return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64, 1>(g, grid, s);
+        if (g.mode == BW_WGT) return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64, 1>(g, grid, s);
       }
       return launch_bw_mfma<1, BW_TB, BW_TB, BW_TB, 64>(g, grid, s);
     case BW_KF: return launch_bw_mfma<1, BW_KF, BW_TB, BW_TB, 32>(g, grid, s);
