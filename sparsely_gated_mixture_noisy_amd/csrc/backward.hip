@@ -1932,13 +1932,12 @@ hipError_t launch_bw_gemm(BwGemm g, bool bf16, int64_t grid, hipStream_t s) {
   switch (ka) {
     case BW_KB: return launch_bw_mfma<1, BW_KB, BW_TB, BW_TB, 64>(g, grid, s);
     case BW_TB:
-      // bf16 expert table gradients: one LDS buffer.  Experts that reach this
-      // kernel average under 256 rows, so each tile runs a few K slices, and
-      // the smaller LDS lets three workgroups share a compute unit, not two
-      // operand rows straight into LDS when they come in whole 16-byte
-      // pieces (no staging registers: four workgroups per compute unit), for
-      // the bf16 expert table gradients and the fp32 partial sums of the
-      // gate-table products
+      // bf16 expert table gradients and the fp32 partial sums of the
+      // gate-table products: one LDS buffer (experts that reach this kernel
+      // average under 256 rows, so a table-gradient tile runs a few K
+      // slices), and operand rows straight into LDS when they come in whole,
+      // aligned 16-byte pieces (no staging registers: four workgroups per
+      // compute unit; otherwise three for the table gradients)
       if ((g.mode == BW_WGT && !g.c_f32) || (g.mode == BW_PLAIN && g.c_f32 && g.ldc % 4 == 0 &&
                                               ((uintptr_t)g.C & 15) == 0)) {
         bool direct = g.zero && g.M % 8 == 0 && g.N % 8 == 0 && ((uintptr_t)g.zero & 15) == 0;
