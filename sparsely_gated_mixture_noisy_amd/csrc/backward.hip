@@ -451,9 +451,43 @@ struct RankBest {
 __device__ __forceinline__ bool rb_before(const RankBest& a, const RankBest& b) {
   return ranks_before(a.v, a.e, b.v, b.e);
 }
-__device__ __forceinline__ RankBest rb_xor(const RankBest& r, int off) {
-  return RankBest{__shfl_xor(r.v, off, 64), __shfl_xor(r.e, off, 64)};
+
+// The rank step's reductions over the 32 lanes of a half-wave (one row, 32
+// experts) run on DPP moves: quad swaps, half-row and row mirrors, then the
+// lower row's total broadcast into the upper row (lanes 16-31 and 48-63 end
+// with the half-wave's result).  Each step combines two equal partial results,
+// so the sums follow the balanced tree of an xor butterfly, bit for bit.
+constexpr int DPP_BCAST15 = 0x142;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ RankBest rb_dpp(const RankBest& r) {  // rows outside ROWS: r
+  return RankBest{__builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                      __builtin_bit_cast(int, r.v), __builtin_bit_cast(int, r.v), CTRL, ROWS, 0xF,
+                      false)),
+                  __builtin_amdgcn_update_dpp(r.e, r.e, CTRL, ROWS, 0xF, false)};
 }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float sum_dpp(float v) {  // rows outside ROWS: 0
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void rank_step(RankBest& wk, RankBest& bd, float& sk, float& sd) {
+  const RankBest ok = rb_dpp<CTRL, ROWS>(wk);
+  if (rb_before(wk, ok)) wk = ok;
+  const RankBest od = rb_dpp<CTRL, ROWS>(bd);
+  if (rb_before(od, bd)) bd = od;
+  sk += sum_dpp<CTRL, ROWS>(sk);
+  sd += sum_dpp<CTRL, ROWS>(sd);
+}
+// worst kept and best dropped expert, and the two sums, over the half-wave
+__device__ __forceinline__ void rank_half_reduce(RankBest& wk, RankBest& bd, float& sk, float& sd) {
+  rank_step<DPP_XOR1, 0xF>(wk, bd, sk, sd);
+  rank_step<DPP_XOR2, 0xF>(wk, bd, sk, sd);
+  rank_step<DPP_HALF_MIRROR, 0xF>(wk, bd, sk, sd);
+  rank_step<DPP_MIRROR, 0xF>(wk, bd, sk, sd);
+  rank_step<DPP_BCAST15, 0xA>(wk, bd, sk, sd);
+}
+constexpr int RANK_LANE = 31;  // the half-wave lane that holds the reductions
 
 // The gate tile's shared set-up: rows, the x tile, kept masks (bit r of
 // sb[e]: tile row r keeps expert e), kept experts per row, thresholds.
@@ -470,21 +504,26 @@ __device__ void bw_tile_setup(const BwGateArgs& a, BwTileShared& sh, uint32_t* s
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
   if (tid < GATE_ROWS) sh.rows[tid] = (int)min<int64_t>(t0 + tid, a.T - 1);
   for (int i = tid; i < a.E; i += GATE_THREADS) sb[i] = 0u;
+  // the rows' kept experts and thresholds are requested before the x tile,
+  // so that the tile's wait covers them too
+  const int64_t t = t0 + tid;
+  const bool valid = tid < GATE_ROWS && t < a.T;
+  int ke[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ke[s] = (valid && s < a.k) ? a.idx[t * a.k + s] : -1;
+  const float kth = (valid && a.thr) ? a.thr[2 * t] : 0.f;
+  const float k1th = (valid && a.thr) ? a.thr[2 * t + 1] : 0.f;
   __syncthreads();
+  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, sh.rows, GATE_ROWS, Xs, xld);
   if (tid < GATE_ROWS) {
-    const int64_t t = t0 + tid;
-    const bool valid = t < a.T;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      int e = -1;
-      if (valid && s < a.k) e = a.idx[t * a.k + s];
-      sh.kle[tid][s] = e;
-      if (e >= 0) atomicOr(&sb[e], 1u << tid);
+      sh.kle[tid][s] = ke[s];
+      if (ke[s] >= 0) atomicOr(&sb[ke[s]], 1u << tid);
     }
-    sh.kth[tid] = (valid && a.thr) ? a.thr[2 * t] : 0.f;
-    sh.k1th[tid] = (valid && a.thr) ? a.thr[2 * t + 1] : 0.f;
+    sh.kth[tid] = kth;
+    sh.k1th[tid] = k1th;
   }
-  if (XLDS) load_x_tile((const bf16_t*)a.x, a.d, sh.rows, GATE_ROWS, Xs, xld);
   __syncthreads();
 }
 
@@ -594,19 +633,9 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_rank_kernel(BwGateArgs a
     }
     // across the 32 lanes of a half-wave (the experts of one row in this block)
 #pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const RankBest ok = rb_xor(worst_kept[r], off);
-        if (rb_before(worst_kept[r], ok)) worst_kept[r] = ok;
-        const RankBest od = rb_xor(best_drop[r], off);
-        if (rb_before(od, best_drop[r])) best_drop[r] = od;
-        s_kept[r] += __shfl_xor(s_kept[r], off, 64);
-        s_drop[r] += __shfl_xor(s_drop[r], off, 64);
-      }
-    }
+    for (int r = 0; r < 16; ++r) rank_half_reduce(worst_kept[r], best_drop[r], s_kept[r], s_drop[r]);
     // into the wave's slots, block after block (each row's slot has one writer)
-    if ((lane & 31) == 0) {
+    if ((lane & 31) == RANK_LANE) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = acc_row(r, lane);
@@ -694,16 +723,8 @@ __device__ __forceinline__ void rank_in_registers(const f32x16& cs, const f32x16
         else s_drop += dt;
       }
     }
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-      const RankBest ok = rb_xor(worst_kept, off);
-      if (rb_before(worst_kept, ok)) worst_kept = ok;
-      const RankBest od = rb_xor(best_drop, off);
-      if (rb_before(od, best_drop)) best_drop = od;
-      s_kept += __shfl_xor(s_kept, off, 64);
-      s_drop += __shfl_xor(s_drop, off, 64);
-    }
-    if ((lane & 31) == 0) {
+    rank_half_reduce(worst_kept, best_drop, s_kept, s_drop);
+    if ((lane & 31) == RANK_LANE) {
       wk[w][row] = worst_kept;
       bn[w][row] = best_drop;
       wsk[w][row] = 0.f + s_kept;
@@ -735,6 +756,9 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
   __shared__ BwTileShared sh;
   __shared__ int4 ri[GATE_ROWS];
   __shared__ float dhk[GATE_ROWS][8];
+  // the tile's gradients to H from the kept gates and the threshold terms, by
+  // (row, expert of the block); zero elsewhere
+  __shared__ float dhm[GATE_ROWS][GATE_BLOCK_E];
   __shared__ RankBest rk_wk[RANK ? GATE_WAVES : 1][GATE_ROWS], rk_bn[RANK ? GATE_WAVES : 1][GATE_ROWS];
   __shared__ float rk_wsk[RANK ? GATE_WAVES : 1][GATE_ROWS], rk_wsn[RANK ? GATE_WAVES : 1][GATE_ROWS];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
@@ -753,13 +777,24 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
   };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * GATE_ROWS;
+  // the row's rank terms and kept gates' gradients: requested here, placed in
+  // LDS once the tile set-up has waited for its own loads
+  int4 ri_r{};
+  float dhk_r[8];
   if (tid < GATE_ROWS) {
     const int64_t t = min<int64_t>(t0 + tid, a.T - 1);
-    if (!RANK) ri[tid] = reinterpret_cast<const int4*>(a.rinfo)[t];
+    if (!RANK) ri_r = reinterpret_cast<const int4*>(a.rinfo)[t];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dhk[tid][s] = s < a.k ? a.dhk[t * a.k + s] : 0.f;
+    for (int s = 0; s < 8; ++s) dhk_r[s] = s < a.k ? a.dhk[t * a.k + s] : 0.f;
   }
+  for (int i = tid; i < GATE_ROWS * GATE_BLOCK_E / 4; i += GATE_THREADS)
+    reinterpret_cast<float4*>(&dhm[0][0])[i] = float4{0.f, 0.f, 0.f, 0.f};
   bw_tile_setup<T, XLDS>(a, sh, sb, Xs, xld);
+  if (tid < GATE_ROWS) {  // read back only by this thread
+    if (!RANK) ri[tid] = ri_r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dhk[tid][s] = dhk_r[s];
+  }
   const bool smooth = NOISY && a.dload != nullptr;
   const int valid = (int)min<int64_t>(GATE_ROWS, a.T - t0);
   for (int blk = 0; blk < a.E; blk += GATE_BLOCK_E) {
@@ -769,6 +804,19 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
     if constexpr (RANK)
       rank_in_registers(cs, ss, hs, e, a.E, sb, sh, a.dload, smooth, rk_wk, rk_bn, rk_wsk, rk_wsn, ri,
                         t0, a.T);
+    // one thread per row places the row's terms: the kept gates' gradients,
+    // then the k-th and (k+1)-th scores' threshold terms added in that order
+    auto in_blk = [&](int x) { return x >= blk && x < blk + GATE_BLOCK_E; };
+    if (tid < GATE_ROWS) {
+      for (int s = 0; s < a.k; ++s) {
+        const int x = sh.kle[tid][s];
+        if (in_blk(x)) dhm[tid][x - blk] = dhk[tid][s];
+      }
+      const int4 rw = ri[tid];
+      if (in_blk(rw.x)) dhm[tid][rw.x - blk] += __int_as_float(rw.z);
+      if (in_blk(rw.y)) dhm[tid][rw.y - blk] += __int_as_float(rw.w);
+    }
+    __syncthreads();
     float bsum = 0.f;
     if (e < a.E) {
       const uint32_t km = sb[e];
@@ -777,15 +825,7 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
       for (int r = 0; r < 16; ++r) {
         const int row = acc_row(r, lane);
         const bool kept = (km >> row) & 1u;
-        float dh = 0.f;
-        if (kept) {
-#pragma unroll
-          for (int s = 0; s < 8; ++s)
-            if (sh.kle[row][s] == e) dh = dhk[row][s];
-        }
-        const int4 rw = ri[row];
-        if (e == rw.x) dh += __int_as_float(rw.z);
-        if (e == rw.y) dh += __int_as_float(rw.w);
+        const float dh = dhm[row][e - blk];
         float dc = dh;
         if (NOISY) {
           float dsp = dh * es[r];
@@ -825,6 +865,18 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
     }
     bsum += __shfl_xor(bsum, 32, 64);
     if (lane < 32 && e < a.E) a.dbias_part[(int64_t)blockIdx.x * a.E + e] = bsum;
+    if (blk + GATE_BLOCK_E < a.E) {  // clear the row's entries for the next block
+      __syncthreads();
+      if (tid < GATE_ROWS) {
+        for (int s = 0; s < a.k; ++s) {
+          const int x = sh.kle[tid][s];
+          if (in_blk(x)) dhm[tid][x - blk] = 0.f;
+        }
+        const int4 rw = ri[tid];
+        if (in_blk(rw.x)) dhm[tid][rw.x - blk] = 0.f;
+        if (in_blk(rw.y)) dhm[tid][rw.y - blk] = 0.f;
+      }
+    }
   }
   if constexpr (DXG) {
     __syncthreads();
@@ -834,39 +886,73 @@ __global__ __launch_bounds__(GATE_THREADS) void bw_gate_grad_kernel(BwGateArgs a
     const bf16_t* Dcl = Ds + GATE_ROWS * BWD_LD;
     const bf16_t* Drh = Ds + 2 * GATE_ROWS * BWD_LD;
     const bf16_t* Drl = Ds + 3 * GATE_ROWS * BWD_LD;
-    for (int cb = w; cb * 32 < a.d; cb += GATE_WAVES) {
-      const int col = cb * 32 + fr;
-      const bool cok = col < a.d;
-      const bf16_t* wg = a.wgt + (int64_t)(cok ? col : 0) * a.e16 + 8 * fh;
-      const bf16_t* wn = NOISY ? a.wnt + (int64_t)(cok ? col : 0) * a.e16 + 8 * fh : nullptr;
-      f32x16 acc = f32x16{};
-      for (int ks = 0; ks < nks; ++ks) {
-        const int k = ks * 16 + 8 * fh;
-        const bf16x8 zg = cok ? load_bf16x8(wg + ks * 16) : zero_bf16x8();
-        acc = mfma32(zg, load_bf16x8(Dch + fr * BWD_LD + k), acc);
-        acc = mfma32(zg, load_bf16x8(Dcl + fr * BWD_LD + k), acc);
-        if (NOISY) {
-          const bf16x8 zn = cok ? load_bf16x8(wn + ks * 16) : zero_bf16x8();
-          acc = mfma32(zn, load_bf16x8(Drh + fr * BWD_LD + k), acc);
-          acc = mfma32(zn, load_bf16x8(Drl + fr * BWD_LD + k), acc);
+    // Column blocks cb and cb + GATE_WAVES in one pass: each score-gradient
+    // fragment read from LDS feeds both blocks' MFMAs, and the two
+    // accumulators are independent chains.  Each block sums its k-steps in
+    // the order of the one-block loop (dclean hi, lo, draw hi, lo per step).
+    auto store_cols = [&](const f32x16& acc, int cb) {
+      // register group g: columns cb*32 + 8g + q4 .. +3 of row fr
+      if (fr >= valid || cb * 32 >= a.d) return;
+      float* orow = a.dxg + (t0 + fr) * a.d;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = cb * 32 + 8 * g + q4;
+        if (c + 3 < a.d) {
+          *reinterpret_cast<float4*>(orow + c) =
+              float4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (c + r < a.d) orow[c + r] = acc[4 * g + r];
         }
       }
-      // register group g: columns cb*32 + 8g + q4 .. +3 of row fr
-      if (fr < valid) {
-        float* orow = a.dxg + (t0 + fr) * a.d;
+    };
+    for (int cb = w; cb * 32 < a.d; cb += 2 * GATE_WAVES) {
+      const int cb2 = cb + GATE_WAVES;
+      const int col = cb * 32 + fr, col2 = cb2 * 32 + fr;
+      const bool cok = col < a.d, cok2 = col2 < a.d;
+      const int64_t o1 = (int64_t)(cok ? col : 0) * a.e16 + 8 * fh;
+      const int64_t o2 = (int64_t)(cok2 ? col2 : 0) * a.e16 + 8 * fh;
+      f32x16 acc = f32x16{}, acc2 = f32x16{};
+      // the tables' fragments of DXG_PF k-steps are requested together
+      // (steps past the last re-read the last one and go unused)
+      constexpr int DXG_PF = 4;
+      for (int ks0 = 0; ks0 < nks; ks0 += DXG_PF) {
+        bf16x8 zg[DXG_PF], zg2[DXG_PF], zn[DXG_PF], zn2[DXG_PF];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = cb * 32 + 8 * g + q4;
-          if (c + 3 < a.d) {
-            *reinterpret_cast<float4*>(orow + c) =
-                float4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-          } else {
+        for (int u = 0; u < DXG_PF; ++u) {
+          const int64_t ko = (int64_t)min(ks0 + u, nks - 1) * 16;
+          zg[u] = load_bf16x8(a.wgt + o1 + ko);
+          zg2[u] = load_bf16x8(a.wgt + o2 + ko);
+          if (NOISY) {
+            zn[u] = load_bf16x8(a.wnt + o1 + ko);
+            zn2[u] = load_bf16x8(a.wnt + o2 + ko);
+          }
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (c + r < a.d) orow[c + r] = acc[4 * g + r];
+        for (int u = 0; u < DXG_PF; ++u) {
+          if (ks0 + u < nks) {
+            const int k = (ks0 + u) * 16 + 8 * fh;
+            const bf16x8 dch = load_bf16x8(Dch + fr * BWD_LD + k);
+            const bf16x8 dcl = load_bf16x8(Dcl + fr * BWD_LD + k);
+            acc = mfma32(zg[u], dch, acc);
+            acc2 = mfma32(zg2[u], dch, acc2);
+            acc = mfma32(zg[u], dcl, acc);
+            acc2 = mfma32(zg2[u], dcl, acc2);
+            if (NOISY) {
+              const bf16x8 drh = load_bf16x8(Drh + fr * BWD_LD + k);
+              const bf16x8 drl = load_bf16x8(Drl + fr * BWD_LD + k);
+              acc = mfma32(zn[u], drh, acc);
+              acc2 = mfma32(zn2[u], drh, acc2);
+              acc = mfma32(zn[u], drl, acc);
+              acc2 = mfma32(zn2[u], drl, acc2);
+            }
           }
         }
       }
+      // lanes of columns past d read column 0 of the tables; those columns are not stored
+      store_cols(acc, cb);
+      store_cols(acc2, cb2);
     }
   }
 }
