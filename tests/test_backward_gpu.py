@@ -108,6 +108,11 @@ CASES = {
     # two expert blocks in the gate tiles, a bias, a ragged last tile, idle experts
     "bf16_e300_bias": (CONFIGS["zipf2048"].replace(tokens=230, n_experts=300, d_model=64,
                                                    d_hidden=128), 0.3, 2.0),
+    # three expert blocks in the gate tiles: a ragged last tile (333 = 10 x 32
+    # + 13) and a part-filled last block (600 = 2 x 256 + 88)
+    "bf16_e600_three_blocks": (CONFIGS["zipf2048"].replace(tokens=333, n_experts=600,
+                                                           d_model=128, d_hidden=64),
+                               0.4, 1.5),
     "bf16_noise_free_k3": (CONFIGS["flat256"].replace(tokens=260, n_experts=10, d_model=192,
                                                       d_hidden=320, noisy=False, top_k=3),
                            1.2, 0.0),
