@@ -413,8 +413,9 @@ typedef struct moe_grads {
 size_t moe_backward_workspace_size(const moe_config* cfg);
 
 /* The backward pass.  x, p (w_gate, w_noise, bias, w1, w2, w3, and for the
- * hierarchy w_gate_p, w_noise_p; packed tables are optional for the gate and
- * not used for the experts, whose unpacked w1 / w2 / w3 are required), noise
+ * hierarchy w_gate_p, w_noise_p; the unpacked w1 / w2 / w3 are required, and
+ * the packed tables are optional: w_gate_packed for the gate, w_packed for
+ * the W1 reads of the ReLU hidden layer's recompute at d_model 512), noise
  * (eps, and eps_p for the hierarchy, when noisy) and `saved` are the
  * forward's inputs and saved tensors (thr is not needed by the hierarchy);
  * dy [T][d] is in the cfg dtype.  Returns MOE_ERR_UNSUPPORTED for fp32

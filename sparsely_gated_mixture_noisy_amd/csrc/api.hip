@@ -464,6 +464,8 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
 struct BwLayout {
   size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, tiles_big, zero, hid, dp, db, dxs, part_g,
       part_n, xs, dys;
+  // tile map with descriptors of the fused hidden-layer kernel
+  size_t tiles_fz, desc_fz;
   // hierarchy: per-slot and per-group score gradients, and the routing
   // without capacity (when the forward capped it) for the secondary tables
   size_t cs, ns, dcp, drp, r_bits, r_base, r_counts, r_offsets, r_perm, r_inv;
@@ -531,6 +533,10 @@ BwLayout bw_layout(const moe_config* c) {
   L.dxg = take(4 * (size_t)T * d);
   L.tiles = take(4 * (size_t)(E + 1));
   L.tiles_big = take(4 * (size_t)(E + 1));
+  const bool fz = bw_hidden_fused_supported(es == 2, d, h, sw);
+  L.tiles_fz = take(fz ? 4 * (size_t)(E + 1) : 0);
+  L.desc_fz = take(fz ? 12 * (size_t)((A + bw_hidden_fused_rows() - 1) / bw_hidden_fused_rows() + E)
+                      : 0);
   L.zero = take(2 * (size_t)std::max(std::max(h, d), 128));
   L.hid = take(es * (size_t)A * h);
   L.dp = take(es * (size_t)A * h);
@@ -859,6 +865,26 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
         ha.d1 = dp;
         ha.d3 = db;
         MOE_TRY(hip_status(launch_bw_hidden_big(ha, sw, se), "backward hidden"));
+      } else if (bw_hidden_fused_supported(bf16, d, h, sw)) {
+        // ReLU at d_model 512: the hidden layer recomputed with its gradient,
+        // each tile streaming W1 and then W2 once
+        int32_t* tfz = at<int32_t>(ws, L.tiles_fz);
+        int32_t* dfz = at<int32_t>(ws, L.desc_fz);
+        MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_fused_rows(), tfz, dfz, se),
+                           "backward tiles"));
+        BwHidFusedArgs ha;
+        ha.xs = xs;
+        ha.dys = dys;
+        ha.tiles = tfz;
+        ha.desc = dfz;
+        ha.E = E;
+        ha.h = h;
+        ha.w1 = p->w1;
+        ha.w2 = p->w2;
+        ha.wp = p->w_packed;
+        ha.hid = hid;
+        ha.dp = dp;
+        MOE_TRY(hip_status(launch_bw_hidden_fused(ha, A, se), "backward hidden"));
       } else {
         // hidden layer recomputed with its gradient
         BwGemm q = product(op_rows(xs, d, f32), per_expert(op_rows(p->w1, d, f32), hd));
@@ -1568,6 +1594,12 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const moe_params* 
   }
   if (!p->w1 || !p->w2 || (sw && !p->w3))
     return fail(MOE_ERR_INVALID_ARG, "the backward pass needs the unpacked w1 / w2 (/ w3)");
+  if (p->w_packed) {
+    if (!packable(cfg))
+      return fail(MOE_ERR_UNSUPPORTED, "packed expert tables need bf16 ReLU, d_model 512");
+    if (reinterpret_cast<uintptr_t>(p->w_packed) & 15)
+      return fail(MOE_ERR_INVALID_ARG, "w_packed must be 16-byte aligned");
+  }
   if (p->w_gate_packed) {
     if (!gate_packable(cfg))
       return fail(MOE_ERR_UNSUPPORTED, "packed gate tables need bf16 and d_model %% 64 == 0");

@@ -162,6 +162,25 @@ struct BwHiddenArgs {
   void* d1;                // [A][h] in: dHid = dY W2; out: dP (ReLU) or dA (SwiGLU)
   void* d3;                // [A][h] out: dB (SwiGLU) or null
 };
+// The ReLU hidden layer's recompute and gradient at d_model 512 on tiles of
+// at most bw_hidden_fused_rows() rows of one expert (tile map with
+// descriptors), the tables streamed once per tile: hid = relu(xs W1^T) and
+// dp = (dys W2) * [xs W1^T > 0], both [A][h] bf16.
+struct BwHidFusedArgs {
+  const void* xs;          // [A][512] routed rows of x, in expert order
+  const void* dys;         // [A][512] gate-scaled output gradients, same order
+  const int32_t* tiles;    // [E+1] tile map (tiles[E] = number of tiles)
+  const int32_t* desc;     // [tiles][3] expert, first position, rows
+  int E, h;
+  const void* w1;          // [E][h][512]
+  const void* w2;          // [E][512][h]
+  const void* wp;          // the forward's packed tables (W1 read from them) or null
+  void* hid;               // [A][h] out
+  void* dp;                // [A][h] out
+};
+bool bw_hidden_fused_supported(bool bf16, int d, int h, bool swiglu);
+int bw_hidden_fused_rows();
+hipError_t launch_bw_hidden_fused(const BwHidFusedArgs& a, int64_t A, hipStream_t s);
 bool bw_hidden_big_tiles(bool bf16, int64_t A, int E);
 int bw_hidden_big_rows();
 hipError_t launch_bw_hidden_big(const BwHiddenArgs& a, bool swiglu, hipStream_t s);

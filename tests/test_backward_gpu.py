@@ -152,6 +152,15 @@ CASES = {
     # with a ragged last slice
     "bf16_zipf_one_buffer": (CONFIGS["zipf2048"].replace(tokens=1200, n_experts=160, d_model=64,
                                                          d_hidden=128), 0.5, 0.5),
+    # d_model 512 ReLU: the hidden layer on the fused per-tile kernel.  About
+    # 250 rows per expert: three tiles each (96, 96 and 58 rows: two and three
+    # 32-row blocks, a ragged last block), four hidden chunks
+    "bf16_d512_three_tiles": (CONFIGS["flat256"].replace(tokens=1000, n_experts=8, top_k=2),
+                              0.6, 1.1),
+    # the same kernel with two hidden chunks, a Zipf bias: idle experts,
+    # single-row experts and hot experts of several tiles
+    "bf16_d512_zipf_h512": (CONFIGS["zipf2048"].replace(tokens=700, n_experts=48, d_hidden=512),
+                            0.5, 0.9),
     # one group, then one expert: both softmax levels are a single weight of 1
     "bf16_hier_k1": (CONFIGS["hier4096"].replace(tokens=200, n_experts=64, d_model=128,
                                                  d_hidden=256, k_groups=1, k_per_group=1,
@@ -186,6 +195,27 @@ def test_backward_matches_oracle(name):
         a, b = getattr(g1, key), getattr(g2, key)
         if a is not None:
             assert torch.equal(a, b), f"{key} differs between two calls"
+
+
+@pytest.mark.parametrize("name", ["bf16_d512_three_tiles", "bf16_d512_zipf_h512"])
+def test_backward_packed_tables_match_plain(name):
+    """With the forward's packed expert tables the backward reads W1 from
+    them (the fused hidden-layer kernel): the same values in the same order,
+    so every gradient is bitwise equal to the plain-table call's."""
+    cfg, wi, wl = CASES[name]
+    seed, inp, _ = _inputs(cfg)
+    _say(f"[backward] packed against plain tables: {name} seed {seed}")
+    dy = make_upstream(cfg, seed=seed, device="cuda")
+    binp = L.packed_params(cfg, inp)
+    assert binp.get("w_packed") is not None
+    fwd = L.forward(cfg, inp["x"], inp, inp, wi, wl, balance=True, save=True)
+    g_plain = L.backward(cfg, inp["x"], inp, inp, fwd, dy, wi, wl)
+    g_packed = L.backward(cfg, inp["x"], binp, binp, fwd, dy, wi, wl)
+    torch.cuda.synchronize()
+    for key in KEYS:
+        a, b = getattr(g_plain, key), getattr(g_packed, key)
+        if a is not None:
+            assert torch.equal(a, b), f"{key} differs between packed and plain tables"
 
 
 @pytest.mark.parametrize("base", ["flat256", "hier4096"])
