@@ -24,6 +24,9 @@
 //     per-wave LDS slot as loaded (units contiguous) and come back in operand
 //     order through gfx950's transposing LDS read; dP is written with the
 //     phase-A sign applied.
+//   * both results leave through two LDS staging tiles (32 rows x 256 units,
+//     used in turn), so that every row's 512 bytes of a chunk are written as
+//     whole 16-byte pieces of contiguous rows.
 //
 // The accumulators of both phases have the same layout (lane l: row l % 32
 // of each 32-row block, four consecutive units per register group), so the
@@ -39,9 +42,10 @@ constexpr int BH_M = 32 * BH_MB;   // rows per tile at most
 constexpr int BH_H = 256;          // hidden units per chunk
 constexpr int BH_WAVES = 8;
 constexpr int BH_THREADS = 64 * BH_WAVES;
-constexpr int BH_RING = 8;         // table loads in flight per wave
+constexpr int BH_RING = 8;         // table loads in flight per wave (a divisor of BH_KS)
 constexpr int BH_MAXCH = 4;        // chunks at most (d_hidden <= 1024): sign bits in LDS
 constexpr int BH_KS = BH_D / 16;   // k-steps per chunk, both phases
+static_assert(BH_KS % BH_RING == 0, "every chunk starts at ring slot 0");
 constexpr int BH_XLD = BH_D + 8;   // LDS row stride of the row tile (elements)
 constexpr int BH_SLD = BH_H + 8;   // row stride of the output staging tile (elements)
 // Fragments per (expert, chunk, wave) in the forward's packed tables
@@ -49,9 +53,10 @@ constexpr int BH_SLD = BH_H + 8;   // row stride of the output staging tile (ele
 // order, followed by its second-layer fragments.
 constexpr int BH_PACK_NE = BH_KS + (BH_D / BH_WAVES / 32) * (BH_H / 16);
 
+// LDS: the row tile, one 16 x 32 slot per wave, the sign bits, two staging tiles
 size_t bw_hidden_fused_lds() {
-  return sizeof(bf16_t) * ((size_t)BH_M * BH_XLD + (size_t)BH_WAVES * 2 * 512) +
-         sizeof(uint64_t) * (size_t)BH_MAXCH * BH_WAVES * 64 + sizeof(bf16_t) * 32 * BH_SLD;
+  return sizeof(bf16_t) * ((size_t)BH_M * BH_XLD + (size_t)BH_WAVES * 512) +
+         sizeof(uint64_t) * (size_t)BH_MAXCH * BH_WAVES * 64 + sizeof(bf16_t) * 2 * 32 * BH_SLD;
 }
 
 bool bw_hidden_fused_supported(bool bf16, int d, int h, bool swiglu) {
@@ -85,21 +90,23 @@ __device__ __forceinline__ bf16x8 bh_slot_frag(const bf16_t* slot) {
 
 // One chunk's results for the tile's rows: wave w holds, for each 32-row
 // block i, pk[i][2g], pk[i][2g+1] = units 32w + 8g + 4 (l / 32) .. +3 of row
-// 32i + l % 32 as bf16 pairs.  Each block goes through the LDS staging tile
-// (32 rows x 256 units), so that the workgroup writes every row's 512 bytes
-// of the chunk as whole 16-byte pieces of contiguous rows; out points at unit
-// 0 of the chunk in the tile's first row.
+// 32i + l % 32 as bf16 pairs.  Each block goes through a staging tile (32
+// rows x 256 units), so that the workgroup writes every row's 512 bytes of
+// the chunk as whole 16-byte pieces of contiguous rows; out points at unit 0
+// of the chunk in the tile's first row.  Block b of the kernel's sequence of
+// blocks (b0 + i here) uses tile b % 2: the barrier after the writes of block
+// b also orders block b - 1's reads before block b + 1's writes.
 template <int MB>
 __device__ __forceinline__ void bh_write_chunk(bf16_t* out, int h, int m,
-                                               const uint32_t (&pk)[MB][8], bf16_t* St) {
+                                               const uint32_t (&pk)[MB][8], bf16_t* St, int b0) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 31, q4 = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    __syncthreads();  // the staging tile's previous readers are done
+    bf16_t* T = St + ((b0 + i) & 1) * 32 * BH_SLD;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<uint2*>(St + fr * BH_SLD + 32 * w + 8 * g + q4) =
+      *reinterpret_cast<uint2*>(T + fr * BH_SLD + 32 * w + 8 * g + q4) =
           uint2{pk[i][2 * g], pk[i][2 * g + 1]};
     __syncthreads();
 #pragma unroll
@@ -107,7 +114,7 @@ __device__ __forceinline__ void bh_write_chunk(bf16_t* out, int h, int m,
       const int c = tid + j * BH_THREADS, r = c >> 5, piece = c & 31;
       if (32 * i + r < m)
         *reinterpret_cast<u32x4*>(out + (int64_t)(32 * i + r) * h + 8 * piece) =
-            *reinterpret_cast<const u32x4*>(St + r * BH_SLD + 8 * piece);
+            *reinterpret_cast<const u32x4*>(T + r * BH_SLD + 8 * piece);
     }
   }
 }
@@ -220,15 +227,16 @@ __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, 
       }
     }
     Mk[(hc * BH_WAVES + w) * 64 + lane] = bits;
-    bh_write_chunk<MB>(hid + (int64_t)p0 * h + hc * BH_H, h, m, pk, St);
+    bh_write_chunk<MB>(hid + (int64_t)p0 * h + hc * BH_H, h, m, pk, St, hc * MB);
   }
 
   // ---- phase B: (dY W2)^T[units][rows] = W2^T[units] dY^T; dP ----
   __syncthreads();  // every wave is done with the x rows
   bh_load_rows<MB>((const bf16_t*)a.dys, p0, m, Rs);
   __syncthreads();
-  // the wave's two LDS slots of 16 x 32 W2 elements; piece s2 goes to slot s2 % 2
-  bf16_t* slot = Ws + w * 1024;
+  // the wave's LDS slot of 16 x 32 W2 elements: each piece is written after
+  // the previous one has been read (one wave's LDS accesses complete in order)
+  bf16_t* slot = Ws + w * 512;
   *reinterpret_cast<u32x4*>(slot + lane * 8) = take(NA, 0);
   bf16x8 wa = bh_slot_frag(slot);
   for (int hc = 0; hc < nch; ++hc) {
@@ -242,12 +250,11 @@ __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, 
 #pragma unroll
     for (int ks = 0; ks < BH_KS; ++ks) {
       // the next piece (of this chunk, the next one, or past the end) goes
-      // to the other slot and comes back as the next operand while this
+      // through the slot and comes back as the next operand while this
       // k-step's MFMAs run
-      bf16_t* nxt = slot + ((ks + 1) & 1) * 512;
-      *reinterpret_cast<u32x4*>(nxt + lane * 8) = take(NA + hc * BH_KS + ks + 1, (ks + 1) % BH_RING);
+      *reinterpret_cast<u32x4*>(slot + lane * 8) = take(NA + hc * BH_KS + ks + 1, (ks + 1) % BH_RING);
       const bf16x8 wcur = wa;
-      wa = bh_slot_frag(nxt);
+      wa = bh_slot_frag(slot);
       bf16x8 av[MB];
 #pragma unroll
       for (int i = 0; i < MB; ++i) av[i] = ya[i];
@@ -274,7 +281,7 @@ __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, 
         pk[i][2 * g + 1] = cvt_pk_bf16(v[2], v[3]);
       }
     }
-    bh_write_chunk<MB>(dp + (int64_t)p0 * h + hc * BH_H, h, m, pk, St);
+    bh_write_chunk<MB>(dp + (int64_t)p0 * h + hc * BH_H, h, m, pk, St, (nch + hc) * MB);
   }
 }
 
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(BH_THREADS, 1) void bw_hidden_fused_kernel(BwHidFus
   extern __shared__ __attribute__((aligned(16))) bf16_t bh_lds[];
   bf16_t* Rs = bh_lds;
   bf16_t* Ws = bh_lds + BH_M * BH_XLD;
-  uint64_t* Mk = reinterpret_cast<uint64_t*>(Ws + BH_WAVES * 2 * 512);
+  uint64_t* Mk = reinterpret_cast<uint64_t*>(Ws + BH_WAVES * 512);
   bf16_t* St = reinterpret_cast<bf16_t*>(Mk + BH_MAXCH * BH_WAVES * 64);
   // Workgroup b takes tile (b % 8) * ceil(Q / 8) + b / 8 of the Q tiles, so
   // that the tiles of an expert (consecutive in the map) run on one XCD
