@@ -822,15 +822,21 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
       // average at most 32 rows (a quarter of the accumulators; three
       // workgroups per compute unit keep more table loads in flight)
       const int prow = bw_pos_tile_rows(bf16, A, E);
-      MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, prow, tiles, nullptr, se),
-                         "backward tiles"));
+      // ReLU at d_model 512: the hidden layer and dX on per-tile streaming
+      // kernels (tile map of bw_hidden_fused_rows() rows, with descriptors)
+      const bool fz = !big && bw_hidden_fused_supported(bf16, d, h, sw);
+      int32_t* tfz = at<int32_t>(ws, L.tiles_fz);
+      int32_t* dfz = at<int32_t>(ws, L.desc_fz);
+      if (!fz)
+        MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, prow, tiles, nullptr, se),
+                           "backward tiles"));
       const int64_t row_tiles = (A + prow - 1) / prow + E;
       int32_t* tiles_big = at<int32_t>(ws, L.tiles_big);
       // dX on the large tiles from 128 rows per expert on average: one 256-row
       // tile then holds most experts whole, so each of an expert's two column
       // tiles reads its dP rows once (flat256 backward 0.849 -> 0.833 ms)
       const bool big_dx = bf16 && A >= 128 * (int64_t)E;
-      if (big || big_dx)
+      if (big || (big_dx && !fz))
         MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_big_rows(), tiles_big,
                                            nullptr, se),
                            "backward tiles"));
@@ -865,11 +871,9 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
         ha.d1 = dp;
         ha.d3 = db;
         MOE_TRY(hip_status(launch_bw_hidden_big(ha, sw, se), "backward hidden"));
-      } else if (bw_hidden_fused_supported(bf16, d, h, sw)) {
-        // ReLU at d_model 512: the hidden layer recomputed with its gradient,
-        // each tile streaming W1 and then W2 once
-        int32_t* tfz = at<int32_t>(ws, L.tiles_fz);
-        int32_t* dfz = at<int32_t>(ws, L.desc_fz);
+      } else if (fz) {
+        // the hidden layer recomputed with its gradient, each tile streaming
+        // W1 and then W2 once
         MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_fused_rows(), tfz, dfz, se),
                            "backward tiles"));
         BwHidFusedArgs ha;
@@ -907,7 +911,17 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
                            "backward hidden"));
       }
       // dX = dP W1 (+ dB W3), per routed row
-      if (big || big_dx) {
+      if (fz) {
+        BwDxFusedArgs da;
+        da.dp = dp;
+        da.tiles = tfz;
+        da.desc = dfz;
+        da.E = E;
+        da.h = h;
+        da.w1 = p->w1;
+        da.dxs = dxs;
+        MOE_TRY(hip_status(launch_bw_dx_fused(da, A, se), "backward expert dx"));
+      } else if (big || big_dx) {
         BwBigProduct q;
         q.a = dp;
         q.a2 = sw ? db : nullptr;

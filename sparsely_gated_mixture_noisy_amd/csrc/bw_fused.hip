@@ -285,6 +285,22 @@ __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, 
   }
 }
 
+// This workgroup's tile of the map: workgroup b takes tile (b % 8) *
+// ceil(Q / 8) + b / 8 of the Q tiles, so that the tiles of an expert
+// (consecutive in the map) run on one XCD (workgroups go to the XCDs
+// round-robin).  False for the workgroups past the last tile.
+__device__ __forceinline__ bool bh_find_tile(const int32_t* tiles, const int32_t* desc, int E,
+                                             int* e, int* p0, int* m) {
+  const int Q = tiles[E];
+  const int perx = (Q + 7) / 8;
+  const int slot = blockIdx.x >> 3, q = (blockIdx.x & 7) * perx + slot;
+  if (slot >= perx || q >= Q) return false;
+  *e = __builtin_amdgcn_readfirstlane(desc[3 * q]);
+  *p0 = __builtin_amdgcn_readfirstlane(desc[3 * q + 1]);
+  *m = __builtin_amdgcn_readfirstlane(desc[3 * q + 2]);
+  return true;
+}
+
 template <bool PACKED>
 __global__ __launch_bounds__(BH_THREADS, 1) void bw_hidden_fused_kernel(BwHidFusedArgs a) {
   extern __shared__ __attribute__((aligned(16))) bf16_t bh_lds[];
@@ -292,16 +308,8 @@ __global__ __launch_bounds__(BH_THREADS, 1) void bw_hidden_fused_kernel(BwHidFus
   bf16_t* Ws = bh_lds + BH_M * BH_XLD;
   uint64_t* Mk = reinterpret_cast<uint64_t*>(Ws + BH_WAVES * 512);
   bf16_t* St = reinterpret_cast<bf16_t*>(Mk + BH_MAXCH * BH_WAVES * 64);
-  // Workgroup b takes tile (b % 8) * ceil(Q / 8) + b / 8 of the Q tiles, so
-  // that the tiles of an expert (consecutive in the map) run on one XCD
-  // (workgroups go to the XCDs round-robin).
-  const int Q = a.tiles[a.E];
-  const int perx = (Q + 7) / 8;
-  const int slot = blockIdx.x >> 3, q = (blockIdx.x & 7) * perx + slot;
-  if (slot >= perx || q >= Q) return;
-  const int e = __builtin_amdgcn_readfirstlane(a.desc[3 * q]);
-  const int p0 = __builtin_amdgcn_readfirstlane(a.desc[3 * q + 1]);
-  const int m = __builtin_amdgcn_readfirstlane(a.desc[3 * q + 2]);
+  int e, p0, m;
+  if (!bh_find_tile(a.tiles, a.desc, a.E, &e, &p0, &m)) return;
   // only the 32-row blocks that hold rows run through the MFMAs
   const int mb = (m + 31) / 32;
   if (mb >= 3)
@@ -331,6 +339,174 @@ hipError_t launch_bw_hidden_fused(const BwHidFusedArgs& a, int64_t A, hipStream_
   if (A == 0) return hipSuccess;
   const int64_t grid = bw_hidden_fused_grid(A, a.E);
   return a.wp ? launch_bh<true>(a, grid, s) : launch_bh<false>(a, grid, s);
+}
+
+// ---------------------------------------------------------------------------
+// dX = dP W1 for the routed rows of the same tiles: dxs[p][c] = sum_u
+// dp[p][u] W1[e][u][c], c < 512.  W1's contraction index (u) is its slow one,
+// so its 16-unit by 32-column pieces take the per-wave LDS slot and the
+// transposing read as W2 does in the hidden-layer kernel.  Wave w owns
+// output columns 64w .. +63 (two 32-column blocks), the accumulators of the
+// tile's rows stay in registers across the hidden chunks, and the tile's dP
+// rows pass through LDS one chunk of 256 units at a time (two buffers: chunk
+// hc + 1 is loaded into registers while chunk hc's MFMAs run).  The output
+// leaves through LDS as 16-byte pieces of whole rows.
+// ---------------------------------------------------------------------------
+constexpr int BD_KS = BH_H / 16;   // k-steps per chunk (16 units each)
+
+size_t bw_dx_fused_lds() {
+  return sizeof(bf16_t) * (2 * (size_t)BH_M * BH_SLD + (size_t)BH_WAVES * 2 * 512);
+}
+
+template <int MB>
+__device__ __forceinline__ void bd_tile(const BwDxFusedArgs& a, int e, int p0, int m, bf16_t* Ps,
+                                        bf16_t* Ws) {
+  constexpr int CPT = 2 * MB;  // 16-byte pieces of a dP chunk per thread
+  static_assert((2 * BD_KS) % BH_RING == 0, "every chunk starts at ring slot 0");
+  static_assert(2 * BH_M * BH_SLD >= BH_M * BH_XLD, "the output tile fits the dP buffers");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int fr = lane & 31, fk = (lane >> 5) * 8, q4 = (lane >> 5) * 4;
+  const int h = a.h, nch = h / BH_H, NS = nch * BD_KS * 2;
+  const bf16_t* w1e = (const bf16_t*)a.w1 + (int64_t)e * h * BH_D;
+  const bf16_t* dp = (const bf16_t*)a.dp;
+  // piece s: k-step s / 2 (units 16 (s / 2) .. +15: W1 row 16 (s / 2) + lane
+  // / 4), column block s % 2 (columns 64w + 32 (s % 2) + 8 (lane % 4) .. +7)
+  auto frag = [&](int s) -> u32x4 {
+    s = min(s, NS - 1);
+    return *reinterpret_cast<const u32x4*>(w1e + (int64_t)(16 * (s >> 1) + (lane >> 2)) * BH_D +
+                                           64 * w + 32 * (s & 1) + 8 * (lane & 3));
+  };
+  u32x4 ring[BH_RING];
+#pragma unroll
+  for (int i = 0; i < BH_RING; ++i) ring[i] = frag(i);
+  auto take = [&](int s, int i) -> u32x4 {
+    const u32x4 v = ring[i];
+    ring[i] = frag(s + BH_RING);
+    return v;
+  };
+  // chunk hc of the tile's dP rows: piece c = tid + BH_THREADS i is row c /
+  // 32, units hc * BH_H + 8 (c % 32) .. +7 (zeros past m)
+  auto load_chunk = [&](int hc, u32x4 (&v)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * BH_THREADS, r = c >> 5;
+      v[i] = r < m ? *reinterpret_cast<const u32x4*>(dp + (int64_t)(p0 + r) * h + hc * BH_H +
+                                                     8 * (c & 31))
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto put_chunk = [&](bf16_t* P, const u32x4 (&v)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * BH_THREADS;
+      *reinterpret_cast<u32x4*>(P + (c >> 5) * BH_SLD + 8 * (c & 31)) = v[i];
+    }
+  };
+  {
+    u32x4 v[CPT];
+    load_chunk(0, v);
+    put_chunk(Ps, v);
+  }
+  // the wave's two LDS slots (one per column block) and the first k-step's
+  // operands; each piece is written after the previous one in its slot has
+  // been read (one wave's LDS accesses complete in order)
+  bf16_t* sl0 = Ws + w * 1024;
+  bf16_t* sl1 = sl0 + 512;
+  *reinterpret_cast<u32x4*>(sl0 + lane * 8) = take(0, 0);
+  *reinterpret_cast<u32x4*>(sl1 + lane * 8) = take(1, 1);
+  bf16x8 wa0 = bh_slot_frag(sl0), wa1 = bh_slot_frag(sl1);
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  __syncthreads();
+  for (int hc = 0; hc < nch; ++hc) {
+    const bf16_t* P = Ps + (hc & 1) * BH_M * BH_SLD;
+    const bool more = hc + 1 < nch;
+    u32x4 nv[CPT];
+    if (more) load_chunk(hc + 1, nv);
+    bf16x8 pa[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      pa[i] = *reinterpret_cast<const bf16x8*>(P + (32 * i + fr) * BH_SLD + fk);
+#pragma unroll
+    for (int ks = 0; ks < BD_KS; ++ks) {
+      // the next k-step's two pieces (this chunk's, the next one's first, or
+      // past the end) go through the slots while this k-step's MFMAs run
+      const int sn = 2 * (hc * BD_KS + ks + 1);
+      *reinterpret_cast<u32x4*>(sl0 + lane * 8) = take(sn, (2 * ks + 2) % BH_RING);
+      *reinterpret_cast<u32x4*>(sl1 + lane * 8) = take(sn + 1, (2 * ks + 3) % BH_RING);
+      const bf16x8 c0 = wa0, c1 = wa1;
+      wa0 = bh_slot_frag(sl0);
+      wa1 = bh_slot_frag(sl1);
+      bf16x8 av[MB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) av[i] = pa[i];
+      if (ks + 1 < BD_KS) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          pa[i] = *reinterpret_cast<const bf16x8*>(P + (32 * i + fr) * BH_SLD + (ks + 1) * 16 + fk);
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        acc[i][0] = mfma32(c0, av[i], acc[i][0]);
+        acc[i][1] = mfma32(c1, av[i], acc[i][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the other buffer was last read in chunk hc - 1, before the previous barrier
+    if (more) put_chunk(Ps + ((hc + 1) & 1) * BH_M * BH_SLD, nv);
+    __syncthreads();
+  }
+  // dX -> bf16 -> LDS (the dP buffers) -> 16-byte pieces of whole rows;
+  // register group g of acc[i][j] holds columns 64w + 32j + 8g + q4 .. +3 of
+  // row 32i + fr
+  bf16_t* O = Ps;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(O + (32 * i + fr) * BH_XLD + 64 * w + 32 * j + 8 * g + q4) =
+            uint2{cvt_pk_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                  cvt_pk_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+  __syncthreads();
+  bf16_t* dxs = (bf16_t*)a.dxs;
+  for (int c = tid; c < m * (BH_D / 8); c += BH_THREADS) {
+    const int r = c / (BH_D / 8), cc = (c % (BH_D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(dxs + (int64_t)(p0 + r) * BH_D + cc) =
+        *reinterpret_cast<const u32x4*>(O + r * BH_XLD + cc);
+  }
+}
+
+__global__ __launch_bounds__(BH_THREADS, 1) void bw_dx_fused_kernel(BwDxFusedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t bd_lds[];
+  bf16_t* Ps = bd_lds;
+  bf16_t* Ws = bd_lds + 2 * BH_M * BH_SLD;
+  int e, p0, m;
+  if (!bh_find_tile(a.tiles, a.desc, a.E, &e, &p0, &m)) return;
+  const int mb = (m + 31) / 32;
+  if (mb >= 3)
+    bd_tile<3>(a, e, p0, m, Ps, Ws);
+  else if (mb == 2)
+    bd_tile<2>(a, e, p0, m, Ps, Ws);
+  else
+    bd_tile<1>(a, e, p0, m, Ps, Ws);
+}
+
+hipError_t launch_bw_dx_fused(const BwDxFusedArgs& a, int64_t A, hipStream_t s) {
+  if (A == 0) return hipSuccess;
+  static bool attr_done = false;
+  const size_t lds = bw_dx_fused_lds();
+  if (!attr_done) {
+    hipError_t err = hipFuncSetAttribute((const void*)bw_dx_fused_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(bw_dx_fused_kernel, dim3((unsigned)bw_hidden_fused_grid(A, a.E)),
+                     dim3(BH_THREADS), lds, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

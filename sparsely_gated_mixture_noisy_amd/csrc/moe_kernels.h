@@ -178,6 +178,16 @@ struct BwHidFusedArgs {
   void* hid;               // [A][h] out
   void* dp;                // [A][h] out
 };
+// dxs = dp W1 ([A][512] bf16) for the same layers, on the same tile map
+struct BwDxFusedArgs {
+  const void* dp;          // [A][h] bf16
+  const int32_t* tiles;    // [E+1] tile map of bw_hidden_fused_rows() rows
+  const int32_t* desc;     // [tiles][3]
+  int E, h;
+  const void* w1;          // [E][h][512]
+  void* dxs;               // [A][512] out
+};
+hipError_t launch_bw_dx_fused(const BwDxFusedArgs& a, int64_t A, hipStream_t s);
 bool bw_hidden_fused_supported(bool bf16, int d, int h, bool swiglu);
 int bw_hidden_fused_rows();
 hipError_t launch_bw_hidden_fused(const BwHidFusedArgs& a, int64_t A, hipStream_t s);
