@@ -808,7 +808,10 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
     // the routed rows of x and the gate-scaled output gradients, in expert order
     void* xs = at<void>(ws, L.xs);
     void* dys = at<void>(ws, L.dys);
-    if (A > 0) {
+    // the fused hidden-layer kernel gathers the rows itself
+    const bool gathers_in_kernel =
+        !bw_hidden_big_tiles(bf16, A, E) && bw_hidden_fused_supported(bf16, d, h, sw);
+    if (A > 0 && !gathers_in_kernel) {
       MOE_TRY(hip_status(launch_bw_gather_rows(x, sv->perm, k, nullptr, A, d, bf16, xs, se),
                          "backward gather x"));
       MOE_TRY(hip_status(launch_bw_gather_rows(dy, sv->perm, k, sv->topk_gate, A, d, bf16, dys, se),
@@ -877,6 +880,11 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
         MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_fused_rows(), tfz, dfz, se),
                            "backward tiles"));
         BwHidFusedArgs ha;
+        ha.x = x;
+        ha.dy = dy;
+        ha.perm = sv->perm;
+        ha.gate = sv->topk_gate;
+        ha.k = k;
         ha.xs = xs;
         ha.dys = dys;
         ha.tiles = tfz;

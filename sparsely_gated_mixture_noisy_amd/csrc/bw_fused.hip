@@ -13,6 +13,9 @@
 //     the tile map (its 32-row blocks spread evenly over the expert's tiles);
 //     the tiles of an expert run on one XCD together and share the table
 //     stream through its L2;
+//   * the tile gathers its routed rows itself (x, and dy times the slot's
+//     gate) and also writes them out in expert order for the table
+//     gradients;
 //   * phase A: the tile's x rows sit in LDS; for each chunk of 256 hidden
 //     units, wave w computes a^T for its 32 units (v_mfma_f32_32x32x16_bf16,
 //     W1 fragment as operand A, streamed through a register ring), writes
@@ -119,10 +122,14 @@ __device__ __forceinline__ void bh_write_chunk(bf16_t* out, int h, int m,
   }
 }
 
-// rows p0 .. p0 + m - 1 of src ([A][D], expert order) into the LDS tile,
-// zeros past m up to the tile's 32-row blocks
+// The tile's routed rows into the LDS tile (zeros past m up to the tile's
+// 32-row blocks) and out to out[p0 + r] (the rows in expert order, for the
+// table gradients): row r is src[src_row[r]], times scale[r] when scale is
+// given (rounded to bf16 as the forward's gate-scaled products are).
 template <int MB>
-__device__ __forceinline__ void bh_load_rows(const bf16_t* src, int p0, int m, bf16_t* Rs) {
+__device__ __forceinline__ void bh_gather_rows(const bf16_t* src, const int* src_row,
+                                               const float* scale, int p0, int m, bf16_t* Rs,
+                                               bf16_t* out) {
   constexpr int CPR = BH_D / 8;
   constexpr int XCH = 32 * MB * CPR;
   constexpr int XPT = (XCH + BH_THREADS - 1) / BH_THREADS;
@@ -131,13 +138,25 @@ __device__ __forceinline__ void bh_load_rows(const bf16_t* src, int p0, int m, b
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int c = tid + i * BH_THREADS, r = c / CPR, cc = (c % CPR) * 8;
-    v[i] = (c < XCH && r < m) ? *reinterpret_cast<const u32x4*>(src + (int64_t)(p0 + r) * BH_D + cc)
-                              : u32x4{0u, 0u, 0u, 0u};
+    v[i] = (c < XCH && r < m)
+               ? *reinterpret_cast<const u32x4*>(src + (int64_t)src_row[r] * BH_D + cc)
+               : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int c = tid + i * BH_THREADS, r = c / CPR, cc = (c % CPR) * 8;
-    if (c < XCH) *reinterpret_cast<u32x4*>(Rs + r * BH_XLD + cc) = v[i];
+    if (c < XCH) {
+      u32x4 o = v[i];
+      if (scale && r < m) {
+        const float sc = scale[r];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = cvt_pk_bf16(__uint_as_float(o[j] << 16) * sc,
+                             __uint_as_float(o[j] & 0xffff0000u) * sc);
+      }
+      *reinterpret_cast<u32x4*>(Rs + r * BH_XLD + cc) = o;
+      if (r < m) *reinterpret_cast<u32x4*>(out + (int64_t)(p0 + r) * BH_D + cc) = o;
+    }
   }
 }
 
@@ -150,7 +169,8 @@ __device__ __forceinline__ void bh_load_rows(const bf16_t* src, int p0, int m, b
 // depth across chunks and phases.
 template <int MB, bool PACKED>
 __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, int m,
-                                        bf16_t* Rs, bf16_t* Ws, uint64_t* Mk, bf16_t* St) {
+                                        bf16_t* Rs, bf16_t* Ws, uint64_t* Mk, bf16_t* St,
+                                        int* s_row, float* s_gate) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 31, fk = (lane >> 5) * 8, q4 = (lane >> 5) * 4;
   const int h = a.h, nch = h / BH_H, NA = nch * BH_KS, NS = 2 * NA;
@@ -183,7 +203,14 @@ __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, 
     return v;
   };
 
-  bh_load_rows<MB>((const bf16_t*)a.xs, p0, m, Rs);
+  // the routed rows' sources (token perm[p] / k) and gates
+  if (tid < m) {
+    const int asg = a.perm[p0 + tid];
+    s_row[tid] = asg / a.k;
+    s_gate[tid] = a.gate[asg];
+  }
+  __syncthreads();
+  bh_gather_rows<MB>((const bf16_t*)a.x, s_row, nullptr, p0, m, Rs, (bf16_t*)a.xs);
   __syncthreads();
   bf16_t* hid = (bf16_t*)a.hid;
   bf16_t* dp = (bf16_t*)a.dp;
@@ -232,7 +259,7 @@ __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, 
 
   // ---- phase B: (dY W2)^T[units][rows] = W2^T[units] dY^T; dP ----
   __syncthreads();  // every wave is done with the x rows
-  bh_load_rows<MB>((const bf16_t*)a.dys, p0, m, Rs);
+  bh_gather_rows<MB>((const bf16_t*)a.dy, s_row, s_gate, p0, m, Rs, (bf16_t*)a.dys);
   __syncthreads();
   // the wave's LDS slot of 16 x 32 W2 elements: each piece is written after
   // the previous one has been read (one wave's LDS accesses complete in order)
@@ -308,16 +335,18 @@ __global__ __launch_bounds__(BH_THREADS, 1) void bw_hidden_fused_kernel(BwHidFus
   bf16_t* Ws = bh_lds + BH_M * BH_XLD;
   uint64_t* Mk = reinterpret_cast<uint64_t*>(Ws + BH_WAVES * 512);
   bf16_t* St = reinterpret_cast<bf16_t*>(Mk + BH_MAXCH * BH_WAVES * 64);
+  __shared__ int s_row[BH_M];
+  __shared__ float s_gate[BH_M];
   int e, p0, m;
   if (!bh_find_tile(a.tiles, a.desc, a.E, &e, &p0, &m)) return;
   // only the 32-row blocks that hold rows run through the MFMAs
   const int mb = (m + 31) / 32;
   if (mb >= 3)
-    bh_tile<3, PACKED>(a, e, p0, m, Rs, Ws, Mk, St);
+    bh_tile<3, PACKED>(a, e, p0, m, Rs, Ws, Mk, St, s_row, s_gate);
   else if (mb == 2)
-    bh_tile<2, PACKED>(a, e, p0, m, Rs, Ws, Mk, St);
+    bh_tile<2, PACKED>(a, e, p0, m, Rs, Ws, Mk, St, s_row, s_gate);
   else
-    bh_tile<1, PACKED>(a, e, p0, m, Rs, Ws, Mk, St);
+    bh_tile<1, PACKED>(a, e, p0, m, Rs, Ws, Mk, St, s_row, s_gate);
 }
 
 template <bool PACKED>

@@ -165,10 +165,16 @@ struct BwHiddenArgs {
 // The ReLU hidden layer's recompute and gradient at d_model 512 on tiles of
 // at most bw_hidden_fused_rows() rows of one expert (tile map with
 // descriptors), the tables streamed once per tile: hid = relu(xs W1^T) and
-// dp = (dys W2) * [xs W1^T > 0], both [A][h] bf16.
+// dp = (dys W2) * [xs W1^T > 0], both [A][h] bf16, where the kernel gathers
+// xs and dys itself (and writes them out).
 struct BwHidFusedArgs {
-  const void* xs;          // [A][512] routed rows of x, in expert order
-  const void* dys;         // [A][512] gate-scaled output gradients, same order
+  const void* x;           // [T][512]
+  const void* dy;          // [T][512] output gradients
+  const int32_t* perm;     // [A] routing: position p holds assignment perm[p]
+  const float* gate;       // [A] the assignments' gates
+  int k;
+  void* xs;                // [A][512] out: routed rows of x, in expert order
+  void* dys;               // [A][512] out: gate-scaled output gradients, same order
   const int32_t* tiles;    // [E+1] tile map (tiles[E] = number of tiles)
   const int32_t* desc;     // [tiles][3] expert, first position, rows
   int E, h;
