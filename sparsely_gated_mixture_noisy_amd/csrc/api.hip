@@ -417,7 +417,29 @@ moe_status do_ffn(const moe_config* c, const Layout& L, const void* x, const int
   return hip_status(launch_expert_ffn(f, bf16, sw, s), "experts");
 }
 
-// have_part: the gate kernel already wrote the smooth-load partial sums.
+// The smooth load's partial sums (flat noisy gate), recomputing the
+// projections from the gate's thresholds.
+moe_status smooth_load_partials(const moe_config* c, const Layout& L, const void* x,
+                                const moe_params* p, const int32_t* idx, const float* thr,
+                                void* ws, hipStream_t s) {
+  LoadArgs la;
+  la.x = x;
+  la.w_gate = p->w_gate;
+  la.w_noise = p->w_noise;
+  la.bias = p->bias;
+  la.idx = idx;
+  la.thr = thr;
+  la.T = c->tokens;
+  la.d = c->d_model;
+  la.E = c->n_experts;
+  la.k = c->top_k;
+  la.part = at<float>(ws, L.part);
+  la.w_pack = p->w_gate_packed;
+  return hip_status(launch_load_partial(la, c->dtype == MOE_BF16, s), "load");
+}
+
+// have_part: the smooth-load partial sums are already written (by the gate
+// kernel, or by smooth_load_partials on the stream s follows).
 moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const moe_params* p,
                       const int32_t* idx, const float* gate, const float* thr,
                       const int32_t* perm, const int32_t* offsets, float wi, float wl,
@@ -426,22 +448,7 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
   const int E = c->n_experts;
   const bool smooth = c->n_groups == 0 && c->noisy && c->tokens > 0;
   float* part = smooth ? at<float>(ws, L.part) : nullptr;
-  if (smooth && !have_part) {
-    LoadArgs la;
-    la.x = x;
-    la.w_gate = p->w_gate;
-    la.w_noise = p->w_noise;
-    la.bias = p->bias;
-    la.idx = idx;
-    la.thr = thr;
-    la.T = c->tokens;
-    la.d = c->d_model;
-    la.E = E;
-    la.k = c->top_k;
-    la.part = part;
-    la.w_pack = p->w_gate_packed;
-    MOE_TRY(hip_status(launch_load_partial(la, c->dtype == MOE_BF16, s), "load"));
-  }
+  if (smooth && !have_part) MOE_TRY(smooth_load_partials(c, L, x, p, idx, thr, ws, s));
   BalanceArgs b;
   b.perm = perm;
   b.offsets = offsets;
@@ -745,7 +752,7 @@ moe_status side_stream(hipStream_t* out) {
 // queued on it after a failed call still follows everything the call launched.
 struct SideJoin {
   hipStream_t main, side;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_mid = nullptr;
   bool forked = false, recorded = false, waited = false;
   explicit SideJoin(hipStream_t s) : main(s), side(s) {}
   SideJoin(const SideJoin&) = delete;
@@ -761,6 +768,14 @@ struct SideJoin {
     side = t;
     forked = true;
     return MOE_OK;
+  }
+  // the side stream waits for everything queued on the caller's stream so far
+  moe_status side_follows_main() {
+    if (!forked) return MOE_OK;
+    if (!ev_mid)
+      MOE_TRY(hip_status(hipEventCreateWithFlags(&ev_mid, hipEventDisableTiming), "hipEventCreate"));
+    MOE_TRY(hip_status(hipEventRecord(ev_mid, main), "hipEventRecord"));
+    return hip_status(hipStreamWaitEvent(side, ev_mid, 0), "hipStreamWaitEvent");
   }
   moe_status record() {
     if (!forked || recorded) return MOE_OK;
@@ -781,6 +796,7 @@ struct SideJoin {
     }
     if (ev_fork) (void)hipEventDestroy(ev_fork);
     if (ev_join) (void)hipEventDestroy(ev_join);
+    if (ev_mid) (void)hipEventDestroy(ev_mid);
   }
 };
 
@@ -1295,9 +1311,10 @@ moe_status check_forward_args(const moe_config* cfg, const void* x, const moe_pa
 }
 
 // The layer on a validated call, with its scratch at ws (layout(cfg) bytes).
+// side: the smooth-load recompute may run on the device's side stream.
 moe_status forward_on(const moe_config* cfg, const void* x, const moe_params* p,
                       const moe_noise* noise, float w_importance, float w_load,
-                      moe_outputs* out, void* ws, void* stream) {
+                      moe_outputs* out, void* ws, void* stream, bool side = true) {
   const Layout L = layout(cfg);
   hipStream_t s = (hipStream_t)stream;
   int32_t* idx = out->topk_idx ? out->topk_idx : at<int32_t>(ws, L.idx);
@@ -1336,6 +1353,17 @@ moe_status forward_on(const moe_config* cfg, const void* x, const moe_params* p,
   }
   MOE_TRY(do_gate(cfg, L, x, p, noise, idx, gate, thr, part, bits,
                   const_cast<float*>(st.imp_part), ws, s));
+  // More than one expert block: the smooth load recomputes the projections
+  // (MFMA and VALU work) on the device's side stream, beside the routing and
+  // the expert stage (bound by the table stream); the balance reduction
+  // waits for both.  The caller's stream waits for the side stream on every
+  // return path.
+  SideJoin join(s);
+  const bool side_load = side && smooth && !fused_stats;
+  if (side_load) {
+    MOE_TRY(join.fork());
+    MOE_TRY(smooth_load_partials(cfg, L, x, p, idx, thr, ws, join.side));
+  }
   MOE_TRY(do_route(cfg, L, idx, counts, offsets, perm, inv, flat, tiles, ws, s, st));
   MOE_TRY(do_ffn(cfg, L, x, perm, offsets, p, y_sorted, tiles, ws, s));
   MOE_TRY(hip_status(launch_combine(y_sorted, inv, gate, cfg->tokens, cfg->top_k, cfg->d_model,
@@ -1354,8 +1382,15 @@ moe_status forward_on(const moe_config* cfg, const void* x, const moe_params* p,
       bperm = perm_u;
       boff = off_u;
     }
-    MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, bperm, boff, w_importance, w_load, imp, load,
-                       out->balance, false, ws, s));
+    if (side_load) {
+      MOE_TRY(join.side_follows_main());
+      MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, bperm, boff, w_importance, w_load, imp,
+                         load, out->balance, true, ws, join.side));
+      MOE_TRY(join.wait());
+    } else {
+      MOE_TRY(do_balance(cfg, L, x, p, idx, gate, thr, bperm, boff, w_importance, w_load, imp,
+                         load, out->balance, false, ws, s));
+    }
   }
   return ok();
 }
@@ -1407,7 +1442,9 @@ moe_status moe_forward_static(const moe_config* cfg, const void* x, const moe_pa
                 need, (size_t)MOE_FORWARD_STATIC_SCRATCH_BYTES);
   void* ws = nullptr;
   MOE_TRY(scratch_ptr(&ws));
-  return forward_on(cfg, x, p, noise, w_importance, w_load, out, ws, stream);
+  // no side stream: its first use would create it, and the fork and join
+  // create events
+  return forward_on(cfg, x, p, noise, w_importance, w_load, out, ws, stream, false);
 }
 
 // ---- per-batch equal-size mask ---------------------------------------------
