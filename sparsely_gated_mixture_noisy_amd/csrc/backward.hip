@@ -973,9 +973,19 @@ __global__ __launch_bounds__(1024) void bw_sum_rows_kernel(const float* part, in
   __shared__ float ws[16][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  // rows w, w + 16, ... in order, eight loads in flight at a time
   float s = 0.f;
-  if (c < ncol)
-    for (int64_t r = w; r < nrow; r += 16) s += part[r * ncol + c];
+  if (c < ncol) {
+    int64_t r = w;
+    for (; r + 16 * 7 < nrow; r += 16 * 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[(r + 16 * j) * ncol + c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; r < nrow; r += 16) s += part[r * ncol + c];
+  }
   ws[w][lane] = s;
   __syncthreads();
   if (w == 0 && c < ncol) {
@@ -991,8 +1001,17 @@ __global__ __launch_bounds__(256) void bw_sum_chunks_kernel(const float* part, i
                                                             int64_t n, TO* out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
+  // eight chunks' loads in flight at a time, added in chunk order
   float s = 0.f;
-  for (int c = 0; c < nchunk; ++c) s += part[(int64_t)c * n + i];
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = part[(int64_t)(c + j) * n + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; c < nchunk; ++c) s += part[(int64_t)c * n + i];
   Elem<TO>::store(out, i, s);
 }
 
