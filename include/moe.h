@@ -281,7 +281,13 @@ typedef struct moe_outputs {
   void* y_sorted;     /* [A][d] expert outputs in routed order */
 } moe_outputs;
 
-/* The whole layer: gate -> route -> experts -> combine (-> balance). */
+/* The whole layer: gate -> route -> experts -> combine (-> balance).
+ * Streams: the work is ordered on `stream`.  For a flat noisy gate with more
+ * than 256 experts and the balance statistics on, the smooth load's
+ * recompute and the balance reduction run on the device's second stream
+ * (the one moe_backward uses for its expert side), forked from `stream`
+ * after the gate and joined back to it with events before the call returns,
+ * on error paths too. */
 moe_status moe_forward(const moe_config* cfg, const void* x,
                        const moe_params* p, const moe_noise* noise,
                        float w_importance, float w_load, moe_outputs* out,
