@@ -471,8 +471,6 @@ moe_status do_balance(const moe_config* c, const Layout& L, const void* x, const
 struct BwLayout {
   size_t dimp, dload, dhk, rinfo, dclean, draw, dbias_part, dxg, tiles, tiles_big, zero, hid, dp, db, dxs, part_g,
       part_n, xs, dys;
-  // tile map with descriptors of the fused hidden-layer kernel
-  size_t tiles_fz, desc_fz;
   // hierarchy: per-slot and per-group score gradients, and the routing
   // without capacity (when the forward capped it) for the secondary tables
   size_t cs, ns, dcp, drp, r_bits, r_base, r_counts, r_offsets, r_perm, r_inv;
@@ -540,10 +538,6 @@ BwLayout bw_layout(const moe_config* c) {
   L.dxg = take(4 * (size_t)T * d);
   L.tiles = take(4 * (size_t)(E + 1));
   L.tiles_big = take(4 * (size_t)(E + 1));
-  const bool fz = bw_hidden_fused_supported(es == 2, d, h, sw);
-  L.tiles_fz = take(fz ? 4 * (size_t)(E + 1) : 0);
-  L.desc_fz = take(fz ? 12 * (size_t)((A + bw_hidden_fused_rows() - 1) / bw_hidden_fused_rows() + E)
-                      : 0);
   L.zero = take(2 * (size_t)std::max(std::max(h, d), 128));
   L.hid = take(es * (size_t)A * h);
   L.dp = take(es * (size_t)A * h);
@@ -842,10 +836,8 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
       // workgroups per compute unit keep more table loads in flight)
       const int prow = bw_pos_tile_rows(bf16, A, E);
       // ReLU at d_model 512: the hidden layer and dX on per-tile streaming
-      // kernels (tile map of bw_hidden_fused_rows() rows, with descriptors)
+      // kernels, which find their tiles from the offsets
       const bool fz = !big && bw_hidden_fused_supported(bf16, d, h, sw);
-      int32_t* tfz = at<int32_t>(ws, L.tiles_fz);
-      int32_t* dfz = at<int32_t>(ws, L.desc_fz);
       if (!fz)
         MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, prow, tiles, nullptr, se),
                            "backward tiles"));
@@ -893,8 +885,6 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
       } else if (fz) {
         // the hidden layer recomputed with its gradient, each tile streaming
         // W1 and then W2 once
-        MOE_TRY(hip_status(launch_tile_map(sv->offsets, E, bw_hidden_fused_rows(), tfz, dfz, se),
-                           "backward tiles"));
         BwHidFusedArgs ha;
         ha.x = x;
         ha.dy = dy;
@@ -903,8 +893,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
         ha.k = k;
         ha.xs = xs;
         ha.dys = dys;
-        ha.tiles = tfz;
-        ha.desc = dfz;
+        ha.offsets = sv->offsets;
         ha.E = E;
         ha.h = h;
         ha.w1 = p->w1;
@@ -938,8 +927,7 @@ moe_status do_backward(const moe_config* c, const BwLayout& L, const void* x, co
       if (fz) {
         BwDxFusedArgs da;
         da.dp = dp;
-        da.tiles = tfz;
-        da.desc = dfz;
+        da.offsets = sv->offsets;
         da.E = E;
         da.h = h;
         da.w1 = p->w1;

@@ -9,8 +9,9 @@
 // k*b/n rows per expert (paper card, section 瓶颈) they are bound by reading
 // the two tables, and this kernel reads each table byte once per tile:
 //
-//   * one workgroup = one tile of at most 96 rows of one expert, found in
-//     the tile map (its 32-row blocks spread evenly over the expert's tiles);
+//   * one workgroup = one tile of at most 96 rows of one expert, found from
+//     the routing offsets as the forward's fused kernel finds its tiles (its
+//     32-row blocks spread evenly over the expert's tiles);
 //     the tiles of an expert run on one XCD together and share the table
 //     stream through its L2;
 //   * the tile gathers its routed rows itself (x, and dy times the slot's
@@ -65,8 +66,6 @@ size_t bw_hidden_fused_lds() {
 bool bw_hidden_fused_supported(bool bf16, int d, int h, bool swiglu) {
   return bf16 && !swiglu && d == BH_D && h % BH_H == 0 && h / BH_H <= BH_MAXCH && h > 0;
 }
-
-int bw_hidden_fused_rows() { return BH_M; }
 
 int64_t bw_hidden_fused_grid(int64_t A, int E) {
   const int64_t q = (A + BH_M - 1) / BH_M + E;  // tiles at most
@@ -312,20 +311,46 @@ __device__ __forceinline__ void bh_tile(const BwHidFusedArgs& a, int e, int p0, 
   }
 }
 
-// This workgroup's tile of the map: workgroup b takes tile (b % 8) *
-// ceil(Q / 8) + b / 8 of the Q tiles, so that the tiles of an expert
-// (consecutive in the map) run on one XCD (workgroups go to the XCDs
-// round-robin).  False for the workgroups past the last tile.
-__device__ __forceinline__ bool bh_find_tile(const int32_t* tiles, const int32_t* desc, int E,
-                                             int* e, int* p0, int* m) {
-  const int Q = tiles[E];
+// This workgroup's tile, found from the routing offsets with the forward's
+// fused-kernel numbering: expert e holds ceil(m_e / BH_M) tiles (m_e its
+// rows), numbered in expert order, its 32-row blocks split over them by
+// tile_rows.  Workgroup b takes tile (b % 8) * ceil(Q / 8) + b / 8 of the Q
+// tiles, so that the tiles of an expert run on one XCD (workgroups go to the
+// XCDs round-robin).  False for the workgroups past the last tile.  Every
+// thread of the workgroup calls it (a block scan and two barriers).
+__device__ __forceinline__ bool bh_find_tile(const int32_t* offsets, int E, int* e, int* p0,
+                                             int* m) {
+  __shared__ int s_info[3];
+  const int tid = threadIdx.x;
+  const int per = (E + BH_THREADS - 1) / BH_THREADS;  // experts per thread
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int nt = 0;
+  for (int x = e0; x < e1; ++x) nt += (offsets[x + 1] - offsets[x] + BH_M - 1) / BH_M;
+  int Q;
+  int run = block_excl_scan<BH_THREADS>(nt, &Q);
   const int perx = (Q + 7) / 8;
   const int slot = blockIdx.x >> 3, q = (blockIdx.x & 7) * perx + slot;
-  if (slot >= perx || q >= Q) return false;
-  *e = __builtin_amdgcn_readfirstlane(desc[3 * q]);
-  *p0 = __builtin_amdgcn_readfirstlane(desc[3 * q + 1]);
-  *m = __builtin_amdgcn_readfirstlane(desc[3 * q + 2]);
-  return true;
+  if (tid == 0) s_info[0] = -1;
+  __syncthreads();
+  if (slot < perx && q < Q && q >= run && q < run + nt) {
+    for (int x = e0; x < e1; ++x) {
+      const int o = offsets[x], mx = offsets[x + 1] - o, n = (mx + BH_M - 1) / BH_M;
+      if (q < run + n) {
+        int first, rows;
+        tile_rows(mx, n, q - run, &first, &rows);
+        s_info[0] = x;
+        s_info[1] = o + first;
+        s_info[2] = rows;
+        break;
+      }
+      run += n;
+    }
+  }
+  __syncthreads();
+  *e = __builtin_amdgcn_readfirstlane(s_info[0]);
+  *p0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+  *m = __builtin_amdgcn_readfirstlane(s_info[2]);
+  return *e >= 0;
 }
 
 template <bool PACKED>
@@ -338,7 +363,7 @@ __global__ __launch_bounds__(BH_THREADS, 1) void bw_hidden_fused_kernel(BwHidFus
   __shared__ int s_row[BH_M];
   __shared__ float s_gate[BH_M];
   int e, p0, m;
-  if (!bh_find_tile(a.tiles, a.desc, a.E, &e, &p0, &m)) return;
+  if (!bh_find_tile(a.offsets, a.E, &e, &p0, &m)) return;
   // only the 32-row blocks that hold rows run through the MFMAs
   const int mb = (m + 31) / 32;
   if (mb >= 3)
@@ -513,7 +538,7 @@ __global__ __launch_bounds__(BH_THREADS, 1) void bw_dx_fused_kernel(BwDxFusedArg
   bf16_t* Ps = bd_lds;
   bf16_t* Ws = bd_lds + 2 * BH_M * BH_SLD;
   int e, p0, m;
-  if (!bh_find_tile(a.tiles, a.desc, a.E, &e, &p0, &m)) return;
+  if (!bh_find_tile(a.offsets, a.E, &e, &p0, &m)) return;
   const int mb = (m + 31) / 32;
   if (mb >= 3)
     bd_tile<3>(a, e, p0, m, Ps, Ws);

@@ -163,8 +163,8 @@ struct BwHiddenArgs {
   void* d3;                // [A][h] out: dB (SwiGLU) or null
 };
 // The ReLU hidden layer's recompute and gradient at d_model 512 on tiles of
-// at most bw_hidden_fused_rows() rows of one expert (tile map with
-// descriptors), the tables streamed once per tile: hid = relu(xs W1^T) and
+// at most 96 rows of one expert (found by each workgroup
+// from the offsets), the tables streamed once per tile: hid = relu(xs W1^T) and
 // dp = (dys W2) * [xs W1^T > 0], both [A][h] bf16, where the kernel gathers
 // xs and dys itself (and writes them out).
 struct BwHidFusedArgs {
@@ -175,8 +175,7 @@ struct BwHidFusedArgs {
   int k;
   void* xs;                // [A][512] out: routed rows of x, in expert order
   void* dys;               // [A][512] out: gate-scaled output gradients, same order
-  const int32_t* tiles;    // [E+1] tile map (tiles[E] = number of tiles)
-  const int32_t* desc;     // [tiles][3] expert, first position, rows
+  const int32_t* offsets;  // [E+1] routing offsets
   int E, h;
   const void* w1;          // [E][h][512]
   const void* w2;          // [E][512][h]
@@ -184,18 +183,16 @@ struct BwHidFusedArgs {
   void* hid;               // [A][h] out
   void* dp;                // [A][h] out
 };
-// dxs = dp W1 ([A][512] bf16) for the same layers, on the same tile map
+// dxs = dp W1 ([A][512] bf16) for the same layers, on the same tiles
 struct BwDxFusedArgs {
   const void* dp;          // [A][h] bf16
-  const int32_t* tiles;    // [E+1] tile map of bw_hidden_fused_rows() rows
-  const int32_t* desc;     // [tiles][3]
+  const int32_t* offsets;  // [E+1] routing offsets
   int E, h;
   const void* w1;          // [E][h][512]
   void* dxs;               // [A][512] out
 };
 hipError_t launch_bw_dx_fused(const BwDxFusedArgs& a, int64_t A, hipStream_t s);
 bool bw_hidden_fused_supported(bool bf16, int d, int h, bool swiglu);
-int bw_hidden_fused_rows();
 hipError_t launch_bw_hidden_fused(const BwHidFusedArgs& a, int64_t A, hipStream_t s);
 bool bw_hidden_big_tiles(bool bf16, int64_t A, int E);
 int bw_hidden_big_rows();
