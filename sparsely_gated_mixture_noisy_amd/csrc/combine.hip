@@ -18,35 +18,42 @@
 
 namespace moe {
 
-template <typename T>
+// K (the slots per token) is a template argument, so that every slot's row
+// load is issued before the first one is used; a dropped slot reads row 0
+// and adds nothing.
+template <typename T, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ ys,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ gate, int64_t Tn,
-                                                      int k, int d, T* __restrict__ y) {
+                                                      int d, T* __restrict__ y) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= Tn) return;
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
-  int rows[8];
-  float g[8];
+  int rows[K];
+  float g[K];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    rows[s] = s < k ? inv[t * k + s] : 0;
-    g[s] = s < k ? gate[t * k + s] : 0.f;
+  for (int s = 0; s < K; ++s) {
+    rows[s] = inv[t * K + s];
+    g[s] = gate[t * K + s];
   }
   if (d % V == 0) {
     for (int c = lane * V; c < d; c += 64 * V) {
+      u32x4 raw[K];
+#pragma unroll
+      for (int s = 0; s < K; ++s)
+        raw[s] = *reinterpret_cast<const u32x4*>(ys + (int64_t)max(rows[s], 0) * d + c);
       float acc[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) acc[j] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (s < k && rows[s] >= 0) {
-          const T* src = ys + (int64_t)rows[s] * d + c;
-          u32x4 raw = *reinterpret_cast<const u32x4*>(src);
-          const T* vals = reinterpret_cast<const T*>(&raw);
+      for (int s = 0; s < K; ++s) {
+        const T* vals = reinterpret_cast<const T*>(&raw[s]);
+        const bool keep = rows[s] >= 0;
 #pragma unroll
-          for (int j = 0; j < V; ++j) acc[j] = fmaf(g[s], Elem<T>::load(vals, j), acc[j]);
+        for (int j = 0; j < V; ++j) {
+          const float f = fmaf(g[s], Elem<T>::load(vals, j), acc[j]);
+          acc[j] = keep ? f : acc[j];
         }
       }
       u32x4 out;
@@ -58,24 +65,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ ys,
   } else {
     for (int c = lane; c < d; c += 64) {
       float acc = 0.f;
-      for (int s = 0; s < k; ++s)
+#pragma unroll
+      for (int s = 0; s < K; ++s)
         if (rows[s] >= 0) acc = fmaf(g[s], Elem<T>::load(ys, (int64_t)rows[s] * d + c), acc);
       Elem<T>::store(y, t * d + c, acc);
     }
   }
 }
 
+template <typename T, int K>
+static hipError_t launch_combine_k(const void* y_sorted, const int32_t* inv, const float* gate,
+                                   int64_t T_, int d, void* y, hipStream_t s) {
+  hipLaunchKernelGGL((combine_kernel<T, K>), dim3((unsigned)((T_ + 3) / 4)), dim3(256), 0, s,
+                     (const T*)y_sorted, inv, gate, T_, d, (T*)y);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_combine_t(const void* y_sorted, const int32_t* inv, const float* gate,
+                                   int64_t T_, int k, int d, void* y, hipStream_t s) {
+  switch (k) {
+    case 1: return launch_combine_k<T, 1>(y_sorted, inv, gate, T_, d, y, s);
+    case 2: return launch_combine_k<T, 2>(y_sorted, inv, gate, T_, d, y, s);
+    case 3: return launch_combine_k<T, 3>(y_sorted, inv, gate, T_, d, y, s);
+    case 4: return launch_combine_k<T, 4>(y_sorted, inv, gate, T_, d, y, s);
+    case 5: return launch_combine_k<T, 5>(y_sorted, inv, gate, T_, d, y, s);
+    case 6: return launch_combine_k<T, 6>(y_sorted, inv, gate, T_, d, y, s);
+    case 7: return launch_combine_k<T, 7>(y_sorted, inv, gate, T_, d, y, s);
+    case 8: return launch_combine_k<T, 8>(y_sorted, inv, gate, T_, d, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_combine(const void* y_sorted, const int32_t* inv, const float* gate, int64_t T,
                           int k, int d, bool bf16, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((unsigned)((T + 3) / 4));
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)y_sorted, inv,
-                       gate, T, k, d, (bf16_t*)y);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const float*)y_sorted, inv,
-                       gate, T, k, d, (float*)y);
-  return hipGetLastError();
+  return bf16 ? launch_combine_t<bf16_t>(y_sorted, inv, gate, T, k, d, y, s)
+              : launch_combine_t<float>(y_sorted, inv, gate, T, k, d, y, s);
 }
 
 // ---------------------------------------------------------------------------
