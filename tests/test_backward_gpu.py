@@ -263,21 +263,25 @@ def test_backward_rejects_missing_and_misplaced_inputs():
     assert e.value.status == L.MOE_ERR_INVALID_ARG
 
 
-def test_backward_flat256_full_size_sampled():
-    """The full paper-shaped layer (8192 tokens, 256 experts, 512 -> 1024 ->
-    512, k = 4, noisy), in the launch configuration the timings use.  The
-    oracle computes, one by one: the table gradients of sampled experts
-    (from those experts' rows only) and the input gradients of sampled
-    tokens (from their own slots; the load-loss and importance gradients
-    need only the per-expert statistics, which the oracle computes over all
-    tokens).  Tokens whose scores around the threshold are within 1e-5 are
-    not sampled, nor experts that hold such a token."""
-    cfg = CONFIGS["flat256"]
+@pytest.mark.parametrize("name", ["flat256", "zipf2048"])
+def test_backward_flat_full_size_sampled(name):
+    """The full flat layers in the launch configuration the timings use: the
+    paper-shaped one (8192 tokens, 256 experts, 512 -> 1024 -> 512, k = 4,
+    noisy) and the Zipf-biased one (32768 tokens, 2048 experts, k = 2: idle,
+    single-row and hot experts of many tiles).  The oracle computes, one by
+    one: the table gradients of sampled experts (from those experts' rows
+    only; the hottest expert is always among them) and the input gradients
+    of sampled tokens (from their own slots; the load-loss and importance
+    gradients need only the per-expert statistics, which the oracle computes
+    over all tokens).  Tokens whose scores around the threshold are within
+    1e-5 are not sampled, nor experts that hold such a token in either
+    routing."""
+    cfg = CONFIGS[name]
     wi, wl = 1.0, 1.0
     inp = make_inputs(cfg, seed=0, device="cuda")
     cpu = {key: (v.to("cpu") if v is not None else None) for key, v in inp.items()}
     dy = make_upstream(cfg, seed=0, device="cuda")
-    _say("[backward] flat256 full size: forward + backward on the GPU")
+    _say(f"[backward] {name} full size: forward + backward on the GPU")
     binp = L.packed_params(cfg, inp)
     fwd = L.forward(cfg, inp["x"], binp, binp, wi, wl, balance=True, save=True)
     g = L.backward(cfg, inp["x"], binp, binp, fwd, dy, wi, wl)
@@ -288,21 +292,24 @@ def test_backward_flat256_full_size_sampled():
     gi = oracle.gate(cpu, cfg)
     T, k, E = cfg.tokens, cfg.top_k, cfg.n_experts
     idx, gates = gi["idx"], gi["gates"]
-    assert (np_(fwd.topk_idx) == idx).all()
+    srt = -np.sort(-gi["H"], axis=1)
+    risky = ((srt[:, k - 2:k + 1] - srt[:, k - 1:k + 2]) < GAP).any(axis=1)
+    gidx = np_(fwd.topk_idx)
+    assert (gidx[~risky] == idx[~risky]).all()
     counts, offsets, perm, inv = oracle.route(idx, E)
     imp = oracle.importance(idx, gates, E)
     load = oracle.load_estimate(gi["clean"], gi["sp"], gi["H"], idx, gi["kth"], gi["k1th"])
     dimp = wi * oracle.cv_squared_grad(imp)
-    srt = -np.sort(-gi["H"], axis=1)
-    risky = ((srt[:, k - 2:k + 1] - srt[:, k - 1:k + 2]) < GAP).any(axis=1)
     w1 = cpu["w1"].double().numpy()
     w2 = cpu["w2"].double().numpy()
     rng = np.random.default_rng(1)
 
     # table gradients of sampled experts
-    risky_e = set(idx[risky].reshape(-1).tolist())
+    risky_e = set(idx[risky].reshape(-1).tolist()) | set(gidx[risky].reshape(-1).tolist())
     cand = [e for e in range(E) if e not in risky_e and counts[e] > 0]
-    for e in rng.choice(cand, size=6, replace=False):
+    hot = max(cand, key=lambda e: counts[e])
+    sample = [hot] + [e for e in rng.choice(cand, size=6, replace=False) if e != hot][:5]
+    for e in sample:
         rows = perm[offsets[e]:offsets[e + 1]]
         toks = rows // k
         dY = gates.reshape(-1)[rows][:, None] * dyn[toks]
